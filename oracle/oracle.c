@@ -1,0 +1,359 @@
+/*
+ * oracle.c -- plain, slow CPU reference of one batch-1 decoder step (TEST INFRASTRUCTURE ONLY).
+ *
+ * Only the test-suite, the smoke check and the benchmark's CPU-baseline leg may load this file's
+ * library. It shares no code, header, table or constant with the GPU library.
+ *
+ * What it computes. The pages describe batch-1 autoregressive decoding of a dense decoder-only
+ * transformer: for each new token every active weight is read once, and the work is "MatMul,
+ * attention, normalization and sampling" inside one GPU-resident program (agentlenshq.com,
+ * 《突破内存墙：在标准 GPU 上实现 3,000 tokens/s 的推理速度》, sections "瓶颈：是内存带宽，而非计算" and
+ * "Kog 的解决方案 / The Monokernel Runtime"; aikraft.ru «3000 токенов в секунду…», §02 and §04
+ * "Моноядро"). The pages never write the decoder down, so this file follows the plainest
+ * Llama-style reading, listed in the design notes:
+ *   pre-RMSNorm blocks, no biases, untied LM head; RoPE with rotate-half pairs (i, i+hd/2) and
+ *   angles p * theta^(-2i/hd) computed in fp64; grouped-query attention where query head h reads
+ *   KV head h / (n_heads / n_kv_heads); causal softmax with scale 1/sqrt(hd); SwiGLU FFN
+ *   silu(Wg u) * (Wu u); K (after RoPE) and V rounded to bf16 (round-to-nearest-even) when written
+ *   to the cache.
+ *
+ * Precision: bf16 weights are widened exactly to fp32; activations and dot products are fp32 with
+ * one accumulator per output summed in ascending index order; the softmax denominator and the
+ * attention-weighted sum of V are fp64 (stored as fp32). No -ffast-math: every reduction runs in
+ * the order written here. Row loops may be split over threads (rows only), which cannot change
+ * any result bit.
+ *
+ * Sampling: greedy = argmax with ties to the lower index. Top-k: z = logits / T (fp32); the k
+ * largest z (ties to the lower index) in descending order; p_j = exp(z_j - z_0) / sum (fp64);
+ * u = (splitmix64(seed ^ splitmix64(pos)) >> 40) * 2^-24; the first j whose running fp64 sum of
+ * p exceeds u is chosen (the last one if none does). SplitMix64 is Steele, Lea & Flood,
+ * "Fast splittable pseudorandom number generators", OOPSLA 2014.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+  int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab_size;
+  float rms_eps, rope_theta;
+  int32_t max_seq;
+} oc_config;
+
+/* All matrices row-major [out][in], bf16 bit patterns. Per-layer arrays hold n_layers pointers. */
+typedef struct {
+  const uint16_t *embed, *final_norm, *lm_head;
+  const uint16_t *const *attn_norm, *const *wq, *const *wk, *const *wv, *const *wo;
+  const uint16_t *const *ffn_norm, *const *w_gate, *const *w_up, *const *w_down;
+} oc_weights;
+
+static int g_threads = 1;
+
+void oc_set_threads(int n) { g_threads = n < 1 ? 1 : n; }
+int oc_get_threads(void) { return g_threads; }
+
+/* ------------------------------------------------------------------ scalar helpers */
+
+float oc_bf16_to_f32(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+/* fp32 -> bf16 with round-to-nearest-even (NaN kept quiet). */
+uint16_t oc_f32_to_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7fffu + lsb;
+  return (uint16_t)(u >> 16);
+}
+
+uint64_t oc_splitmix64(uint64_t x) {
+  uint64_t z = x + 0x9e3779b97f4a7c15ull;
+  z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+  z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+  return z ^ (z >> 31);
+}
+
+/* uniform in [0,1) with 24 random bits, a function of (seed, pos) only */
+double oc_uniform(uint64_t seed, int64_t pos) {
+  uint64_t r = oc_splitmix64(seed ^ oc_splitmix64((uint64_t)pos));
+  return (double)(r >> 40) * (1.0 / 16777216.0);
+}
+
+/* ------------------------------------------------------------------ building blocks */
+
+/* y[r] = sum_k W[r][k] * x[k], fp32, k ascending. W is [rows][cols] bf16. */
+void oc_gemv(const uint16_t* W, const float* x, float* y, int rows, int cols) {
+  int r;
+#pragma omp parallel for num_threads(g_threads) schedule(static) if (g_threads > 1)
+  for (r = 0; r < rows; r++) {
+    const uint16_t* w = W + (size_t)r * cols;
+    float acc = 0.0f;
+    for (int k = 0; k < cols; k++) acc += oc_bf16_to_f32(w[k]) * x[k];
+    y[r] = acc;
+  }
+}
+
+/* u = x * (1/sqrt(mean(x^2) + eps)) * g ; the sum of squares is fp32, i ascending. */
+void oc_rmsnorm(const float* x, const uint16_t* g, float* u, int n, float eps) {
+  float ss = 0.0f;
+  for (int i = 0; i < n; i++) ss += x[i] * x[i];
+  float r = 1.0f / sqrtf(ss / (float)n + eps);
+  for (int i = 0; i < n; i++) u[i] = (x[i] * r) * oc_bf16_to_f32(g[i]);
+}
+
+/* Rotate each pair (y[i], y[i+hd/2]) of one head by angle pos * theta^(-2i/hd). */
+void oc_rope(float* y, int hd, int pos, float theta) {
+  int half = hd / 2;
+  for (int i = 0; i < half; i++) {
+    double freq = pow((double)theta, -2.0 * (double)i / (double)hd);
+    double phi = (double)pos * freq;
+    float c = (float)cos(phi), s = (float)sin(phi);
+    float a = y[i], b = y[i + half];
+    y[i] = a * c - b * s;
+    y[i + half] = b * c + a * s;
+  }
+}
+
+float oc_silu(float g) { return g / (1.0f + expf(-g)); }
+
+/* Softmax attention of one query over n cached rows (K, V rows of length hd, bf16, row stride
+ * `stride` elements). Scores fp32 (dot then / sqrt(hd)); exp, sum and weighted V sum in fp64.
+ * Writes out[hd]; if probs != NULL also the n probabilities (fp64). */
+void oc_attend(const float* q, const uint16_t* K, const uint16_t* V, int n, int hd, size_t stride,
+               float* out, double* probs) {
+  float* s = (float*)malloc(sizeof(float) * (size_t)(n > 0 ? n : 1));
+  double* acc = (double*)calloc((size_t)hd, sizeof(double));
+  float scale_div = sqrtf((float)hd);
+  float m = -INFINITY;
+  for (int t = 0; t < n; t++) {
+    const uint16_t* kr = K + (size_t)t * stride;
+    float dot = 0.0f;
+    for (int i = 0; i < hd; i++) dot += q[i] * oc_bf16_to_f32(kr[i]);
+    s[t] = dot / scale_div;
+    if (s[t] > m) m = s[t];
+  }
+  double S = 0.0;
+  for (int t = 0; t < n; t++) S += exp((double)s[t] - (double)m);
+  for (int t = 0; t < n; t++) {
+    double p = exp((double)s[t] - (double)m) / S;
+    if (probs) probs[t] = p;
+    const uint16_t* vr = V + (size_t)t * stride;
+    for (int i = 0; i < hd; i++) acc[i] += p * (double)oc_bf16_to_f32(vr[i]);
+  }
+  for (int i = 0; i < hd; i++) out[i] = (float)acc[i];
+  free(s);
+  free(acc);
+}
+
+int oc_argmax(const float* v, int n) {
+  int best = 0;
+  for (int i = 1; i < n; i++)
+    if (v[i] > v[best]) best = i;
+  return best;
+}
+
+/* Top-k candidates of z = logits / T in descending order (ties -> lower index), their fp64
+ * probabilities, the uniform draw and the chosen token. Returns the token. */
+int oc_topk_sample(const float* logits, int n, int k, float temperature, uint64_t seed, int64_t pos,
+                   int* cand_idx, double* cand_p, double* u_out) {
+  if (k < 1) k = 1;
+  if (k > n) k = n;
+  float* z = (float*)malloc(sizeof(float) * (size_t)n);
+  for (int i = 0; i < n; i++) z[i] = logits[i] / temperature;
+  /* selection by repeated scans: each round takes the largest remaining (lowest index on ties) */
+  char* used = (char*)calloc((size_t)n, 1);
+  int* idx = (int*)malloc(sizeof(int) * (size_t)k);
+  for (int j = 0; j < k; j++) {
+    int b = -1;
+    for (int i = 0; i < n; i++) {
+      if (used[i]) continue;
+      if (b < 0 || z[i] > z[b]) b = i;
+    }
+    idx[j] = b;
+    used[b] = 1;
+  }
+  double* e = (double*)malloc(sizeof(double) * (size_t)k);
+  double S = 0.0;
+  for (int j = 0; j < k; j++) {
+    e[j] = exp((double)z[idx[j]] - (double)z[idx[0]]);
+    S += e[j];
+  }
+  double u = oc_uniform(seed, pos);
+  int chosen = idx[k - 1];
+  double cum = 0.0;
+  int done = 0;
+  for (int j = 0; j < k; j++) {
+    double p = e[j] / S;
+    if (cand_idx) cand_idx[j] = idx[j];
+    if (cand_p) cand_p[j] = p;
+    cum += p;
+    if (!done && cum > u) {
+      chosen = idx[j];
+      done = 1;
+    }
+  }
+  if (u_out) *u_out = u;
+  free(z);
+  free(used);
+  free(idx);
+  free(e);
+  return chosen;
+}
+
+/* ------------------------------------------------------------------ one decode step */
+
+/* KV cache of the oracle: K and V planes, each [n_layers][n_kv_heads][max_seq][head_dim] bf16. */
+static size_t kv_off(const oc_config* c, int l, int j, int t) {
+  return (((size_t)l * c->n_kv_heads + j) * c->max_seq + t) * c->head_dim;
+}
+
+/* Process `token` at position `pos`: append its K/V to the cache, return the logits [V]. */
+int oc_step(const oc_config* c, const oc_weights* w, uint16_t* kc, uint16_t* vc, int token, int pos,
+            float* logits) {
+  const int d = c->d_model, hd = c->head_dim, nq = c->n_heads, nkv = c->n_kv_heads, F = c->ffn_dim;
+  if (pos < 0 || pos >= c->max_seq || token < 0 || token >= c->vocab_size) return -1;
+  if (nq % nkv != 0) return -1;
+  const int group = nq / nkv;
+  float* x = (float*)malloc(sizeof(float) * d);
+  float* u = (float*)malloc(sizeof(float) * d);
+  float* q = (float*)malloc(sizeof(float) * nq * hd);
+  float* k = (float*)malloc(sizeof(float) * nkv * hd);
+  float* v = (float*)malloc(sizeof(float) * nkv * hd);
+  float* o = (float*)malloc(sizeof(float) * nq * hd);
+  float* t = (float*)malloc(sizeof(float) * (d > F ? d : F));
+  float* g = (float*)malloc(sizeof(float) * F);
+  float* up = (float*)malloc(sizeof(float) * F);
+
+  for (int i = 0; i < d; i++) x[i] = oc_bf16_to_f32(w->embed[(size_t)token * d + i]);
+
+  for (int l = 0; l < c->n_layers; l++) {
+    /* attention block */
+    oc_rmsnorm(x, w->attn_norm[l], u, d, c->rms_eps);
+    oc_gemv(w->wq[l], u, q, nq * hd, d);
+    oc_gemv(w->wk[l], u, k, nkv * hd, d);
+    oc_gemv(w->wv[l], u, v, nkv * hd, d);
+    for (int h = 0; h < nq; h++) oc_rope(q + h * hd, hd, pos, c->rope_theta);
+    for (int j = 0; j < nkv; j++) oc_rope(k + j * hd, hd, pos, c->rope_theta);
+    for (int j = 0; j < nkv; j++)
+      for (int i = 0; i < hd; i++) {
+        kc[kv_off(c, l, j, pos) + i] = oc_f32_to_bf16(k[j * hd + i]);
+        vc[kv_off(c, l, j, pos) + i] = oc_f32_to_bf16(v[j * hd + i]);
+      }
+    for (int h = 0; h < nq; h++) {
+      int j = h / group;
+      oc_attend(q + h * hd, kc + kv_off(c, l, j, 0), vc + kv_off(c, l, j, 0), pos + 1, hd, (size_t)hd,
+                o + h * hd, NULL);
+    }
+    oc_gemv(w->wo[l], o, t, d, nq * hd);
+    for (int i = 0; i < d; i++) x[i] += t[i];
+    /* feed-forward block */
+    oc_rmsnorm(x, w->ffn_norm[l], u, d, c->rms_eps);
+    oc_gemv(w->w_gate[l], u, g, F, d);
+    oc_gemv(w->w_up[l], u, up, F, d);
+    for (int i = 0; i < F; i++) g[i] = oc_silu(g[i]) * up[i];
+    oc_gemv(w->w_down[l], g, t, d, F);
+    for (int i = 0; i < d; i++) x[i] += t[i];
+  }
+  oc_rmsnorm(x, w->final_norm, u, d, c->rms_eps);
+  oc_gemv(w->lm_head, u, logits, c->vocab_size, d);
+
+  free(x); free(u); free(q); free(k); free(v); free(o); free(t); free(g); free(up);
+  return 0;
+}
+
+/* ------------------------------------------------------------------ brute-force recompute */
+
+/* Whole-sequence pass in matrix form with no cache reuse: every position's hidden state is
+ * carried through all layers as a [n][d] matrix and attention applies an explicit causal mask.
+ * K and V are rounded to bf16 like the cache. Writes logits [n][V]. Written independently of
+ * oc_step so that caching, position bookkeeping and masking are cross-checked. */
+int oc_full_recompute(const oc_config* c, const oc_weights* w, const int* tokens, int n, float* logits) {
+  const int d = c->d_model, hd = c->head_dim, nq = c->n_heads, nkv = c->n_kv_heads, F = c->ffn_dim;
+  if (n <= 0 || nq % nkv != 0) return -1;
+  for (int r = 0; r < n; r++)
+    if (tokens[r] < 0 || tokens[r] >= c->vocab_size) return -1;
+  const int group = nq / nkv;
+  float* X = (float*)malloc(sizeof(float) * (size_t)n * d);
+  float* U = (float*)malloc(sizeof(float) * (size_t)n * d);
+  float* Q = (float*)malloc(sizeof(float) * (size_t)n * nq * hd);
+  float* Kf = (float*)malloc(sizeof(float) * (size_t)n * nkv * hd);
+  float* Vf = (float*)malloc(sizeof(float) * (size_t)n * nkv * hd);
+  uint16_t* Kb = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)nkv * n * hd); /* [j][t][i] */
+  uint16_t* Vb = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)nkv * n * hd);
+  float* O = (float*)malloc(sizeof(float) * (size_t)n * nq * hd);
+  float* T = (float*)malloc(sizeof(float) * (size_t)n * (d > F ? d : F));
+  float* G = (float*)malloc(sizeof(float) * (size_t)n * F);
+  float* Up = (float*)malloc(sizeof(float) * (size_t)n * F);
+  float* sc = (float*)malloc(sizeof(float) * (size_t)n);
+
+  for (int r = 0; r < n; r++) {
+    int tok = tokens[r] < 0 || tokens[r] >= c->vocab_size ? 0 : tokens[r];
+    for (int i = 0; i < d; i++) X[(size_t)r * d + i] = oc_bf16_to_f32(w->embed[(size_t)tok * d + i]);
+  }
+  for (int l = 0; l < c->n_layers; l++) {
+    for (int r = 0; r < n; r++) oc_rmsnorm(X + (size_t)r * d, w->attn_norm[l], U + (size_t)r * d, d, c->rms_eps);
+    for (int r = 0; r < n; r++) {
+      oc_gemv(w->wq[l], U + (size_t)r * d, Q + (size_t)r * nq * hd, nq * hd, d);
+      oc_gemv(w->wk[l], U + (size_t)r * d, Kf + (size_t)r * nkv * hd, nkv * hd, d);
+      oc_gemv(w->wv[l], U + (size_t)r * d, Vf + (size_t)r * nkv * hd, nkv * hd, d);
+      for (int h = 0; h < nq; h++) oc_rope(Q + (size_t)r * nq * hd + h * hd, hd, r, c->rope_theta);
+      for (int j = 0; j < nkv; j++) oc_rope(Kf + (size_t)r * nkv * hd + j * hd, hd, r, c->rope_theta);
+    }
+    for (int j = 0; j < nkv; j++)
+      for (int r = 0; r < n; r++)
+        for (int i = 0; i < hd; i++) {
+          Kb[((size_t)j * n + r) * hd + i] = oc_f32_to_bf16(Kf[(size_t)r * nkv * hd + j * hd + i]);
+          Vb[((size_t)j * n + r) * hd + i] = oc_f32_to_bf16(Vf[(size_t)r * nkv * hd + j * hd + i]);
+        }
+    /* masked attention: row r attends to columns s <= r; masked columns get probability 0 */
+    float scale_div = sqrtf((float)hd);
+    for (int r = 0; r < n; r++)
+      for (int h = 0; h < nq; h++) {
+        int j = h / group;
+        const float* qr = Q + (size_t)r * nq * hd + h * hd;
+        float m = -INFINITY;
+        for (int s = 0; s < n; s++) {
+          if (s > r) { sc[s] = -INFINITY; continue; }
+          const uint16_t* kr = Kb + ((size_t)j * n + s) * hd;
+          float dot = 0.0f;
+          for (int i = 0; i < hd; i++) dot += qr[i] * oc_bf16_to_f32(kr[i]);
+          sc[s] = dot / scale_div;
+          if (sc[s] > m) m = sc[s];
+        }
+        double S = 0.0;
+        for (int s = 0; s < n; s++)
+          if (s <= r) S += exp((double)sc[s] - (double)m);
+        for (int i = 0; i < hd; i++) {
+          double a = 0.0;
+          for (int s = 0; s <= r; s++) {
+            double p = exp((double)sc[s] - (double)m) / S;
+            a += p * (double)oc_bf16_to_f32(Vb[((size_t)j * n + s) * hd + i]);
+          }
+          O[(size_t)r * nq * hd + h * hd + i] = (float)a;
+        }
+      }
+    for (int r = 0; r < n; r++) {
+      oc_gemv(w->wo[l], O + (size_t)r * nq * hd, T + (size_t)r * d, d, nq * hd);
+      for (int i = 0; i < d; i++) X[(size_t)r * d + i] += T[(size_t)r * d + i];
+    }
+    for (int r = 0; r < n; r++) oc_rmsnorm(X + (size_t)r * d, w->ffn_norm[l], U + (size_t)r * d, d, c->rms_eps);
+    for (int r = 0; r < n; r++) {
+      oc_gemv(w->w_gate[l], U + (size_t)r * d, G + (size_t)r * F, F, d);
+      oc_gemv(w->w_up[l], U + (size_t)r * d, Up + (size_t)r * F, F, d);
+      for (int i = 0; i < F; i++) G[(size_t)r * F + i] = oc_silu(G[(size_t)r * F + i]) * Up[(size_t)r * F + i];
+      oc_gemv(w->w_down[l], G + (size_t)r * F, T + (size_t)r * d, d, F);
+      for (int i = 0; i < d; i++) X[(size_t)r * d + i] += T[(size_t)r * d + i];
+    }
+  }
+  for (int r = 0; r < n; r++) {
+    oc_rmsnorm(X + (size_t)r * d, w->final_norm, U + (size_t)r * d, d, c->rms_eps);
+    oc_gemv(w->lm_head, U + (size_t)r * d, logits + (size_t)r * c->vocab_size, c->vocab_size, d);
+  }
+  free(X); free(U); free(Q); free(Kf); free(Vf); free(Kb); free(Vb); free(O); free(T); free(G); free(Up); free(sc);
+  return 0;
+}

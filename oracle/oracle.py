@@ -1,0 +1,240 @@
+"""ctypes front end of ``oracle.c`` (test infrastructure only).
+
+Arrays go in as NumPy arrays (bf16 as uint16 bit patterns). Nothing here computes part of the
+decoder: every arithmetic step runs in the C file.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+
+def lib_path() -> str:
+    return _LIB
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (-O2, no fast-math, OpenMP for row splitting only)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC",
+                               "-shared", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = C.CDLL(_LIB)
+        f32p = C.POINTER(C.c_float)
+        f64p = C.POINTER(C.c_double)
+        u16p = C.POINTER(C.c_uint16)
+        i32p = C.POINTER(C.c_int32)
+        lib.oc_gemv.argtypes = [u16p, f32p, f32p, C.c_int, C.c_int]
+        lib.oc_rmsnorm.argtypes = [f32p, u16p, f32p, C.c_int, C.c_float]
+        lib.oc_rope.argtypes = [f32p, C.c_int, C.c_int, C.c_float]
+        lib.oc_silu.argtypes = [C.c_float]
+        lib.oc_silu.restype = C.c_float
+        lib.oc_attend.argtypes = [f32p, u16p, u16p, C.c_int, C.c_int, C.c_size_t, f32p, f64p]
+        lib.oc_argmax.argtypes = [f32p, C.c_int]
+        lib.oc_argmax.restype = C.c_int
+        lib.oc_topk_sample.argtypes = [f32p, C.c_int, C.c_int, C.c_float, C.c_uint64, C.c_int64, i32p, f64p,
+                                       f64p]
+        lib.oc_topk_sample.restype = C.c_int
+        lib.oc_splitmix64.argtypes = [C.c_uint64]
+        lib.oc_splitmix64.restype = C.c_uint64
+        lib.oc_uniform.argtypes = [C.c_uint64, C.c_int64]
+        lib.oc_uniform.restype = C.c_double
+        lib.oc_f32_to_bf16.argtypes = [C.c_float]
+        lib.oc_f32_to_bf16.restype = C.c_uint16
+        lib.oc_bf16_to_f32.argtypes = [C.c_uint16]
+        lib.oc_bf16_to_f32.restype = C.c_float
+        lib.oc_set_threads.argtypes = [C.c_int]
+        lib.oc_step.argtypes = [C.c_void_p, C.c_void_p, u16p, u16p, C.c_int, C.c_int, f32p]
+        lib.oc_step.restype = C.c_int
+        lib.oc_full_recompute.argtypes = [C.c_void_p, C.c_void_p, i32p, C.c_int, f32p]
+        lib.oc_full_recompute.restype = C.c_int
+        _lib = lib
+    return _lib
+
+
+def _p(a: np.ndarray, ct):
+    return a.ctypes.data_as(C.POINTER(ct))
+
+
+def set_threads(n: int) -> None:
+    _load().oc_set_threads(int(n))
+
+
+def gemv(W: np.ndarray, x: np.ndarray) -> np.ndarray:
+    W = np.ascontiguousarray(W, dtype=np.uint16)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, cols = W.shape
+    y = np.empty(rows, dtype=np.float32)
+    _load().oc_gemv(_p(W, C.c_uint16), _p(x, C.c_float), _p(y, C.c_float), rows, cols)
+    return y
+
+
+def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    g = np.ascontiguousarray(g, dtype=np.uint16)
+    u = np.empty_like(x)
+    _load().oc_rmsnorm(_p(x, C.c_float), _p(g, C.c_uint16), _p(u, C.c_float), len(x), eps)
+    return u
+
+
+def rope(y: np.ndarray, pos: int, theta: float) -> np.ndarray:
+    y = np.array(y, dtype=np.float32, copy=True)
+    _load().oc_rope(_p(y, C.c_float), len(y), int(pos), theta)
+    return y
+
+
+def silu(g: float) -> float:
+    return float(_load().oc_silu(float(g)))
+
+
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray):
+    """Softmax attention of q [hd] over K, V [n][hd] (bf16 bits). Returns (out [hd], probs [n])."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    K = np.ascontiguousarray(K, dtype=np.uint16)
+    V = np.ascontiguousarray(V, dtype=np.uint16)
+    n, hd = K.shape
+    out = np.empty(hd, dtype=np.float32)
+    probs = np.empty(max(n, 1), dtype=np.float64)
+    _load().oc_attend(_p(q, C.c_float), _p(K, C.c_uint16), _p(V, C.c_uint16), n, hd, hd, _p(out, C.c_float),
+                      _p(probs, C.c_double))
+    return out, probs[:n]
+
+
+def argmax(v: np.ndarray) -> int:
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    return int(_load().oc_argmax(_p(v, C.c_float), len(v)))
+
+
+def topk_sample(logits: np.ndarray, k: int, temperature: float, seed: int, pos: int):
+    """Returns (token, candidate ids [k], candidate probabilities [k], u)."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    kk = max(1, min(k, len(logits)))
+    idx = np.empty(kk, dtype=np.int32)
+    p = np.empty(kk, dtype=np.float64)
+    u = C.c_double(0.0)
+    tok = _load().oc_topk_sample(_p(logits, C.c_float), len(logits), k, temperature, seed & (2**64 - 1), pos,
+                                 _p(idx, C.c_int32), _p(p, C.c_double), C.byref(u))
+    return int(tok), idx, p, float(u.value)
+
+
+def splitmix64(x: int) -> int:
+    return int(_load().oc_splitmix64(x & (2**64 - 1)))
+
+
+def uniform(seed: int, pos: int) -> float:
+    return float(_load().oc_uniform(seed & (2**64 - 1), pos))
+
+
+def f32_to_bf16(x: float) -> int:
+    return int(_load().oc_f32_to_bf16(float(x)))
+
+
+def bf16_to_f32(b: int) -> float:
+    return float(_load().oc_bf16_to_f32(int(b)))
+
+
+class _Cfg(C.Structure):
+    _fields_ = [("n_layers", C.c_int32), ("d_model", C.c_int32), ("n_heads", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn_dim", C.c_int32),
+                ("vocab_size", C.c_int32), ("rms_eps", C.c_float), ("rope_theta", C.c_float),
+                ("max_seq", C.c_int32)]
+
+
+_PP = C.POINTER(C.POINTER(C.c_uint16))
+
+
+class _W(C.Structure):
+    _fields_ = [("embed", C.POINTER(C.c_uint16)), ("final_norm", C.POINTER(C.c_uint16)),
+                ("lm_head", C.POINTER(C.c_uint16)), ("attn_norm", _PP), ("wq", _PP), ("wk", _PP),
+                ("wv", _PP), ("wo", _PP), ("ffn_norm", _PP), ("w_gate", _PP), ("w_up", _PP),
+                ("w_down", _PP)]
+
+
+_LAYER_KEYS = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")
+
+
+class OracleModel:
+    """The decoder of one configuration with its own bf16 KV cache.
+
+    ``cfg`` needs attributes n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab_size,
+    rms_eps, rope_theta. ``weights`` maps names to uint16 arrays (per-layer names to lists).
+    """
+
+    def __init__(self, cfg, weights: Dict[str, object], max_seq: int):
+        self.cfg = cfg
+        self.max_seq = int(max_seq)
+        self._keep = []
+        self._c = _Cfg(cfg.n_layers, cfg.d_model, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn_dim,
+                       cfg.vocab_size, cfg.rms_eps, cfg.rope_theta, self.max_seq)
+
+        def arr(a):
+            a = np.ascontiguousarray(a, dtype=np.uint16)
+            self._keep.append(a)
+            return a.ctypes.data_as(C.POINTER(C.c_uint16))
+
+        def arrs(lst):
+            ptrs = (C.POINTER(C.c_uint16) * len(lst))(*[arr(a) for a in lst])
+            self._keep.append(ptrs)
+            return C.cast(ptrs, _PP)
+
+        self._w = _W(arr(weights["embed"]), arr(weights["final_norm"]), arr(weights["lm_head"]),
+                     *[arrs(weights[k]) for k in _LAYER_KEYS])
+        kv_elems = cfg.n_layers * cfg.n_kv_heads * self.max_seq * cfg.head_dim
+        self.kcache = np.zeros(kv_elems, dtype=np.uint16)
+        self.vcache = np.zeros(kv_elems, dtype=np.uint16)
+        self.pos = 0
+
+    def kv_view(self):
+        shape = (self.cfg.n_layers, self.cfg.n_kv_heads, self.max_seq, self.cfg.head_dim)
+        return self.kcache.reshape(shape), self.vcache.reshape(shape)
+
+    def step(self, token: int, pos: Optional[int] = None) -> np.ndarray:
+        pos = self.pos if pos is None else int(pos)
+        logits = np.empty(self.cfg.vocab_size, dtype=np.float32)
+        rc = _load().oc_step(C.byref(self._c), C.byref(self._w), _p(self.kcache, C.c_uint16),
+                             _p(self.vcache, C.c_uint16), int(token), pos, _p(logits, C.c_float))
+        if rc != 0:
+            raise ValueError(f"oracle step rejected token={token} pos={pos}")
+        self.pos = pos + 1
+        return logits
+
+    def run(self, tokens: Sequence[int], start_pos: int = 0) -> np.ndarray:
+        """Feed tokens at positions start_pos.. and return all their logits [n][V]."""
+        out = np.empty((len(tokens), self.cfg.vocab_size), dtype=np.float32)
+        for i, t in enumerate(tokens):
+            out[i] = self.step(int(t), start_pos + i)
+        return out
+
+    def full_recompute(self, tokens: Sequence[int]) -> np.ndarray:
+        return full_recompute(self, tokens)
+
+
+def full_recompute(model: OracleModel, tokens: Sequence[int]) -> np.ndarray:
+    toks = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+    n = len(toks)
+    out = np.empty((n, model.cfg.vocab_size), dtype=np.float32)
+    rc = _load().oc_full_recompute(C.byref(model._c), C.byref(model._w), _p(toks, C.c_int32), n,
+                                   _p(out, C.c_float))
+    if rc != 0:
+        raise ValueError("oracle full recompute rejected its input")
+    return out
