@@ -1,0 +1,470 @@
+// api.cpp -- host side of the C ABI declared in include/kie.h: validation, set-up, launches.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/kie.h"
+#include "../../include/kie_measure.h"
+#include "layout.h"
+#include "monokernel.h"
+
+namespace kie {
+hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes, int32_t blocks, hipStream_t st);
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t blocks, hipStream_t st);
+}  // namespace kie
+
+using namespace kie;
+
+struct kie_ctx {
+  Shape s;
+  Exch exo;
+  Workspace wso;
+  int device;
+  hipStream_t stream;
+  uint8_t* packed;
+  uint16_t* kv;
+  uint8_t* ws;
+  KernelFn kernel;
+  int32_t ring;
+  int32_t lds;
+  int32_t pos;
+  uint32_t epoch;  // tag of the next step
+  bool bad_state;
+  int64_t timeout_ticks;
+  std::vector<int64_t> wbase_host;
+  std::string last_error;
+};
+
+static std::string g_create_error;
+
+static void set_err(std::string* dst, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  if (dst) *dst = buf;
+}
+
+#define HIP_TRY(dst, call)                                                               \
+  do {                                                                                   \
+    hipError_t e_ = (call);                                                              \
+    if (e_ != hipSuccess) {                                                              \
+      set_err(dst, "%s failed: %s", #call, hipGetErrorString(e_));                       \
+      return KIE_ERR_HIP;                                                                \
+    }                                                                                    \
+  } while (0)
+
+static int query_cus(int* out, std::string* err) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    set_err(err, "no HIP device");
+    return KIE_ERR_HIP;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    set_err(err, "cannot query the compute-unit count");
+    return KIE_ERR_HIP;
+  }
+  *out = n;
+  return KIE_OK;
+}
+
+// Shape from a config; nwg = compute units of the current device (or `nwg_override` > 0).
+static kie_status make_shape(const kie_config* c, int nwg_override, Shape* s, std::string* err) {
+  if (!c) {
+    set_err(err, "config is NULL");
+    return KIE_ERR_INVALID_ARG;
+  }
+  int nwg = nwg_override;
+  if (nwg <= 0) {
+    kie_status st = query_cus(&nwg, err);
+    if (st != KIE_OK) return st;
+  }
+  s->L = c->n_layers;
+  s->d = c->d_model;
+  s->nq = c->n_heads;
+  s->nkv = c->n_kv_heads;
+  s->hd = c->head_dim;
+  s->F = c->ffn_dim;
+  s->V = c->vocab_size;
+  s->max_seq = c->max_seq_len;
+  s->eps = c->rms_eps;
+  s->theta = c->rope_theta;
+  s->nwg = nwg;
+  if (c->n_layers <= 0 || c->d_model <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 ||
+      c->ffn_dim <= 0 || c->vocab_size <= 0 || c->max_seq_len <= 0 || !(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) {
+    set_err(err, "config has a non-positive size");
+    return KIE_ERR_INVALID_ARG;
+  }
+  if (c->n_experts != 0 || c->n_experts_active != 0 || c->expert_ffn_dim != 0) {
+    set_err(err, "mixture-of-experts layers are not supported by this kernel");
+    return KIE_ERR_UNSUPPORTED;
+  }
+  if (s->d % kTileK || s->qdim() % kTileK || s->F % kTileK) {
+    set_err(err, "d_model (%d), n_heads*head_dim (%d) and ffn_dim (%d) must be multiples of %d", s->d, s->qdim(), s->F,
+            kTileK);
+    return KIE_ERR_UNSUPPORTED;
+  }
+  if (s->hd != 64 && s->hd != 128) {
+    set_err(err, "head_dim must be 64 or 128 (got %d)", s->hd);
+    return KIE_ERR_UNSUPPORTED;
+  }
+  if (s->nq % s->nkv) {
+    set_err(err, "n_heads (%d) must be a multiple of n_kv_heads (%d)", s->nq, s->nkv);
+    return KIE_ERR_UNSUPPORTED;
+  }
+  const int G = s->nq / s->nkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) {
+    set_err(err, "n_heads / n_kv_heads must be 1, 2, 4 or 8 (got %d)", G);
+    return KIE_ERR_UNSUPPORTED;
+  }
+  if (s->V % 2 || s->d % 2) {
+    set_err(err, "vocab_size and d_model must be even");
+    return KIE_ERR_UNSUPPORTED;
+  }
+  if (nwg > kMaxWG || nwg % s->nkv) {
+    set_err(err, "the compute-unit count (%d) must be a multiple of n_kv_heads (%d) and at most %d", nwg, s->nkv,
+            kMaxWG);
+    return KIE_ERR_UNSUPPORTED;
+  }
+  if ((int64_t)s->V * s->d >= (int64_t)1 << 40) {
+    set_err(err, "embedding too large");
+    return KIE_ERR_UNSUPPORTED;
+  }
+  return KIE_OK;
+}
+
+extern "C" {
+
+size_t kie_packed_weight_bytes(const kie_config* cfg) {
+  Shape s;
+  if (make_shape(cfg, 0, &s, nullptr) != KIE_OK) return 0;
+  return (size_t)packed_bytes(s);
+}
+
+size_t kie_kv_cache_bytes(const kie_config* cfg) {
+  Shape s;
+  if (make_shape(cfg, 0, &s, nullptr) != KIE_OK) return 0;
+  return (size_t)kv_bytes(s);
+}
+
+size_t kie_workspace_bytes(const kie_config* cfg) {
+  Shape s;
+  if (make_shape(cfg, 0, &s, nullptr) != KIE_OK) return 0;
+  return (size_t)workspace_layout(s).end;
+}
+
+int32_t kie_num_workgroups(void) {
+  int n = 0;
+  kie_status st = query_cus(&n, nullptr);
+  return st == KIE_OK ? n : st;
+}
+
+const char* kie_status_string(kie_status status) {
+  switch (status) {
+    case KIE_OK: return "ok";
+    case KIE_ERR_INVALID_ARG: return "invalid argument";
+    case KIE_ERR_UNSUPPORTED: return "unsupported configuration or device";
+    case KIE_ERR_CAPACITY: return "KV capacity exceeded";
+    case KIE_ERR_HIP: return "HIP runtime error";
+    case KIE_ERR_STATE: return "context holds a device error (call kie_reset)";
+    case KIE_ERR_TIMEOUT: return "device wait timed out";
+    case KIE_ERR_ABORTED: return "device run aborted";
+    default: return "unknown status";
+  }
+}
+
+const char* kie_last_error(const kie_ctx* ctx) { return ctx ? ctx->last_error.c_str() : g_create_error.c_str(); }
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packed, void* kv_cache, void* workspace,
+                      void* hip_stream, kie_ctx** out) {
+  if (out) *out = nullptr;
+  g_create_error.clear();
+  std::string* err = &g_create_error;
+  if (!out || !src || !packed || !kv_cache || !workspace) {
+    set_err(err, "NULL argument");
+    return KIE_ERR_INVALID_ARG;
+  }
+  Shape s;
+  kie_status st = make_shape(cfg, 0, &s, err);
+  if (st != KIE_OK) return st;
+  const int L = s.L;
+  if (!src->embed || !src->final_norm || !src->lm_head || !src->attn_norm || !src->wq || !src->wk || !src->wv ||
+      !src->wo || !src->ffn_norm || !src->w_gate || !src->w_up || !src->w_down) {
+    set_err(err, "a weight pointer is NULL");
+    return KIE_ERR_INVALID_ARG;
+  }
+  for (int l = 0; l < L; ++l) {
+    const void* ps[] = {src->attn_norm[l], src->wq[l], src->wk[l], src->wv[l], src->wo[l],
+                        src->ffn_norm[l], src->w_gate[l], src->w_up[l], src->w_down[l]};
+    for (const void* p : ps) {
+      if (!p || !aligned16(p)) {
+        set_err(err, "layer %d: a weight pointer is NULL or not 16-byte aligned", l);
+        return KIE_ERR_INVALID_ARG;
+      }
+    }
+  }
+  if (!aligned16(src->embed) || !aligned16(src->lm_head) || !aligned16(packed) || !aligned16(kv_cache) ||
+      !aligned16(workspace)) {
+    set_err(err, "device buffers must be 16-byte aligned");
+    return KIE_ERR_INVALID_ARG;
+  }
+  int dev = 0;
+  HIP_TRY(err, hipGetDevice(&dev));
+  hipDeviceProp_t prop;
+  HIP_TRY(err, hipGetDeviceProperties(&prop, dev));
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+    set_err(err, "device %s is not gfx950", prop.gcnArchName);
+    return KIE_ERR_UNSUPPORTED;
+  }
+  if (!prop.cooperativeLaunch) {
+    set_err(err, "device does not support cooperative launches");
+    return KIE_ERR_UNSUPPORTED;
+  }
+  const int lds_limit = (int)prop.sharedMemPerBlock;
+  const int32_t ring = max_ring_slots(s, lds_limit);
+  if (ring < 16) {
+    set_err(err, "shape needs too much LDS (ring of %d tiles)", ring);
+    return KIE_ERR_UNSUPPORTED;
+  }
+  KernelFn kfn = decode_kernel_for(s.group(), s.hd);
+  if (!kfn) {
+    set_err(err, "no kernel for group %d head_dim %d", s.group(), s.hd);
+    return KIE_ERR_UNSUPPORTED;
+  }
+  const int32_t lds = lds_bytes_for(s, ring);
+  HIP_TRY(err, hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, lds));
+  int occ = 0;
+  HIP_TRY(err, hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)kfn, kThreads, lds));
+  if (occ < 1) {
+    set_err(err, "the decode kernel cannot be resident (occupancy %d)", occ);
+    return KIE_ERR_UNSUPPORTED;
+  }
+
+  kie_ctx* c = new kie_ctx();
+  c->s = s;
+  c->exo = exch_layout(s);
+  c->wso = workspace_layout(s);
+  c->device = dev;
+  c->stream = (hipStream_t)hip_stream;
+  c->packed = (uint8_t*)packed;
+  c->kv = (uint16_t*)kv_cache;
+  c->ws = (uint8_t*)workspace;
+  c->kernel = kfn;
+  c->ring = ring;
+  c->lds = lds;
+  c->pos = 0;
+  c->epoch = 1;
+  c->bad_state = false;
+  c->timeout_ticks = 200000000;  // 2 s per wait
+  c->wbase_host.resize(s.nwg + 1);
+  int64_t acc = 0;
+  for (int w = 0; w < s.nwg; ++w) {
+    c->wbase_host[w] = acc;
+    acc += wg_token_tiles(s, w);
+  }
+  c->wbase_host[s.nwg] = acc;
+
+  auto fail = [&](const char* what, hipError_t e) {
+    set_err(err, "%s: %s", what, hipGetErrorString(e));
+    delete c;
+    return KIE_ERR_HIP;
+  };
+  hipError_t e;
+  hipStream_t stm = c->stream;
+  // workspace: exchange words and error word to zero, RoPE table, stream bases, norm gains
+  if ((e = hipMemsetAsync(c->ws, 0, (size_t)c->wso.end, stm)) != hipSuccess) return fail("clear workspace", e);
+  if ((e = launch_rope_table((float2*)(c->ws + c->wso.rope), s.max_seq, s.hd, s.theta, stm)) != hipSuccess)
+    return fail("rope table", e);
+  if ((e = hipMemcpyAsync(c->ws + c->wso.wbase, c->wbase_host.data(), (size_t)(s.nwg + 1) * 8, hipMemcpyHostToDevice,
+                          stm)) != hipSuccess)
+    return fail("copy stream bases", e);
+  uint16_t* norms = (uint16_t*)(c->ws + c->wso.norms);
+  for (int l = 0; l < L; ++l) {
+    if ((e = hipMemcpyAsync(norms + (size_t)l * 2 * s.d, src->attn_norm[l], (size_t)s.d * 2, hipMemcpyDeviceToDevice,
+                            stm)) != hipSuccess)
+      return fail("copy norms", e);
+    if ((e = hipMemcpyAsync(norms + (size_t)l * 2 * s.d + s.d, src->ffn_norm[l], (size_t)s.d * 2,
+                            hipMemcpyDeviceToDevice, stm)) != hipSuccess)
+      return fail("copy norms", e);
+  }
+  if ((e = hipMemcpyAsync(norms + (size_t)L * 2 * s.d, src->final_norm, (size_t)s.d * 2, hipMemcpyDeviceToDevice,
+                          stm)) != hipSuccess)
+    return fail("copy norms", e);
+  // weights: per-WG token streams, then the embedding table
+  const int64_t* wbase_dev = (const int64_t*)(c->ws + c->wso.wbase);
+  for (int l = 0; l <= L; ++l) {
+    PackArgs a;
+    memset(&a, 0, sizeof a);
+    a.s = s;
+    a.packed = c->packed;
+    a.wbase = wbase_dev;
+    a.layer = l;
+    if (l < L) {
+      a.wq = src->wq[l];
+      a.wk = src->wk[l];
+      a.wv = src->wv[l];
+      a.wo = src->wo[l];
+      a.wgate = src->w_gate[l];
+      a.wup = src->w_up[l];
+      a.wdown = src->w_down[l];
+    } else {
+      a.lm_head = src->lm_head;
+    }
+    if ((e = launch_pack_layer(a, stm)) != hipSuccess) return fail("pack weights", e);
+  }
+  if ((e = hipMemcpyAsync(c->packed + packed_embed_offset(s), src->embed, (size_t)s.V * s.d * 2,
+                          hipMemcpyDeviceToDevice, stm)) != hipSuccess)
+    return fail("copy embedding", e);
+  *out = c;
+  return KIE_OK;
+}
+
+void kie_destroy(kie_ctx* ctx) { delete ctx; }
+
+int32_t kie_position(const kie_ctx* ctx) { return ctx ? ctx->pos : -1; }
+
+kie_status kie_reset(kie_ctx* ctx) {
+  if (!ctx) return KIE_ERR_INVALID_ARG;
+  HIP_TRY(&ctx->last_error, hipSetDevice(ctx->device));
+  HIP_TRY(&ctx->last_error, hipMemsetAsync(ctx->ws + ctx->wso.err, 0, 4, ctx->stream));
+  ctx->pos = 0;
+  ctx->bad_state = false;
+  ctx->last_error.clear();
+  return KIE_OK;
+}
+
+kie_status kie_set_position(kie_ctx* ctx, int32_t pos) {
+  if (!ctx) return KIE_ERR_INVALID_ARG;
+  if (pos < 0 || pos > ctx->pos) {
+    set_err(&ctx->last_error, "position %d outside [0, %d]", pos, ctx->pos);
+    return KIE_ERR_INVALID_ARG;
+  }
+  ctx->pos = pos;
+  return KIE_OK;
+}
+
+kie_status kie_sync(kie_ctx* ctx) {
+  if (!ctx) return KIE_ERR_INVALID_ARG;
+  HIP_TRY(&ctx->last_error, hipSetDevice(ctx->device));
+  HIP_TRY(&ctx->last_error, hipStreamSynchronize(ctx->stream));
+  uint32_t errw = 0;
+  HIP_TRY(&ctx->last_error, hipMemcpy(&errw, ctx->ws + ctx->wso.err, 4, hipMemcpyDeviceToHost));
+  if (errw & (KERR_PRODUCER | KERR_CONSUMER)) {
+    ctx->bad_state = true;
+    set_err(&ctx->last_error, "device wait timed out (error word 0x%x)", errw);
+    return KIE_ERR_TIMEOUT;
+  }
+  if (errw & KERR_BAD_TOKEN) {
+    ctx->bad_state = true;
+    set_err(&ctx->last_error, "an input token id was out of range (replaced by 0)");
+    return KIE_ERR_ABORTED;
+  }
+  return KIE_OK;
+}
+
+static kie_status launch(kie_ctx* ctx, const int32_t* first, int32_t n, const int32_t* forced, int32_t* toks_out,
+                         int32_t* last_tok, float* logits, int lm_last_only, const kie_sampling* smp) {
+  if (ctx->bad_state) {
+    set_err(&ctx->last_error, "context holds a device error; call kie_reset");
+    return KIE_ERR_STATE;
+  }
+  if (!first || n <= 0) {
+    set_err(&ctx->last_error, "first token pointer is NULL or n <= 0");
+    return KIE_ERR_INVALID_ARG;
+  }
+  if (smp && smp->top_k > 1) {
+    set_err(&ctx->last_error, "top-k sampling is not available in this build (use top_k <= 1)");
+    return KIE_ERR_UNSUPPORTED;
+  }
+  if ((int64_t)ctx->pos + n > ctx->s.max_seq) {
+    set_err(&ctx->last_error, "position %d + %d tokens exceeds max_seq_len %d", ctx->pos, n, ctx->s.max_seq);
+    return KIE_ERR_CAPACITY;
+  }
+  HIP_TRY(&ctx->last_error, hipSetDevice(ctx->device));
+  KParams P;
+  P.s = ctx->s;
+  P.exo = ctx->exo;
+  P.packed = ctx->packed;
+  P.embed = (const uint16_t*)(ctx->packed + packed_embed_offset(ctx->s));
+  P.norms = (const uint16_t*)(ctx->ws + ctx->wso.norms);
+  P.kv = ctx->kv;
+  P.ex = (uint64_t*)(ctx->ws + ctx->wso.exch);
+  P.rope = (const float2*)(ctx->ws + ctx->wso.rope);
+  P.wbase = (const int64_t*)(ctx->ws + ctx->wso.wbase);
+  P.err = (uint32_t*)(ctx->ws + ctx->wso.err);
+  P.first_tok = first;
+  P.forced = forced;
+  P.tokens_out = toks_out;
+  P.last_tok_out = last_tok;
+  P.logits_out = logits;
+  P.pos0 = ctx->pos;
+  P.n_steps = n;
+  P.epoch0 = ctx->epoch;
+  P.lm_last_only = lm_last_only;
+  P.ring_slots = ctx->ring;
+  P.timeout_ticks = ctx->timeout_ticks;
+  void* args[] = {&P};
+  HIP_TRY(&ctx->last_error, hipLaunchCooperativeKernel((const void*)ctx->kernel, dim3(ctx->s.nwg), dim3(kThreads), args,
+                                                       (unsigned)ctx->lds, ctx->stream));
+  ctx->pos += n;
+  ctx->epoch += (uint32_t)n;
+  if (ctx->epoch == 0) ctx->epoch = 1;
+  return KIE_OK;
+}
+
+kie_status kie_prefill(kie_ctx* ctx, const int32_t* tokens_dev, int32_t n_tokens, int32_t* first_token_dev,
+                       float* last_logits_dev, const kie_sampling* sampling) {
+  if (!ctx) return KIE_ERR_INVALID_ARG;
+  if (!tokens_dev || !first_token_dev || n_tokens <= 0) {
+    set_err(&ctx->last_error, "prefill needs tokens, an output token and n_tokens > 0");
+    return KIE_ERR_INVALID_ARG;
+  }
+  return launch(ctx, tokens_dev, n_tokens, n_tokens > 1 ? tokens_dev + 1 : nullptr, nullptr, first_token_dev,
+                last_logits_dev, 1, sampling);
+}
+
+kie_status kie_decode_step(kie_ctx* ctx, const int32_t* token_in_dev, const kie_sampling* sampling,
+                           int32_t* token_out_dev, float* logits_dev) {
+  if (!ctx) return KIE_ERR_INVALID_ARG;
+  if (!token_out_dev) {
+    set_err(&ctx->last_error, "token_out_dev is NULL");
+    return KIE_ERR_INVALID_ARG;
+  }
+  return launch(ctx, token_in_dev, 1, nullptr, token_out_dev, nullptr, logits_dev, 0, sampling);
+}
+
+kie_status kie_generate(kie_ctx* ctx, const int32_t* first_token_dev, int32_t n_steps, const kie_sampling* sampling,
+                        const int32_t* forced_dev, int32_t* tokens_out_dev, float* logits_dev) {
+  if (!ctx) return KIE_ERR_INVALID_ARG;
+  if (!tokens_out_dev) {
+    set_err(&ctx->last_error, "tokens_out_dev is NULL");
+    return KIE_ERR_INVALID_ARG;
+  }
+  return launch(ctx, first_token_dev, n_steps, forced_dev, tokens_out_dev, nullptr, logits_dev, 0, sampling);
+}
+
+// ------------------------------------------------------------------ measurement helpers
+kie_status kie_stream_copy(void* dst, const void* src, size_t bytes, void* hip_stream) {
+  if (!dst || !src || bytes % 16 || !aligned16(dst) || !aligned16(src)) return KIE_ERR_INVALID_ARG;
+  int n = 0;
+  if (query_cus(&n, nullptr) != KIE_OK) return KIE_ERR_HIP;
+  return launch_stream_copy(dst, src, (int64_t)bytes, n, (hipStream_t)hip_stream) == hipSuccess ? KIE_OK : KIE_ERR_HIP;
+}
+
+kie_status kie_stream_read(const void* src, size_t bytes, uint32_t* sink_dev, void* hip_stream) {
+  if (!src || !sink_dev || bytes % 16 || !aligned16(src)) return KIE_ERR_INVALID_ARG;
+  int n = 0;
+  if (query_cus(&n, nullptr) != KIE_OK) return KIE_ERR_HIP;
+  return launch_stream_read(src, (int64_t)bytes, sink_dev, n, (hipStream_t)hip_stream) == hipSuccess ? KIE_OK
+                                                                                                       : KIE_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,218 @@
+// layout.h -- where every weight byte and every exchange word lives (host and device).
+//
+// Decoding one token at batch 1 streams every active weight once (agentlenshq.com,
+// 《突破内存墙：在标准 GPU 上实现 3,000 tokens/s 的推理速度》, "瓶颈：是内存带宽，而非计算"). The packer
+// therefore lays the weights out in exactly the order each workgroup (one per compute unit) will
+// consume them within one token, so that every CU streams one contiguous slice with 16-byte
+// lane loads, and the kernel's producer waves can run ahead of the data dependencies.
+//
+// Vocabulary
+//   WG       one persistent workgroup per compute unit; WG w runs on XCD (w mod 8).
+//   pair     two weight rows whose dot products one wave computes together: lanes 0..31 take
+//            row A, lanes 32..63 row B (RoPE partners, gate/up partners, or neighbours).
+//   tile     1 KiB = 64 lanes x 16 B: 256 consecutive k of row A followed by the same 256 k of
+//            row B. K (the row length) is a multiple of 256.
+//   stage    one weight matrix group of a layer: QKV, O, GU (gate+up) or DN (down), plus LM.
+//   round    up to NCW pairs, one per consumer wave, whose tiles are interleaved j-major so that
+//            the consumer waves eat the ring in stream order.
+#pragma once
+#include <stdint.h>
+
+#ifdef __HIPCC__
+#define KIE_HD __host__ __device__ __forceinline__
+#else
+#define KIE_HD inline
+#endif
+
+namespace kie {
+
+constexpr int kWave = 64;
+constexpr int kProducerWaves = 4;
+constexpr int kConsumerWaves = 4;
+constexpr int kThreads = (kProducerWaves + kConsumerWaves) * kWave;  // 512
+constexpr int kConsumerThreads = kConsumerWaves * kWave;             // 256
+constexpr int kTileBytes = 1024;
+constexpr int kTileK = 256;  // k per tile and row
+constexpr int kMaxWG = 1024;
+
+enum Stage : int { ST_QKV = 0, ST_O = 1, ST_GU = 2, ST_DN = 3, ST_LM = 4, ST_COUNT = 5 };
+
+struct Shape {
+  int32_t L, d, nq, nkv, hd, F, V, max_seq;
+  float eps, theta;
+  int32_t nwg;
+  KIE_HD int32_t qdim() const { return nq * hd; }
+  KIE_HD int32_t kvdim() const { return nkv * hd; }
+  KIE_HD int32_t group() const { return nq / nkv; }
+  // pairs and row length (K) of each stage
+  KIE_HD int32_t stage_pairs(int st) const {
+    switch (st) {
+      case ST_QKV: return (nq + 2 * nkv) * (hd / 2);
+      case ST_O: return d / 2;
+      case ST_GU: return F;
+      case ST_DN: return d / 2;
+      default: return V / 2;
+    }
+  }
+  KIE_HD int32_t stage_k(int st) const {
+    switch (st) {
+      case ST_O: return qdim();
+      case ST_DN: return F;
+      default: return d;
+    }
+  }
+  KIE_HD int32_t stage_kt(int st) const { return stage_k(st) / kTileK; }
+};
+
+// Even split of n items over nwg workgroups: WG w owns [begin, end).
+KIE_HD int32_t split_begin(int64_t n, int32_t nwg, int32_t w) { return (int32_t)((n * w) / nwg); }
+KIE_HD int32_t split_end(int64_t n, int32_t nwg, int32_t w) { return (int32_t)((n * (w + 1)) / nwg); }
+
+// Tiles of a stage for a WG owning `np` pairs of row length kt tiles.
+KIE_HD int64_t stage_tiles(int32_t np, int32_t kt) { return (int64_t)np * kt; }
+
+// Stream index (within the stage) of tile j of local pair lp.
+KIE_HD int32_t tile_index(int32_t np, int32_t kt, int32_t lp, int32_t j) {
+  const int32_t r = lp / kConsumerWaves, c = lp % kConsumerWaves;
+  const int32_t full = np / kConsumerWaves;
+  const int32_t nr = r < full ? kConsumerWaves : np - full * kConsumerWaves;
+  return r * kConsumerWaves * kt + j * nr + c;
+}
+
+// Inverse of tile_index: local pair and k-tile of stage tile t.
+KIE_HD void tile_source(int32_t np, int32_t kt, int32_t t, int32_t* lp, int32_t* j) {
+  const int32_t full = np / kConsumerWaves;
+  const int32_t per_round = kConsumerWaves * kt;
+  const int32_t r = t / per_round;
+  if (r < full) {
+    const int32_t q = t - r * per_round;
+    *j = q / kConsumerWaves;
+    *lp = r * kConsumerWaves + q % kConsumerWaves;
+  } else {
+    const int32_t rem = np - full * kConsumerWaves;
+    const int32_t q = t - full * per_round;
+    *j = q / rem;
+    *lp = full * kConsumerWaves + q % rem;
+  }
+}
+
+// Tiles per layer owned by WG w (QKV, O, GU, DN in stream order), and of the LM head.
+KIE_HD int64_t wg_layer_tiles(const Shape& s, int32_t w) {
+  int64_t t = 0;
+  for (int st = ST_QKV; st <= ST_DN; ++st) {
+    const int32_t n = s.stage_pairs(st);
+    t += stage_tiles(split_end(n, s.nwg, w) - split_begin(n, s.nwg, w), s.stage_kt(st));
+  }
+  return t;
+}
+KIE_HD int64_t wg_lm_tiles(const Shape& s, int32_t w) {
+  const int32_t n = s.stage_pairs(ST_LM);
+  return stage_tiles(split_end(n, s.nwg, w) - split_begin(n, s.nwg, w), s.stage_kt(ST_LM));
+}
+KIE_HD int64_t wg_token_tiles(const Shape& s, int32_t w) { return s.L * wg_layer_tiles(s, w) + wg_lm_tiles(s, w); }
+
+// Source rows of global pair gp of a stage. mat selects the matrix: for QKV 0 = Wq, 1 = Wk, 2 = Wv.
+KIE_HD void pair_rows(const Shape& s, int st, int32_t gp, int* mat, int32_t* ra, int32_t* rb) {
+  if (st == ST_QKV) {
+    const int32_t half = s.hd / 2;
+    const int32_t hs = gp / half, i = gp % half;
+    int32_t h = hs;
+    if (hs < s.nq) {
+      *mat = 0;
+    } else if (hs < s.nq + s.nkv) {
+      *mat = 1;
+      h = hs - s.nq;
+    } else {
+      *mat = 2;
+      h = hs - s.nq - s.nkv;
+    }
+    *ra = h * s.hd + i;
+    *rb = h * s.hd + i + half;
+  } else if (st == ST_GU) {
+    *mat = 0;  // row gp of W_gate (A) and of W_up (B)
+    *ra = gp;
+    *rb = gp;
+  } else {
+    *mat = 0;
+    *ra = 2 * gp;
+    *rb = 2 * gp + 1;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Attention split: WG w handles KV head (w mod nkv) over position chunk (w / nkv).
+// ---------------------------------------------------------------------------------------------
+KIE_HD int32_t att_chunks(const Shape& s) { return s.nwg / s.nkv; }
+KIE_HD int32_t att_pos_per_tile(const Shape& s) { return kTileBytes / (s.hd * 2); }
+// chunk length (positions) for a context of n positions; a multiple of the positions per tile
+KIE_HD int32_t att_chunk_len(const Shape& s, int32_t n) {
+  const int32_t nc = att_chunks(s), ppt = att_pos_per_tile(s);
+  int32_t cs = (n + nc - 1) / nc;
+  cs = ((cs + ppt - 1) / ppt) * ppt;
+  return cs < ppt ? ppt : cs;
+}
+// merge units: (query head, slice of 32 dims)
+constexpr int kMergeDims = 32;
+KIE_HD int32_t merge_units(const Shape& s) { return s.nq * (s.hd / kMergeDims); }
+KIE_HD int32_t merge_unit_wg(const Shape& s, int32_t u) { return (int32_t)(((int64_t)u * s.nwg) / merge_units(s)); }
+
+// ---------------------------------------------------------------------------------------------
+// Exchange buffers (64-bit tagged words: value bits << 32 | epoch), per layer, in the workspace.
+// ---------------------------------------------------------------------------------------------
+struct Exch {
+  int64_t xf, xa, q, k, v, part, o, h, lm, end;  // word offsets
+  int32_t part_words;                             // per WG per layer
+};
+KIE_HD Exch exch_layout(const Shape& s) {
+  Exch e;
+  const int32_t G = s.group();
+  e.part_words = G * (s.hd + 2);
+  int64_t o = 0;
+  e.xf = o; o += (int64_t)(s.L + 1) * s.d;
+  e.xa = o; o += (int64_t)s.L * s.d;
+  e.q = o; o += (int64_t)s.L * s.qdim();
+  e.k = o; o += (int64_t)s.L * s.kvdim();
+  e.v = o; o += (int64_t)s.L * s.kvdim();
+  e.part = o; o += (int64_t)s.L * s.nwg * e.part_words;
+  e.o = o; o += (int64_t)s.L * s.qdim();
+  e.h = o; o += (int64_t)s.L * s.F;
+  e.lm = o; o += (int64_t)s.nwg * 2;
+  e.end = o;
+  return e;
+}
+
+// Workspace (bytes, 256-aligned pieces): exchange words, RoPE table [max_seq][hd/2] of (cos,sin),
+// per-WG weight-stream base (in tiles), error word, norm gains [L][2][d] + final [d] (bf16).
+struct Workspace {
+  int64_t exch, rope, wbase, err, norms, end;
+};
+KIE_HD int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+KIE_HD Workspace workspace_layout(const Shape& s) {
+  Workspace w;
+  int64_t o = 0;
+  w.exch = o; o = align256(o + exch_layout(s).end * 8);
+  w.rope = o; o = align256(o + (int64_t)s.max_seq * (s.hd / 2) * 8);
+  w.wbase = o; o = align256(o + (int64_t)(s.nwg + 1) * 8);
+  w.err = o; o = align256(o + 64);
+  w.norms = o; o = align256(o + ((int64_t)s.L * 2 + 1) * s.d * 2);
+  w.end = o;
+  return w;
+}
+
+// Packed image: for each WG its token stream (L layers x [QKV,O,GU,DN] then LM) of tiles,
+// then the embedding table [V][d] bf16 as is.
+KIE_HD int64_t packed_stream_tiles(const Shape& s) {
+  int64_t t = 0;
+  for (int32_t w = 0; w < s.nwg; ++w) t += wg_token_tiles(s, w);
+  return t;
+}
+KIE_HD int64_t packed_embed_offset(const Shape& s) { return packed_stream_tiles(s) * kTileBytes; }
+KIE_HD int64_t packed_bytes(const Shape& s) { return packed_embed_offset(s) + (int64_t)s.V * s.d * 2; }
+
+// KV cache: [L][2][nkv][max_seq][hd] bf16 (K plane, then V plane, per layer).
+KIE_HD int64_t kv_offset(const Shape& s, int32_t l, int32_t kv, int32_t j, int32_t pos) {
+  return ((((int64_t)l * 2 + kv) * s.nkv + j) * s.max_seq + pos) * s.hd;
+}
+KIE_HD int64_t kv_bytes(const Shape& s) { return (int64_t)s.L * 2 * s.nkv * s.max_seq * s.hd * 2; }
+
+}  // namespace kie

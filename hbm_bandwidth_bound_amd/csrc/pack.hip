@@ -1,0 +1,132 @@
+// pack.hip -- set-up kernels: the weight packer and the RoPE table; plus two plain streaming
+// kernels used to measure the memory system (copy and read) next to the decoder.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "device_common.h"
+#include "layout.h"
+#include "monokernel.h"
+
+namespace kie {
+
+// One block per WG; it copies the WG's tiles of one layer (or of the LM head) into the WG's
+// stream. Every 64 threads move one 1 KiB tile: thread q takes 16 B of row A (q < 32) or row B.
+__global__ void __launch_bounds__(256) pack_layer_kernel(PackArgs a) {
+  const Shape& s = a.s;
+  const int32_t w = blockIdx.x;
+  int32_t np[ST_COUNT], pb[ST_COUNT], pre[ST_COUNT];
+  int32_t acc = 0;
+  for (int st = 0; st < ST_COUNT; ++st) {
+    const int32_t n = s.stage_pairs(st);
+    pb[st] = split_begin(n, s.nwg, w);
+    np[st] = split_end(n, s.nwg, w) - pb[st];
+    if (st <= ST_DN) {
+      pre[st] = acc;
+      acc += np[st] * s.stage_kt(st);
+    } else {
+      pre[st] = 0;
+    }
+  }
+  const int32_t t_layer = acc;
+  const bool lm = a.layer == s.L;
+  const int64_t base = a.wbase[w] + (int64_t)a.layer * t_layer;
+  const int32_t ntiles = lm ? np[ST_LM] * s.stage_kt(ST_LM) : t_layer;
+  const int q = threadIdx.x % 64;
+  for (int32_t t = blockIdx.y * 4 + threadIdx.x / 64; t < ntiles; t += gridDim.y * 4) {
+    int st = ST_LM;
+    int32_t tt = t;
+    if (!lm) {
+      st = ST_QKV;
+      while (st < ST_DN && tt >= pre[st + 1]) ++st;
+      tt = t - pre[st];
+    }
+    const int32_t kt = s.stage_kt(st), K = s.stage_k(st);
+    int32_t lp, j;
+    tile_source(np[st], kt, tt, &lp, &j);
+    int mat;
+    int32_t ra, rb;
+    pair_rows(s, st, pb[st] + lp, &mat, &ra, &rb);
+    const bool half_b = q >= 32;
+    const uint16_t* m;
+    if (st == ST_QKV)
+      m = mat == 0 ? a.wq : (mat == 1 ? a.wk : a.wv);
+    else if (st == ST_O)
+      m = a.wo;
+    else if (st == ST_GU)
+      m = half_b ? a.wup : a.wgate;
+    else if (st == ST_DN)
+      m = a.wdown;
+    else
+      m = a.lm_head;
+    const int32_t row = half_b ? rb : ra;
+    const int32_t k = j * kTileK + (q % 32) * 8;
+    const v4u v = *(const v4u*)(m + (int64_t)row * K + k);
+    *(v4u*)(a.packed + (base + t) * kTileBytes + q * 16) = v;
+  }
+}
+
+hipError_t launch_pack_layer(const PackArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(pack_layer_kernel, dim3(a.s.nwg, 16), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// rope[p][i] = (cos, sin) of p * theta^(-2i/hd), angle in fp64, rounded to fp32
+__global__ void rope_table_kernel(float2* rope, int32_t max_seq, int32_t hd, float theta) {
+  const int32_t half = hd / 2;
+  const int64_t n = (int64_t)max_seq * half;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
+    const int32_t p = (int32_t)(e / half), i = (int32_t)(e % half);
+    const double freq = pow((double)theta, -2.0 * (double)i / (double)hd);
+    const double phi = (double)p * freq;
+    rope[e] = make_float2((float)cos(phi), (float)sin(phi));
+  }
+}
+
+hipError_t launch_rope_table(float2* rope, int32_t max_seq, int32_t hd, float theta, hipStream_t st) {
+  hipLaunchKernelGGL(rope_table_kernel, dim3(1024), dim3(256), 0, st, rope, max_seq, hd, theta);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ memory-system probes
+// Plain copy of n16 16-byte words, one contiguous slice per block (the calibration kernel for the
+// hardware traffic counters: it reads and writes exactly 16 * n16 bytes each).
+__global__ void __launch_bounds__(512) stream_copy_kernel(v4u* __restrict__ dst, const v4u* __restrict__ src, int64_t n16) {
+  const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t b = per * blockIdx.x;
+  const int64_t e = b + per < n16 ? b + per : n16;
+  for (int64_t i = b + threadIdx.x; i < e; i += blockDim.x) dst[i] = __builtin_nontemporal_load(src + i);
+}
+
+// Read-only stream: the ceiling a weight-streaming kernel can reach (one slice per block, 8 loads
+// in flight per thread).
+__global__ void __launch_bounds__(512) stream_read_kernel(const v4u* __restrict__ src, int64_t n16, uint32_t* sink) {
+  const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t b = per * blockIdx.x;
+  const int64_t e = b + per < n16 ? b + per : n16;
+  uint32_t acc = 0;
+  int64_t i = b + threadIdx.x;
+  for (; i + 7 * 512 < e; i += 8 * 512) {
+    v4u v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(src + i + u * 512);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < e; i += 512) {
+    const v4u v = src[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9e3779b9u) sink[0] = acc;  // keeps the loads; practically never taken
+}
+
+hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes, int32_t blocks, hipStream_t st) {
+  hipLaunchKernelGGL(stream_copy_kernel, dim3(blocks), dim3(512), 0, st, (v4u*)dst, (const v4u*)src, bytes / 16);
+  return hipGetLastError();
+}
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t blocks, hipStream_t st) {
+  hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(512), 0, st, (const v4u*)src, bytes / 16, sink);
+  return hipGetLastError();
+}
+
+}  // namespace kie

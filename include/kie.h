@@ -1,0 +1,161 @@
+/*
+ * kie.h -- C ABI of the batch-1 decode engine for one AMD MI355X (gfx950).
+ *
+ * What the engine computes. Batch-1 autoregressive decoding of a dense decoder-only transformer,
+ * one token at a time, each token depending on the previous one (agentlenshq.com,
+ * 《突破内存墙：在标准 GPU 上实现 3,000 tokens/s 的推理速度》, opening section; aikraft.ru
+ * «3000 токенов в секунду: как ускорить LLM на обычных GPU», §01). Every active weight is read
+ * from HBM once per generated token (same pages: "瓶颈：是内存带宽，而非计算" and §02), and the
+ * whole decode path -- MatMul, attention, normalisation and sampling -- runs inside one
+ * GPU-resident program that does not return control to the host between tokens ("The Monokernel
+ * Runtime" section; §04 "Моноядро"), with sampling on the GPU (§04). The pages do not give the
+ * decoder's equations; the engine implements the pre-RMSNorm, RoPE (rotate-half pairs),
+ * grouped-query attention and SwiGLU decoder with bf16 weights, a bf16 KV cache, fp32
+ * activations and fp32 accumulation.
+ *
+ * Conventions for every function below
+ *   - C99 types only. bf16 values are passed as raw uint16_t bit patterns.
+ *   - "device pointer" = memory on the GPU the context was created on (e.g. a torch tensor's
+ *     data_ptr()); "host pointer" = ordinary CPU memory.
+ *   - All device memory is owned by the caller. The library never allocates device memory.
+ *   - Every call enqueues work on the context's stream and returns at once; outputs are valid
+ *     after kie_sync() or any synchronisation of that stream.
+ *   - Functions never abort and never throw. They return KIE_OK (0) or a negative status;
+ *     argument, configuration and capacity errors are found on the host, before anything is
+ *     enqueued, and leave the context unchanged. kie_last_error() gives a message.
+ */
+#ifndef KIE_H
+#define KIE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t kie_status;
+enum {
+  KIE_OK = 0,
+  KIE_ERR_INVALID_ARG = -1, /* a NULL pointer, a negative size, a token id out of range */
+  KIE_ERR_UNSUPPORTED = -2, /* a shape or device the kernels do not handle (see kie_create) */
+  KIE_ERR_CAPACITY = -3,    /* position + tokens would exceed max_seq_len */
+  KIE_ERR_HIP = -4,         /* a HIP runtime call failed */
+  KIE_ERR_STATE = -5,       /* the context holds a device error; call kie_reset() */
+  KIE_ERR_TIMEOUT = -6,     /* a device-side wait exceeded its time limit (reported by kie_sync) */
+  KIE_ERR_ABORTED = -7      /* the device run stopped early (reported by kie_sync) */
+};
+
+/* Model shape. Requirements checked by kie_create: d_model, n_heads*head_dim and ffn_dim are
+ * multiples of 256; head_dim is 64 or 128; n_heads is a multiple of n_kv_heads; vocab_size and
+ * d_model are even; the number of compute units is a multiple of n_kv_heads. The MoE fields
+ * must be 0 (dense decoder). */
+typedef struct {
+  int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab_size;
+  float rms_eps, rope_theta;
+  int32_t max_seq_len; /* KV capacity in positions: prompt + generated tokens */
+  int32_t n_experts, n_experts_active, expert_ffn_dim;
+} kie_config;
+
+/* Source weights: device pointers to row-major [out][in] bf16 matrices, borrowed only until the
+ * packing started by kie_create has finished (after the first kie_sync they may be freed).
+ * The per-layer members are HOST arrays of n_layers device pointers.
+ *   embed [V][d], final_norm [d], lm_head [V][d];
+ *   attn_norm[l] [d], wq[l] [n_heads*hd][d], wk[l] and wv[l] [n_kv_heads*hd][d],
+ *   wo[l] [d][n_heads*hd], ffn_norm[l] [d], w_gate[l] and w_up[l] [F][d], w_down[l] [d][F]. */
+typedef struct {
+  const uint16_t *embed, *final_norm, *lm_head;
+  const uint16_t *const *attn_norm, *const *wq, *const *wk, *const *wv, *const *wo;
+  const uint16_t *const *ffn_norm, *const *w_gate, *const *w_up, *const *w_down;
+} kie_weights;
+
+/* Token choice after each step, made on the GPU (aikraft.ru «3000 токенов в секунду…», §04:
+ * sampling is taken off the CPU). top_k <= 1: greedy argmax, ties to the lower id. top_k > 1:
+ * z = logits / temperature, the top_k largest z (ties to the lower id), p = softmax over them in
+ * fp64, u = (splitmix64(seed ^ splitmix64(pos)) >> 40) * 2^-24 with pos the position of the
+ * token being processed, and the first candidate whose running sum of p exceeds u. */
+typedef struct {
+  int32_t top_k;
+  float temperature;
+  uint64_t seed;
+} kie_sampling;
+
+typedef struct kie_ctx kie_ctx;
+
+/* Sizes of the three caller-owned device buffers for a configuration (0 if it is invalid). The
+ * packed-weight image holds every weight in consumption order plus the embedding table; the KV
+ * cache is [n_layers][2][n_kv_heads][max_seq_len][head_dim] bf16 (K plane then V plane); the
+ * workspace holds the inter-workgroup exchange words, the RoPE table and small tables. The GPU
+ * used is the current HIP device; the workspace size depends on its compute-unit count. */
+size_t kie_packed_weight_bytes(const kie_config* cfg);
+size_t kie_kv_cache_bytes(const kie_config* cfg);
+size_t kie_workspace_bytes(const kie_config* cfg);
+
+/* Create a context on the current HIP device and enqueue the packing of `src` into `packed`
+ * (kie_packed_weight_bytes) on `hip_stream` (a hipStream_t, or NULL for the default stream). The
+ * workspace (kie_workspace_bytes) is initialised here; kv_cache (kie_kv_cache_bytes) needs no
+ * initialisation. Position starts at 0. Errors: KIE_ERR_INVALID_ARG, KIE_ERR_UNSUPPORTED (shape,
+ * or a device that is not gfx950 / cannot co-schedule one workgroup per compute unit),
+ * KIE_ERR_HIP. On error *out is NULL. */
+kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packed, void* kv_cache,
+                      void* workspace, void* hip_stream, kie_ctx** out);
+
+/* Process a prompt of n_tokens ids (device int32 [n_tokens]) at positions pos .. pos+n_tokens-1,
+ * writing their K/V rows, then choose the next token (device int32 [1], first_token_dev) from the
+ * logits of the last prompt position; those logits are written to last_logits_dev (device fp32
+ * [V]) unless it is NULL. Advances the position by n_tokens. Errors: KIE_ERR_INVALID_ARG,
+ * KIE_ERR_CAPACITY, KIE_ERR_STATE, KIE_ERR_HIP. */
+kie_status kie_prefill(kie_ctx* ctx, const int32_t* tokens_dev, int32_t n_tokens, int32_t* first_token_dev,
+                       float* last_logits_dev, const kie_sampling* sampling);
+
+/* One decode step: process token_in_dev (device int32 [1]) at the current position, write the
+ * chosen next token to token_out_dev (device int32 [1]) and, unless NULL, the logits to
+ * logits_dev (device fp32 [V]). Identical to kie_generate with n_steps = 1. */
+kie_status kie_decode_step(kie_ctx* ctx, const int32_t* token_in_dev, const kie_sampling* sampling,
+                           int32_t* token_out_dev, float* logits_dev);
+
+/* n_steps decode steps in ONE kernel launch (the tokens never return to the host in between).
+ * Step s processes token t_s at position pos+s, where t_0 = *first_token_dev and t_s is the token
+ * chosen at step s-1, or forced_dev[s-1] when forced_dev (device int32 [n_steps-1 or more]) is
+ * given (teacher forcing; the chosen tokens are still written). tokens_out_dev (device int32
+ * [n_steps]) receives the chosen token of every step; logits_dev, unless NULL, receives the
+ * logits of every step (device fp32 [n_steps][V]). Advances the position by n_steps. The random
+ * draw of step s depends only on (seed, pos+s), so n calls of kie_decode_step produce the same
+ * tokens as one kie_generate of n steps. Errors: KIE_ERR_INVALID_ARG, KIE_ERR_CAPACITY,
+ * KIE_ERR_STATE, KIE_ERR_HIP. */
+kie_status kie_generate(kie_ctx* ctx, const int32_t* first_token_dev, int32_t n_steps, const kie_sampling* sampling,
+                        const int32_t* forced_dev, int32_t* tokens_out_dev, float* logits_dev);
+
+/* Wait for the context's stream and read the device error word. Returns KIE_OK,
+ * KIE_ERR_TIMEOUT or KIE_ERR_ABORTED (after which the context is in the error state until
+ * kie_reset), or KIE_ERR_HIP. */
+kie_status kie_sync(kie_ctx* ctx);
+
+/* Position back to 0 and any device error cleared (the KV contents are simply overwritten by
+ * later steps). */
+kie_status kie_reset(kie_ctx* ctx);
+
+/* Set the position to pos (0 <= pos <= current position): rewinds the sequence so that steps
+ * resume at pos, e.g. to re-run a suffix. KIE_ERR_INVALID_ARG otherwise. */
+kie_status kie_set_position(kie_ctx* ctx, int32_t pos);
+
+/* Current position (number of tokens whose K/V rows are in the cache), or -1 for NULL. */
+int32_t kie_position(const kie_ctx* ctx);
+
+/* Static description of a status code. */
+const char* kie_status_string(kie_status status);
+
+/* Message of the last error on this context ("" if none); for NULL, the last kie_create error. */
+const char* kie_last_error(const kie_ctx* ctx);
+
+/* Release the host-side context (no device memory is owned). NULL is accepted. */
+void kie_destroy(kie_ctx* ctx);
+
+/* Number of workgroups (= compute units) of the persistent kernel on the current device, or a
+ * negative status. */
+int32_t kie_num_workgroups(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KIE_H */

@@ -1,0 +1,35 @@
+/*
+ * kie_measure.h -- plain memory-streaming kernels exported next to the decoder.
+ *
+ * Decode speed at batch 1 is the effective memory bandwidth divided by the bytes each token must
+ * move (aikraft.ru «3000 токенов в секунду: как ускорить LLM на обычных GPU», §02; wink.run
+ * 《GPU 算力越堆越高,生成 token 为什么还是慢》). These kernels measure the first factor on the
+ * running GPU so that the decoder's achieved bandwidth can be set against what a plain stream
+ * reaches, and they calibrate hardware byte counters (a copy of N bytes reads N and writes N).
+ *
+ * Both take device pointers (16-byte aligned), a size in bytes that is a multiple of 16, and a
+ * hipStream_t (NULL = default stream). They enqueue one launch with one 512-thread workgroup per
+ * compute unit, each streaming one contiguous slice, and return KIE_OK, KIE_ERR_INVALID_ARG or
+ * KIE_ERR_HIP. Status codes are those of kie.h.
+ */
+#ifndef KIE_MEASURE_H
+#define KIE_MEASURE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* dst[0..bytes) = src[0..bytes) (the buffers must not overlap). */
+int32_t kie_stream_copy(void* dst, const void* src, size_t bytes, void* hip_stream);
+
+/* Read src[0..bytes) once; sink_dev (device uint32 [1]) is written only in a practically
+ * impossible case and exists to keep the loads. */
+int32_t kie_stream_read(const void* src, size_t bytes, uint32_t* sink_dev, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KIE_MEASURE_H */

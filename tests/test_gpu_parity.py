@@ -1,0 +1,165 @@
+"""GPU path vs the CPU oracle, through the C ABI (needs an MI355X).
+
+Comparison is teacher-forced: the GPU's own token stream is fed to the oracle, so a near-tie at
+one step cannot derail the following ones; logits are compared at every step (rel-L2 <= 1e-3)
+and greedy tokens wherever the oracle's top-2 gap exceeds 0.05.
+"""
+import numpy as np
+import pytest
+
+from hbm_bandwidth_bound_amd import synth
+from tests.gpu_util import check_steps, rel_l2, say, to_device, top2_gap
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+@pytest.fixture(scope="module")
+def tiny(torch_cuda, oracle_lib):
+    cfg = synth.TINY
+    w = synth.make_weights_np(cfg, 0)
+    return cfg, w, to_device(w)
+
+
+def run_gpu(torch, eng, prompt, n_steps, V):
+    tokens = torch.tensor(np.asarray(prompt, dtype=np.int32), device="cuda")
+    last = torch.empty(V, dtype=torch.float32, device="cuda")
+    first = eng.prefill(tokens, logits_out=last)
+    out = torch.empty(n_steps, dtype=torch.int32, device="cuda")
+    logits = torch.empty((n_steps, V), dtype=torch.float32, device="cuda")
+    eng.generate(first, n_steps, out, logits)
+    eng.sync()
+    return int(first.item()), last.cpu().numpy(), out.cpu().numpy(), logits.cpu().numpy()
+
+
+def test_tiny_prefill_then_decode(torch_cuda, tiny, oracle_lib):
+    from hbm_bandwidth_bound_amd.kie import Engine
+    cfg, w, wd = tiny
+    P, N = 64, 32
+    say(f"[tiny] prefill {P} + decode {N}")
+    eng = Engine(cfg, wd, P + N)
+    prompt = synth.prompt_ids(P, cfg.vocab_size, 1)
+    first, last, toks, logits = run_gpu(torch_cuda, eng, prompt, N, cfg.vocab_size)
+    om = oracle_lib.OracleModel(cfg, w, P + N)
+    ref_prompt = om.run(prompt)
+    e = rel_l2(last, ref_prompt[-1])
+    say(f"  prefill last-logits rel-L2 {e:.3e}")
+    assert e <= 1e-3
+    if top2_gap(ref_prompt[-1]) > 0.05:
+        assert first == int(np.argmax(ref_prompt[-1]))
+    inputs = [first] + [int(t) for t in toks[:-1]]
+    ref = om.run(inputs, start_pos=P)
+    worst, checked = check_steps(logits, ref, toks, label="tiny")
+    say(f"  decode worst rel-L2 {worst:.3e}, greedy checked on {checked}/{N} steps")
+    # the GPU's KV cache holds the same bf16 rows as the oracle's (up to rounding flips)
+    kg = eng.kv_view().cpu().numpy().view(np.uint16)
+    ko, vo = om.kv_view()
+    kf = synth.bf16_bits_to_f32(kg[:, 0, :, :P + N])
+    vf = synth.bf16_bits_to_f32(kg[:, 1, :, :P + N])
+    assert rel_l2(kf, synth.bf16_bits_to_f32(ko[:, :, :P + N])) <= 1e-3
+    assert rel_l2(vf, synth.bf16_bits_to_f32(vo[:, :, :P + N])) <= 1e-3
+    eng.close()
+
+
+def test_tiny_deterministic_and_step_equals_generate(torch_cuda, tiny):
+    """Two runs are bitwise identical, and n single-step launches equal one n-step launch."""
+    import torch
+    from hbm_bandwidth_bound_amd.kie import Engine
+    cfg, w, wd = tiny
+    P, N = 40, 12
+    say(f"[tiny] determinism prefill {P} + decode {N}")
+    prompt = synth.prompt_ids(P, cfg.vocab_size, 11)
+    eng = Engine(cfg, wd, P + N)
+    a = run_gpu(torch, eng, prompt, N, cfg.vocab_size)
+    eng.reset()
+    b = run_gpu(torch, eng, prompt, N, cfg.vocab_size)
+    assert a[0] == b[0] and np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2]) and np.array_equal(a[3], b[3])
+    # step-by-step
+    eng.reset()
+    tokens = torch.tensor(prompt, dtype=torch.int32, device="cuda")
+    tok = eng.prefill(tokens)
+    toks, logits = [], []
+    for s in range(N):
+        o = torch.empty(1, dtype=torch.int32, device="cuda")
+        lg = torch.empty(cfg.vocab_size, dtype=torch.float32, device="cuda")
+        eng.decode_step(tok, o, lg)
+        toks.append(o)
+        logits.append(lg)
+        tok = o
+    eng.sync()
+    assert np.array_equal(np.array([int(t.item()) for t in toks]), a[2])
+    assert np.array_equal(np.stack([l.cpu().numpy() for l in logits]), a[3])
+    eng.close()
+
+
+@pytest.mark.parametrize("P,N", [(1, 6), (333, 9), (1000, 8)])
+def test_tiny_context_lengths(torch_cuda, tiny, oracle_lib, P, N):
+    """Contexts that leave most attention chunks empty (P=1), ragged (333) and long (1000)."""
+    from hbm_bandwidth_bound_amd.kie import Engine
+    cfg, w, wd = tiny
+    say(f"[tiny] context P={P} N={N}")
+    prompt = synth.prompt_ids(P, cfg.vocab_size, 100 + P)
+    eng = Engine(cfg, wd, P + N)
+    first, last, toks, logits = run_gpu(torch_cuda, eng, prompt, N, cfg.vocab_size)
+    om = oracle_lib.OracleModel(cfg, w, P + N)
+    ref_prompt = om.run(prompt)
+    assert rel_l2(last, ref_prompt[-1]) <= 1e-3
+    ref = om.run([first] + [int(t) for t in toks[:-1]], start_pos=P)
+    worst, checked = check_steps(logits, ref, toks, label=f"tiny P={P}")
+    say(f"  worst rel-L2 {worst:.3e}, greedy checked {checked}/{N}")
+    eng.close()
+
+
+def test_forced_tokens_follow_the_given_stream(torch_cuda, tiny, oracle_lib):
+    """Teacher forcing: the step inputs are the forced ids; the chosen tokens are still written."""
+    import torch
+    from hbm_bandwidth_bound_amd.kie import Engine
+    cfg, w, wd = tiny
+    P, N = 20, 10
+    say("[tiny] forced tokens")
+    prompt = synth.prompt_ids(P, cfg.vocab_size, 5)
+    forced = synth.prompt_ids(N, cfg.vocab_size, 6)
+    eng = Engine(cfg, wd, P + N)
+    first = eng.prefill(torch.tensor(prompt, dtype=torch.int32, device="cuda"))
+    out = torch.empty(N, dtype=torch.int32, device="cuda")
+    logits = torch.empty((N, cfg.vocab_size), dtype=torch.float32, device="cuda")
+    f = torch.tensor(forced, dtype=torch.int32, device="cuda")
+    eng.generate(first, N, out, logits, forced=f)
+    eng.sync()
+    om = oracle_lib.OracleModel(cfg, w, P + N)
+    om.run(prompt)
+    ref = om.run([int(first.item())] + [int(t) for t in forced[:N - 1]], start_pos=P)
+    check_steps(logits.cpu().numpy(), ref, out.cpu().numpy(), label="forced")
+    eng.close()
+
+
+def test_capacity_and_bad_token_errors(torch_cuda, tiny):
+    import torch
+    from hbm_bandwidth_bound_amd.kie import Engine, KieError
+    cfg, w, wd = tiny
+    say("[tiny] error paths")
+    eng = Engine(cfg, wd, 8)
+    toks = torch.zeros(9, dtype=torch.int32, device="cuda")
+    with pytest.raises(KieError) as ei:
+        eng.prefill(toks)
+    assert ei.value.status == -3 and eng.position == 0
+    # an out-of-range id is replaced by 0 on the device and reported by sync
+    bad = torch.tensor([cfg.vocab_size + 5], dtype=torch.int32, device="cuda")
+    eng.prefill(bad)
+    with pytest.raises(KieError) as ei:
+        eng.sync()
+    assert ei.value.status == -7
+    with pytest.raises(KieError) as ei:
+        eng.prefill(torch.zeros(2, dtype=torch.int32, device="cuda"))
+    assert ei.value.status == -5
+    eng.reset()
+    eng.prefill(torch.zeros(2, dtype=torch.int32, device="cuda"))
+    eng.sync()
+    eng.close()
