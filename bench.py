@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Batch-1 decode benchmark: tokens/s and achieved HBM bandwidth of the decode monokernel.
+
+Default workload: the ~1.6B dense decoder (24 layers, d 2048, 16/8 heads, hd 128, FFN 8192,
+vocab 32768, bf16 weights and KV) with a 1024-token random-id prompt; a "step" is one decoded
+token (one pass of the whole decode path). The K timed steps run as ONE kie_generate launch
+starting at position 1024 (after the untimed prompt pass and W untimed warm-up tokens, the
+position is rewound to 1024 so the timed tokens sit at positions 1024..1024+K-1).
+
+Prints one JSON line. `roofline.achieved` is the algorithmic bytes of the timed launch divided
+by that launch's duration (HIP events on the launch stream); `cpu_baseline` times the CPU oracle
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X published HBM3E bandwidth
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=512)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default="1.6b-1k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--single-step-launches", type=int, default=32,
+                    help="also time this many one-token launches (launch-overhead comparison); 0 = skip")
+    return ap.parse_args()
+
+
+def source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "hbm_bandwidth_bound_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
+    current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_decode_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            m = re.match(r"^\s*([a-z_]+)\s*=\s*(\S+)", line)
+            if m:
+                kv[m.group(1)] = m.group(2)
+    if kv.get("source_sha") != source_hash():
+        return None
+    try:
+        return {"bytes_per_step": float(kv["hbm_bytes_per_step"]), "steps_per_launch": int(kv["steps_per_launch"])}
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(model, weights_dev, prompt_len: int, target_s: float):
+    """Oracle decode steps of the same model at the same context length. The oracle's KV cache
+    is filled with seeded synthetic bf16 rows for positions < prompt_len (the cost of a step does
+    not depend on their values), then whole decode steps are timed."""
+    import numpy as np
+
+    import oracle
+    from hbm_bandwidth_bound_amd import synth
+    try:
+        ncores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncores = os.cpu_count() or 1
+    threads = max(1, min(16, ncores))
+    oracle.build(force=False)
+    oracle.set_threads(threads)
+    w_np = synth.weights_torch_to_np(weights_dev)
+    om = oracle.OracleModel(model, w_np, prompt_len + 64)
+    k, v = om.kv_view()
+    rows = synth._weights_bits_np((model.n_layers * model.n_kv_heads * prompt_len, model.head_dim), 7, 999)
+    rows = rows.reshape(model.n_layers, model.n_kv_heads, prompt_len, model.head_dim)
+    k[:, :, :prompt_len] = rows
+    v[:, :, :prompt_len] = rows[:, :, ::-1]
+    tok = int(synth.prompt_ids(1, model.vocab_size, 1)[0])
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        logits = om.step(tok, prompt_len + n)
+        tok = oracle.argmax(logits)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or n >= 64:
+            break
+    return {"value": n / el, "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} oracle decode steps of the {model.name} model at positions {prompt_len}.."
+                      f"{prompt_len + n - 1} (KV rows < {prompt_len} seeded synthetic), {el:.1f} s, "
+                      f"{threads} threads row-parallel"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this decode path has no multi-GPU "
+              "mode; see the sharding notes in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from hbm_bandwidth_bound_amd import synth, traffic
+    from hbm_bandwidth_bound_amd.kie import Engine, stream_read
+
+    wl = synth.WORKLOADS[args.workload]
+    m = wl.model
+    K, W = int(args.steps), int(args.warmup)
+    P = wl.prompt_len
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream(dev)
+    print(f"[bench] generating {m.name} weights on the GPU", file=sys.stderr, flush=True)
+    wdev = synth.make_weights_torch(m, wl.weight_seed, device=dev)
+    torch.cuda.synchronize()
+    eng = Engine(m, wdev, P + max(K, W))
+    prompt = torch.tensor(synth.prompt_ids(P, m.vocab_size, wl.prompt_seed), dtype=torch.int32, device=dev)
+
+    # prompt pass (untimed for the metric; its time is reported as TTFT)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    print(f"[bench] prompt pass of {P} tokens", file=sys.stderr, flush=True)
+    e0.record(stream)
+    first = eng.prefill(prompt)
+    e1.record(stream)
+    eng.sync()
+    ttft_ms = e0.elapsed_time(e1)
+
+    out = torch.empty(max(K, W), dtype=torch.int32, device=dev)
+    if W > 0:
+        print(f"[bench] warm-up {W} tokens", file=sys.stderr, flush=True)
+        eng.generate(first, W, out)
+        eng.sync()
+        eng.set_position(P)
+    print(f"[bench] timed: {K} tokens in one launch", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    eng.generate(first, K, out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    eng.sync()
+    launch_ms = e0.elapsed_time(e1)
+    wall_s = t1 - t0
+    tok_s = K / wall_s
+    algo_bytes = traffic.launch_bytes(m, P, K)
+    achieved_gbps = algo_bytes / (launch_ms * 1e-3) / 1e9
+
+    # one-token launches (the per-launch overhead comparison)
+    single = None
+    if args.single_step_launches > 0:
+        n1 = min(args.single_step_launches, K)
+        eng.set_position(P)
+        tok_in = first.clone()
+        o = torch.empty(1, dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n1):
+            eng.decode_step(tok_in, o)
+            tok_in, o = o, tok_in
+        e1.record(stream)
+        torch.cuda.synchronize()
+        eng.sync()
+        single = {"tokens": n1, "tok_s": n1 / (e0.elapsed_time(e1) * 1e-3)}
+
+    # streaming-read ceiling of this GPU (plain kernel, 4 GiB)
+    nb = 4 << 30
+    buf = torch.empty(nb, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream_read(buf, nb, sink, stream)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(3):
+        stream_read(buf, nb, sink, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ceiling_gbps = 3 * nb / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf
+
+    tr = read_traffic(args.workload)
+    traffic_bytes = None
+    if tr is not None:
+        traffic_bytes = tr["bytes_per_step"] * K
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(m, wdev, P, args.cpu_seconds)
+
+    res = {
+        "metric": "batch-1 decode tok/s, 1.6B bf16 @1k ctx; achieved HBM GB/s vs peak",
+        "value": round(tok_s, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(wall_s * 1e3 / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "prompt_len": P, "decode_positions": [P, P + K - 1],
+                   "sampling": "greedy", "weights": "bf16, counter-based N(0,0.02) approx., seed 0",
+                   "kv_cache": "bf16", "accumulate": "f32", "launches_per_timed_region": 1},
+        "roofline": {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic_bytes},
+        "cpu_baseline": cpu,
+        "extra": {"kernel_ms": round(launch_ms, 3), "algorithmic_bytes": algo_bytes,
+                  "bytes_per_token": algo_bytes / K, "stream_read_ceiling_GBps": round(ceiling_gbps, 1),
+                  "frac_of_stream_ceiling": round(achieved_gbps / ceiling_gbps, 4),
+                  "ttft_ms_prompt_pass": round(ttft_ms, 2), "one_token_launches": single,
+                  "source_sha": source_hash()},
+    }
+    print(json.dumps(res), flush=True)
+    eng.close()
+
+
+if __name__ == "__main__":
+    main()

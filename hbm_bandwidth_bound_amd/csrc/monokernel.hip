@@ -45,21 +45,21 @@ struct Lds {
 };
 enum Ctl : int { C_BAR = 0, C_STEP = 1, C_ABORT = 2, C_PDONE = 3, C_COUNT = 16 };
 
-__host__ __device__ inline int32_t act_floats(const Shape& s) {
+__host__ __device__ __forceinline__ int32_t act_floats(const Shape& s) {
   int32_t a = s.d;
   if (s.qdim() > a) a = s.qdim();
   if (s.F > a) a = s.F;
   if ((s.group() + 2) * s.hd > a) a = (s.group() + 2) * s.hd;
   return a;
 }
-__host__ __device__ inline int32_t scr_floats(const Shape& s) {
+__host__ __device__ __forceinline__ int32_t scr_floats(const Shape& s) {
   int32_t a = kConsumerWaves * s.group() * (s.hd + 2);
   if (8 * kMergeDims * 3 > a) a = 8 * kMergeDims * 3;
   if (2 * s.nwg > a) a = 2 * s.nwg;
   if (a < 64) a = 64;
   return a;
 }
-__host__ __device__ inline int32_t lds_fixed_bytes(const Shape& s) {
+__host__ __device__ __forceinline__ int32_t lds_fixed_bytes(const Shape& s) {
   return (act_floats(s) + s.d + scr_floats(s)) * 4 + C_COUNT * 4;
 }
 int32_t lds_bytes_for(const Shape& s, int32_t ring) { return ring * (kTileBytes + 8) + lds_fixed_bytes(s); }
@@ -70,7 +70,7 @@ int32_t max_ring_slots(const Shape& s, int32_t lds_limit) {
   return r;
 }
 
-__device__ inline Lds lds_map(uint8_t* smem, const Shape& s, int32_t R) {
+__device__ __forceinline__ Lds lds_map(uint8_t* smem, const Shape& s, int32_t R) {
   Lds L;
   uint8_t* p = smem;
   L.ring = p; p += (size_t)R * kTileBytes;
@@ -96,7 +96,7 @@ struct Plan {
   int64_t wbase;         // first tile of this WG in the packed image
 };
 
-__device__ inline Plan make_plan(const KParams& P, int32_t w) {
+__device__ __forceinline__ Plan make_plan(const KParams& P, int32_t w) {
   Plan pl;
   pl.w = w;
   int32_t acc = 0;
@@ -121,7 +121,7 @@ __device__ inline Plan make_plan(const KParams& P, int32_t w) {
 struct Att {
   int32_t j, chunk, c0, c1, ncache, nkt, has_p, cs, nch;
 };
-__device__ inline Att att_info(const Shape& s, int32_t w, int32_t pos) {
+__device__ __forceinline__ Att att_info(const Shape& s, int32_t w, int32_t pos) {
   Att a;
   const int32_t n = pos + 1;
   a.j = w % s.nkv;
@@ -152,10 +152,10 @@ struct Seg {
   int32_t kind, len, layer;
   int64_t wofs;  // weights: tile offset inside this WG's token stream
 };
-__device__ inline bool step_has_lm(const KParams& P, int32_t step) {
+__device__ __forceinline__ bool step_has_lm(const KParams& P, int32_t step) {
   return !P.lm_last_only || step == P.n_steps - 1;
 }
-__device__ inline Seg seg_info(const KParams& P, const Plan& pl, const Att& at, int32_t step, int32_t seg) {
+__device__ __forceinline__ Seg seg_info(const KParams& P, const Plan& pl, const Att& at, int32_t step, int32_t seg) {
   Seg g;
   const int32_t L = P.s.L;
   if (seg == 5 * L) {
@@ -183,18 +183,18 @@ __device__ inline Seg seg_info(const KParams& P, const Plan& pl, const Att& at, 
 // ------------------------------------------------------------------------------------------
 // Failure handling: every wait is bounded; on expiry the WG records an error and stops.
 // ------------------------------------------------------------------------------------------
-__device__ inline void raise_error(const KParams& P, const Lds& L, uint32_t code) {
+__device__ __forceinline__ void raise_error(const KParams& P, const Lds& L, uint32_t code) {
   lds_st(&L.ctl[C_ABORT], 1u);
   __hip_atomic_fetch_or(P.err, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ inline bool aborted(const Lds& L) { return lds_ld(&L.ctl[C_ABORT]) != 0; }
+__device__ __forceinline__ bool aborted(const Lds& L) { return lds_ld(&L.ctl[C_ABORT]) != 0; }
 
 // Bounded spin: call expired() after every unsuccessful poll. Every 256th call it checks the
 // WG's abort flag, the grid's error word and the elapsed time of this wait.
 struct Waiter {
   uint32_t spins = 0;
   uint64_t start = 0;
-  __device__ bool expired(const KParams& P, const Lds& L) {
+  __device__ __forceinline__ bool expired(const KParams& P, const Lds& L) {
     if ((++spins & 255u) != 0) return false;
     if (aborted(L)) return true;
     if (__hip_atomic_load(P.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return true;
@@ -213,22 +213,22 @@ struct Waiter {
 constexpr int kProdDepth = 16;  // tiles in flight per producer wave
 
 struct Cursor {
-  int64_t next;       // next stream index this producer will issue
-  int64_t seg_start;  // stream index of the current segment's first tile
+  uint32_t next;       // next stream index this producer will issue
+  uint32_t seg_start;  // stream index of the current segment's first tile
   int32_t step, seg;
   Seg g;
   Att at;
   bool end;
 };
 
-__device__ inline void cursor_load_seg(const KParams& P, const Plan& pl, Cursor& c) {
+__device__ __forceinline__ void cursor_load_seg(const KParams& P, const Plan& pl, Cursor& c) {
   if (c.seg == 0) c.at = att_info(P.s, pl.w, P.pos0 + c.step);
   c.g = seg_info(P, pl, c.at, c.step, c.seg);
 }
-__device__ inline void cursor_seek(const KParams& P, const Plan& pl, Cursor& c) {
+__device__ __forceinline__ void cursor_seek(const KParams& P, const Plan& pl, Cursor& c) {
   // advance segments until `next` falls inside the current one
-  while (!c.end && c.next >= c.seg_start + c.g.len) {
-    c.seg_start += c.g.len;
+  while (!c.end && c.next >= c.seg_start + (uint32_t)c.g.len) {
+    c.seg_start += (uint32_t)c.g.len;
     c.seg++;
     if (c.seg > 5 * P.s.L) {
       c.seg = 0;
@@ -242,13 +242,17 @@ __device__ inline void cursor_seek(const KParams& P, const Plan& pl, Cursor& c) 
   }
 }
 
-__device__ inline void producer(const KParams& P, const Lds& L, const Plan& pl, int pw, int lane) {
-  const int32_t R = P.ring_slots;
+// Producer wave pw handles the WG's stream tiles pw, pw+4, pw+8, ...: it keeps kProdDepth of
+// them in flight in registers and writes each into its ring slot once the slot's previous tile
+// has been consumed. Tiles are written in the order they were issued. K/V tiles of step s are
+// only issued once the consumers have started step s (their rows are final by then).
+__device__ __forceinline__ void producer(const KParams& P, const Lds& L, const Plan& pl, int pw, int lane) {
+  const uint32_t R = (uint32_t)P.ring_slots;
   const Shape& s = P.s;
   const int lpp = s.hd / 8;  // lanes per KV position
   const int ppt = att_pos_per_tile(s);
   Cursor cur;
-  cur.next = pw;
+  cur.next = (uint32_t)pw;
   cur.seg_start = 0;
   cur.step = 0;
   cur.seg = 0;
@@ -257,77 +261,69 @@ __device__ inline void producer(const KParams& P, const Lds& L, const Plan& pl, 
   cursor_seek(P, pl, cur);
 
   v4u buf[kProdDepth];
-  int64_t idx[kProdDepth];
-  bool val[kProdDepth];
 #pragma unroll
-  for (int u = 0; u < kProdDepth; ++u) {
-    val[u] = false;
-    idx[u] = 0;
-    buf[u] = v4u{0u, 0u, 0u, 0u};
-  }
+  for (int u = 0; u < kProdDepth; ++u) buf[u] = v4u{0u, 0u, 0u, 0u};
+  uint32_t valid = 0;                 // bit u: buf[u] holds an issued, unwritten tile
+  uint32_t wr_next = (uint32_t)pw;    // stream index of the oldest unwritten tile
+  uint32_t wr_slot = (uint32_t)pw % R;
   bool fail = false;
 
   while (!fail) {
-    bool live = false;
     bool gated = false;
 #pragma unroll
     for (int u = 0; u < kProdDepth; ++u) {
-      if (val[u]) {
-        // write tile idx[u] into its ring slot once the slot's previous tile was consumed
-        const int64_t i = idx[u];
-        const int32_t slot = (int32_t)((uint32_t)i % (uint32_t)R);
-        const uint32_t need = (uint32_t)(i - R + 1);  // freed value that makes the slot free
-        if (i >= R) {
+      if (!fail && (valid & (1u << u))) {
+        if (wr_next >= R) {
+          const uint32_t need = wr_next - R + 1;  // freed value that makes the slot free
           Waiter wt;
-          while ((int32_t)(lds_ld(&L.freed[slot]) - need) < 0) {
+          while ((int32_t)(lds_ld(&L.freed[wr_slot]) - need) < 0) {
             __builtin_amdgcn_s_sleep(1);
             if (wt.expired(P, L)) {
               fail = true;
               break;
             }
           }
-          if (fail) break;
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
         }
-        *(v4u*)(L.ring + (size_t)slot * kTileBytes + lane * 16) = buf[u];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-        if (lane == 0) lds_st(&L.ready[slot], (uint32_t)(i + 1));
-        val[u] = false;
+        if (!fail) {
+          *(v4u*)(L.ring + wr_slot * kTileBytes + lane * 16) = buf[u];
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+          if (lane == 0) lds_st(&L.ready[wr_slot], wr_next + 1);
+        }
+        valid &= ~(1u << u);
+        wr_next += kProducerWaves;
+        wr_slot += kProducerWaves;
+        if (wr_slot >= R) wr_slot -= R;
       }
-      if (!cur.end && !gated) {
-        const Seg& g = cur.g;
-        const int64_t t = cur.next - cur.seg_start;
-        if (g.kind == SK_KV && (int32_t)lds_ld(&L.ctl[C_STEP]) < cur.step) {
-          // K/V rows of this step may only be read once every WG finished the previous step
+      if (!fail && !cur.end && !gated) {
+        const uint32_t t = cur.next - cur.seg_start;
+        if (cur.g.kind == SK_KV && (int32_t)lds_ld(&L.ctl[C_STEP]) < cur.step) {
           gated = true;
         } else {
           v4u v = v4u{0u, 0u, 0u, 0u};
-          if (g.kind == SK_W) {
-            const v4u* src = (const v4u*)(P.packed + (size_t)(pl.wbase + g.wofs + t) * kTileBytes) + lane;
+          if (cur.g.kind == SK_W) {
+            const v4u* src = (const v4u*)(P.packed + (size_t)(pl.wbase + cur.g.wofs + t) * kTileBytes) + lane;
             v = __builtin_nontemporal_load(src);
           } else {
             const int32_t tp = (int32_t)(t >> 1), kvsel = (int32_t)(t & 1);
             const int32_t pos = cur.at.c0 + tp * ppt + lane / lpp;
             if (pos < cur.at.c0 + cur.at.ncache) {
-              const v4u* src =
-                  (const v4u*)(P.kv + kv_offset(s, g.layer, kvsel, cur.at.j, pos)) + (lane % lpp);
+              const v4u* src = (const v4u*)(P.kv + kv_offset(s, cur.g.layer, kvsel, cur.at.j, pos)) + (lane % lpp);
               v = *src;
             }
           }
           buf[u] = v;
-          idx[u] = cur.next;
-          val[u] = true;
+          valid |= 1u << u;
           cur.next += kProducerWaves;
           cursor_seek(P, pl, cur);
         }
       }
-      live |= val[u];
     }
     if (fail) break;
-    if (!live) {
+    if (valid == 0) {
       if (cur.end) break;
       if (gated) {
-        // drained: wait for the consumers to start the step
+        // drained: wait until the consumers have started the step
         Waiter wt;
         while ((int32_t)lds_ld(&L.ctl[C_STEP]) < cur.step) {
           __builtin_amdgcn_s_sleep(2);
@@ -354,11 +350,12 @@ struct Cons {
   int tid;      // 0..255 among consumer threads
   uint32_t bar_target;
   bool fail;
-  __device__ Cons(const KParams& p, const Lds& l, const Plan& q, int c_, int lane_)
+  __device__ __forceinline__ Cons(const KParams& p, const Lds& l, const Plan& q, int c_, int lane_)
       : P(p), L(l), pl(q), c(c_), lane(lane_), tid(c_ * kWave + lane_), bar_target(0), fail(false) {}
 
   // barrier of the 4 consumer waves (LDS counter; the producers are not involved)
-  __device__ void csync() {
+  __device__ __forceinline__ void csync() {
+    fail = __builtin_amdgcn_ballot_w64(fail) != 0;  // one lane's failure is the wave's
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     if (lane == 0) __hip_atomic_fetch_add(&L.ctl[C_BAR], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -375,7 +372,7 @@ struct Cons {
   }
 
   // wait until ring tile i is present
-  __device__ void wait_tile(int64_t i, int32_t slot) {
+  __device__ __forceinline__ void wait_tile(int64_t i, int32_t slot) {
     const uint32_t want = (uint32_t)(i + 1);
     if (lds_ld(&L.ready[slot]) != want) {
       Waiter wt;
@@ -390,76 +387,108 @@ struct Cons {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   }
   // the slot's data has been read (its values are in registers): hand the slot back
-  __device__ void free_tile(int64_t i, int32_t slot) {
+  __device__ __forceinline__ void free_tile(int64_t i, int32_t slot) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     if (lane == 0) lds_st(&L.freed[slot], (uint32_t)(i + 1));
   }
-  __device__ int32_t slot_of(int64_t i) const { return (int32_t)((uint32_t)i % (uint32_t)P.ring_slots); }
+  __device__ __forceinline__ int32_t slot_of(int64_t i) const { return (int32_t)((uint32_t)i % (uint32_t)P.ring_slots); }
 
-  // Gather up to three ranges of tagged words with the given epoch into LDS floats.
-  // Optionally returns the sum of squares of range 0 (all consumer threads get it).
-  __device__ float fetch(const uint64_t* src0, int n0, float* dst0, const uint64_t* src1, int n1, float* dst1,
-                         const uint64_t* src2, int n2, float* dst2, uint32_t epoch, bool want_ss) {
-    constexpr int KMAX = 32;
-    const int ntot = n0 + n1 + n2;
-    float ss = 0.f;
-    for (int base = 0; base < ntot && !fail; base += KMAX * kConsumerThreads) {
+  // Gather n tagged words with the given epoch from src into LDS floats dst. Every consumer
+  // thread polls its words tid, tid+256, ... (all in flight at once), writes each value as soon
+  // as its tag is current, and re-polls only the missing ones. If want_ss, returns the sum of
+  // squares of the n values (fixed summation order) to every consumer thread.
+  // The consumer barrier below is reached by every consumer thread, whatever its word count.
+  __device__ __forceinline__ float fetch(const uint64_t* src, int n, float* dst, uint32_t epoch, bool want_ss) {
+    constexpr int KMAX = 16;
+    for (int base = 0; base < n; base += KMAX * kConsumerThreads) {
+      const uint64_t* sp = src + base + tid;
+      float* dp = dst + base + tid;
       uint32_t missing = 0;
-      float val[KMAX];
 #pragma unroll
-      for (int k = 0; k < KMAX; ++k) {
-        val[k] = 0.f;
-        if (base + tid + k * kConsumerThreads < ntot) missing |= 1u << k;
-      }
+      for (int k = 0; k < KMAX; ++k)
+        if (base + tid + k * kConsumerThreads < n) missing |= 1u << k;
+      uint64_t wv[KMAX];
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k)
+        if (missing & (1u << k)) wv[k] = ld_x(sp + k * kConsumerThreads);
+      if (base == 0) csync();  // earlier readers of dst are done before it is overwritten
       Waiter wt;
-      while (missing) {
-        uint64_t wv[KMAX];
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k) {
-          if (missing & (1u << k)) {
-            const int e = base + tid + k * kConsumerThreads;
-            const uint64_t* p = e < n0 ? src0 + e : (e < n0 + n1 ? src1 + (e - n0) : src2 + (e - n0 - n1));
-            wv[k] = ld_x(p);
-          }
-        }
+      while (true) {
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
           if ((missing & (1u << k)) && (uint32_t)wv[k] == epoch) {
             missing &= ~(1u << k);
-            val[k] = __uint_as_float((uint32_t)(wv[k] >> 32));
+            dp[k * kConsumerThreads] = __uint_as_float((uint32_t)(wv[k] >> 32));
           }
         }
-        if (missing) {
-          __builtin_amdgcn_s_sleep(1);
-          if (wt.expired(P, L)) {
-            fail = true;
-            break;
-          }
+        if (missing == 0 || fail) break;
+        __builtin_amdgcn_s_sleep(1);
+        if (wt.expired(P, L)) {
+          fail = true;
+          break;
         }
-      }
-      csync();  // earlier readers of the destination are done
 #pragma unroll
-      for (int k = 0; k < KMAX; ++k) {
-        const int e = base + tid + k * kConsumerThreads;
-        if (e < ntot) {
-          if (e < n0) {
-            dst0[e] = val[k];
-            if (want_ss) ss = fmaf(val[k], val[k], ss);
-          } else if (e < n0 + n1) {
-            dst1[e - n0] = val[k];
-          } else {
-            dst2[e - n0 - n1] = val[k];
-          }
-        }
+        for (int k = 0; k < KMAX; ++k)
+          if (missing & (1u << k)) wv[k] = ld_x(sp + k * kConsumerThreads);
       }
     }
-    if (want_ss) ss = block_sum(ss);
+    float ss = 0.f;
+    if (want_ss) {
+      for (int e = tid; e < n; e += kConsumerThreads) ss = fmaf(dst[e], dst[e], ss);
+      ss = block_sum(ss);
+    }
     csync();
     return ss;
   }
 
+  // Gather up to three short ranges (query heads and the current K/V row) into LDS floats.
+  __device__ __forceinline__ void fetch3(const uint64_t* s0, int n0, float* d0, const uint64_t* s1, int n1, float* d1,
+                                         const uint64_t* s2, int n2, float* d2, uint32_t epoch) {
+    constexpr int KM = 8;
+    const int ntot = n0 + n1 + n2;
+    for (int base = 0; base < ntot; base += KM * kConsumerThreads) {
+      uint32_t missing = 0;
+#pragma unroll
+      for (int k = 0; k < KM; ++k)
+        if (base + tid + k * kConsumerThreads < ntot) missing |= 1u << k;
+      uint64_t wv[KM];
+      auto reload = [&]() {
+#pragma unroll
+        for (int k = 0; k < KM; ++k) {
+          if (missing & (1u << k)) {
+            const int e = base + tid + k * kConsumerThreads;
+            const uint64_t* p = e < n0 ? s0 + e : (e < n0 + n1 ? s1 + (e - n0) : s2 + (e - n0 - n1));
+            wv[k] = ld_x(p);
+          }
+        }
+      };
+      reload();
+      if (base == 0) csync();
+      Waiter wt;
+      while (true) {
+#pragma unroll
+        for (int k = 0; k < KM; ++k) {
+          if ((missing & (1u << k)) && (uint32_t)wv[k] == epoch) {
+            missing &= ~(1u << k);
+            const int e = base + tid + k * kConsumerThreads;
+            float* d = e < n0 ? d0 + e : (e < n0 + n1 ? d1 + (e - n0) : d2 + (e - n0 - n1));
+            *d = __uint_as_float((uint32_t)(wv[k] >> 32));
+          }
+        }
+        if (missing == 0 || fail) break;
+        __builtin_amdgcn_s_sleep(1);
+        if (wt.expired(P, L)) {
+          fail = true;
+          break;
+        }
+        reload();
+      }
+    }
+    csync();
+  }
+
   // sum over the 256 consumer threads, in a fixed order; every consumer thread gets the result
-  __device__ float block_sum(float v) {
+  __device__ __forceinline__ float block_sum(float v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
     csync();  // scr may still be read by a previous user
@@ -472,7 +501,7 @@ struct Cons {
   }
 
   // act[i] = (xres[i] * r) * g[i],  r = 1/sqrt(ss/d + eps)
-  __device__ void rmsnorm_to_act(float ss, const uint16_t* g) {
+  __device__ __forceinline__ void rmsnorm_to_act(float ss, const uint16_t* g) {
     const int d = P.s.d;
     const float r = 1.0f / sqrtf(ss / (float)d + P.s.eps);
     for (int i = tid; i < d; i += kConsumerThreads) {
@@ -486,7 +515,7 @@ struct Cons {
   // Each consumer wave takes pairs lp = c, c+4, ...; per tile, lane l multiplies its 8 bf16
   // weights by act[256 j + 8 (l mod 32) ...]; halves reduce to the pair's two dot products.
   template <typename Epi>
-  __device__ void gemv(int st, int64_t tile_base, Epi epi) {
+  __device__ __forceinline__ void gemv(int st, int64_t tile_base, Epi epi) {
     const int32_t np = pl.np[st], kt = pl.kt[st];
     const int ql = lane & 31;
     for (int32_t lp = c; lp < np && !fail; lp += kConsumerWaves) {
@@ -525,7 +554,7 @@ struct Cons {
 // query head of the group.
 // ------------------------------------------------------------------------------------------
 template <int G, int HD>
-__device__ void attention_chunk(Cons& C, const Att& at, int32_t l, int32_t pos, int64_t tile_base, uint32_t epoch) {
+__device__ __forceinline__ void attention_chunk(Cons& C, const Att& at, int32_t l, int32_t pos, int64_t tile_base, uint32_t epoch) {
   const KParams& P = C.P;
   const Lds& L = C.L;
   const Shape& s = P.s;
@@ -676,7 +705,7 @@ __device__ void attention_chunk(Cons& C, const Att& at, int32_t l, int32_t pos, 
 }
 
 // merge of the chunk partials of one (query head, 32-dim slice)
-__device__ void merge_unit(Cons& C, const Att& at, int32_t l, int32_t u, uint32_t epoch) {
+__device__ __forceinline__ void merge_unit(Cons& C, const Att& at, int32_t l, int32_t u, uint32_t epoch) {
   const KParams& P = C.P;
   const Lds& L = C.L;
   const Shape& s = P.s;
@@ -755,8 +784,11 @@ __device__ void merge_unit(Cons& C, const Att& at, int32_t l, int32_t u, uint32_
   C.csync();
 }
 
+// A token id that indexes memory is always kept inside [0, V).
+__device__ __forceinline__ int32_t clamp_token(int32_t t, int32_t V) { return t < 0 ? 0 : (t >= V ? V - 1 : t); }
+
 template <int G, int HD>
-__device__ void consumer(const KParams& P, const Lds& L, const Plan& pl, int c, int lane) {
+__device__ __forceinline__ void consumer(const KParams& P, const Lds& L, const Plan& pl, int c, int lane) {
   Cons C(P, L, pl, c, lane);
   const Shape& s = P.s;
   const Exch& X = P.exo;
@@ -773,7 +805,7 @@ __device__ void consumer(const KParams& P, const Lds& L, const Plan& pl, int c, 
   // the token is uniform across consumer waves: broadcast through LDS
   if (C.tid == 0) L.scr[0] = __int_as_float(tok);
   C.csync();
-  tok = __float_as_int(L.scr[0]);
+  tok = clamp_token(__float_as_int(L.scr[0]), s.V);
   C.csync();
 
   for (int32_t step = 0; step < P.n_steps && !C.fail; ++step) {
@@ -792,7 +824,7 @@ __device__ void consumer(const KParams& P, const Lds& L, const Plan& pl, int c, 
 
     for (int32_t l = 0; l < s.L && !C.fail; ++l) {
       // ---------------- QKV
-      if (l > 0) ss = C.fetch(ex + X.xf + (int64_t)l * s.d, s.d, L.xres, nullptr, 0, nullptr, nullptr, 0, nullptr, ep, true);
+      if (l > 0) ss = C.fetch(ex + X.xf + (int64_t)l * s.d, s.d, L.xres, ep, true);
       C.rmsnorm_to_act(ss, P.norms + (int64_t)l * 2 * s.d);
       if (C.fail) break;
       {
@@ -822,10 +854,10 @@ __device__ void consumer(const KParams& P, const Lds& L, const Plan& pl, int c, 
         const int32_t G_ = s.group();
         const uint64_t* qsrc = ex + X.q + (int64_t)l * s.qdim() + (int64_t)at.j * G_ * s.hd;
         if (at.has_p)
-          C.fetch(qsrc, G_ * s.hd, L.act, ex + X.k + (int64_t)l * s.kvdim() + at.j * s.hd, s.hd, L.act + G_ * s.hd,
-                  ex + X.v + (int64_t)l * s.kvdim() + at.j * s.hd, s.hd, L.act + (G_ + 1) * s.hd, ep, false);
+          C.fetch3(qsrc, G_ * s.hd, L.act, ex + X.k + (int64_t)l * s.kvdim() + at.j * s.hd, s.hd, L.act + G_ * s.hd,
+                   ex + X.v + (int64_t)l * s.kvdim() + at.j * s.hd, s.hd, L.act + (G_ + 1) * s.hd, ep);
         else
-          C.fetch(qsrc, G_ * s.hd, L.act, nullptr, 0, nullptr, nullptr, 0, nullptr, ep, false);
+          C.fetch(qsrc, G_ * s.hd, L.act, ep, false);
         if (C.fail) break;
         attention_chunk<G, HD>(C, at, l, pos, tbase, ep);
         tbase += 2 * at.nkt;
@@ -838,7 +870,7 @@ __device__ void consumer(const KParams& P, const Lds& L, const Plan& pl, int c, 
         for (int32_t u = u0; u < nu && merge_unit_wg(s, u) == pl.w && !C.fail; ++u) merge_unit(C, at, l, u, ep);
       }
       // ---------------- O projection + residual
-      C.fetch(ex + X.o + (int64_t)l * s.qdim(), s.qdim(), L.act, nullptr, 0, nullptr, nullptr, 0, nullptr, ep, false);
+      C.fetch(ex + X.o + (int64_t)l * s.qdim(), s.qdim(), L.act, ep, false);
       if (C.fail) break;
       __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this WG's K/V rows are complete before its next outputs
       {
@@ -852,7 +884,7 @@ __device__ void consumer(const KParams& P, const Lds& L, const Plan& pl, int c, 
       }
       // ---------------- gate/up + SwiGLU
       C.csync();  // every wave has finished reading xres before it is replaced
-      ss = C.fetch(ex + X.xa + (int64_t)l * s.d, s.d, L.xres, nullptr, 0, nullptr, nullptr, 0, nullptr, ep, true);
+      ss = C.fetch(ex + X.xa + (int64_t)l * s.d, s.d, L.xres, ep, true);
       C.rmsnorm_to_act(ss, P.norms + (int64_t)l * 2 * s.d + s.d);
       if (C.fail) break;
       {
@@ -865,7 +897,7 @@ __device__ void consumer(const KParams& P, const Lds& L, const Plan& pl, int c, 
       }
       // ---------------- down + residual
       C.csync();
-      C.fetch(ex + X.h + (int64_t)l * s.F, s.F, L.act, nullptr, 0, nullptr, nullptr, 0, nullptr, ep, false);
+      C.fetch(ex + X.h + (int64_t)l * s.F, s.F, L.act, ep, false);
       if (C.fail) break;
       {
         uint64_t* xf = ex + X.xf + (int64_t)(l + 1) * s.d;
@@ -885,7 +917,7 @@ __device__ void consumer(const KParams& P, const Lds& L, const Plan& pl, int c, 
     int32_t best_i = 0x7fffffff;
     const bool lm = step_has_lm(P, step);
     if (lm) {
-      ss = C.fetch(ex + X.xf + (int64_t)s.L * s.d, s.d, L.xres, nullptr, 0, nullptr, nullptr, 0, nullptr, ep, true);
+      ss = C.fetch(ex + X.xf + (int64_t)s.L * s.d, s.d, L.xres, ep, true);
       C.rmsnorm_to_act(ss, P.norms + (int64_t)s.L * 2 * s.d);
       if (C.fail) break;
       float* lo = P.logits_out ? P.logits_out + (P.lm_last_only ? 0 : (int64_t)step * s.V) : nullptr;
@@ -920,7 +952,7 @@ __device__ void consumer(const KParams& P, const Lds& L, const Plan& pl, int c, 
     }
     C.csync();
     // every WG gathers all candidates (this is also the step's grid-wide synchronisation)
-    C.fetch(ex + X.lm, 2 * s.nwg, L.scr, nullptr, 0, nullptr, nullptr, 0, nullptr, ep, false);
+    C.fetch(ex + X.lm, 2 * s.nwg, L.scr, ep, false);
     if (C.fail) break;
     int32_t next = 0;
     {
@@ -951,7 +983,7 @@ __device__ void consumer(const KParams& P, const Lds& L, const Plan& pl, int c, 
         const int32_t i = __float_as_int(L.scr[2 * k + 1]);
         if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
       }
-      next = bi;
+      next = clamp_token(bi, s.V);
       C.csync();
     }
     if (lm && pl.w == 0 && C.tid == 0) {
@@ -968,7 +1000,7 @@ __device__ void consumer(const KParams& P, const Lds& L, const Plan& pl, int c, 
         L.scr[0] = __int_as_float(f);
       }
       C.csync();
-      next = __float_as_int(L.scr[0]);
+      next = clamp_token(__float_as_int(L.scr[0]), s.V);
       C.csync();
     }
     tok = next;
