@@ -132,6 +132,13 @@ static kie_status make_shape(const kie_config* c, int nwg_override, Shape* s, st
             kMaxWG);
     return KIE_ERR_UNSUPPORTED;
   }
+  for (int st = ST_QKV; st < ST_COUNT; ++st) {
+    const int64_t per_wg = ((int64_t)s->stage_pairs(st) + nwg - 1) / nwg;
+    if (per_wg > 256) {  // the kernel stages at most 64 pair outputs per consumer wave
+      set_err(err, "a weight matrix has %lld row pairs per compute unit (at most 256 supported)", (long long)per_wg);
+      return KIE_ERR_UNSUPPORTED;
+    }
+  }
   if ((int64_t)s->V * s->d >= (int64_t)1 << 40) {
     set_err(err, "embedding too large");
     return KIE_ERR_UNSUPPORTED;
@@ -400,6 +407,7 @@ static kie_status launch(kie_ctx* ctx, const int32_t* first, int32_t n, const in
   P.rope = (const float2*)(ctx->ws + ctx->wso.rope);
   P.wbase = (const int64_t*)(ctx->ws + ctx->wso.wbase);
   P.err = (uint32_t*)(ctx->ws + ctx->wso.err);
+  P.trace = (uint64_t*)(ctx->ws + ctx->wso.trace);
   P.first_tok = first;
   P.forced = forced;
   P.tokens_out = toks_out;
@@ -465,6 +473,12 @@ kie_status kie_stream_read(const void* src, size_t bytes, uint32_t* sink_dev, vo
   if (query_cus(&n, nullptr) != KIE_OK) return KIE_ERR_HIP;
   return launch_stream_read(src, (int64_t)bytes, sink_dev, n, (hipStream_t)hip_stream) == hipSuccess ? KIE_OK
                                                                                                        : KIE_ERR_HIP;
+}
+
+int64_t kie_trace_offset(const kie_config* cfg) {
+  Shape s;
+  if (make_shape(cfg, 0, &s, nullptr) != KIE_OK) return -1;
+  return workspace_layout(s).trace;
 }
 
 }  // extern "C"

@@ -60,3 +60,39 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
 }
 
 }  // namespace kie
+
+namespace kie {
+// DPP lane permutations (gfx9 encodings) used for in-register reductions: no LDS round trip.
+constexpr int kDppQuad1032 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuad2301 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowBcast15 = 0x142;
+
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWMASK, 0xF, false));
+}
+// Sum over each row of 16 lanes; every lane of the row receives the row's sum.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<kDppQuad1032>(v);
+  v += dpp_f<kDppQuad2301>(v);
+  v += dpp_f<kDppRowHalfMirror>(v);
+  v += dpp_f<kDppRowMirror>(v);
+  return v;
+}
+// Sum over each row of 8 lanes (half rows); every lane receives its half row's sum.
+__device__ __forceinline__ float row8_sum(float v) {
+  v += dpp_f<kDppQuad1032>(v);
+  v += dpp_f<kDppQuad2301>(v);
+  v += dpp_f<kDppRowHalfMirror>(v);
+  return v;
+}
+// Sums of lanes 0..31 and of lanes 32..63 (fixed order), returned wave-uniform.
+__device__ __forceinline__ void half_wave_sums(float v, float* lo, float* hi) {
+  v = row16_sum(v);
+  v += dpp_f<kDppRowBcast15, 0xA>(v);  // rows 1 and 3 add the last lane of rows 0 and 2
+  *lo = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 31));
+  *hi = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
+}
+}  // namespace kie

@@ -184,8 +184,9 @@ KIE_HD Exch exch_layout(const Shape& s) {
 // Workspace (bytes, 256-aligned pieces): exchange words, RoPE table [max_seq][hd/2] of (cos,sin),
 // per-WG weight-stream base (in tiles), error word, norm gains [L][2][d] + final [d] (bf16).
 struct Workspace {
-  int64_t exch, rope, wbase, err, norms, end;
+  int64_t exch, rope, wbase, err, norms, trace, end;
 };
+constexpr int kTraceWords = 16;  // per wave: cycle counters of a KIE_TRACE build
 KIE_HD int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 KIE_HD Workspace workspace_layout(const Shape& s) {
   Workspace w;
@@ -195,6 +196,7 @@ KIE_HD Workspace workspace_layout(const Shape& s) {
   w.wbase = o; o = align256(o + (int64_t)(s.nwg + 1) * 8);
   w.err = o; o = align256(o + 64);
   w.norms = o; o = align256(o + ((int64_t)s.L * 2 + 1) * s.d * 2);
+  w.trace = o; o = align256(o + (int64_t)s.nwg * (kThreads / kWave) * kTraceWords * 8);
   w.end = o;
   return w;
 }

@@ -25,6 +25,7 @@ struct KParams {
   const float2* rope;        // [max_seq][hd/2] (cos, sin)
   const int64_t* wbase;      // [nwg] first tile of each WG's stream
   uint32_t* err;             // device error word
+  uint64_t* trace;           // [nwg][8 waves][16] cycle counters (written by KIE_TRACE builds only)
   const int32_t* first_tok;  // [1]
   const int32_t* forced;     // [n_steps-1] or null
   int32_t* tokens_out;       // [n_steps] or null

@@ -18,6 +18,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "kie.h"
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -28,6 +30,11 @@ int32_t kie_stream_copy(void* dst, const void* src, size_t bytes, void* hip_stre
 /* Read src[0..bytes) once; sink_dev (device uint32 [1]) is written only in a practically
  * impossible case and exists to keep the loads. */
 int32_t kie_stream_read(const void* src, size_t bytes, uint32_t* sink_dev, void* hip_stream);
+
+/* Byte offset, inside the workspace of a context with this configuration, of the per-wave cycle
+ * counters ([compute units][8 waves][16] uint64) that a build compiled with -DKIE_TRACE writes at
+ * the end of each decode launch (zeros otherwise); -1 for an invalid configuration. */
+int64_t kie_trace_offset(const kie_config* cfg);
 
 #ifdef __cplusplus
 }
