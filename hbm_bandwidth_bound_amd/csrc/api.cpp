@@ -29,7 +29,6 @@ struct kie_ctx {
   uint16_t* kv;
   uint8_t* ws;
   KernelFn kernel;
-  int32_t ring;
   int32_t lds;
   int32_t pos;
   uint32_t epoch;  // tag of the next step
@@ -134,8 +133,10 @@ static kie_status make_shape(const kie_config* c, int nwg_override, Shape* s, st
   }
   for (int st = ST_QKV; st < ST_COUNT; ++st) {
     const int64_t per_wg = ((int64_t)s->stage_pairs(st) + nwg - 1) / nwg;
-    if (per_wg > 256) {  // the kernel stages at most 64 pair outputs per consumer wave
-      set_err(err, "a weight matrix has %lld row pairs per compute unit (at most 256 supported)", (long long)per_wg);
+    const int64_t units = per_wg * (s->stage_kt(st) / unit_tiles(s->stage_kt(st)));
+    if (units > kMaxUnits) {  // per-unit partial sums of one stage live in LDS
+      set_err(err, "a weight matrix needs %lld work units per compute unit (at most %d supported)", (long long)units,
+              kMaxUnits);
       return KIE_ERR_UNSUPPORTED;
     }
   }
@@ -236,9 +237,9 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
     return KIE_ERR_UNSUPPORTED;
   }
   const int lds_limit = (int)prop.sharedMemPerBlock;
-  const int32_t ring = max_ring_slots(s, lds_limit);
-  if (ring < 16) {
-    set_err(err, "shape needs too much LDS (ring of %d tiles)", ring);
+  const int32_t lds = lds_bytes_for(s);
+  if (lds > lds_limit) {
+    set_err(err, "shape needs %d bytes of LDS per workgroup (device limit %d)", lds, lds_limit);
     return KIE_ERR_UNSUPPORTED;
   }
   KernelFn kfn = decode_kernel_for(s.group(), s.hd);
@@ -246,7 +247,6 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
     set_err(err, "no kernel for group %d head_dim %d", s.group(), s.hd);
     return KIE_ERR_UNSUPPORTED;
   }
-  const int32_t lds = lds_bytes_for(s, ring);
   HIP_TRY(err, hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, lds));
   int occ = 0;
   HIP_TRY(err, hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)kfn, kThreads, lds));
@@ -265,19 +265,20 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
   c->kv = (uint16_t*)kv_cache;
   c->ws = (uint8_t*)workspace;
   c->kernel = kfn;
-  c->ring = ring;
   c->lds = lds;
   c->pos = 0;
   c->epoch = 1;
   c->bad_state = false;
   c->timeout_ticks = 200000000;  // 2 s per wait
-  c->wbase_host.resize(s.nwg + 1);
+  c->wbase_host.resize((size_t)s.nwg * kWaves + 1);
   int64_t acc = 0;
   for (int w = 0; w < s.nwg; ++w) {
-    c->wbase_host[w] = acc;
-    acc += wg_token_tiles(s, w);
+    for (int v = 0; v < kWaves; ++v) {
+      c->wbase_host[(size_t)w * kWaves + v] = acc;
+      acc += stream_tiles(s, w, v);
+    }
   }
-  c->wbase_host[s.nwg] = acc;
+  c->wbase_host[(size_t)s.nwg * kWaves] = acc;
 
   auto fail = [&](const char* what, hipError_t e) {
     set_err(err, "%s: %s", what, hipGetErrorString(e));
@@ -290,8 +291,8 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
   if ((e = hipMemsetAsync(c->ws, 0, (size_t)c->wso.end, stm)) != hipSuccess) return fail("clear workspace", e);
   if ((e = launch_rope_table((float2*)(c->ws + c->wso.rope), s.max_seq, s.hd, s.theta, stm)) != hipSuccess)
     return fail("rope table", e);
-  if ((e = hipMemcpyAsync(c->ws + c->wso.wbase, c->wbase_host.data(), (size_t)(s.nwg + 1) * 8, hipMemcpyHostToDevice,
-                          stm)) != hipSuccess)
+  if ((e = hipMemcpyAsync(c->ws + c->wso.wbase, c->wbase_host.data(), c->wbase_host.size() * 8,
+                          hipMemcpyHostToDevice, stm)) != hipSuccess)
     return fail("copy stream bases", e);
   uint16_t* norms = (uint16_t*)(c->ws + c->wso.norms);
   for (int l = 0; l < L; ++l) {
@@ -364,7 +365,7 @@ kie_status kie_sync(kie_ctx* ctx) {
   HIP_TRY(&ctx->last_error, hipStreamSynchronize(ctx->stream));
   uint32_t errw = 0;
   HIP_TRY(&ctx->last_error, hipMemcpy(&errw, ctx->ws + ctx->wso.err, 4, hipMemcpyDeviceToHost));
-  if (errw & (KERR_PRODUCER | KERR_CONSUMER)) {
+  if (errw & KERR_TIMEOUT) {
     ctx->bad_state = true;
     set_err(&ctx->last_error, "device wait timed out (error word 0x%x)", errw);
     return KIE_ERR_TIMEOUT;
@@ -417,7 +418,6 @@ static kie_status launch(kie_ctx* ctx, const int32_t* first, int32_t n, const in
   P.n_steps = n;
   P.epoch0 = ctx->epoch;
   P.lm_last_only = lm_last_only;
-  P.ring_slots = ctx->ring;
   P.timeout_ticks = ctx->timeout_ticks;
   void* args[] = {&P};
   HIP_TRY(&ctx->last_error, hipLaunchCooperativeKernel((const void*)ctx->kernel, dim3(ctx->s.nwg), dim3(kThreads), args,

@@ -51,6 +51,17 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Buffer resource over [base, base + bytes): a raw buffer load through it whose per-lane offset
+// (VGPR offset + immediate) is at or past `bytes` returns zeros without touching memory. The
+// scalar offset is not part of that check, so all offsets here are per-lane.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr int kLoadNT = 2;  // cache policy of weight and KV loads: streamed once (nontemporal)
+__device__ __forceinline__ v4u load16(__amdgpu_buffer_rsrc_t rs, uint32_t voff) {
+  return __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, kLoadNT));
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_bcast(T v, int lane) {
   return __builtin_amdgcn_readlane(v, lane);
@@ -87,6 +98,15 @@ __device__ __forceinline__ float row8_sum(float v) {
   v += dpp_f<kDppQuad2301>(v);
   v += dpp_f<kDppRowHalfMirror>(v);
   return v;
+}
+// Sum over all 64 lanes in a fixed order, returned wave-uniform.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  const float r0 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 0));
+  const float r1 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 16));
+  const float r2 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 32));
+  const float r3 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 48));
+  return (r0 + r1) + (r2 + r3);
 }
 // Sums of lanes 0..31 and of lanes 32..63 (fixed order), returned wave-uniform.
 __device__ __forceinline__ void half_wave_sums(float v, float* lo, float* hi) {

@@ -2,19 +2,21 @@
 //
 // Decoding one token at batch 1 streams every active weight once (agentlenshq.com,
 // 《突破内存墙：在标准 GPU 上实现 3,000 tokens/s 的推理速度》, "瓶颈：是内存带宽，而非计算"). The packer
-// therefore lays the weights out in exactly the order each workgroup (one per compute unit) will
-// consume them within one token, so that every CU streams one contiguous slice with 16-byte
-// lane loads, and the kernel's producer waves can run ahead of the data dependencies.
+// therefore lays the weights out in exactly the order in which each wave of the persistent kernel
+// consumes them within one token: every wave streams one contiguous slice with 16-byte lane loads
+// and can issue its next loads before the inputs they will be multiplied with exist.
 //
 // Vocabulary
-//   WG       one persistent workgroup per compute unit; WG w runs on XCD (w mod 8).
-//   pair     two weight rows whose dot products one wave computes together: lanes 0..31 take
-//            row A, lanes 32..63 row B (RoPE partners, gate/up partners, or neighbours).
-//   tile     1 KiB = 64 lanes x 16 B: 256 consecutive k of row A followed by the same 256 k of
-//            row B. K (the row length) is a multiple of 256.
-//   stage    one weight matrix group of a layer: QKV, O, GU (gate+up) or DN (down), plus LM.
-//   round    up to NCW pairs, one per consumer wave, whose tiles are interleaved j-major so that
-//            the consumer waves eat the ring in stream order.
+//   WG       one persistent workgroup of 8 waves per compute unit.
+//   pair     two weight rows (A, B) that one wave reduces together: RoPE partners, gate/up
+//            partners, or neighbours. Their dot products share every activation load.
+//   tile     1 KiB = 64 lanes x 16 B covering 256 consecutive k of both rows: lane l holds
+//            A[4l..4l+3] then B[4l..4l+3] (bf16, little-endian pairs). K is a multiple of 256.
+//   unit     (pair, k-slice): ks consecutive k-tiles of one pair, ks = 8 when the row has a
+//            multiple of 8 tiles (else 4, 2 or 1); a pair of kt tiles has S = kt / ks units.
+//   batch    8 tile slots = 8 / ks units of one wave; the unit of a WG's stage with index u
+//            belongs to wave u mod 8. Slots of a missing unit are zero tiles.
+//   stream   one wave's batches for a whole token: L x [QKV, O, GU, DN], then the LM head.
 #pragma once
 #include <stdint.h>
 
@@ -27,13 +29,13 @@
 namespace kie {
 
 constexpr int kWave = 64;
-constexpr int kProducerWaves = 4;
-constexpr int kConsumerWaves = 4;
-constexpr int kThreads = (kProducerWaves + kConsumerWaves) * kWave;  // 512
-constexpr int kConsumerThreads = kConsumerWaves * kWave;             // 256
+constexpr int kWaves = 8;  // per WG
+constexpr int kThreads = kWaves * kWave;  // 512
 constexpr int kTileBytes = 1024;
 constexpr int kTileK = 256;  // k per tile and row
+constexpr int kBatch = 8;    // tile slots per batch
 constexpr int kMaxWG = 1024;
+constexpr int kMaxUnits = 2048;  // units of one stage per WG (LDS partial sums)
 
 enum Stage : int { ST_QKV = 0, ST_O = 1, ST_GU = 2, ST_DN = 3, ST_LM = 4, ST_COUNT = 5 };
 
@@ -68,48 +70,43 @@ struct Shape {
 KIE_HD int32_t split_begin(int64_t n, int32_t nwg, int32_t w) { return (int32_t)((n * w) / nwg); }
 KIE_HD int32_t split_end(int64_t n, int32_t nwg, int32_t w) { return (int32_t)((n * (w + 1)) / nwg); }
 
-// Tiles of a stage for a WG owning `np` pairs of row length kt tiles.
-KIE_HD int64_t stage_tiles(int32_t np, int32_t kt) { return (int64_t)np * kt; }
+// k-tiles per unit for a row of kt tiles
+KIE_HD int32_t unit_tiles(int32_t kt) { return kt % 8 == 0 ? 8 : (kt % 4 == 0 ? 4 : (kt % 2 == 0 ? 2 : 1)); }
 
-// Stream index (within the stage) of tile j of local pair lp.
-KIE_HD int32_t tile_index(int32_t np, int32_t kt, int32_t lp, int32_t j) {
-  const int32_t r = lp / kConsumerWaves, c = lp % kConsumerWaves;
-  const int32_t full = np / kConsumerWaves;
-  const int32_t nr = r < full ? kConsumerWaves : np - full * kConsumerWaves;
-  return r * kConsumerWaves * kt + j * nr + c;
+// One stage of one WG: its pairs and how they are cut into units and batches.
+struct StageGeo {
+  int32_t pb, np;   // first global pair, pairs owned
+  int32_t kt, ks;   // k-tiles per pair, per unit
+  int32_t S;        // units per pair
+  int32_t upb;      // units per batch (8 / ks)
+  int32_t nu;       // units of the WG (np * S)
+};
+KIE_HD StageGeo stage_geo(const Shape& s, int st, int32_t w) {
+  StageGeo g;
+  const int32_t n = s.stage_pairs(st);
+  g.pb = split_begin(n, s.nwg, w);
+  g.np = split_end(n, s.nwg, w) - g.pb;
+  g.kt = s.stage_kt(st);
+  g.ks = unit_tiles(g.kt);
+  g.S = g.kt / g.ks;
+  g.upb = kBatch / g.ks;
+  g.nu = g.np * g.S;
+  return g;
 }
+// units of wave v (u = v, v + 8, ...) and its batches
+KIE_HD int32_t wave_units(const StageGeo& g, int32_t v) { return g.nu > v ? (g.nu - v + kWaves - 1) / kWaves : 0; }
+KIE_HD int32_t wave_batches(const StageGeo& g, int32_t v) { return (wave_units(g, v) + g.upb - 1) / g.upb; }
 
-// Inverse of tile_index: local pair and k-tile of stage tile t.
-KIE_HD void tile_source(int32_t np, int32_t kt, int32_t t, int32_t* lp, int32_t* j) {
-  const int32_t full = np / kConsumerWaves;
-  const int32_t per_round = kConsumerWaves * kt;
-  const int32_t r = t / per_round;
-  if (r < full) {
-    const int32_t q = t - r * per_round;
-    *j = q / kConsumerWaves;
-    *lp = r * kConsumerWaves + q % kConsumerWaves;
-  } else {
-    const int32_t rem = np - full * kConsumerWaves;
-    const int32_t q = t - full * per_round;
-    *j = q / rem;
-    *lp = full * kConsumerWaves + q % rem;
-  }
+// Batches of one layer in the stream of (WG w, wave v), and of the LM head.
+KIE_HD int32_t layer_batches(const Shape& s, int32_t w, int32_t v) {
+  int32_t b = 0;
+  for (int st = ST_QKV; st <= ST_DN; ++st) b += wave_batches(stage_geo(s, st, w), v);
+  return b;
 }
-
-// Tiles per layer owned by WG w (QKV, O, GU, DN in stream order), and of the LM head.
-KIE_HD int64_t wg_layer_tiles(const Shape& s, int32_t w) {
-  int64_t t = 0;
-  for (int st = ST_QKV; st <= ST_DN; ++st) {
-    const int32_t n = s.stage_pairs(st);
-    t += stage_tiles(split_end(n, s.nwg, w) - split_begin(n, s.nwg, w), s.stage_kt(st));
-  }
-  return t;
+KIE_HD int32_t lm_batches(const Shape& s, int32_t w, int32_t v) { return wave_batches(stage_geo(s, ST_LM, w), v); }
+KIE_HD int64_t stream_tiles(const Shape& s, int32_t w, int32_t v) {
+  return ((int64_t)s.L * layer_batches(s, w, v) + lm_batches(s, w, v)) * kBatch;
 }
-KIE_HD int64_t wg_lm_tiles(const Shape& s, int32_t w) {
-  const int32_t n = s.stage_pairs(ST_LM);
-  return stage_tiles(split_end(n, s.nwg, w) - split_begin(n, s.nwg, w), s.stage_kt(ST_LM));
-}
-KIE_HD int64_t wg_token_tiles(const Shape& s, int32_t w) { return s.L * wg_layer_tiles(s, w) + wg_lm_tiles(s, w); }
 
 // Source rows of global pair gp of a stage. mat selects the matrix: for QKV 0 = Wq, 1 = Wk, 2 = Wv.
 KIE_HD void pair_rows(const Shape& s, int st, int32_t gp, int* mat, int32_t* ra, int32_t* rb) {
@@ -182,7 +179,7 @@ KIE_HD Exch exch_layout(const Shape& s) {
 }
 
 // Workspace (bytes, 256-aligned pieces): exchange words, RoPE table [max_seq][hd/2] of (cos,sin),
-// per-WG weight-stream base (in tiles), error word, norm gains [L][2][d] + final [d] (bf16).
+// per-stream base (in tiles, [nwg][8] + total), error word, norm gains [L][2][d] + final [d] (bf16).
 struct Workspace {
   int64_t exch, rope, wbase, err, norms, trace, end;
 };
@@ -193,19 +190,20 @@ KIE_HD Workspace workspace_layout(const Shape& s) {
   int64_t o = 0;
   w.exch = o; o = align256(o + exch_layout(s).end * 8);
   w.rope = o; o = align256(o + (int64_t)s.max_seq * (s.hd / 2) * 8);
-  w.wbase = o; o = align256(o + (int64_t)(s.nwg + 1) * 8);
+  w.wbase = o; o = align256(o + ((int64_t)s.nwg * kWaves + 1) * 8);
   w.err = o; o = align256(o + 64);
   w.norms = o; o = align256(o + ((int64_t)s.L * 2 + 1) * s.d * 2);
-  w.trace = o; o = align256(o + (int64_t)s.nwg * (kThreads / kWave) * kTraceWords * 8);
+  w.trace = o; o = align256(o + (int64_t)s.nwg * kWaves * kTraceWords * 8);
   w.end = o;
   return w;
 }
 
-// Packed image: for each WG its token stream (L layers x [QKV,O,GU,DN] then LM) of tiles,
-// then the embedding table [V][d] bf16 as is.
+// Packed image: the streams of (WG 0, wave 0), (WG 0, wave 1), ..., (WG nwg-1, wave 7), then the
+// embedding table [V][d] bf16 as is.
 KIE_HD int64_t packed_stream_tiles(const Shape& s) {
   int64_t t = 0;
-  for (int32_t w = 0; w < s.nwg; ++w) t += wg_token_tiles(s, w);
+  for (int32_t w = 0; w < s.nwg; ++w)
+    for (int32_t v = 0; v < kWaves; ++v) t += stream_tiles(s, w, v);
   return t;
 }
 KIE_HD int64_t packed_embed_offset(const Shape& s) { return packed_stream_tiles(s) * kTileBytes; }

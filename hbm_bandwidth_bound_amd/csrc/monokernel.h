@@ -9,21 +9,21 @@ namespace kie {
 
 // device error word bits
 enum : uint32_t {
-  KERR_PRODUCER = 1u << 0,   // a producer wave's wait timed out
-  KERR_CONSUMER = 1u << 1,   // a consumer wave's wait timed out
+  KERR_TIMEOUT = 1u << 0,    // a wait for another workgroup's data timed out
+  KERR_RESERVED = 1u << 1,
   KERR_BAD_TOKEN = 1u << 2,  // an input token id was out of range (it was replaced by 0)
 };
 
 struct KParams {
   Shape s;
   Exch exo;
-  const uint8_t* packed;     // tile streams of all WGs
+  const uint8_t* packed;     // tile streams of all waves
   const uint16_t* embed;     // [V][d] bf16 (inside the packed image)
   const uint16_t* norms;     // [L][2][d] + [d] bf16 (in the workspace)
   uint16_t* kv;              // [L][2][nkv][max_seq][hd] bf16
   uint64_t* ex;              // exchange words
   const float2* rope;        // [max_seq][hd/2] (cos, sin)
-  const int64_t* wbase;      // [nwg] first tile of each WG's stream
+  const int64_t* wbase;      // [nwg * 8 + 1] first tile of each wave's stream (and the total)
   uint32_t* err;             // device error word
   uint64_t* trace;           // [nwg][8 waves][16] cycle counters (written by KIE_TRACE builds only)
   const int32_t* first_tok;  // [1]
@@ -34,20 +34,18 @@ struct KParams {
   int32_t pos0, n_steps;
   uint32_t epoch0;           // exchange tag of step s is epoch0 + s (never 0)
   int32_t lm_last_only;      // run the LM head and sampler only on the last step (prompt pass)
-  int32_t ring_slots;
   int64_t timeout_ticks;     // per wait, in s_memrealtime ticks (100 MHz)
 };
 
 typedef void (*KernelFn)(KParams);
 KernelFn decode_kernel_for(int group, int head_dim);
-int32_t lds_bytes_for(const Shape& s, int32_t ring);
-int32_t max_ring_slots(const Shape& s, int32_t lds_limit);
+int32_t lds_bytes_for(const Shape& s);
 
 // set-up kernels (pack.hip)
 struct PackArgs {
   Shape s;
   uint8_t* packed;
-  const int64_t* wbase;  // device [nwg]
+  const int64_t* wbase;  // device [nwg * 8]
   int32_t layer;         // 0..L-1, or L for the LM head
   const uint16_t *wq, *wk, *wv, *wo, *wgate, *wup, *wdown;  // layer matrices (layer < L)
   const uint16_t* lm_head;                                   // layer == L

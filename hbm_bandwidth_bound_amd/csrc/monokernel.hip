@@ -4,29 +4,30 @@
 // 《突破内存墙：在标准 GPU 上实现 3,000 tokens/s 的推理速度》, "The Monokernel Runtime"; aikraft.ru
 // «3000 токенов в секунду…», §04 "Моноядро": one resident GPU program covering MatMul,
 // attention, normalisation and sampling, with tight control of synchronisation, prefetch and
-// execution order). The design below is this library's own for CDNA4; the pages only say that the
-// vendor's kernels exist.
+// execution order). The design below is this library's own for CDNA4; the pages only say that
+// such kernels exist.
 //
 // Grid: one 512-thread workgroup (WG) per compute unit, all co-resident (cooperative launch).
-// Each WG runs two kinds of waves:
-//   * 4 producer waves stream the WG's packed weight slice -- and its share of the KV cache --
-//     from HBM into a ring of 1 KiB tiles in LDS, as far ahead as the ring allows. Weights do
-//     not depend on activations, so the HBM stream keeps flowing while the consumers wait for
-//     the inputs of the next stage (the prefetch across synchronisation points the pages name).
-//   * 4 consumer waves wait for a stage's input vector, then reduce the ring's tiles against it
-//     (fp32 FMA on widened bf16 weights), and publish their outputs.
-// Producers publish one progress counter each ("my tiles below index 4m+p are in the ring") and
-// consumers one watermark each ("I have read all my tiles below index W"); both are updated
-// once per batch of tiles.
+// Every one of the 8 waves streams its own contiguous slice of the packed weights from HBM into
+// registers with 16-byte-per-lane buffer loads, one batch of 8 KiB ahead of the batch it is
+// reducing. That batch is issued before the wave waits for the inputs of the next stage, so the
+// weight stream keeps flowing across every synchronisation point (the prefetch across
+// synchronisation points the pages call for); 64 KiB in flight per CU keep the HBM pipe busy.
+// GEMV arithmetic: a lane holds 4 bf16 weights of each of two rows at the same k, so one 16-byte
+// LDS read of the fp32 stage input feeds 8 weights of two rows; the weights are widened to fp32
+// and accumulated with fp32 FMA (the unit has VALU to spare at the streaming rate).
 // Inter-WG exchange uses 64-bit tagged words (fp32 value << 32 | epoch) written and read with
-// agent-scope atomics, so a reader knows a word is current by its tag alone: no grid barrier,
-// no flag round trip, no L2 flush. Epochs are unique per decode step and buffers are per layer.
+// agent-scope atomics, so a reader knows a word is current by its tag alone: no grid barrier, no
+// flag round trip, no cache flush. Epochs are unique per decode step and buffers are per layer.
+// Inside a WG the waves meet at the hardware barrier with LDS-only fences, which never wait for
+// the weight loads in flight.
 //
-// Per layer the stages are: QKV (+RMSNorm, RoPE) -> attention over a chunk of positions of one
-// KV head (split-K: scores, then softmax-weighted values) -> merge of the chunk partials -> O
-// (+residual) -> gate/up (+RMSNorm, SwiGLU) -> down (+residual). Then the final RMSNorm + LM
-// head and the sampler.
+// Per layer: RMSNorm -> QKV (+RoPE) -> attention over a chunk of positions of one KV head
+// (split-K; online softmax per wave, waves merged in LDS) -> merge of the chunk partials ->
+// O (+residual) -> RMSNorm -> gate/up (SwiGLU) -> down (+residual). Then the final RMSNorm, the
+// LM head and the sampler.
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "device_common.h"
@@ -42,9 +43,8 @@ namespace kie {
 #define TR_NOW() 0ull
 #endif
 enum TraceSlot : int {
-  TC_WAIT_TILE = 0, TC_FETCH = 1, TC_CSYNC = 2, TC_GEMV = 3, TC_ATT = 4, TC_MERGE = 5, TC_TOTAL = 6, TC_TILES = 7,
-  TC_SAMPLE = 8, TC_NORM = 9,
-  TP_WAIT_FREE = 0, TP_WRITE = 1, TP_GATE = 2, TP_ISSUE = 3, TP_TOTAL = 6, TP_TILES = 7
+  T_FETCH = 0, T_GEMV = 1, T_FIN = 2, T_ATT = 3, T_MERGE = 4, T_BAR = 5, T_TOTAL = 6, T_BATCHES = 7,
+  T_NORM = 8, T_SAMPLE = 9
 };
 struct Tracer {
 #ifdef KIE_TRACE
@@ -67,117 +67,48 @@ struct Tracer {
 // LDS layout
 // ------------------------------------------------------------------------------------------
 struct Lds {
-  uint8_t* ring;      // R x 1 KiB
-  float* act;         // stage input vector (fp32); during attention: q, k_p, v_p, scores
-  float* xres;        // residual stream of the current layer (fp32, d)
-  float* scr;         // scratch for reductions / attention partials / sampler
-  float* stage;       // per consumer wave: the stage outputs of its pairs, published after the stage
-  float2* rope;       // (cos, sin) of the current position, hd/2 entries
-  uint32_t* ctl;      // control words
+  float* act;      // GEMV input of the current stage (fp32)
+  float* xres;     // residual stream of the current layer (fp32, d)
+  float* part;     // [kMaxUnits][2] per-unit dot products of the current stage
+  float* scr;      // attention / merge / reduction scratch
+  float* q;        // attention: the group's queries [G][hd], the current k [hd] and v [hd]
+  float2* rope;    // (cos, sin) of the current position, hd/2 entries
+  uint32_t* ctl;   // control words
 };
-enum Ctl : int {
-  C_BAR = 0,    // consumer barrier counter
-  C_STEP = 1,   // step the consumers have started
-  C_ABORT = 2,  // set on any failure in this WG
-  C_DONE = 4,   // [4] per producer p: its tiles 4m+p with m below this value are in the ring
-  C_WM = 8,     // [4] per consumer: every one of its tiles below this stream index has been read
-  C_COUNT = 16
-};
-constexpr int kStageWords = 128;  // per consumer wave: at most 64 pairs per wave and stage
+enum Ctl : int { C_ABORT = 0, C_COUNT = 4 };
 
-__host__ __device__ inline int32_t att_scores_max(const Shape& s) { return s.group() * att_chunk_len(s, s.max_seq); }
 __host__ __device__ inline int32_t act_floats(const Shape& s) {
   int32_t a = s.d;
   if (s.qdim() > a) a = s.qdim();
   if (s.F > a) a = s.F;
-  const int32_t att = (s.group() + 2) * s.hd + att_scores_max(s);
-  if (att > a) a = att;
-  return (a + 3) & ~3;
+  return a;
 }
 __host__ __device__ inline int32_t scr_floats(const Shape& s) {
-  int32_t a = kConsumerWaves * s.group() * (s.hd + 2);
-  if (8 * kMergeDims * 3 > a) a = 8 * kMergeDims * 3;
+  int32_t a = kWaves * s.group() * (s.hd + 2);
+  if (16 * kMergeDims * 3 > a) a = 16 * kMergeDims * 3;
   if (2 * s.nwg > a) a = 2 * s.nwg;
   if (a < 64) a = 64;
   return (a + 3) & ~3;
 }
-__host__ __device__ inline int32_t lds_fixed_bytes(const Shape& s) {
-  return (act_floats(s) + s.d + scr_floats(s) + kConsumerWaves * kStageWords + s.hd) * 4 + C_COUNT * 4;
+int32_t lds_bytes_for(const Shape& s) {
+  return (act_floats(s) + s.d + 2 * kMaxUnits + scr_floats(s) + (s.group() + 2) * s.hd + s.hd) * 4 + C_COUNT * 4;
 }
-int32_t lds_bytes_for(const Shape& s, int32_t ring) { return ring * kTileBytes + lds_fixed_bytes(s); }
-int32_t max_ring_slots(const Shape& s, int32_t lds_limit) {
-  int32_t r = (lds_limit - lds_fixed_bytes(s)) / kTileBytes;
-  r &= ~7;
-  if (r > 128) r = 128;
-  return r;
-}
-
-__device__ __forceinline__ Lds lds_map(uint8_t* smem, const Shape& s, int32_t R) {
+__device__ __forceinline__ Lds lds_map(uint8_t* smem, const Shape& s) {
   Lds L;
   uint8_t* p = smem;
-  L.ring = p; p += (size_t)R * kTileBytes;
   L.act = (float*)p; p += (size_t)act_floats(s) * 4;
   L.xres = (float*)p; p += (size_t)s.d * 4;
+  L.part = (float*)p; p += (size_t)2 * kMaxUnits * 4;
   L.scr = (float*)p; p += (size_t)scr_floats(s) * 4;
-  L.stage = (float*)p; p += (size_t)kConsumerWaves * kStageWords * 4;
+  L.q = (float*)p; p += (size_t)(s.group() + 2) * s.hd * 4;
   L.rope = (float2*)p; p += (size_t)s.hd * 4;
   L.ctl = (uint32_t*)p;
   return L;
 }
 
 // ------------------------------------------------------------------------------------------
-// Per-WG plan and the token stream's segments
+// Attention work of this WG at context length n = pos + 1: KV head j over position chunk `chunk`.
 // ------------------------------------------------------------------------------------------
-struct Plan {
-  int32_t w;
-  int32_t pb[ST_COUNT];   // first global pair of each stage
-  int32_t np[ST_COUNT];   // pairs owned
-  int32_t kt[ST_COUNT];   // k-tiles per pair
-  int32_t pre[ST_COUNT];  // tile offset of the stage inside one layer's weight stream (LM: 0)
-  int32_t t_layer;        // weight tiles per layer
-  int64_t wbase;          // first tile of this WG in the packed image
-};
-
-// GEMV inputs are stored in LDS permuted so that lane l's 8 inputs of k-tile j are two 16-byte
-// rows at (j, half h, lane l): element k = 256 j + 8 l + t lives at 256 j + 128 (t >> 2) + 4 l +
-// (t & 3). Each ds_read_b128 of a wave then touches 512 contiguous bytes (no bank conflicts).
-__device__ __forceinline__ int32_t act_perm(int32_t k) {
-  return (k & ~255) | ((k & 4) << 5) | ((k & 248) >> 1) | (k & 3);
-}
-
-// Per-stage fields selected through a switch, so that the arrays stay in registers.
-__device__ __forceinline__ int32_t pick(const int32_t* a, int st) {
-  switch (st) {
-    case ST_QKV: return a[ST_QKV];
-    case ST_O: return a[ST_O];
-    case ST_GU: return a[ST_GU];
-    case ST_DN: return a[ST_DN];
-    default: return a[ST_LM];
-  }
-}
-
-__device__ __forceinline__ Plan make_plan(const KParams& P, int32_t w) {
-  Plan pl;
-  pl.w = w;
-  int32_t acc = 0;
-  for (int st = 0; st < ST_COUNT; ++st) {
-    const int32_t n = P.s.stage_pairs(st);
-    pl.pb[st] = split_begin(n, P.s.nwg, w);
-    pl.np[st] = split_end(n, P.s.nwg, w) - pl.pb[st];
-    pl.kt[st] = P.s.stage_kt(st);
-    if (st <= ST_DN) {
-      pl.pre[st] = acc;
-      acc += pl.np[st] * pl.kt[st];
-    } else {
-      pl.pre[st] = 0;
-    }
-  }
-  pl.t_layer = acc;
-  pl.wbase = P.wbase[w];
-  return pl;
-}
-
-// Attention work of this WG at context length n (= pos + 1).
 struct Att {
   int32_t j, chunk, c0, c1, ncache, nkt, has_p, cs, nch;
 };
@@ -209,38 +140,8 @@ __device__ __forceinline__ bool step_has_lm(const KParams& P, int32_t step) {
   return !P.lm_last_only || step == P.n_steps - 1;
 }
 
-// Segment q of a step's stream: q = 6 l + k with k 0 QKV, 1 K rows, 2 V rows, 3 O, 4 gate/up,
-// 5 down; q = 6 L is the LM head. Every segment is one linear range of 1 KiB tiles.
-struct SegD {
-  const uint8_t* base;  // first tile
-  int32_t len;          // tiles
-  int32_t kv;           // K/V rows (the last tile may be partly past the cached positions)
-  int32_t nval_last;    // lanes of the last tile holding data (64 for weights)
-};
-__device__ __forceinline__ SegD seg_desc(const KParams& P, const Plan& pl, const Att& at, int32_t step, int32_t q) {
-  SegD g;
-  const Shape& s = P.s;
-  g.kv = 0;
-  g.nval_last = kWave;
-  if (q == 6 * s.L) {
-    g.base = P.packed + (size_t)(pl.wbase + (int64_t)s.L * pl.t_layer) * kTileBytes;
-    g.len = step_has_lm(P, step) ? pl.np[ST_LM] * pl.kt[ST_LM] : 0;
-    return g;
-  }
-  const int32_t l = q / 6, k = q % 6;
-  if (k == 1 || k == 2) {
-    g.kv = 1;
-    g.base = (const uint8_t*)(P.kv + kv_offset(s, l, k - 1, at.j, at.c0));
-    g.len = at.nkt;
-    const int32_t ppt = att_pos_per_tile(s);
-    g.nval_last = (at.ncache - (at.nkt - 1) * ppt) * (s.hd / 8);
-    return g;
-  }
-  const int st = k == 0 ? ST_QKV : (k == 3 ? ST_O : (k == 4 ? ST_GU : ST_DN));
-  g.base = P.packed + (size_t)(pl.wbase + (int64_t)l * pl.t_layer + pick(pl.pre, st)) * kTileBytes;
-  g.len = pick(pl.np, st) * pick(pl.kt, st);
-  return g;
-}
+// A token id that indexes memory is always kept inside [0, V).
+__device__ __forceinline__ int32_t clamp_token(int32_t t, int32_t V) { return t < 0 ? 0 : (t >= V ? V - 1 : t); }
 
 // ------------------------------------------------------------------------------------------
 // Failure handling: every wait is bounded; on expiry the WG records an error and stops.
@@ -249,15 +150,14 @@ __device__ __forceinline__ void raise_error(const KParams& P, const Lds& L, uint
   lds_st(&L.ctl[C_ABORT], 1u);
   __hip_atomic_fetch_or(P.err, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// LDS word read by the whole wave (same address): the value is made wave-uniform so that every
-// decision taken on it is a scalar branch.
 __device__ __forceinline__ uint32_t lds_ld_u(const uint32_t* p) { return __builtin_amdgcn_readfirstlane(lds_ld(p)); }
 __device__ __forceinline__ bool aborted(const Lds& L) { return lds_ld_u(&L.ctl[C_ABORT]) != 0; }
+__device__ __forceinline__ bool global_error(const KParams& P) {
+  return __builtin_amdgcn_readfirstlane(__hip_atomic_load(P.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0;
+}
 
-// Bounded spin: call expired() after every unsuccessful poll. Every 256th call it checks the
-// WG's abort flag and the elapsed time of this wait (wave-uniform; no global memory access, so
-// the compiler never has to drain outstanding stores inside an LDS wait loop). Waits on global
-// memory additionally watch the grid's error word (global_error()).
+// Bounded spin: call expired() after every unsuccessful poll. Every 256th call it checks the WG's
+// abort flag and the elapsed time of this wait (wave-uniform).
 struct Waiter {
   uint32_t spins = 0;
   uint64_t start = 0;
@@ -272,585 +172,412 @@ struct Waiter {
     return t - start > (uint64_t)P.timeout_ticks;
   }
 };
-__device__ __forceinline__ bool global_error(const KParams& P) {
-  return __builtin_amdgcn_readfirstlane(__hip_atomic_load(P.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0;
+
+// Barrier of the WG's 8 waves. The fences order LDS only, so weight loads stay in flight.
+__device__ __forceinline__ void bar() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// argmax candidate order: larger value first, then the lower index
+__device__ __forceinline__ bool better(float v, int32_t i, float bv, int32_t bi) {
+  return v > bv || (v == bv && i < bi);
 }
 
 // ------------------------------------------------------------------------------------------
-// Producer waves
+// One wave's state: its weight stream, the batch in flight, the WG's stage geometry.
 // ------------------------------------------------------------------------------------------
-constexpr int kProdBatch = 8;
-
-struct PBatch {
-  uint32_t first;     // stream index of the batch's first tile (the others follow at stride 4)
-  int32_t n;          // tiles in the batch
-  int32_t nval_last;  // lanes of the last tile holding data
-};
-
-// Producer wave pw handles the WG's stream tiles pw, pw+4, pw+8, ... . It walks the segments of
-// each step; within a segment its tiles form batches of up to 8 that are loaded with 8
-// unconditional 16-byte-per-lane loads. Two batches are in flight: while batch X is loading,
-// batch Y (issued before) is written into the ring once the consumers' watermarks show that the
-// slots' previous tiles have been read. K/V rows of step s are only loaded once the consumers
-// have started step s (every row they read is final by then).
-__device__ __forceinline__ void producer(const KParams& P, const Lds& L, const Plan& pl, int pw, int lane) {
-  const uint32_t R = (uint32_t)P.ring_slots;
-  const Shape& s = P.s;
-  Tracer tr;
-  const uint64_t t_start = TR_NOW();
-  bool fail = false;
-  v4u bufA[kProdBatch], bufB[kProdBatch];
-  PBatch ba, bb;
-  ba.first = bb.first = 0;
-  ba.n = bb.n = 0;
-  ba.nval_last = bb.nval_last = kWave;
-  bool pend_a = false, pend_b = false;  // issued and not yet written
-
-  auto write = [&](const PBatch& b, const v4u* buf) {
-    const uint32_t last = b.first + (uint32_t)(4 * (b.n - 1));
-    // every slot of the batch is free once all consumers have read past (last - R)
-    if (last >= R) {
-      const uint64_t t0 = TR_NOW();
-      Waiter wt;
-      for (;;) {
-        const uint32_t w0 = lds_ld(&L.ctl[C_WM + 0]), w1 = lds_ld(&L.ctl[C_WM + 1]);
-        const uint32_t w2 = lds_ld(&L.ctl[C_WM + 2]), w3 = lds_ld(&L.ctl[C_WM + 3]);
-        uint32_t m = w0 < w1 ? w0 : w1;
-        m = m < w2 ? m : w2;
-        m = m < w3 ? m : w3;
-        m = __builtin_amdgcn_readfirstlane(m);
-        if (m + R > last) break;
-        __builtin_amdgcn_s_sleep(1);
-        if (wt.expired(P, L)) {
-          fail = true;
-          return;
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-      tr.add(TP_WAIT_FREE, TR_NOW() - t0);
-    }
-    const uint64_t t0 = TR_NOW();
-    uint32_t slot = b.first % R;
-#pragma unroll
-    for (int k = 0; k < kProdBatch; ++k) {
-      if (k < b.n) {
-        v4u v = buf[k];
-        if (k == b.n - 1 && lane >= b.nval_last) v = v4u{0u, 0u, 0u, 0u};
-        *(v4u*)(L.ring + slot * kTileBytes + lane * 16) = v;
-        slot += kProducerWaves;
-        if (slot >= R) slot -= R;
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    if (lane == 0) lds_st(&L.ctl[C_DONE + pw], (last >> 2) + 1);
-    tr.add(TP_WRITE, TR_NOW() - t0);
-    tr.add(TP_TILES, (uint64_t)b.n);
-  };
-  // 8 loads, always issued (slots beyond n are never written); lanes of a last K/V tile past the
-  // cached positions re-read its first row (zeroed on write)
-  auto issue = [&](v4u* buf, const uint8_t* base, uint32_t t, int32_t n, bool last_partial, int32_t nval_last) {
-#pragma unroll
-    for (int k = 0; k < kProdBatch; ++k) {
-      const uint32_t tk = k < n ? t + 4u * (uint32_t)k : t;
-      // unused slots (k >= n) read only the first row of the batch's first tile, which exists
-      const bool masked = k >= n || (last_partial && k == n - 1 && lane >= nval_last);
-      const uint8_t* src = base + (size_t)tk * kTileBytes + (masked ? 0 : lane * 16);
-      buf[k] = __builtin_nontemporal_load((const v4u*)src);
-    }
-  };
-
-  uint32_t spos = 0;  // stream index of the current segment's first tile
-  for (int32_t step = 0; step < P.n_steps && !fail; ++step) {
-    const Att at = att_info(s, pl.w, P.pos0 + step);
-    for (int32_t q = 0; q <= 6 * s.L && !fail; ++q) {
-      const SegD g = seg_desc(P, pl, at, step, q);
-      if (g.len == 0) continue;
-      if (g.kv && step > 0 && (int32_t)lds_ld_u(&L.ctl[C_STEP]) < step) {
-        // flush what is in flight (oldest first), then wait until the consumers have started
-        // this step
-        if (pend_a && pend_b && bb.first < ba.first) {
-          write(bb, bufB);
-          pend_b = false;
-        }
-        if (pend_a && !fail) { write(ba, bufA); pend_a = false; }
-        if (pend_b && !fail) { write(bb, bufB); pend_b = false; }
-        const uint64_t t0 = TR_NOW();
-        Waiter wt;
-        while (!fail && (int32_t)lds_ld_u(&L.ctl[C_STEP]) < step) {
-          __builtin_amdgcn_s_sleep(2);
-          if (wt.expired(P, L)) fail = true;
-        }
-        tr.add(TP_GATE, TR_NOW() - t0);
-        if (fail) break;
-      }
-      uint32_t t = ((uint32_t)pw - spos) & 3u;  // this producer's first tile in the segment
-      while (t < (uint32_t)g.len && !fail) {
-        const int32_t left = (int32_t)(((uint32_t)g.len - t + 3u) >> 2);
-        const int32_t n = left < kProdBatch ? left : kProdBatch;
-        const bool lastp = g.kv && (t + 4u * (uint32_t)(n - 1) == (uint32_t)g.len - 1u) && g.nval_last < kWave;
-        // the two buffers alternate; the older pending batch is written after the new issue
-        if (!pend_a) {
-          issue(bufA, g.base, t, n, lastp, g.nval_last);
-          ba.first = spos + t;
-          ba.n = n;
-          ba.nval_last = lastp ? g.nval_last : kWave;
-          pend_a = true;
-          if (pend_b) { write(bb, bufB); pend_b = false; }
-        } else {
-          issue(bufB, g.base, t, n, lastp, g.nval_last);
-          bb.first = spos + t;
-          bb.n = n;
-          bb.nval_last = lastp ? g.nval_last : kWave;
-          pend_b = true;
-          write(ba, bufA);
-          pend_a = false;
-        }
-        t += 4u * (uint32_t)n;
-      }
-      spos += (uint32_t)g.len;
-    }
-  }
-  // drain, oldest first
-  if (!fail && pend_a && pend_b && bb.first < ba.first) {
-    write(bb, bufB);
-    pend_b = false;
-  }
-  if (!fail && pend_a) write(ba, bufA);
-  if (!fail && pend_b) write(bb, bufB);
-  tr.add(TP_TOTAL, TR_NOW() - t_start);
-  tr.flush(P.trace + ((int64_t)pl.w * (kThreads / kWave) + pw) * kTraceWords, lane);
-  if (fail) raise_error(P, L, KERR_PRODUCER);
-}
-
-// ------------------------------------------------------------------------------------------
-// Consumer waves
-// ------------------------------------------------------------------------------------------
-struct Cons {
+struct Wk {
   const KParams& P;
   const Lds& L;
-  const Plan& pl;
-  int c;     // consumer wave 0..3 (wave-uniform)
-  int lane;
-  int tid;   // 0..255 among consumer threads
-  uint32_t bar_target;
+  int32_t w, v, lane, tid;
   bool fail;
   Tracer tr;
-  __device__ __forceinline__ Cons(const KParams& p, const Lds& l, const Plan& q, int c_, int lane_)
-      : P(p), L(l), pl(q), c(c_), lane(lane_), tid(c_ * kWave + lane_), bar_target(0), fail(false) {}
+  StageGeo g[ST_COUNT];
+  int32_t nb[ST_COUNT];  // this wave's batches per stage
+  int32_t layer_b, lm_b;
+  const uint8_t* stream;  // this wave's first tile
+  v4u nxt[kBatch];        // the next batch of the stream (loads in flight)
+  int32_t pidx, pstep;    // that batch: index in its step's stream, and the step
 
-  // barrier of the 4 consumer waves (LDS counter; the producers are not involved)
-  __device__ __forceinline__ void csync() {
-    fail = __builtin_amdgcn_ballot_w64(fail) != 0;  // one lane's failure is the wave's
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    if (lane == 0) __hip_atomic_fetch_add(&L.ctl[C_BAR], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    bar_target += kConsumerWaves;
-    Waiter wt;
+  __device__ __forceinline__ Wk(const KParams& p, const Lds& l, int32_t w_, int32_t v_, int32_t lane_)
+      : P(p), L(l), w(w_), v(v_), lane(lane_), tid(v_ * kWave + lane_), fail(false) {
+    layer_b = 0;
+    for (int st = 0; st < ST_COUNT; ++st) {
+      g[st] = stage_geo(P.s, st, w);
+      nb[st] = wave_batches(g[st], v);
+      if (st <= ST_DN) layer_b += nb[st];
+    }
+    lm_b = nb[ST_LM];
+    stream = P.packed + (size_t)P.wbase[w * kWaves + v] * kTileBytes;
+    pidx = -1;
+    pstep = 0;
+  }
+
+  // ------------------------------------------------------------ weight stream
+  __device__ __forceinline__ int32_t step_batches(int32_t step) const {
+    return P.s.L * layer_b + (step_has_lm(P, step) ? lm_b : 0);
+  }
+  // advance (pidx, pstep) to the next batch of the launch; pstep == n_steps once there is none
+  __device__ __forceinline__ void advance() {
+    ++pidx;
+    while (pstep < P.n_steps && pidx >= step_batches(pstep)) {
+      pidx = 0;
+      ++pstep;
+    }
+  }
+  // 8 loads of batch (pidx, pstep); past the launch's last batch the resource is empty and the
+  // loads return zeros without touching memory.
+  __device__ __forceinline__ void issue(v4u* buf) {
+    const bool live = pstep < P.n_steps;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(stream + (live ? (size_t)pidx * kBatch * kTileBytes : 0), live ? kBatch * kTileBytes : 0);
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) buf[b] = load16(rs, (uint32_t)(lane * 16 + b * kTileBytes));
+  }
+  // the launch's first batch
+  __device__ __forceinline__ void start() {
+    advance();
+    issue(nxt);
+  }
+  // hand the batch in flight to the caller and issue the one after it
+  __device__ __forceinline__ void take(v4u* cur) {
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) cur[b] = nxt[b];
+    advance();
+    issue(nxt);
+  }
+
+  // ------------------------------------------------------------ GEMV of one stage
+  // Stage fields selected through a switch, so that the arrays stay in scalar registers.
+  __device__ __forceinline__ StageGeo geo_of(int st) const {
+    switch (st) {
+      case ST_QKV: return g[ST_QKV];
+      case ST_O: return g[ST_O];
+      case ST_GU: return g[ST_GU];
+      case ST_DN: return g[ST_DN];
+      default: return g[ST_LM];
+    }
+  }
+  __device__ __forceinline__ int32_t nb_of(int st) const {
+    switch (st) {
+      case ST_QKV: return nb[ST_QKV];
+      case ST_O: return nb[ST_O];
+      case ST_GU: return nb[ST_GU];
+      case ST_DN: return nb[ST_DN];
+      default: return nb[ST_LM];
+    }
+  }
+  // Batch b of this wave in stage gs, against the input in LDS: the two dot products of each unit
+  // u land in part[2u] and part[2u + 1].
+  __device__ __forceinline__ void reduce_batch(const StageGeo& gs, int32_t b, const v4u* cur) {
+    const int32_t lks = gs.ks == 8 ? 3 : (gs.ks == 4 ? 2 : (gs.ks == 2 ? 1 : 0));
+    {
+      float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+#pragma unroll
+      for (int sl = 0; sl < kBatch; ++sl) {
+        const int32_t us = sl >> lks, t = sl & (gs.ks - 1);
+        const int32_t u = v + kWaves * (b * gs.upb + us);
+        if (u < gs.nu) {
+          const int32_t j = (u % gs.S) * gs.ks + t;
+          const v4f x = *(const v4f*)(L.act + (size_t)j * kTileK + lane * 4);
+          const v4u wt = cur[sl];
+          a0 = fmaf(bf16lo(wt.x), x.x, a0);
+          a1 = fmaf(bf16hi(wt.x), x.y, a1);
+          a0 = fmaf(bf16lo(wt.y), x.z, a0);
+          a1 = fmaf(bf16hi(wt.y), x.w, a1);
+          b0 = fmaf(bf16lo(wt.z), x.x, b0);
+          b1 = fmaf(bf16hi(wt.z), x.y, b1);
+          b0 = fmaf(bf16lo(wt.w), x.z, b0);
+          b1 = fmaf(bf16hi(wt.w), x.w, b1);
+          if (t == gs.ks - 1) {
+            const float ya = wave_sum(a0 + a1), yb = wave_sum(b0 + b1);
+            if (lane == 0) {
+              L.part[2 * u] = ya;
+              L.part[2 * u + 1] = yb;
+            }
+            a0 = a1 = b0 = b1 = 0.f;
+          }
+        }
+      }
+    }
+  }
+  // After the stage's barrier: pair lp's outputs (the sum of its S units in a fixed order) go to
+  // fin(global pair, ya, yb).
+  template <typename Fin>
+  __device__ __forceinline__ void finalize(const StageGeo& gs, Fin fin) {
     const uint64_t t0 = TR_NOW();
-    while ((int32_t)(lds_ld_u(&L.ctl[C_BAR]) - bar_target) < 0) {
-      __builtin_amdgcn_s_sleep(1);
-      if (wt.expired(P, L)) {
-        fail = true;
-        break;
+    for (int32_t lp = tid; lp < gs.np; lp += kThreads) {
+      float ya = 0.f, yb = 0.f;
+      for (int32_t k = 0; k < gs.S; ++k) {
+        ya += L.part[2 * (lp * gs.S + k)];
+        yb += L.part[2 * (lp * gs.S + k) + 1];
       }
+      fin(gs.pb + lp, ya, yb);
     }
-    tr.add(TC_CSYNC, TR_NOW() - t0);
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    tr.add(T_FIN, TR_NOW() - t0);
   }
 
-  // Wait until the ring holds the NB tiles i, i+nr, ... (one read of the 4 producer counters).
-  template <int NB>
-  __device__ __forceinline__ void wait_ready(uint32_t i, uint32_t nr) {
-    const uint64_t t0 = TR_NOW();
-    bool waited = false;
-    Waiter wt;
-    for (;;) {
-      const uint32_t d0 = lds_ld(&L.ctl[C_DONE + 0]), d1 = lds_ld(&L.ctl[C_DONE + 1]);
-      const uint32_t d2 = lds_ld(&L.ctl[C_DONE + 2]), d3 = lds_ld(&L.ctl[C_DONE + 3]);
-      const uint32_t e0 = __builtin_amdgcn_readfirstlane(d0), e1 = __builtin_amdgcn_readfirstlane(d1);
-      const uint32_t e2 = __builtin_amdgcn_readfirstlane(d2), e3 = __builtin_amdgcn_readfirstlane(d3);
-      bool ok = true;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const uint32_t ib = i + (uint32_t)b * nr;
-        const uint32_t p = ib & 3u, need = (ib >> 2) + 1u;
-        const uint32_t have = p == 0 ? e0 : (p == 1 ? e1 : (p == 2 ? e2 : e3));
-        ok &= (int32_t)(have - need) >= 0;
-      }
-      if (ok) break;
-      waited = true;
-      __builtin_amdgcn_s_sleep(1);
-      if (wt.expired(P, L)) {
-        fail = true;
-        break;
-      }
-    }
-    if (waited) tr.add(TC_WAIT_TILE, TR_NOW() - t0);
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-  }
-  // every tile of this wave below stream index w has been read (its data are in registers)
-  __device__ __forceinline__ void watermark(uint32_t w) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    if (lane == 0) lds_st(&L.ctl[C_WM + c], w);
-  }
-  __device__ __forceinline__ uint32_t slot_of(uint32_t i) const { return i % (uint32_t)P.ring_slots; }
-  __device__ __forceinline__ const v4u* tile_ptr(uint32_t slot) const {
-    return (const v4u*)(L.ring + slot * kTileBytes + lane * 16);
-  }
-
-  // Gather n tagged words with the given epoch from src into LDS floats dst. Every consumer
-  // thread polls its words tid, tid+256, ... (all in flight at once), writes each value as soon
-  // as its tag is current, and re-polls only the missing ones. If want_ss, returns the sum of
-  // squares of the n values (fixed summation order) to every consumer thread.
-  // The consumer barrier below is reached by every consumer thread, whatever its word count.
-  __device__ __forceinline__ float fetch(const uint64_t* src, int n, float* dst, uint32_t epoch, bool want_ss,
-                                        bool permute = false) {
-    constexpr int KMAX = 16;
-    const uint64_t tf = TR_NOW();
-    for (int base = 0; base < n; base += KMAX * kConsumerThreads) {
-      const uint64_t* sp = src + base + tid;
-      float* dp = dst + base + tid;
-      uint32_t missing = 0;
-#pragma unroll
-      for (int k = 0; k < KMAX; ++k)
-        if (base + tid + k * kConsumerThreads < n) missing |= 1u << k;
-      uint64_t wv[KMAX];
-#pragma unroll
-      for (int k = 0; k < KMAX; ++k)
-        if (missing & (1u << k)) wv[k] = ld_x(sp + k * kConsumerThreads);
-      if (base == 0) csync();  // earlier readers of dst are done before it is overwritten
-      Waiter wt;
-      while (true) {
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k) {
-          if ((missing & (1u << k)) && (uint32_t)wv[k] == epoch) {
-            missing &= ~(1u << k);
-            const float v = __uint_as_float((uint32_t)(wv[k] >> 32));
-            if (permute)
-              dst[act_perm(base + tid + k * kConsumerThreads)] = v;
-            else
-              dp[k * kConsumerThreads] = v;
-          }
-        }
-        if (__builtin_amdgcn_ballot_w64(missing != 0) == 0 || fail) break;  // the whole wave is done
-        __builtin_amdgcn_s_sleep(1);
-        if (wt.expired(P, L) || ((wt.spins & 255u) == 0 && global_error(P))) {
-          fail = true;
-          break;
-        }
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k)
-          if (missing & (1u << k)) wv[k] = ld_x(sp + k * kConsumerThreads);
-      }
-    }
-    tr.add(TC_FETCH, TR_NOW() - tf);
-    float ss = 0.f;
-    if (want_ss) {
-      const uint64_t tn = TR_NOW();
-      for (int e = tid; e < n; e += kConsumerThreads) ss = fmaf(dst[e], dst[e], ss);
-      ss = block_sum(ss);
-      tr.add(TC_NORM, TR_NOW() - tn);
-    }
-    csync();
-    return ss;
-  }
-
-  // Gather up to three short ranges (query heads and the current K/V row) into LDS floats.
-  __device__ __forceinline__ void fetch3(const uint64_t* s0, int n0, float* d0, const uint64_t* s1, int n1, float* d1,
-                                         const uint64_t* s2, int n2, float* d2, uint32_t epoch) {
-    constexpr int KM = 8;
-    const uint64_t tf = TR_NOW();
-    const int ntot = n0 + n1 + n2;
-    for (int base = 0; base < ntot; base += KM * kConsumerThreads) {
-      uint32_t missing = 0;
-#pragma unroll
-      for (int k = 0; k < KM; ++k)
-        if (base + tid + k * kConsumerThreads < ntot) missing |= 1u << k;
-      uint64_t wv[KM];
-      auto reload = [&]() {
-#pragma unroll
-        for (int k = 0; k < KM; ++k) {
-          if (missing & (1u << k)) {
-            const int e = base + tid + k * kConsumerThreads;
-            const uint64_t* p = e < n0 ? s0 + e : (e < n0 + n1 ? s1 + (e - n0) : s2 + (e - n0 - n1));
-            wv[k] = ld_x(p);
-          }
-        }
-      };
-      reload();
-      if (base == 0) csync();
-      Waiter wt;
-      while (true) {
-#pragma unroll
-        for (int k = 0; k < KM; ++k) {
-          if ((missing & (1u << k)) && (uint32_t)wv[k] == epoch) {
-            missing &= ~(1u << k);
-            const int e = base + tid + k * kConsumerThreads;
-            float* d = e < n0 ? d0 + e : (e < n0 + n1 ? d1 + (e - n0) : d2 + (e - n0 - n1));
-            *d = __uint_as_float((uint32_t)(wv[k] >> 32));
-          }
-        }
-        if (__builtin_amdgcn_ballot_w64(missing != 0) == 0 || fail) break;
-        __builtin_amdgcn_s_sleep(1);
-        if (wt.expired(P, L) || ((wt.spins & 255u) == 0 && global_error(P))) {
-          fail = true;
-          break;
-        }
-        reload();
-      }
-    }
-    tr.add(TC_FETCH, TR_NOW() - tf);
-    csync();
-  }
-
-  // sum over the 256 consumer threads, in a fixed order; every consumer thread gets the result
-  __device__ __forceinline__ float block_sum(float v) {
-    float lo, hi;
-    half_wave_sums(v, &lo, &hi);
-    v = lo + hi;
-    csync();  // scr may still be read by a previous user
-    if (lane == 0) L.scr[c] = v;
-    csync();
+  // ------------------------------------------------------------ reductions
+  // sum over the WG's 512 threads in a fixed order; every thread gets the result
+  __device__ __forceinline__ float block_sum(float x) {
+    const float s = wave_sum(x);
+    if (lane == 0) L.scr[v] = s;
+    bar();
     float t = 0.f;
 #pragma unroll
-    for (int k = 0; k < kConsumerWaves; ++k) t += L.scr[k];
+    for (int k = 0; k < kWaves; ++k) t += L.scr[k];
+    bar();
     return t;
   }
 
-  // act[i] = (xres[i] * r) * g[i],  r = 1/sqrt(ss/d + eps)
-  __device__ __forceinline__ void rmsnorm_to_act(float ss, const uint16_t* g) {
-    const int d = P.s.d;
+  // ------------------------------------------------------------ exchange gathers
+  // Poll the tagged words addr(k) of this thread's slots k < KM with valid(k) until each carries
+  // `epoch`; got(k, value) receives every value once. All waves of the WG call it; the wait is
+  // bounded. k is a compile-time index after unrolling, so per-slot values stay in registers.
+  template <int KM, typename Valid, typename Addr, typename Got>
+  __device__ __forceinline__ void poll(uint32_t epoch, Valid valid, Addr addr, Got got) {
+    uint32_t missing = 0;
+#pragma unroll
+    for (int k = 0; k < KM; ++k)
+      if (valid(k)) missing |= 1u << k;
+    uint64_t wv[KM];
+#pragma unroll
+    for (int k = 0; k < KM; ++k)
+      if (missing & (1u << k)) wv[k] = ld_x(addr(k));
+    Waiter wt;
+    while (true) {
+#pragma unroll
+      for (int k = 0; k < KM; ++k) {
+        if ((missing & (1u << k)) && (uint32_t)wv[k] == epoch) {
+          missing &= ~(1u << k);
+          got(k, __uint_as_float((uint32_t)(wv[k] >> 32)));
+        }
+      }
+      if (__builtin_amdgcn_ballot_w64(missing != 0) == 0 || fail) break;
+      __builtin_amdgcn_s_sleep(1);
+      if (wt.expired(P, L) || ((wt.spins & 255u) == 0 && global_error(P))) {
+        fail = true;
+        raise_error(P, L, KERR_TIMEOUT);
+        break;
+      }
+#pragma unroll
+      for (int k = 0; k < KM; ++k)
+        if (missing & (1u << k)) wv[k] = ld_x(addr(k));
+    }
+  }
+  // n words into LDS floats dst; returns their sum of squares (fixed order) if want_ss.
+  // Ends with a barrier: dst is complete for every wave.
+  __device__ __forceinline__ float fetch_f32(const uint64_t* src, int32_t n, float* dst, uint32_t epoch,
+                                             bool want_ss) {
+    const uint64_t t0 = TR_NOW();
+    constexpr int KM = 8;
+    for (int32_t base = 0; base < n; base += KM * kThreads) {
+      const int32_t e0 = base + tid;
+      poll<KM>(
+          epoch, [&](int k) { return e0 + k * kThreads < n; }, [&](int k) { return src + e0 + k * kThreads; },
+          [&](int k, float x) { dst[e0 + k * kThreads] = x; });
+    }
+    tr.add(T_FETCH, TR_NOW() - t0);
+    float ss = 0.f;
+    if (want_ss) {
+      for (int32_t e = tid; e < n; e += kThreads) ss = fmaf(dst[e], dst[e], ss);  // this thread's own words
+      ss = block_sum(ss);
+    } else {
+      bar();
+    }
+    return ss;
+  }
+  // act = (xres * r) * g with r = 1 / sqrt(ss / d + eps). Ends with a barrier.
+  __device__ __forceinline__ void norm_to_act(float ss, const uint16_t* gain) {
+    const uint64_t t0 = TR_NOW();
+    const int32_t d = P.s.d;
     const float r = 1.0f / sqrtf(ss / (float)d + P.s.eps);
-    for (int i = tid; i < d; i += kConsumerThreads) {
-      const float gi = __uint_as_float((uint32_t)g[i] << 16);
-      L.act[act_perm(i)] = (L.xres[i] * r) * gi;
+    for (int32_t rec = tid; rec < d / 4; rec += kThreads) {
+      const v4f x = *(const v4f*)(L.xres + 4 * rec);
+      const uint2 gg = *(const uint2*)(gain + 4 * rec);
+      *(v4f*)(L.act + 4 * rec) = v4f{(x.x * r) * bf16lo(gg.x), (x.y * r) * bf16hi(gg.x), (x.z * r) * bf16lo(gg.y),
+                                     (x.w * r) * bf16hi(gg.y)};
     }
-    csync();
+    tr.add(T_NORM, TR_NOW() - t0);
+    bar();
   }
 
-  // ------------------------------------------------------------------ GEMV stage
-  // NB tiles of one pair: tiles i, i+nr, ... covering k-tiles j0 .. j0+NB-1.
-  template <int NB>
-  __device__ __forceinline__ void gemv_batch(uint32_t i, uint32_t nr, int32_t j0, float& a0, float& a1) {
-    wait_ready<NB>(i, nr);
-    v4u w[NB];
-    uint32_t slot = slot_of(i);
+  // argmax over the WG's threads (each holds a candidate); every thread gets the winner
+  __device__ __forceinline__ void block_argmax(float* bv, int32_t* bi) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      w[b] = *tile_ptr(slot);
-      slot += nr;
-      if (slot >= (uint32_t)P.ring_slots) slot -= (uint32_t)P.ring_slots;
-    }
-    v4f x0[NB], x1[NB];
-    const float* ap = L.act + j0 * kTileK + (lane & 31) * 4;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      x0[b] = *(const v4f*)(ap + b * kTileK);
-      x1[b] = *(const v4f*)(ap + b * kTileK + 128);
-    }
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      a0 = fmaf(bf16lo(w[b].x), x0[b].x, a0);
-      a1 = fmaf(bf16hi(w[b].x), x0[b].y, a1);
-      a0 = fmaf(bf16lo(w[b].y), x0[b].z, a0);
-      a1 = fmaf(bf16hi(w[b].y), x0[b].w, a1);
-      a0 = fmaf(bf16lo(w[b].z), x1[b].x, a0);
-      a1 = fmaf(bf16hi(w[b].z), x1[b].y, a1);
-      a0 = fmaf(bf16lo(w[b].w), x1[b].z, a0);
-      a1 = fmaf(bf16hi(w[b].w), x1[b].w, a1);
-    }
-    watermark(i + (uint32_t)(NB - 1) * nr + 1u);
-  }
-
-  __device__ __forceinline__ void gemv_pair(uint32_t i, uint32_t nr, int32_t kt, float& a0, float& a1) {
-    constexpr int B = 8;
-    int32_t j0 = 0;
-    for (; j0 + B <= kt; j0 += B, i += (uint32_t)B * nr) gemv_batch<B>(i, nr, j0, a0, a1);
-    switch (kt - j0) {  // remainder (kt is not a multiple of 8 for small K)
-      case 1: gemv_batch<1>(i, nr, j0, a0, a1); break;
-      case 2: gemv_batch<2>(i, nr, j0, a0, a1); break;
-      case 3: gemv_batch<3>(i, nr, j0, a0, a1); break;
-      case 4: gemv_batch<4>(i, nr, j0, a0, a1); break;
-      case 5: gemv_batch<5>(i, nr, j0, a0, a1); break;
-      case 6: gemv_batch<6>(i, nr, j0, a0, a1); break;
-      case 7: gemv_batch<7>(i, nr, j0, a0, a1); break;
-      default: break;
-    }
-  }
-
-  // Each consumer wave takes pairs lp = c, c+4, ...; per tile, lane l multiplies its 8 bf16
-  // weights by act[256 j + 8 (l mod 32) ...]; the two half-waves reduce to the pair's two dot
-  // products. val(gp, ya, yb) turns them into the pair's two outputs (e.g. RoPE, residual);
-  // they are staged in LDS and published by pub(gp, half, value) after the wave's last pair, all
-  // lanes storing at once (no exchange store inside the tile loop, so the compiler never drains
-  // outstanding stores there).
-  template <typename Val, typename Pub>
-  __device__ __forceinline__ void gemv(int st, uint32_t tile_base, Val val, Pub pub) {
-    const uint64_t tg = TR_NOW();
-    const int32_t np = pick(pl.np, st), kt = pick(pl.kt, st);
-    const int32_t pb = pick(pl.pb, st);
-    const int32_t full = np / kConsumerWaves;
-    float* stg = L.stage + c * kStageWords;
-    int32_t k = 0;
-    for (int32_t lp = c; lp < np; lp += kConsumerWaves, ++k) {
-      const int32_t r = lp / kConsumerWaves;
-      const uint32_t nr = r < full ? (uint32_t)kConsumerWaves : (uint32_t)(np - full * kConsumerWaves);
-      const uint32_t i = tile_base + (uint32_t)(r * kConsumerWaves * kt + c);  // tile j = 0 of the pair
-      float a0 = 0.f, a1 = 0.f;
-      gemv_pair(i, nr, kt, a0, a1);
-      if (fail) return;
-      float ya, yb;
-      half_wave_sums(a0 + a1, &ya, &yb);
-      const float2 o = val(pb + lp, ya, yb);
-      if (lane == 0) {
-        stg[2 * k] = o.x;
-        stg[2 * k + 1] = o.y;
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(*bv, o, kWave);
+      const int32_t oi = __shfl_xor(*bi, o, kWave);
+      if (better(ov, oi, *bv, *bi)) {
+        *bv = ov;
+        *bi = oi;
       }
     }
-    watermark(tile_base + (uint32_t)(np * kt));  // nothing of this stage is left for this wave
-    // publish: lane 2q+h stores output h of the wave's q-th pair
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    for (int32_t q0 = 0; q0 < k; q0 += kWave / 2) {
-      const int32_t q = q0 + (lane >> 1), h = lane & 1;
-      if (q < k) pub(pb + c + kConsumerWaves * q, h, stg[2 * q + h]);
+    if (lane == 0) {
+      L.scr[2 * v] = *bv;
+      L.scr[2 * v + 1] = __int_as_float(*bi);
     }
-    tr.add(TC_TILES, (uint64_t)k * kt);
-    tr.add(TC_GEMV, TR_NOW() - tg);
+    bar();
+    float bv2 = L.scr[0];
+    int32_t bi2 = __float_as_int(L.scr[1]);
+    for (int k = 1; k < kWaves; ++k) {
+      const float ov = L.scr[2 * k];
+      const int32_t oi = __float_as_int(L.scr[2 * k + 1]);
+      if (better(ov, oi, bv2, bi2)) {
+        bv2 = ov;
+        bi2 = oi;
+      }
+    }
+    bar();
+    *bv = bv2;
+    *bi = bi2;
   }
 };
 
 // ------------------------------------------------------------------------------------------
-// Attention for one KV head over this WG's chunk of positions: pass 1 computes the scores of
-// the chunk (K tiles), pass 2 the softmax-weighted sum of V rows (V tiles) with the chunk's
-// maximum; the 4 consumer waves' partial sums are added and one partial (acc[hd], m, l) per
-// query head of the group is published (exp2 domain; m is the chunk maximum).
+// Attention for KV head j over this WG's chunk of positions. Wave v takes the chunk's K/V tiles
+// v, v + 8, ...; each lane keeps an online softmax (exp2 domain) over the positions it sees, the
+// position rows of a wave are combined with shuffles and the 8 waves in LDS; one partial
+// (acc[hd], m, l) per query head of the group is published, m being the chunk maximum.
 // ------------------------------------------------------------------------------------------
 template <int G, int HD>
-__device__ __forceinline__ void attention_chunk(Cons& C, const Att& at, int32_t l, int32_t pos, uint32_t tile_base,
-                                                uint32_t epoch) {
-  const KParams& P = C.P;
-  const Lds& L = C.L;
+__device__ __forceinline__ void attention(Wk& K, const Att& at, int32_t l, int32_t pos, uint32_t ep) {
+  const KParams& P = K.P;
+  const Lds& L = K.L;
   const Shape& s = P.s;
+  const Exch& X = P.exo;
   constexpr int LPP = HD / 8;    // lanes per position
   constexpr int PPT = 64 / LPP;  // positions per tile
-  const int lane = C.lane;
+  constexpr int AB = 2;  // K (and V) tiles per batch
+  const int lane = K.lane, v = K.v;
   const int lpos = lane / LPP, dg = lane % LPP;
-  const float* q = L.act;              // [G][HD]
-  const float* kp = L.act + G * HD;    // current position's k (fp32, after RoPE)
-  const float* vp = L.act + (G + 1) * HD;
-  float* sc = L.act + (G + 2) * HD;    // scores [G][positions of the chunk]
-  const int32_t npos = at.ncache + (at.has_p ? 1 : 0);
-  const float scale = 1.4426950408889634f / sqrtf((float)HD);
+  const int32_t ntw = at.nkt > v ? (at.nkt - v + kWaves - 1) / kWaves : 0;  // this wave's tiles
+  const int32_t nbw = (ntw + AB - 1) / AB;
+  const uint32_t kvbytes = (uint32_t)at.ncache * HD * 2;  // lanes past the cached rows read zeros
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(P.kv + kv_offset(s, l, 0, at.j, at.c0), kvbytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(P.kv + kv_offset(s, l, 1, at.j, at.c0), kvbytes);
+  auto kv_issue = [&](int32_t bi, v4u* kb, v4u* vb) {
+#pragma unroll
+    for (int e = 0; e < AB; ++e) {
+      const int32_t i = bi * AB + e;
+      if (i < ntw) {
+        const uint32_t off = (uint32_t)((v + kWaves * i) * kTileBytes + lane * 16);
+        kb[e] = load16(krs, off);
+        vb[e] = load16(vrs, off);
+      } else {
+        kb[e] = v4u{0u, 0u, 0u, 0u};
+        vb[e] = v4u{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  v4u kn[AB], vn[AB];
+  if (nbw > 0) kv_issue(0, kn, vn);  // cached rows do not depend on this step: load before the inputs
 
+  // inputs: the group's queries, then the current position's k and v when it lies in this chunk
+  {
+    const uint64_t t0 = TR_NOW();
+    const uint64_t* qsrc = P.ex + X.q + (int64_t)l * s.qdim() + (int64_t)at.j * G * HD;
+    const uint64_t* ksrc = P.ex + X.k + (int64_t)l * s.kvdim() + at.j * HD;
+    const uint64_t* vsrc = P.ex + X.v + (int64_t)l * s.kvdim() + at.j * HD;
+    const int32_t n = G * HD + (at.has_p ? 2 * HD : 0);
+    constexpr int KM = ((G + 2) * HD + kThreads - 1) / kThreads;
+    K.poll<KM>(
+        ep, [&](int k) { return K.tid + k * kThreads < n; },
+        [&](int k) {
+          const int32_t e = K.tid + k * kThreads;
+          return e < G * HD ? qsrc + e : (e < (G + 1) * HD ? ksrc + (e - G * HD) : vsrc + (e - (G + 1) * HD));
+        },
+        [&](int k, float x) { L.q[K.tid + k * kThreads] = x; });
+    K.tr.add(T_FETCH, TR_NOW() - t0);
+    bar();
+  }
+  const uint64_t ta = TR_NOW();
+  const float scale = 1.4426950408889634f / sqrtf((float)HD);  // softmax in the exp2 domain
   float qr[G][8];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const v4f a = *(const v4f*)(q + g * HD + dg * 8);
-    const v4f b = *(const v4f*)(q + g * HD + dg * 8 + 4);
+    const v4f a = *(const v4f*)(L.q + g * HD + dg * 8);
+    const v4f b = *(const v4f*)(L.q + g * HD + dg * 8 + 4);
     qr[g][0] = a.x; qr[g][1] = a.y; qr[g][2] = a.z; qr[g][3] = a.w;
     qr[g][4] = b.x; qr[g][5] = b.y; qr[g][6] = b.z; qr[g][7] = b.w;
   }
-  auto score = [&](v4u kw, float* out) {
+  float m[G], ls[G], acc[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    ls[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+  }
+  auto update = [&](const v4u kw, const v4u vw, bool valid) {
     const float kf[8] = {bf16lo(kw.x), bf16hi(kw.x), bf16lo(kw.y), bf16hi(kw.y),
                          bf16lo(kw.z), bf16hi(kw.z), bf16lo(kw.w), bf16hi(kw.w)};
+    const float vf[8] = {bf16lo(vw.x), bf16hi(vw.x), bf16lo(vw.y), bf16hi(vw.y),
+                         bf16lo(vw.z), bf16hi(vw.z), bf16lo(vw.w), bf16hi(vw.w)};
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float d = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) d = fmaf(qr[g][e], kf[e], d);
       d = LPP == 16 ? row16_sum(d) : row8_sum(d);
-      out[g] = d * scale;
+      const float sc = d * scale;
+      if (valid) {
+        const float mn = fmaxf(m[g], sc);
+        const float c = exp2f(m[g] - mn);  // 0 while m is -inf
+        const float pr = exp2f(sc - mn);
+        ls[g] = fmaf(ls[g], c, pr);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(acc[g][e], c, pr * vf[e]);
+        m[g] = mn;
+      }
     }
   };
-  // the current position's K/V come from the exchange, rounded to bf16 like the cache
-  auto cur_row = [&](const float* src) {
-    uint32_t b[8];
+  for (int32_t bi = 0; bi < nbw; ++bi) {
+    v4u kc[AB], vc[AB];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) b[e] = f32_to_bf16(src[dg * 8 + e]);
-    return v4u{b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16)};
-  };
-
-  // pass 1: scores of the cached positions (K tiles) and of the current position
-  for (int32_t tp = C.c; tp < at.nkt; tp += kConsumerWaves) {
-    const uint32_t i = tile_base + (uint32_t)tp;
-    C.wait_ready<1>(i, 1);
-    if (C.fail) return;
-    const v4u kw = *C.tile_ptr(C.slot_of(i));
-    float sg[G];
-    score(kw, sg);
-    C.watermark(i + 1);
-    const int32_t p = tp * PPT + lpos;
-    if (dg == 0 && p < at.ncache) {
+    for (int e = 0; e < AB; ++e) {
+      kc[e] = kn[e];
+      vc[e] = vn[e];
+    }
+    if (bi + 1 < nbw) kv_issue(bi + 1, kn, vn);
 #pragma unroll
-      for (int g = 0; g < G; ++g) sc[g * at.cs + p] = sg[g];
+    for (int e = 0; e < AB; ++e) {
+      const int32_t i = bi * AB + e;
+      if (i < ntw) update(kc[e], vc[e], (v + kWaves * i) * PPT + lpos < at.ncache);
     }
   }
-  if (at.has_p && C.c == (at.nkt % kConsumerWaves)) {
-    float sg[G];
-    score(cur_row(kp), sg);
-    if (lane == 0) {
+  // the current position: its K/V come from the exchange, rounded to bf16 like the cache
+  if (at.has_p && v == at.nkt % kWaves) {
+    auto cur_row = [&](const float* src) {
+      uint32_t b[8];
 #pragma unroll
-      for (int g = 0; g < G; ++g) sc[g * at.cs + at.ncache] = sg[g];
-    }
+      for (int e = 0; e < 8; ++e) b[e] = f32_to_bf16(src[dg * 8 + e]);
+      return v4u{b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16)};
+    };
+    update(cur_row(L.q + G * HD), cur_row(L.q + (G + 1) * HD), lpos == 0);
   }
-  C.csync();
-  // chunk maximum per head (every wave computes it; fixed order)
-  float mx[G];
+  // combine the position rows of the wave (lanes with the same dims)
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float m = -INFINITY;
-    for (int32_t p = lane; p < npos; p += kWave) m = fmaxf(m, sc[g * at.cs + p]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    mx[g] = m;
-  }
-  // pass 2: V tiles; lane (lpos, dg) accumulates p * V over its positions for dims dg*8..+8
-  float acc[G][8], lsum[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    lsum[g] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
-  }
-  auto accumulate = [&](v4u vw, int32_t p, bool valid) {
-    const float vf[8] = {bf16lo(vw.x), bf16hi(vw.x), bf16lo(vw.y), bf16hi(vw.y),
-                         bf16lo(vw.z), bf16hi(vw.z), bf16lo(vw.w), bf16hi(vw.w)};
+  for (int off = LPP; off < kWave; off <<= 1) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const float pr = valid ? exp2f(sc[g * at.cs + p] - mx[g]) : 0.f;
-      lsum[g] += pr;
+      const float mo = __shfl_xor(m[g], off, kWave);
+      const float lo = __shfl_xor(ls[g], off, kWave);
+      const float M = fmaxf(m[g], mo);
+      const float f = m[g] == -INFINITY ? 0.f : exp2f(m[g] - M);
+      const float fo = mo == -INFINITY ? 0.f : exp2f(mo - M);
+      ls[g] = ls[g] * f + lo * fo;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(pr, vf[e], acc[g][e]);
+      for (int e = 0; e < 8; ++e) {
+        const float ao = __shfl_xor(acc[g][e], off, kWave);
+        acc[g][e] = acc[g][e] * f + ao * fo;
+      }
+      m[g] = M;
     }
-  };
-  const uint32_t vbase = tile_base + (uint32_t)at.nkt;
-  for (int32_t tp = C.c; tp < at.nkt; tp += kConsumerWaves) {
-    const uint32_t i = vbase + (uint32_t)tp;
-    C.wait_ready<1>(i, 1);
-    if (C.fail) return;
-    const v4u vw = *C.tile_ptr(C.slot_of(i));
-    const int32_t p = tp * PPT + lpos;
-    accumulate(vw, p < at.ncache ? p : 0, p < at.ncache);
-    C.watermark(i + 1);
   }
-  if (at.has_p && C.c == (at.nkt % kConsumerWaves)) accumulate(cur_row(vp), at.ncache, lpos == 0);
-  C.watermark(tile_base + (uint32_t)(2 * at.nkt));
-  // sums over the positions of a tile (lanes with the same dims); lsum counts each position
-  // once (its LPP lanes hold the same probability)
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float v = acc[g][e];
-#pragma unroll
-      for (int o = LPP; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
-      acc[g][e] = v;
-    }
-    float v = lsum[g];
-#pragma unroll
-    for (int o = LPP; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
-    lsum[g] = v;
-  }
-  float* ws = L.scr + C.c * G * (HD + 2);
+  float* ws = L.scr + v * G * (HD + 2);
   if (lpos == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
@@ -859,59 +586,74 @@ __device__ __forceinline__ void attention_chunk(Cons& C, const Att& at, int32_t 
   }
   if (lane == 0) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) ws[g * (HD + 2) + HD + 1] = lsum[g];
+    for (int g = 0; g < G; ++g) {
+      ws[g * (HD + 2) + HD] = m[g];
+      ws[g * (HD + 2) + HD + 1] = ls[g];
+    }
   }
-  C.csync();
-  uint64_t* part = P.ex + P.exo.part + ((int64_t)l * s.nwg + C.pl.w) * P.exo.part_words;
-  for (int e = C.tid; e < G * (HD + 2); e += kConsumerThreads) {
+  bar();
+  // combine the 8 waves and publish
+  uint64_t* part = P.ex + X.part + ((int64_t)l * s.nwg + K.w) * X.part_words;
+  for (int e = K.tid; e < G * (HD + 2); e += kThreads) {
     const int g = e / (HD + 2), k = e % (HD + 2);
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, L.scr[(w * G + g) * (HD + 2) + HD]);
     float out;
     if (k == HD) {
-      out = mx[g];
+      out = M;
     } else {
       out = 0.f;
 #pragma unroll
-      for (int w = 0; w < kConsumerWaves; ++w) out += L.scr[w * G * (HD + 2) + g * (HD + 2) + k];
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = L.scr[(w * G + g) * (HD + 2) + HD];
+        const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
+        out = fmaf(L.scr[(w * G + g) * (HD + 2) + k], f, out);
+      }
     }
-    st_x(part + e, tag_f(out, epoch));
+    st_x(part + e, tag_f(out, ep));
   }
   // the WG whose chunk holds the current position appends its K/V rows to the cache
   if (at.has_p) {
-    for (int e = C.tid; e < HD / 2; e += kConsumerThreads) {
+    const float* kp = L.q + G * HD;
+    const float* vp = L.q + (G + 1) * HD;
+    for (int e = K.tid; e < HD / 2; e += kThreads) {
       const uint32_t k2 = f32_to_bf16(kp[2 * e]) | (f32_to_bf16(kp[2 * e + 1]) << 16);
       const uint32_t v2 = f32_to_bf16(vp[2 * e]) | (f32_to_bf16(vp[2 * e + 1]) << 16);
       st_x32((uint32_t*)(P.kv + kv_offset(s, l, 0, at.j, pos)) + e, k2);
       st_x32((uint32_t*)(P.kv + kv_offset(s, l, 1, at.j, pos)) + e, v2);
     }
   }
-  C.csync();  // scratch reuse
+  K.tr.add(T_ATT, TR_NOW() - ta);
+  bar();  // scratch reuse
 }
 
-// merge of the chunk partials of one (query head, 32-dim slice)
-__device__ __forceinline__ void merge_unit(Cons& C, const Att& at, int32_t l, int32_t u, uint32_t epoch) {
-  const KParams& P = C.P;
-  const Lds& L = C.L;
+// Merge of the chunk partials of one (query head, 32-dim slice): 16 chunk lanes x 32 dims.
+__device__ __forceinline__ void merge_unit(Wk& K, const Att& at, int32_t l, int32_t u, uint32_t epoch) {
+  const KParams& P = K.P;
+  const Lds& L = K.L;
   const Shape& s = P.s;
   const int32_t slices = s.hd / kMergeDims;
   const int32_t h = u / slices, sl = u % slices;
   const int32_t G = s.group();
   const int32_t j = h / G, g = h % G;
-  const int dim = C.tid % kMergeDims, cl = C.tid / kMergeDims;  // 8 chunk lanes
+  constexpr int CL = kThreads / kMergeDims;  // 16 chunk lanes
+  const int dim = K.tid % kMergeDims, cl = K.tid / kMergeDims;
   float M = -INFINITY, S = 0.f, A = 0.f;
-  constexpr int KM = 8;  // chunks per thread in one pass (chunk lane stride 8)
-  for (int32_t c0 = cl; c0 < at.nch && !C.fail; c0 += 8 * KM) {
+  constexpr int KM = 4;  // chunks per thread in one pass (chunk lane stride 16)
+  for (int32_t c0 = cl; c0 < at.nch && !K.fail; c0 += CL * KM) {
     uint64_t wm[KM], wl[KM], wa[KM];
-    uint32_t missing = 0;
+    uint32_t todo = 0;
 #pragma unroll
     for (int k = 0; k < KM; ++k)
-      if (c0 + 8 * k < at.nch) missing |= 1u << k;
+      if (c0 + CL * k < at.nch) todo |= 1u << k;
+    const uint32_t present = todo;
     Waiter wt;
-    uint32_t todo = missing;
     while (__builtin_amdgcn_ballot_w64(todo != 0) != 0) {
 #pragma unroll
       for (int k = 0; k < KM; ++k) {
         if (todo & (1u << k)) {
-          const int32_t ch = c0 + 8 * k;
+          const int32_t ch = c0 + CL * k;
           const uint64_t* pp =
               P.ex + P.exo.part + ((int64_t)l * s.nwg + ch * s.nkv + j) * P.exo.part_words + g * (s.hd + 2);
           wm[k] = ld_x(pp + s.hd);
@@ -926,14 +668,15 @@ __device__ __forceinline__ void merge_unit(Cons& C, const Att& at, int32_t l, in
       if (__builtin_amdgcn_ballot_w64(todo != 0) != 0) {
         __builtin_amdgcn_s_sleep(1);
         if (wt.expired(P, L) || ((wt.spins & 255u) == 0 && global_error(P))) {
-          C.fail = true;
+          K.fail = true;
+          raise_error(P, L, KERR_TIMEOUT);
           break;
         }
       }
     }
 #pragma unroll
     for (int k = 0; k < KM; ++k) {
-      if (missing & (1u << k)) {
+      if (present & (1u << k)) {
         const float mk = __uint_as_float((uint32_t)(wm[k] >> 32));
         const float lk = __uint_as_float((uint32_t)(wl[k] >> 32));
         const float ak = __uint_as_float((uint32_t)(wa[k] >> 32));
@@ -946,275 +689,293 @@ __device__ __forceinline__ void merge_unit(Cons& C, const Att& at, int32_t l, in
       }
     }
   }
-  C.csync();
-  float* ms = C.L.scr;  // [8][32][3]
+  float* ms = L.scr;  // [16][32][3]
   ms[(cl * kMergeDims + dim) * 3 + 0] = M;
   ms[(cl * kMergeDims + dim) * 3 + 1] = S;
   ms[(cl * kMergeDims + dim) * 3 + 2] = A;
-  C.csync();
-  if (C.tid < kMergeDims) {
+  bar();
+  if (K.tid < kMergeDims) {
     float Mt = -INFINITY;
-    for (int k = 0; k < 8; ++k) Mt = fmaxf(Mt, ms[(k * kMergeDims + C.tid) * 3]);
+    for (int k = 0; k < CL; ++k) Mt = fmaxf(Mt, ms[(k * kMergeDims + K.tid) * 3]);
     float St = 0.f, At = 0.f;
-    for (int k = 0; k < 8; ++k) {
-      const float mk = ms[(k * kMergeDims + C.tid) * 3];
+    for (int k = 0; k < CL; ++k) {
+      const float mk = ms[(k * kMergeDims + K.tid) * 3];
       const float f = mk == -INFINITY ? 0.f : exp2f(mk - Mt);
-      St = fmaf(ms[(k * kMergeDims + C.tid) * 3 + 1], f, St);
-      At = fmaf(ms[(k * kMergeDims + C.tid) * 3 + 2], f, At);
+      St = fmaf(ms[(k * kMergeDims + K.tid) * 3 + 1], f, St);
+      At = fmaf(ms[(k * kMergeDims + K.tid) * 3 + 2], f, At);
     }
-    st_x(P.ex + P.exo.o + (int64_t)l * s.qdim() + h * s.hd + sl * kMergeDims + C.tid, tag_f(At / St, epoch));
+    st_x(P.ex + P.exo.o + (int64_t)l * s.qdim() + h * s.hd + sl * kMergeDims + K.tid, tag_f(At / St, epoch));
   }
-  C.csync();
+  bar();
 }
 
-// A token id that indexes memory is always kept inside [0, V).
-__device__ __forceinline__ int32_t clamp_token(int32_t t, int32_t V) { return t < 0 ? 0 : (t >= V ? V - 1 : t); }
+// The decode program of one wave. Its weight batches are consumed by one loop; the batch after
+// the current one is always in flight. Between batches, boundary() runs the work that separates
+// two stages -- finalising the outputs,
+// attention, the merge, the exchange gathers, RMSNorm, sampling -- whenever the current stage has
+// no batch left for this wave. Every wave runs every boundary, so the WG barriers inside match.
+enum Boundary : int { B_START = 0, B_QKV = 1, B_O = 2, B_GU = 3, B_DN = 4, B_LM = 5, B_END = 6 };
 
 template <int G, int HD>
-__device__ __forceinline__ void consumer(const KParams& P, const Lds& L, const Plan& pl, int c, int lane) {
-  Cons C(P, L, pl, c, lane);
-  const uint64_t t_start = TR_NOW();
+__device__ __forceinline__ void decode(Wk& K) {
+  const KParams& P = K.P;
+  const Lds& L = K.L;
   const Shape& s = P.s;
   const Exch& X = P.exo;
   uint64_t* ex = P.ex;
-  uint32_t tbase = 0;  // stream index of the next segment's first tile
-  int32_t tok = 0;
-  if (C.tid == 0) {
-    tok = P.first_tok[0];
-    if (tok < 0 || tok >= s.V) {
-      if (pl.w == 0) __hip_atomic_fetch_or(P.err, KERR_BAD_TOKEN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      tok = 0;
-    }
+  const uint64_t t_start = TR_NOW();
+  const int32_t tid = K.tid;
+  int32_t tok = P.first_tok[0];
+  if (tok < 0 || tok >= s.V) {
+    if (K.w == 0 && tid == 0) __hip_atomic_fetch_or(P.err, KERR_BAD_TOKEN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    tok = 0;
   }
-  // the token is uniform across consumer waves: broadcast through LDS
-  if (C.tid == 0) L.scr[0] = __int_as_float(tok);
-  C.csync();
-  tok = clamp_token(__float_as_int(L.scr[0]), s.V);
-  C.csync();
+  tok = clamp_token(__builtin_amdgcn_readfirstlane(tok), s.V);
+  K.start();  // the stream's first batch
 
-  for (int32_t step = 0; step < P.n_steps && !C.fail; ++step) {
-    const int32_t pos = P.pos0 + step;
-    const uint32_t ep = P.epoch0 + (uint32_t)step;
-    const Att at = att_info(s, pl.w, pos);
-    if (C.tid == 0) lds_st(&L.ctl[C_STEP], (uint32_t)step);
-    if (C.tid < s.hd / 2) L.rope[C.tid] = P.rope[(int64_t)pos * (s.hd / 2) + C.tid];  // visible after block_sum
-    // embedding row -> residual stream; RMSNorm inputs
-    float ss = 0.f;
-    for (int i = C.tid; i < s.d; i += kConsumerThreads) {
-      const float v = __uint_as_float((uint32_t)P.embed[(int64_t)tok * s.d + i] << 16);
-      L.xres[i] = v;
-      ss = fmaf(v, v, ss);
-    }
-    ss = C.block_sum(ss);
+  int32_t step = 0, l = 0;
+  int32_t pos = P.pos0;
+  uint32_t ep = P.epoch0;
+  Att at = att_info(s, K.w, pos);
+  bool lm = step_has_lm(P, 0);
+  float ss = 0.f;
+  int bnd = B_START;  // the next boundary
+  int st = -1;        // stage of the batches being reduced
+  int32_t rem = 0, b = 0;
+  bool done = false;
 
-    for (int32_t l = 0; l < s.L && !C.fail; ++l) {
-      // ---------------- QKV
-      if (l > 0) ss = C.fetch(ex + X.xf + (int64_t)l * s.d, s.d, L.xres, ep, true);
-      C.rmsnorm_to_act(ss, P.norms + (int64_t)l * 2 * s.d);
-      if (C.fail) break;
-      {
-        uint64_t* qx = ex + X.q + (int64_t)l * s.qdim();
-        uint64_t* kx = ex + X.k + (int64_t)l * s.kvdim();
-        uint64_t* vx = ex + X.v + (int64_t)l * s.kvdim();
-        C.gemv(
-            ST_QKV, tbase,
-            [&](int32_t gp, float ya, float yb) {
-              if (gp / (s.hd / 2) < s.nq + s.nkv) {  // query and key heads are rotated
-                const float2 cs = L.rope[gp % (s.hd / 2)];
-                return make_float2(ya * cs.x - yb * cs.y, yb * cs.x + ya * cs.y);
-              }
-              return make_float2(ya, yb);
-            },
-            [&](int32_t gp, int h, float v) {
-              int mat;
-              int32_t ra, rb;
-              pair_rows(s, ST_QKV, gp, &mat, &ra, &rb);
-              uint64_t* dst = mat == 0 ? qx : (mat == 1 ? kx : vx);
-              st_x(dst + (h ? rb : ra), tag_f(v, ep));
-            });
-        tbase += (uint32_t)(pl.np[ST_QKV] * pl.kt[ST_QKV]);
-      }
-      // ---------------- attention over this WG's chunk
-      if (at.c0 <= pos) {
-        const int32_t G_ = s.group();
-        const uint64_t* qsrc = ex + X.q + (int64_t)l * s.qdim() + (int64_t)at.j * G_ * s.hd;
-        if (at.has_p)
-          C.fetch3(qsrc, G_ * s.hd, L.act, ex + X.k + (int64_t)l * s.kvdim() + at.j * s.hd, s.hd, L.act + G_ * s.hd,
-                   ex + X.v + (int64_t)l * s.kvdim() + at.j * s.hd, s.hd, L.act + (G_ + 1) * s.hd, ep);
-        else
-          C.fetch(qsrc, G_ * s.hd, L.act, ep, false);
-        if (C.fail) break;
-        const uint64_t ta = TR_NOW();
-        attention_chunk<G, HD>(C, at, l, pos, tbase, ep);
-        C.tr.add(TC_ATT, TR_NOW() - ta);
-        tbase += (uint32_t)(2 * at.nkt);
-      }
-      // ---------------- merge of chunk partials (the WGs that own merge units)
-      {
-        const int32_t nu = merge_units(s);
-        const int32_t u0 = (int32_t)(((int64_t)pl.w * nu + s.nwg - 1) / s.nwg);
-        const uint64_t tm = TR_NOW();
-        for (int32_t u = u0; u < nu && merge_unit_wg(s, u) == pl.w && !C.fail; ++u) merge_unit(C, at, l, u, ep);
-        C.tr.add(TC_MERGE, TR_NOW() - tm);
-      }
-      // ---------------- O projection + residual
-      C.fetch(ex + X.o + (int64_t)l * s.qdim(), s.qdim(), L.act, ep, false, true);
-      if (C.fail) break;
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this WG's K/V rows are complete before its next outputs
-      {
-        uint64_t* xa = ex + X.xa + (int64_t)l * s.d;
-        C.gemv(
-            ST_O, tbase,
-            [&](int32_t gp, float ya, float yb) { return make_float2(L.xres[2 * gp] + ya, L.xres[2 * gp + 1] + yb); },
-            [&](int32_t gp, int h, float v) { st_x(xa + 2 * gp + h, tag_f(v, ep)); });
-        tbase += (uint32_t)(pl.np[ST_O] * pl.kt[ST_O]);
-      }
-      // ---------------- gate/up + SwiGLU
-      C.csync();  // every wave has finished reading xres before it is replaced
-      ss = C.fetch(ex + X.xa + (int64_t)l * s.d, s.d, L.xres, ep, true);
-      C.rmsnorm_to_act(ss, P.norms + (int64_t)l * 2 * s.d + s.d);
-      if (C.fail) break;
-      {
-        uint64_t* hx = ex + X.h + (int64_t)l * s.F;
-        C.gemv(
-            ST_GU, tbase,
-            [&](int32_t gp, float ya, float yb) { return make_float2((ya / (1.0f + expf(-ya))) * yb, 0.f); },
-            [&](int32_t gp, int h, float v) {
-              if (h == 0) st_x(hx + gp, tag_f(v, ep));
-            });
-        tbase += (uint32_t)(pl.np[ST_GU] * pl.kt[ST_GU]);
-      }
-      // ---------------- down + residual
-      C.csync();
-      C.fetch(ex + X.h + (int64_t)l * s.F, s.F, L.act, ep, false, true);
-      if (C.fail) break;
-      {
-        uint64_t* xf = ex + X.xf + (int64_t)(l + 1) * s.d;
-        C.gemv(
-            ST_DN, tbase,
-            [&](int32_t gp, float ya, float yb) { return make_float2(L.xres[2 * gp] + ya, L.xres[2 * gp + 1] + yb); },
-            [&](int32_t gp, int h, float v) { st_x(xf + 2 * gp + h, tag_f(v, ep)); });
-        tbase += (uint32_t)(pl.np[ST_DN] * pl.kt[ST_DN]);
-      }
-      C.csync();
-    }
-    if (C.fail) break;
-
-    // ---------------- final norm + LM head + local argmax
-    float best_v = -INFINITY;
-    int32_t best_i = 0x7fffffff;
-    const bool lm = step_has_lm(P, step);
-    if (lm) {
-      ss = C.fetch(ex + X.xf + (int64_t)s.L * s.d, s.d, L.xres, ep, true);
-      C.rmsnorm_to_act(ss, P.norms + (int64_t)s.L * 2 * s.d);
-      if (C.fail) break;
-      float* lo = P.logits_out ? P.logits_out + (P.lm_last_only ? 0 : (int64_t)step * s.V) : nullptr;
-      C.gemv(
-          ST_LM, tbase,
-          [&](int32_t gp, float ya, float yb) {
-            const int32_t ra = 2 * gp, rb = 2 * gp + 1;
-            if (ya > best_v || (ya == best_v && ra < best_i)) { best_v = ya; best_i = ra; }
-            if (yb > best_v || (yb == best_v && rb < best_i)) { best_v = yb; best_i = rb; }
-            return make_float2(ya, yb);
-          },
-          [&](int32_t gp, int h, float v) {
-            if (lo) lo[2 * gp + h] = v;
-          });
-      tbase += (uint32_t)(pl.np[ST_LM] * pl.kt[ST_LM]);
-    }
-    // combine the 4 waves' candidates, publish this WG's (value, index)
-    C.csync();
-    if (lane == 0) {
-      L.scr[2 * c] = best_v;
-      L.scr[2 * c + 1] = __int_as_float(best_i);
-    }
-    C.csync();
-    if (C.tid == 0) {
-      float bv = L.scr[0];
-      int32_t bi = __float_as_int(L.scr[1]);
-      for (int k = 1; k < kConsumerWaves; ++k) {
-        const float v = L.scr[2 * k];
-        const int32_t i = __float_as_int(L.scr[2 * k + 1]);
-        if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
-      }
-      st_x(ex + X.lm + 2 * pl.w, tag_f(bv, ep));
-      st_x(ex + X.lm + 2 * pl.w + 1, tag_u((uint32_t)bi, ep));
-    }
-    C.csync();
-    // every WG gathers all candidates (this is also the step's grid-wide synchronisation)
-    const uint64_t tsm = TR_NOW();
-    C.fetch(ex + X.lm, 2 * s.nwg, L.scr, ep, false);
-    C.tr.add(TC_SAMPLE, TR_NOW() - tsm);
-    if (C.fail) break;
-    int32_t next = 0;
-    {
-      // argmax over nwg candidates; each thread scans a strided subset, then a fixed-order merge
-      float bv = -INFINITY;
-      int32_t bi = 0x7fffffff;
-      for (int k = C.tid; k < s.nwg; k += kConsumerThreads) {
-        const float v = L.scr[2 * k];
-        const int32_t i = __float_as_int(L.scr[2 * k + 1]);
-        if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int32_t oi = __shfl_xor(bi, o, 64);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-      }
-      C.csync();
-      if (lane == 0) {
-        L.scr[2 * c] = bv;
-        L.scr[2 * c + 1] = __int_as_float(bi);
-      }
-      C.csync();
-      bv = L.scr[0];
-      bi = __float_as_int(L.scr[1]);
-      for (int k = 1; k < kConsumerWaves; ++k) {
-        const float v = L.scr[2 * k];
-        const int32_t i = __float_as_int(L.scr[2 * k + 1]);
-        if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
-      }
-      next = clamp_token(bi, s.V);
-      C.csync();
-    }
-    if (lm && pl.w == 0 && C.tid == 0) {
-      if (P.tokens_out) P.tokens_out[step] = next;
-      if (P.last_tok_out && step == P.n_steps - 1) P.last_tok_out[0] = next;
-    }
-    if (P.forced && step + 1 < P.n_steps) {
-      if (C.tid == 0) {
-        int32_t f = P.forced[step];
-        if (f < 0 || f >= s.V) {
-          if (pl.w == 0) __hip_atomic_fetch_or(P.err, KERR_BAD_TOKEN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          f = 0;
+  auto boundary = [&]() {
+    while (rem == 0 && !done) {
+      const uint64_t tb = TR_NOW();
+      const int bnd_run = bnd;
+      switch (bnd) {
+        case B_START: {  // embedding row -> residual stream, RMSNorm of layer 0
+          if (tid < s.hd / 2) L.rope[tid] = P.rope[(int64_t)pos * (s.hd / 2) + tid];
+          float sq = 0.f;
+          for (int32_t i = tid; i < s.d; i += kThreads) {
+            const float x = __uint_as_float((uint32_t)P.embed[(int64_t)tok * s.d + i] << 16);
+            L.xres[i] = x;
+            sq = fmaf(x, x, sq);
+          }
+          ss = K.block_sum(sq);
+          K.norm_to_act(ss, P.norms);
+          st = ST_QKV;
+          bnd = B_QKV;
+          break;
         }
-        L.scr[0] = __int_as_float(f);
+        case B_QKV: {  // QKV outputs (+RoPE) -> attention -> merge -> gather o
+          bar();
+          uint64_t* qx = ex + X.q + (int64_t)l * s.qdim();
+          uint64_t* kx = ex + X.k + (int64_t)l * s.kvdim();
+          uint64_t* vx = ex + X.v + (int64_t)l * s.kvdim();
+          K.finalize(K.g[ST_QKV], [&](int32_t gp, float ya, float yb) {
+            const int32_t half = s.hd / 2;
+            const int32_t hs = gp / half, i = gp % half;
+            if (hs < s.nq + s.nkv) {  // query and key heads are rotated
+              const float2 cs = L.rope[i];
+              const float ra = ya * cs.x - yb * cs.y, rb = yb * cs.x + ya * cs.y;
+              ya = ra;
+              yb = rb;
+            }
+            uint64_t* dst;
+            int32_t h;
+            if (hs < s.nq) {
+              dst = qx;
+              h = hs;
+            } else if (hs < s.nq + s.nkv) {
+              dst = kx;
+              h = hs - s.nq;
+            } else {
+              dst = vx;
+              h = hs - s.nq - s.nkv;
+            }
+            st_x(dst + h * s.hd + i, tag_f(ya, ep));
+            st_x(dst + h * s.hd + i + half, tag_f(yb, ep));
+          });
+          if (at.c0 <= pos) attention<G, HD>(K, at, l, pos, ep);
+          {
+            const uint64_t tm = TR_NOW();
+            const int32_t nu = merge_units(s);
+            const int32_t u0 = (int32_t)(((int64_t)K.w * nu + s.nwg - 1) / s.nwg);
+            for (int32_t u = u0; u < nu && merge_unit_wg(s, u) == K.w; ++u) merge_unit(K, at, l, u, ep);
+            K.tr.add(T_MERGE, TR_NOW() - tm);
+          }
+          K.fetch_f32(ex + X.o + (int64_t)l * s.qdim(), s.qdim(), L.act, ep, false);
+          st = ST_O;
+          bnd = B_O;
+          break;
+        }
+        case B_O: {  // O outputs + residual -> gather xa -> RMSNorm
+          bar();
+          if (at.has_p) __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this WG's K/V rows are complete first
+          uint64_t* xa = ex + X.xa + (int64_t)l * s.d;
+          K.finalize(K.g[ST_O], [&](int32_t gp, float ya, float yb) {
+            st_x(xa + 2 * gp, tag_f(L.xres[2 * gp] + ya, ep));
+            st_x(xa + 2 * gp + 1, tag_f(L.xres[2 * gp + 1] + yb, ep));
+          });
+          bar();  // every wave is done with xres before it is replaced
+          ss = K.fetch_f32(xa, s.d, L.xres, ep, true);
+          K.norm_to_act(ss, P.norms + (int64_t)l * 2 * s.d + s.d);
+          st = ST_GU;
+          bnd = B_GU;
+          break;
+        }
+        case B_GU: {  // SwiGLU outputs -> gather h
+          bar();
+          uint64_t* hx = ex + X.h + (int64_t)l * s.F;
+          K.finalize(K.g[ST_GU], [&](int32_t gp, float ya, float yb) {
+            st_x(hx + gp, tag_f((ya / (1.0f + expf(-ya))) * yb, ep));
+          });
+          K.fetch_f32(hx, s.F, L.act, ep, false);
+          st = ST_DN;
+          bnd = B_DN;
+          break;
+        }
+        case B_DN: {  // down outputs + residual -> next layer's input (or the LM head's)
+          bar();
+          uint64_t* xf = ex + X.xf + (int64_t)(l + 1) * s.d;
+          K.finalize(K.g[ST_DN], [&](int32_t gp, float ya, float yb) {
+            st_x(xf + 2 * gp, tag_f(L.xres[2 * gp] + ya, ep));
+            st_x(xf + 2 * gp + 1, tag_f(L.xres[2 * gp + 1] + yb, ep));
+          });
+          bar();
+          if (aborted(L)) {
+            bnd = B_END;
+            st = -1;
+          } else if (l + 1 < s.L) {
+            ++l;
+            ss = K.fetch_f32(xf, s.d, L.xres, ep, true);
+            K.norm_to_act(ss, P.norms + (int64_t)l * 2 * s.d);
+            st = ST_QKV;
+            bnd = B_QKV;
+          } else if (lm) {
+            ss = K.fetch_f32(xf, s.d, L.xres, ep, true);
+            K.norm_to_act(ss, P.norms + (int64_t)s.L * 2 * s.d);
+            st = ST_LM;
+            bnd = B_LM;
+          } else {
+            st = -1;
+            bnd = B_END;
+          }
+          break;
+        }
+        case B_LM:
+        case B_END: {  // LM outputs and this WG's argmax candidate; the grid-wide join; next token
+          float bv = -INFINITY;
+          int32_t bi = 0x7fffffff;
+          if (bnd == B_LM) {
+            bar();
+            float* lo = P.logits_out ? P.logits_out + (P.lm_last_only ? 0 : (int64_t)step * s.V) : nullptr;
+            K.finalize(K.g[ST_LM], [&](int32_t gp, float ya, float yb) {
+              const int32_t ra = 2 * gp, rb = 2 * gp + 1;
+              if (better(ya, ra, bv, bi)) {
+                bv = ya;
+                bi = ra;
+              }
+              if (better(yb, rb, bv, bi)) {
+                bv = yb;
+                bi = rb;
+              }
+              if (lo) {
+                lo[ra] = ya;
+                lo[rb] = yb;
+              }
+            });
+          }
+          // every WG gathers all candidates: no WG reuses a step's exchange buffers before every
+          // WG has finished reading them
+          const uint64_t tsm = TR_NOW();
+          K.block_argmax(&bv, &bi);
+          if (tid == 0) {
+            st_x(ex + X.lm + 2 * K.w, tag_f(bv, ep));
+            st_x(ex + X.lm + 2 * K.w + 1, tag_u((uint32_t)bi, ep));
+          }
+          K.fetch_f32(ex + X.lm, 2 * s.nwg, L.scr, ep, false);
+          bv = -INFINITY;
+          bi = 0x7fffffff;
+          for (int k = tid; k < s.nwg; k += kThreads) {
+            const float cv = L.scr[2 * k];
+            const int32_t ci = __float_as_int(L.scr[2 * k + 1]);
+            if (better(cv, ci, bv, bi)) {
+              bv = cv;
+              bi = ci;
+            }
+          }
+          bar();  // every thread has read its candidates before scr is reused
+          K.block_argmax(&bv, &bi);
+          K.tr.add(T_SAMPLE, TR_NOW() - tsm);
+          int32_t next = clamp_token(bi, s.V);
+          if (lm && K.w == 0 && tid == 0) {
+            if (P.tokens_out) P.tokens_out[step] = next;
+            if (P.last_tok_out && step == P.n_steps - 1) P.last_tok_out[0] = next;
+          }
+          if (P.forced && step + 1 < P.n_steps) {
+            int32_t f = P.forced[step];
+            if (f < 0 || f >= s.V) {
+              if (K.w == 0 && tid == 0)
+                __hip_atomic_fetch_or(P.err, KERR_BAD_TOKEN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              f = 0;
+            }
+            next = clamp_token(__builtin_amdgcn_readfirstlane(f), s.V);
+          }
+          tok = next;
+          ++step;
+          if (step >= P.n_steps || aborted(L)) {
+            done = true;
+          } else {
+            l = 0;
+            pos = P.pos0 + step;
+            ep = P.epoch0 + (uint32_t)step;
+            at = att_info(s, K.w, pos);
+            lm = step_has_lm(P, step);
+          }
+          st = -1;
+          bnd = B_START;
+          break;
+        }
       }
-      C.csync();
-      next = clamp_token(__float_as_int(L.scr[0]), s.V);
-      C.csync();
+      K.tr.add(T_BAR, TR_NOW() - tb);
+      {
+        const uint64_t dt = TR_NOW() - tb;  // per boundary kind (constant slots keep the counters in registers)
+        switch (bnd_run) {
+          case B_START: K.tr.add(10, dt); break;
+          case B_QKV: K.tr.add(11, dt); break;
+          case B_O: K.tr.add(12, dt); break;
+          case B_GU: K.tr.add(13, dt); break;
+          case B_DN: K.tr.add(14, dt); break;
+          default: K.tr.add(15, dt); break;
+        }
+      }
+      rem = st >= 0 ? K.nb_of(st) : 0;
+      b = 0;
     }
-    tok = next;
+  };
+
+  while (true) {
+    boundary();
+    if (done) break;
+    const uint64_t tg = TR_NOW();
+    v4u cur[kBatch];
+    K.take(cur);
+    K.reduce_batch(K.geo_of(st), b, cur);
+    K.tr.add(T_GEMV, TR_NOW() - tg);
+    K.tr.add(T_BATCHES, 1);
+    --rem;
+    ++b;
   }
-  C.tr.add(TC_TOTAL, TR_NOW() - t_start);
-  C.tr.flush(P.trace + ((int64_t)pl.w * (kThreads / kWave) + kProducerWaves + c) * kTraceWords, lane);
-  if (C.fail) raise_error(P, L, KERR_CONSUMER);
+  K.tr.add(T_TOTAL, TR_NOW() - t_start);
+  K.tr.flush(P.trace + ((int64_t)K.w * kWaves + K.v) * kTraceWords, K.lane);
 }
 
 template <int G, int HD>
 __global__ void __launch_bounds__(kThreads, 1) kie_decode_kernel(KParams P) {
   extern __shared__ __align__(16) uint8_t smem[];
-  const Lds L = lds_map(smem, P.s, P.ring_slots);
+  const Lds L = lds_map(smem, P.s);
   if (threadIdx.x < C_COUNT) L.ctl[threadIdx.x] = 0;
   __syncthreads();
-  const Plan pl = make_plan(P, blockIdx.x);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
-  const int lane = threadIdx.x % kWave;
-  if (wave < kProducerWaves)
-    producer(P, L, pl, wave, lane);
-  else
-    consumer<G, HD>(P, L, pl, wave - kProducerWaves, lane);
+  Wk K(P, L, blockIdx.x, wave, threadIdx.x % kWave);
+  decode<G, HD>(K);
 }
 
 // Instantiations for the supported (group size, head_dim) combinations.

@@ -10,64 +10,66 @@
 
 namespace kie {
 
-// One block per WG; it copies the WG's tiles of one layer (or of the LM head) into the WG's
-// stream. Every 64 threads move one 1 KiB tile: thread q takes 16 B of row A (q < 32) or row B.
+// One block row per stream (WG w = x / 8, wave v = x % 8); it writes the stream's tiles of one
+// layer (or of the LM head). Each thread writes one lane (16 B) of a tile: 8 B of row A and 8 B of
+// row B at the same k. Slots of missing units are written as zeros.
 __global__ void __launch_bounds__(256) pack_layer_kernel(PackArgs a) {
   const Shape& s = a.s;
-  const int32_t w = blockIdx.x;
-  int32_t np[ST_COUNT], pb[ST_COUNT], pre[ST_COUNT];
-  int32_t acc = 0;
-  for (int st = 0; st < ST_COUNT; ++st) {
-    const int32_t n = s.stage_pairs(st);
-    pb[st] = split_begin(n, s.nwg, w);
-    np[st] = split_end(n, s.nwg, w) - pb[st];
-    if (st <= ST_DN) {
-      pre[st] = acc;
-      acc += np[st] * s.stage_kt(st);
-    } else {
-      pre[st] = 0;
-    }
-  }
-  const int32_t t_layer = acc;
+  const int32_t w = blockIdx.x / kWaves, v = blockIdx.x % kWaves;
   const bool lm = a.layer == s.L;
-  const int64_t base = a.wbase[w] + (int64_t)a.layer * t_layer;
-  const int32_t ntiles = lm ? np[ST_LM] * s.stage_kt(ST_LM) : t_layer;
+  int32_t boff[ST_COUNT + 1];
+  int32_t acc = 0;
+  for (int st = ST_QKV; st <= ST_DN; ++st) {
+    boff[st] = acc;
+    acc += wave_batches(stage_geo(s, st, w), v);
+  }
+  boff[ST_LM] = acc;
+  const int32_t layer_b = acc;
+  const int32_t nb = lm ? lm_batches(s, w, v) : layer_b;
+  const int64_t base = a.wbase[blockIdx.x] + (int64_t)a.layer * layer_b * kBatch;
   const int q = threadIdx.x % 64;
-  for (int32_t t = blockIdx.y * 4 + threadIdx.x / 64; t < ntiles; t += gridDim.y * 4) {
+  for (int32_t t = blockIdx.y * 4 + threadIdx.x / 64; t < nb * kBatch; t += gridDim.y * 4) {
     int st = ST_LM;
-    int32_t tt = t;
+    int32_t b = t / kBatch;
     if (!lm) {
       st = ST_QKV;
-      while (st < ST_DN && tt >= pre[st + 1]) ++st;
-      tt = t - pre[st];
+      while (st < ST_DN && b >= boff[st + 1]) ++st;
+      b -= boff[st];
     }
-    const int32_t kt = s.stage_kt(st), K = s.stage_k(st);
-    int32_t lp, j;
-    tile_source(np[st], kt, tt, &lp, &j);
-    int mat;
-    int32_t ra, rb;
-    pair_rows(s, st, pb[st] + lp, &mat, &ra, &rb);
-    const bool half_b = q >= 32;
-    const uint16_t* m;
-    if (st == ST_QKV)
-      m = mat == 0 ? a.wq : (mat == 1 ? a.wk : a.wv);
-    else if (st == ST_O)
-      m = a.wo;
-    else if (st == ST_GU)
-      m = half_b ? a.wup : a.wgate;
-    else if (st == ST_DN)
-      m = a.wdown;
-    else
-      m = a.lm_head;
-    const int32_t row = half_b ? rb : ra;
-    const int32_t k = j * kTileK + (q % 32) * 8;
-    const v4u v = *(const v4u*)(m + (int64_t)row * K + k);
-    *(v4u*)(a.packed + (base + t) * kTileBytes + q * 16) = v;
+    const StageGeo g = stage_geo(s, st, w);
+    const int32_t sl = t % kBatch, us = sl / g.ks, tt = sl % g.ks;
+    const int32_t u = v + kWaves * (b * g.upb + us);
+    v4u out = v4u{0u, 0u, 0u, 0u};
+    if (u < g.nu) {
+      const int32_t lp = u / g.S, j = (u % g.S) * g.ks + tt;
+      int mat;
+      int32_t ra, rb;
+      pair_rows(s, st, g.pb + lp, &mat, &ra, &rb);
+      const uint16_t *ma, *mb;
+      if (st == ST_QKV) {
+        ma = mb = mat == 0 ? a.wq : (mat == 1 ? a.wk : a.wv);
+      } else if (st == ST_O) {
+        ma = mb = a.wo;
+      } else if (st == ST_GU) {
+        ma = a.wgate;
+        mb = a.wup;
+      } else if (st == ST_DN) {
+        ma = mb = a.wdown;
+      } else {
+        ma = mb = a.lm_head;
+      }
+      const int32_t K = s.stage_k(st);
+      const int32_t k = j * kTileK + q * 4;
+      const uint2 xa = *(const uint2*)(ma + (int64_t)ra * K + k);
+      const uint2 xb = *(const uint2*)(mb + (int64_t)rb * K + k);
+      out = v4u{xa.x, xa.y, xb.x, xb.y};
+    }
+    *(v4u*)(a.packed + (base + t) * kTileBytes + q * 16) = out;
   }
 }
 
 hipError_t launch_pack_layer(const PackArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(pack_layer_kernel, dim3(a.s.nwg, 16), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(pack_layer_kernel, dim3(a.s.nwg * kWaves, 16), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -18,7 +18,9 @@
  *   to the cache.
  *
  * Precision: bf16 weights are widened exactly to fp32; activations and dot products are fp32 with
- * one accumulator per output summed in ascending index order; the softmax denominator and the
+ * one accumulator per output summed in ascending index order (oc_set_gemv_order(1) sums the
+ * same terms in descending order instead: a second, equally valid rounding of the same model that
+ * the tests use to measure how far two correct fp32 renditions of a deep model drift apart); the softmax denominator and the
  * attention-weighted sum of V are fp64 (stored as fp32). No -ffast-math: every reduction runs in
  * the order written here. Row loops may be split over threads (rows only), which cannot change
  * any result bit.
@@ -48,8 +50,10 @@ typedef struct {
 } oc_weights;
 
 static int g_threads = 1;
+static int g_gemv_desc = 0;
 
 void oc_set_threads(int n) { g_threads = n < 1 ? 1 : n; }
+void oc_set_gemv_order(int descending) { g_gemv_desc = descending ? 1 : 0; }
 int oc_get_threads(void) { return g_threads; }
 
 /* ------------------------------------------------------------------ scalar helpers */
@@ -93,7 +97,10 @@ void oc_gemv(const uint16_t* W, const float* x, float* y, int rows, int cols) {
   for (r = 0; r < rows; r++) {
     const uint16_t* w = W + (size_t)r * cols;
     float acc = 0.0f;
-    for (int k = 0; k < cols; k++) acc += oc_bf16_to_f32(w[k]) * x[k];
+    if (g_gemv_desc)
+      for (int k = cols - 1; k >= 0; k--) acc += oc_bf16_to_f32(w[k]) * x[k];
+    else
+      for (int k = 0; k < cols; k++) acc += oc_bf16_to_f32(w[k]) * x[k];
     y[r] = acc;
   }
 }

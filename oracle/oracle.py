@@ -64,6 +64,7 @@ def _load():
         lib.oc_bf16_to_f32.argtypes = [C.c_uint16]
         lib.oc_bf16_to_f32.restype = C.c_float
         lib.oc_set_threads.argtypes = [C.c_int]
+        lib.oc_set_gemv_order.argtypes = [C.c_int]
         lib.oc_step.argtypes = [C.c_void_p, C.c_void_p, u16p, u16p, C.c_int, C.c_int, f32p]
         lib.oc_step.restype = C.c_int
         lib.oc_full_recompute.argtypes = [C.c_void_p, C.c_void_p, i32p, C.c_int, f32p]
@@ -78,6 +79,12 @@ def _p(a: np.ndarray, ct):
 
 def set_threads(n: int) -> None:
     _load().oc_set_threads(int(n))
+
+
+def set_gemv_order(descending: bool) -> None:
+    """Sum every GEMV row in descending instead of ascending k order (a second valid rounding of
+    the same model; used only to measure the model's own sensitivity to rounding order)."""
+    _load().oc_set_gemv_order(1 if descending else 0)
 
 
 def gemv(W: np.ndarray, x: np.ndarray) -> np.ndarray:

@@ -1,0 +1,85 @@
+// Host-side check of the packed-stream geometry in layout.h: for every workgroup and stage, the
+// batches of the 8 waves cover each (pair, k-tile) exactly once, unit slots beyond the stage stay
+// empty, and the stream lengths add up to the packed image. Prints "ok" or the first violation.
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+
+#include "layout.h"
+
+using namespace kie;
+
+static int check(const Shape& s) {
+  int64_t total = 0;
+  for (int32_t w = 0; w < s.nwg; ++w) {
+    for (int st = ST_QKV; st < ST_COUNT; ++st) {
+      const StageGeo g = stage_geo(s, st, w);
+      if (g.ks * g.S != g.kt || g.upb * g.ks != kBatch) {
+        std::printf("bad unit geometry w=%d st=%d\n", w, st);
+        return 1;
+      }
+      std::vector<int> seen((size_t)g.np * g.kt, 0);
+      for (int32_t v = 0; v < kWaves; ++v) {
+        const int32_t nbv = wave_batches(g, v);
+        for (int32_t b = 0; b < nbv; ++b)
+          for (int32_t sl = 0; sl < kBatch; ++sl) {
+            const int32_t us = sl / g.ks, tt = sl % g.ks;
+            const int32_t u = v + kWaves * (b * g.upb + us);
+            if (u >= g.nu) continue;
+            const int32_t lp = u / g.S, j = (u % g.S) * g.ks + tt;
+            if (lp >= g.np || j >= g.kt) {
+              std::printf("slot out of range w=%d st=%d v=%d b=%d sl=%d\n", w, st, v, b, sl);
+              return 1;
+            }
+            seen[(size_t)lp * g.kt + j] += 1;
+          }
+        // the batch count is the least that holds the wave's units
+        const int32_t nu_v = wave_units(g, v);
+        if (nbv * g.upb < nu_v || (nbv > 0 && (nbv - 1) * g.upb >= nu_v)) {
+          std::printf("batch count w=%d st=%d v=%d\n", w, st, v);
+          return 1;
+        }
+      }
+      for (size_t i = 0; i < seen.size(); ++i)
+        if (seen[i] != 1) {
+          std::printf("tile %zu of w=%d st=%d covered %d times\n", i, w, st, seen[i]);
+          return 1;
+        }
+    }
+    for (int32_t v = 0; v < kWaves; ++v) total += stream_tiles(s, w, v);
+  }
+  if (total != packed_stream_tiles(s)) {
+    std::printf("stream total mismatch\n");
+    return 1;
+  }
+  for (int st = ST_QKV; st < ST_COUNT; ++st) {
+    int64_t np = 0;
+    for (int32_t w = 0; w < s.nwg; ++w) np += stage_geo(s, st, w).np;
+    if (np != s.stage_pairs(st)) {
+      std::printf("pairs of stage %d do not add up\n", st);
+      return 1;
+    }
+  }
+  std::printf("ok %lld tiles\n", (long long)total);
+  return 0;
+}
+
+int main(int argc, char** argv) {
+  if (argc != 10) {
+    std::printf("usage: L d nq nkv hd F V max_seq nwg\n");
+    return 2;
+  }
+  Shape s;
+  s.L = std::atoi(argv[1]);
+  s.d = std::atoi(argv[2]);
+  s.nq = std::atoi(argv[3]);
+  s.nkv = std::atoi(argv[4]);
+  s.hd = std::atoi(argv[5]);
+  s.F = std::atoi(argv[6]);
+  s.V = std::atoi(argv[7]);
+  s.max_seq = std::atoi(argv[8]);
+  s.nwg = std::atoi(argv[9]);
+  s.eps = 1e-5f;
+  s.theta = 10000.f;
+  return check(s);
+}
