@@ -3,9 +3,10 @@
 
 Default workload: the ~1.6B dense decoder (24 layers, d 2048, 16/8 heads, hd 128, FFN 8192,
 vocab 32768, bf16 weights and KV) with a 1024-token random-id prompt; a "step" is one decoded
-token (one pass of the whole decode path). The K timed steps run as ONE kie_generate launch
-starting at position 1024 (after the untimed prompt pass and W untimed warm-up tokens, the
-position is rewound to 1024 so the timed tokens sit at positions 1024..1024+K-1).
+token (one pass of the whole decode path). The W warm-up steps run as one kie_generate launch
+and the K timed steps as another, both starting at position 1024 (the position is rewound after
+the warm-up), so with W = K (the default) every decode-kernel dispatch of a run has the same
+length and a profiler's per-dispatch average is the timed launch's duration.
 
 Prints one JSON line. `roofline.achieved` is the algorithmic bytes of the timed launch divided
 by that launch's duration (HIP events on the launch stream); `cpu_baseline` times the CPU oracle
@@ -29,24 +30,14 @@ PEAK_HBM_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=512)
-    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=None, help="warm-up steps (default: the same as --steps)")
     ap.add_argument("--workload", default="1.6b-1k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
-    ap.add_argument("--single-step-launches", type=int, default=32,
+    ap.add_argument("--single-step-launches", type=int, default=0,
                     help="also time this many one-token launches (launch-overhead comparison); 0 = skip")
     return ap.parse_args()
-
-
-def source_hash() -> str:
-    import hashlib
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "hbm_bandwidth_bound_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
-    return h.hexdigest()[:16]
 
 
 def read_traffic(workload: str):
@@ -61,6 +52,7 @@ def read_traffic(workload: str):
             m = re.match(r"^\s*([a-z_]+)\s*=\s*(\S+)", line)
             if m:
                 kv[m.group(1)] = m.group(2)
+    from hbm_bandwidth_bound_amd.build import source_hash
     if kv.get("source_sha") != source_hash():
         return None
     try:
@@ -117,11 +109,13 @@ def main():
     import torch
 
     from hbm_bandwidth_bound_amd import synth, traffic
+    from hbm_bandwidth_bound_amd.build import source_hash
     from hbm_bandwidth_bound_amd.kie import Engine, stream_read
 
     wl = synth.WORKLOADS[args.workload]
     m = wl.model
-    K, W = int(args.steps), int(args.warmup)
+    K = int(args.steps)
+    W = K if args.warmup is None else int(args.warmup)
     P = wl.prompt_len
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)

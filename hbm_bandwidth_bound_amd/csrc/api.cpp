@@ -29,6 +29,7 @@ struct kie_ctx {
   uint16_t* kv;
   uint8_t* ws;
   KernelFn kernel;
+  KernelFn prompt_kernel;
   int32_t lds;
   int32_t pos;
   uint32_t epoch;  // tag of the next step
@@ -242,12 +243,14 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
     set_err(err, "shape needs %d bytes of LDS per workgroup (device limit %d)", lds, lds_limit);
     return KIE_ERR_UNSUPPORTED;
   }
-  KernelFn kfn = decode_kernel_for(s.group(), s.hd);
-  if (!kfn) {
+  KernelFn kfn = decode_kernel_for(s.group(), s.hd, false);
+  KernelFn pfn = decode_kernel_for(s.group(), s.hd, true);
+  if (!kfn || !pfn) {
     set_err(err, "no kernel for group %d head_dim %d", s.group(), s.hd);
     return KIE_ERR_UNSUPPORTED;
   }
   HIP_TRY(err, hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, lds));
+  HIP_TRY(err, hipFuncSetAttribute((const void*)pfn, hipFuncAttributeMaxDynamicSharedMemorySize, lds));
   int occ = 0;
   HIP_TRY(err, hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)kfn, kThreads, lds));
   if (occ < 1) {
@@ -265,6 +268,7 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
   c->kv = (uint16_t*)kv_cache;
   c->ws = (uint8_t*)workspace;
   c->kernel = kfn;
+  c->prompt_kernel = pfn;
   c->lds = lds;
   c->pos = 0;
   c->epoch = 1;
@@ -420,8 +424,9 @@ static kie_status launch(kie_ctx* ctx, const int32_t* first, int32_t n, const in
   P.lm_last_only = lm_last_only;
   P.timeout_ticks = ctx->timeout_ticks;
   void* args[] = {&P};
-  HIP_TRY(&ctx->last_error, hipLaunchCooperativeKernel((const void*)ctx->kernel, dim3(ctx->s.nwg), dim3(kThreads), args,
-                                                       (unsigned)ctx->lds, ctx->stream));
+  const void* fn = (const void*)(lm_last_only ? ctx->prompt_kernel : ctx->kernel);
+  HIP_TRY(&ctx->last_error,
+          hipLaunchCooperativeKernel(fn, dim3(ctx->s.nwg), dim3(kThreads), args, (unsigned)ctx->lds, ctx->stream));
   ctx->pos += n;
   ctx->epoch += (uint32_t)n;
   if (ctx->epoch == 0) ctx->epoch = 1;

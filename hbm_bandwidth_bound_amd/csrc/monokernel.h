@@ -38,7 +38,7 @@ struct KParams {
 };
 
 typedef void (*KernelFn)(KParams);
-KernelFn decode_kernel_for(int group, int head_dim);
+KernelFn decode_kernel_for(int group, int head_dim, bool prompt);
 int32_t lds_bytes_for(const Shape& s);
 
 // set-up kernels (pack.hip)

@@ -1,1000 +1,17 @@
-// monokernel.hip -- the persistent batch-1 decode kernel for MI355X (gfx950).
-//
-// One launch decodes n tokens; control never returns to the host in between (agentlenshq.com,
-// 《突破内存墙：在标准 GPU 上实现 3,000 tokens/s 的推理速度》, "The Monokernel Runtime"; aikraft.ru
-// «3000 токенов в секунду…», §04 "Моноядро": one resident GPU program covering MatMul,
-// attention, normalisation and sampling, with tight control of synchronisation, prefetch and
-// execution order). The design below is this library's own for CDNA4; the pages only say that
-// such kernels exist.
-//
-// Grid: one 512-thread workgroup (WG) per compute unit, all co-resident (cooperative launch).
-// Every one of the 8 waves streams its own contiguous slice of the packed weights from HBM into
-// registers with 16-byte-per-lane buffer loads, one batch of 8 KiB ahead of the batch it is
-// reducing. That batch is issued before the wave waits for the inputs of the next stage, so the
-// weight stream keeps flowing across every synchronisation point (the prefetch across
-// synchronisation points the pages call for); 64 KiB in flight per CU keep the HBM pipe busy.
-// GEMV arithmetic: a lane holds 4 bf16 weights of each of two rows at the same k, so one 16-byte
-// LDS read of the fp32 stage input feeds 8 weights of two rows; the weights are widened to fp32
-// and accumulated with fp32 FMA (the unit has VALU to spare at the streaming rate).
-// Inter-WG exchange uses 64-bit tagged words (fp32 value << 32 | epoch) written and read with
-// agent-scope atomics, so a reader knows a word is current by its tag alone: no grid barrier, no
-// flag round trip, no cache flush. Epochs are unique per decode step and buffers are per layer.
-// Inside a WG the waves meet at the hardware barrier with LDS-only fences, which never wait for
-// the weight loads in flight.
-//
-// Per layer: RMSNorm -> QKV (+RoPE) -> attention over a chunk of positions of one KV head
-// (split-K; online softmax per wave, waves merged in LDS) -> merge of the chunk partials ->
-// O (+residual) -> RMSNorm -> gate/up (SwiGLU) -> down (+residual). Then the final RMSNorm, the
-// LM head and the sampler.
-#include <hip/hip_runtime.h>
-#include <math.h>
-#include <stdint.h>
-
-#include "device_common.h"
-#include "layout.h"
-#include "monokernel.h"
+// monokernel.hip -- kernel selection and LDS sizing for the decode monokernel (the device code
+// is in monokernel_impl.h; its instantiations are in kernels_hd64.hip and kernels_hd128.hip).
+#include "monokernel_impl.h"
 
 namespace kie {
 
-// Optional per-wave cycle counters (compile with -DKIE_TRACE); free in normal builds.
-#ifdef KIE_TRACE
-#define TR_NOW() __builtin_readcyclecounter()
-#else
-#define TR_NOW() 0ull
-#endif
-enum TraceSlot : int {
-  T_FETCH = 0, T_GEMV = 1, T_FIN = 2, T_ATT = 3, T_MERGE = 4, T_BAR = 5, T_TOTAL = 6, T_BATCHES = 7,
-  T_NORM = 8, T_SAMPLE = 9
-};
-struct Tracer {
-#ifdef KIE_TRACE
-  uint64_t c[kTraceWords];
-  __device__ __forceinline__ Tracer() {
-    for (int i = 0; i < kTraceWords; ++i) c[i] = 0;
-  }
-  __device__ __forceinline__ void add(int k, uint64_t v) { c[k] += v; }
-  __device__ __forceinline__ void flush(uint64_t* dst, int lane) {
-    if (lane == 0)
-      for (int i = 0; i < kTraceWords; ++i) dst[i] = c[i];
-  }
-#else
-  __device__ __forceinline__ void add(int, uint64_t) {}
-  __device__ __forceinline__ void flush(uint64_t*, int) {}
-#endif
-};
+KernelFn kernel_hd64(int G, bool prompt);
+KernelFn kernel_hd128(int G, bool prompt);
 
-// ------------------------------------------------------------------------------------------
-// LDS layout
-// ------------------------------------------------------------------------------------------
-struct Lds {
-  float* act;      // GEMV input of the current stage (fp32)
-  float* xres;     // residual stream of the current layer (fp32, d)
-  float* part;     // [kMaxUnits][2] per-unit dot products of the current stage
-  float* scr;      // attention / merge / reduction scratch
-  float* q;        // attention: the group's queries [G][hd], the current k [hd] and v [hd]
-  float2* rope;    // (cos, sin) of the current position, hd/2 entries
-  uint32_t* ctl;   // control words
-};
-enum Ctl : int { C_ABORT = 0, C_COUNT = 4 };
+int32_t lds_bytes_for(const Shape& s) { return lds_bytes_for_impl(s); }
 
-__host__ __device__ inline int32_t act_floats(const Shape& s) {
-  int32_t a = s.d;
-  if (s.qdim() > a) a = s.qdim();
-  if (s.F > a) a = s.F;
-  return a;
-}
-__host__ __device__ inline int32_t scr_floats(const Shape& s) {
-  int32_t a = kWaves * s.group() * (s.hd + 2);
-  if (16 * kMergeDims * 3 > a) a = 16 * kMergeDims * 3;
-  if (2 * s.nwg > a) a = 2 * s.nwg;
-  if (a < 64) a = 64;
-  return (a + 3) & ~3;
-}
-int32_t lds_bytes_for(const Shape& s) {
-  return (act_floats(s) + s.d + 2 * kMaxUnits + scr_floats(s) + (s.group() + 2) * s.hd + s.hd) * 4 + C_COUNT * 4;
-}
-__device__ __forceinline__ Lds lds_map(uint8_t* smem, const Shape& s) {
-  Lds L;
-  uint8_t* p = smem;
-  L.act = (float*)p; p += (size_t)act_floats(s) * 4;
-  L.xres = (float*)p; p += (size_t)s.d * 4;
-  L.part = (float*)p; p += (size_t)2 * kMaxUnits * 4;
-  L.scr = (float*)p; p += (size_t)scr_floats(s) * 4;
-  L.q = (float*)p; p += (size_t)(s.group() + 2) * s.hd * 4;
-  L.rope = (float2*)p; p += (size_t)s.hd * 4;
-  L.ctl = (uint32_t*)p;
-  return L;
-}
-
-// ------------------------------------------------------------------------------------------
-// Attention work of this WG at context length n = pos + 1: KV head j over position chunk `chunk`.
-// ------------------------------------------------------------------------------------------
-struct Att {
-  int32_t j, chunk, c0, c1, ncache, nkt, has_p, cs, nch;
-};
-__device__ __forceinline__ Att att_info(const Shape& s, int32_t w, int32_t pos) {
-  Att a;
-  const int32_t n = pos + 1;
-  a.j = w % s.nkv;
-  a.chunk = w / s.nkv;
-  a.cs = att_chunk_len(s, n);
-  a.nch = (n + a.cs - 1) / a.cs;
-  a.c0 = a.chunk * a.cs;
-  a.c1 = a.c0 + a.cs < n ? a.c0 + a.cs : n;
-  if (a.c0 >= n) {
-    a.c1 = a.c0;
-    a.ncache = 0;
-    a.nkt = 0;
-    a.has_p = 0;
-  } else {
-    const int32_t ce = a.c1 < pos ? a.c1 : pos;  // cached positions end (pos itself is exchanged)
-    a.ncache = ce > a.c0 ? ce - a.c0 : 0;
-    const int32_t ppt = att_pos_per_tile(s);
-    a.nkt = (a.ncache + ppt - 1) / ppt;
-    a.has_p = pos < a.c1 ? 1 : 0;
-  }
-  return a;
-}
-
-__device__ __forceinline__ bool step_has_lm(const KParams& P, int32_t step) {
-  return !P.lm_last_only || step == P.n_steps - 1;
-}
-
-// A token id that indexes memory is always kept inside [0, V).
-__device__ __forceinline__ int32_t clamp_token(int32_t t, int32_t V) { return t < 0 ? 0 : (t >= V ? V - 1 : t); }
-
-// ------------------------------------------------------------------------------------------
-// Failure handling: every wait is bounded; on expiry the WG records an error and stops.
-// ------------------------------------------------------------------------------------------
-__device__ __forceinline__ void raise_error(const KParams& P, const Lds& L, uint32_t code) {
-  lds_st(&L.ctl[C_ABORT], 1u);
-  __hip_atomic_fetch_or(P.err, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t lds_ld_u(const uint32_t* p) { return __builtin_amdgcn_readfirstlane(lds_ld(p)); }
-__device__ __forceinline__ bool aborted(const Lds& L) { return lds_ld_u(&L.ctl[C_ABORT]) != 0; }
-__device__ __forceinline__ bool global_error(const KParams& P) {
-  return __builtin_amdgcn_readfirstlane(__hip_atomic_load(P.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0;
-}
-
-// Bounded spin: call expired() after every unsuccessful poll. Every 256th call it checks the WG's
-// abort flag and the elapsed time of this wait (wave-uniform).
-struct Waiter {
-  uint32_t spins = 0;
-  uint64_t start = 0;
-  __device__ __forceinline__ bool expired(const KParams& P, const Lds& L) {
-    if ((++spins & 255u) != 0) return false;
-    if (aborted(L)) return true;
-    const uint64_t t = now_ticks();
-    if (start == 0) {
-      start = t;
-      return false;
-    }
-    return t - start > (uint64_t)P.timeout_ticks;
-  }
-};
-
-// Barrier of the WG's 8 waves. The fences order LDS only, so weight loads stay in flight.
-__device__ __forceinline__ void bar() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// argmax candidate order: larger value first, then the lower index
-__device__ __forceinline__ bool better(float v, int32_t i, float bv, int32_t bi) {
-  return v > bv || (v == bv && i < bi);
-}
-
-// ------------------------------------------------------------------------------------------
-// One wave's state: its weight stream, the batch in flight, the WG's stage geometry.
-// ------------------------------------------------------------------------------------------
-struct Wk {
-  const KParams& P;
-  const Lds& L;
-  int32_t w, v, lane, tid;
-  bool fail;
-  Tracer tr;
-  StageGeo g[ST_COUNT];
-  int32_t nb[ST_COUNT];  // this wave's batches per stage
-  int32_t layer_b, lm_b;
-  const uint8_t* stream;  // this wave's first tile
-  v4u nxt[kBatch];        // the next batch of the stream (loads in flight)
-  int32_t pidx, pstep;    // that batch: index in its step's stream, and the step
-
-  __device__ __forceinline__ Wk(const KParams& p, const Lds& l, int32_t w_, int32_t v_, int32_t lane_)
-      : P(p), L(l), w(w_), v(v_), lane(lane_), tid(v_ * kWave + lane_), fail(false) {
-    layer_b = 0;
-    for (int st = 0; st < ST_COUNT; ++st) {
-      g[st] = stage_geo(P.s, st, w);
-      nb[st] = wave_batches(g[st], v);
-      if (st <= ST_DN) layer_b += nb[st];
-    }
-    lm_b = nb[ST_LM];
-    stream = P.packed + (size_t)P.wbase[w * kWaves + v] * kTileBytes;
-    pidx = -1;
-    pstep = 0;
-  }
-
-  // ------------------------------------------------------------ weight stream
-  __device__ __forceinline__ int32_t step_batches(int32_t step) const {
-    return P.s.L * layer_b + (step_has_lm(P, step) ? lm_b : 0);
-  }
-  // advance (pidx, pstep) to the next batch of the launch; pstep == n_steps once there is none
-  __device__ __forceinline__ void advance() {
-    ++pidx;
-    while (pstep < P.n_steps && pidx >= step_batches(pstep)) {
-      pidx = 0;
-      ++pstep;
-    }
-  }
-  // 8 loads of batch (pidx, pstep); past the launch's last batch the resource is empty and the
-  // loads return zeros without touching memory.
-  __device__ __forceinline__ void issue(v4u* buf) {
-    const bool live = pstep < P.n_steps;
-    const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(stream + (live ? (size_t)pidx * kBatch * kTileBytes : 0), live ? kBatch * kTileBytes : 0);
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) buf[b] = load16(rs, (uint32_t)(lane * 16 + b * kTileBytes));
-  }
-  // the launch's first batch
-  __device__ __forceinline__ void start() {
-    advance();
-    issue(nxt);
-  }
-  // hand the batch in flight to the caller and issue the one after it
-  __device__ __forceinline__ void take(v4u* cur) {
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) cur[b] = nxt[b];
-    advance();
-    issue(nxt);
-  }
-
-  // ------------------------------------------------------------ GEMV of one stage
-  // Stage fields selected through a switch, so that the arrays stay in scalar registers.
-  __device__ __forceinline__ StageGeo geo_of(int st) const {
-    switch (st) {
-      case ST_QKV: return g[ST_QKV];
-      case ST_O: return g[ST_O];
-      case ST_GU: return g[ST_GU];
-      case ST_DN: return g[ST_DN];
-      default: return g[ST_LM];
-    }
-  }
-  __device__ __forceinline__ int32_t nb_of(int st) const {
-    switch (st) {
-      case ST_QKV: return nb[ST_QKV];
-      case ST_O: return nb[ST_O];
-      case ST_GU: return nb[ST_GU];
-      case ST_DN: return nb[ST_DN];
-      default: return nb[ST_LM];
-    }
-  }
-  // Batch b of this wave in stage gs, against the input in LDS: the two dot products of each unit
-  // u land in part[2u] and part[2u + 1].
-  __device__ __forceinline__ void reduce_batch(const StageGeo& gs, int32_t b, const v4u* cur) {
-    const int32_t lks = gs.ks == 8 ? 3 : (gs.ks == 4 ? 2 : (gs.ks == 2 ? 1 : 0));
-    {
-      float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
-#pragma unroll
-      for (int sl = 0; sl < kBatch; ++sl) {
-        const int32_t us = sl >> lks, t = sl & (gs.ks - 1);
-        const int32_t u = v + kWaves * (b * gs.upb + us);
-        if (u < gs.nu) {
-          const int32_t j = (u % gs.S) * gs.ks + t;
-          const v4f x = *(const v4f*)(L.act + (size_t)j * kTileK + lane * 4);
-          const v4u wt = cur[sl];
-          a0 = fmaf(bf16lo(wt.x), x.x, a0);
-          a1 = fmaf(bf16hi(wt.x), x.y, a1);
-          a0 = fmaf(bf16lo(wt.y), x.z, a0);
-          a1 = fmaf(bf16hi(wt.y), x.w, a1);
-          b0 = fmaf(bf16lo(wt.z), x.x, b0);
-          b1 = fmaf(bf16hi(wt.z), x.y, b1);
-          b0 = fmaf(bf16lo(wt.w), x.z, b0);
-          b1 = fmaf(bf16hi(wt.w), x.w, b1);
-          if (t == gs.ks - 1) {
-            const float ya = wave_sum(a0 + a1), yb = wave_sum(b0 + b1);
-            if (lane == 0) {
-              L.part[2 * u] = ya;
-              L.part[2 * u + 1] = yb;
-            }
-            a0 = a1 = b0 = b1 = 0.f;
-          }
-        }
-      }
-    }
-  }
-  // After the stage's barrier: pair lp's outputs (the sum of its S units in a fixed order) go to
-  // fin(global pair, ya, yb).
-  template <typename Fin>
-  __device__ __forceinline__ void finalize(const StageGeo& gs, Fin fin) {
-    const uint64_t t0 = TR_NOW();
-    for (int32_t lp = tid; lp < gs.np; lp += kThreads) {
-      float ya = 0.f, yb = 0.f;
-      for (int32_t k = 0; k < gs.S; ++k) {
-        ya += L.part[2 * (lp * gs.S + k)];
-        yb += L.part[2 * (lp * gs.S + k) + 1];
-      }
-      fin(gs.pb + lp, ya, yb);
-    }
-    tr.add(T_FIN, TR_NOW() - t0);
-  }
-
-  // ------------------------------------------------------------ reductions
-  // sum over the WG's 512 threads in a fixed order; every thread gets the result
-  __device__ __forceinline__ float block_sum(float x) {
-    const float s = wave_sum(x);
-    if (lane == 0) L.scr[v] = s;
-    bar();
-    float t = 0.f;
-#pragma unroll
-    for (int k = 0; k < kWaves; ++k) t += L.scr[k];
-    bar();
-    return t;
-  }
-
-  // ------------------------------------------------------------ exchange gathers
-  // Poll the tagged words addr(k) of this thread's slots k < KM with valid(k) until each carries
-  // `epoch`; got(k, value) receives every value once. All waves of the WG call it; the wait is
-  // bounded. k is a compile-time index after unrolling, so per-slot values stay in registers.
-  template <int KM, typename Valid, typename Addr, typename Got>
-  __device__ __forceinline__ void poll(uint32_t epoch, Valid valid, Addr addr, Got got) {
-    uint32_t missing = 0;
-#pragma unroll
-    for (int k = 0; k < KM; ++k)
-      if (valid(k)) missing |= 1u << k;
-    uint64_t wv[KM];
-#pragma unroll
-    for (int k = 0; k < KM; ++k)
-      if (missing & (1u << k)) wv[k] = ld_x(addr(k));
-    Waiter wt;
-    while (true) {
-#pragma unroll
-      for (int k = 0; k < KM; ++k) {
-        if ((missing & (1u << k)) && (uint32_t)wv[k] == epoch) {
-          missing &= ~(1u << k);
-          got(k, __uint_as_float((uint32_t)(wv[k] >> 32)));
-        }
-      }
-      if (__builtin_amdgcn_ballot_w64(missing != 0) == 0 || fail) break;
-      __builtin_amdgcn_s_sleep(1);
-      if (wt.expired(P, L) || ((wt.spins & 255u) == 0 && global_error(P))) {
-        fail = true;
-        raise_error(P, L, KERR_TIMEOUT);
-        break;
-      }
-#pragma unroll
-      for (int k = 0; k < KM; ++k)
-        if (missing & (1u << k)) wv[k] = ld_x(addr(k));
-    }
-  }
-  // n words into LDS floats dst; returns their sum of squares (fixed order) if want_ss.
-  // Ends with a barrier: dst is complete for every wave.
-  __device__ __forceinline__ float fetch_f32(const uint64_t* src, int32_t n, float* dst, uint32_t epoch,
-                                             bool want_ss) {
-    const uint64_t t0 = TR_NOW();
-    constexpr int KM = 8;
-    for (int32_t base = 0; base < n; base += KM * kThreads) {
-      const int32_t e0 = base + tid;
-      poll<KM>(
-          epoch, [&](int k) { return e0 + k * kThreads < n; }, [&](int k) { return src + e0 + k * kThreads; },
-          [&](int k, float x) { dst[e0 + k * kThreads] = x; });
-    }
-    tr.add(T_FETCH, TR_NOW() - t0);
-    float ss = 0.f;
-    if (want_ss) {
-      for (int32_t e = tid; e < n; e += kThreads) ss = fmaf(dst[e], dst[e], ss);  // this thread's own words
-      ss = block_sum(ss);
-    } else {
-      bar();
-    }
-    return ss;
-  }
-  // act = (xres * r) * g with r = 1 / sqrt(ss / d + eps). Ends with a barrier.
-  __device__ __forceinline__ void norm_to_act(float ss, const uint16_t* gain) {
-    const uint64_t t0 = TR_NOW();
-    const int32_t d = P.s.d;
-    const float r = 1.0f / sqrtf(ss / (float)d + P.s.eps);
-    for (int32_t rec = tid; rec < d / 4; rec += kThreads) {
-      const v4f x = *(const v4f*)(L.xres + 4 * rec);
-      const uint2 gg = *(const uint2*)(gain + 4 * rec);
-      *(v4f*)(L.act + 4 * rec) = v4f{(x.x * r) * bf16lo(gg.x), (x.y * r) * bf16hi(gg.x), (x.z * r) * bf16lo(gg.y),
-                                     (x.w * r) * bf16hi(gg.y)};
-    }
-    tr.add(T_NORM, TR_NOW() - t0);
-    bar();
-  }
-
-  // argmax over the WG's threads (each holds a candidate); every thread gets the winner
-  __device__ __forceinline__ void block_argmax(float* bv, int32_t* bi) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(*bv, o, kWave);
-      const int32_t oi = __shfl_xor(*bi, o, kWave);
-      if (better(ov, oi, *bv, *bi)) {
-        *bv = ov;
-        *bi = oi;
-      }
-    }
-    if (lane == 0) {
-      L.scr[2 * v] = *bv;
-      L.scr[2 * v + 1] = __int_as_float(*bi);
-    }
-    bar();
-    float bv2 = L.scr[0];
-    int32_t bi2 = __float_as_int(L.scr[1]);
-    for (int k = 1; k < kWaves; ++k) {
-      const float ov = L.scr[2 * k];
-      const int32_t oi = __float_as_int(L.scr[2 * k + 1]);
-      if (better(ov, oi, bv2, bi2)) {
-        bv2 = ov;
-        bi2 = oi;
-      }
-    }
-    bar();
-    *bv = bv2;
-    *bi = bi2;
-  }
-};
-
-// ------------------------------------------------------------------------------------------
-// Attention for KV head j over this WG's chunk of positions. Wave v takes the chunk's K/V tiles
-// v, v + 8, ...; each lane keeps an online softmax (exp2 domain) over the positions it sees, the
-// position rows of a wave are combined with shuffles and the 8 waves in LDS; one partial
-// (acc[hd], m, l) per query head of the group is published, m being the chunk maximum.
-// ------------------------------------------------------------------------------------------
-template <int G, int HD>
-__device__ __forceinline__ void attention(Wk& K, const Att& at, int32_t l, int32_t pos, uint32_t ep) {
-  const KParams& P = K.P;
-  const Lds& L = K.L;
-  const Shape& s = P.s;
-  const Exch& X = P.exo;
-  constexpr int LPP = HD / 8;    // lanes per position
-  constexpr int PPT = 64 / LPP;  // positions per tile
-  constexpr int AB = 2;  // K (and V) tiles per batch
-  const int lane = K.lane, v = K.v;
-  const int lpos = lane / LPP, dg = lane % LPP;
-  const int32_t ntw = at.nkt > v ? (at.nkt - v + kWaves - 1) / kWaves : 0;  // this wave's tiles
-  const int32_t nbw = (ntw + AB - 1) / AB;
-  const uint32_t kvbytes = (uint32_t)at.ncache * HD * 2;  // lanes past the cached rows read zeros
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(P.kv + kv_offset(s, l, 0, at.j, at.c0), kvbytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(P.kv + kv_offset(s, l, 1, at.j, at.c0), kvbytes);
-  auto kv_issue = [&](int32_t bi, v4u* kb, v4u* vb) {
-#pragma unroll
-    for (int e = 0; e < AB; ++e) {
-      const int32_t i = bi * AB + e;
-      if (i < ntw) {
-        const uint32_t off = (uint32_t)((v + kWaves * i) * kTileBytes + lane * 16);
-        kb[e] = load16(krs, off);
-        vb[e] = load16(vrs, off);
-      } else {
-        kb[e] = v4u{0u, 0u, 0u, 0u};
-        vb[e] = v4u{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  v4u kn[AB], vn[AB];
-  if (nbw > 0) kv_issue(0, kn, vn);  // cached rows do not depend on this step: load before the inputs
-
-  // inputs: the group's queries, then the current position's k and v when it lies in this chunk
-  {
-    const uint64_t t0 = TR_NOW();
-    const uint64_t* qsrc = P.ex + X.q + (int64_t)l * s.qdim() + (int64_t)at.j * G * HD;
-    const uint64_t* ksrc = P.ex + X.k + (int64_t)l * s.kvdim() + at.j * HD;
-    const uint64_t* vsrc = P.ex + X.v + (int64_t)l * s.kvdim() + at.j * HD;
-    const int32_t n = G * HD + (at.has_p ? 2 * HD : 0);
-    constexpr int KM = ((G + 2) * HD + kThreads - 1) / kThreads;
-    K.poll<KM>(
-        ep, [&](int k) { return K.tid + k * kThreads < n; },
-        [&](int k) {
-          const int32_t e = K.tid + k * kThreads;
-          return e < G * HD ? qsrc + e : (e < (G + 1) * HD ? ksrc + (e - G * HD) : vsrc + (e - (G + 1) * HD));
-        },
-        [&](int k, float x) { L.q[K.tid + k * kThreads] = x; });
-    K.tr.add(T_FETCH, TR_NOW() - t0);
-    bar();
-  }
-  const uint64_t ta = TR_NOW();
-  const float scale = 1.4426950408889634f / sqrtf((float)HD);  // softmax in the exp2 domain
-  float qr[G][8];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const v4f a = *(const v4f*)(L.q + g * HD + dg * 8);
-    const v4f b = *(const v4f*)(L.q + g * HD + dg * 8 + 4);
-    qr[g][0] = a.x; qr[g][1] = a.y; qr[g][2] = a.z; qr[g][3] = a.w;
-    qr[g][4] = b.x; qr[g][5] = b.y; qr[g][6] = b.z; qr[g][7] = b.w;
-  }
-  float m[G], ls[G], acc[G][8];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = -INFINITY;
-    ls[g] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
-  }
-  auto update = [&](const v4u kw, const v4u vw, bool valid) {
-    const float kf[8] = {bf16lo(kw.x), bf16hi(kw.x), bf16lo(kw.y), bf16hi(kw.y),
-                         bf16lo(kw.z), bf16hi(kw.z), bf16lo(kw.w), bf16hi(kw.w)};
-    const float vf[8] = {bf16lo(vw.x), bf16hi(vw.x), bf16lo(vw.y), bf16hi(vw.y),
-                         bf16lo(vw.z), bf16hi(vw.z), bf16lo(vw.w), bf16hi(vw.w)};
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float d = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) d = fmaf(qr[g][e], kf[e], d);
-      d = LPP == 16 ? row16_sum(d) : row8_sum(d);
-      const float sc = d * scale;
-      if (valid) {
-        const float mn = fmaxf(m[g], sc);
-        const float c = exp2f(m[g] - mn);  // 0 while m is -inf
-        const float pr = exp2f(sc - mn);
-        ls[g] = fmaf(ls[g], c, pr);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(acc[g][e], c, pr * vf[e]);
-        m[g] = mn;
-      }
-    }
-  };
-  for (int32_t bi = 0; bi < nbw; ++bi) {
-    v4u kc[AB], vc[AB];
-#pragma unroll
-    for (int e = 0; e < AB; ++e) {
-      kc[e] = kn[e];
-      vc[e] = vn[e];
-    }
-    if (bi + 1 < nbw) kv_issue(bi + 1, kn, vn);
-#pragma unroll
-    for (int e = 0; e < AB; ++e) {
-      const int32_t i = bi * AB + e;
-      if (i < ntw) update(kc[e], vc[e], (v + kWaves * i) * PPT + lpos < at.ncache);
-    }
-  }
-  // the current position: its K/V come from the exchange, rounded to bf16 like the cache
-  if (at.has_p && v == at.nkt % kWaves) {
-    auto cur_row = [&](const float* src) {
-      uint32_t b[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) b[e] = f32_to_bf16(src[dg * 8 + e]);
-      return v4u{b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16)};
-    };
-    update(cur_row(L.q + G * HD), cur_row(L.q + (G + 1) * HD), lpos == 0);
-  }
-  // combine the position rows of the wave (lanes with the same dims)
-#pragma unroll
-  for (int off = LPP; off < kWave; off <<= 1) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float mo = __shfl_xor(m[g], off, kWave);
-      const float lo = __shfl_xor(ls[g], off, kWave);
-      const float M = fmaxf(m[g], mo);
-      const float f = m[g] == -INFINITY ? 0.f : exp2f(m[g] - M);
-      const float fo = mo == -INFINITY ? 0.f : exp2f(mo - M);
-      ls[g] = ls[g] * f + lo * fo;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float ao = __shfl_xor(acc[g][e], off, kWave);
-        acc[g][e] = acc[g][e] * f + ao * fo;
-      }
-      m[g] = M;
-    }
-  }
-  float* ws = L.scr + v * G * (HD + 2);
-  if (lpos == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ws[g * (HD + 2) + dg * 8 + e] = acc[g][e];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      ws[g * (HD + 2) + HD] = m[g];
-      ws[g * (HD + 2) + HD + 1] = ls[g];
-    }
-  }
-  bar();
-  // combine the 8 waves and publish
-  uint64_t* part = P.ex + X.part + ((int64_t)l * s.nwg + K.w) * X.part_words;
-  for (int e = K.tid; e < G * (HD + 2); e += kThreads) {
-    const int g = e / (HD + 2), k = e % (HD + 2);
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, L.scr[(w * G + g) * (HD + 2) + HD]);
-    float out;
-    if (k == HD) {
-      out = M;
-    } else {
-      out = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = L.scr[(w * G + g) * (HD + 2) + HD];
-        const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
-        out = fmaf(L.scr[(w * G + g) * (HD + 2) + k], f, out);
-      }
-    }
-    st_x(part + e, tag_f(out, ep));
-  }
-  // the WG whose chunk holds the current position appends its K/V rows to the cache
-  if (at.has_p) {
-    const float* kp = L.q + G * HD;
-    const float* vp = L.q + (G + 1) * HD;
-    for (int e = K.tid; e < HD / 2; e += kThreads) {
-      const uint32_t k2 = f32_to_bf16(kp[2 * e]) | (f32_to_bf16(kp[2 * e + 1]) << 16);
-      const uint32_t v2 = f32_to_bf16(vp[2 * e]) | (f32_to_bf16(vp[2 * e + 1]) << 16);
-      st_x32((uint32_t*)(P.kv + kv_offset(s, l, 0, at.j, pos)) + e, k2);
-      st_x32((uint32_t*)(P.kv + kv_offset(s, l, 1, at.j, pos)) + e, v2);
-    }
-  }
-  K.tr.add(T_ATT, TR_NOW() - ta);
-  bar();  // scratch reuse
-}
-
-// Merge of the chunk partials of one (query head, 32-dim slice): 16 chunk lanes x 32 dims.
-__device__ __forceinline__ void merge_unit(Wk& K, const Att& at, int32_t l, int32_t u, uint32_t epoch) {
-  const KParams& P = K.P;
-  const Lds& L = K.L;
-  const Shape& s = P.s;
-  const int32_t slices = s.hd / kMergeDims;
-  const int32_t h = u / slices, sl = u % slices;
-  const int32_t G = s.group();
-  const int32_t j = h / G, g = h % G;
-  constexpr int CL = kThreads / kMergeDims;  // 16 chunk lanes
-  const int dim = K.tid % kMergeDims, cl = K.tid / kMergeDims;
-  float M = -INFINITY, S = 0.f, A = 0.f;
-  constexpr int KM = 4;  // chunks per thread in one pass (chunk lane stride 16)
-  for (int32_t c0 = cl; c0 < at.nch && !K.fail; c0 += CL * KM) {
-    uint64_t wm[KM], wl[KM], wa[KM];
-    uint32_t todo = 0;
-#pragma unroll
-    for (int k = 0; k < KM; ++k)
-      if (c0 + CL * k < at.nch) todo |= 1u << k;
-    const uint32_t present = todo;
-    Waiter wt;
-    while (__builtin_amdgcn_ballot_w64(todo != 0) != 0) {
-#pragma unroll
-      for (int k = 0; k < KM; ++k) {
-        if (todo & (1u << k)) {
-          const int32_t ch = c0 + CL * k;
-          const uint64_t* pp =
-              P.ex + P.exo.part + ((int64_t)l * s.nwg + ch * s.nkv + j) * P.exo.part_words + g * (s.hd + 2);
-          wm[k] = ld_x(pp + s.hd);
-          wl[k] = ld_x(pp + s.hd + 1);
-          wa[k] = ld_x(pp + sl * kMergeDims + dim);
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < KM; ++k)
-        if ((todo & (1u << k)) && (uint32_t)wm[k] == epoch && (uint32_t)wl[k] == epoch && (uint32_t)wa[k] == epoch)
-          todo &= ~(1u << k);
-      if (__builtin_amdgcn_ballot_w64(todo != 0) != 0) {
-        __builtin_amdgcn_s_sleep(1);
-        if (wt.expired(P, L) || ((wt.spins & 255u) == 0 && global_error(P))) {
-          K.fail = true;
-          raise_error(P, L, KERR_TIMEOUT);
-          break;
-        }
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < KM; ++k) {
-      if (present & (1u << k)) {
-        const float mk = __uint_as_float((uint32_t)(wm[k] >> 32));
-        const float lk = __uint_as_float((uint32_t)(wl[k] >> 32));
-        const float ak = __uint_as_float((uint32_t)(wa[k] >> 32));
-        const float Mn = fmaxf(M, mk);
-        const float fo = M == -INFINITY ? 0.f : exp2f(M - Mn);
-        const float fn = mk == -INFINITY ? 0.f : exp2f(mk - Mn);
-        S = S * fo + lk * fn;
-        A = A * fo + ak * fn;
-        M = Mn;
-      }
-    }
-  }
-  float* ms = L.scr;  // [16][32][3]
-  ms[(cl * kMergeDims + dim) * 3 + 0] = M;
-  ms[(cl * kMergeDims + dim) * 3 + 1] = S;
-  ms[(cl * kMergeDims + dim) * 3 + 2] = A;
-  bar();
-  if (K.tid < kMergeDims) {
-    float Mt = -INFINITY;
-    for (int k = 0; k < CL; ++k) Mt = fmaxf(Mt, ms[(k * kMergeDims + K.tid) * 3]);
-    float St = 0.f, At = 0.f;
-    for (int k = 0; k < CL; ++k) {
-      const float mk = ms[(k * kMergeDims + K.tid) * 3];
-      const float f = mk == -INFINITY ? 0.f : exp2f(mk - Mt);
-      St = fmaf(ms[(k * kMergeDims + K.tid) * 3 + 1], f, St);
-      At = fmaf(ms[(k * kMergeDims + K.tid) * 3 + 2], f, At);
-    }
-    st_x(P.ex + P.exo.o + (int64_t)l * s.qdim() + h * s.hd + sl * kMergeDims + K.tid, tag_f(At / St, epoch));
-  }
-  bar();
-}
-
-// The decode program of one wave. Its weight batches are consumed by one loop; the batch after
-// the current one is always in flight. Between batches, boundary() runs the work that separates
-// two stages -- finalising the outputs,
-// attention, the merge, the exchange gathers, RMSNorm, sampling -- whenever the current stage has
-// no batch left for this wave. Every wave runs every boundary, so the WG barriers inside match.
-enum Boundary : int { B_START = 0, B_QKV = 1, B_O = 2, B_GU = 3, B_DN = 4, B_LM = 5, B_END = 6 };
-
-template <int G, int HD>
-__device__ __forceinline__ void decode(Wk& K) {
-  const KParams& P = K.P;
-  const Lds& L = K.L;
-  const Shape& s = P.s;
-  const Exch& X = P.exo;
-  uint64_t* ex = P.ex;
-  const uint64_t t_start = TR_NOW();
-  const int32_t tid = K.tid;
-  int32_t tok = P.first_tok[0];
-  if (tok < 0 || tok >= s.V) {
-    if (K.w == 0 && tid == 0) __hip_atomic_fetch_or(P.err, KERR_BAD_TOKEN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    tok = 0;
-  }
-  tok = clamp_token(__builtin_amdgcn_readfirstlane(tok), s.V);
-  K.start();  // the stream's first batch
-
-  int32_t step = 0, l = 0;
-  int32_t pos = P.pos0;
-  uint32_t ep = P.epoch0;
-  Att at = att_info(s, K.w, pos);
-  bool lm = step_has_lm(P, 0);
-  float ss = 0.f;
-  int bnd = B_START;  // the next boundary
-  int st = -1;        // stage of the batches being reduced
-  int32_t rem = 0, b = 0;
-  bool done = false;
-
-  auto boundary = [&]() {
-    while (rem == 0 && !done) {
-      const uint64_t tb = TR_NOW();
-      const int bnd_run = bnd;
-      switch (bnd) {
-        case B_START: {  // embedding row -> residual stream, RMSNorm of layer 0
-          if (tid < s.hd / 2) L.rope[tid] = P.rope[(int64_t)pos * (s.hd / 2) + tid];
-          float sq = 0.f;
-          for (int32_t i = tid; i < s.d; i += kThreads) {
-            const float x = __uint_as_float((uint32_t)P.embed[(int64_t)tok * s.d + i] << 16);
-            L.xres[i] = x;
-            sq = fmaf(x, x, sq);
-          }
-          ss = K.block_sum(sq);
-          K.norm_to_act(ss, P.norms);
-          st = ST_QKV;
-          bnd = B_QKV;
-          break;
-        }
-        case B_QKV: {  // QKV outputs (+RoPE) -> attention -> merge -> gather o
-          bar();
-          uint64_t* qx = ex + X.q + (int64_t)l * s.qdim();
-          uint64_t* kx = ex + X.k + (int64_t)l * s.kvdim();
-          uint64_t* vx = ex + X.v + (int64_t)l * s.kvdim();
-          K.finalize(K.g[ST_QKV], [&](int32_t gp, float ya, float yb) {
-            const int32_t half = s.hd / 2;
-            const int32_t hs = gp / half, i = gp % half;
-            if (hs < s.nq + s.nkv) {  // query and key heads are rotated
-              const float2 cs = L.rope[i];
-              const float ra = ya * cs.x - yb * cs.y, rb = yb * cs.x + ya * cs.y;
-              ya = ra;
-              yb = rb;
-            }
-            uint64_t* dst;
-            int32_t h;
-            if (hs < s.nq) {
-              dst = qx;
-              h = hs;
-            } else if (hs < s.nq + s.nkv) {
-              dst = kx;
-              h = hs - s.nq;
-            } else {
-              dst = vx;
-              h = hs - s.nq - s.nkv;
-            }
-            st_x(dst + h * s.hd + i, tag_f(ya, ep));
-            st_x(dst + h * s.hd + i + half, tag_f(yb, ep));
-          });
-          if (at.c0 <= pos) attention<G, HD>(K, at, l, pos, ep);
-          {
-            const uint64_t tm = TR_NOW();
-            const int32_t nu = merge_units(s);
-            const int32_t u0 = (int32_t)(((int64_t)K.w * nu + s.nwg - 1) / s.nwg);
-            for (int32_t u = u0; u < nu && merge_unit_wg(s, u) == K.w; ++u) merge_unit(K, at, l, u, ep);
-            K.tr.add(T_MERGE, TR_NOW() - tm);
-          }
-          K.fetch_f32(ex + X.o + (int64_t)l * s.qdim(), s.qdim(), L.act, ep, false);
-          st = ST_O;
-          bnd = B_O;
-          break;
-        }
-        case B_O: {  // O outputs + residual -> gather xa -> RMSNorm
-          bar();
-          if (at.has_p) __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this WG's K/V rows are complete first
-          uint64_t* xa = ex + X.xa + (int64_t)l * s.d;
-          K.finalize(K.g[ST_O], [&](int32_t gp, float ya, float yb) {
-            st_x(xa + 2 * gp, tag_f(L.xres[2 * gp] + ya, ep));
-            st_x(xa + 2 * gp + 1, tag_f(L.xres[2 * gp + 1] + yb, ep));
-          });
-          bar();  // every wave is done with xres before it is replaced
-          ss = K.fetch_f32(xa, s.d, L.xres, ep, true);
-          K.norm_to_act(ss, P.norms + (int64_t)l * 2 * s.d + s.d);
-          st = ST_GU;
-          bnd = B_GU;
-          break;
-        }
-        case B_GU: {  // SwiGLU outputs -> gather h
-          bar();
-          uint64_t* hx = ex + X.h + (int64_t)l * s.F;
-          K.finalize(K.g[ST_GU], [&](int32_t gp, float ya, float yb) {
-            st_x(hx + gp, tag_f((ya / (1.0f + expf(-ya))) * yb, ep));
-          });
-          K.fetch_f32(hx, s.F, L.act, ep, false);
-          st = ST_DN;
-          bnd = B_DN;
-          break;
-        }
-        case B_DN: {  // down outputs + residual -> next layer's input (or the LM head's)
-          bar();
-          uint64_t* xf = ex + X.xf + (int64_t)(l + 1) * s.d;
-          K.finalize(K.g[ST_DN], [&](int32_t gp, float ya, float yb) {
-            st_x(xf + 2 * gp, tag_f(L.xres[2 * gp] + ya, ep));
-            st_x(xf + 2 * gp + 1, tag_f(L.xres[2 * gp + 1] + yb, ep));
-          });
-          bar();
-          if (aborted(L)) {
-            bnd = B_END;
-            st = -1;
-          } else if (l + 1 < s.L) {
-            ++l;
-            ss = K.fetch_f32(xf, s.d, L.xres, ep, true);
-            K.norm_to_act(ss, P.norms + (int64_t)l * 2 * s.d);
-            st = ST_QKV;
-            bnd = B_QKV;
-          } else if (lm) {
-            ss = K.fetch_f32(xf, s.d, L.xres, ep, true);
-            K.norm_to_act(ss, P.norms + (int64_t)s.L * 2 * s.d);
-            st = ST_LM;
-            bnd = B_LM;
-          } else {
-            st = -1;
-            bnd = B_END;
-          }
-          break;
-        }
-        case B_LM:
-        case B_END: {  // LM outputs and this WG's argmax candidate; the grid-wide join; next token
-          float bv = -INFINITY;
-          int32_t bi = 0x7fffffff;
-          if (bnd == B_LM) {
-            bar();
-            float* lo = P.logits_out ? P.logits_out + (P.lm_last_only ? 0 : (int64_t)step * s.V) : nullptr;
-            K.finalize(K.g[ST_LM], [&](int32_t gp, float ya, float yb) {
-              const int32_t ra = 2 * gp, rb = 2 * gp + 1;
-              if (better(ya, ra, bv, bi)) {
-                bv = ya;
-                bi = ra;
-              }
-              if (better(yb, rb, bv, bi)) {
-                bv = yb;
-                bi = rb;
-              }
-              if (lo) {
-                lo[ra] = ya;
-                lo[rb] = yb;
-              }
-            });
-          }
-          // every WG gathers all candidates: no WG reuses a step's exchange buffers before every
-          // WG has finished reading them
-          const uint64_t tsm = TR_NOW();
-          K.block_argmax(&bv, &bi);
-          if (tid == 0) {
-            st_x(ex + X.lm + 2 * K.w, tag_f(bv, ep));
-            st_x(ex + X.lm + 2 * K.w + 1, tag_u((uint32_t)bi, ep));
-          }
-          K.fetch_f32(ex + X.lm, 2 * s.nwg, L.scr, ep, false);
-          bv = -INFINITY;
-          bi = 0x7fffffff;
-          for (int k = tid; k < s.nwg; k += kThreads) {
-            const float cv = L.scr[2 * k];
-            const int32_t ci = __float_as_int(L.scr[2 * k + 1]);
-            if (better(cv, ci, bv, bi)) {
-              bv = cv;
-              bi = ci;
-            }
-          }
-          bar();  // every thread has read its candidates before scr is reused
-          K.block_argmax(&bv, &bi);
-          K.tr.add(T_SAMPLE, TR_NOW() - tsm);
-          int32_t next = clamp_token(bi, s.V);
-          if (lm && K.w == 0 && tid == 0) {
-            if (P.tokens_out) P.tokens_out[step] = next;
-            if (P.last_tok_out && step == P.n_steps - 1) P.last_tok_out[0] = next;
-          }
-          if (P.forced && step + 1 < P.n_steps) {
-            int32_t f = P.forced[step];
-            if (f < 0 || f >= s.V) {
-              if (K.w == 0 && tid == 0)
-                __hip_atomic_fetch_or(P.err, KERR_BAD_TOKEN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              f = 0;
-            }
-            next = clamp_token(__builtin_amdgcn_readfirstlane(f), s.V);
-          }
-          tok = next;
-          ++step;
-          if (step >= P.n_steps || aborted(L)) {
-            done = true;
-          } else {
-            l = 0;
-            pos = P.pos0 + step;
-            ep = P.epoch0 + (uint32_t)step;
-            at = att_info(s, K.w, pos);
-            lm = step_has_lm(P, step);
-          }
-          st = -1;
-          bnd = B_START;
-          break;
-        }
-      }
-      K.tr.add(T_BAR, TR_NOW() - tb);
-      {
-        const uint64_t dt = TR_NOW() - tb;  // per boundary kind (constant slots keep the counters in registers)
-        switch (bnd_run) {
-          case B_START: K.tr.add(10, dt); break;
-          case B_QKV: K.tr.add(11, dt); break;
-          case B_O: K.tr.add(12, dt); break;
-          case B_GU: K.tr.add(13, dt); break;
-          case B_DN: K.tr.add(14, dt); break;
-          default: K.tr.add(15, dt); break;
-        }
-      }
-      rem = st >= 0 ? K.nb_of(st) : 0;
-      b = 0;
-    }
-  };
-
-  while (true) {
-    boundary();
-    if (done) break;
-    const uint64_t tg = TR_NOW();
-    v4u cur[kBatch];
-    K.take(cur);
-    K.reduce_batch(K.geo_of(st), b, cur);
-    K.tr.add(T_GEMV, TR_NOW() - tg);
-    K.tr.add(T_BATCHES, 1);
-    --rem;
-    ++b;
-  }
-  K.tr.add(T_TOTAL, TR_NOW() - t_start);
-  K.tr.flush(P.trace + ((int64_t)K.w * kWaves + K.v) * kTraceWords, K.lane);
-}
-
-template <int G, int HD>
-__global__ void __launch_bounds__(kThreads, 1) kie_decode_kernel(KParams P) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  const Lds L = lds_map(smem, P.s);
-  if (threadIdx.x < C_COUNT) L.ctl[threadIdx.x] = 0;
-  __syncthreads();
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
-  Wk K(P, L, blockIdx.x, wave, threadIdx.x % kWave);
-  decode<G, HD>(K);
-}
-
-// Instantiations for the supported (group size, head_dim) combinations.
-KernelFn decode_kernel_for(int G, int HD) {
-  if (HD == 128) {
-    switch (G) {
-      case 1: return kie_decode_kernel<1, 128>;
-      case 2: return kie_decode_kernel<2, 128>;
-      case 4: return kie_decode_kernel<4, 128>;
-      case 8: return kie_decode_kernel<8, 128>;
-    }
-  } else if (HD == 64) {
-    switch (G) {
-      case 1: return kie_decode_kernel<1, 64>;
-      case 2: return kie_decode_kernel<2, 64>;
-      case 4: return kie_decode_kernel<4, 64>;
-      case 8: return kie_decode_kernel<8, 64>;
-    }
-  }
+KernelFn decode_kernel_for(int G, int HD, bool prompt) {
+  if (HD == 128) return kernel_hd128(G, prompt);
+  if (HD == 64) return kernel_hd64(G, prompt);
   return nullptr;
 }
 
