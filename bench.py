@@ -156,6 +156,17 @@ def main():
     algo_bytes = traffic.launch_bytes(m, P, K)
     achieved_gbps = algo_bytes / (launch_ms * 1e-3) / 1e9
 
+    # the same K steps with top-k sampling (k 50, T 0.8, seed 2): one more launch
+    from hbm_bandwidth_bound_amd.kie import sampling
+    eng.set_position(P)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    eng.generate(first, K, out, smp=sampling(50, 0.8, 2))
+    e1.record(stream)
+    torch.cuda.synchronize()
+    eng.sync()
+    topk_tok_s = K / (e0.elapsed_time(e1) * 1e-3)
+
     # one-token launches (the per-launch overhead comparison)
     single = None
     if args.single_step_launches > 0:
@@ -220,6 +231,7 @@ def main():
                   "bytes_per_token": algo_bytes / K, "stream_read_ceiling_GBps": round(ceiling_gbps, 1),
                   "frac_of_stream_ceiling": round(achieved_gbps / ceiling_gbps, 4),
                   "ttft_ms_prompt_pass": round(ttft_ms, 2), "one_token_launches": single,
+                  "topk50_T0.8_tok_s": round(topk_tok_s, 2),
                   "source_sha": source_hash()},
     }
     print(json.dumps(res), flush=True)

@@ -1,5 +1,6 @@
 // api.cpp -- host side of the C ABI declared in include/kie.h: validation, set-up, launches.
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -392,9 +393,20 @@ static kie_status launch(kie_ctx* ctx, const int32_t* first, int32_t n, const in
     set_err(&ctx->last_error, "first token pointer is NULL or n <= 0");
     return KIE_ERR_INVALID_ARG;
   }
-  if (smp && smp->top_k > 1) {
-    set_err(&ctx->last_error, "top-k sampling is not available in this build (use top_k <= 1)");
-    return KIE_ERR_UNSUPPORTED;
+  const int32_t top_k = smp && smp->top_k > 1 ? smp->top_k : 1;
+  if (top_k > 1) {
+    if (top_k > kMaxTopK || top_k > ctx->s.V) {
+      set_err(&ctx->last_error, "top_k %d exceeds the supported maximum %d or the vocabulary", top_k, kMaxTopK);
+      return KIE_ERR_UNSUPPORTED;
+    }
+    if (!(smp->temperature > 0.f) || !(smp->temperature < INFINITY)) {
+      set_err(&ctx->last_error, "temperature must be positive and finite for top-k sampling");
+      return KIE_ERR_INVALID_ARG;
+    }
+    if (topk_merge_floats(ctx->s, top_k) > topk_capacity_floats(ctx->s)) {
+      set_err(&ctx->last_error, "top_k %d does not fit this model's on-chip merge space", top_k);
+      return KIE_ERR_UNSUPPORTED;
+    }
   }
   if ((int64_t)ctx->pos + n > ctx->s.max_seq) {
     set_err(&ctx->last_error, "position %d + %d tokens exceeds max_seq_len %d", ctx->pos, n, ctx->s.max_seq);
@@ -422,6 +434,9 @@ static kie_status launch(kie_ctx* ctx, const int32_t* first, int32_t n, const in
   P.n_steps = n;
   P.epoch0 = ctx->epoch;
   P.lm_last_only = lm_last_only;
+  P.top_k = top_k;
+  P.temperature = top_k > 1 ? smp->temperature : 1.0f;
+  P.seed = smp ? smp->seed : 0;
   P.timeout_ticks = ctx->timeout_ticks;
   void* args[] = {&P};
   const void* fn = (const void*)(lm_last_only ? ctx->prompt_kernel : ctx->kernel);

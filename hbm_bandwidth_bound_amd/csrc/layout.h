@@ -36,6 +36,7 @@ constexpr int kTileK = 256;  // k per tile and row
 constexpr int kBatch = 8;    // tile slots per batch
 constexpr int kMaxWG = 1024;
 constexpr int kMaxUnits = 2048;  // units of one stage per WG (LDS partial sums)
+constexpr int kMaxTopK = 64;     // largest k of top-k sampling
 
 enum Stage : int { ST_QKV = 0, ST_O = 1, ST_GU = 2, ST_DN = 3, ST_LM = 4, ST_COUNT = 5 };
 
@@ -136,6 +137,36 @@ KIE_HD void pair_rows(const Shape& s, int st, int32_t gp, int* mat, int32_t* ra,
   }
 }
 
+// LM-head rows of the WG that owns the most of them (an even split never gives more than this)
+KIE_HD int32_t lm_rows_max(const Shape& s) { return 2 * ((s.V / 2 + s.nwg - 1) / s.nwg); }
+
+// Top-k merge of the per-WG candidate lists, in floats of WG-local memory (16-byte aligned
+// pieces): the list heads [nwg][2], the selected lists [nsel], their active lengths [nsel] and
+// offsets [nsel + 1], the merged top k [k][2], the selected lists' entries [nsel][ke][2] and the
+// compacted active entries (as many), where nsel = min(k, nwg) and ke = min(k, lm_rows_max).
+struct TopkLayout {
+  int32_t nsel, ke;
+  int32_t heads, sel, alen, off, top, ent, cmp, total;
+};
+KIE_HD int32_t align4(int32_t x) { return (x + 3) & ~3; }
+KIE_HD TopkLayout topk_layout(const Shape& s, int32_t k) {
+  TopkLayout t;
+  const int32_t lr = lm_rows_max(s);
+  t.nsel = k < s.nwg ? k : s.nwg;
+  t.ke = k < lr ? k : lr;
+  int32_t o = 0;
+  t.heads = o; o = align4(o + 2 * s.nwg);
+  t.sel = o; o = align4(o + t.nsel);
+  t.alen = o; o = align4(o + t.nsel);
+  t.off = o; o = align4(o + t.nsel + 1);
+  t.top = o; o = align4(o + 2 * k);
+  t.ent = o; o = align4(o + 2 * t.nsel * t.ke);
+  t.cmp = o; o = align4(o + 2 * t.nsel * t.ke);
+  t.total = o;
+  return t;
+}
+KIE_HD int32_t topk_merge_floats(const Shape& s, int32_t k) { return topk_layout(s, k).total; }
+
 // ---------------------------------------------------------------------------------------------
 // Attention split: WG w handles KV head (w mod nkv) over position chunk (w / nkv).
 // ---------------------------------------------------------------------------------------------
@@ -173,7 +204,7 @@ KIE_HD Exch exch_layout(const Shape& s) {
   e.part = o; o += (int64_t)s.L * s.nwg * e.part_words;
   e.o = o; o += (int64_t)s.L * s.qdim();
   e.h = o; o += (int64_t)s.L * s.F;
-  e.lm = o; o += (int64_t)s.nwg * 2;
+  e.lm = o; o += (int64_t)kMaxTopK * s.nwg * 2;  // [rank][WG][value, id] sampling candidates
   e.end = o;
   return e;
 }
@@ -183,7 +214,7 @@ KIE_HD Exch exch_layout(const Shape& s) {
 struct Workspace {
   int64_t exch, rope, wbase, err, norms, trace, end;
 };
-constexpr int kTraceWords = 16;  // per wave: cycle counters of a KIE_TRACE build
+constexpr int kTraceWords = 24;  // per wave: cycle counters of a KIE_TRACE build
 KIE_HD int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 KIE_HD Workspace workspace_layout(const Shape& s) {
   Workspace w;

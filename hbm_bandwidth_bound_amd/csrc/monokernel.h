@@ -34,12 +34,16 @@ struct KParams {
   int32_t pos0, n_steps;
   uint32_t epoch0;           // exchange tag of step s is epoch0 + s (never 0)
   int32_t lm_last_only;      // run the LM head and sampler only on the last step (prompt pass)
+  int32_t top_k;             // <= 1: greedy; else top-k sampling (k <= kMaxTopK)
+  float temperature;         // top-k: logits are divided by it (> 0)
+  uint64_t seed;             // top-k: random stream of the draw
   int64_t timeout_ticks;     // per wait, in s_memrealtime ticks (100 MHz)
 };
 
 typedef void (*KernelFn)(KParams);
 KernelFn decode_kernel_for(int group, int head_dim, bool prompt);
 int32_t lds_bytes_for(const Shape& s);
+int32_t topk_capacity_floats(const Shape& s);  // WG-local floats available to the top-k merge
 
 // set-up kernels (pack.hip)
 struct PackArgs {

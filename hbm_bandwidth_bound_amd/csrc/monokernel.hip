@@ -8,6 +8,7 @@ KernelFn kernel_hd64(int G, bool prompt);
 KernelFn kernel_hd128(int G, bool prompt);
 
 int32_t lds_bytes_for(const Shape& s) { return lds_bytes_for_impl(s); }
+int32_t topk_capacity_floats(const Shape& s) { return merge_floats(s); }
 
 KernelFn decode_kernel_for(int G, int HD, bool prompt) {
   if (HD == 128) return kernel_hd128(G, prompt);

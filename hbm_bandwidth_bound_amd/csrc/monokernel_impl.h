@@ -90,11 +90,23 @@ __host__ __device__ inline int32_t scr_floats(const Shape& s) {
   int32_t a = kWaves * s.group() * (s.hd + 2);
   if (16 * kMergeDims * 3 > a) a = 16 * kMergeDims * 3;
   if (2 * s.nwg > a) a = 2 * s.nwg;
+  if (lm_rows_max(s) > a) a = lm_rows_max(s);  // the WG's LM outputs for the top-k draw
   if (a < 64) a = 64;
   return (a + 3) & ~3;
 }
+// act, xres, part and a pad are contiguous: once the LM outputs are final they hold the top-k
+// merge, and the pad makes room for the largest k where the three are smaller
+__host__ __device__ inline int32_t merge_pad_floats(const Shape& s) {
+  const int32_t kmax = kMaxTopK < s.V ? kMaxTopK : s.V;
+  const int32_t need = (topk_merge_floats(s, kmax) + 3) & ~3;
+  const int32_t have = act_floats(s) + s.d + 2 * kMaxUnits;
+  return need > have ? need - have : 0;
+}
+__host__ __device__ inline int32_t merge_floats(const Shape& s) {
+  return act_floats(s) + s.d + 2 * kMaxUnits + merge_pad_floats(s);
+}
 inline int32_t lds_bytes_for_impl(const Shape& s) {
-  return (act_floats(s) + s.d + 2 * kMaxUnits + scr_floats(s) + (s.group() + 2) * s.hd + s.hd) * 4 + C_COUNT * 4;
+  return (merge_floats(s) + scr_floats(s) + (s.group() + 2) * s.hd + s.hd) * 4 + C_COUNT * 4;
 }
 __device__ __forceinline__ Lds lds_map(uint8_t* smem, const Shape& s) {
   Lds L;
@@ -102,6 +114,7 @@ __device__ __forceinline__ Lds lds_map(uint8_t* smem, const Shape& s) {
   L.act = (float*)p; p += (size_t)act_floats(s) * 4;
   L.xres = (float*)p; p += (size_t)s.d * 4;
   L.part = (float*)p; p += (size_t)2 * kMaxUnits * 4;
+  p += (size_t)merge_pad_floats(s) * 4;
   L.scr = (float*)p; p += (size_t)scr_floats(s) * 4;
   L.q = (float*)p; p += (size_t)(s.group() + 2) * s.hd * 4;
   L.rope = (float2*)p; p += (size_t)s.hd * 4;
@@ -391,6 +404,19 @@ struct Wk {
       bar();
     }
     return ss;
+  }
+  // n words at addresses addr(q), q < n, into LDS floats dst (bit copies). Ends with a barrier.
+  template <int KM, typename Addr>
+  __device__ __forceinline__ void fetch_map(int32_t n, Addr addr, float* dst, uint32_t epoch) {
+    const uint64_t t0 = TR_NOW();
+    for (int32_t base = 0; base < n; base += KM * kThreads) {
+      const int32_t e0 = base + tid;
+      poll<KM>(
+          epoch, [&](int k) { return e0 + k * kThreads < n; }, [&](int k) { return addr(e0 + k * kThreads); },
+          [&](int k, float x) { dst[e0 + k * kThreads] = x; });
+    }
+    tr.add(T_FETCH, TR_NOW() - t0);
+    bar();
   }
   // act = (xres * r) * g with r = 1 / sqrt(ss / d + eps). Ends with a barrier.
   __device__ __forceinline__ void norm_to_act(float ss, const uint16_t* gain) {
@@ -712,6 +738,211 @@ __device__ __forceinline__ void merge_unit(Wk& K, const Att& at, int32_t l, int3
   bar();
 }
 
+// ------------------------------------------------------------------------------------------
+// Top-k sampling on the GPU (aikraft.ru «3000 токенов в секунду…», §04: sampling runs inside the
+// monokernel, not on the host). Every WG computes the same token from the same exchanged words.
+// ------------------------------------------------------------------------------------------
+// SplitMix64 (Steele, Lea & Flood, "Fast splittable pseudorandom number generators", OOPSLA 2014)
+__device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
+  uint64_t z = x + 0x9e3779b97f4a7c15ull;
+  z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+  z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+  return z ^ (z >> 31);
+}
+__device__ __forceinline__ double readlane_d(double v, int lane) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)u, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), lane);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+// Candidate (z, id) as one unsigned 64-bit key that orders like the candidate order: an
+// order-preserving image of the float bits above, the complement of the id below (a lower id
+// wins a tie). z is never NaN or -0 here.
+__device__ __forceinline__ uint64_t cand_key(float v, int32_t id) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t hi = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)hi << 32) | (uint32_t)(0x7fffffff - id);
+}
+__device__ __forceinline__ float key_value(uint64_t k) {
+  const uint32_t hi = (uint32_t)(k >> 32);
+  return __uint_as_float((hi & 0x80000000u) ? (hi & 0x7fffffffu) : ~hi);
+}
+__device__ __forceinline__ int32_t key_id(uint64_t k) { return 0x7fffffff - (int32_t)(uint32_t)k; }
+// Number of keys of kk[0 .. n) (16-byte aligned) greater than key; eight per step with 16-byte
+// LDS reads, so that the reads overlap.
+__device__ __forceinline__ int32_t count_greater(const uint64_t* kk, int32_t n, uint64_t key) {
+  typedef uint64_t v2u64 __attribute__((ext_vector_type(2)));
+  int32_t c = 0, i = 0;
+  for (; i + 8 <= n; i += 8) {
+    const v2u64 a = *(const v2u64*)(kk + i), b = *(const v2u64*)(kk + i + 2);
+    const v2u64 e = *(const v2u64*)(kk + i + 4), f = *(const v2u64*)(kk + i + 6);
+    c += (a.x > key ? 1 : 0) + (a.y > key ? 1 : 0) + (b.x > key ? 1 : 0) + (b.y > key ? 1 : 0) + (e.x > key ? 1 : 0) +
+         (e.y > key ? 1 : 0) + (f.x > key ? 1 : 0) + (f.y > key ? 1 : 0);
+  }
+  for (; i < n; ++i) c += kk[i] > key ? 1 : 0;
+  return c;
+}
+
+// On entry the WG's LM outputs divided by the temperature, z, are in scr[0 .. 2 np) (row 2 pb +
+// i at i) and every wave has passed a barrier after they were written. Candidate order is the
+// argmax order (larger z, then the lower id), a strict total order once the padding ids (past V)
+// are unique.
+//  1. Each WG ranks its own rows and publishes its k best, in order, to rank slots [r][WG];
+//     slots past its row count get padding (-inf, unique id >= V).
+//  2. Every WG reads all heads (rank 0) and keeps the nsel = min(k, nwg) best lists: a row of the
+//     global top k is in one of them (k better heads would otherwise precede it), at a list rank
+//     below k, and not worse than H, the k-th best head (when nsel == k).
+//  3. It reads those lists' first ke entries. The active ones (not worse than H; all when
+//     nsel < k) form a prefix of each list and are compacted; an active entry's rank is the
+//     number of active entries better than it. Every row better than a global top-k row is
+//     active, so ranks below k are exact and every other entry counts at least k.
+//  4. z_j of the k winners (in order) -> p_j = exp(z_j - z_0) / S with S summed in fp64 in order;
+//     u = (splitmix64(seed ^ splitmix64(pos)) >> 40) * 2^-24; the first j whose running sum of
+//     p_j exceeds u is drawn, the last candidate if none does.
+// The rank loops read LDS at independent addresses and are unrolled so that the reads overlap.
+__device__ __forceinline__ int32_t sample_topk(Wk& K, const StageGeo& gl, uint64_t* lmx, uint32_t ep, int32_t pos) {
+  const KParams& P = K.P;
+  const Lds& L = K.L;
+  const Shape& s = P.s;
+  const int32_t kk = P.top_k, nwg = s.nwg, tid = K.tid;
+  const int32_t nr = 2 * gl.np, r0 = 2 * gl.pb;
+  uint64_t tp = TR_NOW();
+  auto phase = [&](int slot) {  // top-k phase times of a KIE_TRACE build (constant slots)
+    const uint64_t t = TR_NOW();
+    K.tr.add(slot, t - tp);
+    tp = t;
+  };
+  // 1.
+  for (int32_t i = tid; i < nr; i += kThreads) {
+    const float zi = L.scr[i];
+    int32_t rank = 0;
+#pragma unroll 8
+    for (int32_t j = 0; j < nr; ++j) rank += better(L.scr[j], j, zi, i) ? 1 : 0;
+    if (rank < kk) {
+      st_x(lmx + ((int64_t)rank * nwg + K.w) * 2, tag_f(zi, ep));
+      st_x(lmx + ((int64_t)rank * nwg + K.w) * 2 + 1, tag_u((uint32_t)(r0 + i), ep));
+    }
+  }
+  if (tid >= nr && tid < kk) {
+    st_x(lmx + ((int64_t)tid * nwg + K.w) * 2, tag_f(-INFINITY, ep));
+    st_x(lmx + ((int64_t)tid * nwg + K.w) * 2 + 1, tag_u((uint32_t)(s.V + K.w * kMaxTopK + tid), ep));
+  }
+  // 2.
+  const TopkLayout tl = topk_layout(s, kk);
+  const int32_t nsel = tl.nsel, ke = tl.ke;
+  float* const mg = L.act;  // act, xres and part are free once the LM outputs are final
+  float* heads = mg + tl.heads;
+  int32_t* sel = (int32_t*)(mg + tl.sel);
+  int32_t* alen = (int32_t*)(mg + tl.alen);
+  int32_t* off = (int32_t*)(mg + tl.off);
+  float* top = mg + tl.top;
+  float* ent = mg + tl.ent;
+  uint64_t* ckey = (uint64_t*)(mg + tl.cmp);
+  if (tid < nsel) {
+    sel[tid] = tid;  // (every slot is overwritten below; this keeps it in range)
+    alen[tid] = 0;
+  }
+  phase(16);
+  K.fetch_map<8>(2 * nwg, [&](int32_t q) { return lmx + q; }, heads, ep);
+  phase(17);
+  uint64_t* hkey = (uint64_t*)heads;  // each (z, id) pair becomes its key, in place
+  uint64_t myk[(kMaxWG + kThreads - 1) / kThreads];
+#pragma unroll
+  for (int q = 0; q < (kMaxWG + kThreads - 1) / kThreads; ++q) {
+    const int32_t x = tid + q * kThreads;
+    myk[q] = x < nwg ? cand_key(heads[2 * x], __float_as_int(heads[2 * x + 1])) : 0;
+  }
+  bar();
+#pragma unroll
+  for (int q = 0; q < (kMaxWG + kThreads - 1) / kThreads; ++q)
+    if (tid + q * kThreads < nwg) hkey[tid + q * kThreads] = myk[q];
+  bar();
+#pragma unroll
+  for (int q = 0; q < (kMaxWG + kThreads - 1) / kThreads; ++q) {
+    const int32_t x = tid + q * kThreads;
+    if (x < nwg) {
+      const int32_t rank = count_greater(hkey, nwg, myk[q]);
+      if (rank < nsel) sel[rank] = x;
+    }
+  }
+  if (tid < kk) {
+    top[2 * tid] = -INFINITY;
+    top[2 * tid + 1] = __int_as_float(0x7fffffff);
+  }
+  bar();
+  phase(18);
+  // 3.
+  K.fetch_map<16>(
+      2 * nsel * ke,
+      [&](int32_t q) {
+        const int32_t e = q >> 1, j = e / ke, r = e - j * ke;
+        return lmx + ((int64_t)r * nwg + sel[j]) * 2 + (q & 1);
+      },
+      ent, ep);
+  phase(19);
+  const bool bounded = nsel == kk;
+  const uint64_t hb = hkey[sel[nsel - 1]];  // H
+  for (int32_t e = tid; e < nsel * ke; e += kThreads)
+    if (!bounded || cand_key(ent[2 * e], __float_as_int(ent[2 * e + 1])) >= hb)
+      __hip_atomic_fetch_add(&alen[e / ke], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  bar();
+  if (K.v == 0) {  // exclusive scan of the active lengths (nsel <= 64 lists: one wave)
+    const int32_t lane = K.lane;
+    const int32_t c = lane < nsel ? alen[lane] : 0;
+    int32_t incl = c;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int32_t up = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += up;
+    }
+    if (lane < nsel) off[lane] = incl - c;
+    if (lane == kWave - 1) off[nsel] = incl;
+  }
+  bar();
+  for (int32_t e = tid; e < nsel * ke; e += kThreads) {  // compaction of the active entries
+    const int32_t j = e / ke, r = e - j * ke;
+    if (r < alen[j]) ckey[off[j] + r] = cand_key(ent[2 * e], __float_as_int(ent[2 * e + 1]));
+  }
+  bar();
+  phase(20);
+  const int32_t m = off[nsel];
+  for (int32_t i = tid; i < m; i += kThreads) {
+    const uint64_t ck = ckey[i];
+    const int32_t rank = count_greater(ckey, m, ck);
+    if (rank < kk) {
+      top[2 * rank] = key_value(ck);
+      top[2 * rank + 1] = __int_as_float(key_id(ck));
+    }
+  }
+  bar();
+  phase(21);
+  // 4. (every wave, redundantly: no further barrier is needed to share the token)
+  const int32_t lane = K.lane;
+  const double z0 = (double)top[0];
+  double e = 0.0;
+  int32_t id = 0x7fffffff;
+  if (lane < kk) {
+    e = exp((double)top[2 * lane] - z0);
+    id = __float_as_int(top[2 * lane + 1]);
+  }
+  double S = 0.0;
+  for (int32_t j = 0; j < kk; ++j) S += readlane_d(e, j);
+  const double p = e / S;
+  const double u = (double)(splitmix64(P.seed ^ splitmix64((uint64_t)(int64_t)pos)) >> 40) * (1.0 / 16777216.0);
+  int32_t chosen = __builtin_amdgcn_readlane(id, kk - 1);
+  double cum = 0.0;
+  for (int32_t j = 0; j < kk; ++j) {
+    cum += readlane_d(p, j);
+    if (cum > u) {
+      chosen = __builtin_amdgcn_readlane(id, j);
+      break;
+    }
+  }
+  phase(22);
+  bar();  // every wave has read top before the next step reuses this memory
+  return chosen;
+}
+
 // The decode program of one wave. Its weight batches are consumed by one loop; the batch after
 // the current one is always in flight. Between batches, boundary() runs the work that separates
 // two stages -- finalising the outputs,
@@ -866,9 +1097,11 @@ __device__ __forceinline__ void decode(Wk& K) {
         case B_END: {  // LM outputs and this WG's argmax candidate; the grid-wide join; next token
           float bv = -INFINITY;
           int32_t bi = 0x7fffffff;
+          const bool topk = bnd == B_LM && P.top_k > 1;
           if (bnd == B_LM) {
             bar();
             float* lo = P.logits_out ? P.logits_out + (P.lm_last_only ? 0 : (int64_t)step * s.V) : nullptr;
+            const int32_t pb = K.g[ST_LM].pb;
             K.finalize(K.g[ST_LM], [&](int32_t gp, float ya, float yb) {
               const int32_t ra = 2 * gp, rb = 2 * gp + 1;
               if (better(ya, ra, bv, bi)) {
@@ -883,31 +1116,42 @@ __device__ __forceinline__ void decode(Wk& K) {
                 lo[ra] = ya;
                 lo[rb] = yb;
               }
+              if (topk) {  // NaN ranks as -inf and -0 as +0, so the candidate order stays strict
+                const float za = ya / P.temperature, zb = yb / P.temperature;
+                L.scr[2 * (gp - pb)] = za == za ? (za == 0.f ? 0.f : za) : -INFINITY;
+                L.scr[2 * (gp - pb) + 1] = zb == zb ? (zb == 0.f ? 0.f : zb) : -INFINITY;
+              }
             });
           }
-          // every WG gathers all candidates: no WG reuses a step's exchange buffers before every
-          // WG has finished reading them
           const uint64_t tsm = TR_NOW();
-          K.block_argmax(&bv, &bi);
-          if (tid == 0) {
-            st_x(ex + X.lm + 2 * K.w, tag_f(bv, ep));
-            st_x(ex + X.lm + 2 * K.w + 1, tag_u((uint32_t)bi, ep));
-          }
-          K.fetch_f32(ex + X.lm, 2 * s.nwg, L.scr, ep, false);
-          bv = -INFINITY;
-          bi = 0x7fffffff;
-          for (int k = tid; k < s.nwg; k += kThreads) {
-            const float cv = L.scr[2 * k];
-            const int32_t ci = __float_as_int(L.scr[2 * k + 1]);
-            if (better(cv, ci, bv, bi)) {
-              bv = cv;
-              bi = ci;
+          int32_t next;
+          if (topk) {
+            bar();
+            next = clamp_token(sample_topk(K, K.g[ST_LM], ex + X.lm, ep, pos), s.V);
+          } else {
+            // every WG gathers all candidates: no WG reuses a step's exchange buffers before every
+            // WG has finished reading them
+            K.block_argmax(&bv, &bi);
+            if (tid == 0) {
+              st_x(ex + X.lm + 2 * K.w, tag_f(bv, ep));
+              st_x(ex + X.lm + 2 * K.w + 1, tag_u((uint32_t)bi, ep));
             }
+            K.fetch_f32(ex + X.lm, 2 * s.nwg, L.scr, ep, false);
+            bv = -INFINITY;
+            bi = 0x7fffffff;
+            for (int k = tid; k < s.nwg; k += kThreads) {
+              const float cv = L.scr[2 * k];
+              const int32_t ci = __float_as_int(L.scr[2 * k + 1]);
+              if (better(cv, ci, bv, bi)) {
+                bv = cv;
+                bi = ci;
+              }
+            }
+            bar();  // every thread has read its candidates before scr is reused
+            K.block_argmax(&bv, &bi);
+            next = clamp_token(bi, s.V);
           }
-          bar();  // every thread has read its candidates before scr is reused
-          K.block_argmax(&bv, &bi);
           K.tr.add(T_SAMPLE, TR_NOW() - tsm);
-          int32_t next = clamp_token(bi, s.V);
           if (lm && K.w == 0 && tid == 0) {
             if (P.tokens_out) P.tokens_out[step] = next;
             if (P.last_tok_out && step == P.n_steps - 1) P.last_tok_out[0] = next;

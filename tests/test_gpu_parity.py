@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 from hbm_bandwidth_bound_amd import synth
-from tests.gpu_util import check_steps, rel_l2, say, to_device, top2_gap
+from tests.gpu_util import check_steps, check_topk_steps, rel_l2, say, to_device, top2_gap
 
 pytestmark = pytest.mark.gpu
 
@@ -162,4 +162,74 @@ def test_capacity_and_bad_token_errors(torch_cuda, tiny):
     eng.reset()
     eng.prefill(torch.zeros(2, dtype=torch.int32, device="cuda"))
     eng.sync()
+    eng.close()
+
+
+def run_gpu_topk(torch, eng, prompt, n_steps, V, smp):
+    tokens = torch.tensor(np.asarray(prompt, dtype=np.int32), device="cuda")
+    last = torch.empty(V, dtype=torch.float32, device="cuda")
+    first = eng.prefill(tokens, logits_out=last, smp=smp)
+    out = torch.empty(n_steps, dtype=torch.int32, device="cuda")
+    logits = torch.empty((n_steps, V), dtype=torch.float32, device="cuda")
+    eng.generate(first, n_steps, out, logits, smp=smp)
+    eng.sync()
+    return int(first.item()), last.cpu().numpy(), out.cpu().numpy(), logits.cpu().numpy()
+
+
+@pytest.mark.parametrize("k,T,seed", [(50, 0.8, 2), (64, 1.7, 9), (2, 0.3, 123456789012345)])
+def test_tiny_topk_matches_oracle(torch_cuda, tiny, oracle_lib, k, T, seed):
+    """Top-k sampling on the GPU: every draw equals the oracle sampler's on the same logits, and
+    the oracle's own logits give the same candidates, probabilities and (away from CDF
+    boundaries) tokens."""
+    from hbm_bandwidth_bound_amd.kie import Engine, sampling
+    cfg, w, wd = tiny
+    P, N = 64, 32
+    say(f"[tiny] top-k k={k} T={T} seed={seed}: prefill {P} + decode {N}")
+    smp = sampling(k, T, seed)
+    eng = Engine(cfg, wd, P + N)
+    prompt = synth.prompt_ids(P, cfg.vocab_size, 1)
+    first, last, toks, logits = run_gpu_topk(torch_cuda, eng, prompt, N, cfg.vocab_size, smp)
+    om = oracle_lib.OracleModel(cfg, w, P + N)
+    ref_prompt = om.run(prompt)
+    assert rel_l2(last, ref_prompt[-1]) <= 1e-3
+    check_topk_steps(last[None], ref_prompt[-1:], [first], k, T, seed, P - 1, label="prefill")
+    ref = om.run([first] + [int(t) for t in toks[:-1]], start_pos=P)
+    for s in range(N):
+        assert rel_l2(logits[s], ref[s]) <= 1e-3
+    nt, ns = check_topk_steps(logits, ref, toks, k, T, seed, P, label="tiny top-k")
+    say(f"  sets checked on {ns}/{N} steps, tokens on {nt}/{N}")
+    assert ns > 0 and nt > 0
+    # the draw depends on (seed, position) only: single-step launches give the same stream
+    eng.set_position(P)
+    import torch
+    tok = torch.tensor([first], dtype=torch.int32, device="cuda")
+    got = []
+    for s in range(N):
+        o = torch.empty(1, dtype=torch.int32, device="cuda")
+        eng.decode_step(tok, o, smp=smp)
+        got.append(o)
+        tok = o
+    eng.sync()
+    assert [int(t.item()) for t in got] == [int(t) for t in toks]
+    eng.close()
+
+
+def test_topk_argument_errors(torch_cuda, tiny):
+    import torch
+    from hbm_bandwidth_bound_amd.kie import Engine, KieError, sampling
+    cfg, w, wd = tiny
+    say("[tiny] top-k argument errors")
+    eng = Engine(cfg, wd, 8)
+    toks = torch.zeros(2, dtype=torch.int32, device="cuda")
+    for smp, status in [(sampling(65, 1.0, 0), -2), (sampling(8, 0.0, 0), -1), (sampling(8, float("nan"), 0), -1),
+                        (sampling(8, float("inf"), 0), -1)]:
+        with pytest.raises(KieError) as ei:
+            eng.prefill(toks, smp=smp)
+        assert ei.value.status == status and eng.position == 0
+    # top_k 1 (and 0) is greedy
+    a = eng.prefill(toks, smp=sampling(1, 0.5, 3))
+    eng.reset()
+    b = eng.prefill(toks, smp=sampling(0, 0.0, 0))
+    eng.sync()
+    assert int(a.item()) == int(b.item())
     eng.close()

@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 from hbm_bandwidth_bound_amd import synth
-from tests.gpu_util import check_steps, rel_l2, say, top2_gap
+from tests.gpu_util import check_steps, check_topk_steps, rel_l2, say, top2_gap
 
 pytestmark = pytest.mark.gpu
 
@@ -38,9 +38,18 @@ def test_full_shape_prefill_then_decode(oracle_lib):
     logits = torch.empty((N, cfg.vocab_size), dtype=torch.float32, device="cuda")
     eng.generate(first, N, out, logits)
     eng.sync()
+    kg = eng.kv_view().cpu().numpy().view(np.uint16)
+    # top-k (k 50, T 0.8) over the same inputs: the same logits, then the sampler
+    from hbm_bandwidth_bound_amd.kie import sampling
+    eng.set_position(P)
+    tk_out = torch.empty(N, dtype=torch.int32, device="cuda")
+    tk_logits = torch.empty((N, cfg.vocab_size), dtype=torch.float32, device="cuda")
+    eng.generate(first, N, tk_out, tk_logits, forced=out, smp=sampling(50, 0.8, 2))
+    eng.sync()
     first = int(first.item())
     last, toks, logits = last.cpu().numpy(), out.cpu().numpy(), logits.cpu().numpy()
-    kg = eng.kv_view().cpu().numpy().view(np.uint16)
+    tk_toks, tk_logits = tk_out.cpu().numpy(), tk_logits.cpu().numpy()
+    assert np.array_equal(tk_logits, logits)
     eng.close()
     w = synth.weights_torch_to_np(wd)
     del wd
@@ -71,6 +80,8 @@ def test_full_shape_prefill_then_decode(oracle_lib):
         w_, c_ = check_steps(logits[s_:s_ + 1], ref[s_:s_ + 1], toks[s_:s_ + 1], tol=tol, label=f"1.6b step {s_}")
         worst, checked = max(worst, w_), checked + c_
     say(f"  decode worst rel-L2 {worst:.3e}, greedy checked on {checked}/{N} steps")
+    nt, ns = check_topk_steps(tk_logits, ref, tk_toks, 50, 0.8, 2, P, p_tol="auto", label="1.6b top-k")
+    say(f"  top-k: sets checked on {ns}/{N} steps, tokens on {nt}/{N}")
     ko, vo = om.kv_view()
     kf = synth.bf16_bits_to_f32(kg[:, 0, :, :P + N])
     vf = synth.bf16_bits_to_f32(kg[:, 1, :, :P + N])
