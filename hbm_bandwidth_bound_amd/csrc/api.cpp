@@ -356,8 +356,8 @@ kie_status kie_reset(kie_ctx* ctx) {
 
 kie_status kie_set_position(kie_ctx* ctx, int32_t pos) {
   if (!ctx) return KIE_ERR_INVALID_ARG;
-  if (pos < 0 || pos > ctx->pos) {
-    set_err(&ctx->last_error, "position %d outside [0, %d]", pos, ctx->pos);
+  if (pos < 0 || pos > ctx->s.max_seq) {
+    set_err(&ctx->last_error, "position %d outside [0, %d]", pos, ctx->s.max_seq);
     return KIE_ERR_INVALID_ARG;
   }
   ctx->pos = pos;

@@ -173,8 +173,9 @@ def _mix32_u32(x: np.ndarray) -> np.ndarray:
     return x
 
 
-def _weights_bits_np(shape, seed: int, tidx: int) -> np.ndarray:
+def _weights_bits_np(shape, seed: int, tidx: int, std: float = WEIGHT_STD) -> np.ndarray:
     k1, k2 = tensor_keys(seed, tidx)
+    scale = np.float32(std / _IH_SIGMA)
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.uint16)
     chunk = 1 << 22
@@ -184,20 +185,20 @@ def _weights_bits_np(shape, seed: int, tidx: int) -> np.ndarray:
         h1 = _mix32_u32(i ^ np.uint32(k1))
         h2 = _mix32_u32(i ^ np.uint32(k2))
         t = ((h1 & m16) + (h1 >> np.uint32(16)) + (h2 & m16) + (h2 >> np.uint32(16))).astype(np.int32) - 131070
-        x = t.astype(np.float32) * _IH_SCALE_F32
+        x = t.astype(np.float32) * scale
         u = x.view(np.uint32)
         lsb = (u >> np.uint32(16)) & np.uint32(1)
         out[s:s + len(i)] = ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
     return out.reshape(shape)
 
 
-def _weights_bits_torch(shape, seed: int, tidx: int, device):
+def _weights_bits_torch(shape, seed: int, tidx: int, device, std: float = WEIGHT_STD):
     import torch
     k1, k2 = tensor_keys(seed, tidx)
     n = int(np.prod(shape))
     out = torch.empty(n, dtype=torch.int16, device=device)
     chunk = 1 << 26
-    scale = torch.tensor(float(_IH_SCALE_F32), dtype=torch.float32, device=device)
+    scale = torch.tensor(float(np.float32(std / _IH_SIGMA)), dtype=torch.float32, device=device)
     for s in range(0, n, chunk):
         e = min(n, s + chunk)
         i = torch.arange(s, e, dtype=torch.int64, device=device)
@@ -270,3 +271,26 @@ def prompt_ids(n: int, vocab: int, seed: int = 1) -> np.ndarray:
     i = np.arange(n, dtype=np.int64)
     h = _mix32(np, i ^ k1)
     return ((h * vocab) >> 32).astype(np.int32)
+
+
+# Synthetic KV-cache contents: K and V rows of positions 0..n-1 as bf16 bits, [L][nkv][n][hd]
+# each, drawn like the weights but with standard deviation `std` (so that attention weights are
+# far from uniform). Used where a context longer than the oracle can prefill is needed: both
+# sides start from the same rows.
+KV_TENSOR_K = 0x7FFE0000
+KV_TENSOR_V = 0x7FFE0001
+
+
+def kv_shape(cfg: ModelConfig, n: int):
+    return (cfg.n_layers, cfg.n_kv_heads, n, cfg.head_dim)
+
+
+def synthetic_kv_np(cfg: ModelConfig, n: int, seed: int = 7, std: float = 1.0):
+    return (_weights_bits_np(kv_shape(cfg, n), seed, KV_TENSOR_K, std),
+            _weights_bits_np(kv_shape(cfg, n), seed, KV_TENSOR_V, std))
+
+
+def synthetic_kv_torch(cfg: ModelConfig, n: int, seed: int = 7, device="cuda", std: float = 1.0):
+    """Same bits as synthetic_kv_np, as int16 tensors on a torch device."""
+    return (_weights_bits_torch(kv_shape(cfg, n), seed, KV_TENSOR_K, device, std),
+            _weights_bits_torch(kv_shape(cfg, n), seed, KV_TENSOR_V, device, std))

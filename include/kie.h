@@ -135,8 +135,11 @@ kie_status kie_sync(kie_ctx* ctx);
  * later steps). */
 kie_status kie_reset(kie_ctx* ctx);
 
-/* Set the position to pos (0 <= pos <= current position): rewinds the sequence so that steps
- * resume at pos, e.g. to re-run a suffix. KIE_ERR_INVALID_ARG otherwise. */
+/* Set the position to pos (0 <= pos <= max_seq_len). Below the current position it rewinds the
+ * sequence so that steps resume at pos (e.g. to re-run a suffix). Above it, the caller states that
+ * the K/V rows of positions < pos are already in its kv_cache buffer (written there directly, in
+ * the documented layout): later steps attend over them as they are. KIE_ERR_INVALID_ARG
+ * otherwise. */
 kie_status kie_set_position(kie_ctx* ctx, int32_t pos);
 
 /* Current position (number of tokens whose K/V rows are in the cache), or -1 for NULL. */

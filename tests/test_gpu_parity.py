@@ -233,3 +233,36 @@ def test_topk_argument_errors(torch_cuda, tiny):
     eng.sync()
     assert int(a.item()) == int(b.item())
     eng.close()
+
+
+def test_tiny_decode_over_caller_filled_cache(torch_cuda, tiny, oracle_lib):
+    """kie_set_position forward: K/V rows written by the caller (seeded synthetic rows) are
+    attended over as they are; the oracle starts from the same rows."""
+    import torch
+    from hbm_bandwidth_bound_amd.kie import Engine, KieError
+    cfg, w, wd = tiny
+    n, N = 1500, 8
+    say(f"[tiny] {n} synthetic cached positions + decode {N}")
+    eng = Engine(cfg, wd, n + N)
+    kd, vd = synth.synthetic_kv_torch(cfg, n, seed=3, device="cuda")
+    kv = eng.kv_view()
+    kv[:, 0, :, :n] = kd
+    kv[:, 1, :, :n] = vd
+    with pytest.raises(KieError):
+        eng.set_position(n + N + 1)
+    eng.set_position(n)
+    assert eng.position == n
+    first = torch.tensor([17], dtype=torch.int32, device="cuda")
+    out = torch.empty(N, dtype=torch.int32, device="cuda")
+    logits = torch.empty((N, cfg.vocab_size), dtype=torch.float32, device="cuda")
+    eng.generate(first, N, out, logits)
+    eng.sync()
+    toks = out.cpu().numpy()
+    om = oracle_lib.OracleModel(cfg, w, n + N)
+    k, v = om.kv_view()
+    k[:, :, :n] = kd.cpu().numpy().view(np.uint16)
+    v[:, :, :n] = vd.cpu().numpy().view(np.uint16)
+    ref = om.run([17] + [int(t) for t in toks[:-1]], start_pos=n)
+    worst, checked = check_steps(logits.cpu().numpy(), ref, toks, label="tiny synthetic KV")
+    say(f"  worst rel-L2 {worst:.3e}, greedy checked {checked}/{N}")
+    eng.close()

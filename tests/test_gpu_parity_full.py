@@ -88,3 +88,113 @@ def test_full_shape_prefill_then_decode(oracle_lib):
     # the caches drift like the logits (bf16 rounding flips of fp32-level differences)
     assert rel_l2(kf, synth.bf16_bits_to_f32(ko[:, :, :P + N])) <= max(1e-2, 4 * spread)
     assert rel_l2(vf, synth.bf16_bits_to_f32(vo[:, :, :P + N])) <= max(1e-2, 4 * spread)
+
+
+def oracle_with_spread(oracle_lib, cfg, w, max_seq, fill, runs):
+    """Oracle logits of `runs` (list of (tokens, start_pos)) in ascending and in descending GEMV
+    summation order; `fill(model)` prepares each model's cache first."""
+    out = []
+    for desc in (False, True):
+        oracle_lib.set_gemv_order(desc)
+        try:
+            om = oracle_lib.OracleModel(cfg, w, max_seq)
+            fill(om)
+            out.append([om.run(toks, start_pos=p) for toks, p in runs])
+        finally:
+            oracle_lib.set_gemv_order(False)
+    return out[0], out[1]
+
+
+def test_long_context_over_synthetic_kv(oracle_lib):
+    """1.6B at the long-context length (32768 cached positions): both sides start from the same
+    seeded synthetic K/V rows (the oracle cannot prefill 32k tokens), then decode a few steps.
+    Every attention split, chunk length and merge runs at its production size."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from hbm_bandwidth_bound_amd.kie import Engine
+    cfg = synth.M1_6B
+    n, N = 32768, 3
+    say(f"[1.6b] {n} synthetic cached positions + decode {N}")
+    wd = synth.make_weights_torch(cfg, 0, "cuda")
+    eng = Engine(cfg, wd, n + N)
+    kd, vd = synth.synthetic_kv_torch(cfg, n, seed=7, device="cuda")
+    kv = eng.kv_view()
+    kv[:, 0, :, :n] = kd
+    kv[:, 1, :, :n] = vd
+    eng.set_position(n)
+    tok0 = int(synth.prompt_ids(1, cfg.vocab_size, 5)[0])
+    first = torch.tensor([tok0], dtype=torch.int32, device="cuda")
+    out = torch.empty(N, dtype=torch.int32, device="cuda")
+    logits = torch.empty((N, cfg.vocab_size), dtype=torch.float32, device="cuda")
+    eng.generate(first, N, out, logits)
+    eng.sync()
+    toks, logits = out.cpu().numpy(), logits.cpu().numpy()
+    kg_new = eng.kv_view()[:, :, :, n:n + N].cpu().numpy().view(np.uint16)
+    kn, vn = kd.cpu().numpy().view(np.uint16), vd.cpu().numpy().view(np.uint16)
+    eng.close()
+    w = synth.weights_torch_to_np(wd)
+    del wd, kd, vd, kv
+    torch.cuda.empty_cache()
+    say("  oracle (two summation orders) ...")
+    oracle_lib.set_threads(min(16, os.cpu_count() or 1))
+
+    def fill(om):
+        k, v = om.kv_view()
+        k[:, :, :n] = kn
+        v[:, :, :n] = vn
+
+    (ref,), (alt,) = oracle_with_spread(oracle_lib, cfg, w, n + N, fill, [([tok0] + [int(t) for t in toks[:-1]], n)])
+    worst, checked = 0.0, 0
+    for s_ in range(N):
+        tol = max(1e-3, 2 * rel_l2(alt[s_], ref[s_]))
+        w_, c_ = check_steps(logits[s_:s_ + 1], ref[s_:s_ + 1], toks[s_:s_ + 1], tol=tol, label=f"32k step {s_}")
+        worst, checked = max(worst, w_), checked + c_
+    say(f"  worst rel-L2 {worst:.3e}, greedy checked on {checked}/{N} steps")
+    # the new rows the GPU appended agree with the oracle's
+    om = oracle_lib.OracleModel(cfg, w, n + N)
+    fill(om)
+    om.run([tok0] + [int(t) for t in toks[:-1]], start_pos=n)
+    ko, vo = om.kv_view()
+    assert rel_l2(synth.bf16_bits_to_f32(kg_new[:, 0]), synth.bf16_bits_to_f32(ko[:, :, n:n + N])) <= 1e-2
+    assert rel_l2(synth.bf16_bits_to_f32(kg_new[:, 1]), synth.bf16_bits_to_f32(vo[:, :, n:n + N])) <= 1e-2
+
+
+def test_8b_shape_prefill_then_decode(oracle_lib):
+    """The ~8B shape (32 layers, d 4096, 32/8 heads, F 14336, vocab 128256: group of 4 query heads
+    per KV head, 128256 LM rows) on a short context."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from hbm_bandwidth_bound_amd.kie import Engine
+    cfg = synth.M8B
+    P, N = 6, 3
+    say(f"[8b] prefill {P} + decode {N}")
+    wd = synth.make_weights_torch(cfg, 0, "cuda")
+    eng = Engine(cfg, wd, P + N)
+    prompt = synth.prompt_ids(P, cfg.vocab_size, 4)
+    last = torch.empty(cfg.vocab_size, dtype=torch.float32, device="cuda")
+    first = eng.prefill(torch.tensor(prompt, dtype=torch.int32, device="cuda"), logits_out=last)
+    out = torch.empty(N, dtype=torch.int32, device="cuda")
+    logits = torch.empty((N, cfg.vocab_size), dtype=torch.float32, device="cuda")
+    eng.generate(first, N, out, logits)
+    eng.sync()
+    first, last, toks, logits = int(first.item()), last.cpu().numpy(), out.cpu().numpy(), logits.cpu().numpy()
+    eng.close()
+    w = synth.weights_torch_to_np(wd)
+    del wd
+    torch.cuda.empty_cache()
+    say("  oracle (two summation orders) ...")
+    oracle_lib.set_threads(min(16, os.cpu_count() or 1))
+    runs = [(list(prompt), 0), ([first] + [int(t) for t in toks[:-1]], P)]
+    (ref_p, ref), (alt_p, alt) = oracle_with_spread(oracle_lib, cfg, w, P + N, lambda om: None, runs)
+    spread = rel_l2(alt_p[-1], ref_p[-1])
+    e = rel_l2(last, ref_p[-1])
+    say(f"  prefill last-logits rel-L2 {e:.3e} (oracle order spread {spread:.3e})")
+    assert e <= max(1e-3, 2 * spread)
+    worst, checked = 0.0, 0
+    for s_ in range(N):
+        tol = max(1e-3, 2 * rel_l2(alt[s_], ref[s_]))
+        w_, c_ = check_steps(logits[s_:s_ + 1], ref[s_:s_ + 1], toks[s_:s_ + 1], tol=tol, label=f"8b step {s_}")
+        worst, checked = max(worst, w_), checked + c_
+    say(f"  decode worst rel-L2 {worst:.3e}, greedy checked on {checked}/{N} steps")
