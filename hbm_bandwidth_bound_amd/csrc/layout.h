@@ -179,8 +179,8 @@ KIE_HD int32_t att_chunk_len(const Shape& s, int32_t n) {
   cs = ((cs + ppt - 1) / ppt) * ppt;
   return cs < ppt ? ppt : cs;
 }
-// merge units: (query head, slice of 32 dims)
-constexpr int kMergeDims = 32;
+// merge units: (query head, slice of kMergeDims dims)
+constexpr int kMergeDims = 8;
 KIE_HD int32_t merge_units(const Shape& s) { return s.nq * (s.hd / kMergeDims); }
 KIE_HD int32_t merge_unit_wg(const Shape& s, int32_t u) { return (int32_t)(((int64_t)u * s.nwg) / merge_units(s)); }
 

@@ -88,7 +88,7 @@ __host__ __device__ inline int32_t act_floats(const Shape& s) {
 }
 __host__ __device__ inline int32_t scr_floats(const Shape& s) {
   int32_t a = kWaves * s.group() * (s.hd + 2);
-  if (16 * kMergeDims * 3 > a) a = 16 * kMergeDims * 3;
+  if (kWaves * kMergeDims * 3 > a) a = kWaves * kMergeDims * 3;
   if (2 * s.nwg > a) a = 2 * s.nwg;
   if (lm_rows_max(s) > a) a = lm_rows_max(s);  // the WG's LM outputs for the top-k draw
   if (a < 64) a = 64;
@@ -285,20 +285,23 @@ struct Wk {
       default: return nb[ST_LM];
     }
   }
-  // Batch b of this wave in stage gs, against the input in LDS: the two dot products of each unit
-  // u land in part[2u] and part[2u + 1].
-  __device__ __forceinline__ void reduce_batch(const StageGeo& gs, int32_t b, const v4u* cur) {
-    const int32_t lks = gs.ks == 8 ? 3 : (gs.ks == 4 ? 2 : (gs.ks == 2 ? 1 : 0));
-    {
-      float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+  // Batch b of this wave in stage gs (units of KS tiles), against the input in LDS: the two dot
+  // products of each unit u land in part[2u] and part[2u + 1]. The unit's k-slice (u mod S) is
+  // computed once per unit; every branch inside is wave-uniform.
+  template <int KS>
+  __device__ __forceinline__ void reduce_batch_ks(const StageGeo& gs, int32_t b, const v4u* cur) {
+    constexpr int UPB = kBatch / KS;
 #pragma unroll
-      for (int sl = 0; sl < kBatch; ++sl) {
-        const int32_t us = sl >> lks, t = sl & (gs.ks - 1);
-        const int32_t u = v + kWaves * (b * gs.upb + us);
-        if (u < gs.nu) {
-          const int32_t j = (u % gs.S) * gs.ks + t;
-          const v4f x = *(const v4f*)(L.act + (size_t)j * kTileK + lane * 4);
-          const v4u wt = cur[sl];
+    for (int us = 0; us < UPB; ++us) {
+      const int32_t u = v + kWaves * (b * UPB + us);
+      if (u < gs.nu) {
+        const int32_t r = gs.S == 1 ? 0 : u % gs.S;
+        const float* xa = L.act + (size_t)r * KS * kTileK + lane * 4;
+        float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+#pragma unroll
+        for (int t = 0; t < KS; ++t) {
+          const v4f x = *(const v4f*)(xa + t * kTileK);
+          const v4u wt = cur[us * KS + t];
           a0 = fmaf(bf16lo(wt.x), x.x, a0);
           a1 = fmaf(bf16hi(wt.x), x.y, a1);
           a0 = fmaf(bf16lo(wt.y), x.z, a0);
@@ -307,16 +310,21 @@ struct Wk {
           b1 = fmaf(bf16hi(wt.z), x.y, b1);
           b0 = fmaf(bf16lo(wt.w), x.z, b0);
           b1 = fmaf(bf16hi(wt.w), x.w, b1);
-          if (t == gs.ks - 1) {
-            const float ya = wave_sum(a0 + a1), yb = wave_sum(b0 + b1);
-            if (lane == 0) {
-              L.part[2 * u] = ya;
-              L.part[2 * u + 1] = yb;
-            }
-            a0 = a1 = b0 = b1 = 0.f;
-          }
+        }
+        const float ya = wave_sum(a0 + a1), yb = wave_sum(b0 + b1);
+        if (lane == 0) {
+          L.part[2 * u] = ya;
+          L.part[2 * u + 1] = yb;
         }
       }
+    }
+  }
+  __device__ __forceinline__ void reduce_batch(const StageGeo& gs, int32_t b, const v4u* cur) {
+    switch (gs.ks) {
+      case 8: reduce_batch_ks<8>(gs, b, cur); break;
+      case 4: reduce_batch_ks<4>(gs, b, cur); break;
+      case 2: reduce_batch_ks<2>(gs, b, cur); break;
+      default: reduce_batch_ks<1>(gs, b, cur); break;
     }
   }
   // After the stage's barrier: pair lp's outputs (the sum of its S units in a fixed order) go to
@@ -657,19 +665,32 @@ __device__ __forceinline__ void attention(Wk& K, const Att& at, int32_t l, int32
   bar();  // scratch reuse
 }
 
-// Merge of the chunk partials of one (query head, 32-dim slice): 16 chunk lanes x 32 dims.
+// Online-softmax state (m, S, A) of a set of positions, m in the exp2 domain: combine two.
+__device__ __forceinline__ void softmax_combine(float& M, float& S, float& A, float m2, float s2, float a2) {
+  const float Mn = fmaxf(M, m2);
+  const float fo = M == -INFINITY ? 0.f : exp2f(M - Mn);
+  const float fn = m2 == -INFINITY ? 0.f : exp2f(m2 - Mn);
+  S = S * fo + s2 * fn;
+  A = A * fo + a2 * fn;
+  M = Mn;
+}
+
+// Merge of the chunk partials of one (query head, kMergeDims-dim slice). Thread (chunk lane cl,
+// dim) folds chunks cl, cl + CL, ... in order; the chunk lanes of a wave are combined with
+// shuffles and the 8 waves in LDS, always in the same order.
 __device__ __forceinline__ void merge_unit(Wk& K, const Att& at, int32_t l, int32_t u, uint32_t epoch) {
   const KParams& P = K.P;
   const Lds& L = K.L;
   const Shape& s = P.s;
-  const int32_t slices = s.hd / kMergeDims;
+  constexpr int D = kMergeDims;
+  const int32_t slices = s.hd / D;
   const int32_t h = u / slices, sl = u % slices;
   const int32_t G = s.group();
   const int32_t j = h / G, g = h % G;
-  constexpr int CL = kThreads / kMergeDims;  // 16 chunk lanes
-  const int dim = K.tid % kMergeDims, cl = K.tid / kMergeDims;
+  constexpr int CL = kThreads / D;  // chunk lanes
+  const int dim = K.tid % D, cl = K.tid / D;
   float M = -INFINITY, S = 0.f, A = 0.f;
-  constexpr int KM = 4;  // chunks per thread in one pass (chunk lane stride 16)
+  constexpr int KM = 4;  // chunks per thread in one pass (chunk lane stride CL)
   for (int32_t c0 = cl; c0 < at.nch && !K.fail; c0 += CL * KM) {
     uint64_t wm[KM], wl[KM], wa[KM];
     uint32_t todo = 0;
@@ -687,7 +708,7 @@ __device__ __forceinline__ void merge_unit(Wk& K, const Att& at, int32_t l, int3
               P.ex + P.exo.part + ((int64_t)l * s.nwg + ch * s.nkv + j) * P.exo.part_words + g * (s.hd + 2);
           wm[k] = ld_x(pp + s.hd);
           wl[k] = ld_x(pp + s.hd + 1);
-          wa[k] = ld_x(pp + sl * kMergeDims + dim);
+          wa[k] = ld_x(pp + sl * D + dim);
         }
       }
 #pragma unroll
@@ -704,36 +725,30 @@ __device__ __forceinline__ void merge_unit(Wk& K, const Att& at, int32_t l, int3
       }
     }
 #pragma unroll
-    for (int k = 0; k < KM; ++k) {
-      if (present & (1u << k)) {
-        const float mk = __uint_as_float((uint32_t)(wm[k] >> 32));
-        const float lk = __uint_as_float((uint32_t)(wl[k] >> 32));
-        const float ak = __uint_as_float((uint32_t)(wa[k] >> 32));
-        const float Mn = fmaxf(M, mk);
-        const float fo = M == -INFINITY ? 0.f : exp2f(M - Mn);
-        const float fn = mk == -INFINITY ? 0.f : exp2f(mk - Mn);
-        S = S * fo + lk * fn;
-        A = A * fo + ak * fn;
-        M = Mn;
-      }
-    }
+    for (int k = 0; k < KM; ++k)
+      if (present & (1u << k))
+        softmax_combine(M, S, A, __uint_as_float((uint32_t)(wm[k] >> 32)), __uint_as_float((uint32_t)(wl[k] >> 32)),
+                        __uint_as_float((uint32_t)(wa[k] >> 32)));
   }
-  float* ms = L.scr;  // [16][32][3]
-  ms[(cl * kMergeDims + dim) * 3 + 0] = M;
-  ms[(cl * kMergeDims + dim) * 3 + 1] = S;
-  ms[(cl * kMergeDims + dim) * 3 + 2] = A;
+  // chunk lanes of this wave (lanes dim, dim + D, ...): butterfly over the lane bits above D
+#pragma unroll
+  for (int o = D; o < kWave; o <<= 1) {
+    const float m2 = __shfl_xor(M, o, kWave), s2 = __shfl_xor(S, o, kWave), a2 = __shfl_xor(A, o, kWave);
+    softmax_combine(M, S, A, m2, s2, a2);
+  }
+  float* ms = L.scr;  // [8 waves][D][3]
+  if (K.lane < D) {
+    ms[(K.v * D + dim) * 3 + 0] = M;
+    ms[(K.v * D + dim) * 3 + 1] = S;
+    ms[(K.v * D + dim) * 3 + 2] = A;
+  }
   bar();
-  if (K.tid < kMergeDims) {
-    float Mt = -INFINITY;
-    for (int k = 0; k < CL; ++k) Mt = fmaxf(Mt, ms[(k * kMergeDims + K.tid) * 3]);
-    float St = 0.f, At = 0.f;
-    for (int k = 0; k < CL; ++k) {
-      const float mk = ms[(k * kMergeDims + K.tid) * 3];
-      const float f = mk == -INFINITY ? 0.f : exp2f(mk - Mt);
-      St = fmaf(ms[(k * kMergeDims + K.tid) * 3 + 1], f, St);
-      At = fmaf(ms[(k * kMergeDims + K.tid) * 3 + 2], f, At);
-    }
-    st_x(P.ex + P.exo.o + (int64_t)l * s.qdim() + h * s.hd + sl * kMergeDims + K.tid, tag_f(At / St, epoch));
+  if (K.tid < D) {
+    float Mt = ms[K.tid * 3], St = ms[K.tid * 3 + 1], At = ms[K.tid * 3 + 2];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k)
+      softmax_combine(Mt, St, At, ms[(k * D + K.tid) * 3], ms[(k * D + K.tid) * 3 + 1], ms[(k * D + K.tid) * 3 + 2]);
+    st_x(P.ex + P.exo.o + (int64_t)l * s.qdim() + h * s.hd + sl * D + K.tid, tag_f(At / St, epoch));
   }
   bar();
 }
