@@ -12,6 +12,7 @@
 #include "../../include/kie_measure.h"
 #include "layout.h"
 #include "monokernel.h"
+#include "prefill.h"
 
 namespace kie {
 hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes, int32_t blocks, hipStream_t st);
@@ -383,16 +384,7 @@ kie_status kie_sync(kie_ctx* ctx) {
   return KIE_OK;
 }
 
-static kie_status launch(kie_ctx* ctx, const int32_t* first, int32_t n, const int32_t* forced, int32_t* toks_out,
-                         int32_t* last_tok, float* logits, int lm_last_only, const kie_sampling* smp) {
-  if (ctx->bad_state) {
-    set_err(&ctx->last_error, "context holds a device error; call kie_reset");
-    return KIE_ERR_STATE;
-  }
-  if (!first || n <= 0) {
-    set_err(&ctx->last_error, "first token pointer is NULL or n <= 0");
-    return KIE_ERR_INVALID_ARG;
-  }
+static kie_status check_sampling(kie_ctx* ctx, const kie_sampling* smp) {
   const int32_t top_k = smp && smp->top_k > 1 ? smp->top_k : 1;
   if (top_k > 1) {
     if (top_k > kMaxTopK || top_k > ctx->s.V) {
@@ -408,6 +400,22 @@ static kie_status launch(kie_ctx* ctx, const int32_t* first, int32_t n, const in
       return KIE_ERR_UNSUPPORTED;
     }
   }
+  return KIE_OK;
+}
+
+static kie_status launch(kie_ctx* ctx, const int32_t* first, int32_t n, const int32_t* forced, int32_t* toks_out,
+                         int32_t* last_tok, float* logits, int lm_last_only, const kie_sampling* smp) {
+  if (ctx->bad_state) {
+    set_err(&ctx->last_error, "context holds a device error; call kie_reset");
+    return KIE_ERR_STATE;
+  }
+  if (!first || n <= 0) {
+    set_err(&ctx->last_error, "first token pointer is NULL or n <= 0");
+    return KIE_ERR_INVALID_ARG;
+  }
+  const kie_status sst = check_sampling(ctx, smp);
+  if (sst != KIE_OK) return sst;
+  const int32_t top_k = smp && smp->top_k > 1 ? smp->top_k : 1;
   if ((int64_t)ctx->pos + n > ctx->s.max_seq) {
     set_err(&ctx->last_error, "position %d + %d tokens exceeds max_seq_len %d", ctx->pos, n, ctx->s.max_seq);
     return KIE_ERR_CAPACITY;
@@ -455,8 +463,39 @@ kie_status kie_prefill(kie_ctx* ctx, const int32_t* tokens_dev, int32_t n_tokens
     set_err(&ctx->last_error, "prefill needs tokens, an output token and n_tokens > 0");
     return KIE_ERR_INVALID_ARG;
   }
-  return launch(ctx, tokens_dev, n_tokens, n_tokens > 1 ? tokens_dev + 1 : nullptr, nullptr, first_token_dev,
-                last_logits_dev, 1, sampling);
+  if (ctx->bad_state) {
+    set_err(&ctx->last_error, "context holds a device error; call kie_reset");
+    return KIE_ERR_STATE;
+  }
+  const kie_status sst = check_sampling(ctx, sampling);
+  if (sst != KIE_OK) return sst;
+  if ((int64_t)ctx->pos + n_tokens > ctx->s.max_seq) {
+    set_err(&ctx->last_error, "position %d + %d tokens exceeds max_seq_len %d", ctx->pos, n_tokens, ctx->s.max_seq);
+    return KIE_ERR_CAPACITY;
+  }
+  // all but the last prompt position: every layer as GEMMs on the matrix cores (K/V rows only)
+  if (n_tokens > 1) {
+    HIP_TRY(&ctx->last_error, hipSetDevice(ctx->device));
+    PrefillArgs a;
+    a.s = ctx->s;
+    a.packed = ctx->packed;
+    a.wbase = (const int64_t*)(ctx->ws + ctx->wso.wbase);
+    a.embed = (const uint16_t*)(ctx->packed + packed_embed_offset(ctx->s));
+    a.norms = (const uint16_t*)(ctx->ws + ctx->wso.norms);
+    a.rope = (const float2*)(ctx->ws + ctx->wso.rope);
+    a.kv = ctx->kv;
+    a.err = (uint32_t*)(ctx->ws + ctx->wso.err);
+    a.tokens = tokens_dev;
+    a.x = (float*)(ctx->ws + ctx->wso.px);
+    a.a3 = (uint16_t*)(ctx->ws + ctx->wso.pa3);
+    a.a_part = (int64_t)kPrefillChunk * prefill_kmax(ctx->s);
+    a.c = (float*)(ctx->ws + ctx->wso.pc);
+    a.q = (float*)(ctx->ws + ctx->wso.pq);
+    HIP_TRY(&ctx->last_error, launch_prefill(a, ctx->pos, n_tokens - 1, ctx->stream));
+    ctx->pos += n_tokens - 1;
+  }
+  // the last position through the decode program: its K/V rows, the logits and the first token
+  return launch(ctx, tokens_dev + (n_tokens - 1), 1, nullptr, nullptr, first_token_dev, last_logits_dev, 1, sampling);
 }
 
 kie_status kie_decode_step(kie_ctx* ctx, const int32_t* token_in_dev, const kie_sampling* sampling,

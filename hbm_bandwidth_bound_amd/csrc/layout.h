@@ -209,12 +209,29 @@ KIE_HD Exch exch_layout(const Shape& s) {
   return e;
 }
 
+// Prompt pass scratch: positions per chunk, and the widest GEMM input and output rows.
+constexpr int kPrefillChunk = 512;
+KIE_HD int32_t prefill_kmax(const Shape& s) {
+  int32_t k = s.d;
+  if (s.qdim() > k) k = s.qdim();
+  if (s.F > k) k = s.F;
+  return k;
+}
+KIE_HD int32_t prefill_nmax(const Shape& s) {
+  int32_t n = 2 * s.stage_pairs(ST_QKV);
+  if (2 * s.F > n) n = 2 * s.F;
+  if (s.d > n) n = s.d;
+  return n;
+}
+
 // Workspace (bytes, 256-aligned pieces): exchange words, RoPE table [max_seq][hd/2] of (cos,sin),
-// per-stream base (in tiles, [nwg][8] + total), error word, norm gains [L][2][d] + final [d] (bf16).
+// per-stream base (in tiles, [nwg][8] + total), error word, norm gains [L][2][d] + final [d] (bf16),
+// trace counters, and the prompt-pass scratch (residual [chunk][d] fp32, GEMM input [3][chunk][kmax]
+// bf16, GEMM output [chunk][nmax] fp32, queries [chunk][nq hd] fp32).
 struct Workspace {
-  int64_t exch, rope, wbase, err, norms, trace, end;
+  int64_t exch, rope, wbase, err, norms, trace, px, pa3, pc, pq, end;
 };
-constexpr int kTraceWords = 24;  // per wave: cycle counters of a KIE_TRACE build
+constexpr int kTraceWords = 32;  // per wave: cycle counters of a KIE_TRACE build
 KIE_HD int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 KIE_HD Workspace workspace_layout(const Shape& s) {
   Workspace w;
@@ -225,6 +242,10 @@ KIE_HD Workspace workspace_layout(const Shape& s) {
   w.err = o; o = align256(o + 64);
   w.norms = o; o = align256(o + ((int64_t)s.L * 2 + 1) * s.d * 2);
   w.trace = o; o = align256(o + (int64_t)s.nwg * kWaves * kTraceWords * 8);
+  w.px = o; o = align256(o + (int64_t)kPrefillChunk * s.d * 4);
+  w.pa3 = o; o = align256(o + (int64_t)3 * kPrefillChunk * prefill_kmax(s) * 2);
+  w.pc = o; o = align256(o + (int64_t)kPrefillChunk * prefill_nmax(s) * 4);
+  w.pq = o; o = align256(o + (int64_t)kPrefillChunk * s.qdim() * 4);
   w.end = o;
   return w;
 }
@@ -238,6 +259,32 @@ KIE_HD int64_t packed_stream_tiles(const Shape& s) {
   return t;
 }
 KIE_HD int64_t packed_embed_offset(const Shape& s) { return packed_stream_tiles(s) * kTileBytes; }
+
+// Owner WG of global pair gp of a stage with n pairs (the inverse of the even split).
+KIE_HD int32_t pair_owner(int64_t n, int32_t nwg, int32_t gp) {
+  int32_t w = (int32_t)(((int64_t)gp * nwg) / n);
+  while (w + 1 < nwg && split_begin(n, nwg, w + 1) <= gp) ++w;
+  while (w > 0 && split_begin(n, nwg, w) > gp) --w;
+  return w;
+}
+// Where k-tile kt of pair gp of stage st in layer l lives in the packed image (in tiles); the LM
+// head is st == ST_LM (l ignored). wbase[w * kWaves + v] is the first tile of stream (w, v). This
+// inverts the packer's placement, so that a kernel can read the weights of any row in place.
+KIE_HD int64_t packed_tile(const Shape& s, const int64_t* wbase, int st, int32_t l, int32_t gp, int32_t kt) {
+  const int32_t w = pair_owner(s.stage_pairs(st), s.nwg, gp);
+  const StageGeo g = stage_geo(s, st, w);
+  const int32_t u = (gp - g.pb) * g.S + kt / g.ks;
+  const int32_t v = u % kWaves, m = u / kWaves;
+  const int32_t b = m / g.upb, slot = (m % g.upb) * g.ks + kt % g.ks;
+  int64_t bt;
+  if (st == ST_LM) {
+    bt = (int64_t)s.L * layer_batches(s, w, v);
+  } else {
+    bt = (int64_t)l * layer_batches(s, w, v);
+    for (int st2 = ST_QKV; st2 < st; ++st2) bt += wave_batches(stage_geo(s, st2, w), v);
+  }
+  return wbase[w * kWaves + v] + (bt + b) * kBatch + slot;
+}
 KIE_HD int64_t packed_bytes(const Shape& s) { return packed_embed_offset(s) + (int64_t)s.V * s.d * 2; }
 
 // KV cache: [L][2][nkv][max_seq][hd] bf16 (K plane, then V plane, per layer).

@@ -1081,20 +1081,31 @@ __device__ __forceinline__ void decode(Wk& K) {
           break;
         }
         case B_DN: {  // down outputs + residual -> next layer's input (or the LM head's)
+          uint64_t td = TR_NOW();
+          auto dphase = [&](int slot) {  // phase times of this boundary in a KIE_TRACE build
+            const uint64_t t = TR_NOW();
+            K.tr.add(slot, t - td);
+            td = t;
+          };
           bar();
+          dphase(24);
           uint64_t* xf = ex + X.xf + (int64_t)(l + 1) * s.d;
           K.finalize(K.g[ST_DN], [&](int32_t gp, float ya, float yb) {
             st_x(xf + 2 * gp, tag_f(L.xres[2 * gp] + ya, ep));
             st_x(xf + 2 * gp + 1, tag_f(L.xres[2 * gp + 1] + yb, ep));
           });
+          dphase(25);
           bar();
+          dphase(26);
           if (aborted(L)) {
             bnd = B_END;
             st = -1;
           } else if (l + 1 < s.L) {
             ++l;
             ss = K.fetch_f32(xf, s.d, L.xres, ep, true);
+            dphase(27);
             K.norm_to_act(ss, P.norms + (int64_t)l * 2 * s.d);
+            dphase(28);
             st = ST_QKV;
             bnd = B_QKV;
           } else if (lm) {

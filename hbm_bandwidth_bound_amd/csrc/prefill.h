@@ -1,0 +1,38 @@
+// prefill.h -- the prompt pass on the matrix cores (prefill.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "layout.h"
+
+namespace kie {
+
+// Buffers and tables of one prompt pass. The scratch buffers live in the workspace and hold one
+// chunk of at most kPrefillChunk positions.
+struct PrefillArgs {
+  Shape s;
+  const uint8_t* packed;     // packed weight image
+  const int64_t* wbase;      // [nwg * 8 + 1] first tile of each stream
+  const uint16_t* embed;     // [V][d] bf16
+  const uint16_t* norms;     // [L][2][d] bf16 gains
+  const float2* rope;        // [max_seq][hd/2] (cos, sin)
+  uint16_t* kv;              // cache [L][2][nkv][max_seq][hd] bf16
+  uint32_t* err;             // device error word
+  const int32_t* tokens;     // [n] prompt ids
+  float* x;                  // [chunk][d] residual stream
+  uint16_t* a3;              // [3][chunk][kmax] GEMM input in three bf16 parts
+  int64_t a_part;            // elements between the parts
+  float* c;                  // [chunk][nmax] GEMM output
+  float* q;                  // [chunk][nq * hd] rotated queries
+};
+
+struct GemmStage {
+  int32_t st, layer, K, N;
+  float* out;
+  int32_t ldo, accumulate;
+};
+
+// Run every layer over positions p0 .. p0 + n - 1 (writes their K/V rows).
+hipError_t launch_prefill(const PrefillArgs& a, int32_t p0, int32_t n, hipStream_t stream);
+
+}  // namespace kie

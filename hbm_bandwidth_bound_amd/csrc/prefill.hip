@@ -1,0 +1,330 @@
+// prefill.hip -- the prompt pass as dense matrix products on the matrix cores (MFMA).
+//
+// A prompt of P tokens is the same decoder applied to P positions at once, so its projections are
+// real GEMMs (P x K by K x N) and run on gfx950's bf16 MFMA; only the last prompt position goes
+// through the decode kernel, which adds the LM head and the sampler. The pages treat the prompt
+// pass as compute-bound and outside the per-token budget (wink.run, 《GPU 算力越堆越高,生成 token
+// 为什么还是慢》, the prefill/decode contrast; zdabc.icu 《Kog 推理引擎…》, the time-to-first-token
+// measurement), so nothing here is on the decode path.
+//
+// Precision: activations are fp32 like the decode path. A GEMM input x is split into three bf16
+// parts hi + mid + lo (each the bf16 rounding of what the previous parts leave; 24 bits in all)
+// and every weight tile is multiplied by all three, accumulating in fp32 inside the MFMA. The
+// weights are read in place from the packed image (the packer's placement, inverted per tile by
+// packed_tile), so no second copy of the model is kept.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "device_common.h"
+#include "layout.h"
+#include "monokernel.h"
+#include "prefill.h"
+
+namespace kie {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// x = hi + mid + lo (bf16 bits), each part the round-to-nearest-even of the remainder
+__device__ __forceinline__ void split3(float x, uint16_t* hi, uint16_t* mid, uint16_t* lo) {
+  const uint32_t h = f32_to_bf16(x);
+  const float r1 = x - bf16_to_f32(h);
+  const uint32_t m = f32_to_bf16(r1);
+  const float r2 = r1 - bf16_to_f32(m);
+  *hi = (uint16_t)h;
+  *mid = (uint16_t)m;
+  *lo = (uint16_t)f32_to_bf16(r2);
+}
+
+// ------------------------------------------------------------------------------------------
+// Embedding rows: X[i] = E[tok[i]] (fp32). An id out of range is replaced by 0 and reported.
+// ------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) prefill_embed_kernel(PrefillArgs a, int32_t c0, int32_t pc) {
+  const int32_t i = blockIdx.x;
+  if (i >= pc) return;
+  int32_t t = a.tokens[c0 + i];
+  if (t < 0 || t >= a.s.V) {
+    if (threadIdx.x == 0) __hip_atomic_fetch_or(a.err, KERR_BAD_TOKEN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    t = 0;
+  }
+  for (int32_t e = threadIdx.x; e < a.s.d; e += blockDim.x)
+    a.x[(int64_t)i * a.s.d + e] = bf16_to_f32(a.embed[(int64_t)t * a.s.d + e]);
+}
+
+// ------------------------------------------------------------------------------------------
+// RMSNorm of each row of X with gain g, written as the three-part GEMM input (row stride d).
+// The sum of squares runs in a fixed order (per-thread strided partials, then a fixed tree).
+// ------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) prefill_norm_split_kernel(PrefillArgs a, const uint16_t* gain, int32_t pc) {
+  __shared__ float red[256];
+  const int32_t i = blockIdx.x, d = a.s.d;
+  if (i >= pc) return;
+  const float* xr = a.x + (int64_t)i * d;
+  float ss = 0.f;
+  for (int32_t e = threadIdx.x; e < d; e += 256) ss = fmaf(xr[e], xr[e], ss);
+  red[threadIdx.x] = ss;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  const float r = 1.0f / sqrtf(red[0] / (float)d + a.s.eps);
+  for (int32_t e = threadIdx.x; e < d; e += 256) {
+    const float u = (xr[e] * r) * bf16_to_f32(gain[e]);
+    const int64_t o = (int64_t)i * d + e;
+    split3(u, a.a3 + o, a.a3 + a.a_part + o, a.a3 + 2 * a.a_part + o);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// GEMM on the matrix cores: C[i][n] (= or +=) sum_k A[i][k] W[n][k] for the rows n of one stage
+// in pair order (n = 2 gp + 0 for the pair's row A, + 1 for its row B), A given in three bf16
+// parts. Block: 64 tokens x 64 rows, 4 waves of 16 rows; K in chunks of 128 staged in LDS.
+// MFMA 16x16x32 bf16 operand layout (gfx950): lane l holds A[l%16][8(l/16) .. +7] and
+// B[8(l/16) .. +7][l%16]; the result D[4(l/16) + r][l%16] for r < 4.
+// ------------------------------------------------------------------------------------------
+constexpr int kGemmM = 64, kGemmN = 64, kGemmKC = 128;
+constexpr int kALd = kGemmKC + 8;  // padded LDS row (bf16), spreads the rows over the banks
+
+__global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillArgs a, GemmStage g, int32_t pc) {
+  __shared__ __align__(16) uint16_t As[3][kGemmM][kALd];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int32_t m0 = blockIdx.y * kGemmM;
+  const int nl = lane & 15, kg = lane >> 4;
+  const int32_t n = blockIdx.x * kGemmN + wv * 16 + nl;
+  const bool nvalid = n < g.N;
+  const int32_t gp = nvalid ? n >> 1 : 0;
+  const int sel = n & 1;
+  const int32_t ks_unit = unit_tiles(a.s.stage_kt(g.st));
+  f4 acc[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) acc[mb] = f4{0.f, 0.f, 0.f, 0.f};
+  int64_t tbase = 0;  // first tile of the current unit of this lane's pair
+  for (int32_t kc = 0; kc < g.K; kc += kGemmKC) {
+    for (int q = tid; q < 3 * kGemmM * (kGemmKC / 8); q += 256) {
+      const int p = q / (kGemmM * (kGemmKC / 8)), r = (q / (kGemmKC / 8)) % kGemmM, c = q % (kGemmKC / 8);
+      const int32_t i = m0 + r;
+      uint4 v = {0u, 0u, 0u, 0u};
+      if (i < pc) v = *(const uint4*)(a.a3 + p * a.a_part + (int64_t)i * g.K + kc + c * 8);
+      *(uint4*)&As[p][r][c * 8] = v;
+    }
+    __syncthreads();
+    const int32_t kt = kc / kTileK;
+    if (kt % ks_unit == 0 && kc % kTileK == 0)
+      tbase = nvalid ? packed_tile(a.s, a.wbase, g.st, g.layer, gp, kt) : 0;
+    const uint8_t* tp = a.packed + (tbase + kt % ks_unit) * kTileBytes + 8 * sel;
+#pragma unroll
+    for (int ks = 0; ks < kGemmKC / 32; ++ks) {
+      const int kin = kc % kTileK + ks * 32 + kg * 8;  // k inside the 256-k tile
+      const int L = kin >> 2;                           // tile lane holding k .. k+3
+      uint2 w0 = {0u, 0u}, w1 = {0u, 0u};
+      if (nvalid) {
+        w0 = *(const uint2*)(tp + 16 * L);
+        w1 = *(const uint2*)(tp + 16 * (L + 1));
+      }
+      const bf16x8 b = __builtin_bit_cast(bf16x8, uint4{w0.x, w0.y, w1.x, w1.y});
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+        for (int p = 0; p < 3; ++p) {
+          const bf16x8 av = *(const bf16x8*)&As[p][mb * 16 + nl][ks * 32 + kg * 8];
+          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b, acc[mb], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (!nvalid) return;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int32_t i = m0 + mb * 16 + kg * 4 + r;
+      if (i < pc) {
+        float* o = g.out + (int64_t)i * g.ldo + n;
+        *o = g.accumulate ? *o + acc[mb][r] : acc[mb][r];
+      }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// RoPE and the cache: QKV output (pair order) -> rotated queries Q[i][nq*hd] (fp32), and the
+// rotated keys and the values of positions pos0 + i written to the cache as bf16.
+// ------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) prefill_rope_kv_kernel(PrefillArgs a, int32_t layer, int32_t p0, int32_t pc) {
+  const Shape& s = a.s;
+  const int32_t i = blockIdx.x;
+  if (i >= pc) return;
+  const int32_t pos = p0 + i, half = s.hd / 2;
+  const int32_t npairs = s.stage_pairs(ST_QKV);
+  const float* c = a.c + (int64_t)i * 2 * npairs;
+  for (int32_t gp = threadIdx.x; gp < npairs; gp += blockDim.x) {
+    const int32_t hs = gp / half, e = gp % half;
+    float ya = c[2 * gp], yb = c[2 * gp + 1];
+    if (hs < s.nq + s.nkv) {
+      const float2 cs = a.rope[(int64_t)pos * half + e];
+      const float ra = ya * cs.x - yb * cs.y, rb = yb * cs.x + ya * cs.y;
+      ya = ra;
+      yb = rb;
+    }
+    if (hs < s.nq) {
+      a.q[(int64_t)i * s.qdim() + hs * s.hd + e] = ya;
+      a.q[(int64_t)i * s.qdim() + hs * s.hd + e + half] = yb;
+    } else {
+      const int kv = hs < s.nq + s.nkv ? 0 : 1;
+      const int32_t j = kv == 0 ? hs - s.nq : hs - s.nq - s.nkv;
+      uint16_t* row = a.kv + kv_offset(s, layer, kv, j, pos);
+      row[e] = (uint16_t)f32_to_bf16(ya);
+      row[e + half] = (uint16_t)f32_to_bf16(yb);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Causal attention of the chunk's queries over positions 0 .. pos (cache rows, this chunk's rows
+// included). Block: one query head x 64 queries, 4 lanes per query (HD/4 dimensions each); keys
+// in tiles of 32 positions staged in LDS as fp32; online softmax in the exp2 domain per tile.
+// The output is written as the three-part input of the O projection.
+// ------------------------------------------------------------------------------------------
+constexpr int kAttnQ = 64, kAttnKT = 32;
+
+template <int HD>
+__global__ void __launch_bounds__(256) prefill_attn_kernel(PrefillArgs a, int32_t layer, int32_t p0, int32_t pc) {
+  constexpr int DQ = HD / 4;
+  __shared__ __align__(16) float Ks[kAttnKT][HD];
+  __shared__ __align__(16) float Vs[kAttnKT][HD];
+  const Shape& s = a.s;
+  const int32_t h = blockIdx.x, j = h / s.group();
+  const int tid = threadIdx.x, tq = tid >> 2, part = tid & 3;
+  const int32_t i = blockIdx.y * kAttnQ + tq;
+  const bool valid = i < pc;
+  const int32_t pos = p0 + (valid ? i : pc - 1);
+  const float scale = 1.4426950408889634f / sqrtf((float)HD);  // log2(e) / sqrt(hd)
+  float q[DQ], acc[DQ];
+#pragma unroll
+  for (int e = 0; e < DQ; ++e) {
+    q[e] = a.q[(int64_t)(valid ? i : 0) * s.qdim() + h * HD + part * DQ + e] * scale;
+    acc[e] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  const int32_t ilast = min(pc, (int32_t)(blockIdx.y + 1) * kAttnQ) - 1;
+  const int32_t kend = p0 + ilast;  // last key any query of the block needs
+  const uint16_t* kbase = a.kv + kv_offset(s, layer, 0, j, 0);
+  const uint16_t* vbase = a.kv + kv_offset(s, layer, 1, j, 0);
+  for (int32_t k0 = 0; k0 <= kend; k0 += kAttnKT) {
+    __syncthreads();
+    for (int q2 = tid; q2 < kAttnKT * HD / 2; q2 += 256) {
+      const int r = q2 / (HD / 2), c = (q2 % (HD / 2)) * 2;
+      const int32_t kp = k0 + r;
+      uint32_t kk = 0u, vv = 0u;
+      if (kp <= kend) {
+        kk = *(const uint32_t*)(kbase + (int64_t)kp * HD + c);
+        vv = *(const uint32_t*)(vbase + (int64_t)kp * HD + c);
+      }
+      Ks[r][c] = bf16lo(kk);
+      Ks[r][c + 1] = bf16hi(kk);
+      Vs[r][c] = bf16lo(vv);
+      Vs[r][c + 1] = bf16hi(vv);
+    }
+    __syncthreads();
+    float sc[kAttnKT];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < kAttnKT; ++r) {
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < DQ; ++e) d = fmaf(q[e], Ks[r][part * DQ + e], d);
+      d += __shfl_xor(d, 1, 64);
+      d += __shfl_xor(d, 2, 64);
+      sc[r] = (k0 + r <= pos) ? d : -INFINITY;
+      mt = fmaxf(mt, sc[r]);
+    }
+    const float mn = fmaxf(m, mt);
+    const float corr = m == -INFINITY ? 0.f : exp2f(m - mn);
+    l *= corr;
+#pragma unroll
+    for (int e = 0; e < DQ; ++e) acc[e] *= corr;
+#pragma unroll
+    for (int r = 0; r < kAttnKT; ++r) {
+      const float pr = sc[r] == -INFINITY ? 0.f : exp2f(sc[r] - mn);
+      l += pr;
+#pragma unroll
+      for (int e = 0; e < DQ; ++e) acc[e] = fmaf(pr, Vs[r][part * DQ + e], acc[e]);
+    }
+    m = mn;
+  }
+  if (!valid) return;
+  const float inv = 1.0f / l;
+#pragma unroll
+  for (int e = 0; e < DQ; ++e) {
+    const int64_t o = (int64_t)i * s.qdim() + h * HD + part * DQ + e;
+    split3(acc[e] * inv, a.a3 + o, a.a3 + a.a_part + o, a.a3 + 2 * a.a_part + o);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// SwiGLU of the gate/up output (pair f = gate row f, up row f) into the three-part input of the
+// down projection.
+// ------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) prefill_swiglu_kernel(PrefillArgs a, int32_t pc) {
+  const int32_t i = blockIdx.x, F = a.s.F;
+  if (i >= pc) return;
+  const float* c = a.c + (int64_t)i * 2 * F;
+  for (int32_t f = threadIdx.x; f < F; f += 256) {
+    const float ya = c[2 * f], yb = c[2 * f + 1];
+    const float hv = (ya / (1.0f + expf(-ya))) * yb;
+    const int64_t o = (int64_t)i * F + f;
+    split3(hv, a.a3 + o, a.a3 + a.a_part + o, a.a3 + 2 * a.a_part + o);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// The chunked prompt pass: positions p0 .. p0 + n - 1, every layer, K/V rows written to the cache.
+// ------------------------------------------------------------------------------------------
+static hipError_t gemm(const PrefillArgs& a, int st, int32_t layer, int32_t K, float* out, int32_t ldo, int accumulate,
+                       int32_t pc, hipStream_t stream) {
+  GemmStage g;
+  g.st = st;
+  g.layer = layer;
+  g.K = K;
+  g.N = 2 * a.s.stage_pairs(st);
+  g.out = out;
+  g.ldo = ldo;
+  g.accumulate = accumulate;
+  hipLaunchKernelGGL(prefill_gemm_kernel, dim3((g.N + kGemmN - 1) / kGemmN, (pc + kGemmM - 1) / kGemmM), dim3(256), 0,
+                     stream, a, g, pc);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, int32_t p0, int32_t n, hipStream_t stream) {
+  const Shape& s = a.s;
+  for (int32_t c0 = 0; c0 < n; c0 += kPrefillChunk) {
+    const int32_t pc = n - c0 < kPrefillChunk ? n - c0 : kPrefillChunk;
+    const int32_t pos = p0 + c0;
+    hipLaunchKernelGGL(prefill_embed_kernel, dim3(pc), dim3(256), 0, stream, a, c0, pc);
+    for (int32_t l = 0; l < s.L; ++l) {
+      hipLaunchKernelGGL(prefill_norm_split_kernel, dim3(pc), dim3(256), 0, stream, a, a.norms + (int64_t)l * 2 * s.d, pc);
+      hipError_t e = gemm(a, ST_QKV, l, s.d, a.c, 2 * s.stage_pairs(ST_QKV), 0, pc, stream);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(prefill_rope_kv_kernel, dim3(pc), dim3(256), 0, stream, a, l, pos, pc);
+      if (s.hd == 128)
+        hipLaunchKernelGGL(prefill_attn_kernel<128>, dim3(s.nq, (pc + kAttnQ - 1) / kAttnQ), dim3(256), 0, stream, a, l,
+                           pos, pc);
+      else
+        hipLaunchKernelGGL(prefill_attn_kernel<64>, dim3(s.nq, (pc + kAttnQ - 1) / kAttnQ), dim3(256), 0, stream, a, l,
+                           pos, pc);
+      if ((e = gemm(a, ST_O, l, s.qdim(), a.x, s.d, 1, pc, stream)) != hipSuccess) return e;
+      hipLaunchKernelGGL(prefill_norm_split_kernel, dim3(pc), dim3(256), 0, stream, a,
+                         a.norms + (int64_t)l * 2 * s.d + s.d, pc);
+      if ((e = gemm(a, ST_GU, l, s.d, a.c, 2 * s.F, 0, pc, stream)) != hipSuccess) return e;
+      hipLaunchKernelGGL(prefill_swiglu_kernel, dim3(pc), dim3(256), 0, stream, a, pc);
+      if ((e = gemm(a, ST_DN, l, s.F, a.x, s.d, 1, pc, stream)) != hipSuccess) return e;
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kie

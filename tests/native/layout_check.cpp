@@ -60,6 +60,39 @@ static int check(const Shape& s) {
       return 1;
     }
   }
+  // packed_tile inverts the placement: stream (w, v), batch b, slot sl of stage st in layer l
+  std::vector<int64_t> wbase((size_t)s.nwg * kWaves + 1);
+  int64_t acc = 0;
+  for (int32_t w = 0; w < s.nwg; ++w)
+    for (int32_t v = 0; v < kWaves; ++v) {
+      wbase[(size_t)w * kWaves + v] = acc;
+      acc += stream_tiles(s, w, v);
+    }
+  const int32_t layers[3] = {0, s.L - 1, s.L};  // first layer, last layer, LM head
+  for (int li = 0; li < 3; ++li) {
+    const int32_t l = layers[li];
+    for (int32_t w = 0; w < s.nwg; ++w)
+      for (int32_t v = 0; v < kWaves; ++v) {
+        int64_t t0 = wbase[(size_t)w * kWaves + v] + (int64_t)l * layer_batches(s, w, v) * kBatch;
+        for (int st = (l == s.L ? ST_LM : ST_QKV); st <= (l == s.L ? ST_LM : ST_DN); ++st) {
+          const StageGeo g = stage_geo(s, st, w);
+          const int32_t nbv = wave_batches(g, v);
+          for (int32_t b = 0; b < nbv; ++b)
+            for (int32_t sl = 0; sl < kBatch; ++sl) {
+              const int32_t u = v + kWaves * (b * g.upb + sl / g.ks);
+              if (u >= g.nu) continue;
+              const int32_t gp = g.pb + u / g.S, kt = (u % g.S) * g.ks + sl % g.ks;
+              const int64_t got = packed_tile(s, wbase.data(), st, l, gp, kt);
+              if (got != t0 + (int64_t)b * kBatch + sl) {
+                std::printf("packed_tile mismatch l=%d st=%d gp=%d kt=%d: %lld vs %lld\n", l, st, gp, kt, (long long)got,
+                            (long long)(t0 + (int64_t)b * kBatch + sl));
+                return 1;
+              }
+            }
+          t0 += (int64_t)nbv * kBatch;
+        }
+      }
+  }
   std::printf("ok %lld tiles\n", (long long)total);
   return 0;
 }

@@ -266,3 +266,35 @@ def test_tiny_decode_over_caller_filled_cache(torch_cuda, tiny, oracle_lib):
     worst, checked = check_steps(logits.cpu().numpy(), ref, toks, label="tiny synthetic KV")
     say(f"  worst rel-L2 {worst:.3e}, greedy checked {checked}/{N}")
     eng.close()
+
+
+def test_tiny_prefill_in_two_calls_and_chunks(torch_cuda, tiny, oracle_lib):
+    """The prompt pass continues an existing context: 700 positions, then 600 more (chunks of the
+    matrix-core pass end at ragged lengths); the cache and the last logits match the oracle's."""
+    import torch
+    from hbm_bandwidth_bound_amd.kie import Engine
+    cfg, w, wd = tiny
+    P1, P2 = 700, 600
+    say(f"[tiny] prefill {P1} then {P2}")
+    prompt = synth.prompt_ids(P1 + P2, cfg.vocab_size, 21)
+    eng = Engine(cfg, wd, P1 + P2)
+    eng.prefill(torch.tensor(prompt[:P1], dtype=torch.int32, device="cuda"))
+    last = torch.empty(cfg.vocab_size, dtype=torch.float32, device="cuda")
+    first = eng.prefill(torch.tensor(prompt[P1:], dtype=torch.int32, device="cuda"), logits_out=last)
+    eng.sync()
+    assert eng.position == P1 + P2
+    om = oracle_lib.OracleModel(cfg, w, P1 + P2)
+    ref = om.run(prompt)
+    e = rel_l2(last.cpu().numpy(), ref[-1])
+    say(f"  last-logits rel-L2 {e:.3e}")
+    assert e <= 1e-3
+    if top2_gap(ref[-1]) > 0.05:
+        assert int(first.item()) == int(np.argmax(ref[-1]))
+    kg = eng.kv_view().cpu().numpy().view(np.uint16)
+    ko, vo = om.kv_view()
+    n = P1 + P2
+    ek = rel_l2(synth.bf16_bits_to_f32(kg[:, 0, :, :n]), synth.bf16_bits_to_f32(ko[:, :, :n]))
+    ev = rel_l2(synth.bf16_bits_to_f32(kg[:, 1, :, :n]), synth.bf16_bits_to_f32(vo[:, :, :n]))
+    say(f"  cache rel-L2 K {ek:.3e} V {ev:.3e}")
+    assert ek <= 1e-3 and ev <= 1e-3
+    eng.close()
