@@ -134,6 +134,11 @@ def main():
     e1.record(stream)
     eng.sync()
     ttft_ms = e0.elapsed_time(e1)
+    # the prompt pass's matrix products: 2 x (tokens - 1) x the layer weights (the last position
+    # runs through the decode kernel), plus the causal attention products
+    mm = traffic.weight_bytes(m) // 2 - m.vocab_size * m.d_model - (2 * m.n_layers + 2) * m.d_model
+    attn = 4 * m.n_layers * m.n_heads * m.head_dim * (P - 1) * P // 2
+    prefill_flops = 2 * (P - 1) * mm + attn
 
     out = torch.empty(max(K, W), dtype=torch.int32, device=dev)
     if W > 0:
@@ -230,7 +235,10 @@ def main():
         "extra": {"kernel_ms": round(launch_ms, 3), "algorithmic_bytes": algo_bytes,
                   "bytes_per_token": algo_bytes / K, "stream_read_ceiling_GBps": round(ceiling_gbps, 1),
                   "frac_of_stream_ceiling": round(achieved_gbps / ceiling_gbps, 4),
-                  "ttft_ms_prompt_pass": round(ttft_ms, 2), "one_token_launches": single,
+                  "ttft_ms_prompt_pass": round(ttft_ms, 2),
+                  "prompt_pass": {"flops": prefill_flops, "tflops": round(prefill_flops / (ttft_ms * 1e-3) / 1e12, 1),
+                                  "frac_of_bf16_mfma_peak": round(prefill_flops / (ttft_ms * 1e-3) / 2.5e15, 4)},
+                  "one_token_launches": single,
                   "topk50_T0.8_tok_s": round(topk_tok_s, 2),
                   "source_sha": source_hash()},
     }

@@ -71,7 +71,7 @@ struct Tracer {
 // ------------------------------------------------------------------------------------------
 struct Lds {
   float* act;      // GEMV input of the current stage (fp32)
-  float* xres;     // residual stream of the current layer (fp32, d)
+  float* xres;     // residual stream, two buffers of d floats (the current one alternates)
   float* part;     // [kMaxUnits][2] per-unit dot products of the current stage
   float* scr;      // attention / merge / reduction scratch
   float* q;        // attention: the group's queries [G][hd], the current k [hd] and v [hd]
@@ -99,11 +99,11 @@ __host__ __device__ inline int32_t scr_floats(const Shape& s) {
 __host__ __device__ inline int32_t merge_pad_floats(const Shape& s) {
   const int32_t kmax = kMaxTopK < s.V ? kMaxTopK : s.V;
   const int32_t need = (topk_merge_floats(s, kmax) + 3) & ~3;
-  const int32_t have = act_floats(s) + s.d + 2 * kMaxUnits;
+  const int32_t have = act_floats(s) + 2 * s.d + 2 * kMaxUnits;
   return need > have ? need - have : 0;
 }
 __host__ __device__ inline int32_t merge_floats(const Shape& s) {
-  return act_floats(s) + s.d + 2 * kMaxUnits + merge_pad_floats(s);
+  return act_floats(s) + 2 * s.d + 2 * kMaxUnits + merge_pad_floats(s);
 }
 inline int32_t lds_bytes_for_impl(const Shape& s) {
   return (merge_floats(s) + scr_floats(s) + (s.group() + 2) * s.hd + s.hd) * 4 + C_COUNT * 4;
@@ -112,7 +112,7 @@ __device__ __forceinline__ Lds lds_map(uint8_t* smem, const Shape& s) {
   Lds L;
   uint8_t* p = smem;
   L.act = (float*)p; p += (size_t)act_floats(s) * 4;
-  L.xres = (float*)p; p += (size_t)s.d * 4;
+  L.xres = (float*)p; p += (size_t)2 * s.d * 4;
   L.part = (float*)p; p += (size_t)2 * kMaxUnits * 4;
   p += (size_t)merge_pad_floats(s) * 4;
   L.scr = (float*)p; p += (size_t)scr_floats(s) * 4;
@@ -393,10 +393,10 @@ struct Wk {
   }
   // n words into LDS floats dst; returns their sum of squares (fixed order) if want_ss.
   // Ends with a barrier: dst is complete for every wave.
+  template <int KM = 8>
   __device__ __forceinline__ float fetch_f32(const uint64_t* src, int32_t n, float* dst, uint32_t epoch,
                                              bool want_ss) {
     const uint64_t t0 = TR_NOW();
-    constexpr int KM = 8;
     for (int32_t base = 0; base < n; base += KM * kThreads) {
       const int32_t e0 = base + tid;
       poll<KM>(
@@ -426,14 +426,38 @@ struct Wk {
     tr.add(T_FETCH, TR_NOW() - t0);
     bar();
   }
-  // act = (xres * r) * g with r = 1 / sqrt(ss / d + eps). Ends with a barrier.
-  __device__ __forceinline__ void norm_to_act(float ss, const uint16_t* gain) {
+  // The gains of the next RMSNorm, loaded before the wait for its input so that their latency
+  // overlaps the wait (the first kNormPre groups of 4 of this thread; the rest load on use).
+  static constexpr int kNormPre = 2;
+  uint2 gpre[kNormPre];
+  const uint16_t* gnext;
+  __device__ __forceinline__ void prefetch_gain(const uint16_t* gain) {
+    gnext = gain;
+#pragma unroll
+    for (int k = 0; k < kNormPre; ++k) {
+      const int32_t rec = tid + k * kThreads;
+      gpre[k] = rec < P.s.d / 4 ? *(const uint2*)(gain + 4 * rec) : uint2{0u, 0u};
+    }
+  }
+  // act = (x * r) * g with r = 1 / sqrt(ss / d + eps), x the residual buffer xs and g the gains
+  // of the last prefetch_gain. Ends with a barrier.
+  __device__ __forceinline__ void norm_to_act(float ss, const float* xs) {
     const uint64_t t0 = TR_NOW();
     const int32_t d = P.s.d;
     const float r = 1.0f / sqrtf(ss / (float)d + P.s.eps);
-    for (int32_t rec = tid; rec < d / 4; rec += kThreads) {
-      const v4f x = *(const v4f*)(L.xres + 4 * rec);
-      const uint2 gg = *(const uint2*)(gain + 4 * rec);
+#pragma unroll
+    for (int k = 0; k < kNormPre; ++k) {
+      const int32_t rec = tid + k * kThreads;
+      if (rec < d / 4) {
+        const v4f x = *(const v4f*)(xs + 4 * rec);
+        const uint2 gg = gpre[k];
+        *(v4f*)(L.act + 4 * rec) = v4f{(x.x * r) * bf16lo(gg.x), (x.y * r) * bf16hi(gg.x), (x.z * r) * bf16lo(gg.y),
+                                       (x.w * r) * bf16hi(gg.y)};
+      }
+    }
+    for (int32_t rec = tid + kNormPre * kThreads; rec < d / 4; rec += kThreads) {
+      const v4f x = *(const v4f*)(xs + 4 * rec);
+      const uint2 gg = *(const uint2*)(gnext + 4 * rec);
       *(v4f*)(L.act + 4 * rec) = v4f{(x.x * r) * bf16lo(gg.x), (x.y * r) * bf16hi(gg.x), (x.z * r) * bf16lo(gg.y),
                                      (x.w * r) * bf16hi(gg.y)};
     }
@@ -988,6 +1012,7 @@ __device__ __forceinline__ void decode(Wk& K) {
   Att at = att_info(s, K.w, pos);
   bool lm = step_has_lm(P, 0);
   float ss = 0.f;
+  float* xres = L.xres;  // the current residual buffer (of two)
   int bnd = B_START;  // the next boundary
   int st = -1;        // stage of the batches being reduced
   int32_t rem = 0, b = 0;
@@ -1000,14 +1025,15 @@ __device__ __forceinline__ void decode(Wk& K) {
       switch (bnd) {
         case B_START: {  // embedding row -> residual stream, RMSNorm of layer 0
           if (tid < s.hd / 2) L.rope[tid] = P.rope[(int64_t)pos * (s.hd / 2) + tid];
+          K.prefetch_gain(P.norms);
           float sq = 0.f;
           for (int32_t i = tid; i < s.d; i += kThreads) {
             const float x = __uint_as_float((uint32_t)P.embed[(int64_t)tok * s.d + i] << 16);
-            L.xres[i] = x;
+            xres[i] = x;
             sq = fmaf(x, x, sq);
           }
           ss = K.block_sum(sq);
-          K.norm_to_act(ss, P.norms);
+          K.norm_to_act(ss, xres);
           st = ST_QKV;
           bnd = B_QKV;
           break;
@@ -1058,13 +1084,14 @@ __device__ __forceinline__ void decode(Wk& K) {
           bar();
           if (at.has_p) __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this WG's K/V rows are complete first
           uint64_t* xa = ex + X.xa + (int64_t)l * s.d;
+          K.prefetch_gain(P.norms + (int64_t)l * 2 * s.d + s.d);
           K.finalize(K.g[ST_O], [&](int32_t gp, float ya, float yb) {
-            st_x(xa + 2 * gp, tag_f(L.xres[2 * gp] + ya, ep));
-            st_x(xa + 2 * gp + 1, tag_f(L.xres[2 * gp + 1] + yb, ep));
+            st_x(xa + 2 * gp, tag_f(xres[2 * gp] + ya, ep));
+            st_x(xa + 2 * gp + 1, tag_f(xres[2 * gp + 1] + yb, ep));
           });
-          bar();  // every wave is done with xres before it is replaced
-          ss = K.fetch_f32(xa, s.d, L.xres, ep, true);
-          K.norm_to_act(ss, P.norms + (int64_t)l * 2 * s.d + s.d);
+          xres = xres == L.xres ? L.xres + s.d : L.xres;  // the other buffer: no wave reads it now
+          ss = K.fetch_f32(xa, s.d, xres, ep, true);
+          K.norm_to_act(ss, xres);
           st = ST_GU;
           bnd = B_GU;
           break;
@@ -1075,7 +1102,7 @@ __device__ __forceinline__ void decode(Wk& K) {
           K.finalize(K.g[ST_GU], [&](int32_t gp, float ya, float yb) {
             st_x(hx + gp, tag_f((ya / (1.0f + expf(-ya))) * yb, ep));
           });
-          K.fetch_f32(hx, s.F, L.act, ep, false);
+          K.fetch_f32<16>(hx, s.F, L.act, ep, false);
           st = ST_DN;
           bnd = B_DN;
           break;
@@ -1090,27 +1117,35 @@ __device__ __forceinline__ void decode(Wk& K) {
           bar();
           dphase(24);
           uint64_t* xf = ex + X.xf + (int64_t)(l + 1) * s.d;
+          K.prefetch_gain(P.norms + (l + 1 < s.L ? (int64_t)(l + 1) * 2 * s.d : (int64_t)s.L * 2 * s.d));
           K.finalize(K.g[ST_DN], [&](int32_t gp, float ya, float yb) {
-            st_x(xf + 2 * gp, tag_f(L.xres[2 * gp] + ya, ep));
-            st_x(xf + 2 * gp + 1, tag_f(L.xres[2 * gp + 1] + yb, ep));
+            st_x(xf + 2 * gp, tag_f(xres[2 * gp] + ya, ep));
+            st_x(xf + 2 * gp + 1, tag_f(xres[2 * gp + 1] + yb, ep));
           });
           dphase(25);
-          bar();
+#ifdef KIE_TRACE
+          if (step == 8 && l == 12) K.tr.c[29] = now_ticks();  // one sample of absolute times
+#endif
+          xres = xres == L.xres ? L.xres + s.d : L.xres;  // the other buffer: no wave reads it now
           dphase(26);
           if (aborted(L)) {
+            bar();
             bnd = B_END;
             st = -1;
           } else if (l + 1 < s.L) {
             ++l;
-            ss = K.fetch_f32(xf, s.d, L.xres, ep, true);
+            ss = K.fetch_f32(xf, s.d, xres, ep, true);
+#ifdef KIE_TRACE
+            if (step == 8 && l == 13) K.tr.c[30] = now_ticks();
+#endif
             dphase(27);
-            K.norm_to_act(ss, P.norms + (int64_t)l * 2 * s.d);
+            K.norm_to_act(ss, xres);
             dphase(28);
             st = ST_QKV;
             bnd = B_QKV;
           } else if (lm) {
-            ss = K.fetch_f32(xf, s.d, L.xres, ep, true);
-            K.norm_to_act(ss, P.norms + (int64_t)s.L * 2 * s.d);
+            ss = K.fetch_f32(xf, s.d, xres, ep, true);
+            K.norm_to_act(ss, xres);
             st = ST_LM;
             bnd = B_LM;
           } else {
