@@ -298,3 +298,34 @@ def test_tiny_prefill_in_two_calls_and_chunks(torch_cuda, tiny, oracle_lib):
     say(f"  cache rel-L2 K {ek:.3e} V {ev:.3e}")
     assert ek <= 1e-3 and ev <= 1e-3
     eng.close()
+
+
+# Small shapes that exercise the other kernel instantiations (query heads per KV head 1, 4, 8;
+# head_dim 64 and 128), a vocabulary that does not split evenly, and 2-tile rows.
+OTHER_SHAPES = [
+    synth.ModelConfig("mha-hd64", 2, 256, 4, 4, 64, 512, 2050),        # G = 1 (MHA), hd 64
+    synth.ModelConfig("g4-hd64", 2, 512, 8, 2, 64, 1024, 3002),        # G = 4, hd 64
+    synth.ModelConfig("g8-hd128", 2, 1024, 8, 1, 128, 1536, 4096),     # G = 8, one KV head, hd 128
+    synth.ModelConfig("mha-hd128", 1, 512, 4, 4, 128, 768, 1000),      # G = 1, hd 128, 3-tile FFN rows
+]
+
+
+@pytest.mark.parametrize("cfg", OTHER_SHAPES, ids=[c.name for c in OTHER_SHAPES])
+def test_other_head_groupings(torch_cuda, oracle_lib, cfg):
+    from hbm_bandwidth_bound_amd.kie import Engine
+    P, N = 40, 6
+    say(f"[{cfg.name}] prefill {P} + decode {N}")
+    w = synth.make_weights_np(cfg, 0)
+    wd = to_device(w)
+    eng = Engine(cfg, wd, P + N)
+    prompt = synth.prompt_ids(P, cfg.vocab_size, 9)
+    first, last, toks, logits = run_gpu(torch_cuda, eng, prompt, N, cfg.vocab_size)
+    om = oracle_lib.OracleModel(cfg, w, P + N)
+    ref_prompt = om.run(prompt)
+    assert rel_l2(last, ref_prompt[-1]) <= 1e-3
+    if top2_gap(ref_prompt[-1]) > 0.05:
+        assert first == int(np.argmax(ref_prompt[-1]))
+    ref = om.run([first] + [int(t) for t in toks[:-1]], start_pos=P)
+    worst, checked = check_steps(logits, ref, toks, label=cfg.name)
+    say(f"  worst rel-L2 {worst:.3e}, greedy checked {checked}/{N}")
+    eng.close()
