@@ -74,3 +74,12 @@ def test_no_gpu_paths_fail_cleanly(lib):
     assert lib.kie_reset(None) == -1
     assert lib.kie_set_position(None, 0) == -1
     lib.kie_destroy(None)
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    """No fallback: without the built library the binding raises instead of computing elsewhere."""
+    from hbm_bandwidth_bound_amd import kie
+    monkeypatch.setattr(kie, "_lib", None)
+    monkeypatch.setattr(kie, "LIB_PATH", str(tmp_path / "absent" / "libkie.so"))
+    with pytest.raises(RuntimeError):
+        kie.load()
