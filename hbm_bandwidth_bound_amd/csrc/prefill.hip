@@ -103,29 +103,41 @@ __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillArgs a, GemmSt
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) acc[mb] = f4{0.f, 0.f, 0.f, 0.f};
   int64_t tbase = 0;  // first tile of the current unit of this lane's pair
+  constexpr int KSTEPS = kGemmKC / 32;
   for (int32_t kc = 0; kc < g.K; kc += kGemmKC) {
-    for (int q = tid; q < 3 * kGemmM * (kGemmKC / 8); q += 256) {
-      const int p = q / (kGemmM * (kGemmKC / 8)), r = (q / (kGemmKC / 8)) % kGemmM, c = q % (kGemmKC / 8);
-      const int32_t i = m0 + r;
-      uint4 v = {0u, 0u, 0u, 0u};
-      if (i < pc) v = *(const uint4*)(a.a3 + p * a.a_part + (int64_t)i * g.K + kc + c * 8);
-      *(uint4*)&As[p][r][c * 8] = v;
-    }
-    __syncthreads();
+    // the chunk's weight operands first (all k-steps), so that their loads are in flight
+    // together with the activation loads below
     const int32_t kt = kc / kTileK;
     if (kt % ks_unit == 0 && kc % kTileK == 0)
       tbase = nvalid ? packed_tile(a.s, a.wbase, g.st, g.layer, gp, kt) : 0;
     const uint8_t* tp = a.packed + (tbase + kt % ks_unit) * kTileBytes + 8 * sel;
+    uint2 w0[KSTEPS], w1[KSTEPS];
 #pragma unroll
-    for (int ks = 0; ks < kGemmKC / 32; ++ks) {
-      const int kin = kc % kTileK + ks * 32 + kg * 8;  // k inside the 256-k tile
-      const int L = kin >> 2;                           // tile lane holding k .. k+3
-      uint2 w0 = {0u, 0u}, w1 = {0u, 0u};
-      if (nvalid) {
-        w0 = *(const uint2*)(tp + 16 * L);
-        w1 = *(const uint2*)(tp + 16 * (L + 1));
-      }
-      const bf16x8 b = __builtin_bit_cast(bf16x8, uint4{w0.x, w0.y, w1.x, w1.y});
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const int L = (kc % kTileK + ks * 32 + kg * 8) >> 2;  // tile lane holding k .. k+3
+      w0[ks] = nvalid ? *(const uint2*)(tp + 16 * L) : uint2{0u, 0u};
+      w1[ks] = nvalid ? *(const uint2*)(tp + 16 * (L + 1)) : uint2{0u, 0u};
+    }
+    // the activation chunk: every load issued before any is stored to LDS
+    constexpr int APER = 3 * kGemmM * (kGemmKC / 8) / 256;  // 16-byte pieces per thread
+    uint4 av4[APER];
+#pragma unroll
+    for (int j = 0; j < APER; ++j) {
+      const int q = tid + j * 256;
+      const int p = q / (kGemmM * (kGemmKC / 8)), r = (q / (kGemmKC / 8)) % kGemmM, c = q % (kGemmKC / 8);
+      const int32_t i = m0 + r;
+      av4[j] = i < pc ? *(const uint4*)(a.a3 + p * a.a_part + (int64_t)i * g.K + kc + c * 8) : uint4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < APER; ++j) {
+      const int q = tid + j * 256;
+      const int p = q / (kGemmM * (kGemmKC / 8)), r = (q / (kGemmKC / 8)) % kGemmM, c = q % (kGemmKC / 8);
+      *(uint4*)&As[p][r][c * 8] = av4[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const bf16x8 b = __builtin_bit_cast(bf16x8, uint4{w0[ks].x, w0[ks].y, w1[ks].x, w1[ks].y});
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
@@ -138,15 +150,20 @@ __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillArgs a, GemmSt
     __syncthreads();
   }
   if (!nvalid) return;
+  float old[4][4];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int32_t i = m0 + mb * 16 + kg * 4 + r;
-      if (i < pc) {
-        float* o = g.out + (int64_t)i * g.ldo + n;
-        *o = g.accumulate ? *o + acc[mb][r] : acc[mb][r];
-      }
+      old[mb][r] = (g.accumulate && i < pc) ? g.out[(int64_t)i * g.ldo + n] : 0.f;
+    }
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int32_t i = m0 + mb * 16 + kg * 4 + r;
+      if (i < pc) g.out[(int64_t)i * g.ldo + n] = old[mb][r] + acc[mb][r];
     }
 }
 
