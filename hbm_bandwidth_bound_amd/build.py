@@ -18,11 +18,13 @@ HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
 
 
 def source_hash() -> str:
-    """Short hash of the kernel sources: a counter summary is only used for the sources it was
-    taken on."""
+    """Short hash of the sources the decode kernel is built from (every file of csrc except the
+    prompt pass): a counter summary of that kernel is only used for the sources it was taken on."""
     import hashlib
     h = hashlib.sha256()
     for f in sorted(os.listdir(CSRC)):
+        if f.startswith("prefill."):
+            continue
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
