@@ -491,6 +491,7 @@ kie_status kie_prefill(kie_ctx* ctx, const int32_t* tokens_dev, int32_t n_tokens
     a.a_part = (int64_t)kPrefillChunk * prefill_kmax(ctx->s);
     a.c = (float*)(ctx->ws + ctx->wso.pc);
     a.q = (float*)(ctx->ws + ctx->wso.pq);
+    a.attn_part = (float*)(ctx->ws + ctx->wso.pattn);
     HIP_TRY(&ctx->last_error, launch_prefill(a, ctx->pos, n_tokens - 1, ctx->stream));
     ctx->pos += n_tokens - 1;
   }

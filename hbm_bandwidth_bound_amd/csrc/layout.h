@@ -211,6 +211,8 @@ KIE_HD Exch exch_layout(const Shape& s) {
 
 // Prompt pass scratch: positions per chunk, and the widest GEMM input and output rows.
 constexpr int kPrefillChunk = 512;
+constexpr int kPrefillAttnSeg = 2048;  // key positions per attention block of the prompt pass
+KIE_HD int32_t prefill_attn_segs(const Shape& s) { return (s.max_seq + kPrefillAttnSeg - 1) / kPrefillAttnSeg; }
 KIE_HD int32_t prefill_kmax(const Shape& s) {
   int32_t k = s.d;
   if (s.qdim() > k) k = s.qdim();
@@ -227,9 +229,10 @@ KIE_HD int32_t prefill_nmax(const Shape& s) {
 // Workspace (bytes, 256-aligned pieces): exchange words, RoPE table [max_seq][hd/2] of (cos,sin),
 // per-stream base (in tiles, [nwg][8] + total), error word, norm gains [L][2][d] + final [d] (bf16),
 // trace counters, and the prompt-pass scratch (residual [chunk][d] fp32, GEMM input [3][chunk][kmax]
-// bf16, GEMM output [chunk][nmax] fp32, queries [chunk][nq hd] fp32).
+// bf16, GEMM output [chunk][nmax] fp32, queries [chunk][nq hd] fp32, and for long contexts the
+// per-segment attention states [segments][chunk][nq][hd + 2] fp32).
 struct Workspace {
-  int64_t exch, rope, wbase, err, norms, trace, px, pa3, pc, pq, end;
+  int64_t exch, rope, wbase, err, norms, trace, px, pa3, pc, pq, pattn, end;
 };
 constexpr int kTraceWords = 32;  // per wave: cycle counters of a KIE_TRACE build
 KIE_HD int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
@@ -246,6 +249,8 @@ KIE_HD Workspace workspace_layout(const Shape& s) {
   w.pa3 = o; o = align256(o + (int64_t)3 * kPrefillChunk * prefill_kmax(s) * 2);
   w.pc = o; o = align256(o + (int64_t)kPrefillChunk * prefill_nmax(s) * 4);
   w.pq = o; o = align256(o + (int64_t)kPrefillChunk * s.qdim() * 4);
+  w.pattn = o;
+  if (prefill_attn_segs(s) > 1) o = align256(o + (int64_t)prefill_attn_segs(s) * kPrefillChunk * s.nq * (s.hd + 2) * 4);
   w.end = o;
   return w;
 }

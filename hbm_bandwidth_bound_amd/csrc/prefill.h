@@ -24,6 +24,7 @@ struct PrefillArgs {
   int64_t a_part;            // elements between the parts
   float* c;                  // [chunk][nmax] GEMM output
   float* q;                  // [chunk][nq * hd] rotated queries
+  float* attn_part;          // [segments][chunk][nq][hd + 2] partial attention states
 };
 
 struct GemmStage {

@@ -202,13 +202,15 @@ __global__ void __launch_bounds__(256) prefill_rope_kv_kernel(PrefillArgs a, int
 
 // ------------------------------------------------------------------------------------------
 // Causal attention of the chunk's queries over positions 0 .. pos (cache rows, this chunk's rows
-// included). Block: one query head x 64 queries, 4 lanes per query (HD/4 dimensions each); keys
-// in tiles of 32 positions staged in LDS as fp32; online softmax in the exp2 domain per tile.
-// The output is written as the three-part input of the O projection.
+// included). Block: one query head x 64 queries x one segment of kAttnSeg key positions; 4 lanes
+// per query (HD/4 dimensions each); keys in tiles of 32 positions staged in LDS as fp32; online
+// softmax in the exp2 domain per tile. With one segment the output is written as the three-part
+// input of the O projection; with several, each block writes its partial state (m, l, acc) and
+// prefill_attn_merge_kernel combines the segments.
 // ------------------------------------------------------------------------------------------
 constexpr int kAttnQ = 64, kAttnKT = 32;
 
-template <int HD>
+template <int HD, bool SPLIT>
 __global__ void __launch_bounds__(256) prefill_attn_kernel(PrefillArgs a, int32_t layer, int32_t p0, int32_t pc) {
   constexpr int DQ = HD / 4;
   __shared__ __align__(16) float Ks[kAttnKT][HD];
@@ -229,15 +231,17 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(PrefillArgs a, int32_
   float m = -INFINITY, l = 0.f;
   const int32_t ilast = min(pc, (int32_t)(blockIdx.y + 1) * kAttnQ) - 1;
   const int32_t kend = p0 + ilast;  // last key any query of the block needs
+  const int32_t kbeg = SPLIT ? (int32_t)blockIdx.z * kPrefillAttnSeg : 0;
+  const int32_t klast = SPLIT ? min(kend, kbeg + kPrefillAttnSeg - 1) : kend;
   const uint16_t* kbase = a.kv + kv_offset(s, layer, 0, j, 0);
   const uint16_t* vbase = a.kv + kv_offset(s, layer, 1, j, 0);
-  for (int32_t k0 = 0; k0 <= kend; k0 += kAttnKT) {
+  for (int32_t k0 = kbeg; k0 <= klast; k0 += kAttnKT) {
     __syncthreads();
     for (int q2 = tid; q2 < kAttnKT * HD / 2; q2 += 256) {
       const int r = q2 / (HD / 2), c = (q2 % (HD / 2)) * 2;
       const int32_t kp = k0 + r;
       uint32_t kk = 0u, vv = 0u;
-      if (kp <= kend) {
+      if (kp <= klast) {
         kk = *(const uint32_t*)(kbase + (int64_t)kp * HD + c);
         vv = *(const uint32_t*)(vbase + (int64_t)kp * HD + c);
       }
@@ -256,7 +260,7 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(PrefillArgs a, int32_
       for (int e = 0; e < DQ; ++e) d = fmaf(q[e], Ks[r][part * DQ + e], d);
       d += __shfl_xor(d, 1, 64);
       d += __shfl_xor(d, 2, 64);
-      sc[r] = (k0 + r <= pos) ? d : -INFINITY;
+      sc[r] = (k0 + r <= pos && k0 + r <= klast) ? d : -INFINITY;
       mt = fmaxf(mt, sc[r]);
     }
     const float mn = fmaxf(m, mt);
@@ -274,12 +278,44 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(PrefillArgs a, int32_
     m = mn;
   }
   if (!valid) return;
-  const float inv = 1.0f / l;
+  if (SPLIT) {  // partial state of this segment: [segment][query][head][acc[HD], m, l]
+    float* st = a.attn_part + (((int64_t)blockIdx.z * kPrefillChunk + i) * s.nq + h) * (HD + 2);
 #pragma unroll
-  for (int e = 0; e < DQ; ++e) {
-    const int64_t o = (int64_t)i * s.qdim() + h * HD + part * DQ + e;
-    split3(acc[e] * inv, a.a3 + o, a.a3 + a.a_part + o, a.a3 + 2 * a.a_part + o);
+    for (int e = 0; e < DQ; ++e) st[part * DQ + e] = acc[e];
+    if (part == 0) {
+      st[HD] = m;
+      st[HD + 1] = l;
+    }
+  } else {
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int e = 0; e < DQ; ++e) {
+      const int64_t o = (int64_t)i * s.qdim() + h * HD + part * DQ + e;
+      split3(acc[e] * inv, a.a3 + o, a.a3 + a.a_part + o, a.a3 + 2 * a.a_part + o);
+    }
   }
+}
+
+// Combination of the segments' partial states (in segment order) for one query and head: thread
+// e owns output dimension e.
+template <int HD>
+__global__ void __launch_bounds__(HD) prefill_attn_merge_kernel(PrefillArgs a, int32_t nseg, int32_t pc) {
+  const Shape& s = a.s;
+  const int32_t i = blockIdx.x, h = blockIdx.y, e = threadIdx.x;
+  if (i >= pc) return;
+  float M = -INFINITY, S = 0.f, A = 0.f;
+  for (int32_t g = 0; g < nseg; ++g) {
+    const float* st = a.attn_part + (((int64_t)g * kPrefillChunk + i) * s.nq + h) * (HD + 2);
+    const float m2 = st[HD];
+    if (m2 == -INFINITY) continue;
+    const float Mn = fmaxf(M, m2);
+    const float fo = M == -INFINITY ? 0.f : exp2f(M - Mn), fn = exp2f(m2 - Mn);
+    S = S * fo + st[HD + 1] * fn;
+    A = A * fo + st[e] * fn;
+    M = Mn;
+  }
+  const int64_t o = (int64_t)i * s.qdim() + h * HD + e;
+  split3(A / S, a.a3 + o, a.a3 + a.a_part + o, a.a3 + 2 * a.a_part + o);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -327,12 +363,22 @@ hipError_t launch_prefill(const PrefillArgs& a, int32_t p0, int32_t n, hipStream
       hipError_t e = gemm(a, ST_QKV, l, s.d, a.c, 2 * s.stage_pairs(ST_QKV), 0, pc, stream);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(prefill_rope_kv_kernel, dim3(pc), dim3(256), 0, stream, a, l, pos, pc);
-      if (s.hd == 128)
-        hipLaunchKernelGGL(prefill_attn_kernel<128>, dim3(s.nq, (pc + kAttnQ - 1) / kAttnQ), dim3(256), 0, stream, a, l,
-                           pos, pc);
-      else
-        hipLaunchKernelGGL(prefill_attn_kernel<64>, dim3(s.nq, (pc + kAttnQ - 1) / kAttnQ), dim3(256), 0, stream, a, l,
-                           pos, pc);
+      // keys split into segments when the context is long, so that enough blocks run at once
+      const int32_t nseg = (pos + pc + kPrefillAttnSeg - 1) / kPrefillAttnSeg;
+      const dim3 ag(s.nq, (pc + kAttnQ - 1) / kAttnQ, nseg);
+      if (nseg > 1) {
+        if (s.hd == 128) {
+          hipLaunchKernelGGL((prefill_attn_kernel<128, true>), ag, dim3(256), 0, stream, a, l, pos, pc);
+          hipLaunchKernelGGL(prefill_attn_merge_kernel<128>, dim3(pc, s.nq), dim3(128), 0, stream, a, nseg, pc);
+        } else {
+          hipLaunchKernelGGL((prefill_attn_kernel<64, true>), ag, dim3(256), 0, stream, a, l, pos, pc);
+          hipLaunchKernelGGL(prefill_attn_merge_kernel<64>, dim3(pc, s.nq), dim3(64), 0, stream, a, nseg, pc);
+        }
+      } else if (s.hd == 128) {
+        hipLaunchKernelGGL((prefill_attn_kernel<128, false>), ag, dim3(256), 0, stream, a, l, pos, pc);
+      } else {
+        hipLaunchKernelGGL((prefill_attn_kernel<64, false>), ag, dim3(256), 0, stream, a, l, pos, pc);
+      }
       if ((e = gemm(a, ST_O, l, s.qdim(), a.x, s.d, 1, pc, stream)) != hipSuccess) return e;
       hipLaunchKernelGGL(prefill_norm_split_kernel, dim3(pc), dim3(256), 0, stream, a,
                          a.norms + (int64_t)l * 2 * s.d + s.d, pc);

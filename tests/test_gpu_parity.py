@@ -329,3 +329,30 @@ def test_other_head_groupings(torch_cuda, oracle_lib, cfg):
     worst, checked = check_steps(logits, ref, toks, label=cfg.name)
     say(f"  worst rel-L2 {worst:.3e}, greedy checked {checked}/{N}")
     eng.close()
+
+
+def test_tiny_long_prompt_split_attention(torch_cuda, tiny, oracle_lib):
+    """A prompt longer than one key segment of the prompt pass's attention (2048 positions): the
+    later chunks combine per-segment partial softmax states."""
+    import torch
+    from hbm_bandwidth_bound_amd.kie import Engine
+    cfg, w, wd = tiny
+    P, N = 2600, 4
+    say(f"[tiny] prefill {P} (segmented attention) + decode {N}")
+    eng = Engine(cfg, wd, P + N)
+    prompt = synth.prompt_ids(P, cfg.vocab_size, 33)
+    first, last, toks, logits = run_gpu(torch_cuda, eng, prompt, N, cfg.vocab_size)
+    om = oracle_lib.OracleModel(cfg, w, P + N)
+    ref_prompt = om.run(prompt)
+    e = rel_l2(last, ref_prompt[-1])
+    say(f"  last-logits rel-L2 {e:.3e}")
+    assert e <= 1e-3
+    kg = eng.kv_view().cpu().numpy().view(np.uint16)
+    ko, vo = om.kv_view()
+    ek = rel_l2(synth.bf16_bits_to_f32(kg[:, 0, :, :P]), synth.bf16_bits_to_f32(ko[:, :, :P]))
+    ev = rel_l2(synth.bf16_bits_to_f32(kg[:, 1, :, :P]), synth.bf16_bits_to_f32(vo[:, :, :P]))
+    say(f"  cache rel-L2 K {ek:.3e} V {ev:.3e}")
+    assert ek <= 1e-3 and ev <= 1e-3
+    ref = om.run([first] + [int(t) for t in toks[:-1]], start_pos=P)
+    check_steps(logits, ref, toks, label="long prompt")
+    eng.close()
