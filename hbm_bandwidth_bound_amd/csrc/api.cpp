@@ -36,6 +36,9 @@ struct kie_ctx {
   int32_t pos;
   uint32_t epoch;  // tag of the next step
   bool bad_state;
+  int32_t* tok_ring;       // device view of the caller's host ring, or null
+  int32_t ring_cap;
+  int64_t ring_count;      // tokens streamed to it so far
   int64_t timeout_ticks;
   std::vector<int64_t> wbase_host;
   std::string last_error;
@@ -275,6 +278,9 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
   c->pos = 0;
   c->epoch = 1;
   c->bad_state = false;
+  c->tok_ring = nullptr;
+  c->ring_cap = 0;
+  c->ring_count = 0;
   c->timeout_ticks = 200000000;  // 2 s per wait
   c->wbase_host.resize((size_t)s.nwg * kWaves + 1);
   int64_t acc = 0;
@@ -352,6 +358,32 @@ kie_status kie_reset(kie_ctx* ctx) {
   ctx->pos = 0;
   ctx->bad_state = false;
   ctx->last_error.clear();
+  return KIE_OK;
+}
+
+kie_status kie_set_token_stream(kie_ctx* ctx, int32_t* ring_host, int32_t capacity) {
+  if (!ctx) return KIE_ERR_INVALID_ARG;
+  if (!ring_host) {
+    ctx->tok_ring = nullptr;
+    ctx->ring_cap = 0;
+    ctx->ring_count = 0;
+    return KIE_OK;
+  }
+  if (capacity <= 0) {
+    set_err(&ctx->last_error, "token ring capacity must be positive");
+    return KIE_ERR_INVALID_ARG;
+  }
+  void* dev = nullptr;
+  const hipError_t e = hipHostGetDevicePointer(&dev, ring_host, 0);
+  if (e != hipSuccess || !dev) {
+    (void)hipGetLastError();
+    set_err(&ctx->last_error, "the token ring is not pinned host memory the GPU can write");
+    return KIE_ERR_INVALID_ARG;
+  }
+  ring_host[0] = 0;
+  ctx->tok_ring = (int32_t*)dev;
+  ctx->ring_cap = capacity;
+  ctx->ring_count = 0;
   return KIE_OK;
 }
 
@@ -442,6 +474,9 @@ static kie_status launch(kie_ctx* ctx, const int32_t* first, int32_t n, const in
   P.n_steps = n;
   P.epoch0 = ctx->epoch;
   P.lm_last_only = lm_last_only;
+  P.tok_ring = lm_last_only ? nullptr : ctx->tok_ring;
+  P.ring_cap = ctx->ring_cap;
+  P.ring_base = ctx->ring_count;
   P.top_k = top_k;
   P.temperature = top_k > 1 ? smp->temperature : 1.0f;
   P.seed = smp ? smp->seed : 0;
@@ -451,6 +486,7 @@ static kie_status launch(kie_ctx* ctx, const int32_t* first, int32_t n, const in
   HIP_TRY(&ctx->last_error,
           hipLaunchCooperativeKernel(fn, dim3(ctx->s.nwg), dim3(kThreads), args, (unsigned)ctx->lds, ctx->stream));
   ctx->pos += n;
+  if (P.tok_ring) ctx->ring_count += n;
   ctx->epoch += (uint32_t)n;
   if (ctx->epoch == 0) ctx->epoch = 1;
   return KIE_OK;

@@ -30,6 +30,9 @@ struct KParams {
   const int32_t* forced;     // [n_steps-1] or null
   int32_t* tokens_out;       // [n_steps] or null
   int32_t* last_tok_out;     // [1] or null
+  int32_t* tok_ring;         // host ring [1 + ring_cap] (count, then tokens) or null
+  int32_t ring_cap;
+  int64_t ring_base;         // tokens streamed to the ring before this launch
   float* logits_out;         // [n_steps][V], or [V] when lm_last_only, or null
   int32_t pos0, n_steps;
   uint32_t epoch0;           // exchange tag of step s is epoch0 + s (never 0)

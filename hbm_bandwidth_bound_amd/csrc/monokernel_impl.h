@@ -1216,6 +1216,12 @@ __device__ __forceinline__ void decode(Wk& K) {
           if (lm && K.w == 0 && tid == 0) {
             if (P.tokens_out) P.tokens_out[step] = next;
             if (P.last_tok_out && step == P.n_steps - 1) P.last_tok_out[0] = next;
+            if (P.tok_ring) {  // the host sees each token while the launch goes on
+              const int64_t c = P.ring_base + step;
+              __hip_atomic_store(P.tok_ring + 1 + (int32_t)(c % P.ring_cap), next, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_SYSTEM);
+              __hip_atomic_store(P.tok_ring, (int32_t)(c + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+            }
           }
           if (P.forced && step + 1 < P.n_steps) {
             int32_t f = P.forced[step];

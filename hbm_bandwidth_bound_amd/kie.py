@@ -79,6 +79,8 @@ def load() -> C.CDLL:
     lib.kie_sync.restype = C.c_int32
     lib.kie_reset.argtypes = [vp]
     lib.kie_reset.restype = C.c_int32
+    lib.kie_set_token_stream.argtypes = [vp, vp, C.c_int32]
+    lib.kie_set_token_stream.restype = C.c_int32
     lib.kie_set_position.argtypes = [vp, C.c_int32]
     lib.kie_set_position.restype = C.c_int32
     lib.kie_position.argtypes = [vp]
@@ -183,6 +185,15 @@ class Engine:
 
     def set_position(self, pos: int):
         _check(self.lib, self.lib.kie_set_position(self.ctx, int(pos)), self.ctx)
+
+    def set_token_stream(self, ring=None):
+        """ring: pinned host int32 tensor of 1 + capacity elements (None stops streaming)."""
+        if ring is None:
+            st = self.lib.kie_set_token_stream(self.ctx, None, 0)
+        else:
+            st = self.lib.kie_set_token_stream(self.ctx, _ptr(ring), int(ring.numel()) - 1)
+        _check(self.lib, st, self.ctx)
+        self._ring = ring  # kept alive while streaming
 
     @property
     def position(self) -> int:

@@ -142,6 +142,18 @@ kie_status kie_reset(kie_ctx* ctx);
  * otherwise. */
 kie_status kie_set_position(kie_ctx* ctx, int32_t pos);
 
+/* Stream the chosen tokens to the host while a launch runs (agentlenshq.com, 《突破内存墙…》,
+ * "The Monokernel Runtime", and aikraft.ru «3000 токенов в секунду…», §04: the whole sequence is
+ * decoded on the GPU; an agent loop still wants each token as it is produced). ring_host is
+ * caller-owned pinned host memory (hipHostMalloc, or a pinned torch tensor) of 1 + capacity int32:
+ * ring_host[0] counts the tokens written since this call, and token c sits at ring_host[1 + c %
+ * capacity]. Each decode step stores its token and then, with release ordering, the new count
+ * (system scope), so a host that reads the count and then the tokens below it sees their values
+ * (tokens older than capacity are overwritten). Prompt passes do not write to the ring.
+ * ring_host == NULL stops streaming. Errors: KIE_ERR_INVALID_ARG (capacity <= 0, or memory the
+ * device cannot write). */
+kie_status kie_set_token_stream(kie_ctx* ctx, int32_t* ring_host, int32_t capacity);
+
 /* Current position (number of tokens whose K/V rows are in the cache), or -1 for NULL. */
 int32_t kie_position(const kie_ctx* ctx);
 

@@ -356,3 +356,50 @@ def test_tiny_long_prompt_split_attention(torch_cuda, tiny, oracle_lib):
     ref = om.run([first] + [int(t) for t in toks[:-1]], start_pos=P)
     check_steps(logits, ref, toks, label="long prompt")
     eng.close()
+
+
+def test_tokens_stream_to_the_host_during_a_launch(torch_cuda, tiny):
+    """kie_set_token_stream: each chosen token reaches pinned host memory while the single
+    kie_generate launch is still running (a host thread sees the count grow before the sync)."""
+    import threading
+    import time as _time
+
+    import torch
+    from hbm_bandwidth_bound_amd.kie import Engine, KieError
+    cfg, w, wd = tiny
+    P, N, cap = 8, 1500, 64
+    say(f"[tiny] token stream: {N} steps, ring of {cap}")
+    eng = Engine(cfg, wd, P + N)
+    with pytest.raises(KieError):
+        eng.set_token_stream(torch.zeros(1, dtype=torch.int32, pin_memory=True))  # capacity 0
+    ring = torch.zeros(1 + cap, dtype=torch.int32, pin_memory=True)
+    eng.set_token_stream(ring)
+    first = eng.prefill(torch.tensor(synth.prompt_ids(P, cfg.vocab_size, 2), dtype=torch.int32, device="cuda"))
+    eng.sync()
+    assert int(ring[0]) == 0  # the prompt pass does not stream
+    out = torch.empty(N, dtype=torch.int32, device="cuda")
+    seen = []
+    stop = threading.Event()
+
+    def watch():
+        while not stop.is_set():
+            seen.append(int(ring[0]))
+            _time.sleep(0.0002)
+
+    th = threading.Thread(target=watch)
+    th.start()
+    eng.generate(first, N, out)
+    eng.sync()
+    stop.set()
+    th.join()
+    toks = out.cpu().numpy()
+    assert int(ring[0]) == N
+    got = ring[1:].numpy()
+    for c in range(N - cap, N):
+        assert got[c % cap] == toks[c]
+    inter = [c for c in seen if 0 < c < N]
+    say(f"  host saw {len(set(inter))} intermediate counts (of {len(seen)} reads)")
+    assert inter, "no token reached the host before the launch ended"
+    assert all(b >= a for a, b in zip(seen, seen[1:]))
+    eng.set_token_stream(None)
+    eng.close()
