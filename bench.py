@@ -103,7 +103,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this decode path has no multi-GPU "
-              "mode; see the sharding notes in DESIGN.md", file=sys.stderr)
+              "mode", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

@@ -55,8 +55,7 @@ def load() -> C.CDLL:
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m hbm_bandwidth_bound_amd.build` "
-                           "or __graft_entry__.build()")
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m hbm_bandwidth_bound_amd.build`")
     lib = C.CDLL(LIB_PATH)
     vp = C.c_void_p
     i32p = C.POINTER(C.c_int32)

@@ -15,12 +15,12 @@ Two steps:
 
 Example (on a machine with the GPU; each pass its own run):
 
-    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- \\
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d prof/pmc_fetch -o run -- \\
         python3 -m hbm_bandwidth_bound_amd.traffic_profile run --workload 1.6b-1k --steps 64
-    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- \\
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d prof/pmc_write -o run -- \\
         python3 -m hbm_bandwidth_bound_amd.traffic_profile run --workload 1.6b-1k --steps 64
     python3 -m hbm_bandwidth_bound_amd.traffic_profile summarize --workload 1.6b-1k --steps 64 \\
-        --fetch gpurun_out/pmc_fetch --write gpurun_out/pmc_write --out profiles/traffic_decode_1.6b-1k.txt
+        --fetch prof/pmc_fetch --write prof/pmc_write --out profiles/traffic_decode_1.6b-1k.txt
 """
 import argparse
 import collections
