@@ -202,96 +202,208 @@ __global__ void __launch_bounds__(256) prefill_rope_kv_kernel(PrefillArgs a, int
 
 // ------------------------------------------------------------------------------------------
 // Causal attention of the chunk's queries over positions 0 .. pos (cache rows, this chunk's rows
-// included). Block: one query head x 64 queries x one segment of kAttnSeg key positions; 4 lanes
-// per query (HD/4 dimensions each); keys in tiles of 32 positions staged in LDS as fp32; online
-// softmax in the exp2 domain per tile. With one segment the output is written as the three-part
-// input of the O projection; with several, each block writes its partial state (m, l, acc) and
-// prefill_attn_merge_kernel combines the segments.
+// included), on the matrix cores. Block: 64 (query, head) rows of one KV head --
+// row r is query r / G and head j G + r % G, so the G heads of a group share every K/V tile -- in
+// 4 waves of 16 rows; keys in tiles of 64 staged in LDS (K as stored, V transposed). Per tile a
+// wave computes S^T = K Q^T on the MFMA (A = 16 keys x 32 dims of K, B = Q^T of its rows), takes
+// the online softmax of each row in the exp2 domain, and adds P V on the MFMA (A = P of its 16
+// rows x 32 keys, B = 32 keys x 16 dims of V). The 32 keys of a P operand are taken in the order
+// the S^T result leaves them in the lanes, and V is read in that same order. Q and P enter as two
+// bf16 parts (hi + lo, about 16 significant bits); K and V are bf16 already, so every product is
+// exact and the sums are fp32. With one key segment (blockIdx.z) the output is written as the
+// three-part input of the O projection; with several, each block writes its partial state
+// (acc, m, l) and prefill_attn_merge_kernel combines the segments.
 // ------------------------------------------------------------------------------------------
-constexpr int kAttnQ = 64, kAttnKT = 32;
+constexpr int kFaRows = 64, kFaKT = 64;
+
+__device__ __forceinline__ void split2x8(const float* x, bf16x8* hi, bf16x8* lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t h0 = f32_to_bf16(x[2 * e]), h1 = f32_to_bf16(x[2 * e + 1]);
+    const uint32_t l0 = f32_to_bf16(x[2 * e] - bf16_to_f32(h0)), l1 = f32_to_bf16(x[2 * e + 1] - bf16_to_f32(h1));
+    h[e] = h0 | (h1 << 16);
+    l[e] = l0 | (l1 << 16);
+  }
+  *hi = __builtin_bit_cast(bf16x8, uint4{h[0], h[1], h[2], h[3]});
+  *lo = __builtin_bit_cast(bf16x8, uint4{l[0], l[1], l[2], l[3]});
+}
 
 template <int HD, bool SPLIT>
-__global__ void __launch_bounds__(256) prefill_attn_kernel(PrefillArgs a, int32_t layer, int32_t p0, int32_t pc) {
-  constexpr int DQ = HD / 4;
-  __shared__ __align__(16) float Ks[kAttnKT][HD];
-  __shared__ __align__(16) float Vs[kAttnKT][HD];
+__global__ void __launch_bounds__(256) prefill_fattn_kernel(PrefillArgs a, int32_t layer, int32_t p0, int32_t pc) {
+  constexpr int KP = HD + 8;     // padded K row (bf16): the 16 rows a lane group reads hit distinct banks
+  constexpr int VP = kFaKT + 8;  // padded V^T row (bf16)
+  constexpr int NKP = kFaKT * HD / 8 / 256;          // K pieces (16 bytes) per thread and tile
+  constexpr int NVP = (kFaKT / 2) * (HD / 8) / 256;  // V pieces (two keys x 8 dims) per thread
+  __shared__ __align__(16) uint16_t Ks[kFaKT][KP];
+  __shared__ __align__(16) uint16_t Vt[HD][VP];
   const Shape& s = a.s;
-  const int32_t h = blockIdx.x, j = h / s.group();
-  const int tid = threadIdx.x, tq = tid >> 2, part = tid & 3;
-  const int32_t i = blockIdx.y * kAttnQ + tq;
-  const bool valid = i < pc;
-  const int32_t pos = p0 + (valid ? i : pc - 1);
-  const float scale = 1.4426950408889634f / sqrtf((float)HD);  // log2(e) / sqrt(hd)
-  float q[DQ], acc[DQ];
-#pragma unroll
-  for (int e = 0; e < DQ; ++e) {
-    q[e] = a.q[(int64_t)(valid ? i : 0) * s.qdim() + h * HD + part * DQ + e] * scale;
-    acc[e] = 0.f;
-  }
-  float m = -INFINITY, l = 0.f;
-  const int32_t ilast = min(pc, (int32_t)(blockIdx.y + 1) * kAttnQ) - 1;
-  const int32_t kend = p0 + ilast;  // last key any query of the block needs
+  const int32_t G = s.group(), j = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int rl = lane & 15, lg = lane >> 4;
+  // the row of this lane in the S^T and P layouts (column rl of the wave's 16)
+  const int32_t r = (int32_t)blockIdx.x * kFaRows + wv * 16 + rl;
+  const bool valid = r < pc * G;
+  const int32_t qi = valid ? r / G : pc - 1, h = j * G + r % G;
+  const int32_t qpos = p0 + qi;
+  const int32_t rlast = min((int32_t)(blockIdx.x + 1) * kFaRows, pc * G) - 1;
+  const int32_t kend = p0 + rlast / G;  // last key any row of the block needs
   const int32_t kbeg = SPLIT ? (int32_t)blockIdx.z * kPrefillAttnSeg : 0;
   const int32_t klast = SPLIT ? min(kend, kbeg + kPrefillAttnSeg - 1) : kend;
   const uint16_t* kbase = a.kv + kv_offset(s, layer, 0, j, 0);
   const uint16_t* vbase = a.kv + kv_offset(s, layer, 1, j, 0);
-  for (int32_t k0 = kbeg; k0 <= klast; k0 += kAttnKT) {
-    __syncthreads();
-    for (int q2 = tid; q2 < kAttnKT * HD / 2; q2 += 256) {
-      const int r = q2 / (HD / 2), c = (q2 % (HD / 2)) * 2;
-      const int32_t kp = k0 + r;
-      uint32_t kk = 0u, vv = 0u;
-      if (kp <= klast) {
-        kk = *(const uint32_t*)(kbase + (int64_t)kp * HD + c);
-        vv = *(const uint32_t*)(vbase + (int64_t)kp * HD + c);
-      }
-      Ks[r][c] = bf16lo(kk);
-      Ks[r][c + 1] = bf16hi(kk);
-      Vs[r][c] = bf16lo(vv);
-      Vs[r][c + 1] = bf16hi(vv);
+
+  // Q^T operand of this lane: row rl, dims 32c + 8lg .. +7, scaled into the exp2 domain
+  const float scale = 1.4426950408889634f / sqrtf((float)HD);
+  bf16x8 qh[HD / 32], ql[HD / 32];
+  {
+    const float* qrow = a.q + (int64_t)qi * s.qdim() + h * HD;
+#pragma unroll
+    for (int c = 0; c < HD / 32; ++c) {
+      const float4 x0 = *(const float4*)(qrow + 32 * c + 8 * lg);
+      const float4 x1 = *(const float4*)(qrow + 32 * c + 8 * lg + 4);
+      const float x[8] = {x0.x * scale, x0.y * scale, x0.z * scale, x0.w * scale,
+                          x1.x * scale, x1.y * scale, x1.z * scale, x1.w * scale};
+      split2x8(x, &qh[c], &ql[c]);
     }
+  }
+  f4 o[HD / 16];
+#pragma unroll
+  for (int c = 0; c < HD / 16; ++c) o[c] = f4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;  // softmax state of row rl (the same in the 4 lane groups)
+
+  uint4 kr[NKP], vr[NVP][2];
+  auto fetch = [&](int32_t k0) {  // the tile's K/V pieces of this thread; rows past klast read as 0
+#pragma unroll
+    for (int e = 0; e < NKP; ++e) {
+      const int q = tid + 256 * e, row = q / (HD / 8), c8 = q % (HD / 8);
+      const int32_t kp = k0 + row;
+      kr[e] = kp <= klast ? *(const uint4*)(kbase + (int64_t)kp * HD + 8 * c8) : uint4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int e = 0; e < NVP; ++e) {
+      const int q = tid + 256 * e, row = 2 * (q % (kFaKT / 2)), c8 = q / (kFaKT / 2);
+      const int32_t kp = k0 + row;
+      vr[e][0] = kp <= klast ? *(const uint4*)(vbase + (int64_t)kp * HD + 8 * c8) : uint4{0u, 0u, 0u, 0u};
+      vr[e][1] = kp + 1 <= klast ? *(const uint4*)(vbase + (int64_t)(kp + 1) * HD + 8 * c8) : uint4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto stage = [&]() {  // K rows as they are; V as V^T, two keys per 32-bit word
+#pragma unroll
+    for (int e = 0; e < NKP; ++e) {
+      const int q = tid + 256 * e, row = q / (HD / 8), c8 = q % (HD / 8);
+      *(uint4*)&Ks[row][8 * c8] = kr[e];
+    }
+#pragma unroll
+    for (int e = 0; e < NVP; ++e) {
+      const int q = tid + 256 * e, row = 2 * (q % (kFaKT / 2)), c8 = q / (kFaKT / 2);
+      const uint32_t a0[4] = {vr[e][0].x, vr[e][0].y, vr[e][0].z, vr[e][0].w};
+      const uint32_t a1[4] = {vr[e][1].x, vr[e][1].y, vr[e][1].z, vr[e][1].w};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        *(uint32_t*)&Vt[8 * c8 + 2 * w][row] = (a0[w] & 0xffffu) | (a1[w] << 16);
+        *(uint32_t*)&Vt[8 * c8 + 2 * w + 1][row] = (a0[w] >> 16) | (a1[w] & 0xffff0000u);
+      }
+    }
+  };
+
+  if (kbeg <= klast) fetch(kbeg);
+  for (int32_t k0 = kbeg; k0 <= klast; k0 += kFaKT) {
+    __syncthreads();  // every wave is done with the previous tile
+    stage();
     __syncthreads();
-    float sc[kAttnKT];
+    if (k0 + kFaKT <= klast) fetch(k0 + kFaKT);  // in flight while this tile is computed
+    // S^T: st[ks][i] = score of key k0 + 16 ks + 4 lg + i for row rl
+    f4 st[kFaKT / 16];
+#pragma unroll
+    for (int ks = 0; ks < kFaKT / 16; ++ks) {
+      st[ks] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < HD / 32; ++c) {
+        const bf16x8 kv = *(const bf16x8*)&Ks[16 * ks + rl][32 * c + 8 * lg];
+        st[ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qh[c], st[ks], 0, 0, 0);
+        st[ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, ql[c], st[ks], 0, 0, 0);
+      }
+    }
     float mt = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < kAttnKT; ++r) {
-      float d = 0.f;
+    for (int ks = 0; ks < kFaKT / 16; ++ks)
 #pragma unroll
-      for (int e = 0; e < DQ; ++e) d = fmaf(q[e], Ks[r][part * DQ + e], d);
-      d += __shfl_xor(d, 1, 64);
-      d += __shfl_xor(d, 2, 64);
-      sc[r] = (k0 + r <= pos && k0 + r <= klast) ? d : -INFINITY;
-      mt = fmaxf(mt, sc[r]);
-    }
+      for (int i = 0; i < 4; ++i) {
+        const int32_t kp = k0 + 16 * ks + 4 * lg + i;
+        if (kp > qpos || kp > klast) st[ks][i] = -INFINITY;
+        mt = fmaxf(mt, st[ks][i]);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
     const float mn = fmaxf(m, mt);
-    const float corr = m == -INFINITY ? 0.f : exp2f(m - mn);
-    l *= corr;
+    const float mu = mn == -INFINITY ? 0.f : mn;  // a row with no key yet keeps p = 0
+    const float corr = exp2f(m - mu);
+    float ps = 0.f;
 #pragma unroll
-    for (int e = 0; e < DQ; ++e) acc[e] *= corr;
+    for (int ks = 0; ks < kFaKT / 16; ++ks)
 #pragma unroll
-    for (int r = 0; r < kAttnKT; ++r) {
-      const float pr = sc[r] == -INFINITY ? 0.f : exp2f(sc[r] - mn);
-      l += pr;
-#pragma unroll
-      for (int e = 0; e < DQ; ++e) acc[e] = fmaf(pr, Vs[r][part * DQ + e], acc[e]);
-    }
+      for (int i = 0; i < 4; ++i) {
+        st[ks][i] = exp2f(st[ks][i] - mu);
+        ps += st[ks][i];
+      }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    l = l * corr + ps;
     m = mn;
-  }
-  if (!valid) return;
-  if (SPLIT) {  // partial state of this segment: [segment][query][head][acc[HD], m, l]
-    float* st = a.attn_part + (((int64_t)blockIdx.z * kPrefillChunk + i) * s.nq + h) * (HD + 2);
+    // O rows are 4 lg + i: their factors come from the lanes that hold those rows' state
+    float cr[4];
 #pragma unroll
-    for (int e = 0; e < DQ; ++e) st[part * DQ + e] = acc[e];
-    if (part == 0) {
-      st[HD] = m;
-      st[HD + 1] = l;
+    for (int i = 0; i < 4; ++i) cr[i] = __shfl(corr, 4 * lg + i, 64);
+#pragma unroll
+    for (int c = 0; c < HD / 16; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[c][i] *= cr[i];
+    // O += P V over the tile's 32-key halves; operand slot 8 lg + e is key 32 kc + 4 lg + e
+    // (e < 4) or 32 kc + 16 + 4 lg + (e - 4)
+#pragma unroll
+    for (int kc = 0; kc < kFaKT / 32; ++kc) {
+      const float pv[8] = {st[2 * kc][0], st[2 * kc][1], st[2 * kc][2], st[2 * kc][3],
+                           st[2 * kc + 1][0], st[2 * kc + 1][1], st[2 * kc + 1][2], st[2 * kc + 1][3]};
+      bf16x8 ph, pl;
+      split2x8(pv, &ph, &pl);
+#pragma unroll
+      for (int c = 0; c < HD / 16; ++c) {
+        const uint2 b0 = *(const uint2*)&Vt[16 * c + rl][32 * kc + 4 * lg];
+        const uint2 b1 = *(const uint2*)&Vt[16 * c + rl][32 * kc + 16 + 4 * lg];
+        const bf16x8 vb = __builtin_bit_cast(bf16x8, uint4{b0.x, b0.y, b1.x, b1.y});
+        o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vb, o[c], 0, 0, 0);
+        o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, o[c], 0, 0, 0);
+      }
     }
-  } else {
-    const float inv = 1.0f / l;
+  }
+  // rows 4 lg + i of O: their softmax state, then the output
+  float lr[4], mr[4];
 #pragma unroll
-    for (int e = 0; e < DQ; ++e) {
-      const int64_t o = (int64_t)i * s.qdim() + h * HD + part * DQ + e;
-      split3(acc[e] * inv, a.a3 + o, a.a3 + a.a_part + o, a.a3 + 2 * a.a_part + o);
+  for (int i = 0; i < 4; ++i) {
+    lr[i] = __shfl(l, 4 * lg + i, 64);
+    mr[i] = __shfl(m, 4 * lg + i, 64);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int32_t r2 = (int32_t)blockIdx.x * kFaRows + wv * 16 + 4 * lg + i;
+    if (r2 >= pc * G) continue;
+    const int32_t q2 = r2 / G, h2 = j * G + r2 % G;
+    if (SPLIT) {  // partial state of this segment: [segment][query][head][acc[HD], m, l]
+      float* st = a.attn_part + (((int64_t)blockIdx.z * kPrefillChunk + q2) * s.nq + h2) * (HD + 2);
+#pragma unroll
+      for (int c = 0; c < HD / 16; ++c) st[16 * c + rl] = o[c][i];
+      if (rl == 0) {
+        st[HD] = mr[i];
+        st[HD + 1] = lr[i];
+      }
+    } else {
+      const float inv = 1.0f / lr[i];
+#pragma unroll
+      for (int c = 0; c < HD / 16; ++c) {
+        const int64_t off = (int64_t)q2 * s.qdim() + h2 * HD + 16 * c + rl;
+        split3(o[c][i] * inv, a.a3 + off, a.a3 + a.a_part + off, a.a3 + 2 * a.a_part + off);
+      }
     }
   }
 }
@@ -365,19 +477,19 @@ hipError_t launch_prefill(const PrefillArgs& a, int32_t p0, int32_t n, hipStream
       hipLaunchKernelGGL(prefill_rope_kv_kernel, dim3(pc), dim3(256), 0, stream, a, l, pos, pc);
       // keys split into segments when the context is long, so that enough blocks run at once
       const int32_t nseg = (pos + pc + kPrefillAttnSeg - 1) / kPrefillAttnSeg;
-      const dim3 ag(s.nq, (pc + kAttnQ - 1) / kAttnQ, nseg);
+      const dim3 ag((pc * s.group() + kFaRows - 1) / kFaRows, s.nkv, nseg);
       if (nseg > 1) {
         if (s.hd == 128) {
-          hipLaunchKernelGGL((prefill_attn_kernel<128, true>), ag, dim3(256), 0, stream, a, l, pos, pc);
+          hipLaunchKernelGGL((prefill_fattn_kernel<128, true>), ag, dim3(256), 0, stream, a, l, pos, pc);
           hipLaunchKernelGGL(prefill_attn_merge_kernel<128>, dim3(pc, s.nq), dim3(128), 0, stream, a, nseg, pc);
         } else {
-          hipLaunchKernelGGL((prefill_attn_kernel<64, true>), ag, dim3(256), 0, stream, a, l, pos, pc);
+          hipLaunchKernelGGL((prefill_fattn_kernel<64, true>), ag, dim3(256), 0, stream, a, l, pos, pc);
           hipLaunchKernelGGL(prefill_attn_merge_kernel<64>, dim3(pc, s.nq), dim3(64), 0, stream, a, nseg, pc);
         }
       } else if (s.hd == 128) {
-        hipLaunchKernelGGL((prefill_attn_kernel<128, false>), ag, dim3(256), 0, stream, a, l, pos, pc);
+        hipLaunchKernelGGL((prefill_fattn_kernel<128, false>), ag, dim3(256), 0, stream, a, l, pos, pc);
       } else {
-        hipLaunchKernelGGL((prefill_attn_kernel<64, false>), ag, dim3(256), 0, stream, a, l, pos, pc);
+        hipLaunchKernelGGL((prefill_fattn_kernel<64, false>), ag, dim3(256), 0, stream, a, l, pos, pc);
       }
       if ((e = gemm(a, ST_O, l, s.qdim(), a.x, s.d, 1, pc, stream)) != hipSuccess) return e;
       hipLaunchKernelGGL(prefill_norm_split_kernel, dim3(pc), dim3(256), 0, stream, a,
