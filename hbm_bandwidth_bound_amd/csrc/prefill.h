@@ -20,7 +20,7 @@ struct PrefillArgs {
   uint32_t* err;             // device error word
   const int32_t* tokens;     // [n] prompt ids
   float* x;                  // [chunk][d] residual stream
-  uint16_t* a3;              // [3][chunk][kmax] GEMM input in three bf16 parts
+  uint16_t* a3;              // [2][chunk][kmax] GEMM input in two bf16 parts
   int64_t a_part;            // elements between the parts
   float* c;                  // [chunk][nmax] GEMM output
   float* q;                  // [chunk][nq * hd] rotated queries

@@ -7,9 +7,10 @@
 // 为什么还是慢》, the prefill/decode contrast; zdabc.icu 《Kog 推理引擎…》, the time-to-first-token
 // measurement), so nothing here is on the decode path.
 //
-// Precision: activations are fp32 like the decode path. A GEMM input x is split into three bf16
-// parts hi + mid + lo (each the bf16 rounding of what the previous parts leave; 24 bits in all)
-// and every weight tile is multiplied by all three, accumulating in fp32 inside the MFMA. The
+// Precision: activations are fp32 like the decode path. A GEMM input x is split into two bf16
+// parts hi + lo (hi the bf16 rounding of x, lo that of x - hi; about 16 significant bits, a
+// relative error below 2^-17) and every weight tile is multiplied by both, accumulating in fp32
+// inside the MFMA: each product of a part with a bf16 weight is exact. The
 // weights are read in place from the packed image (the packer's placement, inverted per tile by
 // packed_tile), so no second copy of the model is kept.
 #include <hip/hip_runtime.h>
@@ -28,15 +29,11 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// x = hi + mid + lo (bf16 bits), each part the round-to-nearest-even of the remainder
-__device__ __forceinline__ void split3(float x, uint16_t* hi, uint16_t* mid, uint16_t* lo) {
+// x ~ hi + lo (bf16 bits): hi = bf16(x) and lo = bf16(x - hi), both rounded to nearest even
+__device__ __forceinline__ void split2(float x, uint16_t* hi, uint16_t* lo) {
   const uint32_t h = f32_to_bf16(x);
-  const float r1 = x - bf16_to_f32(h);
-  const uint32_t m = f32_to_bf16(r1);
-  const float r2 = r1 - bf16_to_f32(m);
   *hi = (uint16_t)h;
-  *mid = (uint16_t)m;
-  *lo = (uint16_t)f32_to_bf16(r2);
+  *lo = (uint16_t)f32_to_bf16(x - bf16_to_f32(h));
 }
 
 // ------------------------------------------------------------------------------------------
@@ -55,7 +52,7 @@ __global__ void __launch_bounds__(256) prefill_embed_kernel(PrefillArgs a, int32
 }
 
 // ------------------------------------------------------------------------------------------
-// RMSNorm of each row of X with gain g, written as the three-part GEMM input (row stride d).
+// RMSNorm of each row of X with gain g, written as the two-part GEMM input (row stride d).
 // The sum of squares runs in a fixed order (per-thread strided partials, then a fixed tree).
 // ------------------------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) prefill_norm_split_kernel(PrefillArgs a, const uint16_t* gain, int32_t pc) {
@@ -75,96 +72,117 @@ __global__ void __launch_bounds__(256) prefill_norm_split_kernel(PrefillArgs a, 
   for (int32_t e = threadIdx.x; e < d; e += 256) {
     const float u = (xr[e] * r) * bf16_to_f32(gain[e]);
     const int64_t o = (int64_t)i * d + e;
-    split3(u, a.a3 + o, a.a3 + a.a_part + o, a.a3 + 2 * a.a_part + o);
+    split2(u, a.a3 + o, a.a3 + a.a_part + o);
   }
 }
 
 // ------------------------------------------------------------------------------------------
 // GEMM on the matrix cores: C[i][n] (= or +=) sum_k A[i][k] W[n][k] for the rows n of one stage
-// in pair order (n = 2 gp + 0 for the pair's row A, + 1 for its row B), A given in three bf16
-// parts. Block: 64 tokens x 64 rows, 4 waves of 16 rows; K in chunks of 128 staged in LDS.
+// in pair order (n = 2 gp + 0 for the pair's row A, + 1 for its row B), A given in two bf16 parts.
+// Block: 64 tokens x 128 rows, 4 waves of 32 rows (two 16-row MFMA columns each, so every A
+// operand read from LDS feeds two MFMAs); K in chunks of 128. The next chunk's weight operands
+// and activations are loaded into registers while the current chunk is multiplied.
 // MFMA 16x16x32 bf16 operand layout (gfx950): lane l holds A[l%16][8(l/16) .. +7] and
 // B[8(l/16) .. +7][l%16]; the result D[4(l/16) + r][l%16] for r < 4.
 // ------------------------------------------------------------------------------------------
-constexpr int kGemmM = 64, kGemmN = 64, kGemmKC = 128;
+constexpr int kGemmM = 64, kGemmN = 128, kGemmKC = 128, kGemmParts = 2;
 constexpr int kALd = kGemmKC + 8;  // padded LDS row (bf16), spreads the rows over the banks
 
 __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillArgs a, GemmStage g, int32_t pc) {
-  __shared__ __align__(16) uint16_t As[3][kGemmM][kALd];
+  constexpr int KSTEPS = kGemmKC / 32;
+  constexpr int NB = 2;                                             // 16-row columns per wave
+  constexpr int APER = kGemmParts * kGemmM * (kGemmKC / 8) / 256;  // 16-byte pieces per thread
+  __shared__ __align__(16) uint16_t As[kGemmParts][kGemmM][kALd];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int32_t m0 = blockIdx.y * kGemmM;
   const int nl = lane & 15, kg = lane >> 4;
-  const int32_t n = blockIdx.x * kGemmN + wv * 16 + nl;
-  const bool nvalid = n < g.N;
-  const int32_t gp = nvalid ? n >> 1 : 0;
-  const int sel = n & 1;
+  int32_t n[NB], gp[NB];
+  bool nvalid[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    n[nb] = blockIdx.x * kGemmN + wv * (16 * NB) + 16 * nb + nl;
+    nvalid[nb] = n[nb] < g.N;
+    gp[nb] = nvalid[nb] ? n[nb] >> 1 : 0;
+  }
+  const int sel = nl & 1;  // row A or B of the pair (n and nl have the same parity)
   const int32_t ks_unit = unit_tiles(a.s.stage_kt(g.st));
-  f4 acc[4];
+  int64_t tbase[NB] = {0, 0};  // first tile of the current unit of each column's pair
+  f4 acc[4][NB];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) acc[mb] = f4{0.f, 0.f, 0.f, 0.f};
-  int64_t tbase = 0;  // first tile of the current unit of this lane's pair
-  constexpr int KSTEPS = kGemmKC / 32;
-  for (int32_t kc = 0; kc < g.K; kc += kGemmKC) {
-    // the chunk's weight operands first (all k-steps), so that their loads are in flight
-    // together with the activation loads below
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f4{0.f, 0.f, 0.f, 0.f};
+
+  uint2 w0[NB][KSTEPS], w1[NB][KSTEPS];
+  uint4 av4[APER];
+  auto fetch = [&](int32_t kc) {  // weight operands of chunk kc into w0/w1, activations into av4
     const int32_t kt = kc / kTileK;
-    if (kt % ks_unit == 0 && kc % kTileK == 0)
-      tbase = nvalid ? packed_tile(a.s, a.wbase, g.st, g.layer, gp, kt) : 0;
-    const uint8_t* tp = a.packed + (tbase + kt % ks_unit) * kTileBytes + 8 * sel;
-    uint2 w0[KSTEPS], w1[KSTEPS];
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const int L = (kc % kTileK + ks * 32 + kg * 8) >> 2;  // tile lane holding k .. k+3
-      w0[ks] = nvalid ? *(const uint2*)(tp + 16 * L) : uint2{0u, 0u};
-      w1[ks] = nvalid ? *(const uint2*)(tp + 16 * (L + 1)) : uint2{0u, 0u};
+    for (int nb = 0; nb < NB; ++nb) {
+      if (kt % ks_unit == 0 && kc % kTileK == 0)
+        tbase[nb] = nvalid[nb] ? packed_tile(a.s, a.wbase, g.st, g.layer, gp[nb], kt) : 0;
+      const uint8_t* tp = a.packed + (tbase[nb] + kt % ks_unit) * kTileBytes + 8 * sel;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int L = (kc % kTileK + ks * 32 + kg * 8) >> 2;  // tile lane holding k .. k+3
+        w0[nb][ks] = nvalid[nb] ? *(const uint2*)(tp + 16 * L) : uint2{0u, 0u};
+        w1[nb][ks] = nvalid[nb] ? *(const uint2*)(tp + 16 * (L + 1)) : uint2{0u, 0u};
+      }
     }
-    // the activation chunk: every load issued before any is stored to LDS
-    constexpr int APER = 3 * kGemmM * (kGemmKC / 8) / 256;  // 16-byte pieces per thread
-    uint4 av4[APER];
 #pragma unroll
-    for (int j = 0; j < APER; ++j) {
-      const int q = tid + j * 256;
+    for (int jj = 0; jj < APER; ++jj) {
+      const int q = tid + jj * 256;
       const int p = q / (kGemmM * (kGemmKC / 8)), r = (q / (kGemmKC / 8)) % kGemmM, c = q % (kGemmKC / 8);
       const int32_t i = m0 + r;
-      av4[j] = i < pc ? *(const uint4*)(a.a3 + p * a.a_part + (int64_t)i * g.K + kc + c * 8) : uint4{0u, 0u, 0u, 0u};
+      av4[jj] = i < pc ? *(const uint4*)(a.a3 + p * a.a_part + (int64_t)i * g.K + kc + c * 8) : uint4{0u, 0u, 0u, 0u};
     }
+  };
+
+  fetch(0);
+  for (int32_t kc = 0; kc < g.K; kc += kGemmKC) {
+    __syncthreads();  // every wave is done with the previous chunk's activations
 #pragma unroll
-    for (int j = 0; j < APER; ++j) {
-      const int q = tid + j * 256;
+    for (int jj = 0; jj < APER; ++jj) {
+      const int q = tid + jj * 256;
       const int p = q / (kGemmM * (kGemmKC / 8)), r = (q / (kGemmKC / 8)) % kGemmM, c = q % (kGemmKC / 8);
-      *(uint4*)&As[p][r][c * 8] = av4[j];
+      *(uint4*)&As[p][r][c * 8] = av4[jj];
     }
+    bf16x8 b[NB][KSTEPS];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks)
+        b[nb][ks] = __builtin_bit_cast(bf16x8, uint4{w0[nb][ks].x, w0[nb][ks].y, w1[nb][ks].x, w1[nb][ks].y});
     __syncthreads();
+    if (kc + kGemmKC < g.K) fetch(kc + kGemmKC);  // in flight while this chunk is multiplied
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      const bf16x8 b = __builtin_bit_cast(bf16x8, uint4{w0[ks].x, w0[ks].y, w1[ks].x, w1[ks].y});
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
-        for (int p = 0; p < 3; ++p) {
+        for (int p = 0; p < kGemmParts; ++p) {
           const bf16x8 av = *(const bf16x8*)&As[p][mb * 16 + nl][ks * 32 + kg * 8];
-          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b, acc[mb], 0, 0, 0);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b[nb][ks], acc[mb][nb], 0, 0, 0);
         }
       }
     }
-    __syncthreads();
   }
-  if (!nvalid) return;
-  float old[4][4];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int nb = 0; nb < NB; ++nb) {
+    if (!nvalid[nb]) continue;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int32_t i = m0 + mb * 16 + kg * 4 + r;
-      old[mb][r] = (g.accumulate && i < pc) ? g.out[(int64_t)i * g.ldo + n] : 0.f;
-    }
+    for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int32_t i = m0 + mb * 16 + kg * 4 + r;
-      if (i < pc) g.out[(int64_t)i * g.ldo + n] = old[mb][r] + acc[mb][r];
-    }
+      for (int r = 0; r < 4; ++r) {
+        const int32_t i = m0 + mb * 16 + kg * 4 + r;
+        if (i < pc) {
+          float* dst = g.out + (int64_t)i * g.ldo + n[nb];
+          *dst = (g.accumulate ? *dst : 0.f) + acc[mb][nb][r];
+        }
+      }
+  }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -211,7 +229,7 @@ __global__ void __launch_bounds__(256) prefill_rope_kv_kernel(PrefillArgs a, int
 // the S^T result leaves them in the lanes, and V is read in that same order. Q and P enter as two
 // bf16 parts (hi + lo, about 16 significant bits); K and V are bf16 already, so every product is
 // exact and the sums are fp32. With one key segment (blockIdx.z) the output is written as the
-// three-part input of the O projection; with several, each block writes its partial state
+// two-part input of the O projection; with several, each block writes its partial state
 // (acc, m, l) and prefill_attn_merge_kernel combines the segments.
 // ------------------------------------------------------------------------------------------
 constexpr int kFaRows = 64, kFaKT = 64;
@@ -402,7 +420,7 @@ __global__ void __launch_bounds__(256) prefill_fattn_kernel(PrefillArgs a, int32
 #pragma unroll
       for (int c = 0; c < HD / 16; ++c) {
         const int64_t off = (int64_t)q2 * s.qdim() + h2 * HD + 16 * c + rl;
-        split3(o[c][i] * inv, a.a3 + off, a.a3 + a.a_part + off, a.a3 + 2 * a.a_part + off);
+        split2(o[c][i] * inv, a.a3 + off, a.a3 + a.a_part + off);
       }
     }
   }
@@ -427,11 +445,11 @@ __global__ void __launch_bounds__(HD) prefill_attn_merge_kernel(PrefillArgs a, i
     M = Mn;
   }
   const int64_t o = (int64_t)i * s.qdim() + h * HD + e;
-  split3(A / S, a.a3 + o, a.a3 + a.a_part + o, a.a3 + 2 * a.a_part + o);
+  split2(A / S, a.a3 + o, a.a3 + a.a_part + o);
 }
 
 // ------------------------------------------------------------------------------------------
-// SwiGLU of the gate/up output (pair f = gate row f, up row f) into the three-part input of the
+// SwiGLU of the gate/up output (pair f = gate row f, up row f) into the two-part input of the
 // down projection.
 // ------------------------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) prefill_swiglu_kernel(PrefillArgs a, int32_t pc) {
@@ -442,7 +460,7 @@ __global__ void __launch_bounds__(256) prefill_swiglu_kernel(PrefillArgs a, int3
     const float ya = c[2 * f], yb = c[2 * f + 1];
     const float hv = (ya / (1.0f + expf(-ya))) * yb;
     const int64_t o = (int64_t)i * F + f;
-    split3(hv, a.a3 + o, a.a3 + a.a_part + o, a.a3 + 2 * a.a_part + o);
+    split2(hv, a.a3 + o, a.a3 + a.a_part + o);
   }
 }
 
