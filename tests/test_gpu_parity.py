@@ -358,6 +358,41 @@ def test_tiny_long_prompt_split_attention(torch_cuda, tiny, oracle_lib):
     eng.close()
 
 
+# head_dim 128 shapes small enough for the oracle to run a 2,100-token prompt in seconds
+LONG_HD128 = [
+    synth.ModelConfig("mha-hd128", 1, 512, 4, 4, 128, 768, 1000),   # G = 1
+    synth.ModelConfig("g4-hd128", 1, 512, 4, 1, 128, 512, 1024),    # G = 4, one KV head
+]
+
+
+@pytest.mark.parametrize("cfg", LONG_HD128, ids=lambda c: c.name)
+def test_long_prompt_split_attention_hd128(torch_cuda, oracle_lib, cfg):
+    """The segmented prompt-pass attention at head_dim 128, with one query head per KV head and
+    with four (a block of 64 (query, head) rows then covers 64 or 16 queries)."""
+    from hbm_bandwidth_bound_amd.kie import Engine
+    P, N = 2100, 3
+    say(f"[{cfg.name}] prefill {P} (segmented attention) + decode {N}")
+    w = synth.make_weights_np(cfg, 0)
+    wd = to_device(w)
+    eng = Engine(cfg, wd, P + N)
+    prompt = synth.prompt_ids(P, cfg.vocab_size, 35)
+    first, last, toks, logits = run_gpu(torch_cuda, eng, prompt, N, cfg.vocab_size)
+    om = oracle_lib.OracleModel(cfg, w, P + N)
+    ref_prompt = om.run(prompt)
+    e = rel_l2(last, ref_prompt[-1])
+    say(f"  last-logits rel-L2 {e:.3e}")
+    assert e <= 1e-3
+    kg = eng.kv_view().cpu().numpy().view(np.uint16)
+    ko, vo = om.kv_view()
+    ek = rel_l2(synth.bf16_bits_to_f32(kg[:, 0, :, :P]), synth.bf16_bits_to_f32(ko[:, :, :P]))
+    ev = rel_l2(synth.bf16_bits_to_f32(kg[:, 1, :, :P]), synth.bf16_bits_to_f32(vo[:, :, :P]))
+    say(f"  cache rel-L2 K {ek:.3e} V {ev:.3e}")
+    assert ek <= 1e-3 and ev <= 1e-3
+    ref = om.run([first] + [int(t) for t in toks[:-1]], start_pos=P)
+    check_steps(logits, ref, toks, label=cfg.name)
+    eng.close()
+
+
 def test_tokens_stream_to_the_host_during_a_launch(torch_cuda, tiny):
     """kie_set_token_stream: each chosen token reaches pinned host memory while the single
     kie_generate launch is still running (a host thread sees the count grow before the sync)."""
