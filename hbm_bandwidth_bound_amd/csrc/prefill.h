@@ -31,6 +31,8 @@ struct GemmStage {
   int32_t st, layer, K, N;
   float* out;
   int32_t ldo, accumulate;
+  int32_t splits, kper;  // K is cut into `splits` shares of kper each
+  float* part;           // [splits][chunk][N] partial sums when splits > 1
 };
 
 // Run every layer over positions p0 .. p0 + n - 1 (writes their K/V rows).

@@ -90,23 +90,37 @@ constexpr int kALd = kGemmKC + 8;  // padded LDS row (bf16), spreads the rows ov
 
 __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillArgs a, GemmStage g, int32_t pc) {
   constexpr int KSTEPS = kGemmKC / 32;
-  constexpr int NB = 2;                                             // 16-row columns per wave
+  constexpr int NB = kGemmN / 64;                                  // 16-row columns per wave
   constexpr int APER = kGemmParts * kGemmM * (kGemmKC / 8) / 256;  // 16-byte pieces per thread
   __shared__ __align__(16) uint16_t As[kGemmParts][kGemmM][kALd];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int32_t m0 = blockIdx.y * kGemmM;
+  // Tile of this block. The token tiles of one weight tile run on one XCD in consecutive slots
+  // (workgroup b goes to XCD b mod 8), so the weight tile is fetched from HBM once and then served
+  // by that XCD's L2 to the other token tiles.
+  const int32_t nM = (pc + kGemmM - 1) / kGemmM, nN = (g.N + kGemmN - 1) / kGemmN;
+  const int32_t b = (int32_t)blockIdx.x % (nM * nN), split = (int32_t)blockIdx.x / (nM * nN);
+  const int32_t kbeg = split * g.kper, kend = kbeg + g.kper;  // this block's share of K
+  int32_t mt, nt;
+  if (nN % 8 == 0) {
+    mt = (b / 8) % nM;
+    nt = b % 8 + 8 * ((b / 8) / nM);
+  } else {
+    mt = b % nM;
+    nt = b / nM;
+  }
+  const int32_t m0 = mt * kGemmM;
   const int nl = lane & 15, kg = lane >> 4;
   int32_t n[NB], gp[NB];
   bool nvalid[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    n[nb] = blockIdx.x * kGemmN + wv * (16 * NB) + 16 * nb + nl;
+    n[nb] = nt * kGemmN + wv * (16 * NB) + 16 * nb + nl;
     nvalid[nb] = n[nb] < g.N;
     gp[nb] = nvalid[nb] ? n[nb] >> 1 : 0;
   }
   const int sel = nl & 1;  // row A or B of the pair (n and nl have the same parity)
   const int32_t ks_unit = unit_tiles(a.s.stage_kt(g.st));
-  int64_t tbase[NB] = {0, 0};  // first tile of the current unit of each column's pair
+  int64_t tbase[NB] = {};  // first tile of the current unit of each column's pair
   f4 acc[4][NB];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
@@ -119,8 +133,8 @@ __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillArgs a, GemmSt
     const int32_t kt = kc / kTileK;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      if (kt % ks_unit == 0 && kc % kTileK == 0)
-        tbase[nb] = nvalid[nb] ? packed_tile(a.s, a.wbase, g.st, g.layer, gp[nb], kt) : 0;
+      if (kc == kbeg || (kt % ks_unit == 0 && kc % kTileK == 0))
+        tbase[nb] = nvalid[nb] ? packed_tile(a.s, a.wbase, g.st, g.layer, gp[nb], kt - kt % ks_unit) : 0;
       const uint8_t* tp = a.packed + (tbase[nb] + kt % ks_unit) * kTileBytes + 8 * sel;
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
@@ -138,8 +152,8 @@ __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillArgs a, GemmSt
     }
   };
 
-  fetch(0);
-  for (int32_t kc = 0; kc < g.K; kc += kGemmKC) {
+  fetch(kbeg);
+  for (int32_t kc = kbeg; kc < kend; kc += kGemmKC) {
     __syncthreads();  // every wave is done with the previous chunk's activations
 #pragma unroll
     for (int jj = 0; jj < APER; ++jj) {
@@ -154,7 +168,7 @@ __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillArgs a, GemmSt
       for (int ks = 0; ks < KSTEPS; ++ks)
         b[nb][ks] = __builtin_bit_cast(bf16x8, uint4{w0[nb][ks].x, w0[nb][ks].y, w1[nb][ks].x, w1[nb][ks].y});
     __syncthreads();
-    if (kc + kGemmKC < g.K) fetch(kc + kGemmKC);  // in flight while this chunk is multiplied
+    if (kc + kGemmKC < kend) fetch(kc + kGemmKC);  // in flight while this chunk is multiplied
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
 #pragma unroll
@@ -177,11 +191,40 @@ __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillArgs a, GemmSt
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int32_t i = m0 + mb * 16 + kg * 4 + r;
-        if (i < pc) {
+        if (i >= pc) continue;
+        if (g.splits > 1) {  // partial sum of this share of K, summed by prefill_splitk_reduce_kernel
+          g.part[((int64_t)split * pc + i) * g.N + n[nb]] = acc[mb][nb][r];
+        } else {
           float* dst = g.out + (int64_t)i * g.ldo + n[nb];
           *dst = (g.accumulate ? *dst : 0.f) + acc[mb][nb][r];
         }
       }
+  }
+}
+
+// out (= or +=) the sum of the K shares' partial sums, in share order (the same every run)
+__global__ void __launch_bounds__(256) prefill_splitk_reduce_kernel(GemmStage g, int32_t pc) {
+  const int32_t nq4 = g.N / 4;
+  const int64_t total = (int64_t)pc * nq4;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const int32_t i = (int32_t)(e / nq4), n4 = (int32_t)(e % nq4);
+    float4 sum = *(const float4*)(g.part + (int64_t)i * g.N + 4 * n4);
+    for (int32_t sp = 1; sp < g.splits; ++sp) {
+      const float4 v = *(const float4*)(g.part + ((int64_t)sp * pc + i) * g.N + 4 * n4);
+      sum.x += v.x;
+      sum.y += v.y;
+      sum.z += v.z;
+      sum.w += v.w;
+    }
+    float4* dst = (float4*)(g.out + (int64_t)i * g.ldo + 4 * n4);
+    if (g.accumulate) {
+      const float4 o = *dst;
+      sum.x += o.x;
+      sum.y += o.y;
+      sum.z += o.z;
+      sum.w += o.w;
+    }
+    *dst = sum;
   }
 }
 
@@ -477,8 +520,23 @@ static hipError_t gemm(const PrefillArgs& a, int st, int32_t layer, int32_t K, f
   g.out = out;
   g.ldo = ldo;
   g.accumulate = accumulate;
-  hipLaunchKernelGGL(prefill_gemm_kernel, dim3((g.N + kGemmN - 1) / kGemmN, (pc + kGemmM - 1) / kGemmM), dim3(256), 0,
-                     stream, a, g, pc);
+  // A GEMM with few output tiles (the O and down projections, N = d) splits K over up to 8
+  // blocks per tile so that about two blocks run per CU; the partial sums go to the GEMM output
+  // buffer, which these projections (they accumulate into the residual) leave unused.
+  const int32_t tiles = ((g.N + kGemmN - 1) / kGemmN) * ((pc + kGemmM - 1) / kGemmM);
+  g.splits = 1;
+  if (out != a.c && g.N % 4 == 0)
+    while (g.splits < 8 && tiles * g.splits < 512 && K % (2 * g.splits * kGemmKC) == 0 &&
+           2 * g.splits * g.N <= prefill_nmax(a.s))
+      g.splits *= 2;
+  g.kper = K / g.splits;
+  g.part = a.c;
+  hipLaunchKernelGGL(prefill_gemm_kernel, dim3(tiles * g.splits), dim3(256), 0, stream, a, g, pc);
+  if (g.splits > 1) {
+    const int64_t n4 = (int64_t)pc * (g.N / 4);
+    hipLaunchKernelGGL(prefill_splitk_reduce_kernel, dim3((unsigned)((n4 + 255) / 256 < 2048 ? (n4 + 255) / 256 : 2048)),
+                       dim3(256), 0, stream, g, pc);
+  }
   return hipGetLastError();
 }
 
