@@ -1076,13 +1076,16 @@ __device__ __forceinline__ void decode(Wk& K) {
             K.tr.add(T_MERGE, TR_NOW() - tm);
           }
           K.fetch_f32(ex + X.o + (int64_t)l * s.qdim(), s.qdim(), L.act, ep, false);
+          // The K/V rows this WG appended are complete before it publishes anything more. Here
+          // the wave has just waited for its polls, so nothing newer is queued and the wait
+          // costs nothing; after the next stage's first batch is issued it would wait for that.
+          if (at.has_p) __builtin_amdgcn_s_waitcnt(kWaitVm0);
           st = ST_O;
           bnd = B_O;
           break;
         }
         case B_O: {  // O outputs + residual -> gather xa -> RMSNorm
           bar();
-          if (at.has_p) __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this WG's K/V rows are complete first
           uint64_t* xa = ex + X.xa + (int64_t)l * s.d;
           K.prefetch_gain(P.norms + (int64_t)l * 2 * s.d + s.d);
           K.finalize(K.g[ST_O], [&](int32_t gp, float ya, float yb) {
