@@ -277,21 +277,26 @@ __global__ void __launch_bounds__(256) prefill_rope_kv_kernel(PrefillArgs a, int
 // ------------------------------------------------------------------------------------------
 constexpr int kFaRows = 64, kFaKT = 64;
 
+// two values to a bf16 pair (round to nearest even; gfx950 converts both in one instruction)
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+// eight values as two bf16 operands, x ~ hi + lo
 __device__ __forceinline__ void split2x8(const float* x, bf16x8* hi, bf16x8* lo) {
   uint32_t h[4], l[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const uint32_t h0 = f32_to_bf16(x[2 * e]), h1 = f32_to_bf16(x[2 * e + 1]);
-    const uint32_t l0 = f32_to_bf16(x[2 * e] - bf16_to_f32(h0)), l1 = f32_to_bf16(x[2 * e + 1] - bf16_to_f32(h1));
-    h[e] = h0 | (h1 << 16);
-    l[e] = l0 | (l1 << 16);
+    h[e] = cvt_bf16x2(x[2 * e], x[2 * e + 1]);
+    l[e] = cvt_bf16x2(x[2 * e] - bf16lo(h[e]), x[2 * e + 1] - bf16hi(h[e]));
   }
   *hi = __builtin_bit_cast(bf16x8, uint4{h[0], h[1], h[2], h[3]});
   *lo = __builtin_bit_cast(bf16x8, uint4{l[0], l[1], l[2], l[3]});
 }
 
 template <int HD, bool SPLIT>
-__global__ void __launch_bounds__(256) prefill_fattn_kernel(PrefillArgs a, int32_t layer, int32_t p0, int32_t pc) {
+__global__ void __launch_bounds__(256, 2) prefill_fattn_kernel(PrefillArgs a, int32_t layer, int32_t p0, int32_t pc) {
   constexpr int KP = HD + 8;     // padded K row (bf16): the 16 rows a lane group reads hit distinct banks
   constexpr int VP = kFaKT + 8;  // padded V^T row (bf16)
   constexpr int NKP = kFaKT * HD / 8 / 256;          // K pieces (16 bytes) per thread and tile
@@ -313,6 +318,8 @@ __global__ void __launch_bounds__(256) prefill_fattn_kernel(PrefillArgs a, int32
   const int32_t klast = SPLIT ? min(kend, kbeg + kPrefillAttnSeg - 1) : kend;
   const uint16_t* kbase = a.kv + kv_offset(s, layer, 0, j, 0);
   const uint16_t* vbase = a.kv + kv_offset(s, layer, 1, j, 0);
+  // keys up to kfull are visible to every row of this wave: tiles below it need no mask
+  const int32_t kfull = min(klast, p0 + min(((int32_t)blockIdx.x * kFaRows + wv * 16) / G, pc - 1));
 
   // Q^T operand of this lane: row rl, dims 32c + 8lg .. +7, scaled into the exp2 domain
   const float scale = 1.4426950408889634f / sqrtf((float)HD);
@@ -333,8 +340,9 @@ __global__ void __launch_bounds__(256) prefill_fattn_kernel(PrefillArgs a, int32
   for (int c = 0; c < HD / 16; ++c) o[c] = f4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;  // softmax state of row rl (the same in the 4 lane groups)
 
-  uint4 kr[NKP], vr[NVP][2];
-  auto fetch = [&](int32_t k0) {  // the tile's K/V pieces of this thread; rows past klast read as 0
+  // two register sets of K/V pieces: tile t + 2 is loaded while tile t is multiplied
+  uint4 kr0[NKP], vr0[NVP][2], kr1[NKP], vr1[NVP][2];
+  auto fetch = [&](uint4(&kr)[NKP], uint4(&vr)[NVP][2], int32_t k0) {  // rows past klast read as 0
 #pragma unroll
     for (int e = 0; e < NKP; ++e) {
       const int q = tid + 256 * e, row = q / (HD / 8), c8 = q % (HD / 8);
@@ -349,7 +357,7 @@ __global__ void __launch_bounds__(256) prefill_fattn_kernel(PrefillArgs a, int32
       vr[e][1] = kp + 1 <= klast ? *(const uint4*)(vbase + (int64_t)(kp + 1) * HD + 8 * c8) : uint4{0u, 0u, 0u, 0u};
     }
   };
-  auto stage = [&]() {  // K rows as they are; V as V^T, two keys per 32-bit word
+  auto stage = [&](const uint4(&kr)[NKP], const uint4(&vr)[NVP][2]) {  // K as is; V as V^T, 2 keys a word
 #pragma unroll
     for (int e = 0; e < NKP; ++e) {
       const int q = tid + 256 * e, row = q / (HD / 8), c8 = q % (HD / 8);
@@ -368,12 +376,7 @@ __global__ void __launch_bounds__(256) prefill_fattn_kernel(PrefillArgs a, int32
     }
   };
 
-  if (kbeg <= klast) fetch(kbeg);
-  for (int32_t k0 = kbeg; k0 <= klast; k0 += kFaKT) {
-    __syncthreads();  // every wave is done with the previous tile
-    stage();
-    __syncthreads();
-    if (k0 + kFaKT <= klast) fetch(k0 + kFaKT);  // in flight while this tile is computed
+  auto tile = [&](int32_t k0) {
     // S^T: st[ks][i] = score of key k0 + 16 ks + 4 lg + i for row rl
     f4 st[kFaKT / 16];
 #pragma unroll
@@ -386,26 +389,31 @@ __global__ void __launch_bounds__(256) prefill_fattn_kernel(PrefillArgs a, int32
         st[ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, ql[c], st[ks], 0, 0, 0);
       }
     }
+    if (k0 + kFaKT - 1 > kfull) {  // the tile reaches past some row's position or past klast
+#pragma unroll
+      for (int ks = 0; ks < kFaKT / 16; ++ks)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int32_t kp = k0 + 16 * ks + 4 * lg + i;
+          if (kp > qpos || kp > klast) st[ks][i] = -INFINITY;
+        }
+    }
     float mt = -INFINITY;
 #pragma unroll
     for (int ks = 0; ks < kFaKT / 16; ++ks)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int32_t kp = k0 + 16 * ks + 4 * lg + i;
-        if (kp > qpos || kp > klast) st[ks][i] = -INFINITY;
-        mt = fmaxf(mt, st[ks][i]);
-      }
+      for (int i = 0; i < 4; ++i) mt = fmaxf(mt, st[ks][i]);
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
     const float mn = fmaxf(m, mt);
     const float mu = mn == -INFINITY ? 0.f : mn;  // a row with no key yet keeps p = 0
-    const float corr = exp2f(m - mu);
+    const float corr = __builtin_amdgcn_exp2f(m - mu);  // v_exp_f32: 2^x, 0 at -inf
     float ps = 0.f;
 #pragma unroll
     for (int ks = 0; ks < kFaKT / 16; ++ks)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        st[ks][i] = exp2f(st[ks][i] - mu);
+        st[ks][i] = __builtin_amdgcn_exp2f(st[ks][i] - mu);
         ps += st[ks][i];
       }
     ps += __shfl_xor(ps, 16, 64);
@@ -437,6 +445,22 @@ __global__ void __launch_bounds__(256) prefill_fattn_kernel(PrefillArgs a, int32
         o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, o[c], 0, 0, 0);
       }
     }
+  };
+
+  if (kbeg <= klast) fetch(kr0, vr0, kbeg);
+  if (kbeg + kFaKT <= klast) fetch(kr1, vr1, kbeg + kFaKT);
+  for (int32_t k0 = kbeg; k0 <= klast; k0 += 2 * kFaKT) {
+    __syncthreads();  // every wave is done with the previous tile
+    stage(kr0, vr0);
+    __syncthreads();
+    if (k0 + 2 * kFaKT <= klast) fetch(kr0, vr0, k0 + 2 * kFaKT);
+    tile(k0);
+    if (k0 + kFaKT > klast) break;
+    __syncthreads();
+    stage(kr1, vr1);
+    __syncthreads();
+    if (k0 + 3 * kFaKT <= klast) fetch(kr1, vr1, k0 + 3 * kFaKT);
+    tile(k0 + kFaKT);
   }
   // rows 4 lg + i of O: their softmax state, then the output
   float lr[4], mr[4];
