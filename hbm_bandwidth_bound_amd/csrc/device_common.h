@@ -61,6 +61,15 @@ constexpr int kLoadNT = 2;  // cache policy of weight and KV loads: streamed onc
 __device__ __forceinline__ v4u load16(__amdgpu_buffer_rsrc_t rs, uint32_t voff) {
   return __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, kLoadNT));
 }
+// LDS byte address of a pointer into the workgroup's shared memory
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(const lds_u8*)p; }
+// 16 bytes per lane from the buffer straight into LDS at lds_base + 16 * lane (gfx950
+// buffer_load_dwordx4 ... lds; M0 holds the wave-uniform LDS address). Nothing is returned to
+// registers: the caller waits on the vector memory counter before reading the LDS.
+__device__ __forceinline__ void load16_lds(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t lds_base) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(voff), "s"(rs), "{m0}"(lds_base) : "memory");
+}
 
 template <typename T>
 __device__ __forceinline__ T wave_bcast(T v, int lane) {

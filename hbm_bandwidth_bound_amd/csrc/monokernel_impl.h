@@ -77,6 +77,7 @@ struct Lds {
   float* q;        // attention: the group's queries [G][hd], the current k [hd] and v [hd]
   float2* rope;    // (cos, sin) of the current position, hd/2 entries
   uint32_t* ctl;   // control words
+  uint8_t* xb;     // one extra weight batch per wave (kBatch tiles), or null where LDS is short
 };
 enum Ctl : int { C_ABORT = 0, C_COUNT = 4 };
 
@@ -105,9 +106,14 @@ __host__ __device__ inline int32_t merge_pad_floats(const Shape& s) {
 __host__ __device__ inline int32_t merge_floats(const Shape& s) {
   return act_floats(s) + 2 * s.d + 2 * kMaxUnits + merge_pad_floats(s);
 }
-inline int32_t lds_bytes_for_impl(const Shape& s) {
+// The extra batch slots (8 KiB per wave) are placed where the rest leaves room for them.
+constexpr int32_t kLdsCapacity = 160 * 1024;
+constexpr int32_t kXbBytes = kWaves * kBatch * kTileBytes;
+__host__ __device__ inline int32_t lds_base_bytes(const Shape& s) {
   return (merge_floats(s) + scr_floats(s) + (s.group() + 2) * s.hd + s.hd) * 4 + C_COUNT * 4;
 }
+__host__ __device__ inline bool xb_fits(const Shape& s) { return lds_base_bytes(s) + kXbBytes <= kLdsCapacity; }
+inline int32_t lds_bytes_for_impl(const Shape& s) { return lds_base_bytes(s) + (xb_fits(s) ? kXbBytes : 0); }
 __device__ __forceinline__ Lds lds_map(uint8_t* smem, const Shape& s) {
   Lds L;
   uint8_t* p = smem;
@@ -119,6 +125,8 @@ __device__ __forceinline__ Lds lds_map(uint8_t* smem, const Shape& s) {
   L.q = (float*)p; p += (size_t)(s.group() + 2) * s.hd * 4;
   L.rope = (float2*)p; p += (size_t)s.hd * 4;
   L.ctl = (uint32_t*)p;
+  p += C_COUNT * 4;  // 16-byte aligned: every piece above is a multiple of 4 floats
+  L.xb = xb_fits(s) ? p : nullptr;
   return L;
 }
 
@@ -215,7 +223,10 @@ struct Wk {
   int32_t layer_b, lm_b;
   const uint8_t* stream;  // this wave's first tile
   v4u nxt[kBatch];        // the next batch of the stream (loads in flight)
-  int32_t pidx, pstep;    // that batch: index in its step's stream, and the step
+  int32_t pidx, pstep;    // the last batch issued: index in its step's stream, and the step
+  // The batch after nxt may also be in flight, loaded straight into this wave's LDS slot: xpend
+  // while nxt is still ahead of it, xnext once it is the next to reduce.
+  bool xpend = false, xnext = false;
 
   __device__ __forceinline__ Wk(const KParams& p, const Lds& l, int32_t w_, int32_t v_, int32_t lane_)
       : P(p), L(l), w(w_), v(v_), lane(lane_), tid(v_ * kWave + lane_), fail(false) {
@@ -257,12 +268,39 @@ struct Wk {
     advance();
     issue(nxt);
   }
-  // hand the batch in flight to the caller and issue the one after it
+  // hand the next batch of the stream to the caller and keep the one after it in flight
   __device__ __forceinline__ void take(v4u* cur) {
+    if (xnext) {  // the batch in the LDS slot; only nxt's 8 loads were issued after it
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kBatch) : "memory");
+      const uint8_t* xs = L.xb + (size_t)v * kBatch * kTileBytes + lane * 16;
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) cur[b] = *(const v4u*)(xs + b * kTileBytes);
+      xnext = false;
+      return;
+    }
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) cur[b] = nxt[b];
     advance();
     issue(nxt);
+    if (xpend) {
+      xpend = false;
+      xnext = true;
+    }
+  }
+  // Before a wait at a stage boundary: load the batch after nxt into this wave's LDS slot with
+  // direct buffer->LDS loads, so that two batches stream in across the wait. The loads are
+  // written as assembly so that the compiler, which would otherwise wait for them before every
+  // LDS read, adds no waits; take() waits for them itself. They hold no registers.
+  __device__ __forceinline__ void issue_x() {
+    if (L.xb == nullptr || xpend || xnext) return;
+    advance();
+    const bool live = pstep < P.n_steps;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(stream + (live ? (size_t)pidx * kBatch * kTileBytes : 0), live ? kBatch * kTileBytes : 0);
+    const uint32_t base = lds_addr(L.xb + (size_t)v * kBatch * kTileBytes);
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) load16_lds(rs, (uint32_t)(lane * 16 + b * kTileBytes), base + b * kTileBytes);
+    xpend = true;
   }
 
   // ------------------------------------------------------------ GEMV of one stage
@@ -1092,6 +1130,7 @@ __device__ __forceinline__ void decode(Wk& K) {
             st_x(xa + 2 * gp, tag_f(xres[2 * gp] + ya, ep));
             st_x(xa + 2 * gp + 1, tag_f(xres[2 * gp + 1] + yb, ep));
           });
+          K.issue_x();  // the gate/up stage is the longest: start its second batch now
           xres = xres == L.xres ? L.xres + s.d : L.xres;  // the other buffer: no wave reads it now
           ss = K.fetch_f32(xa, s.d, xres, ep, true);
           K.norm_to_act(ss, xres);
@@ -1105,6 +1144,7 @@ __device__ __forceinline__ void decode(Wk& K) {
           K.finalize(K.g[ST_GU], [&](int32_t gp, float ya, float yb) {
             st_x(hx + gp, tag_f((ya / (1.0f + expf(-ya))) * yb, ep));
           });
+          K.issue_x();
           K.fetch_f32<16>(hx, s.F, L.act, ep, false);
           st = ST_DN;
           bnd = B_DN;
@@ -1126,6 +1166,7 @@ __device__ __forceinline__ void decode(Wk& K) {
             st_x(xf + 2 * gp + 1, tag_f(xres[2 * gp + 1] + yb, ep));
           });
           dphase(25);
+          K.issue_x();  // the next layer's stages
 #ifdef KIE_TRACE
           if (step == 8 && l == 12) K.tr.c[29] = now_ticks();  // one sample of absolute times
 #endif
