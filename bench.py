@@ -126,14 +126,20 @@ def main():
     eng = Engine(m, wdev, P + max(K, W))
     prompt = torch.tensor(synth.prompt_ids(P, m.vocab_size, wl.prompt_seed), dtype=torch.int32, device=dev)
 
-    # prompt pass (untimed for the metric; its time is reported as TTFT)
+    # prompt pass (untimed for the metric; its time is reported as TTFT). The first call in the
+    # process also pays one-time kernel loading; the second, over the same prompt from position
+    # 0 (it rewrites the same cache rows), is the time a warm engine takes.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    print(f"[bench] prompt pass of {P} tokens", file=sys.stderr, flush=True)
-    e0.record(stream)
-    first = eng.prefill(prompt)
-    e1.record(stream)
-    eng.sync()
-    ttft_ms = e0.elapsed_time(e1)
+    ttft = []
+    for rep in range(2):
+        print(f"[bench] prompt pass of {P} tokens ({'first call' if rep == 0 else 'warm'})", file=sys.stderr, flush=True)
+        eng.reset()
+        e0.record(stream)
+        first = eng.prefill(prompt)
+        e1.record(stream)
+        eng.sync()
+        ttft.append(e0.elapsed_time(e1))
+    ttft_ms = ttft[1]
     # the prompt pass's matrix products: 2 x (tokens - 1) x the layer weights (the last position
     # runs through the decode kernel), plus the causal attention products
     mm = traffic.weight_bytes(m) // 2 - m.vocab_size * m.d_model - (2 * m.n_layers + 2) * m.d_model
@@ -235,7 +241,7 @@ def main():
         "extra": {"kernel_ms": round(launch_ms, 3), "algorithmic_bytes": algo_bytes,
                   "bytes_per_token": algo_bytes / K, "stream_read_ceiling_GBps": round(ceiling_gbps, 1),
                   "frac_of_stream_ceiling": round(achieved_gbps / ceiling_gbps, 4),
-                  "ttft_ms_prompt_pass": round(ttft_ms, 2),
+                  "ttft_ms_prompt_pass": round(ttft_ms, 2), "ttft_ms_first_call": round(ttft[0], 2),
                   "prompt_pass": {"flops": prefill_flops, "tflops": round(prefill_flops / (ttft_ms * 1e-3) / 1e12, 1),
                                   "frac_of_bf16_mfma_peak": round(prefill_flops / (ttft_ms * 1e-3) / 2.5e15, 4)},
                   "one_token_launches": single,

@@ -524,6 +524,7 @@ kie_status kie_prefill(kie_ctx* ctx, const int32_t* tokens_dev, int32_t n_tokens
     a.tokens = tokens_dev;
     a.x = (float*)(ctx->ws + ctx->wso.px);
     a.a3 = (uint16_t*)(ctx->ws + ctx->wso.pa3);
+    a.h2 = (uint16_t*)(ctx->ws + ctx->wso.ph2);
     a.a_part = (int64_t)kPrefillChunk * prefill_kmax(ctx->s);
     a.c = (float*)(ctx->ws + ctx->wso.pc);
     a.q = (float*)(ctx->ws + ctx->wso.pq);

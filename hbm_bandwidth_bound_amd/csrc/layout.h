@@ -229,10 +229,11 @@ KIE_HD int32_t prefill_nmax(const Shape& s) {
 // Workspace (bytes, 256-aligned pieces): exchange words, RoPE table [max_seq][hd/2] of (cos,sin),
 // per-stream base (in tiles, [nwg][8] + total), error word, norm gains [L][2][d] + final [d] (bf16),
 // trace counters, and the prompt-pass scratch (residual [chunk][d] fp32, GEMM input [2][chunk][kmax]
-// bf16, GEMM output [chunk][nmax] fp32, queries [chunk][nq hd] fp32, and for long contexts the
-// per-segment attention states [segments][chunk][nq][hd + 2] fp32).
+// bf16, down-projection input [2][chunk][F] bf16, split-K partial sums [chunk][nmax] fp32, queries
+// [chunk][nq hd] fp32, and for long contexts the per-segment attention states
+// [segments][chunk][nq][hd + 2] fp32).
 struct Workspace {
-  int64_t exch, rope, wbase, err, norms, trace, px, pa3, pc, pq, pattn, end;
+  int64_t exch, rope, wbase, err, norms, trace, px, pa3, ph2, pc, pq, pattn, end;
 };
 constexpr int kTraceWords = 32;  // per wave: cycle counters of a KIE_TRACE build
 KIE_HD int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
@@ -247,6 +248,7 @@ KIE_HD Workspace workspace_layout(const Shape& s) {
   w.trace = o; o = align256(o + (int64_t)s.nwg * kWaves * kTraceWords * 8);
   w.px = o; o = align256(o + (int64_t)kPrefillChunk * s.d * 4);
   w.pa3 = o; o = align256(o + (int64_t)2 * kPrefillChunk * prefill_kmax(s) * 2);
+  w.ph2 = o; o = align256(o + (int64_t)2 * kPrefillChunk * s.F * 2);
   w.pc = o; o = align256(o + (int64_t)kPrefillChunk * prefill_nmax(s) * 4);
   w.pq = o; o = align256(o + (int64_t)kPrefillChunk * s.qdim() * 4);
   w.pattn = o;

@@ -22,13 +22,25 @@ struct PrefillArgs {
   float* x;                  // [chunk][d] residual stream
   uint16_t* a3;              // [2][chunk][kmax] GEMM input in two bf16 parts
   int64_t a_part;            // elements between the parts
-  float* c;                  // [chunk][nmax] GEMM output
+  uint16_t* h2;              // [2][chunk][F] down-projection input in two bf16 parts
+  float* c;                  // [chunk][nmax] split-K partial sums
   float* q;                  // [chunk][nq * hd] rotated queries
   float* attn_part;          // [segments][chunk][nq][hd + 2] partial attention states
 };
 
+// What the GEMM does with its result C[i][n]:
+enum GemmEpilogue : int32_t {
+  EPI_STORE = 0,   // out[i][n] = (or +=) C
+  EPI_ROPE_KV = 1, // QKV: RoPE on each (A, B) pair of a query or key head; queries to q (fp32),
+                   // keys and values to the cache rows of positions p0 + i (bf16)
+  EPI_SWIGLU = 2,  // gate/up: h = silu(gate) * up into the two-part down-projection input h2
+};
+
 struct GemmStage {
   int32_t st, layer, K, N;
+  const uint16_t* in;    // [2][chunk][K] two-part input
+  int64_t in_part;       // elements between its parts
+  int32_t epi, p0;       // GemmEpilogue; position of row 0 (EPI_ROPE_KV)
   float* out;
   int32_t ldo, accumulate;
   int32_t splits, kper;  // K is cut into `splits` shares of kper each

@@ -148,7 +148,7 @@ __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillArgs a, GemmSt
       const int q = tid + jj * 256;
       const int p = q / (kGemmM * (kGemmKC / 8)), r = (q / (kGemmKC / 8)) % kGemmM, c = q % (kGemmKC / 8);
       const int32_t i = m0 + r;
-      av4[jj] = i < pc ? *(const uint4*)(a.a3 + p * a.a_part + (int64_t)i * g.K + kc + c * 8) : uint4{0u, 0u, 0u, 0u};
+      av4[jj] = i < pc ? *(const uint4*)(g.in + p * g.in_part + (int64_t)i * g.K + kc + c * 8) : uint4{0u, 0u, 0u, 0u};
     }
   };
 
@@ -183,23 +183,63 @@ __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillArgs a, GemmSt
       }
     }
   }
+  if (g.epi == EPI_STORE) {
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    if (!nvalid[nb]) continue;
+    for (int nb = 0; nb < NB; ++nb) {
+      if (!nvalid[nb]) continue;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int32_t i = m0 + mb * 16 + kg * 4 + r;
+          if (i >= pc) continue;
+          if (g.splits > 1) {  // partial sum of this share of K, summed by prefill_splitk_reduce_kernel
+            g.part[((int64_t)split * pc + i) * g.N + n[nb]] = acc[mb][nb][r];
+          } else {
+            float* dst = g.out + (int64_t)i * g.ldo + n[nb];
+            *dst = (g.accumulate ? *dst : 0.f) + acc[mb][nb][r];
+          }
+        }
+    }
+    return;
+  }
+  // pair epilogues: the other row of this lane's pair is in lane nl ^ 1
+  const Shape& s = a.s;
+  const int32_t half = s.hd / 2;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
+        const float v = acc[mb][nb][r];
+        const float u = __shfl_xor(v, 1, 64);
         const int32_t i = m0 + mb * 16 + kg * 4 + r;
-        if (i >= pc) continue;
-        if (g.splits > 1) {  // partial sum of this share of K, summed by prefill_splitk_reduce_kernel
-          g.part[((int64_t)split * pc + i) * g.N + n[nb]] = acc[mb][nb][r];
-        } else {
-          float* dst = g.out + (int64_t)i * g.ldo + n[nb];
-          *dst = (g.accumulate ? *dst : 0.f) + acc[mb][nb][r];
+        if (!nvalid[nb] || i >= pc) continue;
+        const float ya = sel ? u : v, yb = sel ? v : u;  // rows A and B of pair gp
+        const int32_t q = gp[nb];
+        if (g.epi == EPI_SWIGLU) {  // pair q = gate row q and up row q
+          if (sel == 0) {
+            const int64_t o = (int64_t)i * s.F + q;
+            split2((ya / (1.0f + expf(-ya))) * yb, a.h2 + o, a.h2 + (int64_t)kPrefillChunk * s.F + o);
+          }
+        } else {  // EPI_ROPE_KV: pair q = dims (e, e + hd/2) of head hs
+          const int32_t hs = q / half, e = q % half, pos = g.p0 + i;
+          float y = sel ? yb : ya;
+          if (hs < s.nq + s.nkv) {  // query and key heads are rotated
+            const float2 cs = a.rope[(int64_t)pos * half + e];
+            y = sel ? yb * cs.x + ya * cs.y : ya * cs.x - yb * cs.y;
+          }
+          const int32_t dim = e + sel * half;
+          if (hs < s.nq) {
+            a.q[(int64_t)i * s.qdim() + hs * s.hd + dim] = y;
+          } else {
+            const int kv = hs < s.nq + s.nkv ? 0 : 1;
+            const int32_t jh = kv == 0 ? hs - s.nq : hs - s.nq - s.nkv;
+            a.kv[kv_offset(s, g.layer, kv, jh, pos) + dim] = (uint16_t)f32_to_bf16(y);
+          }
         }
       }
-  }
 }
 
 // out (= or +=) the sum of the K shares' partial sums, in share order (the same every run)
@@ -225,39 +265,6 @@ __global__ void __launch_bounds__(256) prefill_splitk_reduce_kernel(GemmStage g,
       sum.w += o.w;
     }
     *dst = sum;
-  }
-}
-
-// ------------------------------------------------------------------------------------------
-// RoPE and the cache: QKV output (pair order) -> rotated queries Q[i][nq*hd] (fp32), and the
-// rotated keys and the values of positions pos0 + i written to the cache as bf16.
-// ------------------------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) prefill_rope_kv_kernel(PrefillArgs a, int32_t layer, int32_t p0, int32_t pc) {
-  const Shape& s = a.s;
-  const int32_t i = blockIdx.x;
-  if (i >= pc) return;
-  const int32_t pos = p0 + i, half = s.hd / 2;
-  const int32_t npairs = s.stage_pairs(ST_QKV);
-  const float* c = a.c + (int64_t)i * 2 * npairs;
-  for (int32_t gp = threadIdx.x; gp < npairs; gp += blockDim.x) {
-    const int32_t hs = gp / half, e = gp % half;
-    float ya = c[2 * gp], yb = c[2 * gp + 1];
-    if (hs < s.nq + s.nkv) {
-      const float2 cs = a.rope[(int64_t)pos * half + e];
-      const float ra = ya * cs.x - yb * cs.y, rb = yb * cs.x + ya * cs.y;
-      ya = ra;
-      yb = rb;
-    }
-    if (hs < s.nq) {
-      a.q[(int64_t)i * s.qdim() + hs * s.hd + e] = ya;
-      a.q[(int64_t)i * s.qdim() + hs * s.hd + e + half] = yb;
-    } else {
-      const int kv = hs < s.nq + s.nkv ? 0 : 1;
-      const int32_t j = kv == 0 ? hs - s.nq : hs - s.nq - s.nkv;
-      uint16_t* row = a.kv + kv_offset(s, layer, kv, j, pos);
-      row[e] = (uint16_t)f32_to_bf16(ya);
-      row[e + half] = (uint16_t)f32_to_bf16(yb);
-    }
   }
 }
 
@@ -516,40 +523,31 @@ __global__ void __launch_bounds__(HD) prefill_attn_merge_kernel(PrefillArgs a, i
 }
 
 // ------------------------------------------------------------------------------------------
-// SwiGLU of the gate/up output (pair f = gate row f, up row f) into the two-part input of the
-// down projection.
-// ------------------------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) prefill_swiglu_kernel(PrefillArgs a, int32_t pc) {
-  const int32_t i = blockIdx.x, F = a.s.F;
-  if (i >= pc) return;
-  const float* c = a.c + (int64_t)i * 2 * F;
-  for (int32_t f = threadIdx.x; f < F; f += 256) {
-    const float ya = c[2 * f], yb = c[2 * f + 1];
-    const float hv = (ya / (1.0f + expf(-ya))) * yb;
-    const int64_t o = (int64_t)i * F + f;
-    split2(hv, a.a3 + o, a.a3 + a.a_part + o);
-  }
-}
-
-// ------------------------------------------------------------------------------------------
 // The chunked prompt pass: positions p0 .. p0 + n - 1, every layer, K/V rows written to the cache.
 // ------------------------------------------------------------------------------------------
-static hipError_t gemm(const PrefillArgs& a, int st, int32_t layer, int32_t K, float* out, int32_t ldo, int accumulate,
-                       int32_t pc, hipStream_t stream) {
+// One GEMM of a layer stage. The QKV and gate/up products end in their pair epilogues; the O and
+// down products add into the residual stream.
+static hipError_t gemm(const PrefillArgs& a, int st, int32_t layer, int32_t p0, int32_t pc, hipStream_t stream) {
+  const Shape& s = a.s;
   GemmStage g;
   g.st = st;
   g.layer = layer;
-  g.K = K;
-  g.N = 2 * a.s.stage_pairs(st);
-  g.out = out;
-  g.ldo = ldo;
-  g.accumulate = accumulate;
+  g.K = s.stage_k(st);
+  g.N = 2 * s.stage_pairs(st);
+  g.in = st == ST_DN ? a.h2 : a.a3;
+  g.in_part = st == ST_DN ? (int64_t)kPrefillChunk * s.F : a.a_part;
+  g.epi = st == ST_QKV ? EPI_ROPE_KV : (st == ST_GU ? EPI_SWIGLU : EPI_STORE);
+  g.p0 = p0;
+  g.out = a.x;  // EPI_STORE: x += C
+  g.ldo = s.d;
+  g.accumulate = 1;
+  const int32_t K = g.K;
   // A GEMM with few output tiles (the O and down projections, N = d) splits K over up to 8
-  // blocks per tile so that about two blocks run per CU; the partial sums go to the GEMM output
-  // buffer, which these projections (they accumulate into the residual) leave unused.
+  // blocks per tile so that about two blocks run per CU; the partial sums go to the scratch
+  // buffer c, summed in a fixed order by prefill_splitk_reduce_kernel.
   const int32_t tiles = ((g.N + kGemmN - 1) / kGemmN) * ((pc + kGemmM - 1) / kGemmM);
   g.splits = 1;
-  if (out != a.c && g.N % 4 == 0)
+  if (g.epi == EPI_STORE && g.N % 4 == 0)
     while (g.splits < 8 && tiles * g.splits < 512 && K % (2 * g.splits * kGemmKC) == 0 &&
            2 * g.splits * g.N <= prefill_nmax(a.s))
       g.splits *= 2;
@@ -572,9 +570,8 @@ hipError_t launch_prefill(const PrefillArgs& a, int32_t p0, int32_t n, hipStream
     hipLaunchKernelGGL(prefill_embed_kernel, dim3(pc), dim3(256), 0, stream, a, c0, pc);
     for (int32_t l = 0; l < s.L; ++l) {
       hipLaunchKernelGGL(prefill_norm_split_kernel, dim3(pc), dim3(256), 0, stream, a, a.norms + (int64_t)l * 2 * s.d, pc);
-      hipError_t e = gemm(a, ST_QKV, l, s.d, a.c, 2 * s.stage_pairs(ST_QKV), 0, pc, stream);
+      hipError_t e = gemm(a, ST_QKV, l, pos, pc, stream);  // with RoPE; K/V rows to the cache
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(prefill_rope_kv_kernel, dim3(pc), dim3(256), 0, stream, a, l, pos, pc);
       // keys split into segments when the context is long, so that enough blocks run at once
       const int32_t nseg = (pos + pc + kPrefillAttnSeg - 1) / kPrefillAttnSeg;
       const dim3 ag((pc * s.group() + kFaRows - 1) / kFaRows, s.nkv, nseg);
@@ -591,12 +588,11 @@ hipError_t launch_prefill(const PrefillArgs& a, int32_t p0, int32_t n, hipStream
       } else {
         hipLaunchKernelGGL((prefill_fattn_kernel<64, false>), ag, dim3(256), 0, stream, a, l, pos, pc);
       }
-      if ((e = gemm(a, ST_O, l, s.qdim(), a.x, s.d, 1, pc, stream)) != hipSuccess) return e;
+      if ((e = gemm(a, ST_O, l, pos, pc, stream)) != hipSuccess) return e;
       hipLaunchKernelGGL(prefill_norm_split_kernel, dim3(pc), dim3(256), 0, stream, a,
                          a.norms + (int64_t)l * 2 * s.d + s.d, pc);
-      if ((e = gemm(a, ST_GU, l, s.d, a.c, 2 * s.F, 0, pc, stream)) != hipSuccess) return e;
-      hipLaunchKernelGGL(prefill_swiglu_kernel, dim3(pc), dim3(256), 0, stream, a, pc);
-      if ((e = gemm(a, ST_DN, l, s.F, a.x, s.d, 1, pc, stream)) != hipSuccess) return e;
+      if ((e = gemm(a, ST_GU, l, pos, pc, stream)) != hipSuccess) return e;  // SwiGLU into h2
+      if ((e = gemm(a, ST_DN, l, pos, pc, stream)) != hipSuccess) return e;
     }
   }
   return hipGetLastError();
