@@ -1321,6 +1321,9 @@ __device__ __forceinline__ void decode(Wk& K) {
     --rem;
     ++b;
   }
+  // a batch loaded into LDS past the launch's last step may still be in flight: the wave must
+  // not end (and give up its LDS) before that load has landed
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   K.tr.add(T_TOTAL, TR_NOW() - t_start);
   K.tr.flush(P.trace + ((int64_t)K.w * kWaves + K.v) * kTraceWords, K.lane);
 }
