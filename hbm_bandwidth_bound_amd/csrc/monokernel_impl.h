@@ -15,6 +15,8 @@
 // reducing. That batch is issued before the wave waits for the inputs of the next stage, so the
 // weight stream keeps flowing across every synchronisation point (the prefetch across
 // synchronisation points the pages call for); 64 KiB in flight per CU keep the HBM pipe busy.
+// Where LDS has room, the batch after that one also streams in across the O, gate/up and down
+// boundaries, straight into an 8 KiB LDS slot per wave (Wk::issue_x), with no registers held.
 // GEMV arithmetic: a lane holds 4 bf16 weights of each of two rows at the same k, so one 16-byte
 // LDS read of the fp32 stage input feeds 8 weights of two rows; the weights are widened to fp32
 // and accumulated with fp32 FMA (the unit has VALU to spare at the streaming rate).
