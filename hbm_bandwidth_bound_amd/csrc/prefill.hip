@@ -55,10 +55,8 @@ __global__ void __launch_bounds__(256) prefill_embed_kernel(PrefillArgs a, int32
 // RMSNorm of each row of X with gain g, written as the two-part GEMM input (row stride d).
 // The sum of squares runs in a fixed order (per-thread strided partials, then a fixed tree).
 // ------------------------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) prefill_norm_split_kernel(PrefillArgs a, const uint16_t* gain, int32_t pc) {
-  __shared__ float red[256];
-  const int32_t i = blockIdx.x, d = a.s.d;
-  if (i >= pc) return;
+__device__ __forceinline__ void norm_split_row(const PrefillArgs& a, const uint16_t* gain, int32_t i, float* red) {
+  const int32_t d = a.s.d;
   const float* xr = a.x + (int64_t)i * d;
   float ss = 0.f;
   for (int32_t e = threadIdx.x; e < d; e += 256) ss = fmaf(xr[e], xr[e], ss);
@@ -74,6 +72,11 @@ __global__ void __launch_bounds__(256) prefill_norm_split_kernel(PrefillArgs a, 
     const int64_t o = (int64_t)i * d + e;
     split2(u, a.a3 + o, a.a3 + a.a_part + o);
   }
+}
+__global__ void __launch_bounds__(256) prefill_norm_split_kernel(PrefillArgs a, const uint16_t* gain, int32_t pc) {
+  __shared__ float red[256];
+  if ((int32_t)blockIdx.x >= pc) return;
+  norm_split_row(a, gain, blockIdx.x, red);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -240,6 +243,34 @@ __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillArgs a, GemmSt
           }
         }
       }
+}
+
+// Row i of the residual: x += the K shares' partial sums (in share order), then the RMSNorm of
+// the new row as the next GEMM's two-part input.
+__global__ void __launch_bounds__(256) prefill_splitk_reduce_norm_kernel(PrefillArgs a, GemmStage g, const uint16_t* gain,
+                                                                          int32_t pc) {
+  __shared__ float red[256];
+  const int32_t i = blockIdx.x;
+  if (i >= pc) return;
+  float* xr = g.out + (int64_t)i * g.ldo;
+  for (int32_t n4 = threadIdx.x; n4 < g.N / 4; n4 += 256) {
+    float4 sum = *(const float4*)(g.part + (int64_t)i * g.N + 4 * n4);
+    for (int32_t sp = 1; sp < g.splits; ++sp) {
+      const float4 v = *(const float4*)(g.part + ((int64_t)sp * pc + i) * g.N + 4 * n4);
+      sum.x += v.x;
+      sum.y += v.y;
+      sum.z += v.z;
+      sum.w += v.w;
+    }
+    float4 o = *(const float4*)(xr + 4 * n4);
+    o.x += sum.x;
+    o.y += sum.y;
+    o.z += sum.z;
+    o.w += sum.w;
+    *(float4*)(xr + 4 * n4) = o;
+  }
+  __syncthreads();  // the norm reads the row by other columns per thread
+  norm_split_row(a, gain, i, red);
 }
 
 // out (= or +=) the sum of the K shares' partial sums, in share order (the same every run)
@@ -526,8 +557,10 @@ __global__ void __launch_bounds__(HD) prefill_attn_merge_kernel(PrefillArgs a, i
 // The chunked prompt pass: positions p0 .. p0 + n - 1, every layer, K/V rows written to the cache.
 // ------------------------------------------------------------------------------------------
 // One GEMM of a layer stage. The QKV and gate/up products end in their pair epilogues; the O and
-// down products add into the residual stream.
-static hipError_t gemm(const PrefillArgs& a, int st, int32_t layer, int32_t p0, int32_t pc, hipStream_t stream) {
+// down products add into the residual stream, followed by the RMSNorm with gain norm_after when
+// it is given (written as the next GEMM's input).
+static hipError_t gemm(const PrefillArgs& a, int st, int32_t layer, int32_t p0, int32_t pc, hipStream_t stream,
+                       const uint16_t* norm_after = nullptr) {
   const Shape& s = a.s;
   GemmStage g;
   g.st = st;
@@ -554,10 +587,15 @@ static hipError_t gemm(const PrefillArgs& a, int st, int32_t layer, int32_t p0, 
   g.kper = K / g.splits;
   g.part = a.c;
   hipLaunchKernelGGL(prefill_gemm_kernel, dim3(tiles * g.splits), dim3(256), 0, stream, a, g, pc);
-  if (g.splits > 1) {
-    const int64_t n4 = (int64_t)pc * (g.N / 4);
-    hipLaunchKernelGGL(prefill_splitk_reduce_kernel, dim3((unsigned)((n4 + 255) / 256 < 2048 ? (n4 + 255) / 256 : 2048)),
-                       dim3(256), 0, stream, g, pc);
+  if (g.splits > 1 && norm_after) {
+    hipLaunchKernelGGL(prefill_splitk_reduce_norm_kernel, dim3(pc), dim3(256), 0, stream, a, g, norm_after, pc);
+  } else {
+    if (g.splits > 1) {
+      const int64_t n4 = (int64_t)pc * (g.N / 4);
+      hipLaunchKernelGGL(prefill_splitk_reduce_kernel,
+                         dim3((unsigned)((n4 + 255) / 256 < 2048 ? (n4 + 255) / 256 : 2048)), dim3(256), 0, stream, g, pc);
+    }
+    if (norm_after) hipLaunchKernelGGL(prefill_norm_split_kernel, dim3(pc), dim3(256), 0, stream, a, norm_after, pc);
   }
   return hipGetLastError();
 }
@@ -568,8 +606,9 @@ hipError_t launch_prefill(const PrefillArgs& a, int32_t p0, int32_t n, hipStream
     const int32_t pc = n - c0 < kPrefillChunk ? n - c0 : kPrefillChunk;
     const int32_t pos = p0 + c0;
     hipLaunchKernelGGL(prefill_embed_kernel, dim3(pc), dim3(256), 0, stream, a, c0, pc);
+    hipLaunchKernelGGL(prefill_norm_split_kernel, dim3(pc), dim3(256), 0, stream, a, a.norms, pc);
     for (int32_t l = 0; l < s.L; ++l) {
-      hipLaunchKernelGGL(prefill_norm_split_kernel, dim3(pc), dim3(256), 0, stream, a, a.norms + (int64_t)l * 2 * s.d, pc);
+      // the attention RMSNorm of layer l is in a3 here (after the embedding, or layer l-1's down)
       hipError_t e = gemm(a, ST_QKV, l, pos, pc, stream);  // with RoPE; K/V rows to the cache
       if (e != hipSuccess) return e;
       // keys split into segments when the context is long, so that enough blocks run at once
@@ -588,11 +627,11 @@ hipError_t launch_prefill(const PrefillArgs& a, int32_t p0, int32_t n, hipStream
       } else {
         hipLaunchKernelGGL((prefill_fattn_kernel<64, false>), ag, dim3(256), 0, stream, a, l, pos, pc);
       }
-      if ((e = gemm(a, ST_O, l, pos, pc, stream)) != hipSuccess) return e;
-      hipLaunchKernelGGL(prefill_norm_split_kernel, dim3(pc), dim3(256), 0, stream, a,
-                         a.norms + (int64_t)l * 2 * s.d + s.d, pc);
+      if ((e = gemm(a, ST_O, l, pos, pc, stream, a.norms + (int64_t)l * 2 * s.d + s.d)) != hipSuccess) return e;
       if ((e = gemm(a, ST_GU, l, pos, pc, stream)) != hipSuccess) return e;  // SwiGLU into h2
-      if ((e = gemm(a, ST_DN, l, pos, pc, stream)) != hipSuccess) return e;
+      if ((e = gemm(a, ST_DN, l, pos, pc, stream, l + 1 < s.L ? a.norms + (int64_t)(l + 1) * 2 * s.d : nullptr)) !=
+          hipSuccess)
+        return e;
     }
   }
   return hipGetLastError();
