@@ -40,6 +40,7 @@ struct kie_ctx {
   int32_t ring_cap;
   int64_t ring_count;      // tokens streamed to it so far
   int64_t timeout_ticks;
+  uint32_t skew;           // kie_set_skew
   std::vector<int64_t> wbase_host;
   std::string last_error;
 };
@@ -282,6 +283,7 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
   c->ring_cap = 0;
   c->ring_count = 0;
   c->timeout_ticks = 200000000;  // 2 s per wait
+  c->skew = 0;
   c->wbase_host.resize((size_t)s.nwg * kWaves + 1);
   int64_t acc = 0;
   for (int w = 0; w < s.nwg; ++w) {
@@ -481,6 +483,7 @@ static kie_status launch(kie_ctx* ctx, const int32_t* first, int32_t n, const in
   P.temperature = top_k > 1 ? smp->temperature : 1.0f;
   P.seed = smp ? smp->seed : 0;
   P.timeout_ticks = ctx->timeout_ticks;
+  P.skew = ctx->skew;
   void* args[] = {&P};
   const void* fn = (const void*)(lm_last_only ? ctx->prompt_kernel : ctx->kernel);
   HIP_TRY(&ctx->last_error,
@@ -570,6 +573,16 @@ kie_status kie_stream_read(const void* src, size_t bytes, uint32_t* sink_dev, vo
   if (query_cus(&n, nullptr) != KIE_OK) return KIE_ERR_HIP;
   return launch_stream_read(src, (int64_t)bytes, sink_dev, n, (hipStream_t)hip_stream) == hipSuccess ? KIE_OK
                                                                                                        : KIE_ERR_HIP;
+}
+
+kie_status kie_set_skew(kie_ctx* ctx, uint32_t level) {
+  if (!ctx) return KIE_ERR_INVALID_ARG;
+  if (level > 64) {
+    set_err(&ctx->last_error, "skew level %u is above 64", level);
+    return KIE_ERR_INVALID_ARG;
+  }
+  ctx->skew = level;
+  return KIE_OK;
 }
 
 int64_t kie_trace_offset(const kie_config* cfg) {

@@ -41,6 +41,8 @@ struct KParams {
   float temperature;         // top-k: logits are divided by it (> 0)
   uint64_t seed;             // top-k: random stream of the draw
   int64_t timeout_ticks;     // per wait, in s_memrealtime ticks (100 MHz)
+  uint32_t skew;             // > 0: each WG idles a pseudo-random 0..skew-1 x ~3.4 us before
+                             // every stage boundary (protocol stress; results must not change)
 };
 
 typedef void (*KernelFn)(KParams);

@@ -1060,6 +1060,14 @@ __device__ __forceinline__ void decode(Wk& K) {
 
   auto boundary = [&]() {
     while (rem == 0 && !done) {
+      if (P.skew) {  // a WG-uniform, deterministic delay per (WG, step, layer, boundary)
+        uint32_t hsh = (uint32_t)K.w * 0x9E3779B1u ^ (uint32_t)step * 0x85EBCA77u ^ (uint32_t)l * 0xC2B2AE3Du ^
+                       (uint32_t)bnd * 0x27D4EB2Fu;
+        hsh ^= hsh >> 15;
+        hsh *= 0x2C1B3C6Du;
+        hsh ^= hsh >> 12;
+        for (uint32_t i = hsh % P.skew; i > 0; --i) __builtin_amdgcn_s_sleep(127);
+      }
       const uint64_t tb = TR_NOW();
       const int bnd_run = bnd;
       switch (bnd) {

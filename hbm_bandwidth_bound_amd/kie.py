@@ -80,6 +80,8 @@ def load() -> C.CDLL:
     lib.kie_reset.restype = C.c_int32
     lib.kie_set_token_stream.argtypes = [vp, vp, C.c_int32]
     lib.kie_set_token_stream.restype = C.c_int32
+    lib.kie_set_skew.argtypes = [vp, C.c_uint32]
+    lib.kie_set_skew.restype = C.c_int32
     lib.kie_set_position.argtypes = [vp, C.c_int32]
     lib.kie_set_position.restype = C.c_int32
     lib.kie_position.argtypes = [vp]
@@ -184,6 +186,10 @@ class Engine:
 
     def set_position(self, pos: int):
         _check(self.lib, self.lib.kie_set_position(self.ctx, int(pos)), self.ctx)
+
+    def set_skew(self, level: int):
+        """Protocol stress (tests): workgroups idle pseudo-random amounts before stage boundaries."""
+        _check(self.lib, self.lib.kie_set_skew(self.ctx, int(level)), self.ctx)
 
     def set_token_stream(self, ring=None):
         """ring: pinned host int32 tensor of 1 + capacity elements (None stops streaming)."""

@@ -36,6 +36,14 @@ int32_t kie_stream_read(const void* src, size_t bytes, uint32_t* sink_dev, void*
  * the end of each decode launch (zeros otherwise); -1 for an invalid configuration. */
 int64_t kie_trace_offset(const kie_config* cfg);
 
+/* Protocol stress for tests: with level > 0, every workgroup of the decode and prompt kernels
+ * idles a pseudo-random 0 .. level-1 times ~3.4 us before each stage boundary, a different amount
+ * per (workgroup, step, layer, boundary). Workgroups then reach each exchange out of their usual
+ * order; tokens and logits must be bitwise the same as with level 0, which is the default and
+ * adds no work. Applies to launches enqueued after the call. Returns KIE_OK, or
+ * KIE_ERR_INVALID_ARG for a null context or a level above 64. */
+kie_status kie_set_skew(kie_ctx* ctx, uint32_t level);
+
 #ifdef __cplusplus
 }
 #endif

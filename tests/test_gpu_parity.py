@@ -117,6 +117,35 @@ def test_tiny_context_lengths(torch_cuda, tiny, oracle_lib, P, N):
     eng.close()
 
 
+def test_skewed_workgroups_give_bitwise_identical_results(torch_cuda, tiny):
+    """Exchange protocol stress on the GPU: with every workgroup idling a pseudo-random time before
+    each stage boundary (kie_set_skew), the workgroups reach each exchange in other orders; the
+    prompt pass, greedy decode and top-k decode must still give bitwise the same tokens and
+    logits as without."""
+    from hbm_bandwidth_bound_amd.kie import Engine, sampling
+    cfg, w, wd = tiny
+    P, N = 40, 10
+    say(f"[tiny] skewed workgroups: prefill {P} + decode {N}, greedy and top-k")
+    prompt = synth.prompt_ids(P, cfg.vocab_size, 21)
+    eng = Engine(cfg, wd, P + N)
+    smp = sampling(50, 0.8, 2)
+    ref = run_gpu(torch_cuda, eng, prompt, N, cfg.vocab_size)
+    eng.reset()
+    ref_k = run_gpu_topk(torch_cuda, eng, prompt, N, cfg.vocab_size, smp)
+    for level in (4, 16):
+        eng.reset()
+        eng.set_skew(level)
+        got = run_gpu(torch_cuda, eng, prompt, N, cfg.vocab_size)
+        eng.reset()
+        got_k = run_gpu_topk(torch_cuda, eng, prompt, N, cfg.vocab_size, smp)
+        eng.set_skew(0)
+        for a, b in ((ref, got), (ref_k, got_k)):
+            assert a[0] == b[0] and np.array_equal(a[1], b[1]), f"skew {level}: prompt pass differs"
+            assert np.array_equal(a[2], b[2]) and np.array_equal(a[3], b[3]), f"skew {level}: decode differs"
+        say(f"  skew {level}: identical")
+    eng.close()
+
+
 def test_forced_tokens_follow_the_given_stream(torch_cuda, tiny, oracle_lib):
     """Teacher forcing: the step inputs are the forced ids; the chosen tokens are still written."""
     import torch
