@@ -272,7 +272,10 @@ struct Wk {
   }
   // hand the next batch of the stream to the caller and keep the one after it in flight
   __device__ __forceinline__ void take(v4u* cur) {
-    if (xnext) {  // the batch in the LDS slot; only nxt's 8 loads were issued after it
+    if (xnext) {
+      // The batch in the LDS slot. At least nxt's kBatch loads were issued after its loads, and
+      // the counter drains in issue order, so with at most kBatch operations outstanding the slot
+      // is filled.
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kBatch) : "memory");
       const uint8_t* xs = L.xb + (size_t)v * kBatch * kTileBytes + lane * 16;
 #pragma unroll
