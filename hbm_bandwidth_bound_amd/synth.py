@@ -18,7 +18,8 @@ RMSNorm gains are 1.0 (see ``norm_init``). Prompt ids are uniform in ``[0, V)`` 
 multiply-shift of a hashed counter.
 
 The shapes are those of the decoder configurations: tiny (2 layers, d 256), the ~1.6B headline
-model, the ~8B model, and the 128-expert MoE model (whose decode path is not built yet).
+model, the ~8B model, and the 128-expert mixture-of-experts model, plus two small
+mixture-of-experts shapes and a two-layer cut of the full one for the parity tests.
 """
 from __future__ import annotations
 
@@ -83,7 +84,16 @@ M8B = ModelConfig("8b", 32, 4096, 32, 8, 128, 14336, 128256)
 MOE = ModelConfig("moe", 48, 2048, 32, 4, 128, 0, 151936, n_experts=128, n_experts_active=8,
                   expert_ffn_dim=768)
 
-MODELS: Dict[str, ModelConfig] = {m.name: m for m in (TINY, M1_6B, M8B, MOE)}
+# Mixture-of-experts shapes for tests: 8 query heads on one KV head (the group of the full model),
+# 1-tile expert rows (tiny) and 3-tile expert rows whose down-projection units span experts (small),
+# and the full model's layer shape cut to two layers.
+TINY_MOE = ModelConfig("tiny-moe", 2, 256, 8, 1, 128, 0, 4096, n_experts=16, n_experts_active=4,
+                       expert_ffn_dim=256)
+SMALL_MOE = ModelConfig("small-moe", 2, 512, 8, 1, 128, 0, 4096, n_experts=32, n_experts_active=8,
+                        expert_ffn_dim=768)
+MOE_2L = MOE.scaled(name="moe-2l", n_layers=2)
+
+MODELS: Dict[str, ModelConfig] = {m.name: m for m in (TINY, M1_6B, M8B, MOE, TINY_MOE, SMALL_MOE, MOE_2L)}
 
 WORKLOADS: Dict[str, Workload] = {
     "tiny": Workload("tiny", TINY, 64, 32),
@@ -91,6 +101,7 @@ WORKLOADS: Dict[str, Workload] = {
     "1.6b-1k-topk": Workload("1.6b-1k-topk", M1_6B, 1024, 512, top_k=50, temperature=0.8),
     "1.6b-32k": Workload("1.6b-32k", M1_6B, 32768, 256),
     "8b-2k": Workload("8b-2k", M8B, 2048, 256),
+    "moe-1k": Workload("moe-1k", MOE, 1024, 256),
 }
 
 # Tensor numbering for the weight generator: 0 embed, 1 lm_head, then per layer l
@@ -98,11 +109,26 @@ WORKLOADS: Dict[str, Workload] = {
 LAYER_MATS = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
 
 
+# Mixture-of-experts layers: the router [E][d] and the experts' matrices stacked per layer,
+# gate and up [E][Fe][d], down [E][d][Fe]. The stacked matrices take the tensor numbers of w_gate,
+# w_up and w_down; the router of layer l is tensor ROUTER_TENSOR + l.
+MOE_MATS = ("w_router", "moe_gate", "moe_up", "moe_down")
+ROUTER_TENSOR = 0x40000000
+
+
+def layer_mats(cfg: ModelConfig):
+    if cfg.n_experts:
+        return ("wq", "wk", "wv", "wo") + MOE_MATS
+    return LAYER_MATS
+
+
 def mat_shape(cfg: ModelConfig, name: str):
     d, q, kv, f = cfg.d_model, cfg.q_dim, cfg.kv_dim, cfg.ffn_dim
+    E, Fe = cfg.n_experts, cfg.expert_ffn_dim
     return {"wq": (q, d), "wk": (kv, d), "wv": (kv, d), "wo": (d, q), "w_gate": (f, d),
             "w_up": (f, d), "w_down": (d, f), "embed": (cfg.vocab_size, d),
-            "lm_head": (cfg.vocab_size, d)}[name]
+            "lm_head": (cfg.vocab_size, d), "w_router": (E, d), "moe_gate": (E, Fe, d),
+            "moe_up": (E, Fe, d), "moe_down": (E, d, Fe)}[name]
 
 
 def tensor_index(name: str, layer: Optional[int] = None) -> int:
@@ -110,7 +136,10 @@ def tensor_index(name: str, layer: Optional[int] = None) -> int:
         return 0
     if name == "lm_head":
         return 1
-    return 2 + 7 * layer + LAYER_MATS.index(name)
+    if name == "w_router":
+        return ROUTER_TENSOR + layer
+    alias = {"moe_gate": "w_gate", "moe_up": "w_up", "moe_down": "w_down"}
+    return 2 + 7 * layer + LAYER_MATS.index(alias.get(name, name))
 
 
 # ----------------------------------------------------------------------------------------------
@@ -232,7 +261,7 @@ def make_weights_np(cfg: ModelConfig, seed: int = 0) -> Dict[str, object]:
     }
     for name in ("attn_norm", "ffn_norm"):
         w[name] = [norm_init(cfg) for _ in range(cfg.n_layers)]
-    for name in LAYER_MATS:
+    for name in layer_mats(cfg):
         w[name] = [_weights_bits_np(mat_shape(cfg, name), seed, tensor_index(name, l))
                    for l in range(cfg.n_layers)]
     return w
@@ -249,7 +278,7 @@ def make_weights_torch(cfg: ModelConfig, seed: int = 0, device="cuda") -> Dict[s
     for name in ("attn_norm", "ffn_norm"):
         w[name] = [torch.full((cfg.d_model,), 0x3F80, dtype=torch.int16, device=device)
                    for _ in range(cfg.n_layers)]
-    for name in LAYER_MATS:
+    for name in layer_mats(cfg):
         w[name] = [_weights_bits_torch(mat_shape(cfg, name), seed, tensor_index(name, l), device)
                    for l in range(cfg.n_layers)]
     return w

@@ -15,7 +15,8 @@
  *   angles p * theta^(-2i/hd) computed in fp64; grouped-query attention where query head h reads
  *   KV head h / (n_heads / n_kv_heads); causal softmax with scale 1/sqrt(hd); SwiGLU FFN
  *   silu(Wg u) * (Wu u); K (after RoPE) and V rounded to bf16 (round-to-nearest-even) when written
- *   to the cache.
+ *   to the cache. A mixture-of-experts layer replaces the FFN by a router and n_experts SwiGLU
+ *   experts of which n_experts_active run per token (oc_moe_route, oc_moe_ffn).
  *
  * Precision: bf16 weights are widened exactly to fp32; activations and dot products are fp32 with
  * one accumulator per output summed in ascending index order (oc_set_gemv_order(1) sums the
@@ -40,21 +41,35 @@ typedef struct {
   int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab_size;
   float rms_eps, rope_theta;
   int32_t max_seq;
+  int32_t n_experts, n_experts_active, expert_ffn_dim; /* n_experts == 0: dense feed-forward */
 } oc_config;
 
-/* All matrices row-major [out][in], bf16 bit patterns. Per-layer arrays hold n_layers pointers. */
+/* All matrices row-major [out][in], bf16 bit patterns. Per-layer arrays hold n_layers pointers.
+ * Mixture-of-experts layers (n_experts > 0) use w_router[l] [E][d] and, per layer, the experts'
+ * matrices stacked: moe_gate[l] and moe_up[l] [E][Fe][d], moe_down[l] [E][d][Fe]; w_gate, w_up and
+ * w_down are then unused. */
 typedef struct {
   const uint16_t *embed, *final_norm, *lm_head;
   const uint16_t *const *attn_norm, *const *wq, *const *wk, *const *wv, *const *wo;
   const uint16_t *const *ffn_norm, *const *w_gate, *const *w_up, *const *w_down;
+  const uint16_t *const *w_router, *const *moe_gate, *const *moe_up, *const *moe_down;
 } oc_weights;
 
 static int g_threads = 1;
 static int g_gemv_desc = 0;
+/* optional log of the router logits of oc_step: [max_pos][n_layers][n_experts] fp32 */
+static float* g_route_log = NULL;
+static int g_route_log_pos = 0;
 
 void oc_set_threads(int n) { g_threads = n < 1 ? 1 : n; }
 void oc_set_gemv_order(int descending) { g_gemv_desc = descending ? 1 : 0; }
 int oc_get_threads(void) { return g_threads; }
+/* Record the router logits of every mixture-of-experts layer of oc_step at positions < max_pos
+ * into buf ([max_pos][n_layers][n_experts]); NULL stops recording. */
+void oc_set_route_log(float* buf, int max_pos) {
+  g_route_log = buf;
+  g_route_log_pos = max_pos;
+}
 
 /* ------------------------------------------------------------------ scalar helpers */
 
@@ -212,6 +227,72 @@ int oc_topk_sample(const float* logits, int n, int k, float temperature, uint64_
   return chosen;
 }
 
+/* ------------------------------------------------------------------ mixture of experts */
+
+/* Router of a mixture-of-experts layer (the pages: only the routed experts' weights are read per
+ * token, so bandwidth follows the active parameters -- aikraft.ru «3000 токенов в секунду…», §02;
+ * agentlenshq.com, 《突破内存墙…》, opening section). The pages fix no router; the reading here:
+ * p = softmax(z) over all E router logits (fp64), the A experts with the largest z (ties -> lower
+ * index, i.e. the A largest p) in descending order, and their weights renormalised to sum to 1:
+ * w_i = p_i / sum of the selected p. Writes idx[A] and w[A] (fp64); returns 0, or -1 on bad sizes. */
+int oc_moe_route(const float* z, int E, int A, int* idx, double* w) {
+  if (E < 1 || A < 1 || A > E) return -1;
+  double m = -INFINITY;
+  for (int e = 0; e < E; e++)
+    if ((double)z[e] > m) m = (double)z[e];
+  double* p = (double*)malloc(sizeof(double) * (size_t)E);
+  double Z = 0.0;
+  for (int e = 0; e < E; e++) {
+    p[e] = exp((double)z[e] - m);
+    Z += p[e];
+  }
+  for (int e = 0; e < E; e++) p[e] /= Z;
+  char* used = (char*)calloc((size_t)E, 1);
+  double S = 0.0;
+  for (int j = 0; j < A; j++) {
+    int b = -1;
+    for (int e = 0; e < E; e++) {
+      if (used[e]) continue;
+      if (b < 0 || z[e] > z[b]) b = e;
+    }
+    used[b] = 1;
+    idx[j] = b;
+    S += p[b];
+  }
+  for (int j = 0; j < A; j++) w[j] = p[idx[j]] / S;
+  free(p);
+  free(used);
+  return 0;
+}
+
+/* Feed-forward output of a mixture-of-experts layer for the normalised input u[d]:
+ * y = sum over the routed experts i (in rank order) of (float)w_i * down_i(silu(gate_i u) * up_i u),
+ * accumulated in fp32. Writes y[d]; z_out[E] (if not NULL) receives the router logits. */
+void oc_moe_ffn(const oc_config* c, const oc_weights* w, int l, const float* u, float* y, float* z_out) {
+  const int d = c->d_model, E = c->n_experts, A = c->n_experts_active, Fe = c->expert_ffn_dim;
+  float* z = (float*)malloc(sizeof(float) * (size_t)E);
+  int* idx = (int*)malloc(sizeof(int) * (size_t)A);
+  double* wt = (double*)malloc(sizeof(double) * (size_t)A);
+  float* g = (float*)malloc(sizeof(float) * (size_t)Fe);
+  float* up = (float*)malloc(sizeof(float) * (size_t)Fe);
+  float* t = (float*)malloc(sizeof(float) * (size_t)d);
+  oc_gemv(w->w_router[l], u, z, E, d);
+  oc_moe_route(z, E, A, idx, wt);
+  for (int i = 0; i < d; i++) y[i] = 0.0f;
+  for (int j = 0; j < A; j++) {
+    const int e = idx[j];
+    oc_gemv(w->moe_gate[l] + (size_t)e * Fe * d, u, g, Fe, d);
+    oc_gemv(w->moe_up[l] + (size_t)e * Fe * d, u, up, Fe, d);
+    for (int i = 0; i < Fe; i++) g[i] = oc_silu(g[i]) * up[i];
+    oc_gemv(w->moe_down[l] + (size_t)e * d * Fe, g, t, d, Fe);
+    const float wj = (float)wt[j];
+    for (int i = 0; i < d; i++) y[i] += wj * t[i];
+  }
+  if (z_out)
+    for (int e = 0; e < E; e++) z_out[e] = z[e];
+  free(z); free(idx); free(wt); free(g); free(up); free(t);
+}
+
 /* ------------------------------------------------------------------ one decode step */
 
 /* KV cache of the oracle: K and V planes, each [n_layers][n_kv_heads][max_seq][head_dim] bf16. */
@@ -260,10 +341,16 @@ int oc_step(const oc_config* c, const oc_weights* w, uint16_t* kc, uint16_t* vc,
     for (int i = 0; i < d; i++) x[i] += t[i];
     /* feed-forward block */
     oc_rmsnorm(x, w->ffn_norm[l], u, d, c->rms_eps);
-    oc_gemv(w->w_gate[l], u, g, F, d);
-    oc_gemv(w->w_up[l], u, up, F, d);
-    for (int i = 0; i < F; i++) g[i] = oc_silu(g[i]) * up[i];
-    oc_gemv(w->w_down[l], g, t, d, F);
+    if (c->n_experts > 0) {
+      float* zl = g_route_log && pos < g_route_log_pos
+                      ? g_route_log + ((size_t)pos * c->n_layers + l) * c->n_experts : NULL;
+      oc_moe_ffn(c, w, l, u, t, zl);
+    } else {
+      oc_gemv(w->w_gate[l], u, g, F, d);
+      oc_gemv(w->w_up[l], u, up, F, d);
+      for (int i = 0; i < F; i++) g[i] = oc_silu(g[i]) * up[i];
+      oc_gemv(w->w_down[l], g, t, d, F);
+    }
     for (int i = 0; i < d; i++) x[i] += t[i];
   }
   oc_rmsnorm(x, w->final_norm, u, d, c->rms_eps);
@@ -349,6 +436,36 @@ int oc_full_recompute(const oc_config* c, const oc_weights* w, const int* tokens
       for (int i = 0; i < d; i++) X[(size_t)r * d + i] += T[(size_t)r * d + i];
     }
     for (int r = 0; r < n; r++) oc_rmsnorm(X + (size_t)r * d, w->ffn_norm[l], U + (size_t)r * d, d, c->rms_eps);
+    if (c->n_experts > 0) {
+      /* grouped by expert: route every row, then run each expert over the rows sent to it and add
+       * its weighted output to those rows (the rank-order sum of oc_step, in another order) */
+      const int E = c->n_experts, A = c->n_experts_active, Fe = c->expert_ffn_dim;
+      float* Z = (float*)malloc(sizeof(float) * (size_t)E);
+      int* SI = (int*)malloc(sizeof(int) * (size_t)n * A);
+      double* SW = (double*)malloc(sizeof(double) * (size_t)n * A);
+      float* ge = (float*)malloc(sizeof(float) * (size_t)Fe);
+      float* ue = (float*)malloc(sizeof(float) * (size_t)Fe);
+      float* te = (float*)malloc(sizeof(float) * (size_t)d);
+      float* Y = (float*)calloc((size_t)n * d, sizeof(float));
+      for (int r = 0; r < n; r++) {
+        oc_gemv(w->w_router[l], U + (size_t)r * d, Z, E, d);
+        oc_moe_route(Z, E, A, SI + (size_t)r * A, SW + (size_t)r * A);
+      }
+      for (int e = 0; e < E; e++)
+        for (int r = 0; r < n; r++)
+          for (int j = 0; j < A; j++) {
+            if (SI[(size_t)r * A + j] != e) continue;
+            oc_gemv(w->moe_gate[l] + (size_t)e * Fe * d, U + (size_t)r * d, ge, Fe, d);
+            oc_gemv(w->moe_up[l] + (size_t)e * Fe * d, U + (size_t)r * d, ue, Fe, d);
+            for (int i = 0; i < Fe; i++) ge[i] = oc_silu(ge[i]) * ue[i];
+            oc_gemv(w->moe_down[l] + (size_t)e * d * Fe, ge, te, d, Fe);
+            const float wj = (float)SW[(size_t)r * A + j];
+            for (int i = 0; i < d; i++) Y[(size_t)r * d + i] += wj * te[i];
+          }
+      for (size_t i = 0; i < (size_t)n * d; i++) X[i] += Y[i];
+      free(Z); free(SI); free(SW); free(ge); free(ue); free(te); free(Y);
+      continue;
+    }
     for (int r = 0; r < n; r++) {
       oc_gemv(w->w_gate[l], U + (size_t)r * d, G + (size_t)r * F, F, d);
       oc_gemv(w->w_up[l], U + (size_t)r * d, Up + (size_t)r * F, F, d);

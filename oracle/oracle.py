@@ -69,6 +69,12 @@ def _load():
         lib.oc_step.restype = C.c_int
         lib.oc_full_recompute.argtypes = [C.c_void_p, C.c_void_p, i32p, C.c_int, f32p]
         lib.oc_full_recompute.restype = C.c_int
+        lib.oc_moe_route.argtypes = [f32p, C.c_int, C.c_int, i32p, f64p]
+        lib.oc_moe_route.restype = C.c_int
+        lib.oc_moe_ffn.argtypes = [C.c_void_p, C.c_void_p, C.c_int, f32p, f32p, f32p]
+        lib.oc_moe_ffn.restype = None
+        lib.oc_set_route_log.argtypes = [f32p, C.c_int]
+        lib.oc_set_route_log.restype = None
         _lib = lib
     return _lib
 
@@ -144,6 +150,16 @@ def topk_sample(logits: np.ndarray, k: int, temperature: float, seed: int, pos: 
     return int(tok), idx, p, float(u.value)
 
 
+def moe_route(z: np.ndarray, active: int):
+    """Router of a mixture-of-experts layer: (expert ids [A] in rank order, weights [A] fp64)."""
+    z = np.ascontiguousarray(z, dtype=np.float32)
+    idx = np.empty(active, dtype=np.int32)
+    w = np.empty(active, dtype=np.float64)
+    if _load().oc_moe_route(_p(z, C.c_float), len(z), int(active), _p(idx, C.c_int32), _p(w, C.c_double)) != 0:
+        raise ValueError("bad router sizes")
+    return idx, w
+
+
 def splitmix64(x: int) -> int:
     return int(_load().oc_splitmix64(x & (2**64 - 1)))
 
@@ -164,7 +180,8 @@ class _Cfg(C.Structure):
     _fields_ = [("n_layers", C.c_int32), ("d_model", C.c_int32), ("n_heads", C.c_int32),
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn_dim", C.c_int32),
                 ("vocab_size", C.c_int32), ("rms_eps", C.c_float), ("rope_theta", C.c_float),
-                ("max_seq", C.c_int32)]
+                ("max_seq", C.c_int32), ("n_experts", C.c_int32), ("n_experts_active", C.c_int32),
+                ("expert_ffn_dim", C.c_int32)]
 
 
 _PP = C.POINTER(C.POINTER(C.c_uint16))
@@ -174,17 +191,20 @@ class _W(C.Structure):
     _fields_ = [("embed", C.POINTER(C.c_uint16)), ("final_norm", C.POINTER(C.c_uint16)),
                 ("lm_head", C.POINTER(C.c_uint16)), ("attn_norm", _PP), ("wq", _PP), ("wk", _PP),
                 ("wv", _PP), ("wo", _PP), ("ffn_norm", _PP), ("w_gate", _PP), ("w_up", _PP),
-                ("w_down", _PP)]
+                ("w_down", _PP), ("w_router", _PP), ("moe_gate", _PP), ("moe_up", _PP), ("moe_down", _PP)]
 
 
 _LAYER_KEYS = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")
+_MOE_KEYS = ("w_router", "moe_gate", "moe_up", "moe_down")
 
 
 class OracleModel:
     """The decoder of one configuration with its own bf16 KV cache.
 
     ``cfg`` needs attributes n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab_size,
-    rms_eps, rope_theta. ``weights`` maps names to uint16 arrays (per-layer names to lists).
+    rms_eps, rope_theta, n_experts, n_experts_active, expert_ffn_dim. ``weights`` maps names to
+    uint16 arrays (per-layer names to lists). A mixture-of-experts model (n_experts > 0) has
+    w_router, moe_gate, moe_up, moe_down per layer instead of w_gate, w_up, w_down.
     """
 
     def __init__(self, cfg, weights: Dict[str, object], max_seq: int):
@@ -192,7 +212,8 @@ class OracleModel:
         self.max_seq = int(max_seq)
         self._keep = []
         self._c = _Cfg(cfg.n_layers, cfg.d_model, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn_dim,
-                       cfg.vocab_size, cfg.rms_eps, cfg.rope_theta, self.max_seq)
+                       cfg.vocab_size, cfg.rms_eps, cfg.rope_theta, self.max_seq, cfg.n_experts,
+                       cfg.n_experts_active, cfg.expert_ffn_dim)
 
         def arr(a):
             a = np.ascontiguousarray(a, dtype=np.uint16)
@@ -204,8 +225,11 @@ class OracleModel:
             self._keep.append(ptrs)
             return C.cast(ptrs, _PP)
 
+        def arrs_opt(k):
+            return arrs(weights[k]) if k in weights else C.cast(None, _PP)
+
         self._w = _W(arr(weights["embed"]), arr(weights["final_norm"]), arr(weights["lm_head"]),
-                     *[arrs(weights[k]) for k in _LAYER_KEYS])
+                     *[arrs_opt(k) for k in _LAYER_KEYS + _MOE_KEYS])
         kv_elems = cfg.n_layers * cfg.n_kv_heads * self.max_seq * cfg.head_dim
         self.kcache = np.zeros(kv_elems, dtype=np.uint16)
         self.vcache = np.zeros(kv_elems, dtype=np.uint16)
@@ -234,6 +258,28 @@ class OracleModel:
 
     def full_recompute(self, tokens: Sequence[int]) -> np.ndarray:
         return full_recompute(self, tokens)
+
+    def moe_ffn(self, layer: int, u: np.ndarray):
+        """Feed-forward output of mixture-of-experts layer `layer` for the normalised input u [d]:
+        (y [d], router logits [E])."""
+        u = np.ascontiguousarray(u, dtype=np.float32)
+        y = np.empty(self.cfg.d_model, dtype=np.float32)
+        z = np.empty(self.cfg.n_experts, dtype=np.float32)
+        _load().oc_moe_ffn(C.byref(self._c), C.byref(self._w), int(layer), _p(u, C.c_float), _p(y, C.c_float),
+                           _p(z, C.c_float))
+        return y, z
+
+    def record_routes(self, max_pos: int):
+        """Start recording the router logits of step() at positions < max_pos; returns the
+        [max_pos][n_layers][n_experts] fp32 array that fills in."""
+        buf = np.full((max_pos, self.cfg.n_layers, self.cfg.n_experts), np.nan, dtype=np.float32)
+        self._route_buf = buf
+        _load().oc_set_route_log(_p(buf, C.c_float), int(max_pos))
+        return buf
+
+    def stop_recording(self):
+        _load().oc_set_route_log(C.cast(None, C.POINTER(C.c_float)), 0)
+        self._route_buf = None
 
 
 def full_recompute(model: OracleModel, tokens: Sequence[int]) -> np.ndarray:
