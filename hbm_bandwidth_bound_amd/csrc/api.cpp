@@ -102,14 +102,32 @@ static kie_status make_shape(const kie_config* c, int nwg_override, Shape* s, st
   s->eps = c->rms_eps;
   s->theta = c->rope_theta;
   s->nwg = nwg;
+  s->E = 0;
+  s->A = 0;
+  s->Fe = 0;
+  const bool moe = c->n_experts != 0;
   if (c->n_layers <= 0 || c->d_model <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 ||
-      c->ffn_dim <= 0 || c->vocab_size <= 0 || c->max_seq_len <= 0 || !(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) {
-    set_err(err, "config has a non-positive size");
+      (moe ? c->ffn_dim != 0 : c->ffn_dim <= 0) || c->vocab_size <= 0 || c->max_seq_len <= 0 ||
+      !(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) {
+    set_err(err, "config has a non-positive size (or a mixture-of-experts config with ffn_dim != 0)");
     return KIE_ERR_INVALID_ARG;
   }
-  if (c->n_experts != 0 || c->n_experts_active != 0 || c->expert_ffn_dim != 0) {
-    set_err(err, "mixture-of-experts layers are not supported by this kernel");
-    return KIE_ERR_UNSUPPORTED;
+  if (!moe && (c->n_experts_active != 0 || c->expert_ffn_dim != 0)) {
+    set_err(err, "n_experts_active and expert_ffn_dim must be 0 when n_experts is 0");
+    return KIE_ERR_INVALID_ARG;
+  }
+  if (moe) {
+    if (c->n_experts < 2 || c->n_experts % 2 || c->n_experts > kThreads || c->n_experts_active < 1 ||
+        c->n_experts_active > c->n_experts || c->n_experts_active > kMaxActive || c->expert_ffn_dim <= 0 ||
+        c->expert_ffn_dim % kTileK) {
+      set_err(err, "mixture of experts: n_experts must be even and in [2, %d], n_experts_active in [1, min(%d, "
+              "n_experts)], expert_ffn_dim a positive multiple of %d", kThreads, kMaxActive, kTileK);
+      return KIE_ERR_UNSUPPORTED;
+    }
+    s->E = c->n_experts;
+    s->A = c->n_experts_active;
+    s->Fe = c->expert_ffn_dim;
+    s->F = s->A * s->Fe;  // width of the gathered expert activations
   }
   if (s->d % kTileK || s->qdim() % kTileK || s->F % kTileK) {
     set_err(err, "d_model (%d), n_heads*head_dim (%d) and ffn_dim (%d) must be multiples of %d", s->d, s->qdim(), s->F,
@@ -211,14 +229,21 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
   kie_status st = make_shape(cfg, 0, &s, err);
   if (st != KIE_OK) return st;
   const int L = s.L;
+  const bool moe = s.moe();
   if (!src->embed || !src->final_norm || !src->lm_head || !src->attn_norm || !src->wq || !src->wk || !src->wv ||
-      !src->wo || !src->ffn_norm || !src->w_gate || !src->w_up || !src->w_down) {
+      !src->wo || !src->ffn_norm ||
+      (moe ? (!src->w_router || !src->moe_gate || !src->moe_up || !src->moe_down)
+           : (!src->w_gate || !src->w_up || !src->w_down))) {
     set_err(err, "a weight pointer is NULL");
     return KIE_ERR_INVALID_ARG;
   }
   for (int l = 0; l < L; ++l) {
-    const void* ps[] = {src->attn_norm[l], src->wq[l], src->wk[l], src->wv[l], src->wo[l],
-                        src->ffn_norm[l], src->w_gate[l], src->w_up[l], src->w_down[l]};
+    std::vector<const void*> ps = {src->attn_norm[l], src->wq[l], src->wk[l], src->wv[l], src->wo[l],
+                                   src->ffn_norm[l]};
+    if (moe)
+      ps.insert(ps.end(), {src->w_router[l], src->moe_gate[l], src->moe_up[l], src->moe_down[l]});
+    else
+      ps.insert(ps.end(), {src->w_gate[l], src->w_up[l], src->w_down[l]});
     for (const void* p : ps) {
       if (!p || !aligned16(p)) {
         set_err(err, "layer %d: a weight pointer is NULL or not 16-byte aligned", l);
@@ -249,10 +274,10 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
     set_err(err, "shape needs %d bytes of LDS per workgroup (device limit %d)", lds, lds_limit);
     return KIE_ERR_UNSUPPORTED;
   }
-  KernelFn kfn = decode_kernel_for(s.group(), s.hd, false);
-  KernelFn pfn = decode_kernel_for(s.group(), s.hd, true);
+  KernelFn kfn = decode_kernel_for(s.group(), s.hd, false, moe);
+  KernelFn pfn = decode_kernel_for(s.group(), s.hd, true, moe);
   if (!kfn || !pfn) {
-    set_err(err, "no kernel for group %d head_dim %d", s.group(), s.hd);
+    set_err(err, "no kernel for group %d head_dim %d%s", s.group(), s.hd, moe ? " with mixture-of-experts layers" : "");
     return KIE_ERR_UNSUPPORTED;
   }
   HIP_TRY(err, hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, lds));
@@ -334,13 +359,22 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
       a.wk = src->wk[l];
       a.wv = src->wv[l];
       a.wo = src->wo[l];
-      a.wgate = src->w_gate[l];
-      a.wup = src->w_up[l];
-      a.wdown = src->w_down[l];
+      if (moe) {
+        a.wrouter = src->w_router[l];
+        a.egate = src->moe_gate[l];
+        a.eup = src->moe_up[l];
+        a.edown = src->moe_down[l];
+        a.expert_offset = packed_expert_offset(s);
+      } else {
+        a.wgate = src->w_gate[l];
+        a.wup = src->w_up[l];
+        a.wdown = src->w_down[l];
+      }
     } else {
       a.lm_head = src->lm_head;
     }
     if ((e = launch_pack_layer(a, stm)) != hipSuccess) return fail("pack weights", e);
+    if (moe && l < L && (e = launch_pack_experts(a, stm)) != hipSuccess) return fail("pack experts", e);
   }
   if ((e = hipMemcpyAsync(c->packed + packed_embed_offset(s), src->embed, (size_t)s.V * s.d * 2,
                           hipMemcpyDeviceToDevice, stm)) != hipSuccess)
@@ -512,6 +546,10 @@ kie_status kie_prefill(kie_ctx* ctx, const int32_t* tokens_dev, int32_t n_tokens
     set_err(&ctx->last_error, "position %d + %d tokens exceeds max_seq_len %d", ctx->pos, n_tokens, ctx->s.max_seq);
     return KIE_ERR_CAPACITY;
   }
+  // mixture of experts: every position through the decode program, teacher-forced (position i + 1
+  // processes tokens[i + 1]); the LM head and the sampler run on the last one only
+  if (ctx->s.moe())
+    return launch(ctx, tokens_dev, n_tokens, tokens_dev + 1, nullptr, first_token_dev, last_logits_dev, 1, sampling);
   // all but the last prompt position: every layer as GEMMs on the matrix cores (K/V rows only)
   if (n_tokens > 1) {
     HIP_TRY(&ctx->last_error, hipSetDevice(ctx->device));

@@ -17,6 +17,13 @@
 //   batch    8 tile slots = 8 / ks units of one wave; the unit of a WG's stage with index u
 //            belongs to wave u mod 8. Slots of a missing unit are zero tiles.
 //   stream   one wave's batches for a whole token: L x [QKV, O, GU, DN], then the LM head.
+//
+// Mixture-of-experts layers (E > 0) stream L x [QKV, O, RT] (RT: the router's E rows), then the
+// LM head. Which experts a token needs is known only after the router, so their gate/up and down
+// tiles cannot sit in a fixed stream: they live in an expert region, per (layer, expert), where a
+// wave finds the tiles of its units once the experts are chosen. The stages over the A chosen
+// experts have the dense geometry with F = A x Fe: gate/up pair g is row g mod Fe of chosen
+// expert g / Fe, and the down projection's K runs over the chosen experts' Fe columns in turn.
 #pragma once
 #include <stdint.h>
 
@@ -38,20 +45,26 @@ constexpr int kMaxWG = 1024;
 constexpr int kMaxUnits = 2048;  // units of one stage per WG (LDS partial sums)
 constexpr int kMaxTopK = 64;     // largest k of top-k sampling
 
-enum Stage : int { ST_QKV = 0, ST_O = 1, ST_GU = 2, ST_DN = 3, ST_LM = 4, ST_COUNT = 5 };
+enum Stage : int { ST_QKV = 0, ST_O = 1, ST_RT = 2, ST_GU = 3, ST_DN = 4, ST_LM = 5, ST_COUNT = 6 };
+constexpr int kMaxActive = 8;  // most experts routed per token
 
 struct Shape {
-  int32_t L, d, nq, nkv, hd, F, V, max_seq;
+  int32_t L, d, nq, nkv, hd, F, V, max_seq;  // F: FFN width (A x Fe for a mixture of experts)
   float eps, theta;
   int32_t nwg;
+  int32_t E, A, Fe;  // experts, routed per token, FFN width of one expert (E == 0: dense)
+  KIE_HD bool moe() const { return E > 0; }
   KIE_HD int32_t qdim() const { return nq * hd; }
   KIE_HD int32_t kvdim() const { return nkv * hd; }
   KIE_HD int32_t group() const { return nq / nkv; }
+  // whether a stage's tiles are part of the fixed per-wave streams
+  KIE_HD bool in_stream(int st) const { return !(moe() && (st == ST_GU || st == ST_DN)); }
   // pairs and row length (K) of each stage
   KIE_HD int32_t stage_pairs(int st) const {
     switch (st) {
       case ST_QKV: return (nq + 2 * nkv) * (hd / 2);
       case ST_O: return d / 2;
+      case ST_RT: return E / 2;
       case ST_GU: return F;
       case ST_DN: return d / 2;
       default: return V / 2;
@@ -101,7 +114,8 @@ KIE_HD int32_t wave_batches(const StageGeo& g, int32_t v) { return (wave_units(g
 // Batches of one layer in the stream of (WG w, wave v), and of the LM head.
 KIE_HD int32_t layer_batches(const Shape& s, int32_t w, int32_t v) {
   int32_t b = 0;
-  for (int st = ST_QKV; st <= ST_DN; ++st) b += wave_batches(stage_geo(s, st, w), v);
+  for (int st = ST_QKV; st <= ST_DN; ++st)
+    if (s.in_stream(st)) b += wave_batches(stage_geo(s, st, w), v);
   return b;
 }
 KIE_HD int32_t lm_batches(const Shape& s, int32_t w, int32_t v) { return wave_batches(stage_geo(s, ST_LM, w), v); }
@@ -110,6 +124,7 @@ KIE_HD int64_t stream_tiles(const Shape& s, int32_t w, int32_t v) {
 }
 
 // Source rows of global pair gp of a stage. mat selects the matrix: for QKV 0 = Wq, 1 = Wk, 2 = Wv.
+// (The router's pairs are neighbouring rows, like O, DN and the LM head.)
 KIE_HD void pair_rows(const Shape& s, int st, int32_t gp, int* mat, int32_t* ra, int32_t* rb) {
   if (st == ST_QKV) {
     const int32_t half = s.hd / 2;
@@ -188,7 +203,7 @@ KIE_HD int32_t merge_unit_wg(const Shape& s, int32_t u) { return (int32_t)(((int
 // Exchange buffers (64-bit tagged words: value bits << 32 | epoch), per layer, in the workspace.
 // ---------------------------------------------------------------------------------------------
 struct Exch {
-  int64_t xf, xa, q, k, v, part, o, h, lm, end;  // word offsets
+  int64_t xf, xa, q, k, v, part, o, h, rt, lm, end;  // word offsets
   int32_t part_words;                             // per WG per layer
 };
 KIE_HD Exch exch_layout(const Shape& s) {
@@ -204,6 +219,7 @@ KIE_HD Exch exch_layout(const Shape& s) {
   e.part = o; o += (int64_t)s.L * s.nwg * e.part_words;
   e.o = o; o += (int64_t)s.L * s.qdim();
   e.h = o; o += (int64_t)s.L * s.F;
+  e.rt = o; o += (int64_t)s.L * s.E;  // router logits
   e.lm = o; o += (int64_t)kMaxTopK * s.nwg * 2;  // [rank][WG][value, id] sampling candidates
   e.end = o;
   return e;
@@ -257,15 +273,29 @@ KIE_HD Workspace workspace_layout(const Shape& s) {
   return w;
 }
 
-// Packed image: the streams of (WG 0, wave 0), (WG 0, wave 1), ..., (WG nwg-1, wave 7), then the
-// embedding table [V][d] bf16 as is.
+// Packed image: the streams of (WG 0, wave 0), (WG 0, wave 1), ..., (WG nwg-1, wave 7), the
+// expert region (mixture of experts), then the embedding table [V][d] bf16 as is.
 KIE_HD int64_t packed_stream_tiles(const Shape& s) {
   int64_t t = 0;
   for (int32_t w = 0; w < s.nwg; ++w)
     for (int32_t v = 0; v < kWaves; ++v) t += stream_tiles(s, w, v);
   return t;
 }
-KIE_HD int64_t packed_embed_offset(const Shape& s) { return packed_stream_tiles(s) * kTileBytes; }
+// Expert region, in tiles from its start: gate/up tiles [L][E][Fe pairs][d / 256] (pair p = row p
+// of the expert's W_gate (A) and W_up (B)), then down tiles [L][E][d / 2 pairs][Fe / 256] (pair p
+// = rows 2p, 2p + 1 of the expert's W_down).
+KIE_HD int64_t expert_gu_tile(const Shape& s, int32_t l, int32_t e, int32_t p, int32_t kt) {
+  return (((int64_t)l * s.E + e) * s.Fe + p) * (s.d / kTileK) + kt;
+}
+KIE_HD int64_t expert_gu_tiles(const Shape& s) { return (int64_t)s.L * s.E * s.Fe * (s.d / kTileK); }
+KIE_HD int64_t expert_dn_tile(const Shape& s, int32_t l, int32_t e, int32_t p, int32_t kt) {
+  return expert_gu_tiles(s) + (((int64_t)l * s.E + e) * (s.d / 2) + p) * (s.Fe / kTileK) + kt;
+}
+KIE_HD int64_t expert_tiles(const Shape& s) { return s.moe() ? 2 * expert_gu_tiles(s) : 0; }
+KIE_HD int64_t packed_expert_offset(const Shape& s) { return packed_stream_tiles(s) * kTileBytes; }
+KIE_HD int64_t packed_embed_offset(const Shape& s) {
+  return (packed_stream_tiles(s) + expert_tiles(s)) * kTileBytes;
+}
 
 // Owner WG of global pair gp of a stage with n pairs (the inverse of the even split).
 KIE_HD int32_t pair_owner(int64_t n, int32_t nwg, int32_t gp) {
@@ -277,6 +307,7 @@ KIE_HD int32_t pair_owner(int64_t n, int32_t nwg, int32_t gp) {
 // Where k-tile kt of pair gp of stage st in layer l lives in the packed image (in tiles); the LM
 // head is st == ST_LM (l ignored). wbase[w * kWaves + v] is the first tile of stream (w, v). This
 // inverts the packer's placement, so that a kernel can read the weights of any row in place.
+// (Stages in the fixed streams only.)
 KIE_HD int64_t packed_tile(const Shape& s, const int64_t* wbase, int st, int32_t l, int32_t gp, int32_t kt) {
   const int32_t w = pair_owner(s.stage_pairs(st), s.nwg, gp);
   const StageGeo g = stage_geo(s, st, w);
@@ -288,7 +319,8 @@ KIE_HD int64_t packed_tile(const Shape& s, const int64_t* wbase, int st, int32_t
     bt = (int64_t)s.L * layer_batches(s, w, v);
   } else {
     bt = (int64_t)l * layer_batches(s, w, v);
-    for (int st2 = ST_QKV; st2 < st; ++st2) bt += wave_batches(stage_geo(s, st2, w), v);
+    for (int st2 = ST_QKV; st2 < st; ++st2)
+      if (s.in_stream(st2)) bt += wave_batches(stage_geo(s, st2, w), v);
   }
   return wbase[w * kWaves + v] + (bt + b) * kBatch + slot;
 }

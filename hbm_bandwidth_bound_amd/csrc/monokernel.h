@@ -46,7 +46,7 @@ struct KParams {
 };
 
 typedef void (*KernelFn)(KParams);
-KernelFn decode_kernel_for(int group, int head_dim, bool prompt);
+KernelFn decode_kernel_for(int group, int head_dim, bool prompt, bool moe);
 int32_t lds_bytes_for(const Shape& s);
 int32_t topk_capacity_floats(const Shape& s);  // WG-local floats available to the top-k merge
 
@@ -58,8 +58,12 @@ struct PackArgs {
   int32_t layer;         // 0..L-1, or L for the LM head
   const uint16_t *wq, *wk, *wv, *wo, *wgate, *wup, *wdown;  // layer matrices (layer < L)
   const uint16_t* lm_head;                                   // layer == L
+  // mixture of experts (layer < L): router [E][d]; gate, up [E][Fe][d]; down [E][d][Fe]
+  const uint16_t *wrouter, *egate, *eup, *edown;
+  int64_t expert_offset;  // byte offset of the expert region in the packed image
 };
 hipError_t launch_pack_layer(const PackArgs& a, hipStream_t st);
+hipError_t launch_pack_experts(const PackArgs& a, hipStream_t st);
 hipError_t launch_rope_table(float2* rope, int32_t max_seq, int32_t hd, float theta, hipStream_t st);
 
 }  // namespace kie

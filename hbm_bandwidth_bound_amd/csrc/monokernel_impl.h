@@ -29,7 +29,10 @@
 // Per layer: RMSNorm -> QKV (+RoPE) -> attention over a chunk of positions of one KV head
 // (split-K; online softmax per wave, waves merged in LDS) -> merge of the chunk partials ->
 // O (+residual) -> RMSNorm -> gate/up (SwiGLU) -> down (+residual). Then the final RMSNorm, the
-// LM head and the sampler.
+// LM head and the sampler. A mixture-of-experts layer runs the router after the second RMSNorm;
+// every WG chooses the same experts from the gathered router logits, and gate/up and down then
+// stream only the chosen experts' tiles (the pages' point that bandwidth follows the active
+// parameters: aikraft.ru «3000 токенов в секунду…», §02).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -94,6 +97,7 @@ __host__ __device__ inline int32_t scr_floats(const Shape& s) {
   if (kWaves * kMergeDims * 3 > a) a = kWaves * kMergeDims * 3;
   if (2 * s.nwg > a) a = 2 * s.nwg;
   if (lm_rows_max(s) > a) a = lm_rows_max(s);  // the WG's LM outputs for the top-k draw
+  if (s.E > a) a = s.E;                          // router logits
   if (a < 64) a = 64;
   return (a + 3) & ~3;
 }
@@ -212,8 +216,11 @@ __device__ __forceinline__ bool better(float v, int32_t i, float bv, int32_t bi)
 }
 
 // ------------------------------------------------------------------------------------------
-// One wave's state: its weight stream, the batch in flight, the WG's stage geometry.
+// One wave's state: its weight stream, the batch in flight, the WG's stage geometry. MOE: the
+// layers are mixture-of-experts layers, whose gate/up and down batches are read from the expert
+// region at the chosen experts' tiles (routed batches) instead of from the fixed stream.
 // ------------------------------------------------------------------------------------------
+template <bool MOE>
 struct Wk {
   const KParams& P;
   const Lds& L;
@@ -229,6 +236,16 @@ struct Wk {
   // The batch after nxt may also be in flight, loaded straight into this wave's LDS slot: xpend
   // while nxt is still ahead of it, xnext once it is the next to reduce.
   bool xpend = false, xnext = false;
+  // MOE. A step's batches are, per layer, layer_b fixed-stream batches and then dyn_b routed ones
+  // (gate/up, then down), and finally the LM head's. A routed batch can be issued only once its
+  // layer's experts are chosen: until then nxt stays empty (deferred) and the router boundary
+  // issues it. es/ew: the chosen experts of layer sel_key (= step * L + layer) and their weights.
+  int32_t dyn_b = 0;
+  int32_t sel_key = -1;
+  bool deferred = false;
+  const uint8_t* xreg = nullptr;  // expert region of the packed image
+  int32_t es[kMaxActive];
+  float ew[kMaxActive];
 
   __device__ __forceinline__ Wk(const KParams& p, const Lds& l, int32_t w_, int32_t v_, int32_t lane_)
       : P(p), L(l), w(w_), v(v_), lane(lane_), tid(v_ * kWave + lane_), fail(false) {
@@ -236,17 +253,26 @@ struct Wk {
     for (int st = 0; st < ST_COUNT; ++st) {
       g[st] = stage_geo(P.s, st, w);
       nb[st] = wave_batches(g[st], v);
-      if (st <= ST_DN) layer_b += nb[st];
+      if (st <= ST_DN && P.s.in_stream(st)) layer_b += nb[st];
     }
     lm_b = nb[ST_LM];
     stream = P.packed + (size_t)P.wbase[w * kWaves + v] * kTileBytes;
     pidx = -1;
     pstep = 0;
+    if constexpr (MOE) {
+      dyn_b = nb[ST_GU] + nb[ST_DN];
+      xreg = P.packed + (size_t)P.wbase[P.s.nwg * kWaves] * kTileBytes;
+#pragma unroll
+      for (int i = 0; i < kMaxActive; ++i) {
+        es[i] = 0;
+        ew[i] = 0.f;
+      }
+    }
   }
 
   // ------------------------------------------------------------ weight stream
   __device__ __forceinline__ int32_t step_batches(int32_t step) const {
-    return P.s.L * layer_b + (step_has_lm(P, step) ? lm_b : 0);
+    return P.s.L * (layer_b + dyn_b) + (step_has_lm(P, step) ? lm_b : 0);
   }
   // advance (pidx, pstep) to the next batch of the launch; pstep == n_steps once there is none
   __device__ __forceinline__ void advance() {
@@ -256,12 +282,111 @@ struct Wk {
       ++pstep;
     }
   }
+  // MOE: where batch (pidx, pstep) lies. Returns the fixed-stream batch index, or -1 for a routed
+  // batch (then *lb is its layer and *jd its index among the layer's routed batches).
+  __device__ __forceinline__ int32_t locate(int32_t* lb, int32_t* jd) const {
+    const int32_t per = layer_b + dyn_b;
+    if (pidx >= P.s.L * per) return P.s.L * layer_b + (pidx - P.s.L * per);  // the LM head
+    const int32_t l = pidx / per;
+    const int32_t j = pidx - l * per;
+    if (j < layer_b) return l * layer_b + j;
+    *lb = l;
+    *jd = j - layer_b;
+    return -1;
+  }
+  __device__ __forceinline__ int32_t expert_of(int32_t slot) const {
+    switch (slot) {
+      case 1: return es[1];
+      case 2: return es[2];
+      case 3: return es[3];
+      case 4: return es[4];
+      case 5: return es[5];
+      case 6: return es[6];
+      case 7: return es[7];
+      default: return es[0];
+    }
+  }
+  __device__ __forceinline__ float weight_of(int32_t slot) const {
+    switch (slot) {
+      case 1: return ew[1];
+      case 2: return ew[2];
+      case 3: return ew[3];
+      case 4: return ew[4];
+      case 5: return ew[5];
+      case 6: return ew[6];
+      case 7: return ew[7];
+      default: return ew[0];
+    }
+  }
+  // The 8 tile slots of routed batch jd of layer lb: f(b, resource of tile b). A slot of a missing
+  // unit gets an empty resource (its load returns zeros). Gate/up pair gp is row gp mod Fe of
+  // chosen expert gp / Fe; k-tile t of a down pair lies in chosen expert t / (Fe / 256).
+  template <int KS, typename F>
+  __device__ __forceinline__ void routed_tiles_ks(const StageGeo& gs, bool gu, int32_t lb, int32_t bi, F f) const {
+    constexpr int UPB = kBatch / KS;
+    const Shape& s = P.s;
+    const int32_t kte = s.Fe / kTileK;
+#pragma unroll
+    for (int us = 0; us < UPB; ++us) {
+      const int32_t u = v + kWaves * (bi * UPB + us);
+      const bool valid = u < gs.nu;
+      const int32_t lp = gs.S == 1 ? u : u / gs.S, r = gs.S == 1 ? 0 : u - lp * gs.S;
+      const int32_t gp = gs.pb + lp;
+      if (gu) {
+        const int32_t slot = gp / s.Fe, p = gp - slot * s.Fe;
+        const int64_t t0 = expert_gu_tile(s, lb, expert_of(slot), p, r * KS);
+#pragma unroll
+        for (int tt = 0; tt < KS; ++tt)
+          f(us * KS + tt, make_rsrc(xreg + (valid ? (size_t)(t0 + tt) * kTileBytes : 0), valid ? kTileBytes : 0));
+      } else {
+        int32_t slot = (r * KS) / kte, kk = r * KS - slot * kte;
+#pragma unroll
+        for (int tt = 0; tt < KS; ++tt) {
+          const int64_t t = expert_dn_tile(s, lb, expert_of(slot), gp, kk);
+          f(us * KS + tt, make_rsrc(xreg + (valid ? (size_t)t * kTileBytes : 0), valid ? kTileBytes : 0));
+          if (++kk == kte) {
+            kk = 0;
+            ++slot;
+          }
+        }
+      }
+    }
+  }
+  template <typename F>
+  __device__ __forceinline__ void routed_tiles(int32_t lb, int32_t jd, F f) const {
+    const bool gu = jd < nb[ST_GU];
+    const StageGeo gs = gu ? g[ST_GU] : g[ST_DN];
+    const int32_t bi = gu ? jd : jd - nb[ST_GU];
+    switch (gs.ks) {
+      case 8: routed_tiles_ks<8>(gs, gu, lb, bi, f); break;
+      case 4: routed_tiles_ks<4>(gs, gu, lb, bi, f); break;
+      case 2: routed_tiles_ks<2>(gs, gu, lb, bi, f); break;
+      default: routed_tiles_ks<1>(gs, gu, lb, bi, f); break;
+    }
+  }
   // 8 loads of batch (pidx, pstep); past the launch's last batch the resource is empty and the
-  // loads return zeros without touching memory.
+  // loads return zeros without touching memory. MOE: a routed batch of a layer whose experts are
+  // not chosen yet is left deferred.
   __device__ __forceinline__ void issue(v4u* buf) {
     const bool live = pstep < P.n_steps;
-    const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(stream + (live ? (size_t)pidx * kBatch * kTileBytes : 0), live ? kBatch * kTileBytes : 0);
+    size_t off = live ? (size_t)pidx * kBatch * kTileBytes : 0;
+    if constexpr (MOE) {
+      deferred = false;
+      if (live) {
+        int32_t lb = 0, jd = 0;
+        const int32_t sidx = locate(&lb, &jd);
+        if (sidx < 0) {
+          if (sel_key != pstep * P.s.L + lb) {
+            deferred = true;
+            return;
+          }
+          routed_tiles(lb, jd, [&](int b, __amdgpu_buffer_rsrc_t rs) { buf[b] = load16(rs, (uint32_t)(lane * 16)); });
+          return;
+        }
+        off = (size_t)sidx * kBatch * kTileBytes;
+      }
+    }
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(stream + off, live ? kBatch * kTileBytes : 0);
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) buf[b] = load16(rs, (uint32_t)(lane * 16 + b * kTileBytes));
   }
@@ -275,8 +400,11 @@ struct Wk {
     if (xnext) {
       // The batch in the LDS slot. At least nxt's kBatch loads were issued after its loads, and
       // the counter drains in issue order, so with at most kBatch operations outstanding the slot
-      // is filled.
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kBatch) : "memory");
+      // is filled. (A deferred nxt has issued nothing: then everything is waited for.)
+      if (MOE && deferred)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kBatch) : "memory");
       const uint8_t* xs = L.xb + (size_t)v * kBatch * kTileBytes + lane * 16;
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) cur[b] = *(const v4u*)(xs + b * kTileBytes);
@@ -298,14 +426,86 @@ struct Wk {
   // LDS read, adds no waits; take() waits for them itself. They hold no registers.
   __device__ __forceinline__ void issue_x() {
     if (L.xb == nullptr || xpend || xnext) return;
+    const uint32_t base = lds_addr(L.xb + (size_t)v * kBatch * kTileBytes);
+    if constexpr (MOE) {
+      if (deferred) return;  // nxt itself is not issued yet
+      const int32_t sp = pidx, ss = pstep;
+      advance();
+      if (pstep < P.n_steps) {
+        int32_t lb = 0, jd = 0;
+        const int32_t sidx = locate(&lb, &jd);
+        if (sidx < 0) {
+          if (sel_key != pstep * P.s.L + lb) {  // experts not chosen yet: leave it to the stream
+            pidx = sp;
+            pstep = ss;
+            return;
+          }
+          routed_tiles(lb, jd, [&](int b, __amdgpu_buffer_rsrc_t rs) {
+            load16_lds(rs, (uint32_t)(lane * 16), base + b * kTileBytes);
+          });
+        } else {
+          const __amdgpu_buffer_rsrc_t rs = make_rsrc(stream + (size_t)sidx * kBatch * kTileBytes, kBatch * kTileBytes);
+#pragma unroll
+          for (int b = 0; b < kBatch; ++b) load16_lds(rs, (uint32_t)(lane * 16 + b * kTileBytes), base + b * kTileBytes);
+        }
+      } else {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(stream, 0);
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) load16_lds(rs, (uint32_t)(lane * 16 + b * kTileBytes), base + b * kTileBytes);
+      }
+      xpend = true;
+      return;
+    }
     advance();
     const bool live = pstep < P.n_steps;
     const __amdgpu_buffer_rsrc_t rs =
         make_rsrc(stream + (live ? (size_t)pidx * kBatch * kTileBytes : 0), live ? kBatch * kTileBytes : 0);
-    const uint32_t base = lds_addr(L.xb + (size_t)v * kBatch * kTileBytes);
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) load16_lds(rs, (uint32_t)(lane * 16 + b * kTileBytes), base + b * kTileBytes);
     xpend = true;
+  }
+
+  // MOE, at the router boundary of layer l: router logits (all E) are in scr. Every WG takes the
+  // same decision: the A largest logits (ties to the lower index; NaN ranks lowest) and weights
+  // w_i = exp(z_i - z_0) / sum_j exp(z_j - z_0) over the chosen, z_0 the largest -- the softmax
+  // over all experts restricted to the chosen and renormalised. Then the deferred batch, if any,
+  // is issued.
+  __device__ __forceinline__ void route(int32_t step, int32_t l) {
+    const Shape& s = P.s;
+    int32_t* sel = (int32_t*)L.part;  // free between the router stage's finalize and gate/up
+    if (tid < s.E) {
+      float z = L.scr[tid];
+      z = z == z ? z : -INFINITY;
+      int32_t rank = 0;
+      for (int32_t j = 0; j < s.E; ++j) {
+        float zj = L.scr[j];
+        zj = zj == zj ? zj : -INFINITY;
+        rank += better(zj, j, z, tid) ? 1 : 0;
+      }
+      if (rank < s.A) sel[rank] = tid;
+    }
+    bar();
+    float zs[kMaxActive];
+#pragma unroll
+    for (int r = 0; r < kMaxActive; ++r) {
+      int32_t e = r < s.A ? (int32_t)__builtin_amdgcn_readfirstlane(lds_ld((const uint32_t*)&sel[r])) : 0;
+      e = e < 0 ? 0 : (e >= s.E ? s.E - 1 : e);
+      es[r] = e;
+      const float z = L.scr[e];
+      zs[r] = z == z ? z : -INFINITY;
+    }
+    const float z0 = zs[0];
+    float sum = 0.f;
+#pragma unroll
+    for (int r = 0; r < kMaxActive; ++r) {
+      zs[r] = r < s.A ? expf(zs[r] - z0) : 0.f;
+      sum += zs[r];
+    }
+#pragma unroll
+    for (int r = 0; r < kMaxActive; ++r) ew[r] = zs[r] / sum;
+    bar();  // sel and scr are read before the gate/up stage writes part
+    sel_key = step * s.L + l;
+    if (deferred) issue(nxt);
   }
 
   // ------------------------------------------------------------ GEMV of one stage
@@ -314,6 +514,7 @@ struct Wk {
     switch (st) {
       case ST_QKV: return g[ST_QKV];
       case ST_O: return g[ST_O];
+      case ST_RT: return g[ST_RT];
       case ST_GU: return g[ST_GU];
       case ST_DN: return g[ST_DN];
       default: return g[ST_LM];
@@ -323,6 +524,7 @@ struct Wk {
     switch (st) {
       case ST_QKV: return nb[ST_QKV];
       case ST_O: return nb[ST_O];
+      case ST_RT: return nb[ST_RT];
       case ST_GU: return nb[ST_GU];
       case ST_DN: return nb[ST_DN];
       default: return nb[ST_LM];
@@ -546,8 +748,8 @@ struct Wk {
 // position rows of a wave are combined with shuffles and the 8 waves in LDS; one partial
 // (acc[hd], m, l) per query head of the group is published, m being the chunk maximum.
 // ------------------------------------------------------------------------------------------
-template <int G, int HD>
-__device__ __forceinline__ void attention(Wk& K, const Att& at, int32_t l, int32_t pos, uint32_t ep) {
+template <int G, int HD, typename WK>
+__device__ __forceinline__ void attention(WK& K, const Att& at, int32_t l, int32_t pos, uint32_t ep) {
   const KParams& P = K.P;
   const Lds& L = K.L;
   const Shape& s = P.s;
@@ -587,7 +789,7 @@ __device__ __forceinline__ void attention(Wk& K, const Att& at, int32_t l, int32
     const uint64_t* vsrc = P.ex + X.v + (int64_t)l * s.kvdim() + at.j * HD;
     const int32_t n = G * HD + (at.has_p ? 2 * HD : 0);
     constexpr int KM = ((G + 2) * HD + kThreads - 1) / kThreads;
-    K.poll<KM>(
+    K.template poll<KM>(
         ep, [&](int k) { return K.tid + k * kThreads < n; },
         [&](int k) {
           const int32_t e = K.tid + k * kThreads;
@@ -745,7 +947,8 @@ __device__ __forceinline__ void softmax_combine(float& M, float& S, float& A, fl
 // Merge of the chunk partials of one (query head, kMergeDims-dim slice). Thread (chunk lane cl,
 // dim) folds chunks cl, cl + CL, ... in order; the chunk lanes of a wave are combined with
 // shuffles and the 8 waves in LDS, always in the same order.
-__device__ __forceinline__ void merge_unit(Wk& K, const Att& at, int32_t l, int32_t u, uint32_t epoch) {
+template <typename WK>
+__device__ __forceinline__ void merge_unit(WK& K, const Att& at, int32_t l, int32_t u, uint32_t epoch) {
   const KParams& P = K.P;
   const Lds& L = K.L;
   const Shape& s = P.s;
@@ -882,7 +1085,8 @@ __device__ __forceinline__ int32_t count_greater(const uint64_t* kk, int32_t n, 
 //     u = (splitmix64(seed ^ splitmix64(pos)) >> 40) * 2^-24; the first j whose running sum of
 //     p_j exceeds u is drawn, the last candidate if none does.
 // The rank loops read LDS at independent addresses and are unrolled so that the reads overlap.
-__device__ __forceinline__ int32_t sample_topk(Wk& K, const StageGeo& gl, uint64_t* lmx, uint32_t ep, int32_t pos) {
+template <typename WK>
+__device__ __forceinline__ int32_t sample_topk(WK& K, const StageGeo& gl, uint64_t* lmx, uint32_t ep, int32_t pos) {
   const KParams& P = K.P;
   const Lds& L = K.L;
   const Shape& s = P.s;
@@ -925,7 +1129,7 @@ __device__ __forceinline__ int32_t sample_topk(Wk& K, const StageGeo& gl, uint64
     alen[tid] = 0;
   }
   phase(16);
-  K.fetch_map<8>(2 * nwg, [&](int32_t q) { return lmx + q; }, heads, ep);
+  K.template fetch_map<8>(2 * nwg, [&](int32_t q) { return lmx + q; }, heads, ep);
   phase(17);
   uint64_t* hkey = (uint64_t*)heads;  // each (z, id) pair becomes its key, in place
   uint64_t myk[(kMaxWG + kThreads - 1) / kThreads];
@@ -954,7 +1158,7 @@ __device__ __forceinline__ int32_t sample_topk(Wk& K, const StageGeo& gl, uint64
   bar();
   phase(18);
   // 3.
-  K.fetch_map<16>(
+  K.template fetch_map<16>(
       2 * nsel * ke,
       [&](int32_t q) {
         const int32_t e = q >> 1, j = e / ke, r = e - j * ke;
@@ -1030,10 +1234,11 @@ __device__ __forceinline__ int32_t sample_topk(Wk& K, const StageGeo& gl, uint64
 // two stages -- finalising the outputs,
 // attention, the merge, the exchange gathers, RMSNorm, sampling -- whenever the current stage has
 // no batch left for this wave. Every wave runs every boundary, so the WG barriers inside match.
-enum Boundary : int { B_START = 0, B_QKV = 1, B_O = 2, B_GU = 3, B_DN = 4, B_LM = 5, B_END = 6 };
+// MOE: after O the router stage runs, and its boundary (B_RT) chooses the layer's experts.
+enum Boundary : int { B_START = 0, B_QKV = 1, B_O = 2, B_GU = 3, B_DN = 4, B_LM = 5, B_END = 6, B_RT = 7 };
 
-template <int G, int HD>
-__device__ __forceinline__ void decode(Wk& K) {
+template <int G, int HD, bool MOE>
+__device__ __forceinline__ void decode(Wk<MOE>& K) {
   const KParams& P = K.P;
   const Lds& L = K.L;
   const Shape& s = P.s;
@@ -1147,6 +1352,21 @@ __device__ __forceinline__ void decode(Wk& K) {
           xres = xres == L.xres ? L.xres + s.d : L.xres;  // the other buffer: no wave reads it now
           ss = K.fetch_f32(xa, s.d, xres, ep, true);
           K.norm_to_act(ss, xres);
+          st = MOE ? ST_RT : ST_GU;
+          bnd = MOE ? B_RT : B_GU;
+          break;
+        }
+        case B_RT: {  // router logits -> gather all E -> the layer's experts (identical in every WG)
+          if constexpr (MOE) {
+            bar();
+            uint64_t* rx = ex + X.rt + (int64_t)l * s.E;
+            K.finalize(K.g[ST_RT], [&](int32_t gp, float ya, float yb) {
+              st_x(rx + 2 * gp, tag_f(ya, ep));
+              st_x(rx + 2 * gp + 1, tag_f(yb, ep));
+            });
+            K.fetch_f32(rx, s.E, L.scr, ep, false);
+            K.route(step, l);
+          }
           st = ST_GU;
           bnd = B_GU;
           break;
@@ -1155,10 +1375,12 @@ __device__ __forceinline__ void decode(Wk& K) {
           bar();
           uint64_t* hx = ex + X.h + (int64_t)l * s.F;
           K.finalize(K.g[ST_GU], [&](int32_t gp, float ya, float yb) {
-            st_x(hx + gp, tag_f((ya / (1.0f + expf(-ya))) * yb, ep));
+            float h = (ya / (1.0f + expf(-ya))) * yb;
+            if constexpr (MOE) h = K.weight_of(gp / s.Fe) * h;  // the routing weight of its expert
+            st_x(hx + gp, tag_f(h, ep));
           });
           K.issue_x();
-          K.fetch_f32<16>(hx, s.F, L.act, ep, false);
+          K.template fetch_f32<16>(hx, s.F, L.act, ep, false);
           st = ST_DN;
           bnd = B_DN;
           break;
@@ -1344,22 +1566,31 @@ __device__ __forceinline__ void decode(Wk& K) {
 // The kernels. The prompt pass (teacher-forced steps whose only output is the last logits and
 // the first token) runs the same program under its own symbol, so that profiles separate it
 // from decoding.
-#define KIE_KERNEL_BODY(G, HD)                                              \
+#define KIE_KERNEL_BODY(G, HD, MOE)                                         \
   extern __shared__ __align__(16) uint8_t smem[];                          \
   const Lds L = lds_map(smem, P.s);                                        \
   if (threadIdx.x < C_COUNT) L.ctl[threadIdx.x] = 0;                       \
   __syncthreads();                                                         \
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);    \
-  Wk K(P, L, blockIdx.x, wave, threadIdx.x % kWave);                       \
-  decode<G, HD>(K);
+  Wk<MOE> K(P, L, blockIdx.x, wave, threadIdx.x % kWave);                  \
+  decode<G, HD, MOE>(K);
 
 template <int G, int HD>
 __global__ void __launch_bounds__(kThreads, 1) kie_decode_kernel(KParams P) {
-  KIE_KERNEL_BODY(G, HD)
+  KIE_KERNEL_BODY(G, HD, false)
 }
 template <int G, int HD>
 __global__ void __launch_bounds__(kThreads, 1) kie_prompt_kernel(KParams P) {
-  KIE_KERNEL_BODY(G, HD)
+  KIE_KERNEL_BODY(G, HD, false)
+}
+// Mixture-of-experts layers (the same program with the router stage and routed expert batches)
+template <int G, int HD>
+__global__ void __launch_bounds__(kThreads, 1) kie_moe_decode_kernel(KParams P) {
+  KIE_KERNEL_BODY(G, HD, true)
+}
+template <int G, int HD>
+__global__ void __launch_bounds__(kThreads, 1) kie_moe_prompt_kernel(KParams P) {
+  KIE_KERNEL_BODY(G, HD, true)
 }
 
 }  // namespace kie

@@ -21,7 +21,7 @@ __global__ void __launch_bounds__(256) pack_layer_kernel(PackArgs a) {
   int32_t acc = 0;
   for (int st = ST_QKV; st <= ST_DN; ++st) {
     boff[st] = acc;
-    acc += wave_batches(stage_geo(s, st, w), v);
+    if (s.in_stream(st)) acc += wave_batches(stage_geo(s, st, w), v);
   }
   boff[ST_LM] = acc;
   const int32_t layer_b = acc;
@@ -50,6 +50,8 @@ __global__ void __launch_bounds__(256) pack_layer_kernel(PackArgs a) {
         ma = mb = mat == 0 ? a.wq : (mat == 1 ? a.wk : a.wv);
       } else if (st == ST_O) {
         ma = mb = a.wo;
+      } else if (st == ST_RT) {
+        ma = mb = a.wrouter;
       } else if (st == ST_GU) {
         ma = a.wgate;
         mb = a.wup;
@@ -70,6 +72,45 @@ __global__ void __launch_bounds__(256) pack_layer_kernel(PackArgs a) {
 
 hipError_t launch_pack_layer(const PackArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(pack_layer_kernel, dim3(a.s.nwg * kWaves, 16), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// The expert region of one mixture-of-experts layer: every expert's gate/up pairs (row p of W_gate
+// and of W_up) and down pairs (rows 2p, 2p + 1 of W_down), each as whole tiles in k order (the
+// placement of expert_gu_tile / expert_dn_tile). One thread writes one lane of a tile.
+__global__ void __launch_bounds__(256) pack_experts_kernel(PackArgs a) {
+  const Shape& s = a.s;
+  const int32_t ktd = s.d / kTileK, kte = s.Fe / kTileK, hp = s.d / 2;
+  const int64_t ngu = (int64_t)s.E * s.Fe * ktd, ndn = (int64_t)s.E * hp * kte;
+  const int q = threadIdx.x % 64;
+  uint8_t* region = a.packed + a.expert_offset;
+  for (int64_t t = (int64_t)blockIdx.x * 4 + threadIdx.x / 64; t < ngu + ndn; t += (int64_t)gridDim.x * 4) {
+    uint2 xa, xb;
+    int64_t dst;
+    if (t < ngu) {
+      const int32_t kt = (int32_t)(t % ktd);
+      const int64_t r = t / ktd;
+      const int32_t p = (int32_t)(r % s.Fe), e = (int32_t)(r / s.Fe);
+      const int64_t off = ((int64_t)e * s.Fe + p) * s.d + kt * kTileK + q * 4;
+      xa = *(const uint2*)(a.egate + off);
+      xb = *(const uint2*)(a.eup + off);
+      dst = expert_gu_tile(s, a.layer, e, p, kt);
+    } else {
+      const int64_t t2 = t - ngu;
+      const int32_t kk = (int32_t)(t2 % kte);
+      const int64_t r = t2 / kte;
+      const int32_t p = (int32_t)(r % hp), e = (int32_t)(r / hp);
+      const int64_t off = ((int64_t)e * s.d + 2 * p) * s.Fe + kk * kTileK + q * 4;
+      xa = *(const uint2*)(a.edown + off);
+      xb = *(const uint2*)(a.edown + off + s.Fe);
+      dst = expert_dn_tile(s, a.layer, e, p, kk);
+    }
+    *(v4u*)(region + dst * kTileBytes + q * 16) = v4u{xa.x, xa.y, xb.x, xb.y};
+  }
+}
+
+hipError_t launch_pack_experts(const PackArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(pack_experts_kernel, dim3(2048), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

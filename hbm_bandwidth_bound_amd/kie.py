@@ -39,7 +39,11 @@ _U16PP = C.POINTER(_U16P)
 class kie_weights(C.Structure):
     _fields_ = [("embed", _U16P), ("final_norm", _U16P), ("lm_head", _U16P), ("attn_norm", _U16PP),
                 ("wq", _U16PP), ("wk", _U16PP), ("wv", _U16PP), ("wo", _U16PP), ("ffn_norm", _U16PP),
-                ("w_gate", _U16PP), ("w_up", _U16PP), ("w_down", _U16PP)]
+                ("w_gate", _U16PP), ("w_up", _U16PP), ("w_down", _U16PP), ("w_router", _U16PP),
+                ("moe_gate", _U16PP), ("moe_up", _U16PP), ("moe_down", _U16PP)]
+
+_LAYER_KEYS = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down", "w_router", "moe_gate",
+               "moe_up", "moe_down")
 
 
 class kie_sampling(C.Structure):
@@ -126,7 +130,9 @@ class Engine:
     """A decode context over torch-owned device buffers.
 
     weights: dict of torch int16/uint16-bit tensors on the device (keys as in kie_weights; per-layer
-    keys hold lists). The packed image, KV cache and workspace are allocated here as torch tensors.
+    keys hold lists; a dense model has no w_router/moe_* keys, a mixture-of-experts model no
+    w_gate/w_up/w_down). The packed image, KV cache and workspace are allocated here as torch
+    tensors.
     """
 
     def __init__(self, model, weights: Dict[str, object], max_seq: int, stream=None):
@@ -158,13 +164,15 @@ class Engine:
 
         keep = []
         fields = {}
-        for k in ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down"):
-            ptrs, a = arr(weights[k])
-            keep.append(a)
-            fields[k] = ptrs
+        for k in _LAYER_KEYS:
+            if k in weights:
+                ptrs, a = arr(weights[k])
+                keep.append(a)
+                fields[k] = ptrs
+            else:
+                fields[k] = C.cast(None, _U16PP)
         self._w = kie_weights(p(weights["embed"]), p(weights["final_norm"]), p(weights["lm_head"]),
-                              fields["attn_norm"], fields["wq"], fields["wk"], fields["wv"], fields["wo"],
-                              fields["ffn_norm"], fields["w_gate"], fields["w_up"], fields["w_down"])
+                              *[fields[k] for k in _LAYER_KEYS])
         self._keep = keep
         ctx = C.c_void_p()
         st = lib.kie_create(C.byref(self.cfg), C.byref(self._w), _ptr(self.packed), _ptr(self.kv),

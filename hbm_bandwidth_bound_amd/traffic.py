@@ -10,8 +10,14 @@ from __future__ import annotations
 
 
 def weight_bytes(m) -> int:
+    """Weight bytes one step reads. A mixture-of-experts layer reads its router and only the
+    routed experts (n_experts_active of them)."""
     d, q, kv, f, V, L = m.d_model, m.n_heads * m.head_dim, m.n_kv_heads * m.head_dim, m.ffn_dim, m.vocab_size, m.n_layers
-    per_layer_matrices = q * d + 2 * kv * d + d * q + 2 * f * d + d * f
+    if m.n_experts:
+        ffn = m.n_experts * d + m.n_experts_active * 3 * m.expert_ffn_dim * d
+    else:
+        ffn = 3 * f * d
+    per_layer_matrices = q * d + 2 * kv * d + d * q + ffn
     norms = (2 * L + 1) * d
     return 2 * (L * per_layer_matrices + V * d + norms + d)  # + one embedding row
 

@@ -48,8 +48,16 @@ enum {
 
 /* Model shape. Requirements checked by kie_create: d_model, n_heads*head_dim and ffn_dim are
  * multiples of 256; head_dim is 64 or 128; n_heads is a multiple of n_kv_heads; vocab_size and
- * d_model are even; the number of compute units is a multiple of n_kv_heads. The MoE fields
- * must be 0 (dense decoder). */
+ * d_model are even; the number of compute units is a multiple of n_kv_heads.
+ * n_experts == 0: dense decoder (the other two expert fields must be 0 too).
+ * n_experts > 0: every feed-forward block is a mixture of experts (the pages: only the routed
+ * experts' weights are read per token -- aikraft.ru «3000 токенов в секунду…», §02; agentlenshq.com,
+ * 《突破内存墙…》, opening section). A router [n_experts][d_model] gives one logit per expert; the
+ * n_experts_active experts with the largest logits (ties to the lower index) run, each a SwiGLU
+ * block of width expert_ffn_dim, and their outputs are summed with the weights
+ * softmax(logits) restricted to the chosen and renormalised to sum to 1. Then ffn_dim must be 0,
+ * n_experts even and at most 512, 1 <= n_experts_active <= min(8, n_experts), expert_ffn_dim a
+ * multiple of 256, and (kernel instantiation) n_heads / n_kv_heads == 8 with head_dim 128. */
 typedef struct {
   int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab_size;
   float rms_eps, rope_theta;
@@ -62,11 +70,15 @@ typedef struct {
  * The per-layer members are HOST arrays of n_layers device pointers.
  *   embed [V][d], final_norm [d], lm_head [V][d];
  *   attn_norm[l] [d], wq[l] [n_heads*hd][d], wk[l] and wv[l] [n_kv_heads*hd][d],
- *   wo[l] [d][n_heads*hd], ffn_norm[l] [d], w_gate[l] and w_up[l] [F][d], w_down[l] [d][F]. */
+ *   wo[l] [d][n_heads*hd], ffn_norm[l] [d], w_gate[l] and w_up[l] [F][d], w_down[l] [d][F].
+ * Mixture of experts (E experts of width Fe; w_gate, w_up, w_down are then unused and may be NULL):
+ *   w_router[l] [E][d], moe_gate[l] and moe_up[l] [E][Fe][d] (experts stacked), moe_down[l]
+ *   [E][d][Fe]. For a dense model these four may be NULL. */
 typedef struct {
   const uint16_t *embed, *final_norm, *lm_head;
   const uint16_t *const *attn_norm, *const *wq, *const *wk, *const *wv, *const *wo;
   const uint16_t *const *ffn_norm, *const *w_gate, *const *w_up, *const *w_down;
+  const uint16_t *const *w_router, *const *moe_gate, *const *moe_up, *const *moe_down;
 } kie_weights;
 
 /* Token choice after each step, made on the GPU (aikraft.ru «3000 токенов в секунду…», §04:
@@ -103,8 +115,10 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
 /* Process a prompt of n_tokens ids (device int32 [n_tokens]) at positions pos .. pos+n_tokens-1,
  * writing their K/V rows, then choose the next token (device int32 [1], first_token_dev) from the
  * logits of the last prompt position; those logits are written to last_logits_dev (device fp32
- * [V]) unless it is NULL. Advances the position by n_tokens. Errors: KIE_ERR_INVALID_ARG,
- * KIE_ERR_CAPACITY, KIE_ERR_STATE, KIE_ERR_HIP. */
+ * [V]) unless it is NULL. Advances the position by n_tokens. A dense model runs all but the last
+ * position as matrix-core GEMMs; a mixture-of-experts model runs every position, one after the
+ * other, through the decode program in one launch (each position routes its own experts).
+ * Errors: KIE_ERR_INVALID_ARG, KIE_ERR_CAPACITY, KIE_ERR_STATE, KIE_ERR_HIP. */
 kie_status kie_prefill(kie_ctx* ctx, const int32_t* tokens_dev, int32_t n_tokens, int32_t* first_token_dev,
                        float* last_logits_dev, const kie_sampling* sampling);
 

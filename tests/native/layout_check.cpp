@@ -1,6 +1,8 @@
 // Host-side check of the packed-stream geometry in layout.h: for every workgroup and stage, the
 // batches of the 8 waves cover each (pair, k-tile) exactly once, unit slots beyond the stage stay
-// empty, and the stream lengths add up to the packed image. Prints "ok" or the first violation.
+// empty, and the stream lengths add up to the packed image. With mixture-of-experts layers, the
+// expert region's placement is checked to be one-to-one as well. Prints "ok" or the first
+// violation.
 #include <cstdio>
 #include <cstdlib>
 #include <vector>
@@ -75,6 +77,7 @@ static int check(const Shape& s) {
       for (int32_t v = 0; v < kWaves; ++v) {
         int64_t t0 = wbase[(size_t)w * kWaves + v] + (int64_t)l * layer_batches(s, w, v) * kBatch;
         for (int st = (l == s.L ? ST_LM : ST_QKV); st <= (l == s.L ? ST_LM : ST_DN); ++st) {
+          if (!s.in_stream(st)) continue;
           const StageGeo g = stage_geo(s, st, w);
           const int32_t nbv = wave_batches(g, v);
           for (int32_t b = 0; b < nbv; ++b)
@@ -93,16 +96,49 @@ static int check(const Shape& s) {
         }
       }
   }
+  if (s.moe()) {  // expert region: every (layer, expert, pair, k-tile) has its own tile
+    const int64_t n = expert_tiles(s);
+    std::vector<uint8_t> seen((size_t)n, 0);
+    for (int32_t l = 0; l < s.L; ++l)
+      for (int32_t e = 0; e < s.E; ++e) {
+        for (int32_t p = 0; p < s.Fe; ++p)
+          for (int32_t kt = 0; kt < s.d / kTileK; ++kt) {
+            const int64_t t = expert_gu_tile(s, l, e, p, kt);
+            if (t < 0 || t >= n || seen[(size_t)t]++) {
+              std::printf("gate/up tile l=%d e=%d p=%d kt=%d misplaced\n", l, e, p, kt);
+              return 1;
+            }
+          }
+        for (int32_t p = 0; p < s.d / 2; ++p)
+          for (int32_t kt = 0; kt < s.Fe / kTileK; ++kt) {
+            const int64_t t = expert_dn_tile(s, l, e, p, kt);
+            if (t < 0 || t >= n || seen[(size_t)t]++) {
+              std::printf("down tile l=%d e=%d p=%d kt=%d misplaced\n", l, e, p, kt);
+              return 1;
+            }
+          }
+      }
+    if (packed_embed_offset(s) != (packed_stream_tiles(s) + n) * kTileBytes) {
+      std::printf("embedding offset does not follow the expert region\n");
+      return 1;
+    }
+  }
   std::printf("ok %lld tiles\n", (long long)total);
   return 0;
 }
 
 int main(int argc, char** argv) {
-  if (argc != 10) {
-    std::printf("usage: L d nq nkv hd F V max_seq nwg\n");
+  if (argc != 10 && argc != 13) {
+    std::printf("usage: L d nq nkv hd F V max_seq nwg [E A Fe]\n");
     return 2;
   }
   Shape s;
+  s.E = s.A = s.Fe = 0;
+  if (argc == 13) {  // mixture of experts: F is the width of the A routed experts
+    s.E = std::atoi(argv[10]);
+    s.A = std::atoi(argv[11]);
+    s.Fe = std::atoi(argv[12]);
+  }
   s.L = std::atoi(argv[1]);
   s.d = std::atoi(argv[2]);
   s.nq = std::atoi(argv[3]);
@@ -114,5 +150,6 @@ int main(int argc, char** argv) {
   s.nwg = std::atoi(argv[9]);
   s.eps = 1e-5f;
   s.theta = 10000.f;
+  if (s.moe()) s.F = s.A * s.Fe;
   return check(s);
 }

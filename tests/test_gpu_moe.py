@@ -1,0 +1,114 @@
+"""Mixture-of-experts decode on the GPU vs the CPU oracle, through the C ABI (needs an MI355X).
+
+The router's choice is an integer decision taken from fp32 logits on both sides (the A largest,
+ties to the lower index). The GPU's logits differ from the oracle's by rounding only (~1e-6
+relative), so the comparison is meaningful where the oracle's gap between the A-th and (A+1)-th
+router logit is well above that: every test first checks that this margin exceeds 1e-4 at every
+(position, layer) it compares. Logits are then compared at every step (rel-L2 <= 1e-3), greedy
+tokens wherever the oracle's top-2 gap exceeds 0.05, and the KV cache element-wise.
+"""
+import numpy as np
+import pytest
+
+from hbm_bandwidth_bound_amd import synth
+from tests.gpu_util import check_steps, rel_l2, say, to_device, top2_gap
+
+pytestmark = pytest.mark.gpu
+
+ROUTE_MARGIN = 1e-4
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def run_gpu(torch, eng, prompt, n_steps, V):
+    tokens = torch.tensor(np.asarray(prompt, dtype=np.int32), device="cuda")
+    last = torch.empty(V, dtype=torch.float32, device="cuda")
+    first = eng.prefill(tokens, logits_out=last)
+    out = torch.empty(n_steps, dtype=torch.int32, device="cuda")
+    logits = torch.empty((n_steps, V), dtype=torch.float32, device="cuda")
+    eng.generate(first, n_steps, out, logits)
+    eng.sync()
+    return int(first.item()), last.cpu().numpy(), out.cpu().numpy(), logits.cpu().numpy()
+
+
+def route_margin(z, A):
+    """Smallest gap between the A-th and (A+1)-th router logit over all (position, layer)."""
+    s = np.sort(np.asarray(z, dtype=np.float64), axis=-1)[..., ::-1]
+    return float(np.min(s[..., A - 1] - s[..., A]))
+
+
+def compare(torch, oracle_lib, cfg, w, wd, P, N, seed, label):
+    from hbm_bandwidth_bound_amd.kie import Engine
+    say(f"[{label}] prompt {P} + decode {N}")
+    eng = Engine(cfg, wd, P + N)
+    prompt = synth.prompt_ids(P, cfg.vocab_size, seed)
+    first, last, toks, logits = run_gpu(torch, eng, prompt, N, cfg.vocab_size)
+    om = oracle_lib.OracleModel(cfg, w, P + N)
+    z = om.record_routes(P + N)
+    ref_prompt = om.run(prompt)
+    ref = om.run([first] + [int(t) for t in toks[:-1]], start_pos=P)
+    om.stop_recording()
+    m = route_margin(z, cfg.n_experts_active)
+    say(f"  smallest router margin {m:.2e}")
+    assert m > ROUTE_MARGIN, f"{label}: a routing decision is within {ROUTE_MARGIN} of a tie; pick another seed"
+    e = rel_l2(last, ref_prompt[-1])
+    say(f"  prompt last-logits rel-L2 {e:.3e}")
+    assert e <= 1e-3
+    if top2_gap(ref_prompt[-1]) > 0.05:
+        assert first == int(np.argmax(ref_prompt[-1]))
+    worst, checked = check_steps(logits, ref, toks, label=label)
+    say(f"  decode worst rel-L2 {worst:.3e}, greedy checked on {checked}/{N} steps")
+    kg = eng.kv_view().cpu().numpy().view(np.uint16)
+    ko, vo = om.kv_view()
+    n = P + N
+    ek = rel_l2(synth.bf16_bits_to_f32(kg[:, 0, :, :n]), synth.bf16_bits_to_f32(ko[:, :, :n]))
+    ev = rel_l2(synth.bf16_bits_to_f32(kg[:, 1, :, :n]), synth.bf16_bits_to_f32(vo[:, :, :n]))
+    say(f"  cache rel-L2 K {ek:.3e} V {ev:.3e}")
+    assert ek <= 1e-3 and ev <= 1e-3
+    eng.close()
+
+
+@pytest.mark.parametrize("cfg", [synth.TINY_MOE, synth.SMALL_MOE], ids=lambda c: c.name)
+def test_moe_prompt_then_decode(torch_cuda, oracle_lib, cfg):
+    """16 experts of 1-tile rows with 4 active, and 32 experts of 3-tile rows with 8 active (each
+    down-projection unit of 8 k-tiles then spans three experts)."""
+    w = synth.make_weights_np(cfg, 0)
+    compare(torch_cuda, oracle_lib, cfg, w, to_device(w), 40, 12, 1, cfg.name)
+
+
+def test_moe_full_layer_shape(torch_cuda, oracle_lib):
+    """The 128-expert model's layer shape (d 2048, 32/4 heads, 8 of 128 experts of width 768,
+    vocabulary 151,936) with two layers: the launch geometry of the full model per layer."""
+    cfg = synth.MOE_2L
+    oracle_lib.set_threads(16)
+    try:
+        wd = synth.make_weights_torch(cfg, 0, device="cuda")
+        w = synth.weights_torch_to_np(wd)
+        compare(torch_cuda, oracle_lib, cfg, w, wd, 12, 4, 1, cfg.name)
+    finally:
+        oracle_lib.set_threads(1)
+
+
+def test_moe_rejects_unsupported_shapes(torch_cuda):
+    """Configurations the kernels do not handle are refused on the host, before any launch."""
+    from hbm_bandwidth_bound_amd import kie
+    lib = kie.load()
+    ok = synth.TINY_MOE
+    bad = [ok.scaled(n_experts=15), ok.scaled(n_experts_active=9, n_experts=16), ok.scaled(expert_ffn_dim=300),
+           ok.scaled(ffn_dim=1024), ok.scaled(n_experts_active=17)]
+    import ctypes as C
+    assert lib.kie_packed_weight_bytes(C.byref(kie.make_config(ok, 64))) > 0
+    for b in bad:
+        assert lib.kie_packed_weight_bytes(C.byref(kie.make_config(b, 64))) == 0, b
+    # a head grouping without a mixture-of-experts kernel instantiation
+    g2 = ok.scaled(n_kv_heads=4)
+    w = synth.make_weights_torch(g2, 0, device="cuda")
+    with pytest.raises(kie.KieError) as ei:
+        kie.Engine(g2, w, 64)
+    assert ei.value.status == -2

@@ -25,6 +25,11 @@ SHAPES = [
     (32, 4096, 32, 8, 128, 14336, 128256, 64, 256),   # 8B
     (3, 768, 12, 4, 64, 3072, 5000, 64, 96),          # 3-tile and 12-tile rows, 96 units
     (1, 512, 8, 8, 64, 1536, 1002, 64, 40),           # 2-tile rows, 6-tile F
+    # mixture of experts (F is ignored: A x Fe), + E A Fe
+    (2, 256, 8, 1, 128, 0, 4096, 64, 256, 16, 4, 256),          # tiny-moe
+    (2, 512, 8, 1, 128, 0, 4096, 64, 256, 32, 8, 768),          # small-moe: down units span experts
+    (2, 2048, 32, 4, 128, 0, 151936, 64, 256, 128, 8, 768),     # the 128-expert model's layers
+    (1, 768, 8, 1, 128, 0, 1000, 64, 40, 6, 3, 512),            # ragged: 3-tile rows, 40 CUs
 ]
 
 
