@@ -128,6 +128,10 @@ static kie_status make_shape(const kie_config* c, int nwg_override, Shape* s, st
     s->A = c->n_experts_active;
     s->Fe = c->expert_ffn_dim;
     s->F = s->A * s->Fe;  // width of the gathered expert activations
+    if (expert_tiles(*s) >= (int64_t)0xffffffff) {  // routed tiles are indexed with 32 bits
+      set_err(err, "the experts' weights exceed 4 TiB");
+      return KIE_ERR_UNSUPPORTED;
+    }
   }
   if (s->d % kTileK || s->qdim() % kTileK || s->F % kTileK) {
     set_err(err, "d_model (%d), n_heads*head_dim (%d) and ffn_dim (%d) must be multiples of %d", s->d, s->qdim(), s->F,

@@ -82,6 +82,8 @@ struct Lds {
   float* q;        // attention: the group's queries [G][hd], the current k [hd] and v [hd]
   float2* rope;    // (cos, sin) of the current position, hd/2 entries
   uint32_t* ctl;   // control words
+  int32_t* moe;    // mixture of experts: the layer's chosen experts [kMaxActive], then their
+                   // routing weights [kMaxActive] (fp32 bits)
   uint8_t* xb;     // one extra weight batch per wave (kBatch tiles), or null where LDS is short
 };
 enum Ctl : int { C_ABORT = 0, C_COUNT = 4 };
@@ -115,8 +117,9 @@ __host__ __device__ inline int32_t merge_floats(const Shape& s) {
 // The extra batch slots (8 KiB per wave) are placed where the rest leaves room for them.
 constexpr int32_t kLdsCapacity = 160 * 1024;
 constexpr int32_t kXbBytes = kWaves * kBatch * kTileBytes;
+__host__ __device__ inline int32_t moe_words(const Shape& s) { return s.moe() ? 2 * kMaxActive : 0; }
 __host__ __device__ inline int32_t lds_base_bytes(const Shape& s) {
-  return (merge_floats(s) + scr_floats(s) + (s.group() + 2) * s.hd + s.hd) * 4 + C_COUNT * 4;
+  return (merge_floats(s) + scr_floats(s) + (s.group() + 2) * s.hd + s.hd) * 4 + C_COUNT * 4 + moe_words(s) * 4;
 }
 __host__ __device__ inline bool xb_fits(const Shape& s) { return lds_base_bytes(s) + kXbBytes <= kLdsCapacity; }
 inline int32_t lds_bytes_for_impl(const Shape& s) { return lds_base_bytes(s) + (xb_fits(s) ? kXbBytes : 0); }
@@ -132,6 +135,8 @@ __device__ __forceinline__ Lds lds_map(uint8_t* smem, const Shape& s) {
   L.rope = (float2*)p; p += (size_t)s.hd * 4;
   L.ctl = (uint32_t*)p;
   p += C_COUNT * 4;  // 16-byte aligned: every piece above is a multiple of 4 floats
+  L.moe = (int32_t*)p;
+  p += moe_words(s) * 4;
   L.xb = xb_fits(s) ? p : nullptr;
   return L;
 }
@@ -239,21 +244,24 @@ struct Wk {
   // MOE. A step's batches are, per layer, layer_b fixed-stream batches and then dyn_b routed ones
   // (gate/up, then down), and finally the LM head's. A routed batch can be issued only once its
   // layer's experts are chosen: until then nxt stays empty (deferred) and the router boundary
-  // issues it. es/ew: the chosen experts of layer sel_key (= step * L + layer) and their weights.
+  // issues it. L.moe holds the experts of layer sel_key (= step * L + layer) and their weights.
   int32_t dyn_b = 0;
   int32_t sel_key = -1;
   bool deferred = false;
   const uint8_t* xreg = nullptr;  // expert region of the packed image
-  int32_t es[kMaxActive];
-  float ew[kMaxActive];
 
   __device__ __forceinline__ Wk(const KParams& p, const Lds& l, int32_t w_, int32_t v_, int32_t lane_)
       : P(p), L(l), w(w_), v(v_), lane(lane_), tid(v_ * kWave + lane_), fail(false) {
     layer_b = 0;
     for (int st = 0; st < ST_COUNT; ++st) {
+      if (!MOE && st == ST_RT) {  // dense layers have no router: constant zeros
+        g[st] = StageGeo{0, 0, 1, 1, 1, kBatch, 0};
+        nb[st] = 0;
+        continue;
+      }
       g[st] = stage_geo(P.s, st, w);
       nb[st] = wave_batches(g[st], v);
-      if (st <= ST_DN && P.s.in_stream(st)) layer_b += nb[st];
+      if (st <= ST_DN && (!MOE || P.s.in_stream(st))) layer_b += nb[st];
     }
     lm_b = nb[ST_LM];
     stream = P.packed + (size_t)P.wbase[w * kWaves + v] * kTileBytes;
@@ -262,11 +270,6 @@ struct Wk {
     if constexpr (MOE) {
       dyn_b = nb[ST_GU] + nb[ST_DN];
       xreg = P.packed + (size_t)P.wbase[P.s.nwg * kWaves] * kTileBytes;
-#pragma unroll
-      for (int i = 0; i < kMaxActive; ++i) {
-        es[i] = 0;
-        ew[i] = 0.f;
-      }
     }
   }
 
@@ -294,74 +297,34 @@ struct Wk {
     *jd = j - layer_b;
     return -1;
   }
-  __device__ __forceinline__ int32_t expert_of(int32_t slot) const {
-    switch (slot) {
-      case 1: return es[1];
-      case 2: return es[2];
-      case 3: return es[3];
-      case 4: return es[4];
-      case 5: return es[5];
-      case 6: return es[6];
-      case 7: return es[7];
-      default: return es[0];
-    }
-  }
-  __device__ __forceinline__ float weight_of(int32_t slot) const {
-    switch (slot) {
-      case 1: return ew[1];
-      case 2: return ew[2];
-      case 3: return ew[3];
-      case 4: return ew[4];
-      case 5: return ew[5];
-      case 6: return ew[6];
-      case 7: return ew[7];
-      default: return ew[0];
-    }
-  }
+  // routing weight of chosen expert `slot` (0 <= slot < A)
+  __device__ __forceinline__ float weight_of(int32_t slot) const { return __int_as_float(L.moe[kMaxActive + slot]); }
   // The 8 tile slots of routed batch jd of layer lb: f(b, resource of tile b). A slot of a missing
   // unit gets an empty resource (its load returns zeros). Gate/up pair gp is row gp mod Fe of
-  // chosen expert gp / Fe; k-tile t of a down pair lies in chosen expert t / (Fe / 256).
-  template <int KS, typename F>
-  __device__ __forceinline__ void routed_tiles_ks(const StageGeo& gs, bool gu, int32_t lb, int32_t bi, F f) const {
-    constexpr int UPB = kBatch / KS;
-    const Shape& s = P.s;
-    const int32_t kte = s.Fe / kTileK;
-#pragma unroll
-    for (int us = 0; us < UPB; ++us) {
-      const int32_t u = v + kWaves * (bi * UPB + us);
-      const bool valid = u < gs.nu;
-      const int32_t lp = gs.S == 1 ? u : u / gs.S, r = gs.S == 1 ? 0 : u - lp * gs.S;
-      const int32_t gp = gs.pb + lp;
-      if (gu) {
-        const int32_t slot = gp / s.Fe, p = gp - slot * s.Fe;
-        const int64_t t0 = expert_gu_tile(s, lb, expert_of(slot), p, r * KS);
-#pragma unroll
-        for (int tt = 0; tt < KS; ++tt)
-          f(us * KS + tt, make_rsrc(xreg + (valid ? (size_t)(t0 + tt) * kTileBytes : 0), valid ? kTileBytes : 0));
-      } else {
-        int32_t slot = (r * KS) / kte, kk = r * KS - slot * kte;
-#pragma unroll
-        for (int tt = 0; tt < KS; ++tt) {
-          const int64_t t = expert_dn_tile(s, lb, expert_of(slot), gp, kk);
-          f(us * KS + tt, make_rsrc(xreg + (valid ? (size_t)t * kTileBytes : 0), valid ? kTileBytes : 0));
-          if (++kk == kte) {
-            kk = 0;
-            ++slot;
-          }
-        }
-      }
-    }
-  }
+  // chosen expert gp / Fe; k-tile t of a down pair lies in chosen expert t / (Fe / 256). Lane b
+  // (mod 8) works out slot b's tile index; the 8 indices are then read lane by lane.
   template <typename F>
   __device__ __forceinline__ void routed_tiles(int32_t lb, int32_t jd, F f) const {
+    const Shape& s = P.s;
     const bool gu = jd < nb[ST_GU];
     const StageGeo gs = gu ? g[ST_GU] : g[ST_DN];
     const int32_t bi = gu ? jd : jd - nb[ST_GU];
-    switch (gs.ks) {
-      case 8: routed_tiles_ks<8>(gs, gu, lb, bi, f); break;
-      case 4: routed_tiles_ks<4>(gs, gu, lb, bi, f); break;
-      case 2: routed_tiles_ks<2>(gs, gu, lb, bi, f); break;
-      default: routed_tiles_ks<1>(gs, gu, lb, bi, f); break;
+    const int32_t b = lane & (kBatch - 1);
+    const int32_t us = b / gs.ks, tt = b - us * gs.ks;
+    const int32_t u = v + kWaves * (bi * gs.upb + us);
+    const int32_t lp = u / gs.S, r = u - lp * gs.S;
+    const int32_t gp = gs.pb + lp, kt = r * gs.ks + tt;
+    const int32_t kte = s.Fe / kTileK;
+    const int32_t slot = gu ? gp / s.Fe : kt / kte;
+    const bool live = u < gs.nu;
+    const int32_t e = live ? L.moe[slot] : 0;
+    const int64_t t = gu ? expert_gu_tile(s, lb, e, gp - slot * s.Fe, kt) : expert_dn_tile(s, lb, e, gp, kt - slot * kte);
+    const uint32_t t32 = live ? (uint32_t)t : 0xffffffffu;  // the region has fewer than 2^32 - 1 tiles
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const uint32_t ti = __builtin_amdgcn_readlane(t32, i);
+      const bool ok = ti != 0xffffffffu;
+      f(i, make_rsrc(xreg + (ok ? (size_t)ti * kTileBytes : 0), ok ? kTileBytes : 0));
     }
   }
   // 8 loads of batch (pidx, pstep); past the launch's last batch the resource is empty and the
@@ -369,8 +332,13 @@ struct Wk {
   // not chosen yet is left deferred.
   __device__ __forceinline__ void issue(v4u* buf) {
     const bool live = pstep < P.n_steps;
-    size_t off = live ? (size_t)pidx * kBatch * kTileBytes : 0;
-    if constexpr (MOE) {
+    if constexpr (!MOE) {
+      const __amdgpu_buffer_rsrc_t rs =
+          make_rsrc(stream + (live ? (size_t)pidx * kBatch * kTileBytes : 0), live ? kBatch * kTileBytes : 0);
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) buf[b] = load16(rs, (uint32_t)(lane * 16 + b * kTileBytes));
+    } else {
+      size_t off = live ? (size_t)pidx * kBatch * kTileBytes : 0;
       deferred = false;
       if (live) {
         int32_t lb = 0, jd = 0;
@@ -385,10 +353,10 @@ struct Wk {
         }
         off = (size_t)sidx * kBatch * kTileBytes;
       }
-    }
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(stream + off, live ? kBatch * kTileBytes : 0);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(stream + off, live ? kBatch * kTileBytes : 0);
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) buf[b] = load16(rs, (uint32_t)(lane * 16 + b * kTileBytes));
+      for (int b = 0; b < kBatch; ++b) buf[b] = load16(rs, (uint32_t)(lane * 16 + b * kTileBytes));
+    }
   }
   // the launch's first batch
   __device__ __forceinline__ void start() {
@@ -468,8 +436,8 @@ struct Wk {
   // MOE, at the router boundary of layer l: router logits (all E) are in scr. Every WG takes the
   // same decision: the A largest logits (ties to the lower index; NaN ranks lowest) and weights
   // w_i = exp(z_i - z_0) / sum_j exp(z_j - z_0) over the chosen, z_0 the largest -- the softmax
-  // over all experts restricted to the chosen and renormalised. Then the deferred batch, if any,
-  // is issued.
+  // over all experts restricted to the chosen and renormalised -- into L.moe. Then the deferred
+  // batch, if any, is issued.
   __device__ __forceinline__ void route(int32_t step, int32_t l) {
     const Shape& s = P.s;
     int32_t* sel = (int32_t*)L.part;  // free between the router stage's finalize and gate/up
@@ -485,25 +453,23 @@ struct Wk {
       if (rank < s.A) sel[rank] = tid;
     }
     bar();
-    float zs[kMaxActive];
-#pragma unroll
-    for (int r = 0; r < kMaxActive; ++r) {
-      int32_t e = r < s.A ? (int32_t)__builtin_amdgcn_readfirstlane(lds_ld((const uint32_t*)&sel[r])) : 0;
+    if (v == 0) {  // one wave turns the ranks into the table of chosen experts and weights
+      const int32_t r = lane;
+      int32_t e = r < s.A ? sel[r] : 0;
       e = e < 0 ? 0 : (e >= s.E ? s.E - 1 : e);
-      es[r] = e;
-      const float z = L.scr[e];
-      zs[r] = z == z ? z : -INFINITY;
-    }
-    const float z0 = zs[0];
-    float sum = 0.f;
+      float z = L.scr[e];
+      z = z == z ? z : -INFINITY;
+      const float z0 = readlane_f(z, 0);
+      const float x = r < s.A ? expf(z - z0) : 0.f;
+      float sum = 0.f;
 #pragma unroll
-    for (int r = 0; r < kMaxActive; ++r) {
-      zs[r] = r < s.A ? expf(zs[r] - z0) : 0.f;
-      sum += zs[r];
+      for (int i = 0; i < kMaxActive; ++i) sum += readlane_f(x, i);  // in rank order
+      if (r < kMaxActive) {
+        L.moe[r] = e;
+        L.moe[kMaxActive + r] = __float_as_int(x / sum);
+      }
     }
-#pragma unroll
-    for (int r = 0; r < kMaxActive; ++r) ew[r] = zs[r] / sum;
-    bar();  // sel and scr are read before the gate/up stage writes part
+    bar();  // the table is complete, and sel and scr are read before the gate/up stage writes part
     sel_key = step * s.L + l;
     if (deferred) issue(nxt);
   }
@@ -801,9 +767,14 @@ __device__ __forceinline__ void attention(WK& K, const Att& at, int32_t l, int32
   }
   const uint64_t ta = TR_NOW();
   const float scale = 1.4426950408889634f / sqrtf((float)HD);  // softmax in the exp2 domain
-  float qr[G][8];
+  // With 4 or more query heads per KV head the queries are read from LDS at each use: held in
+  // registers next to the accumulators and the weight batch in flight they would spill, and a
+  // spill reload waits behind that batch's loads.
+  constexpr bool kQInLds = G >= 4;
+  constexpr int GR = kQInLds ? 1 : G;
+  float qr[GR][8];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
+  for (int g = 0; g < GR; ++g) {
     const v4f a = *(const v4f*)(L.q + g * HD + dg * 8);
     const v4f b = *(const v4f*)(L.q + g * HD + dg * 8 + 4);
     qr[g][0] = a.x; qr[g][1] = a.y; qr[g][2] = a.z; qr[g][3] = a.w;
@@ -825,8 +796,21 @@ __device__ __forceinline__ void attention(WK& K, const Att& at, int32_t l, int32
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float d = 0.f;
+      if constexpr (kQInLds) {
+        const v4f a = *(const v4f*)(L.q + g * HD + dg * 8);
+        const v4f b = *(const v4f*)(L.q + g * HD + dg * 8 + 4);
+        d = fmaf(a.x, kf[0], d);
+        d = fmaf(a.y, kf[1], d);
+        d = fmaf(a.z, kf[2], d);
+        d = fmaf(a.w, kf[3], d);
+        d = fmaf(b.x, kf[4], d);
+        d = fmaf(b.y, kf[5], d);
+        d = fmaf(b.z, kf[6], d);
+        d = fmaf(b.w, kf[7], d);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) d = fmaf(qr[g][e], kf[e], d);
+        for (int e = 0; e < 8; ++e) d = fmaf(qr[g][e], kf[e], d);
+      }
       d = LPP == 16 ? row16_sum(d) : row8_sum(d);
       const float sc = d * scale;
       if (valid) {
@@ -1278,7 +1262,24 @@ __device__ __forceinline__ void decode(Wk<MOE>& K) {
       }
       const uint64_t tb = TR_NOW();
       const int bnd_run = bnd;
-      switch (bnd) {
+      bool routed = false;  // the router boundary of a mixture-of-experts layer (not in the switch,
+                            // so that the dense program is compiled as if it did not exist)
+      if constexpr (MOE) {
+        if (bnd == B_RT) {  // router logits -> gather all E -> the layer's experts (the same in every WG)
+          bar();
+          uint64_t* rx = ex + X.rt + (int64_t)l * s.E;
+          K.finalize(K.g[ST_RT], [&](int32_t gp, float ya, float yb) {
+            st_x(rx + 2 * gp, tag_f(ya, ep));
+            st_x(rx + 2 * gp + 1, tag_f(yb, ep));
+          });
+          K.template fetch_f32<8>(rx, s.E, L.scr, ep, false);
+          K.route(step, l);
+          st = ST_GU;
+          bnd = B_GU;
+          routed = true;
+        }
+      }
+      if (!routed) switch (bnd) {
         case B_START: {  // embedding row -> residual stream, RMSNorm of layer 0
           if (tid < s.hd / 2) L.rope[tid] = P.rope[(int64_t)pos * (s.hd / 2) + tid];
           K.prefetch_gain(P.norms);
@@ -1354,21 +1355,6 @@ __device__ __forceinline__ void decode(Wk<MOE>& K) {
           K.norm_to_act(ss, xres);
           st = MOE ? ST_RT : ST_GU;
           bnd = MOE ? B_RT : B_GU;
-          break;
-        }
-        case B_RT: {  // router logits -> gather all E -> the layer's experts (identical in every WG)
-          if constexpr (MOE) {
-            bar();
-            uint64_t* rx = ex + X.rt + (int64_t)l * s.E;
-            K.finalize(K.g[ST_RT], [&](int32_t gp, float ya, float yb) {
-              st_x(rx + 2 * gp, tag_f(ya, ep));
-              st_x(rx + 2 * gp + 1, tag_f(yb, ep));
-            });
-            K.fetch_f32(rx, s.E, L.scr, ep, false);
-            K.route(step, l);
-          }
-          st = ST_GU;
-          bnd = B_GU;
           break;
         }
         case B_GU: {  // SwiGLU outputs -> gather h
