@@ -522,6 +522,7 @@ static kie_status launch(kie_ctx* ctx, const int32_t* first, int32_t n, const in
   P.seed = smp ? smp->seed : 0;
   P.timeout_ticks = ctx->timeout_ticks;
   P.skew = ctx->skew;
+  P.xb_lds = (uint32_t)lds_slot_offset(ctx->s);
   void* args[] = {&P};
   const void* fn = (const void*)(lm_last_only ? ctx->prompt_kernel : ctx->kernel);
   HIP_TRY(&ctx->last_error,

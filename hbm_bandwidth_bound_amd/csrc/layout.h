@@ -282,14 +282,16 @@ KIE_HD int64_t packed_stream_tiles(const Shape& s) {
   return t;
 }
 // Expert region, in tiles from its start: gate/up tiles [L][E][Fe pairs][d / 256] (pair p = row p
-// of the expert's W_gate (A) and W_up (B)), then down tiles [L][E][d / 2 pairs][Fe / 256] (pair p
-// = rows 2p, 2p + 1 of the expert's W_down).
+// of the expert's W_gate (A) and W_up (B)), then down tiles [L][d / 2 pairs][E][Fe / 256] (pair p
+// = rows 2p, 2p + 1 of the expert's W_down). A WG's gate/up share lies in one expert, so its
+// tiles are contiguous; its down share (the same output rows in every chosen expert) spans all
+// experts, so the experts are the inner index there and its tiles stay within one short span.
 KIE_HD int64_t expert_gu_tile(const Shape& s, int32_t l, int32_t e, int32_t p, int32_t kt) {
   return (((int64_t)l * s.E + e) * s.Fe + p) * (s.d / kTileK) + kt;
 }
 KIE_HD int64_t expert_gu_tiles(const Shape& s) { return (int64_t)s.L * s.E * s.Fe * (s.d / kTileK); }
 KIE_HD int64_t expert_dn_tile(const Shape& s, int32_t l, int32_t e, int32_t p, int32_t kt) {
-  return expert_gu_tiles(s) + (((int64_t)l * s.E + e) * (s.d / 2) + p) * (s.Fe / kTileK) + kt;
+  return expert_gu_tiles(s) + (((int64_t)l * (s.d / 2) + p) * s.E + e) * (s.Fe / kTileK) + kt;
 }
 KIE_HD int64_t expert_tiles(const Shape& s) { return s.moe() ? 2 * expert_gu_tiles(s) : 0; }
 KIE_HD int64_t packed_expert_offset(const Shape& s) { return packed_stream_tiles(s) * kTileBytes; }

@@ -43,11 +43,14 @@ struct KParams {
   int64_t timeout_ticks;     // per wait, in s_memrealtime ticks (100 MHz)
   uint32_t skew;             // > 0: each WG idles a pseudo-random 0..skew-1 x ~3.4 us before
                              // every stage boundary (protocol stress; results must not change)
+  uint32_t xb_lds;           // byte offset of the extra-batch LDS slots in the dynamic LDS
+                             // (lds_slot_offset; used where the slot is read in assembly)
 };
 
 typedef void (*KernelFn)(KParams);
 KernelFn decode_kernel_for(int group, int head_dim, bool prompt, bool moe);
 int32_t lds_bytes_for(const Shape& s);
+int32_t lds_slot_offset(const Shape& s);  // where the extra-batch slots start in the dynamic LDS
 int32_t topk_capacity_floats(const Shape& s);  // WG-local floats available to the top-k merge
 
 // set-up kernels (pack.hip)

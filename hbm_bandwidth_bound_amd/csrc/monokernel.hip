@@ -10,6 +10,7 @@ KernelFn kernel_hd128(int G, bool prompt);
 KernelFn kernel_moe(int G, int HD, bool prompt);
 
 int32_t lds_bytes_for(const Shape& s) { return lds_bytes_for_impl(s); }
+int32_t lds_slot_offset(const Shape& s) { return xb_fits(s) ? lds_base_bytes(s) : 0; }
 int32_t topk_capacity_floats(const Shape& s) { return merge_floats(s); }
 
 KernelFn decode_kernel_for(int G, int HD, bool prompt, bool moe) {

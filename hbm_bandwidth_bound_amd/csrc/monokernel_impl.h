@@ -44,6 +44,9 @@
 
 namespace kie {
 
+// The kernels' dynamic LDS (the layout of lds_map).
+extern __shared__ __align__(16) uint8_t kie_smem[];
+
 // Optional per-wave cycle counters (compile with -DKIE_TRACE); free in normal builds.
 #ifdef KIE_TRACE
 #define TR_NOW() __builtin_readcyclecounter()
@@ -220,6 +223,34 @@ __device__ __forceinline__ bool better(float v, int32_t i, float bv, int32_t bi)
   return v > bv || (v == bv && i < bi);
 }
 
+// Candidate (z, id) as one unsigned 64-bit key that orders like the candidate order: an
+// order-preserving image of the float bits above, the complement of the id below (a lower id
+// wins a tie). z is never NaN or -0 here.
+__device__ __forceinline__ uint64_t cand_key(float v, int32_t id) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t hi = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)hi << 32) | (uint32_t)(0x7fffffff - id);
+}
+__device__ __forceinline__ float key_value(uint64_t k) {
+  const uint32_t hi = (uint32_t)(k >> 32);
+  return __uint_as_float((hi & 0x80000000u) ? (hi & 0x7fffffffu) : ~hi);
+}
+__device__ __forceinline__ int32_t key_id(uint64_t k) { return 0x7fffffff - (int32_t)(uint32_t)k; }
+// Number of keys of kk[0 .. n) (16-byte aligned) greater than key; eight per step with 16-byte
+// LDS reads, so that the reads overlap.
+__device__ __forceinline__ int32_t count_greater(const uint64_t* kk, int32_t n, uint64_t key) {
+  typedef uint64_t v2u64 __attribute__((ext_vector_type(2)));
+  int32_t c = 0, i = 0;
+  for (; i + 8 <= n; i += 8) {
+    const v2u64 a = *(const v2u64*)(kk + i), b = *(const v2u64*)(kk + i + 2);
+    const v2u64 e = *(const v2u64*)(kk + i + 4), f = *(const v2u64*)(kk + i + 6);
+    c += (a.x > key ? 1 : 0) + (a.y > key ? 1 : 0) + (b.x > key ? 1 : 0) + (b.y > key ? 1 : 0) + (e.x > key ? 1 : 0) +
+         (e.y > key ? 1 : 0) + (f.x > key ? 1 : 0) + (f.y > key ? 1 : 0);
+  }
+  for (; i < n; ++i) c += kk[i] > key ? 1 : 0;
+  return c;
+}
+
 // ------------------------------------------------------------------------------------------
 // One wave's state: its weight stream, the batch in flight, the WG's stage geometry. MOE: the
 // layers are mixture-of-experts layers, whose gate/up and down batches are read from the expert
@@ -299,32 +330,61 @@ struct Wk {
   }
   // routing weight of chosen expert `slot` (0 <= slot < A)
   __device__ __forceinline__ float weight_of(int32_t slot) const { return __int_as_float(L.moe[kMaxActive + slot]); }
-  // The 8 tile slots of routed batch jd of layer lb: f(b, resource of tile b). A slot of a missing
-  // unit gets an empty resource (its load returns zeros). Gate/up pair gp is row gp mod Fe of
-  // chosen expert gp / Fe; k-tile t of a down pair lies in chosen expert t / (Fe / 256). Lane b
-  // (mod 8) works out slot b's tile index; the 8 indices are then read lane by lane.
-  template <typename F>
-  __device__ __forceinline__ void routed_tiles(int32_t lb, int32_t jd, F f) const {
+  // Tile index (in the expert region) of slot (lane mod 8) of routed batch jd of layer lb, or
+  // 0xffffffff for a slot of a missing unit. Gate/up pair gp is row gp mod Fe of chosen expert
+  // gp / Fe; k-tile t of a down pair lies in chosen expert t / (Fe / 256). Callers read the 8
+  // indices lane by lane.
+  __device__ __forceinline__ uint32_t routed_index(int32_t lb, int32_t jd) const {
     const Shape& s = P.s;
     const bool gu = jd < nb[ST_GU];
     const StageGeo gs = gu ? g[ST_GU] : g[ST_DN];
     const int32_t bi = gu ? jd : jd - nb[ST_GU];
     const int32_t b = lane & (kBatch - 1);
-    const int32_t us = b / gs.ks, tt = b - us * gs.ks;
+    const int32_t lks = gs.ks == 8 ? 3 : (gs.ks == 4 ? 2 : (gs.ks == 2 ? 1 : 0));
+    const int32_t us = b >> lks, tt = b & (gs.ks - 1);
     const int32_t u = v + kWaves * (bi * gs.upb + us);
-    const int32_t lp = u / gs.S, r = u - lp * gs.S;
+    const int32_t lp = gs.S == 1 ? u : u / gs.S, r = u - lp * gs.S;
     const int32_t gp = gs.pb + lp, kt = r * gs.ks + tt;
     const int32_t kte = s.Fe / kTileK;
-    const int32_t slot = gu ? gp / s.Fe : kt / kte;
+    // chosen-expert slot of the tile: gp / Fe (gate/up) or kt / kte (down), slot < A <= 8
+    const int32_t q = gu ? gp : kt, span = gu ? s.Fe : kte;
+    int32_t slot = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxActive; ++i) slot += q >= i * span ? 1 : 0;
     const bool live = u < gs.nu;
     const int32_t e = live ? L.moe[slot] : 0;
     const int64_t t = gu ? expert_gu_tile(s, lb, e, gp - slot * s.Fe, kt) : expert_dn_tile(s, lb, e, gp, kt - slot * kte);
-    const uint32_t t32 = live ? (uint32_t)t : 0xffffffffu;  // the region has fewer than 2^32 - 1 tiles
+    return live ? (uint32_t)t : 0xffffffffu;  // the region has fewer than 2^32 - 1 tiles
+  }
+  // MOE: where the 8 tiles of batch (pidx, pstep) are -- the fixed stream, the expert region
+  // (routed), or nowhere (past the launch, or a routed batch whose experts are not chosen yet:
+  // deferred). f(b, resource of tile b) for b < 8; an empty resource loads zeros.
+  template <typename F>
+  __device__ __forceinline__ void batch_tiles(F f) {
+    const bool live = pstep < P.n_steps;
+    bool stat = false, routed = false;
+    size_t off = 0;
+    uint32_t t32 = 0xffffffffu;
+    deferred = false;
+    if (live) {
+      int32_t lb = 0, jd = 0;
+      const int32_t sidx = locate(&lb, &jd);
+      if (sidx >= 0) {
+        stat = true;
+        off = (size_t)sidx * kBatch * kTileBytes;
+      } else if (sel_key == pstep * P.s.L + lb) {
+        routed = true;
+        t32 = routed_index(lb, jd);
+      } else {
+        deferred = true;
+      }
+    }
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const uint32_t ti = __builtin_amdgcn_readlane(t32, i);
-      const bool ok = ti != 0xffffffffu;
-      f(i, make_rsrc(xreg + (ok ? (size_t)ti * kTileBytes : 0), ok ? kTileBytes : 0));
+    for (int b = 0; b < kBatch; ++b) {
+      const uint32_t ti = routed ? __builtin_amdgcn_readlane(t32, b) : 0xffffffffu;
+      const bool okr = ti != 0xffffffffu;
+      const uint8_t* base = okr ? xreg + (size_t)ti * kTileBytes : stream + off + (size_t)b * kTileBytes;
+      f(b, make_rsrc(base, (okr || stat) ? kTileBytes : 0));
     }
   }
   // 8 loads of batch (pidx, pstep); past the launch's last batch the resource is empty and the
@@ -338,24 +398,8 @@ struct Wk {
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) buf[b] = load16(rs, (uint32_t)(lane * 16 + b * kTileBytes));
     } else {
-      size_t off = live ? (size_t)pidx * kBatch * kTileBytes : 0;
-      deferred = false;
-      if (live) {
-        int32_t lb = 0, jd = 0;
-        const int32_t sidx = locate(&lb, &jd);
-        if (sidx < 0) {
-          if (sel_key != pstep * P.s.L + lb) {
-            deferred = true;
-            return;
-          }
-          routed_tiles(lb, jd, [&](int b, __amdgpu_buffer_rsrc_t rs) { buf[b] = load16(rs, (uint32_t)(lane * 16)); });
-          return;
-        }
-        off = (size_t)sidx * kBatch * kTileBytes;
-      }
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(stream + off, live ? kBatch * kTileBytes : 0);
-#pragma unroll
-      for (int b = 0; b < kBatch; ++b) buf[b] = load16(rs, (uint32_t)(lane * 16 + b * kTileBytes));
+      // always 8 loads into buf (zeros for a deferred batch), so that every path writes it alike
+      batch_tiles([&](int b, __amdgpu_buffer_rsrc_t rs) { buf[b] = load16(rs, (uint32_t)(lane * 16)); });
     }
   }
   // the launch's first batch
@@ -368,14 +412,38 @@ struct Wk {
     if (xnext) {
       // The batch in the LDS slot. At least nxt's kBatch loads were issued after its loads, and
       // the counter drains in issue order, so with at most kBatch operations outstanding the slot
-      // is filled. (A deferred nxt has issued nothing: then everything is waited for.)
-      if (MOE && deferred)
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kBatch) : "memory");
-      const uint8_t* xs = L.xb + (size_t)v * kBatch * kTileBytes + lane * 16;
+      // is filled.
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kBatch) : "memory");
+      if constexpr (MOE) {
+        // The lane's slot address is formed inside the block from the lane id and the wave's
+        // slot base (the kernel-argument offset of the slots, a scalar), so that no long-lived
+        // register holds it: where registers are short it would be spilled, and reloading it from
+        // scratch memory would wait behind the weight loads in flight. The reads complete inside
+        // the block.
+        const uint32_t sb = lds_addr(kie_smem) + P.xb_lds + (uint32_t)v * (kBatch * kTileBytes);
+        uint32_t a;
+        asm volatile(
+            "v_mbcnt_lo_u32_b32 %8, -1, 0\n"
+            "v_mbcnt_hi_u32_b32 %8, -1, %8\n"
+            "v_lshl_add_u32 %8, %8, 4, %9\n"
+            "ds_read_b128 %0, %8\n"
+            "ds_read_b128 %1, %8 offset:1024\n"
+            "ds_read_b128 %2, %8 offset:2048\n"
+            "ds_read_b128 %3, %8 offset:3072\n"
+            "ds_read_b128 %4, %8 offset:4096\n"
+            "ds_read_b128 %5, %8 offset:5120\n"
+            "ds_read_b128 %6, %8 offset:6144\n"
+            "ds_read_b128 %7, %8 offset:7168\n"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(cur[0]), "=&v"(cur[1]), "=&v"(cur[2]), "=&v"(cur[3]), "=&v"(cur[4]), "=&v"(cur[5]),
+              "=&v"(cur[6]), "=&v"(cur[7]), "=&v"(a)
+            : "s"(sb)
+            : "memory");
+      } else {
+        const uint8_t* xs = L.xb + (size_t)v * kBatch * kTileBytes + lane * 16;
 #pragma unroll
-      for (int b = 0; b < kBatch; ++b) cur[b] = *(const v4u*)(xs + b * kTileBytes);
+        for (int b = 0; b < kBatch; ++b) cur[b] = *(const v4u*)(xs + b * kTileBytes);
+      }
       xnext = false;
       return;
     }
@@ -396,30 +464,19 @@ struct Wk {
     if (L.xb == nullptr || xpend || xnext) return;
     const uint32_t base = lds_addr(L.xb + (size_t)v * kBatch * kTileBytes);
     if constexpr (MOE) {
-      if (deferred) return;  // nxt itself is not issued yet
+      if (deferred) return;  // nxt itself holds no data yet
       const int32_t sp = pidx, ss = pstep;
       advance();
-      if (pstep < P.n_steps) {
-        int32_t lb = 0, jd = 0;
-        const int32_t sidx = locate(&lb, &jd);
-        if (sidx < 0) {
-          if (sel_key != pstep * P.s.L + lb) {  // experts not chosen yet: leave it to the stream
-            pidx = sp;
-            pstep = ss;
-            return;
-          }
-          routed_tiles(lb, jd, [&](int b, __amdgpu_buffer_rsrc_t rs) {
-            load16_lds(rs, (uint32_t)(lane * 16), base + b * kTileBytes);
-          });
-        } else {
-          const __amdgpu_buffer_rsrc_t rs = make_rsrc(stream + (size_t)sidx * kBatch * kTileBytes, kBatch * kTileBytes);
-#pragma unroll
-          for (int b = 0; b < kBatch; ++b) load16_lds(rs, (uint32_t)(lane * 16 + b * kTileBytes), base + b * kTileBytes);
-        }
-      } else {
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(stream, 0);
-#pragma unroll
-        for (int b = 0; b < kBatch; ++b) load16_lds(rs, (uint32_t)(lane * 16 + b * kTileBytes), base + b * kTileBytes);
+      bool later = false;  // a routed batch whose experts are not chosen yet: leave it to the stream
+      batch_tiles([&](int b, __amdgpu_buffer_rsrc_t rs) {
+        if (!deferred) load16_lds(rs, (uint32_t)(lane * 16), base + b * kTileBytes);
+      });
+      later = deferred;
+      if (later) {
+        deferred = false;
+        pidx = sp;
+        pstep = ss;
+        return;
       }
       xpend = true;
       return;
@@ -440,19 +497,28 @@ struct Wk {
   // batch, if any, is issued.
   __device__ __forceinline__ void route(int32_t step, int32_t l) {
     const Shape& s = P.s;
-    int32_t* sel = (int32_t*)L.part;  // free between the router stage's finalize and gate/up
+    // part is free between the router stage's finalize and gate/up: the E candidate keys (the
+    // argmax order as one 64-bit integer; NaN ranks as -inf and -0 as +0), then the chosen ids
+    uint64_t* keys = (uint64_t*)L.part;
+    int32_t* sel = (int32_t*)(keys + s.E);
+    const uint64_t trk = TR_NOW();
+    uint64_t key = 0;
     if (tid < s.E) {
       float z = L.scr[tid];
-      z = z == z ? z : -INFINITY;
-      int32_t rank = 0;
-      for (int32_t j = 0; j < s.E; ++j) {
-        float zj = L.scr[j];
-        zj = zj == zj ? zj : -INFINITY;
-        rank += better(zj, j, z, tid) ? 1 : 0;
-      }
-      if (rank < s.A) sel[rank] = tid;
+      z = z == z ? (z == 0.f ? 0.f : z) : -INFINITY;
+      key = cand_key(z, tid);
+      keys[tid] = key;
     }
     bar();
+    if (tid < s.E) {
+      const int32_t rank = count_greater(keys, s.E, key);
+      if (rank < s.A) sel[rank] = tid;
+    }
+    uint64_t tq = TR_NOW();
+    tr.add(31, tq - trk);
+    bar();
+    tr.add(19, TR_NOW() - tq);
+    tq = TR_NOW();
     if (v == 0) {  // one wave turns the ranks into the table of chosen experts and weights
       const int32_t r = lane;
       int32_t e = r < s.A ? sel[r] : 0;
@@ -470,8 +536,15 @@ struct Wk {
       }
     }
     bar();  // the table is complete, and sel and scr are read before the gate/up stage writes part
+    tr.add(20, TR_NOW() - tq);
+    tq = TR_NOW();
     sel_key = step * s.L + l;
+    // The first routed batches could not be prefetched: start two now (registers and LDS slot).
     if (deferred) issue(nxt);
+    tr.add(21, TR_NOW() - tq);
+    tq = TR_NOW();
+    issue_x();
+    tr.add(22, TR_NOW() - tq);
   }
 
   // ------------------------------------------------------------ GEMV of one stage
@@ -770,115 +843,220 @@ __device__ __forceinline__ void attention(WK& K, const Att& at, int32_t l, int32
   // With 4 or more query heads per KV head the queries are read from LDS at each use: held in
   // registers next to the accumulators and the weight batch in flight they would spill, and a
   // spill reload waits behind that batch's loads.
-  constexpr bool kQInLds = G >= 4;
-  constexpr int GR = kQInLds ? 1 : G;
-  float qr[GR][8];
+  if constexpr (G > 4) {
+    // Two passes of 4 query heads over the chunk's K/V tiles (the second pass loads them again,
+    // from L2): the accumulators of 8 heads at once would not fit next to the weight batch in
+    // flight without spilling.
+    constexpr int GP = 4;
+    float* ws = L.scr + v * G * (HD + 2);
+#pragma unroll 1
+    for (int g0 = 0; g0 < G; g0 += GP) {
+      if (g0 > 0 && nbw > 0) kv_issue(0, kn, vn);
+      float m[GP], ls[GP], acc[GP][8];
 #pragma unroll
-  for (int g = 0; g < GR; ++g) {
-    const v4f a = *(const v4f*)(L.q + g * HD + dg * 8);
-    const v4f b = *(const v4f*)(L.q + g * HD + dg * 8 + 4);
-    qr[g][0] = a.x; qr[g][1] = a.y; qr[g][2] = a.z; qr[g][3] = a.w;
-    qr[g][4] = b.x; qr[g][5] = b.y; qr[g][6] = b.z; qr[g][7] = b.w;
-  }
-  float m[G], ls[G], acc[G][8];
+      for (int g = 0; g < GP; ++g) {
+        m[g] = -INFINITY;
+        ls[g] = 0.f;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = -INFINITY;
-    ls[g] = 0.f;
+        for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+      }
+      auto update = [&](const v4u kw, const v4u vw, bool valid) {
+        const float kf[8] = {bf16lo(kw.x), bf16hi(kw.x), bf16lo(kw.y), bf16hi(kw.y),
+                             bf16lo(kw.z), bf16hi(kw.z), bf16lo(kw.w), bf16hi(kw.w)};
+        const float vf[8] = {bf16lo(vw.x), bf16hi(vw.x), bf16lo(vw.y), bf16hi(vw.y),
+                             bf16lo(vw.z), bf16hi(vw.z), bf16lo(vw.w), bf16hi(vw.w)};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
-  }
-  auto update = [&](const v4u kw, const v4u vw, bool valid) {
-    const float kf[8] = {bf16lo(kw.x), bf16hi(kw.x), bf16lo(kw.y), bf16hi(kw.y),
-                         bf16lo(kw.z), bf16hi(kw.z), bf16lo(kw.w), bf16hi(kw.w)};
-    const float vf[8] = {bf16lo(vw.x), bf16hi(vw.x), bf16lo(vw.y), bf16hi(vw.y),
-                         bf16lo(vw.z), bf16hi(vw.z), bf16lo(vw.w), bf16hi(vw.w)};
+        for (int g = 0; g < GP; ++g) {
+          const v4f a = *(const v4f*)(L.q + (g0 + g) * HD + dg * 8);
+          const v4f b = *(const v4f*)(L.q + (g0 + g) * HD + dg * 8 + 4);
+          float d = 0.f;
+          d = fmaf(a.x, kf[0], d);
+          d = fmaf(a.y, kf[1], d);
+          d = fmaf(a.z, kf[2], d);
+          d = fmaf(a.w, kf[3], d);
+          d = fmaf(b.x, kf[4], d);
+          d = fmaf(b.y, kf[5], d);
+          d = fmaf(b.z, kf[6], d);
+          d = fmaf(b.w, kf[7], d);
+          d = LPP == 16 ? row16_sum(d) : row8_sum(d);
+          const float sc = d * scale;
+          if (valid) {
+            const float mn = fmaxf(m[g], sc);
+            const float c = exp2f(m[g] - mn);  // 0 while m is -inf
+            const float pr = exp2f(sc - mn);
+            ls[g] = fmaf(ls[g], c, pr);
 #pragma unroll
+            for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(acc[g][e], c, pr * vf[e]);
+            m[g] = mn;
+          }
+        }
+      };
+      for (int32_t bi = 0; bi < nbw; ++bi) {
+        v4u kc[AB], vc[AB];
+#pragma unroll
+        for (int e = 0; e < AB; ++e) {
+          kc[e] = kn[e];
+          vc[e] = vn[e];
+        }
+        if (bi + 1 < nbw) kv_issue(bi + 1, kn, vn);
+#pragma unroll
+        for (int e = 0; e < AB; ++e) {
+          const int32_t i = bi * AB + e;
+          if (i < ntw) update(kc[e], vc[e], (v + kWaves * i) * PPT + lpos < at.ncache);
+        }
+      }
+      if (at.has_p && v == at.nkt % kWaves) {  // the current position, rounded to bf16 like the cache
+        auto cur_row = [&](const float* src) {
+          uint32_t b[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) b[e] = f32_to_bf16(src[dg * 8 + e]);
+          return v4u{b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16)};
+        };
+        update(cur_row(L.q + G * HD), cur_row(L.q + (G + 1) * HD), lpos == 0);
+      }
+#pragma unroll
+      for (int off = LPP; off < kWave; off <<= 1) {  // the position rows of the wave
+#pragma unroll
+        for (int g = 0; g < GP; ++g) {
+          const float mo = __shfl_xor(m[g], off, kWave);
+          const float lo = __shfl_xor(ls[g], off, kWave);
+          const float M = fmaxf(m[g], mo);
+          const float f = m[g] == -INFINITY ? 0.f : exp2f(m[g] - M);
+          const float fo = mo == -INFINITY ? 0.f : exp2f(mo - M);
+          ls[g] = ls[g] * f + lo * fo;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float ao = __shfl_xor(acc[g][e], off, kWave);
+            acc[g][e] = acc[g][e] * f + ao * fo;
+          }
+          m[g] = M;
+        }
+      }
+      if (lpos == 0) {
+#pragma unroll
+        for (int g = 0; g < GP; ++g)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ws[(g0 + g) * (HD + 2) + dg * 8 + e] = acc[g][e];
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int g = 0; g < GP; ++g) {
+          ws[(g0 + g) * (HD + 2) + HD] = m[g];
+          ws[(g0 + g) * (HD + 2) + HD + 1] = ls[g];
+        }
+      }
+    }
+  } else {
+    constexpr bool kQInLds = G >= 4;
+    constexpr int GR = kQInLds ? 1 : G;
+    float qr[GR][8];
+  #pragma unroll
+    for (int g = 0; g < GR; ++g) {
+      const v4f a = *(const v4f*)(L.q + g * HD + dg * 8);
+      const v4f b = *(const v4f*)(L.q + g * HD + dg * 8 + 4);
+      qr[g][0] = a.x; qr[g][1] = a.y; qr[g][2] = a.z; qr[g][3] = a.w;
+      qr[g][4] = b.x; qr[g][5] = b.y; qr[g][6] = b.z; qr[g][7] = b.w;
+    }
+    float m[G], ls[G], acc[G][8];
+  #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float d = 0.f;
-      if constexpr (kQInLds) {
-        const v4f a = *(const v4f*)(L.q + g * HD + dg * 8);
-        const v4f b = *(const v4f*)(L.q + g * HD + dg * 8 + 4);
-        d = fmaf(a.x, kf[0], d);
-        d = fmaf(a.y, kf[1], d);
-        d = fmaf(a.z, kf[2], d);
-        d = fmaf(a.w, kf[3], d);
-        d = fmaf(b.x, kf[4], d);
-        d = fmaf(b.y, kf[5], d);
-        d = fmaf(b.z, kf[6], d);
-        d = fmaf(b.w, kf[7], d);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) d = fmaf(qr[g][e], kf[e], d);
+      m[g] = -INFINITY;
+      ls[g] = 0.f;
+  #pragma unroll
+      for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+    }
+    auto update = [&](const v4u kw, const v4u vw, bool valid) {
+      const float kf[8] = {bf16lo(kw.x), bf16hi(kw.x), bf16lo(kw.y), bf16hi(kw.y),
+                           bf16lo(kw.z), bf16hi(kw.z), bf16lo(kw.w), bf16hi(kw.w)};
+      const float vf[8] = {bf16lo(vw.x), bf16hi(vw.x), bf16lo(vw.y), bf16hi(vw.y),
+                           bf16lo(vw.z), bf16hi(vw.z), bf16lo(vw.w), bf16hi(vw.w)};
+  #pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float d = 0.f;
+        if constexpr (kQInLds) {
+          const v4f a = *(const v4f*)(L.q + g * HD + dg * 8);
+          const v4f b = *(const v4f*)(L.q + g * HD + dg * 8 + 4);
+          d = fmaf(a.x, kf[0], d);
+          d = fmaf(a.y, kf[1], d);
+          d = fmaf(a.z, kf[2], d);
+          d = fmaf(a.w, kf[3], d);
+          d = fmaf(b.x, kf[4], d);
+          d = fmaf(b.y, kf[5], d);
+          d = fmaf(b.z, kf[6], d);
+          d = fmaf(b.w, kf[7], d);
+        } else {
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) d = fmaf(qr[g][e], kf[e], d);
+        }
+        d = LPP == 16 ? row16_sum(d) : row8_sum(d);
+        const float sc = d * scale;
+        if (valid) {
+          const float mn = fmaxf(m[g], sc);
+          const float c = exp2f(m[g] - mn);  // 0 while m is -inf
+          const float pr = exp2f(sc - mn);
+          ls[g] = fmaf(ls[g], c, pr);
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(acc[g][e], c, pr * vf[e]);
+          m[g] = mn;
+        }
       }
-      d = LPP == 16 ? row16_sum(d) : row8_sum(d);
-      const float sc = d * scale;
-      if (valid) {
-        const float mn = fmaxf(m[g], sc);
-        const float c = exp2f(m[g] - mn);  // 0 while m is -inf
-        const float pr = exp2f(sc - mn);
-        ls[g] = fmaf(ls[g], c, pr);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(acc[g][e], c, pr * vf[e]);
-        m[g] = mn;
-      }
-    }
-  };
-  for (int32_t bi = 0; bi < nbw; ++bi) {
-    v4u kc[AB], vc[AB];
-#pragma unroll
-    for (int e = 0; e < AB; ++e) {
-      kc[e] = kn[e];
-      vc[e] = vn[e];
-    }
-    if (bi + 1 < nbw) kv_issue(bi + 1, kn, vn);
-#pragma unroll
-    for (int e = 0; e < AB; ++e) {
-      const int32_t i = bi * AB + e;
-      if (i < ntw) update(kc[e], vc[e], (v + kWaves * i) * PPT + lpos < at.ncache);
-    }
-  }
-  // the current position: its K/V come from the exchange, rounded to bf16 like the cache
-  if (at.has_p && v == at.nkt % kWaves) {
-    auto cur_row = [&](const float* src) {
-      uint32_t b[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) b[e] = f32_to_bf16(src[dg * 8 + e]);
-      return v4u{b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16)};
     };
-    update(cur_row(L.q + G * HD), cur_row(L.q + (G + 1) * HD), lpos == 0);
-  }
-  // combine the position rows of the wave (lanes with the same dims)
-#pragma unroll
-  for (int off = LPP; off < kWave; off <<= 1) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float mo = __shfl_xor(m[g], off, kWave);
-      const float lo = __shfl_xor(ls[g], off, kWave);
-      const float M = fmaxf(m[g], mo);
-      const float f = m[g] == -INFINITY ? 0.f : exp2f(m[g] - M);
-      const float fo = mo == -INFINITY ? 0.f : exp2f(mo - M);
-      ls[g] = ls[g] * f + lo * fo;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float ao = __shfl_xor(acc[g][e], off, kWave);
-        acc[g][e] = acc[g][e] * f + ao * fo;
+    for (int32_t bi = 0; bi < nbw; ++bi) {
+      v4u kc[AB], vc[AB];
+  #pragma unroll
+      for (int e = 0; e < AB; ++e) {
+        kc[e] = kn[e];
+        vc[e] = vn[e];
       }
-      m[g] = M;
+      if (bi + 1 < nbw) kv_issue(bi + 1, kn, vn);
+  #pragma unroll
+      for (int e = 0; e < AB; ++e) {
+        const int32_t i = bi * AB + e;
+        if (i < ntw) update(kc[e], vc[e], (v + kWaves * i) * PPT + lpos < at.ncache);
+      }
     }
-  }
-  float* ws = L.scr + v * G * (HD + 2);
-  if (lpos == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ws[g * (HD + 2) + dg * 8 + e] = acc[g][e];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      ws[g * (HD + 2) + HD] = m[g];
-      ws[g * (HD + 2) + HD + 1] = ls[g];
+    // the current position: its K/V come from the exchange, rounded to bf16 like the cache
+    if (at.has_p && v == at.nkt % kWaves) {
+      auto cur_row = [&](const float* src) {
+        uint32_t b[8];
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) b[e] = f32_to_bf16(src[dg * 8 + e]);
+        return v4u{b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16)};
+      };
+      update(cur_row(L.q + G * HD), cur_row(L.q + (G + 1) * HD), lpos == 0);
+    }
+    // combine the position rows of the wave (lanes with the same dims)
+  #pragma unroll
+    for (int off = LPP; off < kWave; off <<= 1) {
+  #pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float mo = __shfl_xor(m[g], off, kWave);
+        const float lo = __shfl_xor(ls[g], off, kWave);
+        const float M = fmaxf(m[g], mo);
+        const float f = m[g] == -INFINITY ? 0.f : exp2f(m[g] - M);
+        const float fo = mo == -INFINITY ? 0.f : exp2f(mo - M);
+        ls[g] = ls[g] * f + lo * fo;
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float ao = __shfl_xor(acc[g][e], off, kWave);
+          acc[g][e] = acc[g][e] * f + ao * fo;
+        }
+        m[g] = M;
+      }
+    }
+    float* ws = L.scr + v * G * (HD + 2);
+    if (lpos == 0) {
+  #pragma unroll
+      for (int g = 0; g < G; ++g)
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) ws[g * (HD + 2) + dg * 8 + e] = acc[g][e];
+    }
+    if (lane == 0) {
+  #pragma unroll
+      for (int g = 0; g < G; ++g) {
+        ws[g * (HD + 2) + HD] = m[g];
+        ws[g * (HD + 2) + HD + 1] = ls[g];
+      }
     }
   }
   bar();
@@ -1024,34 +1202,6 @@ __device__ __forceinline__ double readlane_d(double v, int lane) {
   const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), lane);
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
-// Candidate (z, id) as one unsigned 64-bit key that orders like the candidate order: an
-// order-preserving image of the float bits above, the complement of the id below (a lower id
-// wins a tie). z is never NaN or -0 here.
-__device__ __forceinline__ uint64_t cand_key(float v, int32_t id) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t hi = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)hi << 32) | (uint32_t)(0x7fffffff - id);
-}
-__device__ __forceinline__ float key_value(uint64_t k) {
-  const uint32_t hi = (uint32_t)(k >> 32);
-  return __uint_as_float((hi & 0x80000000u) ? (hi & 0x7fffffffu) : ~hi);
-}
-__device__ __forceinline__ int32_t key_id(uint64_t k) { return 0x7fffffff - (int32_t)(uint32_t)k; }
-// Number of keys of kk[0 .. n) (16-byte aligned) greater than key; eight per step with 16-byte
-// LDS reads, so that the reads overlap.
-__device__ __forceinline__ int32_t count_greater(const uint64_t* kk, int32_t n, uint64_t key) {
-  typedef uint64_t v2u64 __attribute__((ext_vector_type(2)));
-  int32_t c = 0, i = 0;
-  for (; i + 8 <= n; i += 8) {
-    const v2u64 a = *(const v2u64*)(kk + i), b = *(const v2u64*)(kk + i + 2);
-    const v2u64 e = *(const v2u64*)(kk + i + 4), f = *(const v2u64*)(kk + i + 6);
-    c += (a.x > key ? 1 : 0) + (a.y > key ? 1 : 0) + (b.x > key ? 1 : 0) + (b.y > key ? 1 : 0) + (e.x > key ? 1 : 0) +
-         (e.y > key ? 1 : 0) + (f.x > key ? 1 : 0) + (f.y > key ? 1 : 0);
-  }
-  for (; i < n; ++i) c += kk[i] > key ? 1 : 0;
-  return c;
-}
-
 // On entry the WG's LM outputs divided by the temperature, z, are in scr[0 .. 2 np) (row 2 pb +
 // i at i) and every wave has passed a barrier after they were written. Candidate order is the
 // argmax order (larger z, then the lower id), a strict total order once the padding ids (past V)
@@ -1266,14 +1416,21 @@ __device__ __forceinline__ void decode(Wk<MOE>& K) {
                             // so that the dense program is compiled as if it did not exist)
       if constexpr (MOE) {
         if (bnd == B_RT) {  // router logits -> gather all E -> the layer's experts (the same in every WG)
+          // phase times of a KIE_TRACE build in slots 16-18 (the top-k sampler's, unused when greedy)
+          uint64_t tr0 = TR_NOW();
           bar();
           uint64_t* rx = ex + X.rt + (int64_t)l * s.E;
           K.finalize(K.g[ST_RT], [&](int32_t gp, float ya, float yb) {
             st_x(rx + 2 * gp, tag_f(ya, ep));
             st_x(rx + 2 * gp + 1, tag_f(yb, ep));
           });
+          uint64_t tr1 = TR_NOW();
+          K.tr.add(16, tr1 - tr0);
           K.template fetch_f32<8>(rx, s.E, L.scr, ep, false);
+          tr0 = TR_NOW();
+          K.tr.add(17, tr0 - tr1);
           K.route(step, l);
+          K.tr.add(18, TR_NOW() - tr0);
           st = ST_GU;
           bnd = B_GU;
           routed = true;
@@ -1522,6 +1679,7 @@ __device__ __forceinline__ void decode(Wk<MOE>& K) {
           case B_O: K.tr.add(12, dt); break;
           case B_GU: K.tr.add(13, dt); break;
           case B_DN: K.tr.add(14, dt); break;
+          case B_RT: K.tr.add(23, dt); break;
           default: K.tr.add(15, dt); break;
         }
       }
@@ -1553,8 +1711,7 @@ __device__ __forceinline__ void decode(Wk<MOE>& K) {
 // the first token) runs the same program under its own symbol, so that profiles separate it
 // from decoding.
 #define KIE_KERNEL_BODY(G, HD, MOE)                                         \
-  extern __shared__ __align__(16) uint8_t smem[];                          \
-  const Lds L = lds_map(smem, P.s);                                        \
+  const Lds L = lds_map(kie_smem, P.s);                                    \
   if (threadIdx.x < C_COUNT) L.ctl[threadIdx.x] = 0;                       \
   __syncthreads();                                                         \
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);    \

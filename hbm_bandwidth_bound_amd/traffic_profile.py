@@ -33,8 +33,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-DECODE_KERNEL = "kie_decode_kernel"
+DECODE_KERNEL = "kie_decode_kernel"          # dense layers
+MOE_DECODE_KERNEL = "kie_moe_decode_kernel"  # mixture-of-experts layers
 COPY_KERNEL = "stream_copy_kernel"
+
+
+def decode_kernel(model) -> str:
+    return MOE_DECODE_KERNEL if model.n_experts else DECODE_KERNEL
 
 
 def run(args):
@@ -105,7 +110,7 @@ def summarize(args):
     per = {}
     for counter, run_dir in (("FETCH_SIZE", args.fetch), ("WRITE_SIZE", args.write)):
         d = _counter_per_dispatch(run_dir, counter)
-        dec = _pick(d, DECODE_KERNEL)
+        dec = _pick(d, decode_kernel(wl.model))
         cpy = _pick(d, COPY_KERNEL)
         if len(dec) != 1 or len(cpy) != 1:
             raise SystemExit(f"{counter}: expected one decode and one copy dispatch, got {len(dec)} and {len(cpy)}")
@@ -117,7 +122,7 @@ def summarize(args):
     algo = traffic.launch_bytes(wl.model, wl.prompt_len, K)
     total = per["FETCH_SIZE"] + per["WRITE_SIZE"]
     with open(args.out, "w") as f:
-        f.write(f"# HBM traffic of one kie_decode_kernel dispatch ({wl.name}: prompt {wl.prompt_len}, "
+        f.write(f"# HBM traffic of one {decode_kernel(wl.model)} dispatch ({wl.name}: prompt {wl.prompt_len}, "
                 f"{K} decode steps in one launch)\n")
         f.write("# commands (from the repository root, each pass its own run):\n")
         for c, d in (("FETCH_SIZE", args.fetch), ("WRITE_SIZE", args.write)):
