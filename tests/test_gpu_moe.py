@@ -112,3 +112,46 @@ def test_moe_rejects_unsupported_shapes(torch_cuda):
     with pytest.raises(kie.KieError) as ei:
         kie.Engine(g2, w, 64)
     assert ei.value.status == -2
+
+
+def test_moe_skewed_workgroups_give_bitwise_identical_results(torch_cuda):
+    """Exchange protocol stress with the router hop: every workgroup idles a pseudo-random time
+    before each boundary (kie_set_skew), so the workgroups reach the router gather, the expert
+    choice and the routed stages in other orders; prompt, greedy and top-k decode must give
+    bitwise the same tokens and logits as without."""
+    from hbm_bandwidth_bound_amd.kie import Engine, sampling
+    cfg = synth.SMALL_MOE
+    w = synth.make_weights_np(cfg, 0)
+    wd = to_device(w)
+    P, N = 24, 8
+    say(f"[{cfg.name}] skewed workgroups: prompt {P} + decode {N}, greedy and top-k")
+    prompt = synth.prompt_ids(P, cfg.vocab_size, 21)
+    eng = Engine(cfg, wd, P + N)
+
+    def run(smp):
+        import torch
+        tokens = torch.tensor(np.asarray(prompt, dtype=np.int32), device="cuda")
+        last = torch.empty(cfg.vocab_size, dtype=torch.float32, device="cuda")
+        first = eng.prefill(tokens, logits_out=last, smp=smp)
+        out = torch.empty(N, dtype=torch.int32, device="cuda")
+        logits = torch.empty((N, cfg.vocab_size), dtype=torch.float32, device="cuda")
+        eng.generate(first, N, out, logits, smp=smp)
+        eng.sync()
+        return int(first.item()), last.cpu().numpy(), out.cpu().numpy(), logits.cpu().numpy()
+
+    greedy, topk = sampling(), sampling(50, 0.8, 2)
+    ref = run(greedy)
+    eng.reset()
+    ref_k = run(topk)
+    for level in (4, 16):
+        eng.reset()
+        eng.set_skew(level)
+        got = run(greedy)
+        eng.reset()
+        got_k = run(topk)
+        eng.set_skew(0)
+        for a, b in ((ref, got), (ref_k, got_k)):
+            assert a[0] == b[0] and np.array_equal(a[1], b[1]), f"skew {level}: prompt differs"
+            assert np.array_equal(a[2], b[2]) and np.array_equal(a[3], b[3]), f"skew {level}: decode differs"
+        say(f"  skew {level}: identical")
+    eng.close()
