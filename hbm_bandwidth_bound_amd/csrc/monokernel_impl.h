@@ -339,7 +339,9 @@ struct Wk {
     const bool gu = jd < nb[ST_GU];
     const StageGeo gs = gu ? g[ST_GU] : g[ST_DN];
     const int32_t bi = gu ? jd : jd - nb[ST_GU];
-    const int32_t b = lane & (kBatch - 1);
+    int32_t ln = lane;
+    asm volatile("" : "+v"(ln));  // formed here, not hoisted (see route)
+    const int32_t b = ln & (kBatch - 1);
     const int32_t lks = gs.ks == 8 ? 3 : (gs.ks == 4 ? 2 : (gs.ks == 2 ? 1 : 0));
     const int32_t us = b >> lks, tt = b & (gs.ks - 1);
     const int32_t u = v + kWaves * (bi * gs.upb + us);
@@ -497,22 +499,27 @@ struct Wk {
   // batch, if any, is issued.
   __device__ __forceinline__ void route(int32_t step, int32_t l) {
     const Shape& s = P.s;
+    // The thread index is made opaque here, so that the LDS addresses below are formed where
+    // they are used: hoisted to the kernel start they would live across the whole decode loop,
+    // be spilled, and each reload from scratch memory would wait for every load in flight.
+    int32_t t = tid;
+    asm volatile("" : "+v"(t));
     // part is free between the router stage's finalize and gate/up: the E candidate keys (the
     // argmax order as one 64-bit integer; NaN ranks as -inf and -0 as +0), then the chosen ids
     uint64_t* keys = (uint64_t*)L.part;
     int32_t* sel = (int32_t*)(keys + s.E);
     const uint64_t trk = TR_NOW();
     uint64_t key = 0;
-    if (tid < s.E) {
-      float z = L.scr[tid];
+    if (t < s.E) {
+      float z = L.scr[t];
       z = z == z ? (z == 0.f ? 0.f : z) : -INFINITY;
-      key = cand_key(z, tid);
-      keys[tid] = key;
+      key = cand_key(z, t);
+      keys[t] = key;
     }
     bar();
-    if (tid < s.E) {
+    if (t < s.E) {
       const int32_t rank = count_greater(keys, s.E, key);
-      if (rank < s.A) sel[rank] = tid;
+      if (rank < s.A) sel[rank] = t;
     }
     uint64_t tq = TR_NOW();
     tr.add(31, tq - trk);
@@ -520,7 +527,7 @@ struct Wk {
     tr.add(19, TR_NOW() - tq);
     tq = TR_NOW();
     if (v == 0) {  // one wave turns the ranks into the table of chosen experts and weights
-      const int32_t r = lane;
+      const int32_t r = t;
       int32_t e = r < s.A ? sel[r] : 0;
       e = e < 0 ? 0 : (e >= s.E ? s.E - 1 : e);
       float z = L.scr[e];
