@@ -1192,6 +1192,95 @@ __device__ __forceinline__ void merge_unit(WK& K, const Att& at, int32_t l, int3
   bar();
 }
 
+// Two merge units at once (units u and u + 1 when `two`; the workgroup's halves take one each):
+// one round of polls instead of two where a workgroup owns several units (32 query heads over
+// 256 workgroups). Thread (dim, chunk lane cl) of its half folds chunks cl, cl + 32, ... in
+// order; the chunk lanes of a wave are combined with shuffles and the half's 4 waves in LDS,
+// always in the same order.
+template <typename WK>
+__device__ __forceinline__ void merge_two_units(WK& K, const Att& at, int32_t l, int32_t u, bool two, uint32_t epoch) {
+  const KParams& P = K.P;
+  const Lds& L = K.L;
+  const Shape& s = P.s;
+  constexpr int D = kMergeDims;
+  constexpr int HT = kThreads / 2;  // threads per unit
+  constexpr int CL = HT / D;        // chunk lanes per unit
+  const int32_t ui = K.tid / HT, th = K.tid % HT;
+  const bool mine = ui == 0 || two;
+  const int32_t uu = u + ui;
+  const int32_t slices = s.hd / D;
+  const int32_t h = uu / slices, sl = uu % slices;
+  const int32_t G = s.group();
+  const int32_t j = h / G, g = h % G;
+  const int dim = th % D, cl = th / D;
+  float M = -INFINITY, S = 0.f, A = 0.f;
+  constexpr int KM = 4;
+  for (int32_t c0 = cl; c0 < at.nch && !K.fail; c0 += CL * KM) {
+    uint64_t wm[KM], wl[KM], wa[KM];
+    uint32_t todo = 0;
+#pragma unroll
+    for (int k = 0; k < KM; ++k)
+      if (mine && c0 + CL * k < at.nch) todo |= 1u << k;
+    const uint32_t present = todo;
+    Waiter wt;
+    while (__builtin_amdgcn_ballot_w64(todo != 0) != 0) {
+#pragma unroll
+      for (int k = 0; k < KM; ++k) {
+        if (todo & (1u << k)) {
+          const int32_t ch = c0 + CL * k;
+          const uint64_t* pp =
+              P.ex + P.exo.part + ((int64_t)l * s.nwg + ch * s.nkv + j) * P.exo.part_words + g * (s.hd + 2);
+          wm[k] = ld_x(pp + s.hd);
+          wl[k] = ld_x(pp + s.hd + 1);
+          wa[k] = ld_x(pp + sl * D + dim);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < KM; ++k)
+        if ((todo & (1u << k)) && (uint32_t)wm[k] == epoch && (uint32_t)wl[k] == epoch && (uint32_t)wa[k] == epoch)
+          todo &= ~(1u << k);
+      if (__builtin_amdgcn_ballot_w64(todo != 0) != 0) {
+        __builtin_amdgcn_s_sleep(1);
+        if (wt.expired(P, L) || ((wt.spins & 255u) == 0 && global_error(P))) {
+          K.fail = true;
+          raise_error(P, L, KERR_TIMEOUT);
+          break;
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < KM; ++k)
+      if (present & (1u << k))
+        softmax_combine(M, S, A, __uint_as_float((uint32_t)(wm[k] >> 32)), __uint_as_float((uint32_t)(wl[k] >> 32)),
+                        __uint_as_float((uint32_t)(wa[k] >> 32)));
+  }
+#pragma unroll
+  for (int o = D; o < kWave; o <<= 1) {  // chunk lanes of this wave
+    const float m2 = __shfl_xor(M, o, kWave), s2 = __shfl_xor(S, o, kWave), a2 = __shfl_xor(A, o, kWave);
+    softmax_combine(M, S, A, m2, s2, a2);
+  }
+  float* ms = L.scr;  // [8 waves][D][3]
+  if (K.lane < D) {
+    ms[(K.v * D + dim) * 3 + 0] = M;
+    ms[(K.v * D + dim) * 3 + 1] = S;
+    ms[(K.v * D + dim) * 3 + 2] = A;
+  }
+  bar();
+  constexpr int WPU = kWaves / 2;  // waves per unit
+  if (K.tid < 2 * D && (K.tid < D || two)) {
+    const int32_t ut = K.tid / D, dt = K.tid % D;
+    const int32_t un = u + ut, hn = un / slices, sn = un % slices;
+    const int w0 = ut * WPU;
+    float Mt = ms[(w0 * D + dt) * 3], St = ms[(w0 * D + dt) * 3 + 1], At = ms[(w0 * D + dt) * 3 + 2];
+#pragma unroll
+    for (int k = 1; k < WPU; ++k)
+      softmax_combine(Mt, St, At, ms[((w0 + k) * D + dt) * 3], ms[((w0 + k) * D + dt) * 3 + 1],
+                      ms[((w0 + k) * D + dt) * 3 + 2]);
+    st_x(P.ex + P.exo.o + (int64_t)l * s.qdim() + hn * s.hd + sn * D + dt, tag_f(At / St, epoch));
+  }
+  bar();
+}
+
 // ------------------------------------------------------------------------------------------
 // Top-k sampling on the GPU (aikraft.ru «3000 токенов в секунду…», §04: sampling runs inside the
 // monokernel, not on the host). Every WG computes the same token from the same exchanged words.
@@ -1493,7 +1582,12 @@ __device__ __forceinline__ void decode(Wk<MOE>& K) {
             const uint64_t tm = TR_NOW();
             const int32_t nu = merge_units(s);
             const int32_t u0 = (int32_t)(((int64_t)K.w * nu + s.nwg - 1) / s.nwg);
-            for (int32_t u = u0; u < nu && merge_unit_wg(s, u) == K.w; ++u) merge_unit(K, at, l, u, ep);
+            if constexpr (G >= 8) {  // several units per workgroup at these head counts: two at a time
+              for (int32_t u = u0; u < nu && merge_unit_wg(s, u) == K.w; u += 2)
+                merge_two_units(K, at, l, u, u + 1 < nu && merge_unit_wg(s, u + 1) == K.w, ep);
+            } else {
+              for (int32_t u = u0; u < nu && merge_unit_wg(s, u) == K.w; ++u) merge_unit(K, at, l, u, ep);
+            }
             K.tr.add(T_MERGE, TR_NOW() - tm);
           }
           K.fetch_f32(ex + X.o + (int64_t)l * s.qdim(), s.qdim(), L.act, ep, false);
