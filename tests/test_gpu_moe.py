@@ -155,3 +155,56 @@ def test_moe_skewed_workgroups_give_bitwise_identical_results(torch_cuda):
             assert np.array_equal(a[2], b[2]) and np.array_equal(a[3], b[3]), f"skew {level}: decode differs"
         say(f"  skew {level}: identical")
     eng.close()
+
+
+def test_moe_long_context_over_synthetic_kv(torch_cuda, oracle_lib):
+    """The 128-expert layer shape (2 layers) over 12,288 cached positions: both sides start from
+    the same seeded synthetic K/V rows, then decode 3 steps. Each workgroup's chunk then holds 48
+    K/V tiles (6 per wave, 3 batches), so the two passes of attention over 4 query heads each
+    reload several batches."""
+    import torch
+    from hbm_bandwidth_bound_amd.kie import Engine
+    cfg = synth.MOE_2L
+    n, N = 12288, 3
+    say(f"[{cfg.name}] {n} synthetic cached positions + decode {N}")
+    wd = synth.make_weights_torch(cfg, 0, device="cuda")
+    eng = Engine(cfg, wd, n + N)
+    kd, vd = synth.synthetic_kv_torch(cfg, n, seed=7, device="cuda")
+    kv = eng.kv_view()
+    kv[:, 0, :, :n] = kd
+    kv[:, 1, :, :n] = vd
+    eng.set_position(n)
+    tok0 = int(synth.prompt_ids(1, cfg.vocab_size, 5)[0])
+    first = torch.tensor([tok0], dtype=torch.int32, device="cuda")
+    out = torch.empty(N, dtype=torch.int32, device="cuda")
+    logits = torch.empty((N, cfg.vocab_size), dtype=torch.float32, device="cuda")
+    eng.generate(first, N, out, logits)
+    eng.sync()
+    toks, logits = out.cpu().numpy(), logits.cpu().numpy()
+    kg_new = eng.kv_view()[:, :, :, n:n + N].cpu().numpy().view(np.uint16)
+    kn, vn = kd.cpu().numpy().view(np.uint16), vd.cpu().numpy().view(np.uint16)
+    eng.close()
+    w = synth.weights_torch_to_np(wd)
+    del wd, kd, vd, kv
+    torch.cuda.empty_cache()
+    oracle_lib.set_threads(16)
+    try:
+        om = oracle_lib.OracleModel(cfg, w, n + N)
+        k, v = om.kv_view()
+        k[:, :, :n] = kn
+        v[:, :, :n] = vn
+        z = om.record_routes(n + N)
+        ref = om.run([tok0] + [int(t) for t in toks[:-1]], start_pos=n)
+        om.stop_recording()
+    finally:
+        oracle_lib.set_threads(1)
+    m = route_margin(z[n:n + N], cfg.n_experts_active)
+    say(f"  smallest router margin {m:.2e}")
+    assert m > ROUTE_MARGIN, "a routing decision is within the margin of a tie; pick another seed"
+    worst, checked = check_steps(logits, ref, toks, label=cfg.name)
+    say(f"  worst rel-L2 {worst:.3e}, greedy checked on {checked}/{N} steps")
+    ko, vo = om.kv_view()
+    ek = rel_l2(synth.bf16_bits_to_f32(kg_new[:, 0]), synth.bf16_bits_to_f32(ko[:, :, n:n + N]))
+    ev = rel_l2(synth.bf16_bits_to_f32(kg_new[:, 1]), synth.bf16_bits_to_f32(vo[:, :, n:n + N]))
+    say(f"  appended cache rows rel-L2 K {ek:.3e} V {ev:.3e}")
+    assert ek <= 1e-3 and ev <= 1e-3
