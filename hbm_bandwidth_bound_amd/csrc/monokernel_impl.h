@@ -97,14 +97,21 @@ __host__ __device__ inline int32_t act_floats(const Shape& s) {
   if (s.F > a) a = s.F;
   return a;
 }
-__host__ __device__ inline int32_t scr_floats(const Shape& s) {
-  int32_t a = kWaves * s.group() * (s.hd + 2);
+// The LDS layout, for a kernel compiled for GC query heads per KV head (the host's versions below
+// take the group from the shape). With 8 query heads per KV head attention runs as two passes of
+// 4 heads and its scratch holds one pass.
+template <int GC>
+__host__ __device__ inline int32_t scr_floats_g(const Shape& s) {
+  int32_t a = GC > 4 ? kWaves * 4 * (s.hd + 2) : kWaves * s.group() * (s.hd + 2);
   if (kWaves * kMergeDims * 3 > a) a = kWaves * kMergeDims * 3;
   if (2 * s.nwg > a) a = 2 * s.nwg;
   if (lm_rows_max(s) > a) a = lm_rows_max(s);  // the WG's LM outputs for the top-k draw
   if (s.E > a) a = s.E;                          // router logits
   if (a < 64) a = 64;
   return (a + 3) & ~3;
+}
+__host__ __device__ inline int32_t scr_floats(const Shape& s) {
+  return s.group() > 4 ? scr_floats_g<8>(s) : scr_floats_g<1>(s);
 }
 // act, xres, part and a pad are contiguous: once the LM outputs are final they hold the top-k
 // merge, and the pad makes room for the largest k where the three are smaller
@@ -121,11 +128,18 @@ __host__ __device__ inline int32_t merge_floats(const Shape& s) {
 constexpr int32_t kLdsCapacity = 160 * 1024;
 constexpr int32_t kXbBytes = kWaves * kBatch * kTileBytes;
 __host__ __device__ inline int32_t moe_words(const Shape& s) { return s.moe() ? 2 * kMaxActive : 0; }
+template <int GC>
+__host__ __device__ inline int32_t lds_base_bytes_g(const Shape& s) {
+  return (merge_floats(s) + scr_floats_g<GC>(s) + (s.group() + 2) * s.hd + s.hd) * 4 + C_COUNT * 4 + moe_words(s) * 4;
+}
+template <int GC>
+__host__ __device__ inline bool xb_fits_g(const Shape& s) { return lds_base_bytes_g<GC>(s) + kXbBytes <= kLdsCapacity; }
 __host__ __device__ inline int32_t lds_base_bytes(const Shape& s) {
-  return (merge_floats(s) + scr_floats(s) + (s.group() + 2) * s.hd + s.hd) * 4 + C_COUNT * 4 + moe_words(s) * 4;
+  return s.group() > 4 ? lds_base_bytes_g<8>(s) : lds_base_bytes_g<1>(s);
 }
 __host__ __device__ inline bool xb_fits(const Shape& s) { return lds_base_bytes(s) + kXbBytes <= kLdsCapacity; }
 inline int32_t lds_bytes_for_impl(const Shape& s) { return lds_base_bytes(s) + (xb_fits(s) ? kXbBytes : 0); }
+template <int GC>
 __device__ __forceinline__ Lds lds_map(uint8_t* smem, const Shape& s) {
   Lds L;
   uint8_t* p = smem;
@@ -133,14 +147,14 @@ __device__ __forceinline__ Lds lds_map(uint8_t* smem, const Shape& s) {
   L.xres = (float*)p; p += (size_t)2 * s.d * 4;
   L.part = (float*)p; p += (size_t)2 * kMaxUnits * 4;
   p += (size_t)merge_pad_floats(s) * 4;
-  L.scr = (float*)p; p += (size_t)scr_floats(s) * 4;
+  L.scr = (float*)p; p += (size_t)scr_floats_g<GC>(s) * 4;
   L.q = (float*)p; p += (size_t)(s.group() + 2) * s.hd * 4;
   L.rope = (float2*)p; p += (size_t)s.hd * 4;
   L.ctl = (uint32_t*)p;
   p += C_COUNT * 4;  // 16-byte aligned: every piece above is a multiple of 4 floats
   L.moe = (int32_t*)p;
   p += moe_words(s) * 4;
-  L.xb = xb_fits(s) ? p : nullptr;
+  L.xb = xb_fits_g<GC>(s) ? p : nullptr;
   return L;
 }
 
@@ -855,7 +869,10 @@ __device__ __forceinline__ void attention(WK& K, const Att& at, int32_t l, int32
     // from L2): the accumulators of 8 heads at once would not fit next to the weight batch in
     // flight without spilling.
     constexpr int GP = 4;
-    float* ws = L.scr + v * G * (HD + 2);
+    // each pass's heads are combined over the 8 waves and published before the next pass, so
+    // the scratch holds one pass (which leaves LDS room for the extra weight-batch slot)
+    float* ws = L.scr + v * GP * (HD + 2);
+    uint64_t* part = P.ex + X.part + ((int64_t)l * s.nwg + K.w) * X.part_words;
 #pragma unroll 1
     for (int g0 = 0; g0 < G; g0 += GP) {
       if (g0 > 0 && nbw > 0) kv_issue(0, kn, vn);
@@ -943,21 +960,42 @@ __device__ __forceinline__ void attention(WK& K, const Att& at, int32_t l, int32
 #pragma unroll
         for (int g = 0; g < GP; ++g)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) ws[(g0 + g) * (HD + 2) + dg * 8 + e] = acc[g][e];
+          for (int e = 0; e < 8; ++e) ws[g * (HD + 2) + dg * 8 + e] = acc[g][e];
       }
       if (lane == 0) {
 #pragma unroll
         for (int g = 0; g < GP; ++g) {
-          ws[(g0 + g) * (HD + 2) + HD] = m[g];
-          ws[(g0 + g) * (HD + 2) + HD + 1] = ls[g];
+          ws[g * (HD + 2) + HD] = m[g];
+          ws[g * (HD + 2) + HD + 1] = ls[g];
         }
       }
+      bar();
+      for (int e = K.tid; e < GP * (HD + 2); e += kThreads) {  // combine the 8 waves and publish
+        const int g = e / (HD + 2), k = e % (HD + 2);
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, L.scr[(w * GP + g) * (HD + 2) + HD]);
+        float out;
+        if (k == HD) {
+          out = M;
+        } else {
+          out = 0.f;
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) {
+            const float mw = L.scr[(w * GP + g) * (HD + 2) + HD];
+            const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
+            out = fmaf(L.scr[(w * GP + g) * (HD + 2) + k], f, out);
+          }
+        }
+        st_x(part + g0 * (HD + 2) + e, tag_f(out, ep));
+      }
+      bar();  // the next pass reuses the scratch
     }
   } else {
     constexpr bool kQInLds = G >= 4;
     constexpr int GR = kQInLds ? 1 : G;
     float qr[GR][8];
-  #pragma unroll
+#pragma unroll
     for (int g = 0; g < GR; ++g) {
       const v4f a = *(const v4f*)(L.q + g * HD + dg * 8);
       const v4f b = *(const v4f*)(L.q + g * HD + dg * 8 + 4);
@@ -965,11 +1003,11 @@ __device__ __forceinline__ void attention(WK& K, const Att& at, int32_t l, int32
       qr[g][4] = b.x; qr[g][5] = b.y; qr[g][6] = b.z; qr[g][7] = b.w;
     }
     float m[G], ls[G], acc[G][8];
-  #pragma unroll
+#pragma unroll
     for (int g = 0; g < G; ++g) {
       m[g] = -INFINITY;
       ls[g] = 0.f;
-  #pragma unroll
+#pragma unroll
       for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
     }
     auto update = [&](const v4u kw, const v4u vw, bool valid) {
@@ -977,7 +1015,7 @@ __device__ __forceinline__ void attention(WK& K, const Att& at, int32_t l, int32
                            bf16lo(kw.z), bf16hi(kw.z), bf16lo(kw.w), bf16hi(kw.w)};
       const float vf[8] = {bf16lo(vw.x), bf16hi(vw.x), bf16lo(vw.y), bf16hi(vw.y),
                            bf16lo(vw.z), bf16hi(vw.z), bf16lo(vw.w), bf16hi(vw.w)};
-  #pragma unroll
+#pragma unroll
       for (int g = 0; g < G; ++g) {
         float d = 0.f;
         if constexpr (kQInLds) {
@@ -992,7 +1030,7 @@ __device__ __forceinline__ void attention(WK& K, const Att& at, int32_t l, int32
           d = fmaf(b.z, kf[6], d);
           d = fmaf(b.w, kf[7], d);
         } else {
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < 8; ++e) d = fmaf(qr[g][e], kf[e], d);
         }
         d = LPP == 16 ? row16_sum(d) : row8_sum(d);
@@ -1002,7 +1040,7 @@ __device__ __forceinline__ void attention(WK& K, const Att& at, int32_t l, int32
           const float c = exp2f(m[g] - mn);  // 0 while m is -inf
           const float pr = exp2f(sc - mn);
           ls[g] = fmaf(ls[g], c, pr);
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(acc[g][e], c, pr * vf[e]);
           m[g] = mn;
         }
@@ -1010,13 +1048,13 @@ __device__ __forceinline__ void attention(WK& K, const Att& at, int32_t l, int32
     };
     for (int32_t bi = 0; bi < nbw; ++bi) {
       v4u kc[AB], vc[AB];
-  #pragma unroll
+#pragma unroll
       for (int e = 0; e < AB; ++e) {
         kc[e] = kn[e];
         vc[e] = vn[e];
       }
       if (bi + 1 < nbw) kv_issue(bi + 1, kn, vn);
-  #pragma unroll
+#pragma unroll
       for (int e = 0; e < AB; ++e) {
         const int32_t i = bi * AB + e;
         if (i < ntw) update(kc[e], vc[e], (v + kWaves * i) * PPT + lpos < at.ncache);
@@ -1026,16 +1064,16 @@ __device__ __forceinline__ void attention(WK& K, const Att& at, int32_t l, int32
     if (at.has_p && v == at.nkt % kWaves) {
       auto cur_row = [&](const float* src) {
         uint32_t b[8];
-  #pragma unroll
+#pragma unroll
         for (int e = 0; e < 8; ++e) b[e] = f32_to_bf16(src[dg * 8 + e]);
         return v4u{b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16)};
       };
       update(cur_row(L.q + G * HD), cur_row(L.q + (G + 1) * HD), lpos == 0);
     }
     // combine the position rows of the wave (lanes with the same dims)
-  #pragma unroll
+#pragma unroll
     for (int off = LPP; off < kWave; off <<= 1) {
-  #pragma unroll
+#pragma unroll
       for (int g = 0; g < G; ++g) {
         const float mo = __shfl_xor(m[g], off, kWave);
         const float lo = __shfl_xor(ls[g], off, kWave);
@@ -1043,7 +1081,7 @@ __device__ __forceinline__ void attention(WK& K, const Att& at, int32_t l, int32
         const float f = m[g] == -INFINITY ? 0.f : exp2f(m[g] - M);
         const float fo = mo == -INFINITY ? 0.f : exp2f(mo - M);
         ls[g] = ls[g] * f + lo * fo;
-  #pragma unroll
+#pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float ao = __shfl_xor(acc[g][e], off, kWave);
           acc[g][e] = acc[g][e] * f + ao * fo;
@@ -1053,40 +1091,42 @@ __device__ __forceinline__ void attention(WK& K, const Att& at, int32_t l, int32
     }
     float* ws = L.scr + v * G * (HD + 2);
     if (lpos == 0) {
-  #pragma unroll
+#pragma unroll
       for (int g = 0; g < G; ++g)
-  #pragma unroll
+#pragma unroll
         for (int e = 0; e < 8; ++e) ws[g * (HD + 2) + dg * 8 + e] = acc[g][e];
     }
     if (lane == 0) {
-  #pragma unroll
+#pragma unroll
       for (int g = 0; g < G; ++g) {
         ws[g * (HD + 2) + HD] = m[g];
         ws[g * (HD + 2) + HD + 1] = ls[g];
       }
     }
   }
-  bar();
-  // combine the 8 waves and publish
-  uint64_t* part = P.ex + X.part + ((int64_t)l * s.nwg + K.w) * X.part_words;
-  for (int e = K.tid; e < G * (HD + 2); e += kThreads) {
-    const int g = e / (HD + 2), k = e % (HD + 2);
-    float M = -INFINITY;
+  if constexpr (G <= 4) {
+    bar();
+    // combine the 8 waves and publish
+    uint64_t* part = P.ex + X.part + ((int64_t)l * s.nwg + K.w) * X.part_words;
+    for (int e = K.tid; e < G * (HD + 2); e += kThreads) {
+      const int g = e / (HD + 2), k = e % (HD + 2);
+      float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, L.scr[(w * G + g) * (HD + 2) + HD]);
-    float out;
-    if (k == HD) {
-      out = M;
-    } else {
-      out = 0.f;
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, L.scr[(w * G + g) * (HD + 2) + HD]);
+      float out;
+      if (k == HD) {
+        out = M;
+      } else {
+        out = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = L.scr[(w * G + g) * (HD + 2) + HD];
-        const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
-        out = fmaf(L.scr[(w * G + g) * (HD + 2) + k], f, out);
+        for (int w = 0; w < kWaves; ++w) {
+          const float mw = L.scr[(w * G + g) * (HD + 2) + HD];
+          const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
+          out = fmaf(L.scr[(w * G + g) * (HD + 2) + k], f, out);
+        }
       }
+      st_x(part + e, tag_f(out, ep));
     }
-    st_x(part + e, tag_f(out, ep));
   }
   // the WG whose chunk holds the current position appends its K/V rows to the cache
   if (at.has_p) {
@@ -1812,7 +1852,7 @@ __device__ __forceinline__ void decode(Wk<MOE>& K) {
 // the first token) runs the same program under its own symbol, so that profiles separate it
 // from decoding.
 #define KIE_KERNEL_BODY(G, HD, MOE)                                         \
-  const Lds L = lds_map(kie_smem, P.s);                                    \
+  const Lds L = lds_map<G>(kie_smem, P.s);                                 \
   if (threadIdx.x < C_COUNT) L.ctl[threadIdx.x] = 0;                       \
   __syncthreads();                                                         \
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);    \
