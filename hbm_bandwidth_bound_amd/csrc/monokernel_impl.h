@@ -209,7 +209,8 @@ __device__ __forceinline__ bool global_error(const KParams& P) {
 }
 
 // Bounded spin: call expired() after every unsuccessful poll. Every 256th call it checks the WG's
-// abort flag and the elapsed time of this wait (wave-uniform).
+// abort flag and the elapsed time of this wait (wave-uniform). Poll rounds follow each other
+// without a sleep: each round already waits for its own loads, which paces it.
 struct Waiter {
   uint32_t spins = 0;
   uint64_t start = 0;
@@ -685,7 +686,6 @@ struct Wk {
         }
       }
       if (__builtin_amdgcn_ballot_w64(missing != 0) == 0 || fail) break;
-      __builtin_amdgcn_s_sleep(1);
       if (wt.expired(P, L) || ((wt.spins & 255u) == 0 && global_error(P))) {
         fail = true;
         raise_error(P, L, KERR_TIMEOUT);
@@ -1195,7 +1195,6 @@ __device__ __forceinline__ void merge_unit(WK& K, const Att& at, int32_t l, int3
         if ((todo & (1u << k)) && (uint32_t)wm[k] == epoch && (uint32_t)wl[k] == epoch && (uint32_t)wa[k] == epoch)
           todo &= ~(1u << k);
       if (__builtin_amdgcn_ballot_w64(todo != 0) != 0) {
-        __builtin_amdgcn_s_sleep(1);
         if (wt.expired(P, L) || ((wt.spins & 255u) == 0 && global_error(P))) {
           K.fail = true;
           raise_error(P, L, KERR_TIMEOUT);
@@ -1280,7 +1279,6 @@ __device__ __forceinline__ void merge_two_units(WK& K, const Att& at, int32_t l,
         if ((todo & (1u << k)) && (uint32_t)wm[k] == epoch && (uint32_t)wl[k] == epoch && (uint32_t)wa[k] == epoch)
           todo &= ~(1u << k);
       if (__builtin_amdgcn_ballot_w64(todo != 0) != 0) {
-        __builtin_amdgcn_s_sleep(1);
         if (wt.expired(P, L) || ((wt.spins & 255u) == 0 && global_error(P))) {
           K.fail = true;
           raise_error(P, L, KERR_TIMEOUT);

@@ -208,3 +208,35 @@ def test_moe_long_context_over_synthetic_kv(torch_cuda, oracle_lib):
     ev = rel_l2(synth.bf16_bits_to_f32(kg_new[:, 1]), synth.bf16_bits_to_f32(vo[:, :, n:n + N]))
     say(f"  appended cache rows rel-L2 K {ek:.3e} V {ev:.3e}")
     assert ek <= 1e-3 and ev <= 1e-3
+
+
+def test_moe_topk_matches_oracle(torch_cuda, oracle_lib):
+    """Top-k sampling (k 50, T 0.8) on the mixture-of-experts program: the GPU's draw equals the
+    oracle sampler's draw on the GPU's own logits at every step, and against the oracle's logits
+    the candidate sets, probabilities and (away from ties) tokens agree."""
+    import torch
+    from hbm_bandwidth_bound_amd.kie import Engine, sampling
+    from tests.gpu_util import check_topk_steps
+    cfg = synth.SMALL_MOE
+    w = synth.make_weights_np(cfg, 0)
+    P, N, k, T, seed = 24, 12, 50, 0.8, 2
+    say(f"[{cfg.name}] top-k {k}, T {T}: prompt {P} + decode {N}")
+    eng = Engine(cfg, to_device(w), P + N)
+    prompt = synth.prompt_ids(P, cfg.vocab_size, 3)
+    smp = sampling(k, T, seed)
+    first = eng.prefill(torch.tensor(prompt, dtype=torch.int32, device="cuda"), smp=smp)
+    out = torch.empty(N, dtype=torch.int32, device="cuda")
+    logits = torch.empty((N, cfg.vocab_size), dtype=torch.float32, device="cuda")
+    eng.generate(first, N, out, logits, smp=smp)
+    eng.sync()
+    toks, logits = out.cpu().numpy(), logits.cpu().numpy()
+    eng.close()
+    om = oracle_lib.OracleModel(cfg, w, P + N)
+    z = om.record_routes(P + N)
+    om.run(prompt)
+    ref = om.run([int(first.item())] + [int(t) for t in toks[:-1]], start_pos=P)
+    om.stop_recording()
+    assert route_margin(z, cfg.n_experts_active) > ROUTE_MARGIN
+    tok_checked, set_checked = check_topk_steps(logits, ref, toks, k, T, seed, P, label=cfg.name)
+    say(f"  token checks {tok_checked}/{N}, set checks {set_checked}/{N}")
+    assert set_checked > 0
