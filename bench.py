@@ -10,7 +10,9 @@ length and a profiler's per-dispatch average is the timed launch's duration.
 
 Prints one JSON line. `roofline.achieved` is the algorithmic bytes of the timed launch divided
 by that launch's duration (HIP events on the launch stream); `cpu_baseline` times the CPU oracle
-on a bounded sample of the same workload.
+on a bounded sample of the same workload. Other workloads: `--workload 1.6b-32k`, `8b-2k`, and
+`moe-1k` (the 128-expert model with 8 experts routed per token; its prompt runs through the
+decode program, and its CPU baseline is the oracle on 2- and 4-layer cuts of the model, scaled).
 """
 from __future__ import annotations
 

@@ -2,7 +2,8 @@
 
 One decode step at position p reads every layer matrix and the LM head once (bf16), the norm
 gains, one embedding row, the K and V rows of positions 0..p of every layer and KV head, and
-writes the K and V rows of position p. This is the pages' bytes-per-token model (aikraft.ru
+writes the K and V rows of position p. In a mixture-of-experts layer the matrices read are the
+attention's, the router's and those of the routed experts only. This is the pages' bytes-per-token model (aikraft.ru
 «3000 токенов в секунду…», §02: tokens/s = effective bandwidth / active bytes) with the KV term
 added, since the pages' bound leaves KV traffic out.
 """
