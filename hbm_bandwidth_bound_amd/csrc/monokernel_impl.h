@@ -532,7 +532,23 @@ struct Wk {
       keys[t] = key;
     }
     bar();
-    if (t < s.E) {
+    if (4 * s.E <= kThreads) {
+      // four lanes per candidate (a quad), each counting a quarter of the keys; the quad's sum is
+      // the rank. The quarters start at even indices, so the 16-byte key reads stay aligned.
+      const int32_t c = t >> 2, q = t & 3;
+      const int32_t chunk = ((s.E + 7) / 8) * 2;
+      const int32_t b0 = q * chunk < s.E ? q * chunk : s.E, b1 = b0 + chunk < s.E ? b0 + chunk : s.E;
+      uint64_t ck = 0;
+      if (c < s.E) {
+        float z = L.scr[c];
+        z = z == z ? (z == 0.f ? 0.f : z) : -INFINITY;
+        ck = cand_key(z, c);
+      }
+      int32_t part = c < s.E ? count_greater(keys + b0, b1 - b0, ck) : 0;
+      part += __builtin_amdgcn_update_dpp(0, part, kDppQuad1032, 0xF, 0xF, false);
+      part += __builtin_amdgcn_update_dpp(0, part, kDppQuad2301, 0xF, 0xF, false);
+      if (c < s.E && q == 0 && part < s.A) sel[part] = c;
+    } else if (t < s.E) {
       const int32_t rank = count_greater(keys, s.E, key);
       if (rank < s.A) sel[rank] = t;
     }
