@@ -289,8 +289,9 @@ struct Wk {
   bool xpend = false, xnext = false;
   // MOE. A step's batches are, per layer, layer_b fixed-stream batches and then dyn_b routed ones
   // (gate/up, then down), and finally the LM head's. A routed batch can be issued only once its
-  // layer's experts are chosen: until then nxt stays empty (deferred) and the router boundary
-  // issues it. L.moe holds the experts of layer sel_key (= step * L + layer) and their weights.
+  // layer's experts are chosen: until then nxt receives zeros from empty loads (deferred) and the
+  // router boundary issues it for real. L.moe holds the experts of layer sel_key (= step * L +
+  // layer) and their weights.
   int32_t dyn_b = 0;
   int32_t sel_key = -1;
   bool deferred = false;
@@ -484,12 +485,10 @@ struct Wk {
       if (deferred) return;  // nxt itself holds no data yet
       const int32_t sp = pidx, ss = pstep;
       advance();
-      bool later = false;  // a routed batch whose experts are not chosen yet: leave it to the stream
       batch_tiles([&](int b, __amdgpu_buffer_rsrc_t rs) {
         if (!deferred) load16_lds(rs, (uint32_t)(lane * 16), base + b * kTileBytes);
       });
-      later = deferred;
-      if (later) {
+      if (deferred) {  // a routed batch whose experts are not chosen yet: leave it to the stream
         deferred = false;
         pidx = sp;
         pstep = ss;
