@@ -14,6 +14,13 @@ milliseconds while the oracle still sees exactly the same bits:
   4·(65536²−1)/12), centred, and scaled in fp32 to standard deviation 0.02;
 * the fp32 value is rounded to bf16 with round-to-nearest-even.
 
+8-bit models (``weight_format`` 1) take the same bf16 values of every streamed matrix (the seven
+per-layer matrices and the LM head) times 128, encoded as e4m3fn codes with round-to-nearest-even
+by integer operations on the bit pattern (again identical on both backends), and give tensor t the
+scale 2^-7 * (0.75 + 0.25 * (t mod 4)): a synthetic 8-bit checkpoint whose matrices differ in scale,
+so that a scale applied to the wrong matrix shows. (The decoder itself never quantizes: it reads
+the codes and scales it is given.) The embedding and the norm gains stay bf16.
+
 RMSNorm gains are 1.0 (see ``norm_init``). Prompt ids are uniform in ``[0, V)`` by a
 multiply-shift of a hashed counter.
 
@@ -47,6 +54,7 @@ class ModelConfig:
     n_experts: int = 0
     n_experts_active: int = 0
     expert_ffn_dim: int = 0
+    weight_format: int = 0  # 0: bf16 matrices; 1: e4m3fn codes with one fp32 scale per matrix
 
     @property
     def q_dim(self) -> int:
@@ -93,7 +101,16 @@ SMALL_MOE = ModelConfig("small-moe", 2, 512, 8, 1, 128, 0, 4096, n_experts=32, n
                         expert_ffn_dim=768)
 MOE_2L = MOE.scaled(name="moe-2l", n_layers=2)
 
-MODELS: Dict[str, ModelConfig] = {m.name: m for m in (TINY, M1_6B, M8B, MOE, TINY_MOE, SMALL_MOE, MOE_2L)}
+# 8-bit weights: the tile holds 512 weights of a row, so d_model, n_heads * head_dim and ffn_dim are
+# multiples of 512 (the bf16 tiny shape is not): a small shape for the parity tests, and the 1.6B
+# and 8B shapes with 8-bit matrices.
+TINY_FP8 = ModelConfig("tiny-fp8", 2, 512, 8, 4, 64, 1536, 4096, weight_format=1)
+M1_6B_FP8 = M1_6B.scaled(name="1.6b-fp8", weight_format=1)
+M1_6B_FP8_2L = M1_6B.scaled(name="1.6b-fp8-2l", n_layers=2, weight_format=1)
+M8B_FP8 = M8B.scaled(name="8b-fp8", weight_format=1)
+
+MODELS: Dict[str, ModelConfig] = {m.name: m for m in (TINY, M1_6B, M8B, MOE, TINY_MOE, SMALL_MOE, MOE_2L, TINY_FP8,
+                                                       M1_6B_FP8, M1_6B_FP8_2L, M8B_FP8)}
 
 WORKLOADS: Dict[str, Workload] = {
     "tiny": Workload("tiny", TINY, 64, 32),
@@ -102,6 +119,8 @@ WORKLOADS: Dict[str, Workload] = {
     "1.6b-32k": Workload("1.6b-32k", M1_6B, 32768, 256),
     "8b-2k": Workload("8b-2k", M8B, 2048, 256),
     "moe-1k": Workload("moe-1k", MOE, 1024, 256),
+    "1.6b-1k-fp8": Workload("1.6b-1k-fp8", M1_6B_FP8, 1024, 512),
+    "8b-2k-fp8": Workload("8b-2k-fp8", M8B_FP8, 2048, 256),
 }
 
 # Tensor numbering for the weight generator: 0 embed, 1 lm_head, then per layer l
@@ -241,6 +260,68 @@ def _weights_bits_torch(shape, seed: int, tidx: int, device, std: float = WEIGHT
     return out.view(shape)
 
 
+FP8_MATS = LAYER_MATS + ("lm_head",)
+
+
+def fp8_scale(tidx: int) -> float:
+    """Scale of tensor tidx of an 8-bit model (exact in fp32)."""
+    return 2.0 ** -7 * (0.75 + 0.25 * (tidx % 4))
+
+
+def fp8_scales(cfg: ModelConfig) -> np.ndarray:
+    """[n_layers * 7 + 1] fp32: per layer wq, wk, wv, wo, w_gate, w_up, w_down, then lm_head."""
+    sc = [fp8_scale(tensor_index(m, l)) for l in range(cfg.n_layers) for m in LAYER_MATS]
+    return np.array(sc + [fp8_scale(tensor_index("lm_head"))], dtype=np.float32)
+
+
+def _e4m3_codes(xp, b):
+    """bf16 bit patterns (int64) -> e4m3fn codes of 128 times their values, round to nearest even.
+
+    Integer operations on the fp32 pattern (b << 16, exponent raised by 7): exponents >= 121 give
+    normal codes (3 mantissa bits kept, a carry may raise the exponent), smaller ones the subnormal
+    codes m * 2^-9 (m = 0..8; 8 is the smallest normal code). The inputs here stay far below 448.
+    """
+    u = (b & 0xFFFF) << 16
+    sign = (u >> 31) & 1
+    a = u & 0x7FFFFFFF
+    a = xp.where(a == 0, a, a + (7 << 23))
+    e = a >> 23
+    mant = a & 0x7FFFFF
+    m3 = mant >> 20
+    rem = mant & 0xFFFFF
+    up = ((rem > 0x80000) | ((rem == 0x80000) & ((m3 & 1) == 1))).astype(m3.dtype) if xp is np else \
+        ((rem > 0x80000) | ((rem == 0x80000) & ((m3 & 1) == 1))).to(m3.dtype)
+    normal = (((e - 120) << 3) | m3) + up
+    sig = mant | 0x800000
+    shift = xp.clip(141 - e, 21, 40) if xp is np else (141 - e).clamp(21, 40)
+    q = sig >> shift
+    r = sig - (q << shift)
+    half = xp.ones_like(r) << (shift - 1)
+    upq = (r > half) | ((r == half) & ((q & 1) == 1))
+    sub = q + (upq.astype(q.dtype) if xp is np else upq.to(q.dtype))
+    sub = xp.where(e == 0, xp.zeros_like(sub), sub)
+    code = xp.where(e >= 121, normal, sub)
+    code = xp.minimum(code, xp.full_like(code, 0x7E))
+    return code | (sign << 7)
+
+
+def fp8_codes_np(bits: np.ndarray) -> np.ndarray:
+    """uint16 bf16 bits -> uint8 e4m3fn codes (see _e4m3_codes)."""
+    return _e4m3_codes(np, bits.astype(np.int64)).astype(np.uint8)
+
+
+def fp8_codes_torch(bits):
+    """int16 bf16 bits (torch) -> uint8 codes on the same device, chunked."""
+    import torch
+    flat = bits.reshape(-1)
+    out = torch.empty(flat.numel(), dtype=torch.uint8, device=flat.device)
+    chunk = 1 << 26
+    for s in range(0, flat.numel(), chunk):
+        b = flat[s:s + chunk].to(torch.int64) & 0xFFFF
+        out[s:s + chunk] = _e4m3_codes(torch, b).to(torch.uint8)
+    return out.view(bits.shape)
+
+
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << 16).view(np.float32)
 
@@ -264,6 +345,10 @@ def make_weights_np(cfg: ModelConfig, seed: int = 0) -> Dict[str, object]:
     for name in layer_mats(cfg):
         w[name] = [_weights_bits_np(mat_shape(cfg, name), seed, tensor_index(name, l))
                    for l in range(cfg.n_layers)]
+    if cfg.weight_format == 1:
+        for name in FP8_MATS:
+            w[name] = [fp8_codes_np(a) for a in w[name]] if isinstance(w[name], list) else fp8_codes_np(w[name])
+        w["w_scale"] = fp8_scales(cfg)
     return w
 
 
@@ -281,15 +366,23 @@ def make_weights_torch(cfg: ModelConfig, seed: int = 0, device="cuda") -> Dict[s
     for name in layer_mats(cfg):
         w[name] = [_weights_bits_torch(mat_shape(cfg, name), seed, tensor_index(name, l), device)
                    for l in range(cfg.n_layers)]
+    if cfg.weight_format == 1:
+        for name in FP8_MATS:
+            w[name] = [fp8_codes_torch(t) for t in w[name]] if isinstance(w[name], list) else fp8_codes_torch(w[name])
+        w["w_scale"] = fp8_scales(cfg)
     return w
 
 
 def weights_torch_to_np(w) -> Dict[str, object]:
     """Copy a torch weight dict to host uint16 arrays (the oracle's input format)."""
     def cv(t):
-        return t.cpu().numpy().view(np.uint16)
+        a = t.cpu().numpy()
+        return a if a.dtype == np.uint8 else a.view(np.uint16)
     out = {}
     for k, v in w.items():
+        if isinstance(v, np.ndarray):
+            out[k] = v
+            continue
         out[k] = [cv(t) for t in v] if isinstance(v, list) else cv(v)
     return out
 

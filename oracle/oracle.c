@@ -26,6 +26,14 @@
  * the order written here. Row loops may be split over threads (rows only), which cannot change
  * any result bit.
  *
+ * 8-bit weights (weight_format 1). The pages note that 8-bit weights halve the bytes read per
+ * token and so roughly double a bandwidth-bound decoder's ceiling, at some cost in accuracy
+ * (aikraft.ru, §02; wink.run, 《GPU 算力越堆越高,生成 token 为什么还是慢》, the section on what
+ * optimisations change), while the engine they describe itself quantizes nothing (zdabc.icu,
+ * 《Kog 推理引擎：不砍精度，单请求冲到 3000 tokens/s》). They fix no 8-bit format, so this file reads
+ * it as the OCP E4M3 encoding (e4m3fn) with one fp32 scale per matrix: the matrix is the scale
+ * times the decoded codes (oc_e4m3_to_f32, oc_gemv_e4m3). Everything else is the bf16 model.
+ *
  * Sampling: greedy = argmax with ties to the lower index. Top-k: z = logits / T (fp32); the k
  * largest z (ties to the lower index) in descending order; p_j = exp(z_j - z_0) / sum (fp64);
  * u = (splitmix64(seed ^ splitmix64(pos)) >> 40) * 2^-24; the first j whose running fp64 sum of
@@ -42,6 +50,7 @@ typedef struct {
   float rms_eps, rope_theta;
   int32_t max_seq;
   int32_t n_experts, n_experts_active, expert_ffn_dim; /* n_experts == 0: dense feed-forward */
+  int32_t weight_format; /* 0: bf16 matrices; 1: fp8 e4m3fn codes with one fp32 scale per matrix */
 } oc_config;
 
 /* All matrices row-major [out][in], bf16 bit patterns. Per-layer arrays hold n_layers pointers.
@@ -53,6 +62,11 @@ typedef struct {
   const uint16_t *const *attn_norm, *const *wq, *const *wk, *const *wv, *const *wo;
   const uint16_t *const *ffn_norm, *const *w_gate, *const *w_up, *const *w_down;
   const uint16_t *const *w_router, *const *moe_gate, *const *moe_up, *const *moe_down;
+  /* weight_format 1: wq, wk, wv, wo, w_gate, w_up, w_down and lm_head hold one byte per weight
+   * (e4m3fn codes, same [out][in] layout) and the matrix is scale * decoded codes, with the scales
+   * in w_scale: [n_layers][7] in the order wq, wk, wv, wo, w_gate, w_up, w_down, then lm_head.
+   * Embedding and norm gains stay bf16. */
+  const float* w_scale;
 } oc_weights;
 
 static int g_threads = 1;
@@ -78,6 +92,21 @@ float oc_bf16_to_f32(uint16_t b) {
   float f;
   memcpy(&f, &u, 4);
   return f;
+}
+
+/* Value of an fp8 e4m3fn code (the OCP 8-bit floating-point format's E4M3 encoding): sign bit 7,
+ * exponent bits 6..3 with bias 7, mantissa bits 2..0; exponent 0 encodes the subnormals
+ * m * 2^-9; there are no infinities, and exponent 15 with mantissa 7 is NaN. Every value is exact
+ * in fp32. */
+float oc_e4m3_to_f32(uint8_t b) {
+  const int sign = b >> 7, e = (b >> 3) & 15, m = b & 7;
+  float v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexpf((float)m, -9);
+  else
+    v = ldexpf(1.0f + (float)m / 8.0f, e - 7);
+  return sign ? -v : v;
 }
 
 /* fp32 -> bf16 with round-to-nearest-even (NaN kept quiet). */
@@ -118,6 +147,32 @@ void oc_gemv(const uint16_t* W, const float* x, float* y, int rows, int cols) {
       for (int k = 0; k < cols; k++) acc += oc_bf16_to_f32(w[k]) * x[k];
     y[r] = acc;
   }
+}
+
+/* y[r] = scale * sum_k q(W[r][k]) * x[k] for a matrix of e4m3fn codes: the products and the sum
+ * are fp32 in the order of oc_gemv, and the scale multiplies the finished sum. */
+void oc_gemv_e4m3(const uint8_t* W, float scale, const float* x, float* y, int rows, int cols) {
+  int r;
+#pragma omp parallel for num_threads(g_threads) schedule(static) if (g_threads > 1)
+  for (r = 0; r < rows; r++) {
+    const uint8_t* w = W + (size_t)r * cols;
+    float acc = 0.0f;
+    if (g_gemv_desc)
+      for (int k = cols - 1; k >= 0; k--) acc += oc_e4m3_to_f32(w[k]) * x[k];
+    else
+      for (int k = 0; k < cols; k++) acc += oc_e4m3_to_f32(w[k]) * x[k];
+    y[r] = acc * scale;
+  }
+}
+
+/* Matrix m (0..6: wq, wk, wv, wo, w_gate, w_up, w_down) of layer l, or the LM head (l == n_layers),
+ * in the model's weight format. */
+static void mat_gemv(const oc_config* c, const oc_weights* w, int l, int m, const uint16_t* W, const float* x,
+                     float* y, int rows, int cols) {
+  if (c->weight_format == 1)
+    oc_gemv_e4m3((const uint8_t*)W, w->w_scale[l < c->n_layers ? l * 7 + m : c->n_layers * 7], x, y, rows, cols);
+  else
+    oc_gemv(W, x, y, rows, cols);
 }
 
 /* u = x * (1/sqrt(mean(x^2) + eps)) * g ; the sum of squares is fp32, i ascending. */
@@ -306,6 +361,7 @@ int oc_step(const oc_config* c, const oc_weights* w, uint16_t* kc, uint16_t* vc,
   const int d = c->d_model, hd = c->head_dim, nq = c->n_heads, nkv = c->n_kv_heads, F = c->ffn_dim;
   if (pos < 0 || pos >= c->max_seq || token < 0 || token >= c->vocab_size) return -1;
   if (nq % nkv != 0) return -1;
+  if (c->weight_format != 0 && (c->weight_format != 1 || c->n_experts > 0 || !w->w_scale)) return -1;
   const int group = nq / nkv;
   float* x = (float*)malloc(sizeof(float) * d);
   float* u = (float*)malloc(sizeof(float) * d);
@@ -322,9 +378,9 @@ int oc_step(const oc_config* c, const oc_weights* w, uint16_t* kc, uint16_t* vc,
   for (int l = 0; l < c->n_layers; l++) {
     /* attention block */
     oc_rmsnorm(x, w->attn_norm[l], u, d, c->rms_eps);
-    oc_gemv(w->wq[l], u, q, nq * hd, d);
-    oc_gemv(w->wk[l], u, k, nkv * hd, d);
-    oc_gemv(w->wv[l], u, v, nkv * hd, d);
+    mat_gemv(c, w, l, 0, w->wq[l], u, q, nq * hd, d);
+    mat_gemv(c, w, l, 1, w->wk[l], u, k, nkv * hd, d);
+    mat_gemv(c, w, l, 2, w->wv[l], u, v, nkv * hd, d);
     for (int h = 0; h < nq; h++) oc_rope(q + h * hd, hd, pos, c->rope_theta);
     for (int j = 0; j < nkv; j++) oc_rope(k + j * hd, hd, pos, c->rope_theta);
     for (int j = 0; j < nkv; j++)
@@ -337,7 +393,7 @@ int oc_step(const oc_config* c, const oc_weights* w, uint16_t* kc, uint16_t* vc,
       oc_attend(q + h * hd, kc + kv_off(c, l, j, 0), vc + kv_off(c, l, j, 0), pos + 1, hd, (size_t)hd,
                 o + h * hd, NULL);
     }
-    oc_gemv(w->wo[l], o, t, d, nq * hd);
+    mat_gemv(c, w, l, 3, w->wo[l], o, t, d, nq * hd);
     for (int i = 0; i < d; i++) x[i] += t[i];
     /* feed-forward block */
     oc_rmsnorm(x, w->ffn_norm[l], u, d, c->rms_eps);
@@ -346,15 +402,15 @@ int oc_step(const oc_config* c, const oc_weights* w, uint16_t* kc, uint16_t* vc,
                       ? g_route_log + ((size_t)pos * c->n_layers + l) * c->n_experts : NULL;
       oc_moe_ffn(c, w, l, u, t, zl);
     } else {
-      oc_gemv(w->w_gate[l], u, g, F, d);
-      oc_gemv(w->w_up[l], u, up, F, d);
+      mat_gemv(c, w, l, 4, w->w_gate[l], u, g, F, d);
+      mat_gemv(c, w, l, 5, w->w_up[l], u, up, F, d);
       for (int i = 0; i < F; i++) g[i] = oc_silu(g[i]) * up[i];
-      oc_gemv(w->w_down[l], g, t, d, F);
+      mat_gemv(c, w, l, 6, w->w_down[l], g, t, d, F);
     }
     for (int i = 0; i < d; i++) x[i] += t[i];
   }
   oc_rmsnorm(x, w->final_norm, u, d, c->rms_eps);
-  oc_gemv(w->lm_head, u, logits, c->vocab_size, d);
+  mat_gemv(c, w, c->n_layers, 0, w->lm_head, u, logits, c->vocab_size, d);
 
   free(x); free(u); free(q); free(k); free(v); free(o); free(t); free(g); free(up);
   return 0;
@@ -369,6 +425,7 @@ int oc_step(const oc_config* c, const oc_weights* w, uint16_t* kc, uint16_t* vc,
 int oc_full_recompute(const oc_config* c, const oc_weights* w, const int* tokens, int n, float* logits) {
   const int d = c->d_model, hd = c->head_dim, nq = c->n_heads, nkv = c->n_kv_heads, F = c->ffn_dim;
   if (n <= 0 || nq % nkv != 0) return -1;
+  if (c->weight_format != 0 && (c->weight_format != 1 || c->n_experts > 0 || !w->w_scale)) return -1;
   for (int r = 0; r < n; r++)
     if (tokens[r] < 0 || tokens[r] >= c->vocab_size) return -1;
   const int group = nq / nkv;
@@ -392,9 +449,9 @@ int oc_full_recompute(const oc_config* c, const oc_weights* w, const int* tokens
   for (int l = 0; l < c->n_layers; l++) {
     for (int r = 0; r < n; r++) oc_rmsnorm(X + (size_t)r * d, w->attn_norm[l], U + (size_t)r * d, d, c->rms_eps);
     for (int r = 0; r < n; r++) {
-      oc_gemv(w->wq[l], U + (size_t)r * d, Q + (size_t)r * nq * hd, nq * hd, d);
-      oc_gemv(w->wk[l], U + (size_t)r * d, Kf + (size_t)r * nkv * hd, nkv * hd, d);
-      oc_gemv(w->wv[l], U + (size_t)r * d, Vf + (size_t)r * nkv * hd, nkv * hd, d);
+      mat_gemv(c, w, l, 0, w->wq[l], U + (size_t)r * d, Q + (size_t)r * nq * hd, nq * hd, d);
+      mat_gemv(c, w, l, 1, w->wk[l], U + (size_t)r * d, Kf + (size_t)r * nkv * hd, nkv * hd, d);
+      mat_gemv(c, w, l, 2, w->wv[l], U + (size_t)r * d, Vf + (size_t)r * nkv * hd, nkv * hd, d);
       for (int h = 0; h < nq; h++) oc_rope(Q + (size_t)r * nq * hd + h * hd, hd, r, c->rope_theta);
       for (int j = 0; j < nkv; j++) oc_rope(Kf + (size_t)r * nkv * hd + j * hd, hd, r, c->rope_theta);
     }
@@ -432,7 +489,7 @@ int oc_full_recompute(const oc_config* c, const oc_weights* w, const int* tokens
         }
       }
     for (int r = 0; r < n; r++) {
-      oc_gemv(w->wo[l], O + (size_t)r * nq * hd, T + (size_t)r * d, d, nq * hd);
+      mat_gemv(c, w, l, 3, w->wo[l], O + (size_t)r * nq * hd, T + (size_t)r * d, d, nq * hd);
       for (int i = 0; i < d; i++) X[(size_t)r * d + i] += T[(size_t)r * d + i];
     }
     for (int r = 0; r < n; r++) oc_rmsnorm(X + (size_t)r * d, w->ffn_norm[l], U + (size_t)r * d, d, c->rms_eps);
@@ -467,16 +524,17 @@ int oc_full_recompute(const oc_config* c, const oc_weights* w, const int* tokens
       continue;
     }
     for (int r = 0; r < n; r++) {
-      oc_gemv(w->w_gate[l], U + (size_t)r * d, G + (size_t)r * F, F, d);
-      oc_gemv(w->w_up[l], U + (size_t)r * d, Up + (size_t)r * F, F, d);
+      mat_gemv(c, w, l, 4, w->w_gate[l], U + (size_t)r * d, G + (size_t)r * F, F, d);
+      mat_gemv(c, w, l, 5, w->w_up[l], U + (size_t)r * d, Up + (size_t)r * F, F, d);
       for (int i = 0; i < F; i++) G[(size_t)r * F + i] = oc_silu(G[(size_t)r * F + i]) * Up[(size_t)r * F + i];
-      oc_gemv(w->w_down[l], G + (size_t)r * F, T + (size_t)r * d, d, F);
+      mat_gemv(c, w, l, 6, w->w_down[l], G + (size_t)r * F, T + (size_t)r * d, d, F);
       for (int i = 0; i < d; i++) X[(size_t)r * d + i] += T[(size_t)r * d + i];
     }
   }
   for (int r = 0; r < n; r++) {
     oc_rmsnorm(X + (size_t)r * d, w->final_norm, U + (size_t)r * d, d, c->rms_eps);
-    oc_gemv(w->lm_head, U + (size_t)r * d, logits + (size_t)r * c->vocab_size, c->vocab_size, d);
+    mat_gemv(c, w, c->n_layers, 0, w->lm_head, U + (size_t)r * d, logits + (size_t)r * c->vocab_size,
+             c->vocab_size, d);
   }
   free(X); free(U); free(Q); free(Kf); free(Vf); free(Kb); free(Vb); free(O); free(T); free(G); free(Up); free(sc);
   return 0;

@@ -75,6 +75,11 @@ def _load():
         lib.oc_moe_ffn.restype = None
         lib.oc_set_route_log.argtypes = [f32p, C.c_int]
         lib.oc_set_route_log.restype = None
+        u8p = C.POINTER(C.c_uint8)
+        lib.oc_e4m3_to_f32.argtypes = [C.c_uint8]
+        lib.oc_e4m3_to_f32.restype = C.c_float
+        lib.oc_gemv_e4m3.argtypes = [u8p, C.c_float, f32p, f32p, C.c_int, C.c_int]
+        lib.oc_gemv_e4m3.restype = None
         _lib = lib
     return _lib
 
@@ -99,6 +104,21 @@ def gemv(W: np.ndarray, x: np.ndarray) -> np.ndarray:
     rows, cols = W.shape
     y = np.empty(rows, dtype=np.float32)
     _load().oc_gemv(_p(W, C.c_uint16), _p(x, C.c_float), _p(y, C.c_float), rows, cols)
+    return y
+
+
+def e4m3_to_f32(code: int) -> float:
+    """Value of one fp8 e4m3fn code (0..255)."""
+    return float(_load().oc_e4m3_to_f32(int(code) & 0xFF))
+
+
+def gemv_e4m3(W: np.ndarray, scale: float, x: np.ndarray) -> np.ndarray:
+    """scale * (decoded W) x for a [rows][cols] matrix of e4m3fn codes (uint8)."""
+    W = np.ascontiguousarray(W, dtype=np.uint8)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, cols = W.shape
+    y = np.empty(rows, dtype=np.float32)
+    _load().oc_gemv_e4m3(_p(W, C.c_uint8), float(scale), _p(x, C.c_float), _p(y, C.c_float), rows, cols)
     return y
 
 
@@ -181,7 +201,7 @@ class _Cfg(C.Structure):
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn_dim", C.c_int32),
                 ("vocab_size", C.c_int32), ("rms_eps", C.c_float), ("rope_theta", C.c_float),
                 ("max_seq", C.c_int32), ("n_experts", C.c_int32), ("n_experts_active", C.c_int32),
-                ("expert_ffn_dim", C.c_int32)]
+                ("expert_ffn_dim", C.c_int32), ("weight_format", C.c_int32)]
 
 
 _PP = C.POINTER(C.POINTER(C.c_uint16))
@@ -191,7 +211,8 @@ class _W(C.Structure):
     _fields_ = [("embed", C.POINTER(C.c_uint16)), ("final_norm", C.POINTER(C.c_uint16)),
                 ("lm_head", C.POINTER(C.c_uint16)), ("attn_norm", _PP), ("wq", _PP), ("wk", _PP),
                 ("wv", _PP), ("wo", _PP), ("ffn_norm", _PP), ("w_gate", _PP), ("w_up", _PP),
-                ("w_down", _PP), ("w_router", _PP), ("moe_gate", _PP), ("moe_up", _PP), ("moe_down", _PP)]
+                ("w_down", _PP), ("w_router", _PP), ("moe_gate", _PP), ("moe_up", _PP), ("moe_down", _PP),
+                ("w_scale", C.POINTER(C.c_float))]
 
 
 _LAYER_KEYS = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")
@@ -204,7 +225,10 @@ class OracleModel:
     ``cfg`` needs attributes n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab_size,
     rms_eps, rope_theta, n_experts, n_experts_active, expert_ffn_dim. ``weights`` maps names to
     uint16 arrays (per-layer names to lists). A mixture-of-experts model (n_experts > 0) has
-    w_router, moe_gate, moe_up, moe_down per layer instead of w_gate, w_up, w_down.
+    w_router, moe_gate, moe_up, moe_down per layer instead of w_gate, w_up, w_down. With
+    ``cfg.weight_format == 1`` (optional attribute, default 0) wq, wk, wv, wo, w_gate, w_up, w_down
+    and lm_head are uint8 arrays of e4m3fn codes and ``weights["w_scale"]`` holds the fp32 scales
+    [n_layers * 7 + 1] (per layer wq, wk, wv, wo, w_gate, w_up, w_down; then lm_head).
     """
 
     def __init__(self, cfg, weights: Dict[str, object], max_seq: int):
@@ -213,10 +237,11 @@ class OracleModel:
         self._keep = []
         self._c = _Cfg(cfg.n_layers, cfg.d_model, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn_dim,
                        cfg.vocab_size, cfg.rms_eps, cfg.rope_theta, self.max_seq, cfg.n_experts,
-                       cfg.n_experts_active, cfg.expert_ffn_dim)
+                       cfg.n_experts_active, cfg.expert_ffn_dim, int(getattr(cfg, "weight_format", 0)))
 
-        def arr(a):
-            a = np.ascontiguousarray(a, dtype=np.uint16)
+        def arr(a):  # bf16 bit patterns, or bytes (fp8 codes) passed through the same pointer type
+            a = np.asarray(a)
+            a = np.ascontiguousarray(a, dtype=np.uint8 if a.dtype == np.uint8 else np.uint16)
             self._keep.append(a)
             return a.ctypes.data_as(C.POINTER(C.c_uint16))
 
@@ -228,8 +253,14 @@ class OracleModel:
         def arrs_opt(k):
             return arrs(weights[k]) if k in weights else C.cast(None, _PP)
 
+        if "w_scale" in weights:
+            sc = np.ascontiguousarray(weights["w_scale"], dtype=np.float32)
+            self._keep.append(sc)
+            scp = sc.ctypes.data_as(C.POINTER(C.c_float))
+        else:
+            scp = C.cast(None, C.POINTER(C.c_float))
         self._w = _W(arr(weights["embed"]), arr(weights["final_norm"]), arr(weights["lm_head"]),
-                     *[arrs_opt(k) for k in _LAYER_KEYS + _MOE_KEYS])
+                     *[arrs_opt(k) for k in _LAYER_KEYS + _MOE_KEYS], scp)
         kv_elems = cfg.n_layers * cfg.n_kv_heads * self.max_seq * cfg.head_dim
         self.kcache = np.zeros(kv_elems, dtype=np.uint16)
         self.vcache = np.zeros(kv_elems, dtype=np.uint16)
