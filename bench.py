@@ -167,10 +167,10 @@ def main():
     ttft_ms = ttft[1]
     # the prompt pass's matrix products: 2 x (tokens - 1) x the layer weights (the last position
     # runs through the decode kernel), plus the causal attention products
-    mm = traffic.weight_bytes(m) // 2 - m.vocab_size * m.d_model - (2 * m.n_layers + 2) * m.d_model
+    mm = traffic.matrix_weights(m) - m.vocab_size * m.d_model
     attn = 4 * m.n_layers * m.n_heads * m.head_dim * (P - 1) * P // 2
     prefill_flops = 2 * (P - 1) * mm + attn
-    if m.n_experts:  # every prompt position runs through the decode program (per-position routing)
+    if m.n_experts or m.weight_format:  # every prompt position runs through the decode program
         prompt_pass = {"kind": "decode program, teacher-forced, one position after the other",
                        "positions_per_s": round(P / (ttft_ms * 1e-3), 1)}
     else:
@@ -263,10 +263,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8-e4m3 weights, f32 activations" if m.weight_format else "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "prompt_len": P, "decode_positions": [P, P + K - 1],
-                   "sampling": "greedy", "weights": "bf16, counter-based N(0,0.02) approx., seed 0",
+                   "sampling": "greedy",
+                   "weights": ("e4m3fn codes of the seeded bf16 values x 128, one fp32 scale per matrix"
+                               if m.weight_format else "bf16, counter-based N(0,0.02) approx., seed 0"),
                    "experts": (f"{m.n_experts_active} of {m.n_experts} routed per token, width {m.expert_ffn_dim}"
                                if m.n_experts else None),
                    "kv_cache": "bf16", "accumulate": "f32", "launches_per_timed_region": 1},

@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkie.so")
-SOURCES = ["api.cpp", "monokernel.hip", "kernels_hd64.hip", "kernels_hd128.hip", "kernels_moe.hip", "pack.hip",
+SOURCES = ["api.cpp", "monokernel.hip", "kernels_hd64.hip", "kernels_hd128.hip", "kernels_moe.hip", "kernels_fp8.hip", "pack.hip",
            "prefill.hip"]
 
 # Packed fp32 instructions are disabled: the compiler may not form v_pk_* f32 ops from float code.

@@ -33,6 +33,7 @@ struct kie_ctx {
   KernelFn kernel;
   KernelFn prompt_kernel;
   int32_t lds;
+  bool w8;                 // 8-bit (e4m3fn) layer matrices and LM head
   int32_t pos;
   uint32_t epoch;  // tag of the next step
   bool bad_state;
@@ -79,6 +80,17 @@ static int query_cus(int* out, std::string* err) {
   *out = n;
   return KIE_OK;
 }
+
+// Packed-image geometry in the config's weight format (tiles of kTileK bf16 or 2 * kTileK 8-bit
+// weights per row).
+static bool cfg_w8(const kie_config* c) { return c && c->weight_format == KIE_WEIGHTS_FP8_E4M3; }
+static int64_t pk_stream_tiles(const Shape& s, bool w8, int32_t w, int32_t v) {
+  return w8 ? stream_tiles<2 * kTileK>(s, w, v) : stream_tiles(s, w, v);
+}
+static int64_t pk_embed_offset(const Shape& s, bool w8) {
+  return w8 ? packed_embed_offset<2 * kTileK>(s) : packed_embed_offset(s);
+}
+static int64_t pk_bytes(const Shape& s, bool w8) { return w8 ? packed_bytes<2 * kTileK>(s) : packed_bytes(s); }
 
 // Shape from a config; nwg = compute units of the current device (or `nwg_override` > 0).
 static kie_status make_shape(const kie_config* c, int nwg_override, Shape* s, std::string* err) {
@@ -133,9 +145,19 @@ static kie_status make_shape(const kie_config* c, int nwg_override, Shape* s, st
       return KIE_ERR_UNSUPPORTED;
     }
   }
-  if (s->d % kTileK || s->qdim() % kTileK || s->F % kTileK) {
+  if (c->weight_format != KIE_WEIGHTS_BF16 && c->weight_format != KIE_WEIGHTS_FP8_E4M3) {
+    set_err(err, "unknown weight_format %d", c->weight_format);
+    return KIE_ERR_INVALID_ARG;
+  }
+  const bool w8 = cfg_w8(c);
+  if (w8 && moe) {
+    set_err(err, "8-bit weights are supported for dense layers only");
+    return KIE_ERR_UNSUPPORTED;
+  }
+  const int tk = w8 ? 2 * kTileK : kTileK;
+  if (s->d % tk || s->qdim() % tk || s->F % tk) {
     set_err(err, "d_model (%d), n_heads*head_dim (%d) and ffn_dim (%d) must be multiples of %d", s->d, s->qdim(), s->F,
-            kTileK);
+            tk);
     return KIE_ERR_UNSUPPORTED;
   }
   if (s->hd != 64 && s->hd != 128) {
@@ -162,7 +184,8 @@ static kie_status make_shape(const kie_config* c, int nwg_override, Shape* s, st
   }
   for (int st = ST_QKV; st < ST_COUNT; ++st) {
     const int64_t per_wg = ((int64_t)s->stage_pairs(st) + nwg - 1) / nwg;
-    const int64_t units = per_wg * (s->stage_kt(st) / unit_tiles(s->stage_kt(st)));
+    const int32_t kt = s->stage_k(st) / tk;
+    const int64_t units = per_wg * (kt / unit_tiles(kt));
     if (units > kMaxUnits) {  // per-unit partial sums of one stage live in LDS
       set_err(err, "a weight matrix needs %lld work units per compute unit (at most %d supported)", (long long)units,
               kMaxUnits);
@@ -181,7 +204,7 @@ extern "C" {
 size_t kie_packed_weight_bytes(const kie_config* cfg) {
   Shape s;
   if (make_shape(cfg, 0, &s, nullptr) != KIE_OK) return 0;
-  return (size_t)packed_bytes(s);
+  return (size_t)pk_bytes(s, cfg_w8(cfg));
 }
 
 size_t kie_kv_cache_bytes(const kie_config* cfg) {
@@ -234,6 +257,18 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
   if (st != KIE_OK) return st;
   const int L = s.L;
   const bool moe = s.moe();
+  const bool w8 = cfg_w8(cfg);
+  if (w8) {
+    if (!src->weight_scales) {
+      set_err(err, "8-bit weights need weight_scales");
+      return KIE_ERR_INVALID_ARG;
+    }
+    for (int i = 0; i < L * 7 + 1; ++i)
+      if (!(fabsf(src->weight_scales[i]) < INFINITY)) {
+        set_err(err, "weight_scales[%d] is not finite", i);
+        return KIE_ERR_INVALID_ARG;
+      }
+  }
   if (!src->embed || !src->final_norm || !src->lm_head || !src->attn_norm || !src->wq || !src->wk || !src->wv ||
       !src->wo || !src->ffn_norm ||
       (moe ? (!src->w_router || !src->moe_gate || !src->moe_up || !src->moe_down)
@@ -278,10 +313,11 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
     set_err(err, "shape needs %d bytes of LDS per workgroup (device limit %d)", lds, lds_limit);
     return KIE_ERR_UNSUPPORTED;
   }
-  KernelFn kfn = decode_kernel_for(s.group(), s.hd, false, moe);
-  KernelFn pfn = decode_kernel_for(s.group(), s.hd, true, moe);
+  KernelFn kfn = decode_kernel_for(s.group(), s.hd, false, moe, w8);
+  KernelFn pfn = decode_kernel_for(s.group(), s.hd, true, moe, w8);
   if (!kfn || !pfn) {
-    set_err(err, "no kernel for group %d head_dim %d%s", s.group(), s.hd, moe ? " with mixture-of-experts layers" : "");
+    set_err(err, "no kernel for group %d head_dim %d%s", s.group(), s.hd,
+            moe ? " with mixture-of-experts layers" : (w8 ? " with 8-bit weights" : ""));
     return KIE_ERR_UNSUPPORTED;
   }
   HIP_TRY(err, hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, lds));
@@ -305,6 +341,7 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
   c->kernel = kfn;
   c->prompt_kernel = pfn;
   c->lds = lds;
+  c->w8 = w8;
   c->pos = 0;
   c->epoch = 1;
   c->bad_state = false;
@@ -318,7 +355,7 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
   for (int w = 0; w < s.nwg; ++w) {
     for (int v = 0; v < kWaves; ++v) {
       c->wbase_host[(size_t)w * kWaves + v] = acc;
-      acc += stream_tiles(s, w, v);
+      acc += pk_stream_tiles(s, w8, w, v);
     }
   }
   c->wbase_host[(size_t)s.nwg * kWaves] = acc;
@@ -349,6 +386,10 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
   if ((e = hipMemcpyAsync(norms + (size_t)L * 2 * s.d, src->final_norm, (size_t)s.d * 2, hipMemcpyDeviceToDevice,
                           stm)) != hipSuccess)
     return fail("copy norms", e);
+  // 8-bit weights: the matrix scales (a blocking copy from the caller's host array)
+  if (w8 && (e = hipMemcpy(c->ws + c->wso.wscale, src->weight_scales, ((size_t)L * 7 + 1) * 4, hipMemcpyHostToDevice)) !=
+                hipSuccess)
+    return fail("copy weight scales", e);
   // weights: per-WG token streams, then the embedding table
   const int64_t* wbase_dev = (const int64_t*)(c->ws + c->wso.wbase);
   for (int l = 0; l <= L; ++l) {
@@ -358,6 +399,7 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
     a.packed = c->packed;
     a.wbase = wbase_dev;
     a.layer = l;
+    a.w8 = w8 ? 1 : 0;
     if (l < L) {
       a.wq = src->wq[l];
       a.wk = src->wk[l];
@@ -380,7 +422,7 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
     if ((e = launch_pack_layer(a, stm)) != hipSuccess) return fail("pack weights", e);
     if (moe && l < L && (e = launch_pack_experts(a, stm)) != hipSuccess) return fail("pack experts", e);
   }
-  if ((e = hipMemcpyAsync(c->packed + packed_embed_offset(s), src->embed, (size_t)s.V * s.d * 2,
+  if ((e = hipMemcpyAsync(c->packed + pk_embed_offset(s, w8), src->embed, (size_t)s.V * s.d * 2,
                           hipMemcpyDeviceToDevice, stm)) != hipSuccess)
     return fail("copy embedding", e);
   *out = c;
@@ -497,7 +539,7 @@ static kie_status launch(kie_ctx* ctx, const int32_t* first, int32_t n, const in
   P.s = ctx->s;
   P.exo = ctx->exo;
   P.packed = ctx->packed;
-  P.embed = (const uint16_t*)(ctx->packed + packed_embed_offset(ctx->s));
+  P.embed = (const uint16_t*)(ctx->packed + pk_embed_offset(ctx->s, ctx->w8));
   P.norms = (const uint16_t*)(ctx->ws + ctx->wso.norms);
   P.kv = ctx->kv;
   P.ex = (uint64_t*)(ctx->ws + ctx->wso.exch);
@@ -523,6 +565,7 @@ static kie_status launch(kie_ctx* ctx, const int32_t* first, int32_t n, const in
   P.timeout_ticks = ctx->timeout_ticks;
   P.skew = ctx->skew;
   P.xb_lds = (uint32_t)lds_slot_offset(ctx->s);
+  P.wscale = ctx->w8 ? (const float*)(ctx->ws + ctx->wso.wscale) : nullptr;
   void* args[] = {&P};
   const void* fn = (const void*)(lm_last_only ? ctx->prompt_kernel : ctx->kernel);
   HIP_TRY(&ctx->last_error,
@@ -551,9 +594,10 @@ kie_status kie_prefill(kie_ctx* ctx, const int32_t* tokens_dev, int32_t n_tokens
     set_err(&ctx->last_error, "position %d + %d tokens exceeds max_seq_len %d", ctx->pos, n_tokens, ctx->s.max_seq);
     return KIE_ERR_CAPACITY;
   }
-  // mixture of experts: every position through the decode program, teacher-forced (position i + 1
-  // processes tokens[i + 1]); the LM head and the sampler run on the last one only
-  if (ctx->s.moe())
+  // mixture of experts and 8-bit weights: every position through the decode program,
+  // teacher-forced (position i + 1 processes tokens[i + 1]); the LM head and the sampler run on the
+  // last one only
+  if (ctx->s.moe() || ctx->w8)
     return launch(ctx, tokens_dev, n_tokens, tokens_dev + 1, nullptr, first_token_dev, last_logits_dev, 1, sampling);
   // all but the last prompt position: every layer as GEMMs on the matrix cores (K/V rows only)
   if (n_tokens > 1) {

@@ -9,6 +9,7 @@ namespace kie {
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0]|[15:14], expcnt[6:4], lgkmcnt[11:8])
 constexpr int kWaitLgkm0 = 0xC07F;

@@ -77,7 +77,9 @@ struct Shape {
       default: return d;
     }
   }
-  KIE_HD int32_t stage_kt(int st) const { return stage_k(st) / kTileK; }
+  // k-tiles of a row: TK weights per tile row (kTileK for bf16; 8-bit weights pack 2 * kTileK)
+  template <int TK = kTileK>
+  KIE_HD int32_t stage_kt(int st) const { return stage_k(st) / TK; }
 };
 
 // Even split of n items over nwg workgroups: WG w owns [begin, end).
@@ -95,12 +97,13 @@ struct StageGeo {
   int32_t upb;      // units per batch (8 / ks)
   int32_t nu;       // units of the WG (np * S)
 };
+template <int TK = kTileK>
 KIE_HD StageGeo stage_geo(const Shape& s, int st, int32_t w) {
   StageGeo g;
   const int32_t n = s.stage_pairs(st);
   g.pb = split_begin(n, s.nwg, w);
   g.np = split_end(n, s.nwg, w) - g.pb;
-  g.kt = s.stage_kt(st);
+  g.kt = s.stage_kt<TK>(st);
   g.ks = unit_tiles(g.kt);
   g.S = g.kt / g.ks;
   g.upb = kBatch / g.ks;
@@ -111,16 +114,20 @@ KIE_HD StageGeo stage_geo(const Shape& s, int st, int32_t w) {
 KIE_HD int32_t wave_units(const StageGeo& g, int32_t v) { return g.nu > v ? (g.nu - v + kWaves - 1) / kWaves : 0; }
 KIE_HD int32_t wave_batches(const StageGeo& g, int32_t v) { return (wave_units(g, v) + g.upb - 1) / g.upb; }
 
-// Batches of one layer in the stream of (WG w, wave v), and of the LM head.
+// Batches of one layer in the stream of (WG w, wave v), and of the LM head. (TK: as stage_kt; a
+// tile is kTileBytes either way, 2 rows of TK weights.)
+template <int TK = kTileK>
 KIE_HD int32_t layer_batches(const Shape& s, int32_t w, int32_t v) {
   int32_t b = 0;
   for (int st = ST_QKV; st <= ST_DN; ++st)
-    if (s.in_stream(st)) b += wave_batches(stage_geo(s, st, w), v);
+    if (s.in_stream(st)) b += wave_batches(stage_geo<TK>(s, st, w), v);
   return b;
 }
-KIE_HD int32_t lm_batches(const Shape& s, int32_t w, int32_t v) { return wave_batches(stage_geo(s, ST_LM, w), v); }
+template <int TK = kTileK>
+KIE_HD int32_t lm_batches(const Shape& s, int32_t w, int32_t v) { return wave_batches(stage_geo<TK>(s, ST_LM, w), v); }
+template <int TK = kTileK>
 KIE_HD int64_t stream_tiles(const Shape& s, int32_t w, int32_t v) {
-  return ((int64_t)s.L * layer_batches(s, w, v) + lm_batches(s, w, v)) * kBatch;
+  return ((int64_t)s.L * layer_batches<TK>(s, w, v) + lm_batches<TK>(s, w, v)) * kBatch;
 }
 
 // Source rows of global pair gp of a stage. mat selects the matrix: for QKV 0 = Wq, 1 = Wk, 2 = Wv.
@@ -244,12 +251,12 @@ KIE_HD int32_t prefill_nmax(const Shape& s) {
 
 // Workspace (bytes, 256-aligned pieces): exchange words, RoPE table [max_seq][hd/2] of (cos,sin),
 // per-stream base (in tiles, [nwg][8] + total), error word, norm gains [L][2][d] + final [d] (bf16),
-// trace counters, and the prompt-pass scratch (residual [chunk][d] fp32, GEMM input [2][chunk][kmax]
+// trace counters, the prompt-pass scratch (residual [chunk][d] fp32, GEMM input [2][chunk][kmax]
 // bf16, down-projection input [2][chunk][F] bf16, split-K partial sums [chunk][nmax] fp32, queries
 // [chunk][nq hd] fp32, and for long contexts the per-segment attention states
-// [segments][chunk][nq][hd + 2] fp32).
+// [segments][chunk][nq][hd + 2] fp32), and the matrix scales of 8-bit weights [L][7] + [1] fp32.
 struct Workspace {
-  int64_t exch, rope, wbase, err, norms, trace, px, pa3, ph2, pc, pq, pattn, end;
+  int64_t exch, rope, wbase, err, norms, trace, px, pa3, ph2, pc, pq, pattn, wscale, end;
 };
 constexpr int kTraceWords = 32;  // per wave: cycle counters of a KIE_TRACE build
 KIE_HD int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
@@ -269,16 +276,18 @@ KIE_HD Workspace workspace_layout(const Shape& s) {
   w.pq = o; o = align256(o + (int64_t)kPrefillChunk * s.qdim() * 4);
   w.pattn = o;
   if (prefill_attn_segs(s) > 1) o = align256(o + (int64_t)prefill_attn_segs(s) * kPrefillChunk * s.nq * (s.hd + 2) * 4);
+  w.wscale = o; o = align256(o + ((int64_t)s.L * 7 + 1) * 4);  // 8-bit weights: the matrix scales
   w.end = o;
   return w;
 }
 
 // Packed image: the streams of (WG 0, wave 0), (WG 0, wave 1), ..., (WG nwg-1, wave 7), the
 // expert region (mixture of experts), then the embedding table [V][d] bf16 as is.
+template <int TK = kTileK>
 KIE_HD int64_t packed_stream_tiles(const Shape& s) {
   int64_t t = 0;
   for (int32_t w = 0; w < s.nwg; ++w)
-    for (int32_t v = 0; v < kWaves; ++v) t += stream_tiles(s, w, v);
+    for (int32_t v = 0; v < kWaves; ++v) t += stream_tiles<TK>(s, w, v);
   return t;
 }
 // Expert region, in tiles from its start: gate/up tiles [L][E][Fe pairs][d / 256] (pair p = row p
@@ -295,8 +304,9 @@ KIE_HD int64_t expert_dn_tile(const Shape& s, int32_t l, int32_t e, int32_t p, i
 }
 KIE_HD int64_t expert_tiles(const Shape& s) { return s.moe() ? 2 * expert_gu_tiles(s) : 0; }
 KIE_HD int64_t packed_expert_offset(const Shape& s) { return packed_stream_tiles(s) * kTileBytes; }
+template <int TK = kTileK>
 KIE_HD int64_t packed_embed_offset(const Shape& s) {
-  return (packed_stream_tiles(s) + expert_tiles(s)) * kTileBytes;
+  return (packed_stream_tiles<TK>(s) + expert_tiles(s)) * kTileBytes;
 }
 
 // Owner WG of global pair gp of a stage with n pairs (the inverse of the even split).
@@ -326,7 +336,8 @@ KIE_HD int64_t packed_tile(const Shape& s, const int64_t* wbase, int st, int32_t
   }
   return wbase[w * kWaves + v] + (bt + b) * kBatch + slot;
 }
-KIE_HD int64_t packed_bytes(const Shape& s) { return packed_embed_offset(s) + (int64_t)s.V * s.d * 2; }
+template <int TK = kTileK>
+KIE_HD int64_t packed_bytes(const Shape& s) { return packed_embed_offset<TK>(s) + (int64_t)s.V * s.d * 2; }
 
 // KV cache: [L][2][nkv][max_seq][hd] bf16 (K plane, then V plane, per layer).
 KIE_HD int64_t kv_offset(const Shape& s, int32_t l, int32_t kv, int32_t j, int32_t pos) {

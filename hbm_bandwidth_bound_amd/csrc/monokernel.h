@@ -45,10 +45,12 @@ struct KParams {
                              // every stage boundary (protocol stress; results must not change)
   uint32_t xb_lds;           // byte offset of the extra-batch LDS slots in the dynamic LDS
                              // (lds_slot_offset; used where the slot is read in assembly)
+  const float* wscale;       // 8-bit weights: [L][7] + [1] matrix scales (wq, wk, wv, wo, w_gate,
+                             // w_up, w_down; then the LM head), else null
 };
 
 typedef void (*KernelFn)(KParams);
-KernelFn decode_kernel_for(int group, int head_dim, bool prompt, bool moe);
+KernelFn decode_kernel_for(int group, int head_dim, bool prompt, bool moe, bool w8);
 int32_t lds_bytes_for(const Shape& s);
 int32_t lds_slot_offset(const Shape& s);  // where the extra-batch slots start in the dynamic LDS
 int32_t topk_capacity_floats(const Shape& s);  // WG-local floats available to the top-k merge
@@ -64,6 +66,7 @@ struct PackArgs {
   // mixture of experts (layer < L): router [E][d]; gate, up [E][Fe][d]; down [E][d][Fe]
   const uint16_t *wrouter, *egate, *eup, *edown;
   int64_t expert_offset;  // byte offset of the expert region in the packed image
+  int32_t w8;             // the layer matrices are one-byte codes (tiles of 2 * kTileK weights)
 };
 hipError_t launch_pack_layer(const PackArgs& a, hipStream_t st);
 hipError_t launch_pack_experts(const PackArgs& a, hipStream_t st);

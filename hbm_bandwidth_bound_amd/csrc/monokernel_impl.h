@@ -271,8 +271,10 @@ __device__ __forceinline__ int32_t count_greater(const uint64_t* kk, int32_t n, 
 // layers are mixture-of-experts layers, whose gate/up and down batches are read from the expert
 // region at the chosen experts' tiles (routed batches) instead of from the fixed stream.
 // ------------------------------------------------------------------------------------------
-template <bool MOE>
+template <bool MOE, bool W8 = false>
 struct Wk {
+  // W8: the layer matrices and the LM head are one-byte e4m3fn codes, 2 * kTileK of a row per tile
+  static constexpr int TK = W8 ? 2 * kTileK : kTileK;
   const KParams& P;
   const Lds& L;
   int32_t w, v, lane, tid;
@@ -306,7 +308,7 @@ struct Wk {
         nb[st] = 0;
         continue;
       }
-      g[st] = stage_geo(P.s, st, w);
+      g[st] = stage_geo<TK>(P.s, st, w);
       nb[st] = wave_batches(g[st], v);
       if (st <= ST_DN && (!MOE || P.s.in_stream(st))) layer_b += nb[st];
     }
@@ -405,6 +407,31 @@ struct Wk {
       f(b, make_rsrc(base, (okr || stat) ? kTileBytes : 0));
     }
   }
+  // Bytes of batch idx of a step's stream that hold weights. A wave's last batch of a stage can end
+  // in zero tiles (fewer units left than a batch holds); W8 streams do not read those (loads past
+  // the resource's end return zeros without touching memory), since at 8 bits the QKV and O
+  // stages of the 1.6B shape give each wave half a batch. bf16 streams read whole batches.
+  __device__ __forceinline__ uint32_t batch_bytes(int32_t idx) const {
+    if constexpr (!W8) {
+      return kBatch * kTileBytes;
+    } else {
+      int32_t r = idx, st = ST_LM;
+      const int32_t lb = P.s.L * layer_b;
+      if (r < lb) {
+        r = r % layer_b;
+        st = ST_QKV;
+        while (st < ST_DN && r >= nb_of(st)) {  // (the router stage of a dense layer has none)
+          r -= nb_of(st);
+          ++st;
+        }
+      } else {
+        r -= lb;
+      }
+      const StageGeo gs = geo_of(st);
+      const int32_t left = wave_units(gs, v) - r * gs.upb;
+      return (uint32_t)((left < gs.upb ? left : gs.upb) * gs.ks * kTileBytes);
+    }
+  }
   // 8 loads of batch (pidx, pstep); past the launch's last batch the resource is empty and the
   // loads return zeros without touching memory. MOE: a routed batch of a layer whose experts are
   // not chosen yet is left deferred.
@@ -412,7 +439,7 @@ struct Wk {
     const bool live = pstep < P.n_steps;
     if constexpr (!MOE) {
       const __amdgpu_buffer_rsrc_t rs =
-          make_rsrc(stream + (live ? (size_t)pidx * kBatch * kTileBytes : 0), live ? kBatch * kTileBytes : 0);
+          make_rsrc(stream + (live ? (size_t)pidx * kBatch * kTileBytes : 0), live ? batch_bytes(pidx) : 0);
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) buf[b] = load16(rs, (uint32_t)(lane * 16 + b * kTileBytes));
     } else {
@@ -500,7 +527,7 @@ struct Wk {
     advance();
     const bool live = pstep < P.n_steps;
     const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(stream + (live ? (size_t)pidx * kBatch * kTileBytes : 0), live ? kBatch * kTileBytes : 0);
+        make_rsrc(stream + (live ? (size_t)pidx * kBatch * kTileBytes : 0), live ? batch_bytes(pidx) : 0);
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) load16_lds(rs, (uint32_t)(lane * 16 + b * kTileBytes), base + b * kTileBytes);
     xpend = true;
@@ -615,8 +642,42 @@ struct Wk {
       const int32_t u = v + kWaves * (b * UPB + us);
       if (u < gs.nu) {
         const int32_t r = gs.S == 1 ? 0 : u % gs.S;
-        const float* xa = L.act + (size_t)r * KS * kTileK + lane * 4;
+        const float* xa = L.act + (size_t)r * KS * TK + lane * 4;
         float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+        if constexpr (W8) {
+          // lane's 16 B: row A's codes at k = 4 lane .. +3 and 256 + 4 lane .. +3 of the tile's 512,
+          // then row B's at the same k; each code widens exactly to fp32
+#pragma unroll
+          for (int t = 0; t < KS; ++t) {
+            const v4f x0 = *(const v4f*)(xa + t * TK);
+            const v4f x1 = *(const v4f*)(xa + t * TK + kTileK);
+            const v4u wt = cur[us * KS + t];
+            v2f p = __builtin_amdgcn_cvt_pk_f32_fp8((int)wt.x, false);
+            a0 = fmaf(p.x, x0.x, a0);
+            a1 = fmaf(p.y, x0.y, a1);
+            p = __builtin_amdgcn_cvt_pk_f32_fp8((int)wt.x, true);
+            a0 = fmaf(p.x, x0.z, a0);
+            a1 = fmaf(p.y, x0.w, a1);
+            p = __builtin_amdgcn_cvt_pk_f32_fp8((int)wt.y, false);
+            a0 = fmaf(p.x, x1.x, a0);
+            a1 = fmaf(p.y, x1.y, a1);
+            p = __builtin_amdgcn_cvt_pk_f32_fp8((int)wt.y, true);
+            a0 = fmaf(p.x, x1.z, a0);
+            a1 = fmaf(p.y, x1.w, a1);
+            p = __builtin_amdgcn_cvt_pk_f32_fp8((int)wt.z, false);
+            b0 = fmaf(p.x, x0.x, b0);
+            b1 = fmaf(p.y, x0.y, b1);
+            p = __builtin_amdgcn_cvt_pk_f32_fp8((int)wt.z, true);
+            b0 = fmaf(p.x, x0.z, b0);
+            b1 = fmaf(p.y, x0.w, b1);
+            p = __builtin_amdgcn_cvt_pk_f32_fp8((int)wt.w, false);
+            b0 = fmaf(p.x, x1.x, b0);
+            b1 = fmaf(p.y, x1.y, b1);
+            p = __builtin_amdgcn_cvt_pk_f32_fp8((int)wt.w, true);
+            b0 = fmaf(p.x, x1.z, b0);
+            b1 = fmaf(p.y, x1.w, b1);
+          }
+        } else {
 #pragma unroll
         for (int t = 0; t < KS; ++t) {
           const v4f x = *(const v4f*)(xa + t * kTileK);
@@ -629,6 +690,7 @@ struct Wk {
           b1 = fmaf(bf16hi(wt.z), x.y, b1);
           b0 = fmaf(bf16lo(wt.w), x.z, b0);
           b1 = fmaf(bf16hi(wt.w), x.w, b1);
+        }
         }
         const float ya = wave_sum(a0 + a1), yb = wave_sum(b0 + b1);
         if (lane == 0) {
@@ -1518,8 +1580,8 @@ __device__ __forceinline__ int32_t sample_topk(WK& K, const StageGeo& gl, uint64
 // MOE: after O the router stage runs, and its boundary (B_RT) chooses the layer's experts.
 enum Boundary : int { B_START = 0, B_QKV = 1, B_O = 2, B_GU = 3, B_DN = 4, B_LM = 5, B_END = 6, B_RT = 7 };
 
-template <int G, int HD, bool MOE>
-__device__ __forceinline__ void decode(Wk<MOE>& K) {
+template <int G, int HD, bool MOE, bool W8>
+__device__ __forceinline__ void decode(Wk<MOE, W8>& K) {
   const KParams& P = K.P;
   const Lds& L = K.L;
   const Shape& s = P.s;
@@ -1604,9 +1666,20 @@ __device__ __forceinline__ void decode(Wk<MOE>& K) {
           uint64_t* qx = ex + X.q + (int64_t)l * s.qdim();
           uint64_t* kx = ex + X.k + (int64_t)l * s.kvdim();
           uint64_t* vx = ex + X.v + (int64_t)l * s.kvdim();
+          float sq = 1.f, sk = 1.f, sv = 1.f;
+          if constexpr (W8) {
+            sq = P.wscale[l * 7];
+            sk = P.wscale[l * 7 + 1];
+            sv = P.wscale[l * 7 + 2];
+          }
           K.finalize(K.g[ST_QKV], [&](int32_t gp, float ya, float yb) {
             const int32_t half = s.hd / 2;
             const int32_t hs = gp / half, i = gp % half;
+            if constexpr (W8) {  // the matrix's scale times the codes' dot product
+              const float sc = hs < s.nq ? sq : (hs < s.nq + s.nkv ? sk : sv);
+              ya *= sc;
+              yb *= sc;
+            }
             if (hs < s.nq + s.nkv) {  // query and key heads are rotated
               const float2 cs = L.rope[i];
               const float ra = ya * cs.x - yb * cs.y, rb = yb * cs.x + ya * cs.y;
@@ -1654,7 +1727,12 @@ __device__ __forceinline__ void decode(Wk<MOE>& K) {
           bar();
           uint64_t* xa = ex + X.xa + (int64_t)l * s.d;
           K.prefetch_gain(P.norms + (int64_t)l * 2 * s.d + s.d);
+          const float so = W8 ? P.wscale[l * 7 + 3] : 1.f;
           K.finalize(K.g[ST_O], [&](int32_t gp, float ya, float yb) {
+            if constexpr (W8) {
+              ya *= so;
+              yb *= so;
+            }
             st_x(xa + 2 * gp, tag_f(xres[2 * gp] + ya, ep));
             st_x(xa + 2 * gp + 1, tag_f(xres[2 * gp + 1] + yb, ep));
           });
@@ -1669,7 +1747,12 @@ __device__ __forceinline__ void decode(Wk<MOE>& K) {
         case B_GU: {  // SwiGLU outputs -> gather h
           bar();
           uint64_t* hx = ex + X.h + (int64_t)l * s.F;
+          const float sg = W8 ? P.wscale[l * 7 + 4] : 1.f, su = W8 ? P.wscale[l * 7 + 5] : 1.f;
           K.finalize(K.g[ST_GU], [&](int32_t gp, float ya, float yb) {
+            if constexpr (W8) {
+              ya *= sg;
+              yb *= su;
+            }
             float h = (ya / (1.0f + expf(-ya))) * yb;
             if constexpr (MOE) h = K.weight_of(gp / s.Fe) * h;  // the routing weight of its expert
             st_x(hx + gp, tag_f(h, ep));
@@ -1691,7 +1774,12 @@ __device__ __forceinline__ void decode(Wk<MOE>& K) {
           dphase(24);
           uint64_t* xf = ex + X.xf + (int64_t)(l + 1) * s.d;
           K.prefetch_gain(P.norms + (l + 1 < s.L ? (int64_t)(l + 1) * 2 * s.d : (int64_t)s.L * 2 * s.d));
+          const float sd = W8 ? P.wscale[l * 7 + 6] : 1.f;
           K.finalize(K.g[ST_DN], [&](int32_t gp, float ya, float yb) {
+            if constexpr (W8) {
+              ya *= sd;
+              yb *= sd;
+            }
             st_x(xf + 2 * gp, tag_f(xres[2 * gp] + ya, ep));
             st_x(xf + 2 * gp + 1, tag_f(xres[2 * gp + 1] + yb, ep));
           });
@@ -1737,8 +1825,13 @@ __device__ __forceinline__ void decode(Wk<MOE>& K) {
             bar();
             float* lo = P.logits_out ? P.logits_out + (P.lm_last_only ? 0 : (int64_t)step * s.V) : nullptr;
             const int32_t pb = K.g[ST_LM].pb;
+            const float sl = W8 ? P.wscale[s.L * 7] : 1.f;
             K.finalize(K.g[ST_LM], [&](int32_t gp, float ya, float yb) {
               const int32_t ra = 2 * gp, rb = 2 * gp + 1;
+              if constexpr (W8) {
+                ya *= sl;
+                yb *= sl;
+              }
               if (better(ya, ra, bv, bi)) {
                 bv = ya;
                 bi = ra;
@@ -1862,30 +1955,39 @@ __device__ __forceinline__ void decode(Wk<MOE>& K) {
 // The kernels. The prompt pass (teacher-forced steps whose only output is the last logits and
 // the first token) runs the same program under its own symbol, so that profiles separate it
 // from decoding.
-#define KIE_KERNEL_BODY(G, HD, MOE)                                         \
+#define KIE_KERNEL_BODY(G, HD, MOE, W8)                                     \
   const Lds L = lds_map<G>(kie_smem, P.s);                                 \
   if (threadIdx.x < C_COUNT) L.ctl[threadIdx.x] = 0;                       \
   __syncthreads();                                                         \
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);    \
-  Wk<MOE> K(P, L, blockIdx.x, wave, threadIdx.x % kWave);                  \
-  decode<G, HD, MOE>(K);
+  Wk<MOE, W8> K(P, L, blockIdx.x, wave, threadIdx.x % kWave);              \
+  decode<G, HD, MOE, W8>(K);
 
 template <int G, int HD>
 __global__ void __launch_bounds__(kThreads, 1) kie_decode_kernel(KParams P) {
-  KIE_KERNEL_BODY(G, HD, false)
+  KIE_KERNEL_BODY(G, HD, false, false)
 }
 template <int G, int HD>
 __global__ void __launch_bounds__(kThreads, 1) kie_prompt_kernel(KParams P) {
-  KIE_KERNEL_BODY(G, HD, false)
+  KIE_KERNEL_BODY(G, HD, false, false)
 }
 // Mixture-of-experts layers (the same program with the router stage and routed expert batches)
 template <int G, int HD>
 __global__ void __launch_bounds__(kThreads, 1) kie_moe_decode_kernel(KParams P) {
-  KIE_KERNEL_BODY(G, HD, true)
+  KIE_KERNEL_BODY(G, HD, true, false)
 }
 template <int G, int HD>
 __global__ void __launch_bounds__(kThreads, 1) kie_moe_prompt_kernel(KParams P) {
-  KIE_KERNEL_BODY(G, HD, true)
+  KIE_KERNEL_BODY(G, HD, true, false)
+}
+// 8-bit (e4m3fn) layer matrices and LM head with one scale per matrix
+template <int G, int HD>
+__global__ void __launch_bounds__(kThreads, 1) kie_fp8_decode_kernel(KParams P) {
+  KIE_KERNEL_BODY(G, HD, false, true)
+}
+template <int G, int HD>
+__global__ void __launch_bounds__(kThreads, 1) kie_fp8_prompt_kernel(KParams P) {
+  KIE_KERNEL_BODY(G, HD, false, true)
 }
 
 }  // namespace kie

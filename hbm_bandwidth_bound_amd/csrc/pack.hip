@@ -12,8 +12,11 @@ namespace kie {
 
 // One block row per stream (WG w = x / 8, wave v = x % 8); it writes the stream's tiles of one
 // layer (or of the LM head). Each thread writes one lane (16 B) of a tile: 8 B of row A and 8 B of
-// row B at the same k. Slots of missing units are written as zeros.
+// row B at the same k (4 bf16 weights each; with TK = 2 * kTileK, 8 one-byte codes: 4 from each
+// half of the tile's 512). Slots of missing units are written as zeros.
+template <int TK>
 __global__ void __launch_bounds__(256) pack_layer_kernel(PackArgs a) {
+  constexpr int EB = 2 * kTileK / TK;  // bytes per weight
   const Shape& s = a.s;
   const int32_t w = blockIdx.x / kWaves, v = blockIdx.x % kWaves;
   const bool lm = a.layer == s.L;
@@ -21,11 +24,11 @@ __global__ void __launch_bounds__(256) pack_layer_kernel(PackArgs a) {
   int32_t acc = 0;
   for (int st = ST_QKV; st <= ST_DN; ++st) {
     boff[st] = acc;
-    if (s.in_stream(st)) acc += wave_batches(stage_geo(s, st, w), v);
+    if (s.in_stream(st)) acc += wave_batches(stage_geo<TK>(s, st, w), v);
   }
   boff[ST_LM] = acc;
   const int32_t layer_b = acc;
-  const int32_t nb = lm ? lm_batches(s, w, v) : layer_b;
+  const int32_t nb = lm ? lm_batches<TK>(s, w, v) : layer_b;
   const int64_t base = a.wbase[blockIdx.x] + (int64_t)a.layer * layer_b * kBatch;
   const int q = threadIdx.x % 64;
   for (int32_t t = blockIdx.y * 4 + threadIdx.x / 64; t < nb * kBatch; t += gridDim.y * 4) {
@@ -36,7 +39,7 @@ __global__ void __launch_bounds__(256) pack_layer_kernel(PackArgs a) {
       while (st < ST_DN && b >= boff[st + 1]) ++st;
       b -= boff[st];
     }
-    const StageGeo g = stage_geo(s, st, w);
+    const StageGeo g = stage_geo<TK>(s, st, w);
     const int32_t sl = t % kBatch, us = sl / g.ks, tt = sl % g.ks;
     const int32_t u = v + kWaves * (b * g.upb + us);
     v4u out = v4u{0u, 0u, 0u, 0u};
@@ -61,17 +64,27 @@ __global__ void __launch_bounds__(256) pack_layer_kernel(PackArgs a) {
         ma = mb = a.lm_head;
       }
       const int32_t K = s.stage_k(st);
-      const int32_t k = j * kTileK + q * 4;
-      const uint2 xa = *(const uint2*)(ma + (int64_t)ra * K + k);
-      const uint2 xb = *(const uint2*)(mb + (int64_t)rb * K + k);
-      out = v4u{xa.x, xa.y, xb.x, xb.y};
+      if constexpr (EB == 2) {  // bf16: k = 4q .. 4q + 3 of the tile's 256
+        const int32_t k = j * TK + q * 4;
+        const uint2 xa = *(const uint2*)(ma + (int64_t)ra * K + k);
+        const uint2 xb = *(const uint2*)(mb + (int64_t)rb * K + k);
+        out = v4u{xa.x, xa.y, xb.x, xb.y};
+      } else {  // 8-bit: k = 4q .. 4q + 3 and 256 + 4q .. + 3 of the tile's 512 (one word each)
+        const uint8_t* pa = (const uint8_t*)ma + (int64_t)ra * K + j * TK + q * 4;
+        const uint8_t* pb = (const uint8_t*)mb + (int64_t)rb * K + j * TK + q * 4;
+        out = v4u{*(const uint32_t*)pa, *(const uint32_t*)(pa + kTileK), *(const uint32_t*)pb,
+                  *(const uint32_t*)(pb + kTileK)};
+      }
     }
     *(v4u*)(a.packed + (base + t) * kTileBytes + q * 16) = out;
   }
 }
 
 hipError_t launch_pack_layer(const PackArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(pack_layer_kernel, dim3(a.s.nwg * kWaves, 16), dim3(256), 0, st, a);
+  if (a.w8)
+    hipLaunchKernelGGL(pack_layer_kernel<2 * kTileK>, dim3(a.s.nwg * kWaves, 16), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(pack_layer_kernel<kTileK>, dim3(a.s.nwg * kWaves, 16), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -29,7 +29,7 @@ class kie_config(C.Structure):
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn_dim", C.c_int32),
                 ("vocab_size", C.c_int32), ("rms_eps", C.c_float), ("rope_theta", C.c_float),
                 ("max_seq_len", C.c_int32), ("n_experts", C.c_int32), ("n_experts_active", C.c_int32),
-                ("expert_ffn_dim", C.c_int32)]
+                ("expert_ffn_dim", C.c_int32), ("weight_format", C.c_int32)]
 
 
 _U16P = C.POINTER(C.c_uint16)
@@ -40,7 +40,8 @@ class kie_weights(C.Structure):
     _fields_ = [("embed", _U16P), ("final_norm", _U16P), ("lm_head", _U16P), ("attn_norm", _U16PP),
                 ("wq", _U16PP), ("wk", _U16PP), ("wv", _U16PP), ("wo", _U16PP), ("ffn_norm", _U16PP),
                 ("w_gate", _U16PP), ("w_up", _U16PP), ("w_down", _U16PP), ("w_router", _U16PP),
-                ("moe_gate", _U16PP), ("moe_up", _U16PP), ("moe_down", _U16PP)]
+                ("moe_gate", _U16PP), ("moe_up", _U16PP), ("moe_down", _U16PP),
+                ("weight_scales", C.POINTER(C.c_float))]
 
 _LAYER_KEYS = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down", "w_router", "moe_gate",
                "moe_up", "moe_down")
@@ -109,7 +110,8 @@ def load() -> C.CDLL:
 def make_config(model, max_seq: int) -> kie_config:
     return kie_config(model.n_layers, model.d_model, model.n_heads, model.n_kv_heads, model.head_dim,
                       model.ffn_dim, model.vocab_size, model.rms_eps, model.rope_theta, int(max_seq),
-                      model.n_experts, model.n_experts_active, model.expert_ffn_dim)
+                      model.n_experts, model.n_experts_active, model.expert_ffn_dim,
+                      int(getattr(model, "weight_format", 0)))
 
 
 def _ptr(t) -> C.c_void_p:
@@ -131,7 +133,9 @@ class Engine:
 
     weights: dict of torch int16/uint16-bit tensors on the device (keys as in kie_weights; per-layer
     keys hold lists; a dense model has no w_router/moe_* keys, a mixture-of-experts model no
-    w_gate/w_up/w_down). The packed image, KV cache and workspace are allocated here as torch
+    w_gate/w_up/w_down). An 8-bit model (``model.weight_format == 1``) has uint8 code tensors for
+    wq, wk, wv, wo, w_gate, w_up, w_down and lm_head, and ``weights["w_scale"]``: the
+    n_layers * 7 + 1 fp32 matrix scales as a host array. The packed image, KV cache and workspace are allocated here as torch
     tensors.
     """
 
@@ -171,8 +175,15 @@ class Engine:
                 fields[k] = ptrs
             else:
                 fields[k] = C.cast(None, _U16PP)
+        if "w_scale" in weights:
+            import numpy as np
+            sc = np.ascontiguousarray(weights["w_scale"], dtype=np.float32)
+            keep.append(sc)
+            scp = sc.ctypes.data_as(C.POINTER(C.c_float))
+        else:
+            scp = C.cast(None, C.POINTER(C.c_float))
         self._w = kie_weights(p(weights["embed"]), p(weights["final_norm"]), p(weights["lm_head"]),
-                              *[fields[k] for k in _LAYER_KEYS])
+                              *[fields[k] for k in _LAYER_KEYS], scp)
         self._keep = keep
         ctx = C.c_void_p()
         st = lib.kie_create(C.byref(self.cfg), C.byref(self._w), _ptr(self.packed), _ptr(self.kv),

@@ -1,6 +1,7 @@
 """Algorithmic bytes of the decode path (what one step must move), used for the roofline.
 
-One decode step at position p reads every layer matrix and the LM head once (bf16), the norm
+One decode step at position p reads every layer matrix and the LM head once (bf16, or 8-bit codes
+and their scales), the norm
 gains, one embedding row, the K and V rows of positions 0..p of every layer and KV head, and
 writes the K and V rows of position p. In a mixture-of-experts layer the matrices read are the
 attention's, the router's and those of the routed experts only. This is the pages' bytes-per-token model (aikraft.ru
@@ -10,17 +11,26 @@ added, since the pages' bound leaves KV traffic out.
 from __future__ import annotations
 
 
-def weight_bytes(m) -> int:
-    """Weight bytes one step reads. A mixture-of-experts layer reads its router and only the
-    routed experts (n_experts_active of them)."""
+def matrix_weights(m) -> int:
+    """Weights of the layer matrices and the LM head one step reads. A mixture-of-experts layer
+    reads its router and only the routed experts (n_experts_active of them)."""
     d, q, kv, f, V, L = m.d_model, m.n_heads * m.head_dim, m.n_kv_heads * m.head_dim, m.ffn_dim, m.vocab_size, m.n_layers
     if m.n_experts:
         ffn = m.n_experts * d + m.n_experts_active * 3 * m.expert_ffn_dim * d
     else:
         ffn = 3 * f * d
-    per_layer_matrices = q * d + 2 * kv * d + d * q + ffn
-    norms = (2 * L + 1) * d
-    return 2 * (L * per_layer_matrices + V * d + norms + d)  # + one embedding row
+    return L * (q * d + 2 * kv * d + d * q + ffn) + V * d
+
+
+def weight_bytes(m) -> int:
+    """Weight bytes one step reads: the matrices (2 bytes a weight, or 1 with 8-bit weights plus
+    their fp32 scales), the bf16 norm gains and one bf16 embedding row."""
+    d, L = m.d_model, m.n_layers
+    if getattr(m, "weight_format", 0) == 1:
+        mats = matrix_weights(m) + 4 * (7 * L + 1)
+    else:
+        mats = 2 * matrix_weights(m)
+    return mats + 2 * ((2 * L + 1) * d + d)
 
 
 def kv_row_bytes(m) -> int:
@@ -43,5 +53,5 @@ def launch_bytes(m, pos0: int, n_steps: int) -> int:
 
 def step_flops(m, pos: int) -> int:
     """Multiply-adds x 2 of one step: every weight once, plus QK and PV over pos+1 positions."""
-    macs = (weight_bytes(m) // 2) + 2 * m.n_layers * m.n_heads * m.head_dim * (pos + 1)
+    macs = matrix_weights(m) + 2 * m.n_layers * m.n_heads * m.head_dim * (pos + 1)
     return 2 * macs

@@ -57,12 +57,27 @@ enum {
  * block of width expert_ffn_dim, and their outputs are summed with the weights
  * softmax(logits) restricted to the chosen and renormalised to sum to 1. Then ffn_dim must be 0,
  * n_experts even and at most 512, 1 <= n_experts_active <= min(8, n_experts), expert_ffn_dim a
- * multiple of 256, and (kernel instantiation) n_heads / n_kv_heads == 8 with head_dim 128. */
+ * multiple of 256, and (kernel instantiation) n_heads / n_kv_heads == 8 with head_dim 128.
+ * weight_format: KIE_WEIGHTS_BF16 (0), or KIE_WEIGHTS_FP8_E4M3 (1): the seven matrices of every
+ * layer and the LM head are 8-bit codes, which halves the bytes read per token (the pages: 8-bit
+ * weights halve the bytes and so about double a bandwidth-bound decoder's ceiling, at a cost in
+ * accuracy -- aikraft.ru «3000 токенов в секунду…», §02; wink.run, 《GPU 算力越堆越高,生成 token
+ * 为什么还是慢》, on what optimisations change; the engine they describe itself does not quantize,
+ * zdabc.icu, 《Kog 推理引擎…》). The pages fix no 8-bit format; this one is the OCP E4M3 encoding
+ * (e4m3fn: bias 7, subnormals, no infinities, 0x7F and 0xFF are NaN) with one fp32 scale per matrix
+ * (kie_weights.weight_scales): a matrix is its scale times its decoded codes, and each output of
+ * a product is the scale times the fp32 sum of code x activation products. Embedding, norm gains
+ * and the KV cache stay bf16. Then d_model, n_heads*head_dim and ffn_dim must be multiples of 512,
+ * n_experts must be 0, and (kernel instantiation) n_heads / n_kv_heads is 2 with head_dim 64 or
+ * 128, or 4 with head_dim 128. A prompt of an 8-bit model runs through the decode program one
+ * position after the other (see kie_prefill). */
+enum { KIE_WEIGHTS_BF16 = 0, KIE_WEIGHTS_FP8_E4M3 = 1 };
 typedef struct {
   int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab_size;
   float rms_eps, rope_theta;
   int32_t max_seq_len; /* KV capacity in positions: prompt + generated tokens */
   int32_t n_experts, n_experts_active, expert_ffn_dim;
+  int32_t weight_format; /* KIE_WEIGHTS_BF16 or KIE_WEIGHTS_FP8_E4M3 */
 } kie_config;
 
 /* Source weights: device pointers to row-major [out][in] bf16 matrices, borrowed only until the
@@ -73,12 +88,18 @@ typedef struct {
  *   wo[l] [d][n_heads*hd], ffn_norm[l] [d], w_gate[l] and w_up[l] [F][d], w_down[l] [d][F].
  * Mixture of experts (E experts of width Fe; w_gate, w_up, w_down are then unused and may be NULL):
  *   w_router[l] [E][d], moe_gate[l] and moe_up[l] [E][Fe][d] (experts stacked), moe_down[l]
- *   [E][d][Fe]. For a dense model these four may be NULL. */
+ *   [E][d][Fe]. For a dense model these four may be NULL.
+ * KIE_WEIGHTS_FP8_E4M3: wq, wk, wv, wo, w_gate, w_up, w_down and lm_head point at one-byte codes
+ * in the same [out][in] layouts (read through the uint16_t pointer type as bytes; still 16-byte
+ * aligned), and weight_scales is a HOST array of n_layers * 7 + 1 finite floats: per layer the
+ * scales of wq, wk, wv, wo, w_gate, w_up, w_down, then the LM head's. It is copied during
+ * kie_create (a blocking copy) and may be freed when kie_create returns. NULL for bf16. */
 typedef struct {
   const uint16_t *embed, *final_norm, *lm_head;
   const uint16_t *const *attn_norm, *const *wq, *const *wk, *const *wv, *const *wo;
   const uint16_t *const *ffn_norm, *const *w_gate, *const *w_up, *const *w_down;
   const uint16_t *const *w_router, *const *moe_gate, *const *moe_up, *const *moe_down;
+  const float* weight_scales;
 } kie_weights;
 
 /* Token choice after each step, made on the GPU (aikraft.ru «3000 токенов в секунду…», §04:
@@ -116,8 +137,9 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
  * writing their K/V rows, then choose the next token (device int32 [1], first_token_dev) from the
  * logits of the last prompt position; those logits are written to last_logits_dev (device fp32
  * [V]) unless it is NULL. Advances the position by n_tokens. A dense model runs all but the last
- * position as matrix-core GEMMs; a mixture-of-experts model runs every position, one after the
- * other, through the decode program in one launch (each position routes its own experts).
+ * position as matrix-core GEMMs; a mixture-of-experts model (each position routes its own
+ * experts) and an 8-bit model run every position, one after the other, through the decode program
+ * in one launch.
  * Errors: KIE_ERR_INVALID_ARG, KIE_ERR_CAPACITY, KIE_ERR_STATE, KIE_ERR_HIP. */
 kie_status kie_prefill(kie_ctx* ctx, const int32_t* tokens_dev, int32_t n_tokens, int32_t* first_token_dev,
                        float* last_logits_dev, const kie_sampling* sampling);

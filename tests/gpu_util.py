@@ -17,9 +17,12 @@ def to_device(w_np, device="cuda"):
     import torch
 
     def cv(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device)
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a if a.dtype == np.uint8 else a.view(np.int16)).to(device)
 
-    return {k: ([cv(x) for x in v] if isinstance(v, list) else cv(v)) for k, v in w_np.items()}
+    # the 8-bit models' matrix scales stay a host array
+    return {k: (v if k == "w_scale" else [cv(x) for x in v] if isinstance(v, list) else cv(v))
+            for k, v in w_np.items()}
 
 
 def rel_l2(a, b) -> float:

@@ -5,18 +5,20 @@
 // violation.
 #include <cstdio>
 #include <cstdlib>
+#include <string>
 #include <vector>
 
 #include "layout.h"
 
 using namespace kie;
 
+template <int TK>
 static int check(const Shape& s) {
   int64_t total = 0;
   for (int32_t w = 0; w < s.nwg; ++w) {
     for (int st = ST_QKV; st < ST_COUNT; ++st) {
-      const StageGeo g = stage_geo(s, st, w);
-      if (g.ks * g.S != g.kt || g.upb * g.ks != kBatch) {
+      const StageGeo g = stage_geo<TK>(s, st, w);
+      if (g.ks * g.S != g.kt || g.upb * g.ks != kBatch || g.kt * TK != s.stage_k(st)) {
         std::printf("bad unit geometry w=%d st=%d\n", w, st);
         return 1;
       }
@@ -48,15 +50,15 @@ static int check(const Shape& s) {
           return 1;
         }
     }
-    for (int32_t v = 0; v < kWaves; ++v) total += stream_tiles(s, w, v);
+    for (int32_t v = 0; v < kWaves; ++v) total += stream_tiles<TK>(s, w, v);
   }
-  if (total != packed_stream_tiles(s)) {
+  if (total != packed_stream_tiles<TK>(s)) {
     std::printf("stream total mismatch\n");
     return 1;
   }
   for (int st = ST_QKV; st < ST_COUNT; ++st) {
     int64_t np = 0;
-    for (int32_t w = 0; w < s.nwg; ++w) np += stage_geo(s, st, w).np;
+    for (int32_t w = 0; w < s.nwg; ++w) np += stage_geo<TK>(s, st, w).np;
     if (np != s.stage_pairs(st)) {
       std::printf("pairs of stage %d do not add up\n", st);
       return 1;
@@ -68,23 +70,24 @@ static int check(const Shape& s) {
   for (int32_t w = 0; w < s.nwg; ++w)
     for (int32_t v = 0; v < kWaves; ++v) {
       wbase[(size_t)w * kWaves + v] = acc;
-      acc += stream_tiles(s, w, v);
+      acc += stream_tiles<TK>(s, w, v);
     }
   const int32_t layers[3] = {0, s.L - 1, s.L};  // first layer, last layer, LM head
   for (int li = 0; li < 3; ++li) {
     const int32_t l = layers[li];
     for (int32_t w = 0; w < s.nwg; ++w)
       for (int32_t v = 0; v < kWaves; ++v) {
-        int64_t t0 = wbase[(size_t)w * kWaves + v] + (int64_t)l * layer_batches(s, w, v) * kBatch;
+        int64_t t0 = wbase[(size_t)w * kWaves + v] + (int64_t)l * layer_batches<TK>(s, w, v) * kBatch;
         for (int st = (l == s.L ? ST_LM : ST_QKV); st <= (l == s.L ? ST_LM : ST_DN); ++st) {
           if (!s.in_stream(st)) continue;
-          const StageGeo g = stage_geo(s, st, w);
+          const StageGeo g = stage_geo<TK>(s, st, w);
           const int32_t nbv = wave_batches(g, v);
           for (int32_t b = 0; b < nbv; ++b)
             for (int32_t sl = 0; sl < kBatch; ++sl) {
               const int32_t u = v + kWaves * (b * g.upb + sl / g.ks);
               if (u >= g.nu) continue;
               const int32_t gp = g.pb + u / g.S, kt = (u % g.S) * g.ks + sl % g.ks;
+              if (TK != kTileK) continue;  // packed_tile serves the bf16 prompt pass only
               const int64_t got = packed_tile(s, wbase.data(), st, l, gp, kt);
               if (got != t0 + (int64_t)b * kBatch + sl) {
                 std::printf("packed_tile mismatch l=%d st=%d gp=%d kt=%d: %lld vs %lld\n", l, st, gp, kt, (long long)got,
@@ -118,7 +121,7 @@ static int check(const Shape& s) {
             }
           }
       }
-    if (packed_embed_offset(s) != (packed_stream_tiles(s) + n) * kTileBytes) {
+    if (packed_embed_offset<TK>(s) != (packed_stream_tiles<TK>(s) + n) * kTileBytes) {
       std::printf("embedding offset does not follow the expert region\n");
       return 1;
     }
@@ -128,8 +131,11 @@ static int check(const Shape& s) {
 }
 
 int main(int argc, char** argv) {
+  // a trailing "fp8": the geometry of 8-bit weights (2 * kTileK weights of a row per tile)
+  const bool w8 = argc > 1 && std::string(argv[argc - 1]) == "fp8";
+  if (w8) --argc;
   if (argc != 10 && argc != 13) {
-    std::printf("usage: L d nq nkv hd F V max_seq nwg [E A Fe]\n");
+    std::printf("usage: L d nq nkv hd F V max_seq nwg [E A Fe] [fp8]\n");
     return 2;
   }
   Shape s;
@@ -151,5 +157,5 @@ int main(int argc, char** argv) {
   s.eps = 1e-5f;
   s.theta = 10000.f;
   if (s.moe()) s.F = s.A * s.Fe;
-  return check(s);
+  return w8 ? check<2 * kTileK>(s) : check<kTileK>(s);
 }

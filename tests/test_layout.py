@@ -30,6 +30,11 @@ SHAPES = [
     (2, 512, 8, 1, 128, 0, 4096, 64, 256, 32, 8, 768),          # small-moe: down units span experts
     (2, 2048, 32, 4, 128, 0, 151936, 64, 256, 128, 8, 768),     # the 128-expert model's layers
     (1, 768, 8, 1, 128, 0, 1000, 64, 40, 6, 3, 512),            # ragged: 3-tile rows, 40 CUs
+    # 8-bit weights: tiles of 512 weights of a row
+    (2, 512, 8, 4, 64, 1536, 4096, 64, 256, "fp8"),             # tiny-fp8: 1- and 3-tile rows
+    (24, 2048, 16, 8, 128, 8192, 32768, 64, 256, "fp8"),        # 1.6B
+    (32, 4096, 32, 8, 128, 14336, 128256, 64, 256, "fp8"),      # 8B: 28-tile FFN rows
+    (1, 1536, 12, 4, 128, 2560, 1002, 64, 40, "fp8"),           # 3-tile and 5-tile rows, 40 CUs
 ]
 
 
