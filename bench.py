@@ -251,7 +251,7 @@ def main():
         cpu = cpu_baseline(m, wdev, P, args.cpu_seconds)
 
     metric = HEADLINE_METRIC if args.workload == "1.6b-1k" else \
-        f"batch-1 decode tok/s, {wl.name} bf16; achieved HBM GB/s vs peak"
+        f"batch-1 decode tok/s, {wl.name} {'fp8-e4m3 weights' if m.weight_format else 'bf16'}; achieved HBM GB/s vs peak"
     res = {
         "metric": metric,
         "value": round(tok_s, 2),

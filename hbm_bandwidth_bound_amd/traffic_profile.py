@@ -35,11 +35,14 @@ if ROOT not in sys.path:
 
 DECODE_KERNEL = "kie_decode_kernel"          # dense layers
 MOE_DECODE_KERNEL = "kie_moe_decode_kernel"  # mixture-of-experts layers
+FP8_DECODE_KERNEL = "kie_fp8_decode_kernel"  # 8-bit weights
 COPY_KERNEL = "stream_copy_kernel"
 
 
 def decode_kernel(model) -> str:
-    return MOE_DECODE_KERNEL if model.n_experts else DECODE_KERNEL
+    if model.n_experts:
+        return MOE_DECODE_KERNEL
+    return FP8_DECODE_KERNEL if getattr(model, "weight_format", 0) else DECODE_KERNEL
 
 
 def run(args):
