@@ -128,12 +128,14 @@ def summarize(args):
         f.write(f"# HBM traffic of one {decode_kernel(wl.model)} dispatch ({wl.name}: prompt {wl.prompt_len}, "
                 f"{K} decode steps in one launch)\n")
         f.write("# commands (from the repository root, each pass its own run):\n")
+        filt = f"--kernel-include-regex '{args.kernel_regex}' " if args.kernel_regex else ""
         for c, d in (("FETCH_SIZE", args.fetch), ("WRITE_SIZE", args.write)):
-            f.write(f"#   rocprofv3 --pmc {c} --output-format csv -d {d} -o run -- python3 -m "
+            f.write(f"#   rocprofv3 --pmc {c} {filt}--output-format csv -d {d} -o run -- python3 -m "
                     f"hbm_bandwidth_bound_amd.traffic_profile run --workload {wl.name} --steps {K} "
                     f"--copy-mib {args.copy_mib}\n")
         f.write(f"#   python3 -m hbm_bandwidth_bound_amd.traffic_profile summarize --workload {wl.name} "
-                f"--steps {K} --copy-mib {args.copy_mib} --fetch {args.fetch} --write {args.write} --out {args.out}\n")
+                f"--steps {K} --copy-mib {args.copy_mib} --fetch {args.fetch} --write {args.write} --out {args.out}"
+                + (f" --kernel-regex '{args.kernel_regex}'" if args.kernel_regex else "") + "\n")
         for ln in lines:
             f.write(ln + "\n")
         f.write(f"source_sha = {source_hash()}\n")
@@ -158,6 +160,8 @@ def main():
             p.add_argument("--fetch", required=True)
             p.add_argument("--write", required=True)
             p.add_argument("--out", required=True)
+            p.add_argument("--kernel-regex", default=None,
+                           help="the --kernel-include-regex the counter passes ran with (recorded only)")
     args = ap.parse_args()
     (run if args.cmd == "run" else summarize)(args)
 
