@@ -21,6 +21,8 @@ hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, in
 
 using namespace kie;
 
+static const int64_t kDefaultTimeoutTicks = 200000000;  // 2 s per wait (s_memrealtime runs at 100 MHz)
+
 struct kie_ctx {
   Shape s;
   Exch exo;
@@ -42,6 +44,8 @@ struct kie_ctx {
   int64_t ring_count;      // tokens streamed to it so far
   int64_t timeout_ticks;
   uint32_t skew;           // kie_set_skew
+  int32_t* abort_dev;      // device view of the caller's host abort word, or null
+  std::vector<float> wscale_host;  // 8-bit weights: the matrix scales, copied from the caller
   std::vector<int64_t> wbase_host;
   std::string last_error;
 };
@@ -242,6 +246,7 @@ const char* kie_status_string(kie_status status) {
 const char* kie_last_error(const kie_ctx* ctx) { return ctx ? ctx->last_error.c_str() : g_create_error.c_str(); }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+static bool aligned256(const void* p) { return ((uintptr_t)p & 255u) == 0; }
 
 kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packed, void* kv_cache, void* workspace,
                       void* hip_stream, kie_ctx** out) {
@@ -250,6 +255,14 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
   std::string* err = &g_create_error;
   if (!out || !src || !packed || !kv_cache || !workspace) {
     set_err(err, "NULL argument");
+    return KIE_ERR_INVALID_ARG;
+  }
+  // Checked before anything touches the device. The KV cache and the workspace start on a
+  // 256-byte boundary, so that every cache row (128 or 256 bytes) and every workspace piece owns
+  // whole cache lines: a row appended by one workgroup is never in a line another workgroup
+  // read earlier in the same launch.
+  if (!aligned16(packed) || !aligned256(kv_cache) || !aligned256(workspace)) {
+    set_err(err, "packed must be 16-byte aligned, kv_cache and workspace 256-byte aligned");
     return KIE_ERR_INVALID_ARG;
   }
   Shape s;
@@ -290,9 +303,8 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
       }
     }
   }
-  if (!aligned16(src->embed) || !aligned16(src->lm_head) || !aligned16(packed) || !aligned16(kv_cache) ||
-      !aligned16(workspace)) {
-    set_err(err, "device buffers must be 16-byte aligned");
+  if (!aligned16(src->embed) || !aligned16(src->lm_head)) {
+    set_err(err, "embed and lm_head must be 16-byte aligned");
     return KIE_ERR_INVALID_ARG;
   }
   int dev = 0;
@@ -348,8 +360,10 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
   c->tok_ring = nullptr;
   c->ring_cap = 0;
   c->ring_count = 0;
-  c->timeout_ticks = 200000000;  // 2 s per wait
+  c->timeout_ticks = kDefaultTimeoutTicks;
   c->skew = 0;
+  c->abort_dev = nullptr;
+  if (w8) c->wscale_host.assign(src->weight_scales, src->weight_scales + (size_t)L * 7 + 1);
   c->wbase_host.resize((size_t)s.nwg * kWaves + 1);
   int64_t acc = 0;
   for (int w = 0; w < s.nwg; ++w) {
@@ -386,9 +400,10 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
   if ((e = hipMemcpyAsync(norms + (size_t)L * 2 * s.d, src->final_norm, (size_t)s.d * 2, hipMemcpyDeviceToDevice,
                           stm)) != hipSuccess)
     return fail("copy norms", e);
-  // 8-bit weights: the matrix scales (a blocking copy from the caller's host array)
-  if (w8 && (e = hipMemcpy(c->ws + c->wso.wscale, src->weight_scales, ((size_t)L * 7 + 1) * 4, hipMemcpyHostToDevice)) !=
-                hipSuccess)
+  // 8-bit weights: the matrix scales, from the context's own host copy (the caller's array may be
+  // freed when kie_create returns), ordered after the workspace clear on the same stream
+  if (w8 && (e = hipMemcpyAsync(c->ws + c->wso.wscale, c->wscale_host.data(), c->wscale_host.size() * 4,
+                                hipMemcpyHostToDevice, stm)) != hipSuccess)
     return fail("copy weight scales", e);
   // weights: per-WG token streams, then the embedding table
   const int64_t* wbase_dev = (const int64_t*)(c->ws + c->wso.wbase);
@@ -469,6 +484,23 @@ kie_status kie_set_token_stream(kie_ctx* ctx, int32_t* ring_host, int32_t capaci
   return KIE_OK;
 }
 
+kie_status kie_set_abort_flag(kie_ctx* ctx, int32_t* host_word) {
+  if (!ctx) return KIE_ERR_INVALID_ARG;
+  if (!host_word) {
+    ctx->abort_dev = nullptr;
+    return KIE_OK;
+  }
+  void* dev = nullptr;
+  const hipError_t e = hipHostGetDevicePointer(&dev, host_word, 0);
+  if (e != hipSuccess || !dev) {
+    (void)hipGetLastError();
+    set_err(&ctx->last_error, "the abort word is not pinned host memory the GPU can read");
+    return KIE_ERR_INVALID_ARG;
+  }
+  ctx->abort_dev = (int32_t*)dev;
+  return KIE_OK;
+}
+
 kie_status kie_set_position(kie_ctx* ctx, int32_t pos) {
   if (!ctx) return KIE_ERR_INVALID_ARG;
   if (pos < 0 || pos > ctx->s.max_seq) {
@@ -485,6 +517,11 @@ kie_status kie_sync(kie_ctx* ctx) {
   HIP_TRY(&ctx->last_error, hipStreamSynchronize(ctx->stream));
   uint32_t errw = 0;
   HIP_TRY(&ctx->last_error, hipMemcpy(&errw, ctx->ws + ctx->wso.err, 4, hipMemcpyDeviceToHost));
+  if (errw & KERR_ABORTED) {
+    ctx->bad_state = true;
+    set_err(&ctx->last_error, "the launch stopped at the host's abort word (error word 0x%x)", errw);
+    return KIE_ERR_ABORTED;
+  }
   if (errw & KERR_TIMEOUT) {
     ctx->bad_state = true;
     set_err(&ctx->last_error, "device wait timed out (error word 0x%x)", errw);
@@ -563,6 +600,7 @@ static kie_status launch(kie_ctx* ctx, const int32_t* first, int32_t n, const in
   P.temperature = top_k > 1 ? smp->temperature : 1.0f;
   P.seed = smp ? smp->seed : 0;
   P.timeout_ticks = ctx->timeout_ticks;
+  P.abort_word = ctx->abort_dev;
   P.skew = ctx->skew;
   P.xb_lds = (uint32_t)lds_slot_offset(ctx->s);
   P.wscale = ctx->w8 ? (const float*)(ctx->ws + ctx->wso.wscale) : nullptr;
@@ -669,6 +707,16 @@ kie_status kie_set_skew(kie_ctx* ctx, uint32_t level) {
     return KIE_ERR_INVALID_ARG;
   }
   ctx->skew = level;
+  return KIE_OK;
+}
+
+kie_status kie_set_wait_timeout(kie_ctx* ctx, uint64_t microseconds) {
+  if (!ctx) return KIE_ERR_INVALID_ARG;
+  if (microseconds > (uint64_t)3600 * 1000000) {
+    set_err(&ctx->last_error, "wait timeout above one hour");
+    return KIE_ERR_INVALID_ARG;
+  }
+  ctx->timeout_ticks = microseconds == 0 ? kDefaultTimeoutTicks : (int64_t)microseconds * 100;
   return KIE_OK;
 }
 

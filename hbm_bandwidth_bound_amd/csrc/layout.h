@@ -258,7 +258,9 @@ KIE_HD int32_t prefill_nmax(const Shape& s) {
 struct Workspace {
   int64_t exch, rope, wbase, err, norms, trace, px, pa3, ph2, pc, pq, pattn, wscale, end;
 };
-constexpr int kTraceWords = 32;  // per wave: cycle counters of a KIE_TRACE build
+constexpr int kTraceWords = 64;  // per wave: cycle counters of a KIE_TRACE build (0..31), and the
+                                 // hop timeline of one sampled layer (32..63, wave 0 only)
+constexpr int kTraceHop = 32;    // first word of the hop timeline
 KIE_HD int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 KIE_HD Workspace workspace_layout(const Shape& s) {
   Workspace w;

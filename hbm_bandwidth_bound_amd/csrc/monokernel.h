@@ -10,7 +10,7 @@ namespace kie {
 // device error word bits
 enum : uint32_t {
   KERR_TIMEOUT = 1u << 0,    // a wait for another workgroup's data timed out
-  KERR_RESERVED = 1u << 1,
+  KERR_ABORTED = 1u << 1,    // the host's abort word was set during the launch
   KERR_BAD_TOKEN = 1u << 2,  // an input token id was out of range (it was replaced by 0)
 };
 
@@ -41,6 +41,7 @@ struct KParams {
   float temperature;         // top-k: logits are divided by it (> 0)
   uint64_t seed;             // top-k: random stream of the draw
   int64_t timeout_ticks;     // per wait, in s_memrealtime ticks (100 MHz)
+  const int32_t* abort_word; // device view of the caller's pinned host abort word, or null
   uint32_t skew;             // > 0: each WG idles a pseudo-random 0..skew-1 x ~3.4 us before
                              // every stage boundary (protocol stress; results must not change)
   uint32_t xb_lds;           // byte offset of the extra-batch LDS slots in the dynamic LDS

@@ -53,6 +53,27 @@ extern __shared__ __align__(16) uint8_t kie_smem[];
 #else
 #define TR_NOW() 0ull
 #endif
+// Hop timeline of a KIE_TRACE or KIE_TRACE_HOPS build (the latter without the cycle counters): wave 0 of every WG stores the absolute time (s_memrealtime,
+// 100 MHz, one clock for the whole chip) of each boundary event of one sampled (step, layer)
+// into trace words kTraceHop + event, so that publication spreads and per-XCD gather latencies
+// can be read off afterwards. Free in normal builds.
+constexpr int kHopStep = 8, kHopLayer = 12;
+enum HopEvent : int {
+  H_QKV_IN = 0, H_QKV_PUB = 1, H_ATT_IN = 2, H_ATT_PUB = 3, H_MERGE_PUB = 4, H_O_GOT = 5, H_O_IN = 6,
+  H_XA_PUB = 7, H_XA_GOT = 8, H_GU_IN = 9, H_H_PUB = 10, H_H_GOT = 11, H_DN_IN = 12, H_XF_PUB = 13,
+  H_XF_GOT = 14, H_NORM_DONE = 15
+};
+#if defined(KIE_TRACE) || defined(KIE_TRACE_HOPS)
+#define TR_HOP(K, ev)                                                                                     \
+  do {                                                                                                    \
+    if ((K).hop_on && (K).v == 0) /* wave-uniform: every lane stores the same time */                      \
+      (K).P.trace[((int64_t)(K).w * kWaves) * kTraceWords + kTraceHop + (ev)] = now_ticks();              \
+  } while (0)
+#else
+#define TR_HOP(K, ev) \
+  do {                \
+  } while (0)
+#endif
 enum TraceSlot : int {
   T_FETCH = 0, T_GEMV = 1, T_FIN = 2, T_ATT = 3, T_MERGE = 4, T_BAR = 5, T_TOTAL = 6, T_BATCHES = 7,
   T_NORM = 8, T_SAMPLE = 9
@@ -208,15 +229,26 @@ __device__ __forceinline__ bool global_error(const KParams& P) {
   return __builtin_amdgcn_readfirstlane(__hip_atomic_load(P.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0;
 }
 
-// Bounded spin: call expired() after every unsuccessful poll. Every 256th call it checks the WG's
-// abort flag and the elapsed time of this wait (wave-uniform). Poll rounds follow each other
-// without a sleep: each round already waits for its own loads, which paces it.
+// The caller's abort word (pinned host memory), read at system scope; 0 when there is none.
+__device__ __forceinline__ int32_t host_abort(const KParams& P) {
+  return P.abort_word ? __hip_atomic_load(P.abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) : 0;
+}
+
+// Bounded spin: call expired() after every unsuccessful poll. Every 64th call it checks the WG's
+// abort flag, the host's abort word and the elapsed time of this wait (wave-uniform); `why` then
+// names the error to raise. Poll rounds follow each other without a sleep: each round already
+// waits for its own loads, which paces it.
 struct Waiter {
   uint32_t spins = 0;
   uint64_t start = 0;
+  uint32_t why = KERR_TIMEOUT;
   __device__ __forceinline__ bool expired(const KParams& P, const Lds& L) {
-    if ((++spins & 255u) != 0) return false;
+    if ((++spins & 63u) != 0) return false;
     if (aborted(L)) return true;
+    if (__builtin_amdgcn_readfirstlane(host_abort(P)) != 0) {
+      why = KERR_ABORTED;
+      return true;
+    }
     const uint64_t t = now_ticks();
     if (start == 0) {
       start = t;
@@ -298,6 +330,7 @@ struct Wk {
   int32_t sel_key = -1;
   bool deferred = false;
   const uint8_t* xreg = nullptr;  // expert region of the packed image
+  bool hop_on = false;            // KIE_TRACE: this boundary belongs to the sampled (step, layer)
 
   __device__ __forceinline__ Wk(const KParams& p, const Lds& l, int32_t w_, int32_t v_, int32_t lane_)
       : P(p), L(l), w(w_), v(v_), lane(lane_), tid(v_ * kWave + lane_), fail(false) {
@@ -761,9 +794,9 @@ struct Wk {
         }
       }
       if (__builtin_amdgcn_ballot_w64(missing != 0) == 0 || fail) break;
-      if (wt.expired(P, L) || ((wt.spins & 255u) == 0 && global_error(P))) {
+      if (wt.expired(P, L) || ((wt.spins & 63u) == 0 && global_error(P))) {
         fail = true;
-        raise_error(P, L, KERR_TIMEOUT);
+        raise_error(P, L, wt.why);
         break;
       }
 #pragma unroll
@@ -932,6 +965,7 @@ __device__ __forceinline__ void attention(WK& K, const Att& at, int32_t l, int32
         },
         [&](int k, float x) { L.q[K.tid + k * kThreads] = x; });
     K.tr.add(T_FETCH, TR_NOW() - t0);
+    TR_HOP(K, H_ATT_IN);
     bar();
   }
   const uint64_t ta = TR_NOW();
@@ -1270,9 +1304,9 @@ __device__ __forceinline__ void merge_unit(WK& K, const Att& at, int32_t l, int3
         if ((todo & (1u << k)) && (uint32_t)wm[k] == epoch && (uint32_t)wl[k] == epoch && (uint32_t)wa[k] == epoch)
           todo &= ~(1u << k);
       if (__builtin_amdgcn_ballot_w64(todo != 0) != 0) {
-        if (wt.expired(P, L) || ((wt.spins & 255u) == 0 && global_error(P))) {
+        if (wt.expired(P, L) || ((wt.spins & 63u) == 0 && global_error(P))) {
           K.fail = true;
-          raise_error(P, L, KERR_TIMEOUT);
+          raise_error(P, L, wt.why);
           break;
         }
       }
@@ -1354,9 +1388,9 @@ __device__ __forceinline__ void merge_two_units(WK& K, const Att& at, int32_t l,
         if ((todo & (1u << k)) && (uint32_t)wm[k] == epoch && (uint32_t)wl[k] == epoch && (uint32_t)wa[k] == epoch)
           todo &= ~(1u << k);
       if (__builtin_amdgcn_ballot_w64(todo != 0) != 0) {
-        if (wt.expired(P, L) || ((wt.spins & 255u) == 0 && global_error(P))) {
+        if (wt.expired(P, L) || ((wt.spins & 63u) == 0 && global_error(P))) {
           K.fail = true;
-          raise_error(P, L, KERR_TIMEOUT);
+          raise_error(P, L, wt.why);
           break;
         }
       }
@@ -1621,6 +1655,9 @@ __device__ __forceinline__ void decode(Wk<MOE, W8>& K) {
       }
       const uint64_t tb = TR_NOW();
       const int bnd_run = bnd;
+#if defined(KIE_TRACE) || defined(KIE_TRACE_HOPS)
+      K.hop_on = step == kHopStep && l == kHopLayer;
+#endif
       bool routed = false;  // the router boundary of a mixture-of-experts layer (not in the switch,
                             // so that the dense program is compiled as if it did not exist)
       if constexpr (MOE) {
@@ -1663,6 +1700,7 @@ __device__ __forceinline__ void decode(Wk<MOE, W8>& K) {
         }
         case B_QKV: {  // QKV outputs (+RoPE) -> attention -> merge -> gather o
           bar();
+          TR_HOP(K, H_QKV_IN);
           uint64_t* qx = ex + X.q + (int64_t)l * s.qdim();
           uint64_t* kx = ex + X.k + (int64_t)l * s.kvdim();
           uint64_t* vx = ex + X.v + (int64_t)l * s.kvdim();
@@ -1701,7 +1739,9 @@ __device__ __forceinline__ void decode(Wk<MOE, W8>& K) {
             st_x(dst + h * s.hd + i, tag_f(ya, ep));
             st_x(dst + h * s.hd + i + half, tag_f(yb, ep));
           });
+          TR_HOP(K, H_QKV_PUB);
           if (at.c0 <= pos) attention<G, HD>(K, at, l, pos, ep);
+          TR_HOP(K, H_ATT_PUB);
           {
             const uint64_t tm = TR_NOW();
             const int32_t nu = merge_units(s);
@@ -1714,7 +1754,9 @@ __device__ __forceinline__ void decode(Wk<MOE, W8>& K) {
             }
             K.tr.add(T_MERGE, TR_NOW() - tm);
           }
+          TR_HOP(K, H_MERGE_PUB);
           K.fetch_f32(ex + X.o + (int64_t)l * s.qdim(), s.qdim(), L.act, ep, false);
+          TR_HOP(K, H_O_GOT);
           // The K/V rows this WG appended are complete before it publishes anything more. Here
           // the wave has just waited for its polls, so nothing newer is queued and the wait
           // costs nothing; after the next stage's first batch is issued it would wait for that.
@@ -1725,6 +1767,7 @@ __device__ __forceinline__ void decode(Wk<MOE, W8>& K) {
         }
         case B_O: {  // O outputs + residual -> gather xa -> RMSNorm
           bar();
+          TR_HOP(K, H_O_IN);
           uint64_t* xa = ex + X.xa + (int64_t)l * s.d;
           K.prefetch_gain(P.norms + (int64_t)l * 2 * s.d + s.d);
           const float so = W8 ? P.wscale[l * 7 + 3] : 1.f;
@@ -1736,16 +1779,19 @@ __device__ __forceinline__ void decode(Wk<MOE, W8>& K) {
             st_x(xa + 2 * gp, tag_f(xres[2 * gp] + ya, ep));
             st_x(xa + 2 * gp + 1, tag_f(xres[2 * gp + 1] + yb, ep));
           });
+          TR_HOP(K, H_XA_PUB);
           K.issue_x();  // the gate/up stage is the longest: start its second batch now
           xres = xres == L.xres ? L.xres + s.d : L.xres;  // the other buffer: no wave reads it now
           ss = K.fetch_f32(xa, s.d, xres, ep, true);
           K.norm_to_act(ss, xres);
+          TR_HOP(K, H_XA_GOT);
           st = MOE ? ST_RT : ST_GU;
           bnd = MOE ? B_RT : B_GU;
           break;
         }
         case B_GU: {  // SwiGLU outputs -> gather h
           bar();
+          TR_HOP(K, H_GU_IN);
           uint64_t* hx = ex + X.h + (int64_t)l * s.F;
           const float sg = W8 ? P.wscale[l * 7 + 4] : 1.f, su = W8 ? P.wscale[l * 7 + 5] : 1.f;
           K.finalize(K.g[ST_GU], [&](int32_t gp, float ya, float yb) {
@@ -1757,8 +1803,10 @@ __device__ __forceinline__ void decode(Wk<MOE, W8>& K) {
             if constexpr (MOE) h = K.weight_of(gp / s.Fe) * h;  // the routing weight of its expert
             st_x(hx + gp, tag_f(h, ep));
           });
+          TR_HOP(K, H_H_PUB);
           K.issue_x();
           K.template fetch_f32<16>(hx, s.F, L.act, ep, false);
+          TR_HOP(K, H_H_GOT);
           st = ST_DN;
           bnd = B_DN;
           break;
@@ -1771,6 +1819,7 @@ __device__ __forceinline__ void decode(Wk<MOE, W8>& K) {
             td = t;
           };
           bar();
+          TR_HOP(K, H_DN_IN);
           dphase(24);
           uint64_t* xf = ex + X.xf + (int64_t)(l + 1) * s.d;
           K.prefetch_gain(P.norms + (l + 1 < s.L ? (int64_t)(l + 1) * 2 * s.d : (int64_t)s.L * 2 * s.d));
@@ -1784,6 +1833,7 @@ __device__ __forceinline__ void decode(Wk<MOE, W8>& K) {
             st_x(xf + 2 * gp + 1, tag_f(xres[2 * gp + 1] + yb, ep));
           });
           dphase(25);
+          TR_HOP(K, H_XF_PUB);
           K.issue_x();  // the next layer's stages
 #ifdef KIE_TRACE
           if (step == 8 && l == 12) K.tr.c[29] = now_ticks();  // one sample of absolute times
@@ -1800,8 +1850,10 @@ __device__ __forceinline__ void decode(Wk<MOE, W8>& K) {
 #ifdef KIE_TRACE
             if (step == 8 && l == 13) K.tr.c[30] = now_ticks();
 #endif
+            TR_HOP(K, H_XF_GOT);
             dphase(27);
             K.norm_to_act(ss, xres);
+            TR_HOP(K, H_NORM_DONE);
             dphase(28);
             st = ST_QKV;
             bnd = B_QKV;
@@ -1818,6 +1870,10 @@ __device__ __forceinline__ void decode(Wk<MOE, W8>& K) {
         }
         case B_LM:
         case B_END: {  // LM outputs and this WG's argmax candidate; the grid-wide join; next token
+          // Once per step, wave 0 reads the caller's abort word. Its decision reaches the other
+          // waves through the LDS flag, which they read only after the barriers below.
+          if (P.abort_word && K.v == 0 && __builtin_amdgcn_readfirstlane(host_abort(P)) != 0)
+            raise_error(P, L, KERR_ABORTED);
           float bv = -INFINITY;
           int32_t bi = 0x7fffffff;
           const bool topk = bnd == B_LM && P.top_k > 1;

@@ -87,6 +87,10 @@ def load() -> C.CDLL:
     lib.kie_set_token_stream.restype = C.c_int32
     lib.kie_set_skew.argtypes = [vp, C.c_uint32]
     lib.kie_set_skew.restype = C.c_int32
+    lib.kie_set_abort_flag.argtypes = [vp, vp]
+    lib.kie_set_abort_flag.restype = C.c_int32
+    lib.kie_set_wait_timeout.argtypes = [vp, C.c_uint64]
+    lib.kie_set_wait_timeout.restype = C.c_int32
     lib.kie_set_position.argtypes = [vp, C.c_int32]
     lib.kie_set_position.restype = C.c_int32
     lib.kie_position.argtypes = [vp]
@@ -209,6 +213,16 @@ class Engine:
     def set_skew(self, level: int):
         """Protocol stress (tests): workgroups idle pseudo-random amounts before stage boundaries."""
         _check(self.lib, self.lib.kie_set_skew(self.ctx, int(level)), self.ctx)
+
+    def set_abort_flag(self, word=None):
+        """word: pinned host int32 tensor of one element that the device reads (None removes it)."""
+        st = self.lib.kie_set_abort_flag(self.ctx, _ptr(word) if word is not None else None)
+        _check(self.lib, st, self.ctx)
+        self._abort_word = word  # kept alive while installed
+
+    def set_wait_timeout(self, microseconds: int):
+        """Time limit of every device-side wait of later launches (0: the default)."""
+        _check(self.lib, self.lib.kie_set_wait_timeout(self.ctx, int(microseconds)), self.ctx)
 
     def set_token_stream(self, ring=None):
         """ring: pinned host int32 tensor of 1 + capacity elements (None stops streaming)."""

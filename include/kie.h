@@ -125,15 +125,27 @@ size_t kie_kv_cache_bytes(const kie_config* cfg);
 size_t kie_workspace_bytes(const kie_config* cfg);
 
 /* Create a context on the current HIP device and enqueue the packing of `src` into `packed`
- * (kie_packed_weight_bytes) on `hip_stream` (a hipStream_t, or NULL for the default stream). The
- * workspace (kie_workspace_bytes) is initialised here; kv_cache (kie_kv_cache_bytes) needs no
- * initialisation. Position starts at 0. Errors: KIE_ERR_INVALID_ARG, KIE_ERR_UNSUPPORTED (shape,
- * or a device that is not gfx950 / cannot co-schedule one workgroup per compute unit),
- * KIE_ERR_HIP. On error *out is NULL. */
+ * (kie_packed_weight_bytes) on `hip_stream` (a hipStream_t, or NULL for the default stream).
+ * The packing lays every weight out in the order in which each wave of each compute unit reads it
+ * during one token, one contiguous slice per wave, so that the memory accesses follow the
+ * chip's layout (aikraft.ru «3000 токенов в секунду…», §05 on the MI300X chiplet topology;
+ * setupai.cc 《Monokernel 推論引擎在 MI300X 上達到每秒 3,300 token》, 技術深入: memory accesses
+ * mapped to the physical chiplet topology). The workspace (kie_workspace_bytes) is initialised
+ * here; kv_cache (kie_kv_cache_bytes) needs no initialisation. Alignment: packed 16 bytes,
+ * kv_cache and workspace 256 bytes (every cache row then owns whole cache lines). Every buffer
+ * stays owned by the caller. Position starts at 0. All work is enqueued on hip_stream in order;
+ * the call returns before it completes, and `src` must stay valid until the first kie_sync.
+ * Errors: KIE_ERR_INVALID_ARG (a NULL or misaligned pointer, bad weight scales), KIE_ERR_UNSUPPORTED
+ * (shape, or a device that is not gfx950 / cannot co-schedule one workgroup per compute unit),
+ * KIE_ERR_HIP. On error *out is NULL and nothing was enqueued. */
 kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packed, void* kv_cache,
                       void* workspace, void* hip_stream, kie_ctx** out);
 
-/* Process a prompt of n_tokens ids (device int32 [n_tokens]) at positions pos .. pos+n_tokens-1,
+/* The prompt pass: time to first token is a metric of its own, separate from the per-token decode
+ * speed (aikraft.ru «3000 токенов в секунду…», §01), and processing a long prompt is bound by
+ * arithmetic rather than by memory bandwidth (zdabc.icu, 《Kog 推理引擎：不砍精度，单请求冲到 3000
+ * tokens/s》, "AMD vs NVIDIA：两个数字的读法"), so it runs on the matrix cores.
+ * Process a prompt of n_tokens ids (device int32 [n_tokens]) at positions pos .. pos+n_tokens-1,
  * writing their K/V rows, then choose the next token (device int32 [1], first_token_dev) from the
  * logits of the last prompt position; those logits are written to last_logits_dev (device fp32
  * [V]) unless it is NULL. Advances the position by n_tokens. A dense model runs all but the last
@@ -144,13 +156,20 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
 kie_status kie_prefill(kie_ctx* ctx, const int32_t* tokens_dev, int32_t n_tokens, int32_t* first_token_dev,
                        float* last_logits_dev, const kie_sampling* sampling);
 
-/* One decode step: process token_in_dev (device int32 [1]) at the current position, write the
- * chosen next token to token_out_dev (device int32 [1]) and, unless NULL, the logits to
- * logits_dev (device fp32 [V]). Identical to kie_generate with n_steps = 1. */
+/* One decode step as one kernel launch: the per-launch cost that the monokernel removes
+ * (agentlenshq.com, 《突破内存墙…》, "微秒级的损失在哪里": ~4.5 us to launch and clean up a kernel;
+ * aikraft.ru «3000 токенов в секунду…», §03) can be measured against kie_generate with it.
+ * Process token_in_dev (device int32 [1]) at the current position, write the chosen next token to
+ * token_out_dev (device int32 [1]) and, unless NULL, the logits to logits_dev (device fp32 [V]).
+ * Identical in results to kie_generate with n_steps = 1. Errors: as kie_generate. */
 kie_status kie_decode_step(kie_ctx* ctx, const int32_t* token_in_dev, const kie_sampling* sampling,
                            int32_t* token_out_dev, float* logits_dev);
 
-/* n_steps decode steps in ONE kernel launch (the tokens never return to the host in between).
+/* The monokernel: n_steps decode steps in ONE kernel launch, the whole decode path (matrix
+ * products, attention, normalisation and sampling) in one GPU-resident program that does not
+ * return control to the host between tokens (agentlenshq.com, 《突破内存墙…》, "The Monokernel
+ * Runtime"; aikraft.ru «3000 токенов в секунду…», §04 "Моноядро"; setupai.cc 《Monokernel
+ * 推論引擎…》, 技術深入).
  * Step s processes token t_s at position pos+s, where t_0 = *first_token_dev and t_s is the token
  * chosen at step s-1, or forced_dev[s-1] when forced_dev (device int32 [n_steps-1 or more]) is
  * given (teacher forcing; the chosen tokens are still written). tokens_out_dev (device int32
@@ -162,16 +181,25 @@ kie_status kie_decode_step(kie_ctx* ctx, const int32_t* token_in_dev, const kie_
 kie_status kie_generate(kie_ctx* ctx, const int32_t* first_token_dev, int32_t n_steps, const kie_sampling* sampling,
                         const int32_t* forced_dev, int32_t* tokens_out_dev, float* logits_dev);
 
-/* Wait for the context's stream and read the device error word. Returns KIE_OK,
- * KIE_ERR_TIMEOUT or KIE_ERR_ABORTED (after which the context is in the error state until
- * kie_reset), or KIE_ERR_HIP. */
+/* The host's only synchronisation point: the launches run without host round trips (the host-side
+ * scheduling and GPU-CPU communication the pages remove from the token loop: agentlenshq.com,
+ * 《突破内存墙…》, "微秒级的损失在哪里"), so the host learns their outcome here. Waits for the
+ * context's stream and reads the device error word. Returns KIE_OK, KIE_ERR_TIMEOUT (a bounded
+ * device wait expired), KIE_ERR_ABORTED (the abort word of kie_set_abort_flag was set, or an
+ * input token id was out of range) -- after either the context is in the error state until
+ * kie_reset -- or KIE_ERR_HIP. */
 kie_status kie_sync(kie_ctx* ctx);
 
-/* Position back to 0 and any device error cleared (the KV contents are simply overwritten by
- * later steps). */
+/* Start a new sequence: an agent runs many requests one after the other, each a fresh prompt
+ * (agentlenshq.com, 《突破内存墙…》, opening section; aikraft.ru «3000 токенов в секунду…», §01).
+ * Position back to 0 and any device error cleared (the KV contents are simply overwritten by
+ * later steps). Enqueued on the context's stream. Errors: KIE_ERR_INVALID_ARG, KIE_ERR_HIP. */
 kie_status kie_reset(kie_ctx* ctx);
 
-/* Set the position to pos (0 <= pos <= max_seq_len). Below the current position it rewinds the
+/* Reuse or supply cached context: an agent's loop re-runs from an earlier point of its sequence
+ * (agentlenshq.com, 《突破内存墙…》, opening section; aikraft.ru «3000 токенов в секунду…», §01:
+ * inspect, plan, edit, test, fix, each step depending on the previous).
+ * Set the position to pos (0 <= pos <= max_seq_len). Below the current position it rewinds the
  * sequence so that steps resume at pos (e.g. to re-run a suffix). Above it, the caller states that
  * the K/V rows of positions < pos are already in its kv_cache buffer (written there directly, in
  * the documented layout): later steps attend over them as they are. KIE_ERR_INVALID_ARG
@@ -189,6 +217,16 @@ kie_status kie_set_position(kie_ctx* ctx, int32_t pos);
  * ring_host == NULL stops streaming. Errors: KIE_ERR_INVALID_ARG (capacity <= 0, or memory the
  * device cannot write). */
 kie_status kie_set_token_stream(kie_ctx* ctx, int32_t* ring_host, int32_t capacity);
+
+/* Stop a running launch from the host. host_word is caller-owned pinned host memory (hipHostMalloc,
+ * or a pinned torch tensor) holding one int32 that the library only reads. While it is nonzero,
+ * every launch of this context stops at the end of the current decode step (each workgroup reads
+ * the word once per step, and while it waits for another workgroup), kie_sync then returns
+ * KIE_ERR_ABORTED and the context needs kie_reset. Clear the word before later launches.
+ * host_word == NULL removes it (the default). The pages' engine leaves the token loop entirely to
+ * the GPU (agentlenshq.com, 《突破内存墙…》, "The Monokernel Runtime"); this is the host's way back
+ * in. Errors: KIE_ERR_INVALID_ARG (memory the device cannot read). */
+kie_status kie_set_abort_flag(kie_ctx* ctx, int32_t* host_word);
 
 /* Current position (number of tokens whose K/V rows are in the cache), or -1 for NULL. */
 int32_t kie_position(const kie_ctx* ctx);

@@ -44,6 +44,13 @@ int64_t kie_trace_offset(const kie_config* cfg);
  * KIE_ERR_INVALID_ARG for a null context or a level above 64. */
 kie_status kie_set_skew(kie_ctx* ctx, uint32_t level);
 
+/* Time limit of every device-side wait of later launches, in microseconds (0 restores the
+ * default of 2 s). A wait that exceeds it raises the timeout error (kie_sync then returns
+ * KIE_ERR_TIMEOUT) and every workgroup leaves its waits and ends the launch. Tests set a tiny limit
+ * together with kie_set_skew to exercise that path; waits are checked every 64 polls. Returns
+ * KIE_OK, or KIE_ERR_INVALID_ARG for a null context or a limit above one hour. */
+kie_status kie_set_wait_timeout(kie_ctx* ctx, uint64_t microseconds);
+
 #ifdef __cplusplus
 }
 #endif

@@ -76,6 +76,29 @@ def test_no_gpu_paths_fail_cleanly(lib):
     lib.kie_destroy(None)
 
 
+def test_create_rejects_misaligned_buffers_before_touching_the_device(lib):
+    """The KV cache and the workspace must start on a 256-byte boundary (each cache row then owns
+    whole cache lines); the check is made before any HIP call, so it holds without a GPU. The
+    pointers are never dereferenced."""
+    from hbm_bandwidth_bound_amd import kie, synth
+    cfg = kie.make_config(synth.TINY, 96)
+    w = kie.kie_weights()
+    ctx = C.c_void_p()
+    base = 1 << 20
+    for packed, kv, ws in ((base, base + 16, base), (base, base + 128, base), (base, base, base + 64),
+                           (base + 8, base, base)):
+        st = lib.kie_create(C.byref(cfg), C.byref(w), C.c_void_p(packed), C.c_void_p(kv), C.c_void_p(ws), None,
+                            C.byref(ctx))
+        assert st == -1 and not ctx.value  # KIE_ERR_INVALID_ARG
+        assert b"256-byte" in lib.kie_last_error(None)
+
+
+def test_setters_reject_a_null_context(lib):
+    assert lib.kie_set_abort_flag(None, None) == -1
+    assert lib.kie_set_wait_timeout(None, 5) == -1
+    assert lib.kie_set_skew(None, 1) == -1
+
+
 def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     """No fallback: without the built library the binding raises instead of computing elsewhere."""
     from hbm_bandwidth_bound_amd import kie
