@@ -88,27 +88,18 @@ def _oracle_steps(model, w_np, prompt_len: int, target_s: float, max_steps: int 
             return n, el
 
 
-def cpu_baseline(model, weights_dev, prompt_len: int, target_s: float):
-    """Oracle decode steps of the same model at the same context length. A model too large to
-    copy to the host whole (the mixture-of-experts one) is timed on two cuts of itself, its
-    first 2 and first 4 layers with the real embedding and LM head; the per-layer time (their
-    difference over 2 layers) then scales the 4-layer time to the full depth."""
+def _oracle_rate(model, weights_dev, prompt_len: int, target_s: float, threads: int, w_np=None):
+    """(tok/s, description) of the oracle at `threads` threads on the same model and context. A
+    model too large to copy to the host whole (the mixture-of-experts one) is timed on two cuts of
+    itself, its first 2 and first 4 layers with the real embedding and LM head; the per-layer time
+    (their difference over 2 layers) then scales the 4-layer time to the full depth."""
     import oracle
     from hbm_bandwidth_bound_amd import synth
-    try:
-        ncores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        ncores = os.cpu_count() or 1
-    threads = max(1, min(16, ncores))
-    oracle.build(force=False)
     oracle.set_threads(threads)
     if not model.n_experts:
-        w_np = synth.weights_torch_to_np(weights_dev)
         n, el = _oracle_steps(model, w_np, prompt_len, target_s)
-        return {"value": n / el, "unit": "tok/s", "cores": threads, "kind": "oracle",
-                "sample": f"{n} oracle decode steps of the {model.name} model at positions {prompt_len}.."
-                          f"{prompt_len + n - 1} (KV rows < {prompt_len} seeded synthetic), {el:.1f} s, "
-                          f"{threads} threads row-parallel"}
+        return n / el, (f"{n} oracle decode steps of the {model.name} model at positions {prompt_len}.."
+                        f"{prompt_len + n - 1} (KV rows < {prompt_len} seeded synthetic), {el:.1f} s")
     cut = {k: (v[:4] if isinstance(v, list) else v) for k, v in weights_dev.items()}
     w4 = synth.weights_torch_to_np(cut)
     w2 = {k: (v[:2] if isinstance(v, list) else v) for k, v in w4.items()}
@@ -117,11 +108,31 @@ def cpu_baseline(model, weights_dev, prompt_len: int, target_s: float):
     t2, t4 = e2 / n2, e4 / n4
     per_layer = max(t4 - t2, 0.0) / 2
     t_full = t4 + (model.n_layers - 4) * per_layer
-    return {"value": 1.0 / t_full, "unit": "tok/s", "cores": threads, "kind": "oracle",
-            "sample": f"oracle decode steps at positions {prompt_len}.. of the {model.name} model cut to its "
-                      f"first 2 layers ({n2} steps, {t2:.3f} s/step) and 4 layers ({n4} steps, {t4:.3f} s/step), "
-                      f"real embedding and LM head; per-token time = t4 + {model.n_layers - 4} x (t4 - t2) / 2 = "
-                      f"{t_full:.2f} s; {threads} threads row-parallel"}
+    return 1.0 / t_full, (f"oracle decode steps at positions {prompt_len}.. of the {model.name} model cut to its "
+                          f"first 2 layers ({n2} steps, {t2:.3f} s/step) and 4 layers ({n4} steps, {t4:.3f} "
+                          f"s/step), real embedding and LM head; per-token time = t4 + {model.n_layers - 4} x "
+                          f"(t4 - t2) / 2 = {t_full:.2f} s")
+
+
+def cpu_baseline(model, weights_dev, prompt_len: int, target_s: float):
+    """The oracle on the machine's host cores: one core (the reported value), then rows split over up
+    to 16 threads (same arithmetic, bitwise the same results), each for about half the time."""
+    import oracle
+    from hbm_bandwidth_bound_amd import synth
+    try:
+        ncores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncores = os.cpu_count() or 1
+    threads = max(1, min(16, ncores))
+    oracle.build(force=False)
+    w_np = None if model.n_experts else synth.weights_torch_to_np(weights_dev)
+    v1, d1 = _oracle_rate(model, weights_dev, prompt_len, target_s / 2, 1, w_np)
+    vn, dn = _oracle_rate(model, weights_dev, prompt_len, target_s / 2, threads, w_np)
+    oracle.set_threads(1)
+    return {"value": v1, "unit": "tok/s", "cores": 1, "kind": "oracle", "sample": d1 + ", 1 thread",
+            "box_cores": ncores,
+            "threaded": {"value": vn, "unit": "tok/s", "threads": threads, "sample": dn + f", {threads} threads "
+                         "(rows split over threads; each row's summation order unchanged)"}}
 
 
 def main():
@@ -285,7 +296,12 @@ def main():
                   "source_sha": source_hash()},
     }
     print(json.dumps(res), flush=True)
+    # explicit teardown before the interpreter exits: the context, every device tensor, then the
+    # stream, so that nothing of the GPU runtime is released by exit handlers
     eng.close()
+    del eng, wdev, prompt, out, first, sink
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":

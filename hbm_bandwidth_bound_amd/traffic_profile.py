@@ -71,7 +71,12 @@ def run(args):
     stream_copy(dst, src, nb, stream)
     torch.cuda.synchronize()
     print("done", out[:4].tolist(), flush=True)
+    # explicit teardown before the interpreter exits: the context, every device tensor, then the
+    # stream, so that nothing of the GPU runtime is released by exit handlers
     eng.close()
+    del eng, w, prompt, first, out, src, dst
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
 
 def _counter_per_dispatch(run_dir: str, counter: str):

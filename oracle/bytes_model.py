@@ -80,3 +80,15 @@ def mean_decode_bytes(cfg, prompt_len: int, steps: int) -> float:
     """Mean of decode_step_bytes over the decode positions prompt_len .. prompt_len+steps-1."""
     tot = sum(decode_step_bytes(cfg, prompt_len + s) for s in range(steps))
     return tot / steps
+
+
+def decode_step_bytes_8bit(cfg, pos: int) -> int:
+    """decode_step_bytes for a model whose layer matrices and LM head are 8-bit codes: one byte per
+    matrix weight and one fp32 scale per matrix (seven per layer and the LM head's), while the norm
+    gains, the embedding row and the KV cache stay bf16 (the pages: 8-bit weights halve the bytes
+    a bandwidth-bound decoder streams; aikraft.ru «3000 токенов в секунду…», §02)."""
+    d = cfg.d_model
+    gains = (2 * cfg.n_layers + 1) * d        # attention and FFN norms per layer, final norm
+    matrices = active_params(cfg) - gains - d  # everything else but the one embedding row
+    kvp = kv_bytes_per_position(cfg)
+    return matrices + 4 * (7 * cfg.n_layers + 1) + 2 * (gains + d) + kvp * (pos + 1) + kvp

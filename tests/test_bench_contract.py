@@ -56,3 +56,18 @@ def test_committed_summary_agrees_with_the_byte_model():
     algo = traffic.launch_bytes(wl.model, wl.prompt_len, steps) / steps
     assert abs(float(kv["algorithmic_bytes_per_step"]) - algo) <= 1.0
     assert float(kv["hbm_bytes_per_step"]) >= 0.99 * algo
+
+
+def test_bench_byte_model_is_the_pinned_one():
+    """bench.py prices its roofline with hbm_bandwidth_bound_amd/traffic.py; the byte model pinned
+    to the pages' closed forms is oracle/bytes_model.py. They must give the same bytes for every
+    workload, at every position, and for whole launches."""
+    import oracle
+    from hbm_bandwidth_bound_amd import synth, traffic
+    for name, wl in synth.WORKLOADS.items():
+        m = wl.model
+        pinned = oracle.bytes_model.decode_step_bytes_8bit if m.weight_format else oracle.bytes_model.decode_step_bytes
+        for pos in (0, wl.prompt_len, wl.prompt_len + 255):
+            assert traffic.step_bytes(m, pos) == pinned(m, pos), (name, pos)
+        n = 17
+        assert traffic.launch_bytes(m, wl.prompt_len, n) == sum(pinned(m, wl.prompt_len + s) for s in range(n)), name

@@ -412,3 +412,17 @@ def test_gemv_order_is_a_rounding_level_variant(oracle_lib):
     assert not np.array_equal(y_asc, y_desc)
     spread = np.linalg.norm(a.astype(np.float64) - b) / np.linalg.norm(b.astype(np.float64))
     assert 0 < spread < 1e-4
+
+
+def test_8bit_bytes_halve_the_weight_stream(oracle_lib):
+    """The pages: 8-bit weights halve the bytes a bandwidth-bound decoder streams per token. With
+    the KV rows set aside, the 8-bit model's bytes are half the bf16 model's, up to the bf16 norm
+    gains and embedding row and the per-matrix scales (below 0.1% at these shapes)."""
+    from hbm_bandwidth_bound_amd import synth
+    bm = oracle_lib.bytes_model
+    for m in (synth.M1_6B, synth.M8B):
+        kv = bm.kv_bytes_per_position(m) * 2
+        b16 = bm.decode_step_bytes(m, 0) - kv
+        b8 = bm.decode_step_bytes_8bit(m, 0) - kv
+        assert abs(b8 / b16 - 0.5) < 1e-3, (m.name, b8 / b16)
+        assert b8 > b16 / 2  # the bf16 pieces and the scales only add
