@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -46,7 +47,7 @@ struct kie_ctx {
   uint32_t skew;           // kie_set_skew
   int32_t* abort_dev;      // device view of the caller's host abort word, or null
   std::vector<float> wscale_host;  // 8-bit weights: the matrix scales, copied from the caller
-  std::vector<int64_t> wbase_host;
+  bool static_ws;          // the workspace is this GPU's static array (kie_create_static)
   std::string last_error;
 };
 
@@ -88,9 +89,6 @@ static int query_cus(int* out, std::string* err) {
 // Packed-image geometry in the config's weight format (tiles of kTileK bf16 or 2 * kTileK 8-bit
 // weights per row).
 static bool cfg_w8(const kie_config* c) { return c && c->weight_format == KIE_WEIGHTS_FP8_E4M3; }
-static int64_t pk_stream_tiles(const Shape& s, bool w8, int32_t w, int32_t v) {
-  return w8 ? stream_tiles<2 * kTileK>(s, w, v) : stream_tiles(s, w, v);
-}
 static int64_t pk_embed_offset(const Shape& s, bool w8) {
   return w8 ? packed_embed_offset<2 * kTileK>(s) : packed_embed_offset(s);
 }
@@ -248,12 +246,53 @@ const char* kie_last_error(const kie_ctx* ctx) { return ctx ? ctx->last_error.c_
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 static bool aligned256(const void* p) { return ((uintptr_t)p & 255u) == 0; }
 
-kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packed, void* kv_cache, void* workspace,
-                      void* hip_stream, kie_ctx** out) {
+// ------------------------------------------------------------------ the static workspace
+// For callers that cannot allocate device memory: the workspace of contexts made by
+// kie_create_static lives in this array, one copy per GPU (the HIP runtime places it in each
+// device's memory when the library's code is loaded there; it stays until the process ends).
+// Host code uses only the device address hipGetSymbolAddress returns for the current device,
+// never the array's name, which on the host is a stand-in and not a device address.
+static __device__ __align__(256) uint8_t scratch[KIE_STATIC_WORKSPACE_MAX];
+constexpr int kMaxDevices = 64;
+static std::mutex g_static_mu;
+static uint8_t* g_static_addr[kMaxDevices];          // device address of `scratch`, once looked up
+static const kie_ctx* g_static_owner[kMaxDevices];   // the static context now using it
+
+// Device address of this GPU's `scratch` (the current device), looked up once per device.
+static kie_status static_workspace(int dev, uint8_t** addr, std::string* err) {
+  if (dev < 0 || dev >= kMaxDevices) {
+    set_err(err, "device %d is beyond the %d devices the static workspace supports", dev, kMaxDevices);
+    return KIE_ERR_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lk(g_static_mu);
+  if (!g_static_addr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      set_err(err, "hipGetSymbolAddress of the static workspace failed: %s", hipGetErrorString(e));
+      return KIE_ERR_HIP;
+    }
+    g_static_addr[dev] = (uint8_t*)p;
+  }
+  *addr = g_static_addr[dev];
+  return KIE_OK;
+}
+// A static context may enqueue work only while it is the one that last took over the array.
+static bool static_owner_ok(const kie_ctx* ctx) {
+  if (!ctx->static_ws) return true;
+  std::lock_guard<std::mutex> lk(g_static_mu);
+  return g_static_owner[ctx->device] == ctx;
+}
+
+// kie_create and kie_create_static: workspace == NULL selects this GPU's static array.
+static kie_status create_impl(const kie_config* cfg, const kie_weights* src, void* packed, void* kv_cache,
+                              void* workspace, void* hip_stream, kie_ctx** out) {
   if (out) *out = nullptr;
   g_create_error.clear();
   std::string* err = &g_create_error;
-  if (!out || !src || !packed || !kv_cache || !workspace) {
+  const bool static_ws = workspace == nullptr;
+  if (!out || !src || !packed || !kv_cache) {
     set_err(err, "NULL argument");
     return KIE_ERR_INVALID_ARG;
   }
@@ -261,7 +300,7 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
   // 256-byte boundary, so that every cache row (128 or 256 bytes) and every workspace piece owns
   // whole cache lines: a row appended by one workgroup is never in a line another workgroup
   // read earlier in the same launch.
-  if (!aligned16(packed) || !aligned256(kv_cache) || !aligned256(workspace)) {
+  if (!aligned16(packed) || !aligned256(kv_cache) || (!static_ws && !aligned256(workspace))) {
     set_err(err, "packed must be 16-byte aligned, kv_cache and workspace 256-byte aligned");
     return KIE_ERR_INVALID_ARG;
   }
@@ -341,10 +380,25 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
     return KIE_ERR_UNSUPPORTED;
   }
 
+  const Workspace wso = workspace_layout(s, !static_ws);
+  if (static_ws) {
+    if (wso.end > (int64_t)KIE_STATIC_WORKSPACE_MAX) {
+      set_err(err, "this configuration needs a %lld-byte workspace; the static workspace holds %llu bytes",
+              (long long)wso.end, (unsigned long long)KIE_STATIC_WORKSPACE_MAX);
+      return KIE_ERR_CAPACITY;
+    }
+    uint8_t* ws = nullptr;
+    HIP_TRY(err, hipSetDevice(dev));
+    st = static_workspace(dev, &ws, err);
+    if (st != KIE_OK) return st;
+    workspace = ws;
+  }
+
   kie_ctx* c = new kie_ctx();
   c->s = s;
   c->exo = exch_layout(s);
-  c->wso = workspace_layout(s);
+  c->wso = wso;
+  c->static_ws = static_ws;
   c->device = dev;
   c->stream = (hipStream_t)hip_stream;
   c->packed = (uint8_t*)packed;
@@ -364,15 +418,6 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
   c->skew = 0;
   c->abort_dev = nullptr;
   if (w8) c->wscale_host.assign(src->weight_scales, src->weight_scales + (size_t)L * 7 + 1);
-  c->wbase_host.resize((size_t)s.nwg * kWaves + 1);
-  int64_t acc = 0;
-  for (int w = 0; w < s.nwg; ++w) {
-    for (int v = 0; v < kWaves; ++v) {
-      c->wbase_host[(size_t)w * kWaves + v] = acc;
-      acc += pk_stream_tiles(s, w8, w, v);
-    }
-  }
-  c->wbase_host[(size_t)s.nwg * kWaves] = acc;
 
   auto fail = [&](const char* what, hipError_t e) {
     set_err(err, "%s: %s", what, hipGetErrorString(e));
@@ -381,13 +426,13 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
   };
   hipError_t e;
   hipStream_t stm = c->stream;
-  // workspace: exchange words and error word to zero, RoPE table, stream bases, norm gains
-  if ((e = hipMemsetAsync(c->ws, 0, (size_t)c->wso.end, stm)) != hipSuccess) return fail("clear workspace", e);
+  // workspace: exchange words and error word to zero, RoPE table, stream bases, norm gains, all by
+  // kernels and device-to-device copies on the context's stream (no host staging, no memset)
+  if ((e = launch_fill_zero(c->ws, c->wso.end, stm)) != hipSuccess) return fail("clear workspace", e);
   if ((e = launch_rope_table((float2*)(c->ws + c->wso.rope), s.max_seq, s.hd, s.theta, stm)) != hipSuccess)
     return fail("rope table", e);
-  if ((e = hipMemcpyAsync(c->ws + c->wso.wbase, c->wbase_host.data(), c->wbase_host.size() * 8,
-                          hipMemcpyHostToDevice, stm)) != hipSuccess)
-    return fail("copy stream bases", e);
+  if ((e = launch_stream_bases(s, w8, (int64_t*)(c->ws + c->wso.wbase), stm)) != hipSuccess)
+    return fail("stream bases", e);
   uint16_t* norms = (uint16_t*)(c->ws + c->wso.norms);
   for (int l = 0; l < L; ++l) {
     if ((e = hipMemcpyAsync(norms + (size_t)l * 2 * s.d, src->attn_norm[l], (size_t)s.d * 2, hipMemcpyDeviceToDevice,
@@ -400,11 +445,11 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
   if ((e = hipMemcpyAsync(norms + (size_t)L * 2 * s.d, src->final_norm, (size_t)s.d * 2, hipMemcpyDeviceToDevice,
                           stm)) != hipSuccess)
     return fail("copy norms", e);
-  // 8-bit weights: the matrix scales, from the context's own host copy (the caller's array may be
-  // freed when kie_create returns), ordered after the workspace clear on the same stream
-  if (w8 && (e = hipMemcpyAsync(c->ws + c->wso.wscale, c->wscale_host.data(), c->wscale_host.size() * 4,
-                                hipMemcpyHostToDevice, stm)) != hipSuccess)
-    return fail("copy weight scales", e);
+  // 8-bit weights: the matrix scales travel as kernel arguments (the caller's array may be freed
+  // when kie_create returns), ordered after the workspace clear on the same stream
+  if (w8 && (e = launch_set_floats((float*)(c->ws + c->wso.wscale), c->wscale_host.data(),
+                                   (int32_t)c->wscale_host.size(), stm)) != hipSuccess)
+    return fail("weight scales", e);
   // weights: per-WG token streams, then the embedding table
   const int64_t* wbase_dev = (const int64_t*)(c->ws + c->wso.wbase);
   for (int l = 0; l <= L; ++l) {
@@ -444,14 +489,44 @@ kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packe
   return KIE_OK;
 }
 
-void kie_destroy(kie_ctx* ctx) { delete ctx; }
+kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packed, void* kv_cache, void* workspace,
+                      void* hip_stream, kie_ctx** out) {
+  if (!workspace) {
+    if (out) *out = nullptr;
+    set_err(&g_create_error, "NULL argument");
+    return KIE_ERR_INVALID_ARG;
+  }
+  return create_impl(cfg, src, packed, kv_cache, workspace, hip_stream, out);
+}
+
+kie_status kie_create_static(const kie_config* cfg, const kie_weights* src, void* packed, void* kv_cache,
+                             void* hip_stream, kie_ctx** out) {
+  const kie_status st = create_impl(cfg, src, packed, kv_cache, nullptr, hip_stream, out);
+  if (st == KIE_OK) {
+    std::lock_guard<std::mutex> lk(g_static_mu);
+    g_static_owner[(*out)->device] = *out;
+  }
+  return st;
+}
+
+void kie_destroy(kie_ctx* ctx) {
+  if (ctx && ctx->static_ws) {
+    std::lock_guard<std::mutex> lk(g_static_mu);
+    if (g_static_owner[ctx->device] == ctx) g_static_owner[ctx->device] = nullptr;
+  }
+  delete ctx;
+}
 
 int32_t kie_position(const kie_ctx* ctx) { return ctx ? ctx->pos : -1; }
 
 kie_status kie_reset(kie_ctx* ctx) {
   if (!ctx) return KIE_ERR_INVALID_ARG;
+  if (!static_owner_ok(ctx)) {
+    set_err(&ctx->last_error, "another context now uses this GPU's static workspace");
+    return KIE_ERR_STATE;
+  }
   HIP_TRY(&ctx->last_error, hipSetDevice(ctx->device));
-  HIP_TRY(&ctx->last_error, hipMemsetAsync(ctx->ws + ctx->wso.err, 0, 4, ctx->stream));
+  HIP_TRY(&ctx->last_error, launch_fill_zero(ctx->ws + ctx->wso.err, 4, ctx->stream));
   ctx->pos = 0;
   ctx->bad_state = false;
   ctx->last_error.clear();
@@ -560,6 +635,10 @@ static kie_status launch(kie_ctx* ctx, const int32_t* first, int32_t n, const in
     set_err(&ctx->last_error, "context holds a device error; call kie_reset");
     return KIE_ERR_STATE;
   }
+  if (!static_owner_ok(ctx)) {
+    set_err(&ctx->last_error, "another context now uses this GPU's static workspace");
+    return KIE_ERR_STATE;
+  }
   if (!first || n <= 0) {
     set_err(&ctx->last_error, "first token pointer is NULL or n <= 0");
     return KIE_ERR_INVALID_ARG;
@@ -632,10 +711,10 @@ kie_status kie_prefill(kie_ctx* ctx, const int32_t* tokens_dev, int32_t n_tokens
     set_err(&ctx->last_error, "position %d + %d tokens exceeds max_seq_len %d", ctx->pos, n_tokens, ctx->s.max_seq);
     return KIE_ERR_CAPACITY;
   }
-  // mixture of experts and 8-bit weights: every position through the decode program,
-  // teacher-forced (position i + 1 processes tokens[i + 1]); the LM head and the sampler run on the
-  // last one only
-  if (ctx->s.moe() || ctx->w8)
+  // mixture of experts, 8-bit weights, and contexts on the static workspace (which has no room for
+  // the matrix-core pass's scratch): every position through the decode program, teacher-forced
+  // (position i + 1 processes tokens[i + 1]); the LM head and the sampler run on the last one only
+  if (ctx->s.moe() || ctx->w8 || ctx->static_ws)
     return launch(ctx, tokens_dev, n_tokens, tokens_dev + 1, nullptr, first_token_dev, last_logits_dev, 1, sampling);
   // all but the last prompt position: every layer as GEMMs on the matrix cores (K/V rows only)
   if (n_tokens > 1) {

@@ -262,7 +262,9 @@ constexpr int kTraceWords = 64;  // per wave: cycle counters of a KIE_TRACE buil
                                  // hop timeline of one sampled layer (32..63, wave 0 only)
 constexpr int kTraceHop = 32;    // first word of the hop timeline
 KIE_HD int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
-KIE_HD Workspace workspace_layout(const Shape& s) {
+// prefill == false: without the matrix-core prompt pass's scratch (a context whose prompt runs
+// through the decode program); px .. pattn are then empty pieces at the end of the rest.
+KIE_HD Workspace workspace_layout(const Shape& s, bool prefill = true) {
   Workspace w;
   int64_t o = 0;
   w.exch = o; o = align256(o + exch_layout(s).end * 8);
@@ -271,6 +273,11 @@ KIE_HD Workspace workspace_layout(const Shape& s) {
   w.err = o; o = align256(o + 64);
   w.norms = o; o = align256(o + ((int64_t)s.L * 2 + 1) * s.d * 2);
   w.trace = o; o = align256(o + (int64_t)s.nwg * kWaves * kTraceWords * 8);
+  w.wscale = o; o = align256(o + ((int64_t)s.L * 7 + 1) * 4);  // 8-bit weights: the matrix scales
+  if (!prefill) {
+    w.px = w.pa3 = w.ph2 = w.pc = w.pq = w.pattn = w.end = o;
+    return w;
+  }
   w.px = o; o = align256(o + (int64_t)kPrefillChunk * s.d * 4);
   w.pa3 = o; o = align256(o + (int64_t)2 * kPrefillChunk * prefill_kmax(s) * 2);
   w.ph2 = o; o = align256(o + (int64_t)2 * kPrefillChunk * s.F * 2);
@@ -278,7 +285,6 @@ KIE_HD Workspace workspace_layout(const Shape& s) {
   w.pq = o; o = align256(o + (int64_t)kPrefillChunk * s.qdim() * 4);
   w.pattn = o;
   if (prefill_attn_segs(s) > 1) o = align256(o + (int64_t)prefill_attn_segs(s) * kPrefillChunk * s.nq * (s.hd + 2) * 4);
-  w.wscale = o; o = align256(o + ((int64_t)s.L * 7 + 1) * 4);  // 8-bit weights: the matrix scales
   w.end = o;
   return w;
 }

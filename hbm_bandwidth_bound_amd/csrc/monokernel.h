@@ -72,5 +72,14 @@ struct PackArgs {
 hipError_t launch_pack_layer(const PackArgs& a, hipStream_t st);
 hipError_t launch_pack_experts(const PackArgs& a, hipStream_t st);
 hipError_t launch_rope_table(float2* rope, int32_t max_seq, int32_t hd, float theta, hipStream_t st);
+hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t st);
+hipError_t launch_stream_bases(const Shape& s, bool w8, int64_t* wbase, hipStream_t st);
+constexpr int32_t kFloatChunk = 256;
+struct FloatChunk {
+  float* dst;
+  int32_t n;
+  float v[kFloatChunk];
+};
+hipError_t launch_set_floats(float* dst, const float* src, int32_t n, hipStream_t st);
 
 }  // namespace kie

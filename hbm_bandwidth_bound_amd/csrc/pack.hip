@@ -128,6 +128,79 @@ hipError_t launch_pack_experts(const PackArgs& a, hipStream_t st) {
 }
 
 // rope[p][i] = (cos, sin) of p * theta^(-2i/hd), angle in fp64, rounded to fp32
+// Zero `bytes` bytes at p (16-byte aligned, bytes a multiple of 4): 16-byte stores for the body,
+// then 4-byte stores. A kernel rather than a memset, so that the set-up can be captured in a graph.
+__global__ void __launch_bounds__(256) fill_zero_kernel(uint8_t* p, int64_t bytes) {
+  const int64_t n16 = bytes / 16;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    ((v4u*)p)[i] = v4u{0u, 0u, 0u, 0u};
+  const int64_t t = n16 * 16 + ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (t < bytes) *(uint32_t*)(p + t) = 0u;
+}
+hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t st) {
+  if (bytes <= 0) return hipSuccess;
+  int64_t blocks = (bytes / 16 + 255) / 256;
+  blocks = blocks < 1 ? 1 : (blocks > 4096 ? 4096 : blocks);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((uint32_t)blocks), dim3(256), 0, st, (uint8_t*)p, bytes);
+  return hipGetLastError();
+}
+
+// First tile of every wave's stream in the packed image (an exclusive prefix sum of the stream
+// lengths in (WG, wave) order) and the total, wbase[nwg * 8]. One block: each thread sums a run of
+// consecutive streams, the block scans the run totals.
+template <int TK>
+__global__ void __launch_bounds__(1024) stream_bases_kernel(Shape s, int64_t* wbase) {
+  __shared__ int64_t part[1024];
+  const int32_t n = s.nwg * kWaves;
+  const int32_t per = (n + 1023) / 1024;
+  const int32_t b0 = threadIdx.x * per, b1 = b0 + per < n ? b0 + per : n;
+  int64_t sum = 0;
+  for (int32_t i = b0; i < b1; ++i) sum += stream_tiles<TK>(s, i / kWaves, i % kWaves);
+  part[threadIdx.x] = sum;
+  __syncthreads();
+  if (threadIdx.x == 0) {  // 1024 run totals, in order
+    int64_t acc = 0;
+    for (int i = 0; i < 1024; ++i) {
+      const int64_t x = part[i];
+      part[i] = acc;
+      acc += x;
+    }
+    wbase[n] = acc;
+  }
+  __syncthreads();
+  int64_t acc = part[threadIdx.x];
+  for (int32_t i = b0; i < b1; ++i) {
+    wbase[i] = acc;
+    acc += stream_tiles<TK>(s, i / kWaves, i % kWaves);
+  }
+}
+hipError_t launch_stream_bases(const Shape& s, bool w8, int64_t* wbase, hipStream_t st) {
+  if (w8)
+    hipLaunchKernelGGL(stream_bases_kernel<2 * kTileK>, dim3(1), dim3(1024), 0, st, s, wbase);
+  else
+    hipLaunchKernelGGL(stream_bases_kernel<kTileK>, dim3(1), dim3(1024), 0, st, s, wbase);
+  return hipGetLastError();
+}
+
+// Host floats to device memory through kernel arguments (no host staging, capturable): chunks of
+// up to kFloatChunk values.
+__global__ void set_floats_kernel(FloatChunk c) {
+  if ((int32_t)threadIdx.x < c.n) c.dst[threadIdx.x] = c.v[threadIdx.x];
+}
+hipError_t launch_set_floats(float* dst, const float* src, int32_t n, hipStream_t st) {
+  for (int32_t i = 0; i < n; i += kFloatChunk) {
+    FloatChunk c;
+    c.dst = dst + i;
+    c.n = n - i < kFloatChunk ? n - i : kFloatChunk;
+    for (int32_t j = 0; j < c.n; ++j) c.v[j] = src[i + j];
+    hipLaunchKernelGGL(set_floats_kernel, dim3(1), dim3(kFloatChunk), 0, st, c);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 __global__ void rope_table_kernel(float2* rope, int32_t max_seq, int32_t hd, float theta) {
   const int32_t half = hd / 2;
   const int64_t n = (int64_t)max_seq * half;

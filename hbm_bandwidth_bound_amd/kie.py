@@ -73,6 +73,8 @@ def load() -> C.CDLL:
     lib.kie_workspace_bytes.restype = C.c_size_t
     lib.kie_create.argtypes = [cfgp, C.POINTER(kie_weights), vp, vp, vp, vp, C.POINTER(vp)]
     lib.kie_create.restype = C.c_int32
+    lib.kie_create_static.argtypes = [cfgp, C.POINTER(kie_weights), vp, vp, vp, C.POINTER(vp)]
+    lib.kie_create_static.restype = C.c_int32
     lib.kie_prefill.argtypes = [vp, vp, C.c_int32, vp, vp, C.POINTER(kie_sampling)]
     lib.kie_prefill.restype = C.c_int32
     lib.kie_decode_step.argtypes = [vp, vp, C.POINTER(kie_sampling), vp, vp]
@@ -140,10 +142,10 @@ class Engine:
     w_gate/w_up/w_down). An 8-bit model (``model.weight_format == 1``) has uint8 code tensors for
     wq, wk, wv, wo, w_gate, w_up, w_down and lm_head, and ``weights["w_scale"]``: the
     n_layers * 7 + 1 fp32 matrix scales as a host array. The packed image, KV cache and workspace are allocated here as torch
-    tensors.
+    tensors (no workspace with ``static_workspace=True``: kie_create_static).
     """
 
-    def __init__(self, model, weights: Dict[str, object], max_seq: int, stream=None):
+    def __init__(self, model, weights: Dict[str, object], max_seq: int, stream=None, static_workspace=False):
         import torch
         self.torch = torch
         self.lib = load()
@@ -159,7 +161,8 @@ class Engine:
             raise KieError(-2, "configuration rejected by the library: " + lib.kie_last_error(None).decode())
         self.packed = torch.empty(nb_packed, dtype=torch.uint8, device=dev)
         self.kv = torch.empty(nb_kv // 2, dtype=torch.int16, device=dev)
-        self.workspace = torch.empty(nb_ws, dtype=torch.uint8, device=dev)
+        # static_workspace: kie_create_static, whose workspace is the library's own per-GPU array
+        self.workspace = None if static_workspace else torch.empty(nb_ws, dtype=torch.uint8, device=dev)
         self.stream = stream if stream is not None else torch.cuda.current_stream(dev)
         L = model.n_layers
 
@@ -190,8 +193,12 @@ class Engine:
                               *[fields[k] for k in _LAYER_KEYS], scp)
         self._keep = keep
         ctx = C.c_void_p()
-        st = lib.kie_create(C.byref(self.cfg), C.byref(self._w), _ptr(self.packed), _ptr(self.kv),
-                            _ptr(self.workspace), C.c_void_p(self.stream.cuda_stream), C.byref(ctx))
+        if static_workspace:
+            st = lib.kie_create_static(C.byref(self.cfg), C.byref(self._w), _ptr(self.packed), _ptr(self.kv),
+                                       C.c_void_p(self.stream.cuda_stream), C.byref(ctx))
+        else:
+            st = lib.kie_create(C.byref(self.cfg), C.byref(self._w), _ptr(self.packed), _ptr(self.kv),
+                                _ptr(self.workspace), C.c_void_p(self.stream.cuda_stream), C.byref(ctx))
         _check(lib, st, None)
         self.ctx = ctx
         # the packing reads the source weights: keep them until the first sync

@@ -141,6 +141,23 @@ size_t kie_workspace_bytes(const kie_config* cfg);
 kie_status kie_create(const kie_config* cfg, const kie_weights* src, void* packed, void* kv_cache,
                       void* workspace, void* hip_stream, kie_ctx** out);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): kie_create without the workspace argument. The workspace lives
+ * in a static device array of KIE_STATIC_WORKSPACE_MAX bytes inside the library, one per GPU,
+ * which each GPU the library runs on holds until the process ends. The call allocates no device
+ * memory: it clears the array with a kernel, fills its tables with kernels and device-to-device
+ * copies, and packs `src` into `packed` on hip_stream, like kie_create. Such a context runs its
+ * prompt through the decode program (kie_prefill), since the matrix-core prompt pass's scratch
+ * does not fit the array; everything else behaves as with kie_create. The array keeps the last
+ * call's contents and is shared by every context made this way on the GPU: the latest one owns
+ * it, and calls that enqueue work on an earlier one (kie_prefill, kie_decode_step, kie_generate,
+ * kie_reset) return KIE_ERR_STATE. Calls that overlap on one GPU race. Errors: as kie_create, and
+ * KIE_ERR_CAPACITY when the configuration's workspace (without the prompt-pass scratch) exceeds
+ * KIE_STATIC_WORKSPACE_MAX. */
+#define KIE_STATIC_WORKSPACE_MAX (64u << 20)
+kie_status kie_create_static(const kie_config* cfg, const kie_weights* src, void* packed, void* kv_cache,
+                             void* hip_stream, kie_ctx** out);
+
 /* The prompt pass: time to first token is a metric of its own, separate from the per-token decode
  * speed (aikraft.ru «3000 токенов в секунду…», §01), and processing a long prompt is bound by
  * arithmetic rather than by memory bandwidth (zdabc.icu, 《Kog 推理引擎：不砍精度，单请求冲到 3000
