@@ -44,6 +44,9 @@ constexpr int kBatch = 8;    // tile slots per batch
 constexpr int kMaxWG = 1024;
 constexpr int kMaxUnits = 2048;  // units of one stage per WG (LDS partial sums)
 constexpr int kMaxTopK = 64;     // largest k of top-k sampling
+// Exchange words each thread of the decode kernel has in flight per pass of the FFN-width gather
+// (the other gathers take 8): 16 * 512 covers the FFN widths of the models here in one pass.
+constexpr int kGatherH = 16;
 
 enum Stage : int { ST_QKV = 0, ST_O = 1, ST_RT = 2, ST_GU = 3, ST_DN = 4, ST_LM = 5, ST_COUNT = 6 };
 constexpr int kMaxActive = 8;  // most experts routed per token

@@ -61,17 +61,31 @@ constexpr int kHopStep = 8, kHopLayer = 12;
 enum HopEvent : int {
   H_QKV_IN = 0, H_QKV_PUB = 1, H_ATT_IN = 2, H_ATT_PUB = 3, H_MERGE_PUB = 4, H_O_GOT = 5, H_O_IN = 6,
   H_XA_PUB = 7, H_XA_GOT = 8, H_GU_IN = 9, H_H_PUB = 10, H_H_GOT = 11, H_DN_IN = 12, H_XF_PUB = 13,
-  H_XF_GOT = 14, H_NORM_DONE = 15
+  H_XF_GOT = 14, H_NORM_DONE = 15, H_ATT_ALLQ = 16, H_ATT_DONE = 17, H_ATT_COMB = 18
 };
+// GEMV batches of the sampled layer: 2 b = batch b taken, 2 b + 1 = reduced (wave 0's batches;
+// at most 16), stored after the events.
+// The stamps go to a small LDS area (kHopWords words) and are copied to the trace words of waves 0
+// (events) and 1 (batches) when the kernel ends, so that taking them adds no vector-memory
+// operation that the kernel's own waits would have to drain.
 #if defined(KIE_TRACE) || defined(KIE_TRACE_HOPS)
+constexpr int kHopWords = 64;
 #define TR_HOP(K, ev)                                                                                     \
   do {                                                                                                    \
     if ((K).hop_on && (K).v == 0) /* wave-uniform: every lane stores the same time */                      \
-      (K).P.trace[((int64_t)(K).w * kWaves) * kTraceWords + kTraceHop + (ev)] = now_ticks();              \
+      *(volatile uint64_t*)((K).L.hopt + (ev)) = now_ticks();                                             \
+  } while (0)
+#define TR_BATCH(K, ev)                                                                                   \
+  do {                                                                                                    \
+    if ((K).v == 0 && (ev) < 32) *(volatile uint64_t*)((K).L.hopt + 32 + (ev)) = now_ticks();            \
   } while (0)
 #else
+constexpr int kHopWords = 0;
 #define TR_HOP(K, ev) \
   do {                \
+  } while (0)
+#define TR_BATCH(K, ev) \
+  do {                  \
   } while (0)
 #endif
 enum TraceSlot : int {
@@ -109,6 +123,7 @@ struct Lds {
   int32_t* moe;    // mixture of experts: the layer's chosen experts [kMaxActive], then their
                    // routing weights [kMaxActive] (fp32 bits)
   uint8_t* xb;     // one extra weight batch per wave (kBatch tiles), or null where LDS is short
+  uint64_t* hopt;  // KIE_TRACE / KIE_TRACE_HOPS builds: the hop timeline stamps (kHopWords)
 };
 enum Ctl : int { C_ABORT = 0, C_COUNT = 4 };
 
@@ -151,7 +166,8 @@ constexpr int32_t kXbBytes = kWaves * kBatch * kTileBytes;
 __host__ __device__ inline int32_t moe_words(const Shape& s) { return s.moe() ? 2 * kMaxActive : 0; }
 template <int GC>
 __host__ __device__ inline int32_t lds_base_bytes_g(const Shape& s) {
-  return (merge_floats(s) + scr_floats_g<GC>(s) + (s.group() + 2) * s.hd + s.hd) * 4 + C_COUNT * 4 + moe_words(s) * 4;
+  return (merge_floats(s) + scr_floats_g<GC>(s) + (s.group() + 2) * s.hd + s.hd) * 4 + C_COUNT * 4 + moe_words(s) * 4 +
+         kHopWords * 8;
 }
 template <int GC>
 __host__ __device__ inline bool xb_fits_g(const Shape& s) { return lds_base_bytes_g<GC>(s) + kXbBytes <= kLdsCapacity; }
@@ -175,6 +191,8 @@ __device__ __forceinline__ Lds lds_map(uint8_t* smem, const Shape& s) {
   p += C_COUNT * 4;  // 16-byte aligned: every piece above is a multiple of 4 floats
   L.moe = (int32_t*)p;
   p += moe_words(s) * 4;
+  L.hopt = (uint64_t*)p;  // 16-byte aligned: the pieces above are multiples of 16 bytes
+  p += kHopWords * 8;
   L.xb = xb_fits_g<GC>(s) ? p : nullptr;
   return L;
 }
@@ -967,6 +985,7 @@ __device__ __forceinline__ void attention(WK& K, const Att& at, int32_t l, int32
     K.tr.add(T_FETCH, TR_NOW() - t0);
     TR_HOP(K, H_ATT_IN);
     bar();
+    TR_HOP(K, H_ATT_ALLQ);
   }
   const uint64_t ta = TR_NOW();
   const float scale = 1.4426950408889634f / sqrtf((float)HD);  // softmax in the exp2 domain
@@ -1179,6 +1198,7 @@ __device__ __forceinline__ void attention(WK& K, const Att& at, int32_t l, int32
       };
       update(cur_row(L.q + G * HD), cur_row(L.q + (G + 1) * HD), lpos == 0);
     }
+    TR_HOP(K, H_ATT_DONE);
     // combine the position rows of the wave (lanes with the same dims)
 #pragma unroll
     for (int off = LPP; off < kWave; off <<= 1) {
@@ -1236,6 +1256,7 @@ __device__ __forceinline__ void attention(WK& K, const Att& at, int32_t l, int32
       }
       st_x(part + e, tag_f(out, ep));
     }
+    TR_HOP(K, H_ATT_COMB);
   }
   // the WG whose chunk holds the current position appends its K/V rows to the cache
   if (at.has_p) {
@@ -1805,7 +1826,7 @@ __device__ __forceinline__ void decode(Wk<MOE, W8>& K) {
           });
           TR_HOP(K, H_H_PUB);
           K.issue_x();
-          K.template fetch_f32<16>(hx, s.F, L.act, ep, false);
+          K.template fetch_f32<kGatherH>(hx, s.F, L.act, ep, false);
           TR_HOP(K, H_H_GOT);
           st = ST_DN;
           bnd = B_DN;
@@ -1989,13 +2010,27 @@ __device__ __forceinline__ void decode(Wk<MOE, W8>& K) {
     }
   };
 
+#if defined(KIE_TRACE) || defined(KIE_TRACE_HOPS)
+  int32_t lbatch = 0;  // wave 0's batches of the current layer so far
+#endif
   while (true) {
     boundary();
     if (done) break;
     const uint64_t tg = TR_NOW();
     v4u cur[kBatch];
+#if defined(KIE_TRACE) || defined(KIE_TRACE_HOPS)
+    if (st == ST_QKV && b == 0) lbatch = 0;
+    const bool bt = step == kHopStep && l == kHopLayer && st != ST_LM;
+#endif
     K.take(cur);
+#if defined(KIE_TRACE) || defined(KIE_TRACE_HOPS)
+    if (bt) TR_BATCH(K, 2 * lbatch);
+#endif
     K.reduce_batch(K.geo_of(st), b, cur);
+#if defined(KIE_TRACE) || defined(KIE_TRACE_HOPS)
+    if (bt) TR_BATCH(K, 2 * lbatch + 1);
+    ++lbatch;
+#endif
     K.tr.add(T_GEMV, TR_NOW() - tg);
     K.tr.add(T_BATCHES, 1);
     --rem;
@@ -2004,6 +2039,13 @@ __device__ __forceinline__ void decode(Wk<MOE, W8>& K) {
   // a batch loaded into LDS past the launch's last step may still be in flight: the wave must
   // not end (and give up its LDS) before that load has landed
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#if defined(KIE_TRACE) || defined(KIE_TRACE_HOPS)
+  if (K.v == 0) {  // wave 0's stamps, to the trace words of waves 0 (events) and 1 (batches)
+    const int64_t base = (int64_t)K.w * kWaves * kTraceWords + kTraceHop;
+    if (K.lane < 32) P.trace[base + K.lane] = L.hopt[K.lane];
+    else P.trace[base + kTraceWords + (K.lane - 32)] = L.hopt[K.lane];
+  }
+#endif
   K.tr.add(T_TOTAL, TR_NOW() - t_start);
   K.tr.flush(P.trace + ((int64_t)K.w * kWaves + K.v) * kTraceWords, K.lane);
 }
@@ -2014,6 +2056,7 @@ __device__ __forceinline__ void decode(Wk<MOE, W8>& K) {
 #define KIE_KERNEL_BODY(G, HD, MOE, W8)                                     \
   const Lds L = lds_map<G>(kie_smem, P.s);                                 \
   if (threadIdx.x < C_COUNT) L.ctl[threadIdx.x] = 0;                       \
+  if (threadIdx.x < kHopWords) L.hopt[threadIdx.x] = 0;                    \
   __syncthreads();                                                         \
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);    \
   Wk<MOE, W8> K(P, L, blockIdx.x, wave, threadIdx.x % kWave);              \
