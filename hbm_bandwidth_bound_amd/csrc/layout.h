@@ -89,23 +89,65 @@ struct Shape {
 KIE_HD int32_t split_begin(int64_t n, int32_t nwg, int32_t w) { return (int32_t)((n * w) / nwg); }
 KIE_HD int32_t split_end(int64_t n, int32_t nwg, int32_t w) { return (int32_t)((n * (w + 1)) / nwg); }
 
+// Chiplet-major order of the workgroups. The dispatcher hands workgroup w to chiplet (XCD) w mod 8,
+// so rank(w) = (w mod 8) * (nwg / 8) + w / 8 numbers the workgroups of chiplet 0 first, then those of
+// chiplet 1, and so on (the identity where nwg is not a multiple of 8). Work that is split over the
+// ranks in order keeps neighbouring shares on one chiplet. Placement only: any bijection is correct.
+constexpr int kXcds = 8;
+KIE_HD int32_t xcd_rank(int32_t nwg, int32_t w) {
+  return nwg % kXcds ? w : (w % kXcds) * (nwg / kXcds) + w / kXcds;
+}
+KIE_HD int32_t xcd_wg(int32_t nwg, int32_t r) {  // the inverse of xcd_rank
+  return nwg % kXcds ? r : (r % (nwg / kXcds)) * kXcds + r / (nwg / kXcds);
+}
+
 // k-tiles per unit for a row of kt tiles
 KIE_HD int32_t unit_tiles(int32_t kt) { return kt % 8 == 0 ? 8 : (kt % 4 == 0 ? 4 : (kt % 2 == 0 ? 2 : 1)); }
 
 // One stage of one WG: its pairs and how they are cut into units and batches.
 struct StageGeo {
-  int32_t pb, np;   // first global pair, pairs owned
+  int32_t pb, np;   // first position, positions owned (a position is a pair; see stage_pair)
   int32_t kt, ks;   // k-tiles per pair, per unit
   int32_t S;        // units per pair
   int32_t upb;      // units per batch (8 / ks)
   int32_t nu;       // units of the WG (np * S)
 };
+// The QKV stage orders its pairs by KV group -- the query heads of group j, then K head j, then V
+// head j -- and splits them over the workgroups in chiplet-major order: with 8 KV groups and a
+// multiple of 8 workgroups, group j is computed on chiplet j, where the attention of KV head j
+// runs (att_info), so the exchange of its queries, key and value stays within one chiplet's L2.
+// Position p of the QKV stage is pair qkv_pair(p); the other stages take pair p at position p.
+KIE_HD int32_t qkv_pair(const Shape& s, int32_t p) {
+  const int32_t half = s.hd / 2, G = s.group();
+  const int32_t per = (G + 2) * half;  // pairs of one KV group
+  const int32_t j = p / per, t = p % per, slot = t / half;
+  const int32_t hs = slot < G ? j * G + slot : (slot == G ? s.nq + j : s.nq + s.nkv + j);
+  return hs * half + t % half;
+}
+KIE_HD int32_t qkv_position(const Shape& s, int32_t gp) {  // the inverse of qkv_pair
+  const int32_t half = s.hd / 2, G = s.group();
+  const int32_t hs = gp / half, i = gp % half;
+  int32_t j, slot;
+  if (hs < s.nq) {
+    j = hs / G;
+    slot = hs % G;
+  } else if (hs < s.nq + s.nkv) {
+    j = hs - s.nq;
+    slot = G;
+  } else {
+    j = hs - s.nq - s.nkv;
+    slot = G + 1;
+  }
+  return j * (G + 2) * half + slot * half + i;
+}
+KIE_HD int32_t stage_pair(const Shape& s, int st, int32_t p) { return st == ST_QKV ? qkv_pair(s, p) : p; }
 template <int TK = kTileK>
 KIE_HD StageGeo stage_geo(const Shape& s, int st, int32_t w) {
   StageGeo g;
   const int32_t n = s.stage_pairs(st);
-  g.pb = split_begin(n, s.nwg, w);
-  g.np = split_end(n, s.nwg, w) - g.pb;
+  const int32_t r = st == ST_QKV ? xcd_rank(s.nwg, w) : w;
+  g.pb = split_begin(n, s.nwg, r);
+  g.np = split_end(n, s.nwg, r) - g.pb;
   g.kt = s.stage_kt<TK>(st);
   g.ks = unit_tiles(g.kt);
   g.S = g.kt / g.ks;
@@ -204,10 +246,12 @@ KIE_HD int32_t att_chunk_len(const Shape& s, int32_t n) {
   cs = ((cs + ppt - 1) / ppt) * ppt;
   return cs < ppt ? ppt : cs;
 }
-// merge units: (query head, slice of kMergeDims dims)
+// merge units: (query head, slice of kMergeDims dims), split over the workgroups in chiplet-major
+// order (xcd_rank), so that the units of KV group j's query heads sit on chiplet j with that
+// group's attention partials. merge_unit_rank(u) is the rank of unit u's workgroup.
 constexpr int kMergeDims = 8;
 KIE_HD int32_t merge_units(const Shape& s) { return s.nq * (s.hd / kMergeDims); }
-KIE_HD int32_t merge_unit_wg(const Shape& s, int32_t u) { return (int32_t)(((int64_t)u * s.nwg) / merge_units(s)); }
+KIE_HD int32_t merge_unit_rank(const Shape& s, int32_t u) { return (int32_t)(((int64_t)u * s.nwg) / merge_units(s)); }
 
 // ---------------------------------------------------------------------------------------------
 // Exchange buffers (64-bit tagged words: value bits << 32 | epoch), per layer, in the workspace.
@@ -320,11 +364,12 @@ KIE_HD int64_t packed_embed_offset(const Shape& s) {
   return (packed_stream_tiles<TK>(s) + expert_tiles(s)) * kTileBytes;
 }
 
-// Owner WG of global pair gp of a stage with n pairs (the inverse of the even split).
-KIE_HD int32_t pair_owner(int64_t n, int32_t nwg, int32_t gp) {
-  int32_t w = (int32_t)(((int64_t)gp * nwg) / n);
-  while (w + 1 < nwg && split_begin(n, nwg, w + 1) <= gp) ++w;
-  while (w > 0 && split_begin(n, nwg, w) > gp) --w;
+// The share (rank or WG) owning position p of a stage with n positions (the inverse of the even
+// split).
+KIE_HD int32_t pair_owner(int64_t n, int32_t nwg, int32_t p) {
+  int32_t w = (int32_t)(((int64_t)p * nwg) / n);
+  while (w + 1 < nwg && split_begin(n, nwg, w + 1) <= p) ++w;
+  while (w > 0 && split_begin(n, nwg, w) > p) --w;
   return w;
 }
 // Where k-tile kt of pair gp of stage st in layer l lives in the packed image (in tiles); the LM
@@ -332,9 +377,11 @@ KIE_HD int32_t pair_owner(int64_t n, int32_t nwg, int32_t gp) {
 // inverts the packer's placement, so that a kernel can read the weights of any row in place.
 // (Stages in the fixed streams only.)
 KIE_HD int64_t packed_tile(const Shape& s, const int64_t* wbase, int st, int32_t l, int32_t gp, int32_t kt) {
-  const int32_t w = pair_owner(s.stage_pairs(st), s.nwg, gp);
+  const int32_t p = st == ST_QKV ? qkv_position(s, gp) : gp;
+  const int32_t owner = pair_owner(s.stage_pairs(st), s.nwg, p);
+  const int32_t w = st == ST_QKV ? xcd_wg(s.nwg, owner) : owner;
   const StageGeo g = stage_geo(s, st, w);
-  const int32_t u = (gp - g.pb) * g.S + kt / g.ks;
+  const int32_t u = (p - g.pb) * g.S + kt / g.ks;
   const int32_t v = u % kWaves, m = u / kWaves;
   const int32_t b = m / g.upb, slot = (m % g.upb) * g.ks + kt % g.ks;
   int64_t bt;

@@ -761,8 +761,9 @@ struct Wk {
   }
   // After the stage's barrier: pair lp's outputs (the sum of its S units in a fixed order) go to
   // fin(global pair, ya, yb).
-  template <typename Fin>
-  __device__ __forceinline__ void finalize(const StageGeo& gs, Fin fin) {
+  template <int ST, typename Fin>
+  __device__ __forceinline__ void finalize(Fin fin) {
+    const StageGeo& gs = g[ST];
     const uint64_t t0 = TR_NOW();
     for (int32_t lp = tid; lp < gs.np; lp += kThreads) {
       float ya = 0.f, yb = 0.f;
@@ -770,7 +771,7 @@ struct Wk {
         ya += L.part[2 * (lp * gs.S + k)];
         yb += L.part[2 * (lp * gs.S + k) + 1];
       }
-      fin(gs.pb + lp, ya, yb);
+      fin(stage_pair(P.s, ST, gs.pb + lp), ya, yb);
     }
     tr.add(T_FIN, TR_NOW() - t0);
   }
@@ -1687,7 +1688,7 @@ __device__ __forceinline__ void decode(Wk<MOE, W8>& K) {
           uint64_t tr0 = TR_NOW();
           bar();
           uint64_t* rx = ex + X.rt + (int64_t)l * s.E;
-          K.finalize(K.g[ST_RT], [&](int32_t gp, float ya, float yb) {
+          K.template finalize<ST_RT>([&](int32_t gp, float ya, float yb) {
             st_x(rx + 2 * gp, tag_f(ya, ep));
             st_x(rx + 2 * gp + 1, tag_f(yb, ep));
           });
@@ -1731,7 +1732,7 @@ __device__ __forceinline__ void decode(Wk<MOE, W8>& K) {
             sk = P.wscale[l * 7 + 1];
             sv = P.wscale[l * 7 + 2];
           }
-          K.finalize(K.g[ST_QKV], [&](int32_t gp, float ya, float yb) {
+          K.template finalize<ST_QKV>([&](int32_t gp, float ya, float yb) {
             const int32_t half = s.hd / 2;
             const int32_t hs = gp / half, i = gp % half;
             if constexpr (W8) {  // the matrix's scale times the codes' dot product
@@ -1766,12 +1767,13 @@ __device__ __forceinline__ void decode(Wk<MOE, W8>& K) {
           {
             const uint64_t tm = TR_NOW();
             const int32_t nu = merge_units(s);
-            const int32_t u0 = (int32_t)(((int64_t)K.w * nu + s.nwg - 1) / s.nwg);
+            const int32_t rk = xcd_rank(s.nwg, K.w);
+            const int32_t u0 = (int32_t)(((int64_t)rk * nu + s.nwg - 1) / s.nwg);
             if constexpr (G >= 8) {  // several units per workgroup at these head counts: two at a time
-              for (int32_t u = u0; u < nu && merge_unit_wg(s, u) == K.w; u += 2)
-                merge_two_units(K, at, l, u, u + 1 < nu && merge_unit_wg(s, u + 1) == K.w, ep);
+              for (int32_t u = u0; u < nu && merge_unit_rank(s, u) == rk; u += 2)
+                merge_two_units(K, at, l, u, u + 1 < nu && merge_unit_rank(s, u + 1) == rk, ep);
             } else {
-              for (int32_t u = u0; u < nu && merge_unit_wg(s, u) == K.w; ++u) merge_unit(K, at, l, u, ep);
+              for (int32_t u = u0; u < nu && merge_unit_rank(s, u) == rk; ++u) merge_unit(K, at, l, u, ep);
             }
             K.tr.add(T_MERGE, TR_NOW() - tm);
           }
@@ -1792,7 +1794,7 @@ __device__ __forceinline__ void decode(Wk<MOE, W8>& K) {
           uint64_t* xa = ex + X.xa + (int64_t)l * s.d;
           K.prefetch_gain(P.norms + (int64_t)l * 2 * s.d + s.d);
           const float so = W8 ? P.wscale[l * 7 + 3] : 1.f;
-          K.finalize(K.g[ST_O], [&](int32_t gp, float ya, float yb) {
+          K.template finalize<ST_O>([&](int32_t gp, float ya, float yb) {
             if constexpr (W8) {
               ya *= so;
               yb *= so;
@@ -1815,7 +1817,7 @@ __device__ __forceinline__ void decode(Wk<MOE, W8>& K) {
           TR_HOP(K, H_GU_IN);
           uint64_t* hx = ex + X.h + (int64_t)l * s.F;
           const float sg = W8 ? P.wscale[l * 7 + 4] : 1.f, su = W8 ? P.wscale[l * 7 + 5] : 1.f;
-          K.finalize(K.g[ST_GU], [&](int32_t gp, float ya, float yb) {
+          K.template finalize<ST_GU>([&](int32_t gp, float ya, float yb) {
             if constexpr (W8) {
               ya *= sg;
               yb *= su;
@@ -1845,7 +1847,7 @@ __device__ __forceinline__ void decode(Wk<MOE, W8>& K) {
           uint64_t* xf = ex + X.xf + (int64_t)(l + 1) * s.d;
           K.prefetch_gain(P.norms + (l + 1 < s.L ? (int64_t)(l + 1) * 2 * s.d : (int64_t)s.L * 2 * s.d));
           const float sd = W8 ? P.wscale[l * 7 + 6] : 1.f;
-          K.finalize(K.g[ST_DN], [&](int32_t gp, float ya, float yb) {
+          K.template finalize<ST_DN>([&](int32_t gp, float ya, float yb) {
             if constexpr (W8) {
               ya *= sd;
               yb *= sd;
@@ -1903,7 +1905,7 @@ __device__ __forceinline__ void decode(Wk<MOE, W8>& K) {
             float* lo = P.logits_out ? P.logits_out + (P.lm_last_only ? 0 : (int64_t)step * s.V) : nullptr;
             const int32_t pb = K.g[ST_LM].pb;
             const float sl = W8 ? P.wscale[s.L * 7] : 1.f;
-            K.finalize(K.g[ST_LM], [&](int32_t gp, float ya, float yb) {
+            K.template finalize<ST_LM>([&](int32_t gp, float ya, float yb) {
               const int32_t ra = 2 * gp, rb = 2 * gp + 1;
               if constexpr (W8) {
                 ya *= sl;

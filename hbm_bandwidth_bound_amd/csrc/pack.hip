@@ -47,7 +47,7 @@ __global__ void __launch_bounds__(256) pack_layer_kernel(PackArgs a) {
       const int32_t lp = u / g.S, j = (u % g.S) * g.ks + tt;
       int mat;
       int32_t ra, rb;
-      pair_rows(s, st, g.pb + lp, &mat, &ra, &rb);
+      pair_rows(s, st, stage_pair(s, st, g.pb + lp), &mat, &ra, &rb);
       const uint16_t *ma, *mb;
       if (st == ST_QKV) {
         ma = mb = mat == 0 ? a.wq : (mat == 1 ? a.wk : a.wv);

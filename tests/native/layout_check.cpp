@@ -63,7 +63,33 @@ static int check(const Shape& s) {
       std::printf("pairs of stage %d do not add up\n", st);
       return 1;
     }
+    // positions map one-to-one onto pairs, and every position has exactly one owning workgroup
+    const int32_t n = s.stage_pairs(st);
+    std::vector<int> hit((size_t)n, 0), own((size_t)n, 0);
+    for (int32_t p = 0; p < n; ++p) {
+      const int32_t gp = stage_pair(s, st, p);
+      if (gp < 0 || gp >= n || (st == ST_QKV && qkv_position(s, gp) != p)) {
+        std::printf("stage %d: position %d maps to pair %d\n", st, p, gp);
+        return 1;
+      }
+      hit[(size_t)gp] += 1;
+    }
+    for (int32_t w = 0; w < s.nwg; ++w) {
+      const StageGeo g = stage_geo<TK>(s, st, w);
+      for (int32_t lp = 0; lp < g.np; ++lp) own[(size_t)(g.pb + lp)] += 1;
+    }
+    for (int32_t i = 0; i < n; ++i)
+      if (hit[(size_t)i] != 1 || own[(size_t)i] != 1) {
+        std::printf("stage %d: pair %d hit %d times, position %d owned %d times\n", st, i, hit[(size_t)i], i,
+                    own[(size_t)i]);
+        return 1;
+      }
   }
+  for (int32_t w = 0; w < s.nwg; ++w)
+    if (xcd_wg(s.nwg, xcd_rank(s.nwg, w)) != w || xcd_rank(s.nwg, w) < 0 || xcd_rank(s.nwg, w) >= s.nwg) {
+      std::printf("chiplet-major rank of workgroup %d does not invert\n", w);
+      return 1;
+    }
   // packed_tile inverts the placement: stream (w, v), batch b, slot sl of stage st in layer l
   std::vector<int64_t> wbase((size_t)s.nwg * kWaves + 1);
   int64_t acc = 0;
@@ -86,7 +112,7 @@ static int check(const Shape& s) {
             for (int32_t sl = 0; sl < kBatch; ++sl) {
               const int32_t u = v + kWaves * (b * g.upb + sl / g.ks);
               if (u >= g.nu) continue;
-              const int32_t gp = g.pb + u / g.S, kt = (u % g.S) * g.ks + sl % g.ks;
+              const int32_t gp = stage_pair(s, st, g.pb + u / g.S), kt = (u % g.S) * g.ks + sl % g.ks;
               if (TK != kTileK) continue;  // packed_tile serves the bf16 prompt pass only
               const int64_t got = packed_tile(s, wbase.data(), st, l, gp, kt);
               if (got != t0 + (int64_t)b * kBatch + sl) {
