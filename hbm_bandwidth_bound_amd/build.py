@@ -10,7 +10,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkie.so")
 SOURCES = ["api.cpp", "monokernel.hip", "kernels_hd64.hip", "kernels_hd128.hip", "kernels_moe.hip", "kernels_fp8.hip", "pack.hip",
-           "prefill.hip"]
+           "prefill.hip", "exchange_probe.hip"]
 
 # Packed fp32 instructions are disabled: the compiler may not form v_pk_* f32 ops from float code.
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",

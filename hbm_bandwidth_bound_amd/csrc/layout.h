@@ -89,10 +89,12 @@ struct Shape {
 KIE_HD int32_t split_begin(int64_t n, int32_t nwg, int32_t w) { return (int32_t)((n * w) / nwg); }
 KIE_HD int32_t split_end(int64_t n, int32_t nwg, int32_t w) { return (int32_t)((n * (w + 1)) / nwg); }
 
-// Chiplet-major order of the workgroups. The dispatcher hands workgroup w to chiplet (XCD) w mod 8,
-// so rank(w) = (w mod 8) * (nwg / 8) + w / 8 numbers the workgroups of chiplet 0 first, then those of
-// chiplet 1, and so on (the identity where nwg is not a multiple of 8). Work that is split over the
-// ranks in order keeps neighbouring shares on one chiplet. Placement only: any bijection is correct.
+// Chiplet-major order of the workgroups. The dispatcher hands consecutive workgroups to the 8
+// chiplets (XCDs) in turn, so the workgroups with one value of w mod 8 share a chiplet (which one
+// can change from launch to launch). rank(w) = (w mod 8) * (nwg / 8) + w / 8 numbers those of
+// residue 0 first, then those of residue 1, and so on (the identity where nwg is not a multiple of
+// 8): work split over the ranks in order keeps neighbouring shares on one chiplet. Placement only:
+// any bijection is correct.
 constexpr int kXcds = 8;
 KIE_HD int32_t xcd_rank(int32_t nwg, int32_t w) {
   return nwg % kXcds ? w : (w % kXcds) * (nwg / kXcds) + w / kXcds;
@@ -114,8 +116,8 @@ struct StageGeo {
 };
 // The QKV stage orders its pairs by KV group -- the query heads of group j, then K head j, then V
 // head j -- and splits them over the workgroups in chiplet-major order: with 8 KV groups and a
-// multiple of 8 workgroups, group j is computed on chiplet j, where the attention of KV head j
-// runs (att_info), so the exchange of its queries, key and value stays within one chiplet's L2.
+// multiple of 8 workgroups, group j is computed by the workgroups w = j mod 8, the chiplet where
+// the attention of KV head j runs (att_info), so its queries, key and value stay on one chiplet.
 // Position p of the QKV stage is pair qkv_pair(p); the other stages take pair p at position p.
 KIE_HD int32_t qkv_pair(const Shape& s, int32_t p) {
   const int32_t half = s.hd / 2, G = s.group();

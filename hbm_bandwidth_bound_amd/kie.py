@@ -109,6 +109,12 @@ def load() -> C.CDLL:
     lib.kie_stream_copy.restype = C.c_int32
     lib.kie_stream_read.argtypes = [vp, C.c_size_t, vp, vp]
     lib.kie_stream_read.restype = C.c_int32
+    lib.kie_probe_pingpong.argtypes = [C.c_int32, C.c_int32, C.c_int32, vp, vp, vp]
+    lib.kie_probe_pingpong.restype = C.c_int32
+    lib.kie_probe_allgather.argtypes = [C.c_int32, C.c_int32, C.c_int32, vp, vp, vp, vp, vp]
+    lib.kie_probe_allgather.restype = C.c_int32
+    lib.kie_probe_page_latency.argtypes = [C.c_int32, C.c_int32, C.c_int32, vp, vp, vp, vp, vp]
+    lib.kie_probe_page_latency.restype = C.c_int32
     _lib = lib
     return lib
 
