@@ -3,7 +3,8 @@
 
 Two steps:
 
-* ``run`` is the profiled program: the prompt pass, one ``kie_generate`` launch of ``--steps``
+* ``run`` is the profiled program: the prompt pass (or, with ``--synthetic-kv``, seeded cache rows
+  in its place), one ``kie_generate`` launch of ``--steps``
   tokens (the decode kernel dispatch that is measured), then one plain copy of ``--copy-mib`` MiB
   (``stream_copy_kernel``: reads and writes exactly that many bytes), the calibration dispatch.
   It is run twice under ``rocprofv3 --pmc``, once with ``FETCH_SIZE`` and once with
@@ -60,7 +61,18 @@ def run(args):
     P, K = wl.prompt_len, args.steps
     eng = Engine(m, w, P + K)
     prompt = torch.tensor(synth.prompt_ids(P, m.vocab_size, wl.prompt_seed), dtype=torch.int32, device=dev)
-    first = eng.prefill(prompt)
+    if args.synthetic_kv:
+        # the decode launch reads the same bytes whatever the cached rows hold: seeded bf16 rows of
+        # about the prompt's magnitude stand in for them, so that the profiled program has no
+        # prompt pass (tens of thousands of dispatches at long context)
+        g = torch.Generator(device=dev).manual_seed(wl.prompt_seed)
+        rows = torch.randn(eng.kv.numel(), generator=g, device=dev, dtype=torch.float32) * 0.5
+        eng.kv.copy_(rows.to(torch.bfloat16).view(torch.int16))
+        del rows
+        eng.set_position(P)
+        first = prompt[-1:].clone()
+    else:
+        first = eng.prefill(prompt)
     eng.sync()
     out = torch.empty(K, dtype=torch.int32, device=dev)
     eng.generate(first, K, out)
@@ -134,12 +146,13 @@ def summarize(args):
                 f"{K} decode steps in one launch)\n")
         f.write("# commands (from the repository root, each pass its own run):\n")
         filt = f"--kernel-include-regex '{args.kernel_regex}' " if args.kernel_regex else ""
+        syn = " --synthetic-kv" if args.synthetic_kv else ""
         for c, d in (("FETCH_SIZE", args.fetch), ("WRITE_SIZE", args.write)):
             f.write(f"#   rocprofv3 --pmc {c} {filt}--output-format csv -d {d} -o run -- python3 -m "
                     f"hbm_bandwidth_bound_amd.traffic_profile run --workload {wl.name} --steps {K} "
-                    f"--copy-mib {args.copy_mib}\n")
+                    f"--copy-mib {args.copy_mib}{syn}\n")
         f.write(f"#   python3 -m hbm_bandwidth_bound_amd.traffic_profile summarize --workload {wl.name} "
-                f"--steps {K} --copy-mib {args.copy_mib} --fetch {args.fetch} --write {args.write} --out {args.out}"
+                f"--steps {K} --copy-mib {args.copy_mib}{syn} --fetch {args.fetch} --write {args.write} --out {args.out}"
                 + (f" --kernel-regex '{args.kernel_regex}'" if args.kernel_regex else "") + "\n")
         for ln in lines:
             f.write(ln + "\n")
@@ -161,6 +174,8 @@ def main():
         p.add_argument("--workload", default="1.6b-1k")
         p.add_argument("--steps", type=int, default=64)
         p.add_argument("--copy-mib", type=int, default=1024)
+        p.add_argument("--synthetic-kv", action="store_true",
+                       help="no prompt pass: seeded rows stand in for the cached K/V of the prompt")
         if name == "summarize":
             p.add_argument("--fetch", required=True)
             p.add_argument("--write", required=True)
