@@ -181,10 +181,10 @@ def main():
     mm = traffic.matrix_weights(m) - m.vocab_size * m.d_model
     attn = 4 * m.n_layers * m.n_heads * m.head_dim * (P - 1) * P // 2
     prefill_flops = 2 * (P - 1) * mm + attn
-    if m.n_experts or m.weight_format:  # every prompt position runs through the decode program
+    if m.n_experts:  # every prompt position runs through the decode program
         prompt_pass = {"kind": "decode program, teacher-forced, one position after the other",
                        "positions_per_s": round(P / (ttft_ms * 1e-3), 1)}
-    else:
+    else:  # matrix-core GEMMs (8-bit codes widened to bf16 operands as they are read)
         prompt_pass = {"flops": prefill_flops, "tflops": round(prefill_flops / (ttft_ms * 1e-3) / 1e12, 1),
                        "frac_of_bf16_mfma_peak": round(prefill_flops / (ttft_ms * 1e-3) / 2.5e15, 4)}
 

@@ -711,10 +711,10 @@ kie_status kie_prefill(kie_ctx* ctx, const int32_t* tokens_dev, int32_t n_tokens
     set_err(&ctx->last_error, "position %d + %d tokens exceeds max_seq_len %d", ctx->pos, n_tokens, ctx->s.max_seq);
     return KIE_ERR_CAPACITY;
   }
-  // mixture of experts, 8-bit weights, and contexts on the static workspace (which has no room for
-  // the matrix-core pass's scratch): every position through the decode program, teacher-forced
+  // mixture of experts and contexts on the static workspace (which has no room for the
+  // matrix-core pass's scratch): every position through the decode program, teacher-forced
   // (position i + 1 processes tokens[i + 1]); the LM head and the sampler run on the last one only
-  if (ctx->s.moe() || ctx->w8 || ctx->static_ws)
+  if (ctx->s.moe() || ctx->static_ws)
     return launch(ctx, tokens_dev, n_tokens, tokens_dev + 1, nullptr, first_token_dev, last_logits_dev, 1, sampling);
   // all but the last prompt position: every layer as GEMMs on the matrix cores (K/V rows only)
   if (n_tokens > 1) {
@@ -723,7 +723,7 @@ kie_status kie_prefill(kie_ctx* ctx, const int32_t* tokens_dev, int32_t n_tokens
     a.s = ctx->s;
     a.packed = ctx->packed;
     a.wbase = (const int64_t*)(ctx->ws + ctx->wso.wbase);
-    a.embed = (const uint16_t*)(ctx->packed + packed_embed_offset(ctx->s));
+    a.embed = (const uint16_t*)(ctx->packed + pk_embed_offset(ctx->s, ctx->w8));
     a.norms = (const uint16_t*)(ctx->ws + ctx->wso.norms);
     a.rope = (const float2*)(ctx->ws + ctx->wso.rope);
     a.kv = ctx->kv;
@@ -736,6 +736,7 @@ kie_status kie_prefill(kie_ctx* ctx, const int32_t* tokens_dev, int32_t n_tokens
     a.c = (float*)(ctx->ws + ctx->wso.pc);
     a.q = (float*)(ctx->ws + ctx->wso.pq);
     a.attn_part = (float*)(ctx->ws + ctx->wso.pattn);
+    a.wscale = ctx->w8 ? (const float*)(ctx->ws + ctx->wso.wscale) : nullptr;
     HIP_TRY(&ctx->last_error, launch_prefill(a, ctx->pos, n_tokens - 1, ctx->stream));
     ctx->pos += n_tokens - 1;
   }

@@ -377,22 +377,23 @@ KIE_HD int32_t pair_owner(int64_t n, int32_t nwg, int32_t p) {
 // Where k-tile kt of pair gp of stage st in layer l lives in the packed image (in tiles); the LM
 // head is st == ST_LM (l ignored). wbase[w * kWaves + v] is the first tile of stream (w, v). This
 // inverts the packer's placement, so that a kernel can read the weights of any row in place.
-// (Stages in the fixed streams only.)
+// (Stages in the fixed streams only; TK as stage_geo: kTileK for bf16, 2 * kTileK for 8-bit.)
+template <int TK = kTileK>
 KIE_HD int64_t packed_tile(const Shape& s, const int64_t* wbase, int st, int32_t l, int32_t gp, int32_t kt) {
   const int32_t p = st == ST_QKV ? qkv_position(s, gp) : gp;
   const int32_t owner = pair_owner(s.stage_pairs(st), s.nwg, p);
   const int32_t w = st == ST_QKV ? xcd_wg(s.nwg, owner) : owner;
-  const StageGeo g = stage_geo(s, st, w);
+  const StageGeo g = stage_geo<TK>(s, st, w);
   const int32_t u = (p - g.pb) * g.S + kt / g.ks;
   const int32_t v = u % kWaves, m = u / kWaves;
   const int32_t b = m / g.upb, slot = (m % g.upb) * g.ks + kt % g.ks;
   int64_t bt;
   if (st == ST_LM) {
-    bt = (int64_t)s.L * layer_batches(s, w, v);
+    bt = (int64_t)s.L * layer_batches<TK>(s, w, v);
   } else {
-    bt = (int64_t)l * layer_batches(s, w, v);
+    bt = (int64_t)l * layer_batches<TK>(s, w, v);
     for (int st2 = ST_QKV; st2 < st; ++st2)
-      if (s.in_stream(st2)) bt += wave_batches(stage_geo(s, st2, w), v);
+      if (s.in_stream(st2)) bt += wave_batches(stage_geo<TK>(s, st2, w), v);
   }
   return wbase[w * kWaves + v] + (bt + b) * kBatch + slot;
 }

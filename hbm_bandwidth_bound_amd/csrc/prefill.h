@@ -26,6 +26,7 @@ struct PrefillArgs {
   float* c;                  // [chunk][nmax] split-K partial sums
   float* q;                  // [chunk][nq * hd] rotated queries
   float* attn_part;          // [segments][chunk][nq][hd + 2] partial attention states
+  const float* wscale;       // 8-bit weights: the matrix scales [L][7] (+ the LM head's); null for bf16
 };
 
 // What the GEMM does with its result C[i][n]:

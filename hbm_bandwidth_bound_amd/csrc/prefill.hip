@@ -91,7 +91,26 @@ __global__ void __launch_bounds__(256) prefill_norm_split_kernel(PrefillArgs a, 
 constexpr int kGemmM = 64, kGemmN = 128, kGemmKC = 128, kGemmParts = 2;
 constexpr int kALd = kGemmKC + 8;  // padded LDS row (bf16), spreads the rows over the banks
 
+// Eight e4m3fn codes (k .. k+3 in c0, k+4 .. k+7 in c1, lowest k in the lowest byte) as eight
+// bf16, exactly: each code widens exactly to fp32 (gfx950 pair conversion), and an e4m3 value
+// has 3 significand bits and an exponent inside bf16's range, so the fp32's upper half is it.
+typedef float v2f_t __attribute__((ext_vector_type(2)));
+template <bool HI>
+__device__ __forceinline__ uint32_t codes2_to_bf16(uint32_t c) {  // codes 0, 1 (or 2, 3 with HI)
+  const v2f_t f = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, HI);
+  return (__float_as_uint(f.x) >> 16) | (__float_as_uint(f.y) & 0xffff0000u);
+}
+__device__ __forceinline__ bf16x8 codes8_to_bf16(uint32_t c0, uint32_t c1) {
+  return __builtin_bit_cast(bf16x8, uint4{codes2_to_bf16<false>(c0), codes2_to_bf16<true>(c0),
+                                          codes2_to_bf16<false>(c1), codes2_to_bf16<true>(c1)});
+}
+
+// W8: the weights are e4m3fn codes (8-bit tiles: lane q holds row A's codes at k = 4q .. 4q+3
+// and 256 + 4q .. +3 of the tile's 512, then row B's at the same k), widened to bf16 as they are
+// read; the matrix's scale multiplies the products in the epilogue.
+template <bool W8>
 __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillArgs a, GemmStage g, int32_t pc) {
+  constexpr int TK = W8 ? 2 * kTileK : kTileK;  // weights of a row per tile
   constexpr int KSTEPS = kGemmKC / 32;
   constexpr int NB = kGemmN / 64;                                  // 16-row columns per wave
   constexpr int APER = kGemmParts * kGemmM * (kGemmKC / 8) / 256;  // 16-byte pieces per thread
@@ -122,7 +141,7 @@ __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillArgs a, GemmSt
     gp[nb] = nvalid[nb] ? n[nb] >> 1 : 0;
   }
   const int sel = nl & 1;  // row A or B of the pair (n and nl have the same parity)
-  const int32_t ks_unit = unit_tiles(a.s.stage_kt(g.st));
+  const int32_t ks_unit = unit_tiles(a.s.template stage_kt<TK>(g.st));
   int64_t tbase[NB] = {};  // first tile of the current unit of each column's pair
   f4 acc[4][NB];
 #pragma unroll
@@ -133,17 +152,25 @@ __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillArgs a, GemmSt
   uint2 w0[NB][KSTEPS], w1[NB][KSTEPS];
   uint4 av4[APER];
   auto fetch = [&](int32_t kc) {  // weight operands of chunk kc into w0/w1, activations into av4
-    const int32_t kt = kc / kTileK;
+    const int32_t kt = kc / TK;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      if (kc == kbeg || (kt % ks_unit == 0 && kc % kTileK == 0))
-        tbase[nb] = nvalid[nb] ? packed_tile(a.s, a.wbase, g.st, g.layer, gp[nb], kt - kt % ks_unit) : 0;
+      if (kc == kbeg || (kt % ks_unit == 0 && kc % TK == 0))
+        tbase[nb] = nvalid[nb] ? packed_tile<TK>(a.s, a.wbase, g.st, g.layer, gp[nb], kt - kt % ks_unit) : 0;
       const uint8_t* tp = a.packed + (tbase[nb] + kt % ks_unit) * kTileBytes + 8 * sel;
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        const int L = (kc % kTileK + ks * 32 + kg * 8) >> 2;  // tile lane holding k .. k+3
-        w0[nb][ks] = nvalid[nb] ? *(const uint2*)(tp + 16 * L) : uint2{0u, 0u};
-        w1[nb][ks] = nvalid[nb] ? *(const uint2*)(tp + 16 * (L + 1)) : uint2{0u, 0u};
+        if constexpr (W8) {  // codes k .. k+7 of row sel: words of tile lanes q and q + 1
+          const int kk = kc % TK + ks * 32 + kg * 8;
+          const uint8_t* pw = tp + 4 * (kk >> 8);  // the word of the tile's first or second 256
+          const int q = (kk & 255) >> 2;
+          w0[nb][ks] = nvalid[nb] ? uint2{*(const uint32_t*)(pw + 16 * q), *(const uint32_t*)(pw + 16 * (q + 1))}
+                                  : uint2{0u, 0u};
+        } else {
+          const int L = (kc % kTileK + ks * 32 + kg * 8) >> 2;  // tile lane holding k .. k+3
+          w0[nb][ks] = nvalid[nb] ? *(const uint2*)(tp + 16 * L) : uint2{0u, 0u};
+          w1[nb][ks] = nvalid[nb] ? *(const uint2*)(tp + 16 * (L + 1)) : uint2{0u, 0u};
+        }
       }
     }
 #pragma unroll
@@ -169,7 +196,8 @@ __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillArgs a, GemmSt
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks)
-        b[nb][ks] = __builtin_bit_cast(bf16x8, uint4{w0[nb][ks].x, w0[nb][ks].y, w1[nb][ks].x, w1[nb][ks].y});
+        b[nb][ks] = W8 ? codes8_to_bf16(w0[nb][ks].x, w0[nb][ks].y)
+                       : __builtin_bit_cast(bf16x8, uint4{w0[nb][ks].x, w0[nb][ks].y, w1[nb][ks].x, w1[nb][ks].y});
     __syncthreads();
     if (kc + kGemmKC < kend) fetch(kc + kGemmKC);  // in flight while this chunk is multiplied
 #pragma unroll
@@ -186,7 +214,11 @@ __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillArgs a, GemmSt
       }
     }
   }
+  // 8-bit: matrix m of this layer is its scale times the codes (scales [L][7]: wq, wk, wv, wo,
+  // w_gate, w_up, w_down)
+  auto scale = [&](int m) { return W8 ? a.wscale[g.layer * 7 + m] : 1.f; };
   if (g.epi == EPI_STORE) {
+    const float sc = scale(g.st == ST_O ? 3 : 6);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       if (!nvalid[nb]) continue;
@@ -196,11 +228,12 @@ __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillArgs a, GemmSt
         for (int r = 0; r < 4; ++r) {
           const int32_t i = m0 + mb * 16 + kg * 4 + r;
           if (i >= pc) continue;
+          const float y = W8 ? acc[mb][nb][r] * sc : acc[mb][nb][r];
           if (g.splits > 1) {  // partial sum of this share of K, summed by prefill_splitk_reduce_kernel
-            g.part[((int64_t)split * pc + i) * g.N + n[nb]] = acc[mb][nb][r];
+            g.part[((int64_t)split * pc + i) * g.N + n[nb]] = y;
           } else {
             float* dst = g.out + (int64_t)i * g.ldo + n[nb];
-            *dst = (g.accumulate ? *dst : 0.f) + acc[mb][nb][r];
+            *dst = (g.accumulate ? *dst : 0.f) + y;
           }
         }
     }
@@ -219,15 +252,24 @@ __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillArgs a, GemmSt
         const float u = __shfl_xor(v, 1, 64);
         const int32_t i = m0 + mb * 16 + kg * 4 + r;
         if (!nvalid[nb] || i >= pc) continue;
-        const float ya = sel ? u : v, yb = sel ? v : u;  // rows A and B of pair gp
+        float ya = sel ? u : v, yb = sel ? v : u;  // rows A and B of pair gp
         const int32_t q = gp[nb];
         if (g.epi == EPI_SWIGLU) {  // pair q = gate row q and up row q
+          if (W8) {
+            ya *= scale(4);
+            yb *= scale(5);
+          }
           if (sel == 0) {
             const int64_t o = (int64_t)i * s.F + q;
             split2((ya / (1.0f + expf(-ya))) * yb, a.h2 + o, a.h2 + (int64_t)kPrefillChunk * s.F + o);
           }
         } else {  // EPI_ROPE_KV: pair q = dims (e, e + hd/2) of head hs
           const int32_t hs = q / half, e = q % half, pos = g.p0 + i;
+          if (W8) {  // the scale of Wq, Wk or Wv
+            const float sc = scale(hs < s.nq ? 0 : (hs < s.nq + s.nkv ? 1 : 2));
+            ya *= sc;
+            yb *= sc;
+          }
           float y = sel ? yb : ya;
           if (hs < s.nq + s.nkv) {  // query and key heads are rotated
             const float2 cs = a.rope[(int64_t)pos * half + e];
@@ -586,7 +628,10 @@ static hipError_t gemm(const PrefillArgs& a, int st, int32_t layer, int32_t p0, 
       g.splits *= 2;
   g.kper = K / g.splits;
   g.part = a.c;
-  hipLaunchKernelGGL(prefill_gemm_kernel, dim3(tiles * g.splits), dim3(256), 0, stream, a, g, pc);
+  if (a.wscale)
+    hipLaunchKernelGGL(prefill_gemm_kernel<true>, dim3(tiles * g.splits), dim3(256), 0, stream, a, g, pc);
+  else
+    hipLaunchKernelGGL(prefill_gemm_kernel<false>, dim3(tiles * g.splits), dim3(256), 0, stream, a, g, pc);
   if (g.splits > 1 && norm_after) {
     hipLaunchKernelGGL(prefill_splitk_reduce_norm_kernel, dim3(pc), dim3(256), 0, stream, a, g, norm_after, pc);
   } else {

@@ -113,8 +113,7 @@ static int check(const Shape& s) {
               const int32_t u = v + kWaves * (b * g.upb + sl / g.ks);
               if (u >= g.nu) continue;
               const int32_t gp = stage_pair(s, st, g.pb + u / g.S), kt = (u % g.S) * g.ks + sl % g.ks;
-              if (TK != kTileK) continue;  // packed_tile serves the bf16 prompt pass only
-              const int64_t got = packed_tile(s, wbase.data(), st, l, gp, kt);
+              const int64_t got = packed_tile<TK>(s, wbase.data(), st, l, gp, kt);
               if (got != t0 + (int64_t)b * kBatch + sl) {
                 std::printf("packed_tile mismatch l=%d st=%d gp=%d kt=%d: %lld vs %lld\n", l, st, gp, kt, (long long)got,
                             (long long)(t0 + (int64_t)b * kBatch + sl));

@@ -7,7 +7,8 @@ the order of fp32 sums only, as in the bf16 path: logits are compared at every s
 (rel-L2 <= 1e-3); at the full 24-layer depth every vector is held to rel-L2(GPU, fp64) <=
 rel-L2(oracle, fp64) + 1e-3 against the float64 reference, see compare(). The synthetic scales
 differ per matrix, so a scale applied to the wrong matrix fails; one test fills the LM head with every finite code, so each code's widening on the GPU is
-checked against the oracle's decoder.
+checked against the oracle's decoder. Prompts run through the matrix-core prompt pass
+(`kie_prefill`), whose GEMMs widen the codes to bf16 as they read them.
 """
 import ctypes as C
 
@@ -83,7 +84,7 @@ def compare(torch, oracle_lib, cfg, w, wd, P, N, seed, label, deep=False):
 
 def test_fp8_prompt_then_decode(torch_cuda, oracle_lib):
     """d 512, 8 query / 4 KV heads of 64, FFN 1536 (3 tiles of 512 per row), vocabulary 4096:
-    several tiles per unit, a ragged last batch, and the token-serial prompt."""
+    several tiles per unit, a ragged last batch, and the prompt pass on the matrix cores."""
     cfg = synth.TINY_FP8
     w = synth.make_weights_np(cfg, 0)
     compare(torch_cuda, oracle_lib, cfg, w, to_device(w), 40, 12, 1, cfg.name)
@@ -130,6 +131,22 @@ def test_fp8_1_6b_layer_shape(torch_cuda, oracle_lib):
         wq1 = synth._weights_bits_np(synth.mat_shape(cfg, "wq"), 0, synth.tensor_index("wq", 1))
         assert np.array_equal(w["wq"][1], synth.fp8_codes_np(wq1))
         compare(torch_cuda, oracle_lib, cfg, w, wd, 12, 4, 1, cfg.name)
+    finally:
+        oracle_lib.set_threads(1)
+
+
+def test_fp8_prompt_pass_two_chunks(torch_cuda, oracle_lib):
+    """The matrix-core prompt pass with 8-bit weights (codes widened to bf16 as they are read, the
+    matrix scales in the GEMM epilogues): the 1.6B shape cut to two layers with a 600-token prompt
+    (a full 512-position chunk and a ragged one, split-K O and down projections), every prompt K/V
+    row and the last prompt logits against the oracle, which runs the prompt position by position,
+    at 1e-3 flat; then 3 decode steps."""
+    cfg = synth.M1_6B_FP8_2L
+    oracle_lib.set_threads(16)
+    try:
+        wd = synth.make_weights_torch(cfg, 0, device="cuda")
+        w = synth.weights_torch_to_np(wd)
+        compare(torch_cuda, oracle_lib, cfg, w, wd, 600, 3, 4, "1.6b-fp8-2l, prompt 600")
     finally:
         oracle_lib.set_threads(1)
 
