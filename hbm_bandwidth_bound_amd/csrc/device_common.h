@@ -89,6 +89,7 @@ constexpr int kDppQuad2301 = 0x4E;      // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppRowMirror = 0x140;
 constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowRor8 = 0x128;  // row_ror:8 -- within each row of 16 lanes, lane i reads lane i ^ 8
 
 template <int CTRL, int ROWMASK = 0xF>
 __device__ __forceinline__ float dpp_f(float v) {
@@ -117,6 +118,29 @@ __device__ __forceinline__ float wave_sum(float v) {
   const float r2 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 32));
   const float r3 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 48));
   return (r0 + r1) + (r2 + r3);
+}
+// The two values of the lane pair {i, i ^ off}, off = 8, 16 or 32 (a compile-time constant after
+// unrolling), in a fixed order: *lo from the lane whose bit `off` is clear, *hi from the other;
+// both lanes of the pair get the same two values. No LDS round trip: off 8 is a DPP rotation by 8
+// within the rows of 16 lanes; 16 and 32 are the gfx950 lane-swap instructions, which exchange a
+// row of 16 lanes with its neighbour row (v_permlane16_swap) and a half wave with the other half
+// (v_permlane32_swap). Given the same register twice, the swap leaves the even row's (lower
+// half's) values in its first result and the odd row's (upper half's) in its second, in every lane.
+__device__ __forceinline__ void lane_pair(float v, int off, int lane, float* lo, float* hi) {
+  if (off == 8) {
+    const float o = dpp_f<kDppRowRor8>(v);
+    const bool up = (lane & 8) != 0;
+    *lo = up ? o : v;
+    *hi = up ? v : o;
+  } else if (off == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    *lo = __uint_as_float(r[0]);
+    *hi = __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    *lo = __uint_as_float(r[0]);
+    *hi = __uint_as_float(r[1]);
+  }
 }
 // Sums of lanes 0..31 and of lanes 32..63 (fixed order), returned wave-uniform.
 __device__ __forceinline__ void half_wave_sums(float v, float* lo, float* hi) {

@@ -951,18 +951,16 @@ __device__ __forceinline__ void attention(WK& K, const Att& at, int32_t l, int32
   const uint32_t kvbytes = (uint32_t)at.ncache * HD * 2;  // lanes past the cached rows read zeros
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(P.kv + kv_offset(s, l, 0, at.j, at.c0), kvbytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(P.kv + kv_offset(s, l, 1, at.j, at.c0), kvbytes);
+  // Batch bi's K and V tiles, always 2 AB loads: a tile past this wave's last lies wholly past the
+  // resources' end (tile t >= nkt starts at or past ncache rows), so its loads read zeros without
+  // touching memory. With no branch around them, every path of the batch loop below issues the
+  // same loads, and the wait before a batch is used need not cover the batch issued after it.
   auto kv_issue = [&](int32_t bi, v4u* kb, v4u* vb) {
 #pragma unroll
     for (int e = 0; e < AB; ++e) {
-      const int32_t i = bi * AB + e;
-      if (i < ntw) {
-        const uint32_t off = (uint32_t)((v + kWaves * i) * kTileBytes + lane * 16);
-        kb[e] = load16(krs, off);
-        vb[e] = load16(vrs, off);
-      } else {
-        kb[e] = v4u{0u, 0u, 0u, 0u};
-        vb[e] = v4u{0u, 0u, 0u, 0u};
-      }
+      const uint32_t off = (uint32_t)((v + kWaves * (bi * AB + e)) * kTileBytes + lane * 16);
+      kb[e] = load16(krs, off);
+      vb[e] = load16(vrs, off);
     }
   };
   v4u kn[AB], vn[AB];
@@ -1044,20 +1042,25 @@ __device__ __forceinline__ void attention(WK& K, const Att& at, int32_t l, int32
           }
         }
       };
-      for (int32_t bi = 0; bi < nbw; ++bi) {
+      auto kv_batch = [&](int32_t bi, const v4u* kc, const v4u* vc) {
+#pragma unroll
+        for (int e = 0; e < AB; ++e) {
+          const int32_t i = bi * AB + e;
+          if (i < ntw) update(kc[e], vc[e], (v + kWaves * i) * PPT + lpos < at.ncache);
+        }
+      };
+      // every batch but the last with the next one in flight; the last on its own, with no loads
+      for (int32_t bi = 0; bi + 1 < nbw; ++bi) {
         v4u kc[AB], vc[AB];
 #pragma unroll
         for (int e = 0; e < AB; ++e) {
           kc[e] = kn[e];
           vc[e] = vn[e];
         }
-        if (bi + 1 < nbw) kv_issue(bi + 1, kn, vn);
-#pragma unroll
-        for (int e = 0; e < AB; ++e) {
-          const int32_t i = bi * AB + e;
-          if (i < ntw) update(kc[e], vc[e], (v + kWaves * i) * PPT + lpos < at.ncache);
-        }
+        kv_issue(bi + 1, kn, vn);
+        kv_batch(bi, kc, vc);
       }
+      if (nbw > 0) kv_batch(nbw - 1, kn, vn);
       if (at.has_p && v == at.nkt % kWaves) {  // the current position, rounded to bf16 like the cache
         auto cur_row = [&](const float* src) {
           uint32_t b[8];
@@ -1068,19 +1071,21 @@ __device__ __forceinline__ void attention(WK& K, const Att& at, int32_t l, int32
         update(cur_row(L.q + G * HD), cur_row(L.q + (G + 1) * HD), lpos == 0);
       }
 #pragma unroll
-      for (int off = LPP; off < kWave; off <<= 1) {  // the position rows of the wave
+      for (int off = LPP; off < kWave; off <<= 1) {  // the position rows of the wave (lane pairs, no LDS)
 #pragma unroll
         for (int g = 0; g < GP; ++g) {
-          const float mo = __shfl_xor(m[g], off, kWave);
-          const float lo = __shfl_xor(ls[g], off, kWave);
-          const float M = fmaxf(m[g], mo);
-          const float f = m[g] == -INFINITY ? 0.f : exp2f(m[g] - M);
-          const float fo = mo == -INFINITY ? 0.f : exp2f(mo - M);
-          ls[g] = ls[g] * f + lo * fo;
+          float ma, mb, la, lb;
+          lane_pair(m[g], off, lane, &ma, &mb);
+          lane_pair(ls[g], off, lane, &la, &lb);
+          const float M = fmaxf(ma, mb);
+          const float f = ma == -INFINITY ? 0.f : exp2f(ma - M);
+          const float fo = mb == -INFINITY ? 0.f : exp2f(mb - M);
+          ls[g] = la * f + lb * fo;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float ao = __shfl_xor(acc[g][e], off, kWave);
-            acc[g][e] = acc[g][e] * f + ao * fo;
+            float aa, ab;
+            lane_pair(acc[g][e], off, lane, &aa, &ab);
+            acc[g][e] = aa * f + ab * fo;
           }
           m[g] = M;
         }
@@ -1101,20 +1106,23 @@ __device__ __forceinline__ void attention(WK& K, const Att& at, int32_t l, int32
       bar();
       for (int e = K.tid; e < GP * (HD + 2); e += kThreads) {  // combine the 8 waves and publish
         const int g = e / (HD + 2), k = e % (HD + 2);
+        // every wave's maximum and value first, so that the 16 LDS reads are in flight together
+        float mw[kWaves], vw[kWaves];
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          mw[w] = L.scr[(w * GP + g) * (HD + 2) + HD];
+          vw[w] = L.scr[(w * GP + g) * (HD + 2) + k];
+        }
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, L.scr[(w * GP + g) * (HD + 2) + HD]);
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mw[w]);
         float out;
         if (k == HD) {
           out = M;
         } else {
           out = 0.f;
 #pragma unroll
-          for (int w = 0; w < kWaves; ++w) {
-            const float mw = L.scr[(w * GP + g) * (HD + 2) + HD];
-            const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
-            out = fmaf(L.scr[(w * GP + g) * (HD + 2) + k], f, out);
-          }
+          for (int w = 0; w < kWaves; ++w) out = fmaf(vw[w], mw[w] == -INFINITY ? 0.f : exp2f(mw[w] - M), out);
         }
         st_x(part + g0 * (HD + 2) + e, tag_f(out, ep));
       }
@@ -1175,20 +1183,25 @@ __device__ __forceinline__ void attention(WK& K, const Att& at, int32_t l, int32
         }
       }
     };
-    for (int32_t bi = 0; bi < nbw; ++bi) {
+    auto kv_batch = [&](int32_t bi, const v4u* kc, const v4u* vc) {
+#pragma unroll
+      for (int e = 0; e < AB; ++e) {
+        const int32_t i = bi * AB + e;
+        if (i < ntw) update(kc[e], vc[e], (v + kWaves * i) * PPT + lpos < at.ncache);
+      }
+    };
+    // every batch but the last with the next one in flight; the last on its own, with no loads
+    for (int32_t bi = 0; bi + 1 < nbw; ++bi) {
       v4u kc[AB], vc[AB];
 #pragma unroll
       for (int e = 0; e < AB; ++e) {
         kc[e] = kn[e];
         vc[e] = vn[e];
       }
-      if (bi + 1 < nbw) kv_issue(bi + 1, kn, vn);
-#pragma unroll
-      for (int e = 0; e < AB; ++e) {
-        const int32_t i = bi * AB + e;
-        if (i < ntw) update(kc[e], vc[e], (v + kWaves * i) * PPT + lpos < at.ncache);
-      }
+      kv_issue(bi + 1, kn, vn);
+      kv_batch(bi, kc, vc);
     }
+    if (nbw > 0) kv_batch(nbw - 1, kn, vn);
     // the current position: its K/V come from the exchange, rounded to bf16 like the cache
     if (at.has_p && v == at.nkt % kWaves) {
       auto cur_row = [&](const float* src) {
@@ -1200,21 +1213,23 @@ __device__ __forceinline__ void attention(WK& K, const Att& at, int32_t l, int32
       update(cur_row(L.q + G * HD), cur_row(L.q + (G + 1) * HD), lpos == 0);
     }
     TR_HOP(K, H_ATT_DONE);
-    // combine the position rows of the wave (lanes with the same dims)
+    // combine the position rows of the wave (lanes with the same dims: pairs exchanged in registers)
 #pragma unroll
     for (int off = LPP; off < kWave; off <<= 1) {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float mo = __shfl_xor(m[g], off, kWave);
-        const float lo = __shfl_xor(ls[g], off, kWave);
-        const float M = fmaxf(m[g], mo);
-        const float f = m[g] == -INFINITY ? 0.f : exp2f(m[g] - M);
-        const float fo = mo == -INFINITY ? 0.f : exp2f(mo - M);
-        ls[g] = ls[g] * f + lo * fo;
+        float ma, mb, la, lb;
+        lane_pair(m[g], off, lane, &ma, &mb);
+        lane_pair(ls[g], off, lane, &la, &lb);
+        const float M = fmaxf(ma, mb);
+        const float f = ma == -INFINITY ? 0.f : exp2f(ma - M);
+        const float fo = mb == -INFINITY ? 0.f : exp2f(mb - M);
+        ls[g] = la * f + lb * fo;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float ao = __shfl_xor(acc[g][e], off, kWave);
-          acc[g][e] = acc[g][e] * f + ao * fo;
+          float aa, ab;
+          lane_pair(acc[g][e], off, lane, &aa, &ab);
+          acc[g][e] = aa * f + ab * fo;
         }
         m[g] = M;
       }
@@ -1240,20 +1255,23 @@ __device__ __forceinline__ void attention(WK& K, const Att& at, int32_t l, int32
     uint64_t* part = P.ex + X.part + ((int64_t)l * s.nwg + K.w) * X.part_words;
     for (int e = K.tid; e < G * (HD + 2); e += kThreads) {
       const int g = e / (HD + 2), k = e % (HD + 2);
+      // every wave's maximum and value first, so that the 16 LDS reads are in flight together
+      float mw[kWaves], vw[kWaves];
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        mw[w] = L.scr[(w * G + g) * (HD + 2) + HD];
+        vw[w] = L.scr[(w * G + g) * (HD + 2) + k];
+      }
       float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, L.scr[(w * G + g) * (HD + 2) + HD]);
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mw[w]);
       float out;
       if (k == HD) {
         out = M;
       } else {
         out = 0.f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          const float mw = L.scr[(w * G + g) * (HD + 2) + HD];
-          const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
-          out = fmaf(L.scr[(w * G + g) * (HD + 2) + k], f, out);
-        }
+        for (int w = 0; w < kWaves; ++w) out = fmaf(vw[w], mw[w] == -INFINITY ? 0.f : exp2f(mw[w] - M), out);
       }
       st_x(part + e, tag_f(out, ep));
     }
@@ -1341,8 +1359,14 @@ __device__ __forceinline__ void merge_unit(WK& K, const Att& at, int32_t l, int3
   }
   // chunk lanes of this wave (lanes dim, dim + D, ...): butterfly over the lane bits above D
 #pragma unroll
-  for (int o = D; o < kWave; o <<= 1) {
-    const float m2 = __shfl_xor(M, o, kWave), s2 = __shfl_xor(S, o, kWave), a2 = __shfl_xor(A, o, kWave);
+  for (int o = D; o < kWave; o <<= 1) {  // lane pairs exchanged in registers, lower lane first
+    float m1, m2, s1, s2, a1, a2;
+    lane_pair(M, o, K.lane, &m1, &m2);
+    lane_pair(S, o, K.lane, &s1, &s2);
+    lane_pair(A, o, K.lane, &a1, &a2);
+    M = m1;
+    S = s1;
+    A = a1;
     softmax_combine(M, S, A, m2, s2, a2);
   }
   float* ms = L.scr;  // [8 waves][D][3]
@@ -1353,10 +1377,16 @@ __device__ __forceinline__ void merge_unit(WK& K, const Att& at, int32_t l, int3
   }
   bar();
   if (K.tid < D) {
-    float Mt = ms[K.tid * 3], St = ms[K.tid * 3 + 1], At = ms[K.tid * 3 + 2];
+    float mv[kWaves], sv[kWaves], av[kWaves];  // all 24 LDS reads in flight together
 #pragma unroll
-    for (int k = 1; k < kWaves; ++k)
-      softmax_combine(Mt, St, At, ms[(k * D + K.tid) * 3], ms[(k * D + K.tid) * 3 + 1], ms[(k * D + K.tid) * 3 + 2]);
+    for (int k = 0; k < kWaves; ++k) {
+      mv[k] = ms[(k * D + K.tid) * 3];
+      sv[k] = ms[(k * D + K.tid) * 3 + 1];
+      av[k] = ms[(k * D + K.tid) * 3 + 2];
+    }
+    float Mt = mv[0], St = sv[0], At = av[0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) softmax_combine(Mt, St, At, mv[k], sv[k], av[k]);
     st_x(P.ex + P.exo.o + (int64_t)l * s.qdim() + h * s.hd + sl * D + K.tid, tag_f(At / St, epoch));
   }
   bar();
@@ -1424,8 +1454,14 @@ __device__ __forceinline__ void merge_two_units(WK& K, const Att& at, int32_t l,
                         __uint_as_float((uint32_t)(wa[k] >> 32)));
   }
 #pragma unroll
-  for (int o = D; o < kWave; o <<= 1) {  // chunk lanes of this wave
-    const float m2 = __shfl_xor(M, o, kWave), s2 = __shfl_xor(S, o, kWave), a2 = __shfl_xor(A, o, kWave);
+  for (int o = D; o < kWave; o <<= 1) {  // chunk lanes of this wave: lane pairs in registers, lower first
+    float m1, m2, s1, s2, a1, a2;
+    lane_pair(M, o, K.lane, &m1, &m2);
+    lane_pair(S, o, K.lane, &s1, &s2);
+    lane_pair(A, o, K.lane, &a1, &a2);
+    M = m1;
+    S = s1;
+    A = a1;
     softmax_combine(M, S, A, m2, s2, a2);
   }
   float* ms = L.scr;  // [8 waves][D][3]
@@ -1440,11 +1476,16 @@ __device__ __forceinline__ void merge_two_units(WK& K, const Att& at, int32_t l,
     const int32_t ut = K.tid / D, dt = K.tid % D;
     const int32_t un = u + ut, hn = un / slices, sn = un % slices;
     const int w0 = ut * WPU;
-    float Mt = ms[(w0 * D + dt) * 3], St = ms[(w0 * D + dt) * 3 + 1], At = ms[(w0 * D + dt) * 3 + 2];
+    float mv[WPU], sv[WPU], av[WPU];  // all LDS reads in flight together
 #pragma unroll
-    for (int k = 1; k < WPU; ++k)
-      softmax_combine(Mt, St, At, ms[((w0 + k) * D + dt) * 3], ms[((w0 + k) * D + dt) * 3 + 1],
-                      ms[((w0 + k) * D + dt) * 3 + 2]);
+    for (int k = 0; k < WPU; ++k) {
+      mv[k] = ms[((w0 + k) * D + dt) * 3];
+      sv[k] = ms[((w0 + k) * D + dt) * 3 + 1];
+      av[k] = ms[((w0 + k) * D + dt) * 3 + 2];
+    }
+    float Mt = mv[0], St = sv[0], At = av[0];
+#pragma unroll
+    for (int k = 1; k < WPU; ++k) softmax_combine(Mt, St, At, mv[k], sv[k], av[k]);
     st_x(P.ex + P.exo.o + (int64_t)l * s.qdim() + hn * s.hd + sn * D + dt, tag_f(At / St, epoch));
   }
   bar();
