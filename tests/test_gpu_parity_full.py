@@ -234,17 +234,23 @@ def test_8b_shape_prefill_then_decode(torch_cuda, oracle_lib):
 
 
 def test_full_shape_topk_sampling(torch_cuda, oracle_lib):
-    """Top-k (k 50, T 0.8) on the full 1.6B model over a short prompt: the GPU's draws equal the
-    oracle sampler's on the GPU's own logits, and the candidate sets and probabilities follow the
-    oracle's logits within the softmax bound of their distance."""
+    """Top-k on the full 1.6B model over a short prompt, k 50 at T 0.8 (the served setting) and
+    k 4 at T 1: the GPU's draws equal the oracle sampler's on the GPU's own logits; the candidate
+    sets and probabilities follow the oracle's logits within the softmax bound of their distance
+    wherever the k-th/(k+1)-th gap exceeds twice that distance. At 24 layers the gaps around the
+    50th logit are narrower than the distance, so k 50 is held at the sampler level only; the gaps
+    between the few largest logits are wider, and the k 4 run checks the sets (and the tokens, where
+    the draw is clear of the CDF boundaries) against the oracle at this depth."""
     torch = torch_cuda
     from hbm_bandwidth_bound_amd.kie import sampling
     cfg = synth.M1_6B
     P, N = 12, 4
-    say(f"[1.6b top-k] prefill {P} + decode {N}")
+    say(f"[1.6b top-k] prefill {P} + decode {N}, k 50 and k 4")
     wd = synth.make_weights_torch(cfg, 0, "cuda")
     prompt = synth.prompt_ids(P, cfg.vocab_size, 3)
     first, last, toks, logits, kv = _gpu_prompt_and_decode(torch, cfg, wd, prompt, N, smp=sampling(50, 0.8, 2))
+    first4, _, toks4, logits4, _ = _gpu_prompt_and_decode(torch, cfg, wd, prompt, N, smp=sampling(4, 1.0, 5))
+    assert first4 == first  # the prompt pass's token is the greedy one either way
     w = synth.weights_torch_to_np(wd)
     del wd
     torch.cuda.empty_cache()
@@ -253,4 +259,9 @@ def test_full_shape_topk_sampling(torch_cuda, oracle_lib):
     om.run(prompt)
     ora = om.run([first] + [int(t) for t in toks[:-1]], start_pos=P)
     nt, ns = check_topk_steps(logits, ora, toks, 50, 0.8, 2, P, p_tol="auto", label="1.6b top-k")
-    say(f"  top-k: sets checked on {ns}/{N} steps, tokens on {nt}/{N}")
+    say(f"  top-k 50: sets checked on {ns}/{N} steps, tokens on {nt}/{N}")
+    # the oracle's cache rows < P stay; positions P.. are rewritten along the k 4 run's tokens
+    ora4 = om.run([first] + [int(t) for t in toks4[:-1]], start_pos=P)
+    nt4, ns4 = check_topk_steps(logits4, ora4, toks4, 4, 1.0, 5, P, p_tol="auto", label="1.6b top-4")
+    say(f"  top-k 4: sets checked on {ns4}/{N} steps, tokens on {nt4}/{N}")
+    assert ns4 >= 1, "no step of the k 4 run had a 4th/5th logit gap above twice the GPU-oracle distance"
