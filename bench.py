@@ -11,8 +11,8 @@ length and a profiler's per-dispatch average is the timed launch's duration.
 Prints one JSON line. `roofline.achieved` is the algorithmic bytes of the timed launch divided
 by that launch's duration (HIP events on the launch stream); `cpu_baseline` times the CPU oracle
 on a bounded sample of the same workload. Other workloads: `--workload 1.6b-32k`, `8b-2k`, and
-`moe-1k` (the 128-expert model with 8 experts routed per token; its prompt runs through the
-decode program, and its CPU baseline is the oracle on 2- and 4-layer cuts of the model, scaled).
+`moe-1k` (the 128-expert model with 8 experts routed per token; its CPU baseline is the oracle
+on 2- and 4-layer cuts of the model, scaled).
 """
 from __future__ import annotations
 
@@ -176,17 +176,15 @@ def main():
         eng.sync()
         ttft.append(e0.elapsed_time(e1))
     ttft_ms = ttft[1]
-    # the prompt pass's matrix products: 2 x (tokens - 1) x the layer weights (the last position
-    # runs through the decode kernel), plus the causal attention products
+    # the prompt pass's matrix products: 2 x (tokens - 1) x the layer weights a position uses (the
+    # routed experts' only, with experts; the last position runs through the decode kernel), plus
+    # the causal attention products. They run as matrix-core GEMMs (8-bit codes widened to bf16
+    # operands as they are read; each expert's positions as its own products).
     mm = traffic.matrix_weights(m) - m.vocab_size * m.d_model
     attn = 4 * m.n_layers * m.n_heads * m.head_dim * (P - 1) * P // 2
     prefill_flops = 2 * (P - 1) * mm + attn
-    if m.n_experts:  # every prompt position runs through the decode program
-        prompt_pass = {"kind": "decode program, teacher-forced, one position after the other",
-                       "positions_per_s": round(P / (ttft_ms * 1e-3), 1)}
-    else:  # matrix-core GEMMs (8-bit codes widened to bf16 operands as they are read)
-        prompt_pass = {"flops": prefill_flops, "tflops": round(prefill_flops / (ttft_ms * 1e-3) / 1e12, 1),
-                       "frac_of_bf16_mfma_peak": round(prefill_flops / (ttft_ms * 1e-3) / 2.5e15, 4)}
+    prompt_pass = {"flops": prefill_flops, "tflops": round(prefill_flops / (ttft_ms * 1e-3) / 1e12, 1),
+                   "frac_of_bf16_mfma_peak": round(prefill_flops / (ttft_ms * 1e-3) / 2.5e15, 4)}
 
     out = torch.empty(max(K, W), dtype=torch.int32, device=dev)
     if W > 0:

@@ -711,10 +711,11 @@ kie_status kie_prefill(kie_ctx* ctx, const int32_t* tokens_dev, int32_t n_tokens
     set_err(&ctx->last_error, "position %d + %d tokens exceeds max_seq_len %d", ctx->pos, n_tokens, ctx->s.max_seq);
     return KIE_ERR_CAPACITY;
   }
-  // mixture of experts and contexts on the static workspace (which has no room for the
-  // matrix-core pass's scratch): every position through the decode program, teacher-forced
-  // (position i + 1 processes tokens[i + 1]); the LM head and the sampler run on the last one only
-  if (ctx->s.moe() || ctx->static_ws)
+  // contexts on the static workspace (which has no room for the matrix-core pass's scratch), and
+  // shapes the matrix-core pass does not handle: every position through the decode program,
+  // teacher-forced (position i + 1 processes tokens[i + 1]); the LM head and the sampler run on
+  // the last one only
+  if (ctx->static_ws || !prefill_supports(ctx->s))
     return launch(ctx, tokens_dev, n_tokens, tokens_dev + 1, nullptr, first_token_dev, last_logits_dev, 1, sampling);
   // all but the last prompt position: every layer as GEMMs on the matrix cores (K/V rows only)
   if (n_tokens > 1) {
@@ -737,6 +738,20 @@ kie_status kie_prefill(kie_ctx* ctx, const int32_t* tokens_dev, int32_t n_tokens
     a.q = (float*)(ctx->ws + ctx->wso.pq);
     a.attn_part = (float*)(ctx->ws + ctx->wso.pattn);
     a.wscale = ctx->w8 ? (const float*)(ctx->ws + ctx->wso.wscale) : nullptr;
+    a.rlogits = a.wt = a.ey = nullptr;
+    a.sel = a.place = a.lists = a.counts = a.offs = nullptr;
+    if (ctx->s.moe()) {  // the experts' scratch
+      const MoePrefill m = moe_prefill_layout(ctx->s);
+      uint8_t* mb = ctx->ws + ctx->wso.pmoe;
+      a.rlogits = (float*)(mb + m.logits);
+      a.sel = (int32_t*)(mb + m.sel);
+      a.wt = (float*)(mb + m.wt);
+      a.place = (int32_t*)(mb + m.place);
+      a.lists = (int32_t*)(mb + m.lists);
+      a.counts = (int32_t*)(mb + m.counts);
+      a.offs = (int32_t*)(mb + m.offs);
+      a.ey = (float*)(mb + m.y);
+    }
     HIP_TRY(&ctx->last_error, launch_prefill(a, ctx->pos, n_tokens - 1, ctx->stream));
     ctx->pos += n_tokens - 1;
   }

@@ -302,17 +302,42 @@ KIE_HD int32_t prefill_nmax(const Shape& s) {
 // per-stream base (in tiles, [nwg][8] + total), error word, norm gains [L][2][d] + final [d] (bf16),
 // trace counters, the prompt-pass scratch (residual [chunk][d] fp32, GEMM input [2][chunk][kmax]
 // bf16, down-projection input [2][chunk][F] bf16, split-K partial sums [chunk][nmax] fp32, queries
-// [chunk][nq hd] fp32, and for long contexts the per-segment attention states
-// [segments][chunk][nq][hd + 2] fp32), and the matrix scales of 8-bit weights [L][7] + [1] fp32.
+// [chunk][nq hd] fp32, for long contexts the per-segment attention states
+// [segments][chunk][nq][hd + 2] fp32, and with experts moe_prefill_layout's pieces), and the
+// matrix scales of 8-bit weights [L][7] + [1] fp32.
 struct Workspace {
-  int64_t exch, rope, wbase, err, norms, trace, px, pa3, ph2, pc, pq, pattn, wscale, end;
+  int64_t exch, rope, wbase, err, norms, trace, px, pa3, ph2, pc, pq, pattn, pmoe, wscale, end;
 };
 constexpr int kTraceWords = 64;  // per wave: cycle counters of a KIE_TRACE build (0..31), and the
                                  // hop timeline of one sampled layer (32..63, wave 0 only)
 constexpr int kTraceHop = 32;    // first word of the hop timeline
 KIE_HD int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+// The mixture-of-experts part of the prompt pass's scratch (one chunk of positions): router logits
+// [chunk][E] fp32; per position its A chosen experts [chunk][A] int32 in rank order, their
+// weights [chunk][A] fp32 and each choice's place in its expert's token list [chunk][A] int32;
+// the token lists [E][chunk] int32 (position << 4 | rank); the lists' lengths [E] and first rows
+// [E] int32; the experts' down-projection rows [chunk * A][d] fp32 (expert e's rows from its
+// first row on, in list order).
+struct MoePrefill {
+  int64_t logits, sel, wt, place, lists, counts, offs, y, end;
+};
+KIE_HD MoePrefill moe_prefill_layout(const Shape& s) {
+  MoePrefill m;
+  const int64_t C = kPrefillChunk;
+  int64_t o = 0;
+  m.logits = o; o = align256(o + C * s.E * 4);
+  m.sel = o; o = align256(o + C * s.A * 4);
+  m.wt = o; o = align256(o + C * s.A * 4);
+  m.place = o; o = align256(o + C * s.A * 4);
+  m.lists = o; o = align256(o + (int64_t)s.E * C * 4);
+  m.counts = o; o = align256(o + (int64_t)s.E * 4);
+  m.offs = o; o = align256(o + (int64_t)s.E * 4);
+  m.y = o; o = align256(o + C * s.A * s.d * 4);
+  m.end = o;
+  return m;
+}
 // prefill == false: without the matrix-core prompt pass's scratch (a context whose prompt runs
-// through the decode program); px .. pattn are then empty pieces at the end of the rest.
+// through the decode program); px .. pmoe are then empty pieces at the end of the rest.
 KIE_HD Workspace workspace_layout(const Shape& s, bool prefill = true) {
   Workspace w;
   int64_t o = 0;
@@ -324,7 +349,7 @@ KIE_HD Workspace workspace_layout(const Shape& s, bool prefill = true) {
   w.trace = o; o = align256(o + (int64_t)s.nwg * kWaves * kTraceWords * 8);
   w.wscale = o; o = align256(o + ((int64_t)s.L * 7 + 1) * 4);  // 8-bit weights: the matrix scales
   if (!prefill) {
-    w.px = w.pa3 = w.ph2 = w.pc = w.pq = w.pattn = w.end = o;
+    w.px = w.pa3 = w.ph2 = w.pc = w.pq = w.pattn = w.pmoe = w.end = o;
     return w;
   }
   w.px = o; o = align256(o + (int64_t)kPrefillChunk * s.d * 4);
@@ -334,6 +359,8 @@ KIE_HD Workspace workspace_layout(const Shape& s, bool prefill = true) {
   w.pq = o; o = align256(o + (int64_t)kPrefillChunk * s.qdim() * 4);
   w.pattn = o;
   if (prefill_attn_segs(s) > 1) o = align256(o + (int64_t)prefill_attn_segs(s) * kPrefillChunk * s.nq * (s.hd + 2) * 4);
+  w.pmoe = o;
+  if (s.moe()) o = align256(o + moe_prefill_layout(s).end);
   w.end = o;
   return w;
 }

@@ -27,6 +27,15 @@ struct PrefillArgs {
   float* q;                  // [chunk][nq * hd] rotated queries
   float* attn_part;          // [segments][chunk][nq][hd + 2] partial attention states
   const float* wscale;       // 8-bit weights: the matrix scales [L][7] (+ the LM head's); null for bf16
+  // mixture of experts (moe_prefill_layout; null for dense models)
+  float* rlogits;            // [chunk][E] router logits
+  int32_t* sel;              // [chunk][A] chosen experts, rank order
+  float* wt;                 // [chunk][A] their routing weights
+  int32_t* place;            // [chunk][A] each choice's place in its expert's token list
+  int32_t* lists;            // [E][chunk] position << 4 | rank, in position order
+  int32_t* counts;           // [E] list lengths
+  int32_t* offs;             // [E] first row of each expert's rows in ey (and in h2)
+  float* ey;                 // [chunk * A][d] the experts' down-projection rows
 };
 
 // What the GEMM does with its result C[i][n]:
@@ -50,5 +59,9 @@ struct GemmStage {
 
 // Run every layer over positions p0 .. p0 + n - 1 (writes their K/V rows).
 hipError_t launch_prefill(const PrefillArgs& a, int32_t p0, int32_t n, hipStream_t stream);
+// Whether launch_prefill handles the shape: a mixture of experts needs whole output tiles and K
+// chunks in its experts' products (d and the expert width multiples of 128) and at most 15 experts
+// routed per position.
+bool prefill_supports(const Shape& s);
 
 }  // namespace kie

@@ -108,7 +108,12 @@ __device__ __forceinline__ bf16x8 codes8_to_bf16(uint32_t c0, uint32_t c1) {
 // W8: the weights are e4m3fn codes (8-bit tiles: lane q holds row A's codes at k = 4q .. 4q+3
 // and 256 + 4q .. +3 of the tile's 512, then row B's at the same k), widened to bf16 as they are
 // read; the matrix's scale multiplies the products in the epilogue.
-template <bool W8>
+//
+// XM (mixture of experts; bf16): 1 = an expert's gate/up product, 2 = its down product, over the
+// positions that chose it. blockIdx.y is the expert e; the block's rows are rows of e's token
+// list (XM 1: the rows of the positions in the list, from the RMSNorm input a3; XM 2: e's rows of
+// h2 from its first row offs[e] on), and its weights are e's tiles in the expert region.
+template <bool W8, int XM = 0>
 __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillArgs a, GemmStage g, int32_t pc) {
   constexpr int TK = W8 ? 2 * kTileK : kTileK;  // weights of a row per tile
   constexpr int KSTEPS = kGemmKC / 32;
@@ -116,14 +121,22 @@ __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillArgs a, GemmSt
   constexpr int APER = kGemmParts * kGemmM * (kGemmKC / 8) / 256;  // 16-byte pieces per thread
   __shared__ __align__(16) uint16_t As[kGemmParts][kGemmM][kALd];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // XM: this block's expert, its number of positions (the GEMM's rows) and its first row
+  const int32_t ex = XM ? (int32_t)blockIdx.y : 0;
+  const int32_t rows = XM ? a.counts[ex] : pc;
+  const int32_t erow0 = XM ? a.offs[ex] : 0;
   // Tile of this block. The token tiles of one weight tile run on one XCD in consecutive slots
   // (workgroup b goes to XCD b mod 8), so the weight tile is fetched from HBM once and then served
   // by that XCD's L2 to the other token tiles.
-  const int32_t nM = (pc + kGemmM - 1) / kGemmM, nN = (g.N + kGemmN - 1) / kGemmN;
+  const int32_t nM = ((XM ? kPrefillChunk : pc) + kGemmM - 1) / kGemmM, nN = (g.N + kGemmN - 1) / kGemmN;
   const int32_t b = (int32_t)blockIdx.x % (nM * nN), split = (int32_t)blockIdx.x / (nM * nN);
   const int32_t kbeg = split * g.kper, kend = kbeg + g.kper;  // this block's share of K
   int32_t mt, nt;
-  if (nN % 8 == 0) {
+  if (XM) {
+    mt = b % nM;
+    nt = b / nM;
+    if (mt * kGemmM >= rows) return;  // (uniform over the block)
+  } else if (nN % 8 == 0) {
     mt = (b / 8) % nM;
     nt = b % 8 + 8 * ((b / 8) / nM);
   } else {
@@ -141,7 +154,9 @@ __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillArgs a, GemmSt
     gp[nb] = nvalid[nb] ? n[nb] >> 1 : 0;
   }
   const int sel = nl & 1;  // row A or B of the pair (n and nl have the same parity)
-  const int32_t ks_unit = unit_tiles(a.s.template stage_kt<TK>(g.st));
+  // XM: an expert pair's k-tiles are contiguous in the expert region, so one unit spans them all
+  const int32_t ks_unit = XM ? g.K / kTileK : unit_tiles(a.s.template stage_kt<TK>(g.st));
+  const int64_t xregion = XM ? a.wbase[a.s.nwg * kWaves] : 0;  // the expert region's first tile
   int64_t tbase[NB] = {};  // first tile of the current unit of each column's pair
   f4 acc[4][NB];
 #pragma unroll
@@ -155,8 +170,14 @@ __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillArgs a, GemmSt
     const int32_t kt = kc / TK;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      if (kc == kbeg || (kt % ks_unit == 0 && kc % TK == 0))
-        tbase[nb] = nvalid[nb] ? packed_tile<TK>(a.s, a.wbase, g.st, g.layer, gp[nb], kt - kt % ks_unit) : 0;
+      if (kc == kbeg || (kt % ks_unit == 0 && kc % TK == 0)) {
+        if constexpr (XM == 1)
+          tbase[nb] = nvalid[nb] ? xregion + expert_gu_tile(a.s, g.layer, ex, gp[nb], 0) : 0;
+        else if constexpr (XM == 2)
+          tbase[nb] = nvalid[nb] ? xregion + expert_dn_tile(a.s, g.layer, ex, gp[nb], 0) : 0;
+        else
+          tbase[nb] = nvalid[nb] ? packed_tile<TK>(a.s, a.wbase, g.st, g.layer, gp[nb], kt - kt % ks_unit) : 0;
+      }
       const uint8_t* tp = a.packed + (tbase[nb] + kt % ks_unit) * kTileBytes + 8 * sel;
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
@@ -178,7 +199,10 @@ __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillArgs a, GemmSt
       const int q = tid + jj * 256;
       const int p = q / (kGemmM * (kGemmKC / 8)), r = (q / (kGemmKC / 8)) % kGemmM, c = q % (kGemmKC / 8);
       const int32_t i = m0 + r;
-      av4[jj] = i < pc ? *(const uint4*)(g.in + p * g.in_part + (int64_t)i * g.K + kc + c * 8) : uint4{0u, 0u, 0u, 0u};
+      int64_t src = i;  // the input row of GEMM row i
+      if constexpr (XM == 1) src = i < rows ? a.lists[(int64_t)ex * kPrefillChunk + i] >> 4 : 0;
+      if constexpr (XM == 2) src = erow0 + i;
+      av4[jj] = i < rows ? *(const uint4*)(g.in + p * g.in_part + src * g.K + kc + c * 8) : uint4{0u, 0u, 0u, 0u};
     }
   };
 
@@ -227,9 +251,11 @@ __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillArgs a, GemmSt
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int32_t i = m0 + mb * 16 + kg * 4 + r;
-          if (i >= pc) continue;
+          if (i >= rows) continue;
           const float y = W8 ? acc[mb][nb][r] * sc : acc[mb][nb][r];
-          if (g.splits > 1) {  // partial sum of this share of K, summed by prefill_splitk_reduce_kernel
+          if (XM == 2) {  // the expert's down-projection row of this position and rank
+            a.ey[(int64_t)(erow0 + i) * g.N + n[nb]] = y;
+          } else if (g.splits > 1) {  // partial sum of this share of K, summed by prefill_splitk_reduce_kernel
             g.part[((int64_t)split * pc + i) * g.N + n[nb]] = y;
           } else {
             float* dst = g.out + (int64_t)i * g.ldo + n[nb];
@@ -251,10 +277,17 @@ __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillArgs a, GemmSt
         const float v = acc[mb][nb][r];
         const float u = __shfl_xor(v, 1, 64);
         const int32_t i = m0 + mb * 16 + kg * 4 + r;
-        if (!nvalid[nb] || i >= pc) continue;
+        if (!nvalid[nb] || i >= rows) continue;
         float ya = sel ? u : v, yb = sel ? v : u;  // rows A and B of pair gp
         const int32_t q = gp[nb];
-        if (g.epi == EPI_SWIGLU) {  // pair q = gate row q and up row q
+        if (XM == 1) {  // pair q = gate row q and up row q of the expert; h times the routing weight
+          if (sel == 0) {
+            const int32_t le = a.lists[(int64_t)ex * kPrefillChunk + i];
+            const float w = a.wt[(int64_t)(le >> 4) * s.A + (le & 15)];
+            const int64_t o = (int64_t)(erow0 + i) * s.Fe + q;
+            split2(w * ((ya / (1.0f + expf(-ya))) * yb), a.h2 + o, a.h2 + (int64_t)kPrefillChunk * s.F + o);
+          }
+        } else if (g.epi == EPI_SWIGLU) {  // pair q = gate row q and up row q
           if (W8) {
             ya *= scale(4);
             yb *= scale(5);
@@ -596,6 +629,105 @@ __global__ void __launch_bounds__(HD) prefill_attn_merge_kernel(PrefillArgs a, i
 }
 
 // ------------------------------------------------------------------------------------------
+// Mixture-of-experts layers: routing, per-expert token lists, and the weighted sum of the experts'
+// outputs. The choice follows the decode kernel's: the A largest logits (ties to the lower index;
+// NaN ranks lowest, -0 as +0) and weights exp(z_i - z_0) / sum_j exp(z_j - z_0) over the chosen
+// in rank order, z_0 the largest.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t route_key(float z, int32_t e) {  // larger key = ranks first
+  z = z == z ? (z == 0.f ? 0.f : z) : -INFINITY;
+  const uint32_t u = __float_as_uint(z);
+  return ((uint64_t)((u & 0x80000000u) ? ~u : (u | 0x80000000u)) << 32) | (uint32_t)(0x7fffffff - e);
+}
+// one block per position: sel[i][rank] and wt[i][rank]
+__global__ void __launch_bounds__(256) prefill_route_kernel(PrefillArgs a, int32_t pc) {
+  const Shape& s = a.s;
+  const int32_t i = blockIdx.x;
+  if (i >= pc) return;
+  __shared__ int32_t chosen[kMaxActive];
+  const float* z = a.rlogits + (int64_t)i * s.E;
+  for (int32_t e = threadIdx.x; e < s.E; e += blockDim.x) {
+    const uint64_t k = route_key(z[e], e);
+    int32_t rank = 0;
+    for (int32_t f = 0; f < s.E; ++f) rank += route_key(z[f], f) > k ? 1 : 0;
+    if (rank < s.A) chosen[rank] = e;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float x[kMaxActive];
+    const float z0 = z[chosen[0]] == z[chosen[0]] ? z[chosen[0]] : -INFINITY;
+    float sum = 0.f;
+    for (int32_t r = 0; r < s.A; ++r) {
+      const float zr = z[chosen[r]] == z[chosen[r]] ? z[chosen[r]] : -INFINITY;
+      x[r] = expf(zr - z0);
+      sum += x[r];
+    }
+    for (int32_t r = 0; r < s.A; ++r) {
+      a.sel[(int64_t)i * s.A + r] = chosen[r];
+      a.wt[(int64_t)i * s.A + r] = x[r] / sum;
+    }
+  }
+}
+// one block per expert: its positions in order (lists), their number (counts), and each choice's
+// place in the list (place)
+__global__ void __launch_bounds__(256) prefill_expert_lists_kernel(PrefillArgs a, int32_t pc) {
+  const int32_t e = blockIdx.x, A = a.s.A, t = threadIdx.x;
+  __shared__ int32_t scan[256];
+  int32_t base = 0;
+  for (int32_t i0 = 0; i0 < pc; i0 += 256) {
+    const int32_t i = i0 + t;
+    int32_t rank = -1;
+    if (i < pc)
+      for (int32_t r = 0; r < A; ++r)
+        if (a.sel[(int64_t)i * A + r] == e) rank = r;
+    scan[t] = rank >= 0 ? 1 : 0;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {  // inclusive prefix sum over the block
+      const int32_t add = t >= o ? scan[t - o] : 0;
+      __syncthreads();
+      scan[t] += add;
+      __syncthreads();
+    }
+    if (rank >= 0) {
+      const int32_t at = base + scan[t] - 1;
+      a.lists[(int64_t)e * kPrefillChunk + at] = (i << 4) | rank;
+      a.place[(int64_t)i * A + rank] = at;
+    }
+    base += scan[255];
+    __syncthreads();  // scan is reused
+  }
+  if (t == 0) a.counts[e] = base;
+}
+// the experts' first rows: the exclusive prefix sum of the list lengths (one thread, E is small)
+__global__ void __launch_bounds__(64) prefill_expert_offsets_kernel(PrefillArgs a) {
+  if (threadIdx.x != 0) return;
+  int32_t o = 0;
+  for (int32_t e = 0; e < a.s.E; ++e) {
+    a.offs[e] = o;
+    o += a.counts[e];
+  }
+}
+// Row i of the residual: x += the chosen experts' down-projection rows (already weighted), summed
+// in rank order; then the RMSNorm with gain (when given) as the next GEMM's two-part input.
+__global__ void __launch_bounds__(256) prefill_moe_combine_kernel(PrefillArgs a, const uint16_t* gain, int32_t pc) {
+  __shared__ float red[256];
+  const Shape& s = a.s;
+  const int32_t i = blockIdx.x;
+  if (i >= pc) return;
+  int64_t row[kMaxActive];
+  for (int32_t r = 0; r < s.A; ++r)
+    row[r] = (int64_t)(a.offs[a.sel[(int64_t)i * s.A + r]] + a.place[(int64_t)i * s.A + r]) * s.d;
+  float* xr = a.x + (int64_t)i * s.d;
+  for (int32_t c = threadIdx.x; c < s.d; c += 256) {
+    float y = 0.f;
+    for (int32_t r = 0; r < s.A; ++r) y += a.ey[row[r] + c];
+    xr[c] += y;
+  }
+  __syncthreads();  // the norm reads the row by other columns per thread
+  if (gain) norm_split_row(a, gain, i, red);
+}
+
+// ------------------------------------------------------------------------------------------
 // The chunked prompt pass: positions p0 .. p0 + n - 1, every layer, K/V rows written to the cache.
 // ------------------------------------------------------------------------------------------
 // One GEMM of a layer stage. The QKV and gate/up products end in their pair epilogues; the O and
@@ -616,6 +748,11 @@ static hipError_t gemm(const PrefillArgs& a, int st, int32_t layer, int32_t p0, 
   g.out = a.x;  // EPI_STORE: x += C
   g.ldo = s.d;
   g.accumulate = 1;
+  if (st == ST_RT) {  // the router: logits = C
+    g.out = a.rlogits;
+    g.ldo = s.E;
+    g.accumulate = 0;
+  }
   const int32_t K = g.K;
   // A GEMM with few output tiles (the O and down projections, N = d) splits K over up to 8
   // blocks per tile so that about two blocks run per CU; the partial sums go to the scratch
@@ -643,6 +780,49 @@ static hipError_t gemm(const PrefillArgs& a, int st, int32_t layer, int32_t p0, 
     if (norm_after) hipLaunchKernelGGL(prefill_norm_split_kernel, dim3(pc), dim3(256), 0, stream, a, norm_after, pc);
   }
   return hipGetLastError();
+}
+
+// A mixture-of-experts FFN over the chunk (its RMSNorm input in a3): router logits, the choice of
+// experts per position, the experts' token lists, each expert's gate/up and down products over its
+// positions (grouped GEMMs, one grid row per expert), and the weighted sum into the residual
+// followed by the next RMSNorm.
+static hipError_t moe_ffn(const PrefillArgs& a, int32_t layer, int32_t p0, int32_t pc, hipStream_t stream,
+                          const uint16_t* next_gain) {
+  const Shape& s = a.s;
+  hipError_t e = gemm(a, ST_RT, layer, p0, pc, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(prefill_route_kernel, dim3(pc), dim3(256), 0, stream, a, pc);
+  hipLaunchKernelGGL(prefill_expert_lists_kernel, dim3(s.E), dim3(256), 0, stream, a, pc);
+  hipLaunchKernelGGL(prefill_expert_offsets_kernel, dim3(1), dim3(64), 0, stream, a);
+  const int32_t nM = kPrefillChunk / kGemmM;  // token tiles per expert at most
+  GemmStage g{};
+  g.layer = layer;
+  g.p0 = p0;
+  g.splits = 1;
+  g.st = ST_GU;  // gate/up of the chosen experts: rows of a3, h (weighted) into h2
+  g.K = s.d;
+  g.N = 2 * s.Fe;
+  g.kper = g.K;
+  g.in = a.a3;
+  g.in_part = a.a_part;
+  g.epi = EPI_SWIGLU;
+  hipLaunchKernelGGL((prefill_gemm_kernel<false, 1>), dim3(nM * (g.N / kGemmN), s.E), dim3(256), 0, stream, a, g, pc);
+  g.st = ST_DN;  // down: rows of h2 into the experts' rows of ey
+  g.K = s.Fe;
+  g.N = s.d;
+  g.kper = g.K;
+  g.in = a.h2;
+  g.in_part = (int64_t)kPrefillChunk * s.F;
+  g.epi = EPI_STORE;
+  hipLaunchKernelGGL((prefill_gemm_kernel<false, 2>), dim3(nM * (g.N / kGemmN), s.E), dim3(256), 0, stream, a, g, pc);
+  hipLaunchKernelGGL(prefill_moe_combine_kernel, dim3(pc), dim3(256), 0, stream, a, next_gain, pc);
+  return hipGetLastError();
+}
+
+bool prefill_supports(const Shape& s) {
+  if (!s.moe()) return true;
+  return s.A >= 1 && s.A <= kMaxActive && s.A <= 15 && (2 * s.Fe) % kGemmN == 0 && s.d % kGemmN == 0 &&
+         s.Fe % kGemmKC == 0 && s.d % kGemmKC == 0;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int32_t p0, int32_t n, hipStream_t stream) {
@@ -673,10 +853,13 @@ hipError_t launch_prefill(const PrefillArgs& a, int32_t p0, int32_t n, hipStream
         hipLaunchKernelGGL((prefill_fattn_kernel<64, false>), ag, dim3(256), 0, stream, a, l, pos, pc);
       }
       if ((e = gemm(a, ST_O, l, pos, pc, stream, a.norms + (int64_t)l * 2 * s.d + s.d)) != hipSuccess) return e;
+      const uint16_t* next_gain = l + 1 < s.L ? a.norms + (int64_t)(l + 1) * 2 * s.d : nullptr;
+      if (s.moe()) {
+        if ((e = moe_ffn(a, l, pos, pc, stream, next_gain)) != hipSuccess) return e;
+        continue;
+      }
       if ((e = gemm(a, ST_GU, l, pos, pc, stream)) != hipSuccess) return e;  // SwiGLU into h2
-      if ((e = gemm(a, ST_DN, l, pos, pc, stream, l + 1 < s.L ? a.norms + (int64_t)(l + 1) * 2 * s.d : nullptr)) !=
-          hipSuccess)
-        return e;
+      if ((e = gemm(a, ST_DN, l, pos, pc, stream, next_gain)) != hipSuccess) return e;
     }
   }
   return hipGetLastError();

@@ -165,10 +165,12 @@ kie_status kie_create_static(const kie_config* cfg, const kie_weights* src, void
  * Process a prompt of n_tokens ids (device int32 [n_tokens]) at positions pos .. pos+n_tokens-1,
  * writing their K/V rows, then choose the next token (device int32 [1], first_token_dev) from the
  * logits of the last prompt position; those logits are written to last_logits_dev (device fp32
- * [V]) unless it is NULL. Advances the position by n_tokens. A dense model runs all but the last
- * position as matrix-core GEMMs; a mixture-of-experts model (each position routes its own
- * experts) and an 8-bit model run every position, one after the other, through the decode program
- * in one launch.
+ * [V]) unless it is NULL. Advances the position by n_tokens. All but the last position run as
+ * matrix-core GEMMs (8-bit codes are widened to bf16 as the GEMMs read them; in a mixture of
+ * experts each position's choice is made as in the decode program and every expert's positions
+ * form its own products); the last position runs through the decode program. A context created
+ * with kie_create_static has no room for the GEMMs' scratch: there every position runs through
+ * the decode program, one after the other, in one launch.
  * Errors: KIE_ERR_INVALID_ARG, KIE_ERR_CAPACITY, KIE_ERR_STATE, KIE_ERR_HIP. */
 kie_status kie_prefill(kie_ctx* ctx, const int32_t* tokens_dev, int32_t n_tokens, int32_t* first_token_dev,
                        float* last_logits_dev, const kie_sampling* sampling);
