@@ -345,9 +345,23 @@ def test_thread_split_is_bitwise_identical(oracle_lib, tiny_model):
 
 def test_against_torch_cpu_library_rendition(oracle_lib, tiny_model):
     """The decoder written with PyTorch CPU library routines (rms_norm, scaled_dot_product_attention
-    with its causal mask and 1/sqrt(hd) scale, silu, matmul) in fp32 over the whole sequence."""
+    with its causal mask and 1/sqrt(hd) scale, silu, matmul) in fp32 over the whole sequence: the
+    two fp32 renditions agree to 1e-6 in logits. The rendition runs on one thread: the thread count
+    changes the library's summation order, and where that moves a key or value across a bf16
+    rounding boundary, the positions after it differ by up to ~1e-5."""
     import torch
     import torch.nn.functional as F
+    threads = torch.get_num_threads()
+    torch.set_num_threads(1)
+    try:
+        ref, got = _torch_rendition(oracle_lib, tiny_model, torch, F)
+    finally:
+        torch.set_num_threads(threads)
+    assert rel_l2(got, ref) <= 1e-6
+    assert np.array_equal(got.argmax(1), ref.argmax(1))
+
+
+def _torch_rendition(oracle_lib, tiny_model, torch, F):
     cfg = synth.TINY
     d, hd, nq, nkv = cfg.d_model, cfg.head_dim, cfg.n_heads, cfg.n_kv_heads
 
@@ -383,9 +397,7 @@ def test_against_torch_cpu_library_rendition(oracle_lib, tiny_model):
         x = x + h @ t(tiny_model["w_down"][l]).T
     u = F.rms_norm(x, (d,), weight=t(tiny_model["final_norm"]), eps=cfg.rms_eps)
     ref = (u @ t(tiny_model["lm_head"]).T).numpy()
-    got = oracle_lib.OracleModel(cfg, tiny_model, n).run(prompt)
-    assert rel_l2(got, ref) <= 1e-4
-    assert np.array_equal(got.argmax(1), ref.argmax(1)) or rel_l2(got, ref) <= 1e-5
+    return ref, oracle_lib.OracleModel(cfg, tiny_model, n).run(prompt)
 
 
 def test_gemv_order_is_a_rounding_level_variant(oracle_lib):
