@@ -433,6 +433,11 @@ static kie_status create_impl(const kie_config* cfg, const kie_weights* src, voi
     return fail("rope table", e);
   if ((e = launch_stream_bases(s, w8, (int64_t*)(c->ws + c->wso.wbase), stm)) != hipSuccess)
     return fail("stream bases", e);
+  // the prompt pass's tile table (contexts with the prompt pass's scratch)
+  if (c->wso.end > c->wso.ptab &&
+      (e = launch_ptab(s, w8, (const int64_t*)(c->ws + c->wso.wbase), (int32_t*)(c->ws + c->wso.ptab), stm)) !=
+          hipSuccess)
+    return fail("prompt tile table", e);
   uint16_t* norms = (uint16_t*)(c->ws + c->wso.norms);
   for (int l = 0; l < L; ++l) {
     if ((e = hipMemcpyAsync(norms + (size_t)l * 2 * s.d, src->attn_norm[l], (size_t)s.d * 2, hipMemcpyDeviceToDevice,
@@ -738,6 +743,7 @@ kie_status kie_prefill(kie_ctx* ctx, const int32_t* tokens_dev, int32_t n_tokens
     a.q = (float*)(ctx->ws + ctx->wso.pq);
     a.attn_part = (float*)(ctx->ws + ctx->wso.pattn);
     a.wscale = ctx->w8 ? (const float*)(ctx->ws + ctx->wso.wscale) : nullptr;
+    a.ptab = (const int32_t*)(ctx->ws + ctx->wso.ptab);
     a.rlogits = a.wt = a.ey = nullptr;
     a.sel = a.place = a.lists = a.counts = a.offs = nullptr;
     if (ctx->s.moe()) {  // the experts' scratch

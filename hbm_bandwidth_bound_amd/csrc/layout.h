@@ -298,15 +298,38 @@ KIE_HD int32_t prefill_nmax(const Shape& s) {
   return n;
 }
 
+// The prompt pass's tile table: for every layer, stage of the fixed streams (QKV, O, the router,
+// gate/up, down), pair and unit (a run of consecutive k-tiles of one pair, unit_tiles long), the
+// unit's first tile in the packed image as packed_tile gives it, so that the prompt pass's GEMMs
+// look the placement up instead of recomputing it (int32: the image holds fewer than 2^31 tiles).
+template <int TK = kTileK>
+KIE_HD int32_t ptab_units(const Shape& s, int st) {  // entries of one stage of one layer
+  if (!s.in_stream(st)) return 0;
+  const int32_t kt = s.stage_kt<TK>(st);
+  return s.stage_pairs(st) * (kt / unit_tiles(kt));
+}
+template <int TK = kTileK>
+KIE_HD int64_t ptab_layer(const Shape& s) {
+  int64_t n = 0;
+  for (int st = ST_QKV; st <= ST_DN; ++st) n += ptab_units<TK>(s, st);
+  return n;
+}
+template <int TK = kTileK>
+KIE_HD int64_t ptab_index(const Shape& s, int st, int32_t l, int32_t gp, int32_t unit) {
+  int64_t o = (int64_t)l * ptab_layer<TK>(s);
+  for (int st2 = ST_QKV; st2 < st; ++st2) o += ptab_units<TK>(s, st2);
+  const int32_t kt = s.stage_kt<TK>(st);
+  return o + (int64_t)gp * (kt / unit_tiles(kt)) + unit;
+}
 // Workspace (bytes, 256-aligned pieces): exchange words, RoPE table [max_seq][hd/2] of (cos,sin),
 // per-stream base (in tiles, [nwg][8] + total), error word, norm gains [L][2][d] + final [d] (bf16),
 // trace counters, the prompt-pass scratch (residual [chunk][d] fp32, GEMM input [2][chunk][kmax]
 // bf16, down-projection input [2][chunk][F] bf16, split-K partial sums [chunk][nmax] fp32, queries
 // [chunk][nq hd] fp32, for long contexts the per-segment attention states
-// [segments][chunk][nq][hd + 2] fp32, and with experts moe_prefill_layout's pieces), and the
-// matrix scales of 8-bit weights [L][7] + [1] fp32.
+// [segments][chunk][nq][hd + 2] fp32, with experts moe_prefill_layout's pieces, and the tile table
+// of ptab_index, int32), and the matrix scales of 8-bit weights [L][7] + [1] fp32.
 struct Workspace {
-  int64_t exch, rope, wbase, err, norms, trace, px, pa3, ph2, pc, pq, pattn, pmoe, wscale, end;
+  int64_t exch, rope, wbase, err, norms, trace, px, pa3, ph2, pc, pq, pattn, pmoe, ptab, wscale, end;
 };
 constexpr int kTraceWords = 64;  // per wave: cycle counters of a KIE_TRACE build (0..31), and the
                                  // hop timeline of one sampled layer (32..63, wave 0 only)
@@ -349,7 +372,7 @@ KIE_HD Workspace workspace_layout(const Shape& s, bool prefill = true) {
   w.trace = o; o = align256(o + (int64_t)s.nwg * kWaves * kTraceWords * 8);
   w.wscale = o; o = align256(o + ((int64_t)s.L * 7 + 1) * 4);  // 8-bit weights: the matrix scales
   if (!prefill) {
-    w.px = w.pa3 = w.ph2 = w.pc = w.pq = w.pattn = w.pmoe = w.end = o;
+    w.px = w.pa3 = w.ph2 = w.pc = w.pq = w.pattn = w.pmoe = w.ptab = w.end = o;
     return w;
   }
   w.px = o; o = align256(o + (int64_t)kPrefillChunk * s.d * 4);
@@ -361,6 +384,11 @@ KIE_HD Workspace workspace_layout(const Shape& s, bool prefill = true) {
   if (prefill_attn_segs(s) > 1) o = align256(o + (int64_t)prefill_attn_segs(s) * kPrefillChunk * s.nq * (s.hd + 2) * 4);
   w.pmoe = o;
   if (s.moe()) o = align256(o + moe_prefill_layout(s).end);
+  w.ptab = o;
+  {  // sized for either weight format (tiles of 256 bf16 or 512 8-bit weights per row)
+    const int64_t a = ptab_layer<kTileK>(s), b = ptab_layer<2 * kTileK>(s);
+    o = align256(o + (int64_t)s.L * (a > b ? a : b) * 4);
+  }
   w.end = o;
   return w;
 }

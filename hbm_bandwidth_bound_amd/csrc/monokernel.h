@@ -74,6 +74,7 @@ hipError_t launch_pack_experts(const PackArgs& a, hipStream_t st);
 hipError_t launch_rope_table(float2* rope, int32_t max_seq, int32_t hd, float theta, hipStream_t st);
 hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t st);
 hipError_t launch_stream_bases(const Shape& s, bool w8, int64_t* wbase, hipStream_t st);
+hipError_t launch_ptab(const Shape& s, bool w8, const int64_t* wbase, int32_t* tab, hipStream_t st);
 constexpr int32_t kFloatChunk = 256;
 struct FloatChunk {
   float* dst;

@@ -175,6 +175,29 @@ __global__ void __launch_bounds__(1024) stream_bases_kernel(Shape s, int64_t* wb
     acc += stream_tiles<TK>(s, i / kWaves, i % kWaves);
   }
 }
+// The prompt pass's tile table (ptab_index): one thread per entry, each a packed_tile lookup;
+// blockIdx.y is the layer.
+template <int TK>
+__global__ void __launch_bounds__(256) ptab_kernel(Shape s, const int64_t* wbase, int32_t* tab) {
+  const int32_t l = blockIdx.y;
+  const int64_t per = ptab_layer<TK>(s);
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < per; e += (int64_t)gridDim.x * 256) {
+    int st = ST_QKV;
+    int64_t o = e;
+    while (o >= ptab_units<TK>(s, st)) o -= ptab_units<TK>(s, st++);
+    const int32_t kt = s.stage_kt<TK>(st), ks = unit_tiles(kt), S = kt / ks;
+    tab[(int64_t)l * per + e] = (int32_t)packed_tile<TK>(s, wbase, st, l, (int32_t)(o / S), (int32_t)(o % S) * ks);
+  }
+}
+hipError_t launch_ptab(const Shape& s, bool w8, const int64_t* wbase, int32_t* tab, hipStream_t st) {
+  const int64_t per = w8 ? ptab_layer<2 * kTileK>(s) : ptab_layer<kTileK>(s);
+  const dim3 grid((unsigned)((per + 255) / 256 < 1024 ? (per + 255) / 256 : 1024), (unsigned)s.L);
+  if (w8)
+    hipLaunchKernelGGL(ptab_kernel<2 * kTileK>, grid, dim3(256), 0, st, s, wbase, tab);
+  else
+    hipLaunchKernelGGL(ptab_kernel<kTileK>, grid, dim3(256), 0, st, s, wbase, tab);
+  return hipGetLastError();
+}
 hipError_t launch_stream_bases(const Shape& s, bool w8, int64_t* wbase, hipStream_t st) {
   if (w8)
     hipLaunchKernelGGL(stream_bases_kernel<2 * kTileK>, dim3(1), dim3(1024), 0, st, s, wbase);

@@ -27,6 +27,7 @@ struct PrefillArgs {
   float* q;                  // [chunk][nq * hd] rotated queries
   float* attn_part;          // [segments][chunk][nq][hd + 2] partial attention states
   const float* wscale;       // 8-bit weights: the matrix scales [L][7] (+ the LM head's); null for bf16
+  const int32_t* ptab;       // first tile of every unit of the streamed stages (ptab_index)
   // mixture of experts (moe_prefill_layout; null for dense models)
   float* rlogits;            // [chunk][E] router logits
   int32_t* sel;              // [chunk][A] chosen experts, rank order

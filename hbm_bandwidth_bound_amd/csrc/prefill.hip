@@ -176,7 +176,7 @@ __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillArgs a, GemmSt
         else if constexpr (XM == 2)
           tbase[nb] = nvalid[nb] ? xregion + expert_dn_tile(a.s, g.layer, ex, gp[nb], 0) : 0;
         else
-          tbase[nb] = nvalid[nb] ? packed_tile<TK>(a.s, a.wbase, g.st, g.layer, gp[nb], kt - kt % ks_unit) : 0;
+          tbase[nb] = nvalid[nb] ? a.ptab[ptab_index<TK>(a.s, g.st, g.layer, gp[nb], kt / ks_unit)] : 0;
       }
       const uint8_t* tp = a.packed + (tbase[nb] + kt % ks_unit) * kTileBytes + 8 * sel;
 #pragma unroll
@@ -318,6 +318,223 @@ __global__ void __launch_bounds__(256) prefill_gemm_kernel(PrefillArgs a, GemmSt
           }
         }
       }
+}
+
+// ------------------------------------------------------------------------------------------
+// The dense bf16 products (QKV, O, gate/up, down) as a pipelined GEMM on a larger tile: 128 tokens x
+// 64 pairs (128 rows) per block, 4 waves of 64 tokens x 32 pairs (2 x 2). Both operands are
+// staged in LDS by direct loads (gfx950 global_load_lds_dwordx4: 16 bytes per lane written at
+// M0 + 16 lane, no registers held while in flight), through kMmStages stages of 64 k, so that the
+// next stages' loads are in flight while one is multiplied; the 64 x 64 wave tile reads 12
+// operands from LDS per 32 MFMAs (LDS bandwidth, not the matrix cores, bounds smaller tiles).
+// Each weight operand is a whole packed tile lane: 4 k of the pair's row A and 4 k of its row B,
+// so a lane reading tile lanes L and L + 1 holds 8 k of both rows -- the operands of two MFMAs,
+// one for the pair's row A and one for its row B -- and its results hold both rows of the pair
+// (the epilogues need no lane exchange). Every accumulator takes its products in the same order
+// as in prefill_gemm_kernel (k ascending, the high part before the low part at each k step).
+// LDS layout of a stage (48 KB):
+//   A: [part 2][row 128][8 pieces of 16 bytes], piece c of row r stored at slot c ^ sa(r);
+//   B: [pair 64][16 pieces], tile lane L of pair P (16 per stage) stored at slot L ^ (P mod 16);
+// the XOR placements put the lanes of an operand read on distinct banks.
+// ------------------------------------------------------------------------------------------
+constexpr int kMmM = 128, kMmKC = 64, kMmStages = 3;
+constexpr int kMmPairs = kGemmN / 2;                      // pairs per block
+constexpr int kMmABytes = kGemmParts * kMmM * kMmKC * 2;  // 32 KB
+constexpr int kMmStageBytes = kMmABytes + kMmPairs * kMmKC * 4;
+// the first tile of each unit (a run of consecutive k-tiles of one pair) the block reads, per pair
+constexpr int kMmUnits = 16;
+constexpr int kMmLds = kMmStages * kMmStageBytes + kMmUnits * kMmPairs * 8;
+constexpr int kMmLoads = (kMmABytes + kMmPairs * kMmKC * 4) / 1024 / 4;  // wave loads per stage and wave
+extern __shared__ __align__(16) uint8_t mm_smem[];
+
+__device__ __forceinline__ int mm_sa(int r) { return (r ^ (r >> 3)) & 7; }
+// s_waitcnt immediate that waits until at most n vector memory operations are outstanding
+constexpr int mm_vmcnt(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+static_assert(kMmLoads * (kMmStages - 2) < 64, "vmcnt holds at most 63");
+// 16 bytes per lane from the 64-bit address p into LDS at lds_base + 16 * lane
+__device__ __forceinline__ void mm_load_lds(const void* p, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(p), "{m0}"(lds_base) : "memory");
+}
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u4v lds_read16(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) u4v*)(uintptr_t)addr;
+}
+
+// One block per CU (its LDS), so one wave per SIMD: the compiler is told so, and schedules the
+// operand reads ahead of the MFMAs instead of saving registers for waves that cannot run.
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+prefill_mm_kernel(PrefillArgs a, GemmStage g, int32_t pc) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int p = lane & 15, kg = lane >> 4, wm = wv & 1, wn = wv >> 1;
+  const int32_t nM = (pc + kMmM - 1) / kMmM, nN = g.N / kGemmN;
+  const int32_t b = (int32_t)blockIdx.x % (nM * nN), split = (int32_t)blockIdx.x / (nM * nN);
+  int32_t mt, nt;
+  if (nN % 8 == 0) {  // the token tiles of one weight tile on one XCD (as in prefill_gemm_kernel)
+    mt = (b / 8) % nM;
+    nt = b % 8 + 8 * ((b / 8) / nM);
+  } else {
+    mt = b % nM;
+    nt = b / nM;
+  }
+  const int32_t m0 = mt * kMmM;
+  const int32_t kbeg = split * g.kper, nk = g.kper / kMmKC;
+  const int32_t ks_unit = unit_tiles(a.s.stage_kt(g.st));
+  const uint32_t smem = lds_addr(mm_smem);
+
+  // the first packed tile of units u0 .. u0 + nu - 1 of the block's 64 pairs, from the tile table
+  int64_t* tbl = (int64_t*)(mm_smem + kMmStages * kMmStageBytes);
+  const int32_t u0 = (kbeg / kTileK) / ks_unit;
+  const int32_t nu = ((kbeg + g.kper - 1) / kTileK) / ks_unit - u0 + 1;  // at most kMmUnits (host)
+  for (int e = tid; e < kMmPairs * nu; e += 256) {
+    const int P = e % kMmPairs, ui = e / kMmPairs;
+    tbl[e] = a.ptab[ptab_index(a.s, g.st, g.layer, nt * kMmPairs + P, u0 + ui)];
+  }
+  __syncthreads();
+
+  // this lane's loads of a stage: A wave loads t = 8 wv + q (part t / 16, rows 8 (t % 16) ..
+  // + 7), B wave loads t = 4 wv + q (pairs 4 t .. 4 t + 3)
+  const uint8_t* abase[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int t = 8 * wv + q, part = t / 16, r = 8 * (t % 16) + (lane >> 3);
+    const int c = (lane & 7) ^ mm_sa(r);
+    abase[q] = (const uint8_t*)(g.in + part * g.in_part + (int64_t)(m0 + r) * g.K) + 16 * c;
+  }
+  // this lane's B sources in the current unit (the table is read again when a unit begins)
+  const uint8_t* bptr[4];
+  int32_t cur_unit = -1;
+  auto issue = [&](int32_t c) {  // chunk c of K into stage c % kMmStages
+    const int32_t k0 = kbeg + c * kMmKC, kt = k0 / kTileK;
+    const uint32_t st = smem + (uint32_t)(c % kMmStages) * kMmStageBytes;
+    if (kt / ks_unit != cur_unit) {
+      cur_unit = kt / ks_unit;
+      const int64_t* trow = tbl + (cur_unit - u0) * kMmPairs + 16 * wv + kg;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) bptr[q] = a.packed + trow[4 * q] * kTileBytes + 16 * ((lane & 15) ^ ((4 * q + kg) & 15));
+    }
+    const int64_t boff = (int64_t)(kt % ks_unit) * kTileBytes + 16 * ((k0 % kTileK) >> 2);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) mm_load_lds(bptr[q] + boff, st + kMmABytes + (16 * wv + 4 * q) * 256);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int t = 8 * wv + q;
+      mm_load_lds(abase[q] + 2 * (int64_t)k0, st + (t / 16) * (kMmM * kMmKC * 2) + (t % 16) * 1024);
+    }
+  };
+
+  f4 acc[4][2][2];  // [mb][pair group][row A, row B]
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[mb][j][0] = acc[mb][j][1] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < kMmStages - 1; ++c)
+    if (c < nk) issue(c);
+  for (int32_t c = 0; c < nk; ++c) {
+    // chunk c's loads of this wave have landed when at most the later chunks' loads remain
+    if (c + kMmStages - 2 < nk)
+      __builtin_amdgcn_s_waitcnt(mm_vmcnt(kMmLoads * (kMmStages - 2)));
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();  // every wave's loads of chunk c landed; chunk c - 1's stage is free
+    const uint32_t st = smem + (uint32_t)(c % kMmStages) * kMmStageBytes;
+    // every operand of the chunk is read before the first MFMA, so the reads overlap
+    constexpr int KS = kMmKC / 32;
+    u4v bu[KS][2][2], av[KS][4][kGemmParts];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int L = ks * 8 + 2 * kg;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t bs = st + kMmABytes + (32 * wn + 16 * j + p) * (kMmKC * 4);
+        bu[ks][j][0] = lds_read16(bs + 16 * (L ^ p));
+        bu[ks][j][1] = lds_read16(bs + 16 * ((L + 1) ^ p));
+      }
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int r = 64 * wm + mb * 16 + p, cc = ks * 4 + kg;
+#pragma unroll
+        for (int part = 0; part < kGemmParts; ++part)
+          av[ks][mb][part] = lds_read16(st + part * (kMmM * kMmKC * 2) + r * (kMmKC * 2) + 16 * (cc ^ mm_sa(r)));
+      }
+    }
+    // the loads of chunk c + 2, issued after this chunk's operand reads
+    if (c + kMmStages - 1 < nk) issue(c + kMmStages - 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 bx[2], by[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        bx[j] = __builtin_bit_cast(bf16x8, u4v{bu[ks][j][0].x, bu[ks][j][0].y, bu[ks][j][1].x, bu[ks][j][1].y});
+        by[j] = __builtin_bit_cast(bf16x8, u4v{bu[ks][j][0].z, bu[ks][j][0].w, bu[ks][j][1].z, bu[ks][j][1].w});
+      }
+#pragma unroll
+      for (int part = 0; part < kGemmParts; ++part)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          const bf16x8 A = __builtin_bit_cast(bf16x8, av[ks][mb][part]);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            acc[mb][j][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bx[j], acc[mb][j][0], 0, 0, 0);
+            acc[mb][j][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, by[j], acc[mb][j][1], 0, 0, 0);
+          }
+        }
+    }
+    // schedule: the chunk's LDS reads (12 per k step), then its MFMAs (32 per k step)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) __builtin_amdgcn_sched_group_barrier(0x100, 4 + 4 * kGemmParts, 0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) __builtin_amdgcn_sched_group_barrier(0x008, 16 * kGemmParts, 0);
+  }
+
+  // epilogue: the lane holds rows A and B of pair gp for tokens m0 + 64 wm + 16 mb + 4 kg + r
+  const Shape& s = a.s;
+  const int32_t half = s.hd / 2;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int32_t gp = nt * kMmPairs + 32 * wn + 16 * j + p;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int32_t i = m0 + 64 * wm + mb * 16 + kg * 4 + r;
+        if (i >= pc) continue;
+        const float ya = acc[mb][j][0][r], yb = acc[mb][j][1][r];
+        if (g.epi == EPI_STORE) {
+          if (g.splits > 1) {
+            *(float2*)(g.part + ((int64_t)split * pc + i) * g.N + 2 * gp) = float2{ya, yb};
+          } else {
+            float2* dst = (float2*)(g.out + (int64_t)i * g.ldo + 2 * gp);
+            float2 o = g.accumulate ? *dst : float2{0.f, 0.f};
+            o.x += ya;
+            o.y += yb;
+            *dst = o;
+          }
+        } else if (g.epi == EPI_SWIGLU) {
+          const int64_t o = (int64_t)i * s.F + gp;
+          split2((ya / (1.0f + expf(-ya))) * yb, a.h2 + o, a.h2 + (int64_t)kPrefillChunk * s.F + o);
+        } else {  // EPI_ROPE_KV: pair gp = dims (e, e + hd/2) of head hs
+          const int32_t hs = gp / half, e = gp % half, pos = g.p0 + i;
+          float y0 = ya, y1 = yb;
+          if (hs < s.nq + s.nkv) {
+            const float2 cs = a.rope[(int64_t)pos * half + e];
+            y0 = ya * cs.x - yb * cs.y;
+            y1 = yb * cs.x + ya * cs.y;
+          }
+          if (hs < s.nq) {
+            float* qr = a.q + (int64_t)i * s.qdim() + hs * s.hd;
+            qr[e] = y0;
+            qr[e + half] = y1;
+          } else {
+            const int kv = hs < s.nq + s.nkv ? 0 : 1;
+            const int32_t jh = kv == 0 ? hs - s.nq : hs - s.nq - s.nkv;
+            uint16_t* row = a.kv + kv_offset(s, g.layer, kv, jh, pos);
+            row[e] = (uint16_t)f32_to_bf16(y0);
+            row[e + half] = (uint16_t)f32_to_bf16(y1);
+          }
+        }
+      }
+  }
 }
 
 // Row i of the residual: x += the K shares' partial sums (in share order), then the RMSNorm of
@@ -765,7 +982,11 @@ static hipError_t gemm(const PrefillArgs& a, int st, int32_t layer, int32_t p0, 
       g.splits *= 2;
   g.kper = K / g.splits;
   g.part = a.c;
-  if (a.wscale)
+  const int32_t ks = unit_tiles(s.stage_kt(st));
+  if (!a.wscale && g.N % kGemmN == 0 && (g.kper / kTileK + ks - 1) / ks + 1 <= kMmUnits)
+    hipLaunchKernelGGL(prefill_mm_kernel, dim3((g.N / kGemmN) * ((pc + kMmM - 1) / kMmM) * g.splits), dim3(256), kMmLds,
+                       stream, a, g, pc);
+  else if (a.wscale)
     hipLaunchKernelGGL(prefill_gemm_kernel<true>, dim3(tiles * g.splits), dim3(256), 0, stream, a, g, pc);
   else
     hipLaunchKernelGGL(prefill_gemm_kernel<false>, dim3(tiles * g.splits), dim3(256), 0, stream, a, g, pc);
@@ -827,6 +1048,8 @@ bool prefill_supports(const Shape& s) {
 
 hipError_t launch_prefill(const PrefillArgs& a, int32_t p0, int32_t n, hipStream_t stream) {
   const Shape& s = a.s;
+  hipError_t e0 = hipFuncSetAttribute((const void*)prefill_mm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kMmLds);
+  if (e0 != hipSuccess) return e0;
   for (int32_t c0 = 0; c0 < n; c0 += kPrefillChunk) {
     const int32_t pc = n - c0 < kPrefillChunk ? n - c0 : kPrefillChunk;
     const int32_t pos = p0 + c0;
