@@ -983,9 +983,12 @@ static hipError_t gemm(const PrefillArgs& a, int st, int32_t layer, int32_t p0, 
   g.kper = K / g.splits;
   g.part = a.c;
   const int32_t ks = unit_tiles(s.stage_kt(st));
-  if (!a.wscale && g.N % kGemmN == 0 && (g.kper / kTileK + ks - 1) / ks + 1 <= kMmUnits)
-    hipLaunchKernelGGL(prefill_mm_kernel, dim3((g.N / kGemmN) * ((pc + kMmM - 1) / kMmM) * g.splits), dim3(256), kMmLds,
-                       stream, a, g, pc);
+  // prefill_mm_kernel holds a CU's LDS per block: it is used where its grid covers every CU (the
+  // QKV product of a 512-token chunk of the 1.6B shape has 128 blocks and runs faster on the
+  // smaller tiles of prefill_gemm_kernel, whose products are accumulated in the same order)
+  const int32_t mm_blocks = (g.N / kGemmN) * ((pc + kMmM - 1) / kMmM) * g.splits;
+  if (!a.wscale && g.N % kGemmN == 0 && (g.kper / kTileK + ks - 1) / ks + 1 <= kMmUnits && mm_blocks >= s.nwg)
+    hipLaunchKernelGGL(prefill_mm_kernel, dim3(mm_blocks), dim3(256), kMmLds, stream, a, g, pc);
   else if (a.wscale)
     hipLaunchKernelGGL(prefill_gemm_kernel<true>, dim3(tiles * g.splits), dim3(256), 0, stream, a, g, pc);
   else
