@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--workload", default="1.6b-1k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="greedy launches of the same K steps after the timed one, reported as median and "
+                         "stdev; 0 = skip")
     ap.add_argument("--single-step-launches", type=int, default=0,
                     help="also time this many one-token launches (launch-overhead comparison); 0 = skip")
     return ap.parse_args()
@@ -218,6 +221,23 @@ def main():
     eng.sync()
     topk_tok_s = K / (e0.elapsed_time(e1) * 1e-3)
 
+    # the timed launch repeated (same positions, same tokens): the spread of the rate on this machine
+    reps = None
+    if args.repeats > 0:
+        rates = []
+        for _ in range(args.repeats):
+            eng.set_position(P)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            eng.generate(first, K, out)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            eng.sync()
+            rates.append(K / (e0.elapsed_time(e1) * 1e-3))
+        reps = {"launches": len(rates), "tok_s": [round(r, 2) for r in rates],
+                "median": round(float(np.median(rates)), 2), "stdev": round(float(np.std(rates, ddof=1)), 2)
+                if len(rates) > 1 else 0.0}
+
     # one-token launches (the per-launch overhead comparison)
     single = None
     if args.single_step_launches > 0:
@@ -290,6 +310,7 @@ def main():
                   "ttft_ms_prompt_pass": round(ttft_ms, 2), "ttft_ms_first_call": round(ttft[0], 2),
                   "prompt_pass": prompt_pass,
                   "one_token_launches": single,
+                  "repeat_launches": reps,
                   "topk50_T0.8_tok_s": round(topk_tok_s, 2),
                   "source_sha": source_hash()},
     }

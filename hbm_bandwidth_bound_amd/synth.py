@@ -109,8 +109,16 @@ M1_6B_FP8 = M1_6B.scaled(name="1.6b-fp8", weight_format=1)
 M1_6B_FP8_2L = M1_6B.scaled(name="1.6b-fp8-2l", n_layers=2, weight_format=1)
 M8B_FP8 = M8B.scaled(name="8b-fp8", weight_format=1)
 
+# One GPU's share of the 1.6B model under 8-way tensor parallelism: QKV and gate/up split by
+# output rows (2 query heads and their KV head, 1,024 of the FFN's 8,192), O and down by input
+# columns (each GPU's partial residual update of all 2,048 outputs), the LM head by vocabulary
+# (4,096 rows). On one GPU the all-reduce of the partial sums over a single member is the
+# identity, so the share runs as a decoder of this shape; the 2-layer cut is a parity shape.
+M1_6B_TP8 = M1_6B.scaled(name="1.6b-tp8", n_heads=2, n_kv_heads=1, ffn_dim=1024, vocab_size=4096)
+M1_6B_TP8_2L = M1_6B_TP8.scaled(name="1.6b-tp8-2l", n_layers=2)
+
 MODELS: Dict[str, ModelConfig] = {m.name: m for m in (TINY, M1_6B, M8B, MOE, TINY_MOE, SMALL_MOE, MOE_2L, TINY_FP8,
-                                                       M1_6B_FP8, M1_6B_FP8_2L, M8B_FP8)}
+                                                       M1_6B_FP8, M1_6B_FP8_2L, M8B_FP8, M1_6B_TP8, M1_6B_TP8_2L)}
 
 WORKLOADS: Dict[str, Workload] = {
     "tiny": Workload("tiny", TINY, 64, 32),
@@ -121,6 +129,7 @@ WORKLOADS: Dict[str, Workload] = {
     "moe-1k": Workload("moe-1k", MOE, 1024, 256),
     "1.6b-1k-fp8": Workload("1.6b-1k-fp8", M1_6B_FP8, 1024, 512),
     "8b-2k-fp8": Workload("8b-2k-fp8", M8B_FP8, 2048, 256),
+    "1.6b-tp8-1k": Workload("1.6b-tp8-1k", M1_6B_TP8, 1024, 512),
 }
 
 # Tensor numbering for the weight generator: 0 embed, 1 lm_head, then per layer l

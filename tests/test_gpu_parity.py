@@ -336,6 +336,7 @@ OTHER_SHAPES = [
     synth.ModelConfig("g4-hd64", 2, 512, 8, 2, 64, 1024, 3002),        # G = 4, hd 64
     synth.ModelConfig("g8-hd128", 2, 1024, 8, 1, 128, 1536, 4096),     # G = 8, one KV head, hd 128
     synth.ModelConfig("mha-hd128", 1, 512, 4, 4, 128, 768, 1000),      # G = 1, hd 128, 3-tile FFN rows
+    synth.M1_6B_TP8_2L,  # one GPU's 8-way tensor-parallel share of the 1.6B layer shape
 ]
 
 
