@@ -729,9 +729,16 @@ struct Wk {
             b1 = fmaf(p.y, x1.w, b1);
           }
         } else {
+        // the unit's activations are read from LDS before its products (the schedule barrier keeps
+        // the KS reads together), so that their latency is paid once per unit: read tile by tile,
+        // each read was waited for on its own before the tile's products
+        v4f xs[KS];
+#pragma unroll
+        for (int t = 0; t < KS; ++t) xs[t] = *(const v4f*)(xa + t * kTileK);
+        __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);
 #pragma unroll
         for (int t = 0; t < KS; ++t) {
-          const v4f x = *(const v4f*)(xa + t * kTileK);
+          const v4f x = xs[t];
           const v4u wt = cur[us * KS + t];
           a0 = fmaf(bf16lo(wt.x), x.x, a0);
           a1 = fmaf(bf16hi(wt.x), x.y, a1);
