@@ -45,11 +45,12 @@ __device__ __forceinline__ void lds_st(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN kept quiet)
+// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN kept quiet). Written as a select,
+// so that no branch (and no change of the execution mask) surrounds each conversion.
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return (u & 0x7fffffffu) > 0x7f800000u ? ((u >> 16) | 0x40u) : rne;
 }
 
 // Buffer resource over [base, base + bytes): a raw buffer load through it whose per-lane offset

@@ -789,9 +789,10 @@ struct Wk {
     const float s = wave_sum(x);
     if (lane == 0) L.scr[v] = s;
     bar();
-    float t = 0.f;
-#pragma unroll
-    for (int k = 0; k < kWaves; ++k) t += L.scr[k];
+    // the 8 wave sums in two 16-byte reads, then added in wave order
+    static_assert(kWaves == 8, "two 16-byte reads hold the wave sums");
+    const v4f lo = *(const v4f*)L.scr, hi = *(const v4f*)(L.scr + 4);
+    const float t = (((((((0.f + lo.x) + lo.y) + lo.z) + lo.w) + hi.x) + hi.y) + hi.z) + hi.w;
     bar();
     return t;
   }
@@ -1069,11 +1070,11 @@ __device__ __forceinline__ void attention(WK& K, const Att& at, int32_t l, int32
       }
       if (nbw > 0) kv_batch(nbw - 1, kn, vn);
       if (at.has_p && v == at.nkt % kWaves) {  // the current position, rounded to bf16 like the cache
-        auto cur_row = [&](const float* src) {
-          uint32_t b[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) b[e] = f32_to_bf16(src[dg * 8 + e]);
-          return v4u{b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16)};
+        auto cur_row = [&](const float* src) {  // the lane's 8 values in two 16-byte LDS reads
+          const v4f a = *(const v4f*)(src + dg * 8);
+          const v4f c = *(const v4f*)(src + dg * 8 + 4);
+          return v4u{f32_to_bf16(a.x) | (f32_to_bf16(a.y) << 16), f32_to_bf16(a.z) | (f32_to_bf16(a.w) << 16),
+                     f32_to_bf16(c.x) | (f32_to_bf16(c.y) << 16), f32_to_bf16(c.z) | (f32_to_bf16(c.w) << 16)};
         };
         update(cur_row(L.q + G * HD), cur_row(L.q + (G + 1) * HD), lpos == 0);
       }
@@ -1211,11 +1212,11 @@ __device__ __forceinline__ void attention(WK& K, const Att& at, int32_t l, int32
     if (nbw > 0) kv_batch(nbw - 1, kn, vn);
     // the current position: its K/V come from the exchange, rounded to bf16 like the cache
     if (at.has_p && v == at.nkt % kWaves) {
-      auto cur_row = [&](const float* src) {
-        uint32_t b[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) b[e] = f32_to_bf16(src[dg * 8 + e]);
-        return v4u{b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16)};
+      auto cur_row = [&](const float* src) {  // the lane's 8 values in two 16-byte LDS reads
+        const v4f a = *(const v4f*)(src + dg * 8);
+        const v4f c = *(const v4f*)(src + dg * 8 + 4);
+        return v4u{f32_to_bf16(a.x) | (f32_to_bf16(a.y) << 16), f32_to_bf16(a.z) | (f32_to_bf16(a.w) << 16),
+                   f32_to_bf16(c.x) | (f32_to_bf16(c.y) << 16), f32_to_bf16(c.z) | (f32_to_bf16(c.w) << 16)};
       };
       update(cur_row(L.q + G * HD), cur_row(L.q + (G + 1) * HD), lpos == 0);
     }
